@@ -1,0 +1,274 @@
+// C ABI of the KDA layer library: argument validation and dispatch.
+//
+// Every check runs before the first launch, so a call that returns an error
+// has touched no buffer (refuse unsupported configurations up front rather
+// than failing mid-run, as llama.cpp PR #27754 does for its indexer cache;
+// a missing kda.gate_lower_bound is an error, never a silent default, as in
+// its metadata commit; a rollback depth is never silently clamped, as its
+// KDA commit warns).
+#include "../../include/kda.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "kda_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kda_status fail(kda_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+kda_status ok() {
+  g_last_error[0] = '\0';
+  return KDA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kda_status check_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is null", name);
+  if (!aligned16(p)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  return KDA_OK;
+}
+
+#define KDA_TRY(expr)                      \
+  do {                                     \
+    kda_status _s = (expr);                \
+    if (_s != KDA_OK) return _s;           \
+  } while (0)
+
+kda_status check_desc(const kda_layer_desc* d) {
+  if (d == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is null");
+  if (d->num_heads < 1 || d->head_dim_k < 1 || d->head_dim_v < 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "num_heads / head dims must be >= 1");
+  if (d->num_heads > 65535) return fail(KDA_ERR_UNSUPPORTED, "num_heads > 65535");
+  if (d->head_dim_k != d->head_dim_v)
+    return fail(KDA_ERR_UNSUPPORTED, "head_dim_k (%d) != head_dim_v (%d)", d->head_dim_k, d->head_dim_v);
+  const int D = d->head_dim_k;
+  if (D != 16 && D != 32 && D != 64 && D != 128)
+    return fail(KDA_ERR_UNSUPPORTED, "head dim %d not in {16, 32, 64, 128}", D);
+  if (d->conv_width < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "conv_width must be >= 1");
+  if (d->conv_width > kda::kMaxConvWidth)
+    return fail(KDA_ERR_UNSUPPORTED, "conv_width %d > %d", d->conv_width, kda::kMaxConvWidth);
+  if ((d->io_dtype != KDA_F32 && d->io_dtype != KDA_BF16) || (d->out_dtype != KDA_F32 && d->out_dtype != KDA_BF16))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "io_dtype / out_dtype must be KDA_F32 or KDA_BF16");
+  if (std::isnan(d->gate_lower_bound))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "gate_lower_bound is absent (NaN); it is required");
+  if (!std::isfinite(d->gate_lower_bound)) return fail(KDA_ERR_INVALID_ARGUMENT, "gate_lower_bound is not finite");
+  if (!std::isfinite(d->l2_eps) || !(d->l2_eps > 0.f)) return fail(KDA_ERR_INVALID_ARGUMENT, "l2_eps must be > 0");
+  if (!std::isfinite(d->rms_eps) || d->rms_eps < 0.f) return fail(KDA_ERR_INVALID_ARGUMENT, "rms_eps must be >= 0");
+  if (!std::isfinite(d->scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  KDA_TRY(check_ptr(d->conv_w, "desc.conv_w"));
+  KDA_TRY(check_ptr(d->A_log, "desc.A_log"));
+  KDA_TRY(check_ptr(d->dt_bias, "desc.dt_bias"));
+  KDA_TRY(check_ptr(d->norm_w, "desc.norm_w"));
+  return KDA_OK;
+}
+
+kda_status check_batch(int32_t B, int32_t T) {
+  if (B < 0 || T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B and T must be >= 0");
+  if (B > 65535) return fail(KDA_ERR_UNSUPPORTED, "B > 65535");
+  return KDA_OK;
+}
+
+kda_status check_chunk(const kda_layer_desc* d) {
+  if (d->chunk_size < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "chunk_size must be >= 1");
+  if (d->chunk_size != 16 && d->chunk_size != 32 && d->chunk_size != 64)
+    return fail(KDA_ERR_UNSUPPORTED, "chunk_size %d not in {16, 32, 64}", d->chunk_size);
+  return KDA_OK;
+}
+
+kda::LayerArgs make_args(const kda_layer_desc* d, int B, int T) {
+  kda::LayerArgs a{};
+  a.B = B;
+  a.T = T;
+  a.H = d->num_heads;
+  a.D = d->head_dim_k;
+  a.W = d->conv_width;
+  a.lb = d->gate_lower_bound;
+  a.l2_eps = d->l2_eps;
+  a.rms_eps = d->rms_eps;
+  a.scale = d->scale;
+  a.conv_w = d->conv_w;
+  a.A_log = d->A_log;
+  a.dt_bias = d->dt_bias;
+  a.norm_w = d->norm_w;
+  return a;
+}
+
+kda_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+kda_status check_token_tensors(const void* qkv, const void* f, const void* beta, const void* g_out) {
+  KDA_TRY(check_ptr(qkv, "qkv"));
+  KDA_TRY(check_ptr(f, "f"));
+  KDA_TRY(check_ptr(beta, "beta"));
+  KDA_TRY(check_ptr(g_out, "g_out"));
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KDA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* kda_last_error(void) { return g_last_error; }
+
+size_t kda_prefill_workspace_size(const kda_layer_desc* desc, int32_t B, int32_t T) {
+  if (check_desc(desc) != KDA_OK || check_batch(B, T) != KDA_OK || check_chunk(desc) != KDA_OK) return (size_t)-1;
+  if (!kda::prefill_mfma_supported(desc->head_dim_k, desc->chunk_size, desc->io_dtype)) return 0;
+  return kda::prefill_mfma_workspace(B, T, desc->num_heads, desc->head_dim_k, desc->chunk_size);
+}
+
+kda_status kda_prefill(const kda_layer_desc* desc, int32_t B, int32_t T, const void* qkv, const void* f,
+                       const void* beta, const void* g_out, float* state, void* conv_state, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  KDA_TRY(check_desc(desc));
+  KDA_TRY(check_batch(B, T));
+  KDA_TRY(check_chunk(desc));
+  if (B == 0 || T == 0) return ok();
+  KDA_TRY(check_token_tensors(qkv, f, beta, g_out));
+  KDA_TRY(check_ptr(state, "state"));
+  if (desc->conv_width > 1) KDA_TRY(check_ptr(conv_state, "conv_state"));
+  KDA_TRY(check_ptr(out, "out"));
+  kda::LayerArgs a = make_args(desc, B, T);
+  a.qkv = qkv;
+  a.f = f;
+  a.beta = beta;
+  a.g_out = g_out;
+  a.state_in = state;
+  a.state_out = state;
+  a.conv_in = conv_state;
+  a.conv_out = desc->conv_width > 1 ? conv_state : nullptr;
+  a.out = out;
+  a.snapshots = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kda::prefill_mfma_supported(a.D, desc->chunk_size, desc->io_dtype)) {
+    const size_t need = kda::prefill_mfma_workspace(B, T, a.H, a.D, desc->chunk_size);
+    if (need > 0) {
+      if (workspace == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is null (%zu bytes needed)", need);
+      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+      if (workspace_bytes < need)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    }
+    return launched(kda::launch_prefill_mfma(a, workspace, workspace_bytes, desc->out_dtype, s), "kda_prefill");
+  }
+  return launched(kda::launch_prefill_generic(a, desc->chunk_size, desc->io_dtype, desc->out_dtype, s),
+                  "kda_prefill");
+}
+
+kda_status kda_decode_step(const kda_layer_desc* desc, int32_t B, const void* qkv, const void* f,
+                           const void* beta, const void* g_out, float* state, void* conv_state, void* out,
+                           void* stream) {
+  KDA_TRY(check_desc(desc));
+  KDA_TRY(check_batch(B, 1));
+  if (B == 0) return ok();
+  KDA_TRY(check_token_tensors(qkv, f, beta, g_out));
+  KDA_TRY(check_ptr(state, "state"));
+  if (desc->conv_width > 1) KDA_TRY(check_ptr(conv_state, "conv_state"));
+  KDA_TRY(check_ptr(out, "out"));
+  kda::LayerArgs a = make_args(desc, B, 1);
+  a.qkv = qkv;
+  a.f = f;
+  a.beta = beta;
+  a.g_out = g_out;
+  a.state_in = state;
+  a.state_out = state;
+  a.conv_in = conv_state;
+  a.conv_out = desc->conv_width > 1 ? conv_state : nullptr;
+  a.out = out;
+  a.snapshots = 0;
+  return launched(kda::launch_recurrent(a, desc->io_dtype, desc->out_dtype, static_cast<hipStream_t>(stream)),
+                  "kda_decode_step");
+}
+
+kda_status kda_verify_block(const kda_layer_desc* desc, int32_t B, int32_t T_d, const void* qkv, const void* f,
+                            const void* beta, const void* g_out, const float* state, const void* conv_state,
+                            float* snaps, void* out, void* stream) {
+  KDA_TRY(check_desc(desc));
+  KDA_TRY(check_batch(B, T_d));
+  if (T_d > 255) return fail(KDA_ERR_UNSUPPORTED, "draft block T_d = %d > 255", T_d);
+  if (B == 0 || T_d == 0) return ok();
+  KDA_TRY(check_token_tensors(qkv, f, beta, g_out));
+  KDA_TRY(check_ptr(state, "state"));
+  if (desc->conv_width > 1) KDA_TRY(check_ptr(conv_state, "conv_state"));
+  KDA_TRY(check_ptr(snaps, "snaps"));
+  KDA_TRY(check_ptr(out, "out"));
+  kda::LayerArgs a = make_args(desc, B, T_d);
+  a.qkv = qkv;
+  a.f = f;
+  a.beta = beta;
+  a.g_out = g_out;
+  a.state_in = state;
+  a.state_out = snaps;
+  a.conv_in = conv_state;
+  a.conv_out = nullptr;
+  a.out = out;
+  a.snapshots = 1;
+  return launched(kda::launch_recurrent(a, desc->io_dtype, desc->out_dtype, static_cast<hipStream_t>(stream)),
+                  "kda_verify_block");
+}
+
+kda_status kda_rollback(const kda_layer_desc* desc, int32_t B, int32_t T_d, const int32_t* accepted_host,
+                        const float* snaps, const void* qkv_block, float* state, void* conv_state, void* stream) {
+  KDA_TRY(check_desc(desc));
+  KDA_TRY(check_batch(B, T_d));
+  if (T_d > 255) return fail(KDA_ERR_UNSUPPORTED, "draft block T_d = %d > 255", T_d);
+  if (B == 0) return ok();
+  if (accepted_host == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "accepted_host is null");
+  bool any = false;
+  for (int32_t b = 0; b < B; ++b) {
+    if (accepted_host[b] < 0 || accepted_host[b] > T_d)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "accepted[%d] = %d outside 0..%d", b, accepted_host[b], T_d);
+    any = any || accepted_host[b] > 0;
+  }
+  if (!any) return ok();
+  KDA_TRY(check_ptr(snaps, "snaps"));
+  KDA_TRY(check_ptr(qkv_block, "qkv_block"));
+  KDA_TRY(check_ptr(state, "state"));
+  if (desc->conv_width > 1) KDA_TRY(check_ptr(conv_state, "conv_state"));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t b0 = 0; b0 < B; b0 += kda::kRollbackBatch) {
+    kda::RollbackArgs r{};
+    r.B0 = b0;
+    r.nB = (B - b0) < kda::kRollbackBatch ? (B - b0) : kda::kRollbackBatch;
+    r.T_d = T_d;
+    r.H = desc->num_heads;
+    r.D = desc->head_dim_k;
+    r.W = desc->conv_width;
+    r.snaps = snaps;
+    r.qkv = qkv_block;
+    r.state = state;
+    r.conv_state = conv_state;
+    for (int i = 0; i < r.nB; ++i) r.accepted[i] = (uint8_t)accepted_host[b0 + i];
+    kda_status st = launched(kda::launch_rollback(r, desc->io_dtype, s), "kda_rollback");
+    if (st != KDA_OK) return st;
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Device-side helpers shared by the KDA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// bf16 values travel as raw 16-bit patterns; fp32 as float.
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float x) {
+  // round to nearest even; NaN stays NaN (quiet bit forced)
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ void store_as(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_as(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+
+template <typename T>
+__device__ __forceinline__ float load_f32(const T* p) { return to_f32(*p); }
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming (non-temporal) 16-byte store: data written once and not re-read by this kernel.
+__device__ __forceinline__ void store_nt(float* p, float4 v) {
+  f32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// Sum over the 64 lanes of a wavefront; every lane gets the total.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Sum over groups of `width` consecutive lanes (width a power of two <= 64).
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = WIDTH / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace kda

@@ -1,0 +1,56 @@
+// Internal launch interface between the C ABI (kda_abi.cpp) and the kernels.
+// Not part of the public ABI: the public declarations live in include/kda.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kMaxConvWidth = 8;       // conv taps supported (W - 1 <= 7 raw inputs of state)
+constexpr int kRollbackBatch = 256;    // sequences per rollback launch (accepted counts ride in the args)
+
+enum IoType { kF32 = 0, kBF16 = 1 };
+
+// Arguments shared by the recurrent (decode / verify) kernels and the prefill kernels.
+struct LayerArgs {
+  int B, T, H, D, W;
+  float lb, l2_eps, rms_eps, scale;
+  const void* qkv;      // [B, T, 3*H*D] io
+  const void* f;        // [B, T, H*D] io
+  const void* beta;     // [B, T, H] io
+  const void* g_out;    // [B, T, H*D] io
+  const void* conv_w;   // [3*H*D, W] io
+  const float* A_log;   // [H]
+  const float* dt_bias; // [H*D]
+  const void* norm_w;   // [D] io
+  const float* state_in;
+  float* state_out;     // decode / prefill: [B, H, D, D] (may alias state_in); verify: snapshots [B, T, H, D, D]
+  const void* conv_in;  // [B, 3*H*D, W-1] io
+  void* conv_out;       // may alias conv_in; nullptr: conv state not written (verify)
+  void* out;            // [B, T, H*D] out type
+  int snapshots;        // 1: write the state after every token to state_out (verify)
+};
+
+struct RollbackArgs {
+  int B0, nB, T_d, H, D, W;
+  const float* snaps;   // [B, T_d, H, D, D]
+  const void* qkv;      // [B, T_d, 3*H*D] io
+  float* state;         // [B, H, D, D]
+  void* conv_state;     // [B, 3*H*D, W-1] io
+  uint8_t accepted[kRollbackBatch];
+};
+
+hipError_t launch_recurrent(const LayerArgs& a, int io, int ot, hipStream_t s);
+hipError_t launch_rollback(const RollbackArgs& a, int io, hipStream_t s);
+
+// Chunked prefill, fp32 VALU form (any supported head size; internal chunk <= 4096 / D).
+hipError_t launch_prefill_generic(const LayerArgs& a, int chunk, int io, int ot, hipStream_t s);
+
+// Chunked prefill on bf16 MFMA (D = 128, chunk 64, bf16 io).
+bool prefill_mfma_supported(int D, int chunk, int io);
+size_t prefill_mfma_workspace(int B, int T, int H, int D, int chunk);
+hipError_t launch_prefill_mfma(const LayerArgs& a, void* ws, size_t ws_bytes, int ot, hipStream_t s);
+
+}  // namespace kda

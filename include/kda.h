@@ -1,0 +1,153 @@
+/*
+ * kda.h — C ABI of the MI355X-native Kimi Delta Attention (KDA) layer library.
+ *
+ * The layer (llama.cpp PR #27754 "model: add GLM-5-Next (GLM-5.3-Flash)",
+ * KDA commit message; Splash issue #740, maintainer answer):
+ *   1. one depthwise causal conv over the concatenated q|k|v channels, whose
+ *      state is one contiguous block of the W-1 previous raw inputs;
+ *   2. SiLU on the conv output;
+ *   3. q and k L2-normalised per head as x / max(||x||, l2_eps) (l2_eps is a
+ *      literal 1e-6 in the model), q then multiplied by `scale`;
+ *   4. a bounded-sigmoid per-channel log-decay
+ *        g = gate_lower_bound * sigmoid(exp(A_log[h]) * (f + dt_bias)),
+ *      dt_bias added per channel before the reshape to heads, A per head;
+ *   5. per head a d_k x d_v fp32 state S (row = key channel) that decays on
+ *      the key axis and takes a beta-weighted delta-rule update per token:
+ *        S <- Diag(exp(g_t)) S;  u = beta_t (v_t - S^T k_t);  S <- S + k_t u^T;
+ *        o_t = S^T q_t;
+ *   6. a gated output RMSNorm with a plain weight over d_v per (token, head):
+ *        out = o / sqrt(mean(o^2) + rms_eps) * norm_w * sigmoid(g_out).
+ * Speculative decoding needs the state to roll back to an accepted prefix of
+ * a verified draft block (dflash-mlx issue #63, "What the backend needs";
+ * the DFlash2 drafter proposes blocks of 8 tokens, "Context").
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller, row-major,
+ *     16-byte aligned.  The library allocates no device memory and keeps no
+ *     state between calls; prefill scratch comes from the caller's workspace.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  The returned status covers argument validation and launch
+ *     errors only.  Validation runs before any launch: a call that returns an
+ *     error has touched no buffer.
+ *   - The library never aborts or throws; kda_last_error() returns a
+ *     thread-local description of the most recent error.
+ *   - Channel order of qkv: [q head 0..H-1 | k head 0..H-1 | v head 0..H-1],
+ *     each head's d channels contiguous.  f and g_out are [.., H*d] in head
+ *     order; beta is [.., H].
+ *   - io_dtype (KDA_F32 or KDA_BF16) is the type of qkv, f, beta, g_out,
+ *     conv_w, norm_w and conv_state; out_dtype the type of out; the state,
+ *     the snapshots, A_log and dt_bias are always fp32.
+ *   - Supported: d_k == d_v in {16, 32, 64, 128}; conv_width 1..8;
+ *     prefill chunk_size in {16, 32, 64}.  Other shapes return
+ *     KDA_ERR_UNSUPPORTED.  bf16 io with d = 128 and chunk 64 runs the bf16
+ *     matrix-core prefill; every other prefill runs the fp32 vector-ALU form.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARGUMENT = 1, /* null / misaligned pointer, bad size, NaN gate bound, ... */
+  KDA_ERR_UNSUPPORTED = 2,      /* valid request for a shape or dtype this build does not run */
+  KDA_ERR_HIP = 3               /* a HIP launch failed */
+} kda_status;
+
+typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Per-layer description.  Parameter pointers are device pointers. */
+typedef struct kda_layer_desc {
+  int32_t num_heads;        /* H */
+  int32_t head_dim_k;       /* d_k */
+  int32_t head_dim_v;       /* d_v (must equal d_k) */
+  int32_t conv_width;       /* W: conv taps; the conv state holds W-1 inputs */
+  int32_t chunk_size;       /* prefill chunk length C */
+  int32_t io_dtype;         /* kda_dtype */
+  int32_t out_dtype;        /* kda_dtype */
+  float gate_lower_bound;   /* kda.gate_lower_bound: required, finite (NaN = absent -> error) */
+  float l2_eps;             /* q/k L2 clamp, > 0 (1e-6 in the model) */
+  float rms_eps;            /* output RMSNorm eps, >= 0 (1e-5 in the model) */
+  float scale;              /* query scale applied after the L2 norm */
+  const void* conv_w;       /* [3*H*d, W] io_dtype; tap W-1 multiplies the current token */
+  const float* A_log;       /* [H] fp32 */
+  const float* dt_bias;     /* [H*d_k] fp32 */
+  const void* norm_w;       /* [d_v] io_dtype, plain weight (not 1 + w) */
+} kda_layer_desc;
+
+/* Version of this ABI (KDA_ABI_VERSION). */
+int32_t kda_abi_version(void);
+
+/* Static description of a status code. */
+const char* kda_status_string(kda_status status);
+
+/* Thread-local description of the last error returned on this thread ("" if none). */
+const char* kda_last_error(void);
+
+/*
+ * Workspace bytes kda_prefill needs for (desc, B, T); 0 when no workspace is
+ * needed.  Returns (size_t)-1 if the arguments are invalid.
+ */
+size_t kda_prefill_workspace_size(const kda_layer_desc* desc, int32_t B, int32_t T);
+
+/*
+ * Chunked prefill of T tokens on each of B sequences (steps 1-6 above; the
+ * recurrence in chunked WY/UT form with chunk desc->chunk_size).
+ *   qkv        [B, T, 3*H*d]   raw pre-conv projections        (in)
+ *   f          [B, T, H*d]     gate pre-activation             (in)
+ *   beta       [B, T, H]       delta-rule step, in (0, 1)      (in)
+ *   g_out      [B, T, H*d]     output-gate logits              (in)
+ *   state      [B, H, d, d]    fp32 recurrent state            (in/out)
+ *   conv_state [B, 3*H*d, W-1] previous raw inputs, oldest first (in/out)
+ *   out        [B, T, H*d]     gated RMSNorm output            (out)
+ *   workspace  >= kda_prefill_workspace_size(desc, B, T) bytes, 256-byte aligned
+ * Any T >= 0 (T need not be a multiple of the chunk; T = 0 or B = 0 is a
+ * no-op).  Calls that pass state and conv_state along equal one longer call.
+ * out must not alias any input.
+ */
+kda_status kda_prefill(const kda_layer_desc* desc, int32_t B, int32_t T, const void* qkv, const void* f,
+                       const void* beta, const void* g_out, float* state, void* conv_state, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step: one new token per sequence, state and conv_state updated
+ * in place.  Tensor shapes as kda_prefill with T = 1.
+ */
+kda_status kda_decode_step(const kda_layer_desc* desc, int32_t B, const void* qkv, const void* f,
+                           const void* beta, const void* g_out, float* state, void* conv_state, void* out,
+                           void* stream);
+
+/*
+ * Verify a draft block of T_d tokens per sequence from the live state,
+ * recording the state after every token.  state and conv_state are read only.
+ *   qkv, f, beta, g_out  [B, T_d, ...] as kda_prefill
+ *   snaps  [B, T_d, H, d, d] fp32: snaps[b, t] = state after draft token t+1 (out)
+ *   out    [B, T_d, H*d] (out)
+ */
+kda_status kda_verify_block(const kda_layer_desc* desc, int32_t B, int32_t T_d, const void* qkv, const void* f,
+                            const void* beta, const void* g_out, const float* state, const void* conv_state,
+                            float* snaps, void* out, void* stream);
+
+/*
+ * Commit the accepted prefix of a verified block.  accepted_host is a HOST
+ * array of B counts m_b in 0..T_d (outside that range the call fails; no
+ * clamping).  For each b with m_b > 0:
+ *   state[b]      <- snaps[b, m_b - 1]
+ *   conv_state[b] <- the last W-1 raw inputs of (conv_state[b] || qkv_block[b, :m_b])
+ * Sequences with m_b = 0 are left untouched.  qkv_block is the verify call's qkv.
+ */
+kda_status kda_rollback(const kda_layer_desc* desc, int32_t B, int32_t T_d, const int32_t* accepted_host,
+                        const float* snaps, const void* qkv_block, float* state, void* conv_state, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

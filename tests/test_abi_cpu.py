@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI: the library loads, exports what include/kda.h
+declares, and refuses bad arguments before touching any device memory.
+
+No call here reaches a kernel: every case fails validation (or is an empty
+no-op), which happens before the first HIP call, so these run without a GPU.
+"""
+import ctypes
+import math
+
+import pytest
+
+from hybrid_linear_attention_kda_amd import abi
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails or returns before any launch
+
+
+def desc(**kw):
+    d = dict(num_heads=2, head_dim_k=16, head_dim_v=16, conv_width=4, chunk_size=16, io_dtype=0, out_dtype=0,
+             gate_lower_bound=-5.0, l2_eps=1e-6, rms_eps=1e-5, scale=0.25, conv_w=FAKE, A_log=FAKE,
+             dt_bias=FAKE, norm_w=FAKE)
+    d.update(kw)
+    return abi.KdaLayerDesc(*[d[n] for n, _ in abi.KdaLayerDesc._fields_])
+
+
+def prefill(d, B=1, T=8, ptr=FAKE, ws=0, ws_bytes=0):
+    lib = abi.load()
+    return lib.kda_prefill(ctypes.byref(d) if d is not None else None, B, T, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
+                           ws, ws_bytes, None)
+
+
+def test_library_exports_every_header_function():
+    lib = abi.load()
+    names = abi.header_functions()
+    assert set(names) == {"kda_abi_version", "kda_status_string", "kda_last_error", "kda_prefill_workspace_size",
+                          "kda_prefill", "kda_decode_step", "kda_verify_block", "kda_rollback"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.kda_abi_version() == 1
+    assert lib.kda_status_string(0) == b"ok"
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(gate_lower_bound=math.nan), abi.KDA_ERR_INVALID_ARGUMENT, b"gate_lower_bound is absent"),
+    (dict(gate_lower_bound=math.inf), abi.KDA_ERR_INVALID_ARGUMENT, b"not finite"),
+    (dict(head_dim_v=8), abi.KDA_ERR_UNSUPPORTED, b"head_dim_k"),
+    (dict(head_dim_k=48, head_dim_v=48), abi.KDA_ERR_UNSUPPORTED, b"head dim 48"),
+    (dict(conv_width=9), abi.KDA_ERR_UNSUPPORTED, b"conv_width"),
+    (dict(conv_width=0), abi.KDA_ERR_INVALID_ARGUMENT, b"conv_width"),
+    (dict(chunk_size=128), abi.KDA_ERR_UNSUPPORTED, b"chunk_size"),
+    (dict(chunk_size=0), abi.KDA_ERR_INVALID_ARGUMENT, b"chunk_size"),
+    (dict(io_dtype=7), abi.KDA_ERR_INVALID_ARGUMENT, b"io_dtype"),
+    (dict(l2_eps=0.0), abi.KDA_ERR_INVALID_ARGUMENT, b"l2_eps"),
+    (dict(rms_eps=-1.0), abi.KDA_ERR_INVALID_ARGUMENT, b"rms_eps"),
+    (dict(num_heads=0), abi.KDA_ERR_INVALID_ARGUMENT, b"num_heads"),
+    (dict(A_log=0), abi.KDA_ERR_INVALID_ARGUMENT, b"desc.A_log is null"),
+    (dict(conv_w=FAKE + 4), abi.KDA_ERR_INVALID_ARGUMENT, b"not 16-byte aligned"),
+])
+def test_prefill_rejects_bad_descriptor(kw, status, needle):
+    assert prefill(desc(**kw)) == status
+    assert needle in abi.load().kda_last_error()
+
+
+def test_null_descriptor_and_bad_sizes():
+    lib = abi.load()
+    assert prefill(None) == abi.KDA_ERR_INVALID_ARGUMENT
+    assert prefill(desc(), B=-1) == abi.KDA_ERR_INVALID_ARGUMENT
+    assert prefill(desc(), B=70000) == abi.KDA_ERR_UNSUPPORTED
+    assert prefill(desc(), ptr=0) == abi.KDA_ERR_INVALID_ARGUMENT
+    assert prefill(desc(), ptr=FAKE + 2) == abi.KDA_ERR_INVALID_ARGUMENT
+    assert b"not 16-byte aligned" in lib.kda_last_error()
+
+
+def test_empty_calls_are_no_ops():
+    # B = 0 or T = 0: nothing to do, no pointer is looked at and no kernel runs.
+    assert prefill(desc(), B=0, ptr=0) == abi.KDA_OK
+    assert prefill(desc(), T=0, ptr=0) == abi.KDA_OK
+    lib = abi.load()
+    d = desc()
+    assert lib.kda_decode_step(ctypes.byref(d), 0, 0, 0, 0, 0, 0, 0, 0, None) == abi.KDA_OK
+    assert lib.kda_verify_block(ctypes.byref(d), 3, 0, 0, 0, 0, 0, 0, 0, 0, 0, None) == abi.KDA_OK
+    acc = (ctypes.c_int32 * 2)(0, 0)  # nothing accepted: no-op
+    assert lib.kda_rollback(ctypes.byref(d), 2, 8, ctypes.cast(acc, ctypes.c_void_p), 0, 0, 0, 0, None) == abi.KDA_OK
+
+
+def test_verify_and_rollback_validation():
+    lib = abi.load()
+    d = desc()
+    P = FAKE
+    assert lib.kda_verify_block(ctypes.byref(d), 1, 256, P, P, P, P, P, P, P, P, None) == abi.KDA_ERR_UNSUPPORTED
+    assert lib.kda_verify_block(ctypes.byref(d), 1, 8, P, P, P, P, P, P, 0, P, None) == abi.KDA_ERR_INVALID_ARGUMENT
+    assert b"snaps is null" in lib.kda_last_error()
+    for bad in (-1, 9):
+        acc = (ctypes.c_int32 * 2)(3, bad)
+        st = lib.kda_rollback(ctypes.byref(d), 2, 8, ctypes.cast(acc, ctypes.c_void_p), P, P, P, P, None)
+        assert st == abi.KDA_ERR_INVALID_ARGUMENT
+        assert f"accepted[1] = {bad} outside 0..8".encode() in lib.kda_last_error()
+    assert lib.kda_rollback(ctypes.byref(d), 2, 8, None, P, P, P, P, None) == abi.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_size():
+    lib = abi.load()
+    d = desc()
+    assert lib.kda_prefill_workspace_size(ctypes.byref(d), 1, 64) == 0  # fp32 vector-ALU path needs none
+    bad = desc(gate_lower_bound=math.nan)
+    assert lib.kda_prefill_workspace_size(ctypes.byref(bad), 1, 64) == ctypes.c_size_t(-1).value
