@@ -22,104 +22,135 @@ namespace kda {
 
 template <int D>
 struct RecLayout {
-  static constexpr int NT = (D >= 64) ? 256 : (D == 32 ? 128 : 64);
+#ifndef KDA_REC_NT128
+#define KDA_REC_NT128 512
+#endif
+  static constexpr int NT = (D == 128) ? KDA_REC_NT128 : (D == 64 ? 256 : (D == 32 ? 128 : 64));
   static constexpr int CG = D / 4;     // float4 column groups of a state row
   static constexpr int RG = NT / CG;   // row groups
-  static constexpr int RPT = D / RG;   // state rows held per lane
+  static constexpr int RPT = D / RG;   // consecutive state rows held per lane
+  static constexpr int NCH = (3 * D + NT - 1) / NT;  // conv channels per lane
   static_assert(RG * CG == NT && RPT * RG == D, "layout");
 };
 
-template <int D, typename IO, typename OT>
+// MULTI: the call carries several tokens (verify); otherwise exactly one (decode).
+// WMAX: compile-time bound on the conv width, so taps and window stay in registers.
+template <int D, int WMAX, bool MULTI, typename IO, typename OT>
 __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerArgs a) {
   using L = RecLayout<D>;
   constexpr int NT = L::NT;
   constexpr int C3 = 3 * D;
+  constexpr int NCH = L::NCH;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
-  const int H = a.H, W = a.W, T = a.T;
-  const long long Cqkv = 3LL * H * D;
+  const int lane = tid & 63;
+  const int H = a.H, W = a.W, T = MULTI ? a.T : 1;
+  const int HD = H * D;
+  const int Cqkv = 3 * HD;
 
-  __shared__ float s_win[C3][kMaxConvWidth - 1];
   __shared__ float s_q[D], s_k[D], s_v[D], s_alpha[D], s_u[D], s_o[D];
   __shared__ float s_part[2][L::RG][D];
-  __shared__ float s_red[4];
 
-  const IO* qkv = static_cast<const IO*>(a.qkv);
-  const IO* fin = static_cast<const IO*>(a.f);
-  const IO* bin = static_cast<const IO*>(a.beta);
-  const IO* gin = static_cast<const IO*>(a.g_out);
-  const IO* cw = static_cast<const IO*>(a.conv_w);
-  const IO* nw = static_cast<const IO*>(a.norm_w);
-  const IO* cin = static_cast<const IO*>(a.conv_in);
-  OT* out = static_cast<OT*>(a.out);
-
-  // 1. Issue the state loads first so the prologue below overlaps them.
-  const int cg = tid % L::CG;
-  const int rg = tid / L::CG;
+  // Uniform (per-workgroup) base pointers; lanes add 32-bit offsets.
   const long long bh = (long long)b * H + h;
-  float4 S[L::RPT];
-  {
-    const float* src = a.state_in + bh * D * D + 4 * cg;
-#pragma unroll
-    for (int r = 0; r < L::RPT; ++r)
-      S[r] = *reinterpret_cast<const float4*>(src + (long long)(rg + r * L::RG) * D);
-  }
+  const IO* __restrict__ xq = static_cast<const IO*>(a.qkv) + (long long)b * T * Cqkv + h * D;
+  const IO* __restrict__ xf = static_cast<const IO*>(a.f) + (long long)b * T * HD + h * D;
+  const IO* __restrict__ xg = static_cast<const IO*>(a.g_out) + (long long)b * T * HD + h * D;
+  const IO* __restrict__ xb = static_cast<const IO*>(a.beta) + (long long)b * T * H + h;
+  OT* __restrict__ out = static_cast<OT*>(a.out) + (long long)b * T * HD + h * D;
 
-  // 2. Conv window: the W-1 raw inputs before the first token, oldest first.
-  for (int c = tid; c < C3; c += NT) {
-    const long long gc = (long long)(c / D) * H * D + (long long)h * D + (c % D);
-    for (int w = 0; w < W - 1; ++w) s_win[c][w] = to_f32(cin[(b * Cqkv + gc) * (W - 1) + w]);
+  // 1. Small per-token and per-channel inputs first.  Loads retire in order, so issuing them
+  //    ahead of the state lets the prologue below run while the state is still in flight.
+  //    Conv taps are held right-aligned (tapr[0] multiplies the current token) and the window
+  //    newest-first (win[j] = input j tokens back), so no register is indexed at run time.
+  int choff[NCH];
+  float tapr[NCH][WMAX], win[NCH][WMAX], xin[NCH];
+#pragma unroll
+  for (int n = 0; n < NCH; ++n) {
+    const int c = tid + n * NT;
+    const int cc = c < C3 ? c : 0;
+    choff[n] = (cc / D) * HD + (cc % D);  // offset of the channel inside a token row (head h base)
+    const IO* cwp = static_cast<const IO*>(a.conv_w) + ((long long)h * D + (long long)(cc / D) * HD + (cc % D)) * W;
+    const IO* csp = static_cast<const IO*>(a.conv_in) +
+                    ((long long)b * Cqkv + (long long)h * D + (long long)(cc / D) * HD + (cc % D)) * (W - 1);
+#pragma unroll
+    for (int j = 0; j < WMAX; ++j) {
+      tapr[n][j] = (j < W) ? to_f32(cwp[W - 1 - j]) : 0.f;
+      win[n][j] = (j >= 1 && j < W) ? to_f32(csp[W - 1 - j]) : 0.f;
+    }
+    xin[n] = to_f32(xq[choff[n]]);
   }
+  const int ci = tid < D ? tid : 0;
+  float fin = to_f32(xf[ci]);
+  float gin = to_f32(xg[ci]);
+  float bin = to_f32(xb[0]);
+  const float dtb = a.dt_bias[h * D + ci];
+  const float nwj = to_f32(static_cast<const IO*>(a.norm_w)[ci]);
   const float Ah = __expf(a.A_log[h]);
 
+  // 2. The state: read once (streaming), kept in registers for the whole call.
+  const int cg = tid % L::CG;
+  const int rg = tid / L::CG;
+  const int soff = rg * L::RPT * D + 4 * cg;
+  float4 S[L::RPT];
+  {
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.state_in + bh * D * D + soff);
+#pragma unroll
+    for (int r = 0; r < L::RPT; ++r) {
+      const f32x4 v = __builtin_nontemporal_load(src + r * (D / 4));
+      S[r] = make_float4(v.x, v.y, v.z, v.w);
+    }
+  }
+
   for (int t = 0; t < T; ++t) {
-    const long long tok = (long long)b * T + t;
-    __syncthreads();  // window ready; previous token's shared values consumed
-    // conv + SiLU over this head's q|k|v channels; advance the window
-    for (int c = tid; c < C3; c += NT) {
-      const int part = c / D, i = c % D;
-      const long long gc = (long long)part * H * D + (long long)h * D + i;
-      const float x = to_f32(qkv[tok * Cqkv + gc]);
-      float y = to_f32(cw[gc * W + (W - 1)]) * x;
-      for (int w = 0; w < W - 1; ++w) y += to_f32(cw[gc * W + w]) * s_win[c][w];
-      for (int w = 0; w + 1 < W - 1; ++w) s_win[c][w] = s_win[c][w + 1];
-      if (W > 1) s_win[c][W - 2] = x;
-      const float z = y / (1.0f + expf(-y));
-      (part == 0 ? s_q : part == 1 ? s_k : s_v)[i] = z;
+    // conv + SiLU over this lane's channels; advance the window
+#pragma unroll
+    for (int n = 0; n < NCH; ++n) {
+      const int c = tid + n * NT;
+      float y = tapr[n][0] * xin[n];
+#pragma unroll
+      for (int j = 1; j < WMAX; ++j) y += tapr[n][j] * win[n][j];
+#pragma unroll
+      for (int j = WMAX - 1; j >= 2; --j) win[n][j] = win[n][j - 1];
+      win[n][1 % WMAX] = (WMAX > 1) ? xin[n] : win[n][0];
+      if (c < C3) {
+        const float z = y / (1.0f + expf(-y));
+        const int part = c / D, i = c % D;
+        (part == 0 ? s_q : part == 1 ? s_k : s_v)[i] = z;
+      }
     }
     // bounded-sigmoid decay gate (log-decay in (lb, 0)), per key channel
-    for (int i = tid; i < D; i += NT) {
-      const float fv = to_f32(fin[tok * H * D + (long long)h * D + i]) + a.dt_bias[(long long)h * D + i];
-      s_alpha[i] = expf(a.lb / (1.0f + expf(-Ah * fv)));
+    if (tid < D) s_alpha[tid] = expf(a.lb / (1.0f + expf(-Ah * (fin + dtb))));
+    const float bt = bin, gcur = gin;
+    if (MULTI && t + 1 < T) {  // next token's inputs: issued before this token's stores
+      const int tn = t + 1;
+#pragma unroll
+      for (int n = 0; n < NCH; ++n) xin[n] = to_f32(xq[(long long)tn * Cqkv + choff[n]]);
+      fin = to_f32(xf[(long long)tn * HD + ci]);
+      gin = to_f32(xg[(long long)tn * HD + ci]);
+      bin = to_f32(xb[(long long)tn * H]);
     }
     __syncthreads();
-    if (tid < 64) {
-      float qq = 0.f, kk = 0.f, qk = 0.f;
-      for (int i = tid; i < D; i += 64) {
-        qq += s_q[i] * s_q[i];
-        kk += s_k[i] * s_k[i];
-        qk += s_q[i] * s_k[i];
-      }
-      qq = wave_sum(qq);
-      kk = wave_sum(kk);
-      qk = wave_sum(qk);
-      if (tid == 0) {
-        const float rq = a.scale / fmaxf(sqrtf(qq), a.l2_eps);
-        const float rk = 1.0f / fmaxf(sqrtf(kk), a.l2_eps);
-        s_red[0] = rq;
-        s_red[1] = rk;
-        s_red[2] = qk * rq * rk;
-      }
+    // q/k norms and q.k, computed redundantly by every wave (no extra barrier)
+    float qq = 0.f, kk = 0.f, qk = 0.f;
+    for (int i = lane; i < D; i += 64) {
+      qq += s_q[i] * s_q[i];
+      kk += s_k[i] * s_k[i];
+      qk += s_q[i] * s_k[i];
     }
-    __syncthreads();
-    const float rq = s_red[0], rk = s_red[1], qkn = s_red[2];
+    qq = wave_sum(qq);
+    kk = wave_sum(kk);
+    qk = wave_sum(qk);
+    const float rq = a.scale / fmaxf(sqrtf(qq), a.l2_eps);
+    const float rk = 1.0f / fmaxf(sqrtf(kk), a.l2_eps);
+    const float qkn = qk * rq * rk;
 
     // 3. One sweep over this lane's rows: decay, then partial S'^T k and S'^T q.
     float4 kS = make_float4(0.f, 0.f, 0.f, 0.f), qS = kS;
 #pragma unroll
     for (int r = 0; r < L::RPT; ++r) {
-      const int i = rg + r * L::RG;
+      const int i = rg * L::RPT + r;
       const float al = s_alpha[i], ki = s_k[i] * rk, qi = s_q[i] * rq;
       S[r].x *= al; S[r].y *= al; S[r].z *= al; S[r].w *= al;
       kS.x += ki * S[r].x; kS.y += ki * S[r].y; kS.z += ki * S[r].z; kS.w += ki * S[r].w;
@@ -128,64 +159,56 @@ __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerAr
     *reinterpret_cast<float4*>(&s_part[0][rg][4 * cg]) = kS;
     *reinterpret_cast<float4*>(&s_part[1][rg][4 * cg]) = qS;
     __syncthreads();
-    const float bt = to_f32(bin[tok * H + h]);
-    for (int j = tid; j < D; j += NT) {
+    if (tid < D) {
       float ks = 0.f, qs = 0.f;
 #pragma unroll
       for (int g = 0; g < L::RG; ++g) {
-        ks += s_part[0][g][j];
-        qs += s_part[1][g][j];
+        ks += s_part[0][g][tid];
+        qs += s_part[1][g][tid];
       }
-      const float u = bt * (s_v[j] - ks);
-      s_u[j] = u;
-      s_o[j] = qs + qkn * u;
+      const float u = bt * (s_v[tid] - ks);
+      s_u[tid] = u;
+      s_o[tid] = qs + qkn * u;
     }
     __syncthreads();
 
-    // 4. Rank-1 update in registers; verify streams a snapshot per token.
+    // 4. Rank-1 update in registers; verify streams a snapshot per token, decode the final state.
     {
       const float4 u4 = *reinterpret_cast<const float4*>(&s_u[4 * cg]);
 #pragma unroll
       for (int r = 0; r < L::RPT; ++r) {
-        const float ki = s_k[rg + r * L::RG] * rk;
+        const float ki = s_k[rg * L::RPT + r] * rk;
         S[r].x += ki * u4.x; S[r].y += ki * u4.y; S[r].z += ki * u4.z; S[r].w += ki * u4.w;
       }
-      if (a.snapshots) {
-        float* dst = a.state_out + (tok * H + h) * D * D + 4 * cg;
+      float* dst = a.snapshots ? a.state_out + (((long long)b * T + t) * H + h) * D * D
+                               : a.state_out + bh * D * D;
+      if (a.snapshots || t + 1 == T) {
 #pragma unroll
-        for (int r = 0; r < L::RPT; ++r)
-          store_nt(dst + (long long)(rg + r * L::RG) * D, S[r]);
+        for (int r = 0; r < L::RPT; ++r) store_nt(dst + soff + r * D, S[r]);
       }
     }
 
-    // 5. Gated RMSNorm over d_v.
-    if (tid < 64) {
-      float oo = 0.f;
-      for (int j = tid; j < D; j += 64) oo += s_o[j] * s_o[j];
-      oo = wave_sum(oo);
-      if (tid == 0) s_red[3] = rsqrtf(oo / (float)D + a.rms_eps);
+    // 5. Gated RMSNorm over d_v (every wave reduces; lanes < D write).
+    float oo = 0.f;
+    for (int j = lane; j < D; j += 64) oo += s_o[j] * s_o[j];
+    oo = wave_sum(oo);
+    if (tid < D) {
+      const float rr = rsqrtf(oo / (float)D + a.rms_eps);
+      store_as(&out[(long long)t * HD + tid], s_o[tid] * rr * nwj / (1.0f + expf(-gcur)));
     }
-    __syncthreads();
-    const float rr = s_red[3];
-    for (int j = tid; j < D; j += NT) {
-      const float gv = to_f32(gin[tok * H * D + (long long)h * D + j]);
-      const float y = s_o[j] * rr * to_f32(nw[j]) / (1.0f + expf(-gv));
-      store_as(&out[tok * H * D + (long long)h * D + j], y);
-    }
+    if (MULTI && t + 1 < T) __syncthreads();  // s_q/s_k/s_o are rewritten by the next token
   }
 
-  if (!a.snapshots) {
-    float* dst = a.state_out + bh * D * D + 4 * cg;
-#pragma unroll
-    for (int r = 0; r < L::RPT; ++r)
-      *reinterpret_cast<float4*>(dst + (long long)(rg + r * L::RG) * D) = S[r];
-  }
   if (a.conv_out != nullptr) {
-    IO* cout_ = static_cast<IO*>(a.conv_out);
-    __syncthreads();
-    for (int c = tid; c < C3; c += NT) {
-      const long long gc = (long long)(c / D) * H * D + (long long)h * D + (c % D);
-      for (int w = 0; w < W - 1; ++w) store_as(&cout_[(b * Cqkv + gc) * (W - 1) + w], s_win[c][w]);
+#pragma unroll
+    for (int n = 0; n < NCH; ++n) {
+      const int c = tid + n * NT;
+      if (c < C3) {
+        IO* csp = static_cast<IO*>(a.conv_out) + ((long long)b * Cqkv + (long long)h * D + (long long)(c / D) * HD + (c % D)) * (W - 1);
+#pragma unroll
+        for (int j = 1; j < WMAX; ++j)
+          if (j < W) store_as(&csp[W - 1 - j], win[n][j]);
+      }
     }
   }
 }
@@ -222,21 +245,28 @@ __global__ __launch_bounds__(256) void kda_rollback_kernel(RollbackArgs a) {
   }
 }
 
-template <int D>
-static hipError_t launch_rec_d(const LayerArgs& a, int io, int ot, hipStream_t s) {
+template <int D, int WMAX, bool MULTI>
+static hipError_t launch_rec_t(const LayerArgs& a, int io, int ot, hipStream_t s) {
   dim3 grid(a.H, a.B), block(RecLayout<D>::NT);
   if (io == kBF16) {
     if (ot == kBF16)
-      kda_recurrent_kernel<D, bf16_t, bf16_t><<<grid, block, 0, s>>>(a);
+      kda_recurrent_kernel<D, WMAX, MULTI, bf16_t, bf16_t><<<grid, block, 0, s>>>(a);
     else
-      kda_recurrent_kernel<D, bf16_t, float><<<grid, block, 0, s>>>(a);
+      kda_recurrent_kernel<D, WMAX, MULTI, bf16_t, float><<<grid, block, 0, s>>>(a);
   } else {
     if (ot == kBF16)
-      kda_recurrent_kernel<D, float, bf16_t><<<grid, block, 0, s>>>(a);
+      kda_recurrent_kernel<D, WMAX, MULTI, float, bf16_t><<<grid, block, 0, s>>>(a);
     else
-      kda_recurrent_kernel<D, float, float><<<grid, block, 0, s>>>(a);
+      kda_recurrent_kernel<D, WMAX, MULTI, float, float><<<grid, block, 0, s>>>(a);
   }
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_rec_d(const LayerArgs& a, int io, int ot, hipStream_t s) {
+  const bool multi = a.T > 1;
+  if (a.W <= 4) return multi ? launch_rec_t<D, 4, true>(a, io, ot, s) : launch_rec_t<D, 4, false>(a, io, ot, s);
+  return multi ? launch_rec_t<D, kMaxConvWidth, true>(a, io, ot, s) : launch_rec_t<D, kMaxConvWidth, false>(a, io, ot, s);
 }
 
 hipError_t launch_recurrent(const LayerArgs& a, int io, int ot, hipStream_t s) {
