@@ -106,6 +106,11 @@ kda::LayerArgs make_args(const kda_layer_desc* d, int B, int T) {
   return a;
 }
 
+// bf16 io at the model's head size runs the matrix-core prefill; everything else the fp32 form.
+bool mfma_path(const kda_layer_desc* d) {
+  return kda::prefill_mfma_supported(d->head_dim_k, d->chunk_size, d->io_dtype, d->conv_width, d->gate_lower_bound);
+}
+
 kda_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -139,7 +144,7 @@ const char* kda_last_error(void) { return g_last_error; }
 
 size_t kda_prefill_workspace_size(const kda_layer_desc* desc, int32_t B, int32_t T) {
   if (check_desc(desc) != KDA_OK || check_batch(B, T) != KDA_OK || check_chunk(desc) != KDA_OK) return (size_t)-1;
-  if (!kda::prefill_mfma_supported(desc->head_dim_k, desc->chunk_size, desc->io_dtype)) return 0;
+  if (!mfma_path(desc)) return 0;
   return kda::prefill_mfma_workspace(B, T, desc->num_heads, desc->head_dim_k, desc->chunk_size);
 }
 
@@ -166,7 +171,7 @@ kda_status kda_prefill(const kda_layer_desc* desc, int32_t B, int32_t T, const v
   a.out = out;
   a.snapshots = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (kda::prefill_mfma_supported(a.D, desc->chunk_size, desc->io_dtype)) {
+  if (mfma_path(desc)) {
     const size_t need = kda::prefill_mfma_workspace(B, T, a.H, a.D, desc->chunk_size);
     if (need > 0) {
       if (workspace == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is null (%zu bytes needed)", need);

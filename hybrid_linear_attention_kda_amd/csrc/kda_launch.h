@@ -48,8 +48,8 @@ hipError_t launch_rollback(const RollbackArgs& a, int io, hipStream_t s);
 // Chunked prefill, fp32 VALU form (any supported head size; internal chunk <= 4096 / D).
 hipError_t launch_prefill_generic(const LayerArgs& a, int chunk, int io, int ot, hipStream_t s);
 
-// Chunked prefill on bf16 MFMA (D = 128, chunk 64, bf16 io).
-bool prefill_mfma_supported(int D, int chunk, int io);
+// Chunked prefill on bf16 MFMA (D = 128, chunk 64, bf16 io, conv width <= 4, -5.5 <= lb <= 0).
+bool prefill_mfma_supported(int D, int chunk, int io, int W, float lb);
 size_t prefill_mfma_workspace(int B, int T, int H, int D, int chunk);
 hipError_t launch_prefill_mfma(const LayerArgs& a, void* ws, size_t ws_bytes, int ot, hipStream_t s);
 
