@@ -11,17 +11,24 @@
 // max(||x||, eps), bounded-sigmoid per-channel decay on the key axis, gated
 // output RMSNorm with a plain weight).
 //
-// Work split.  The columns of S are independent (decay acts on rows, u is per
-// column), so one workgroup owns (sequence, head, 16-column block of d_v):
-// grid = 8 column blocks x H heads x B, 512 lanes, ~150 KB of LDS.  Each
-// workgroup walks its head's chunks in order, recomputes the d_v-independent
-// chunk quantities (conv, norms, gate, A_kk, T, W, A_qk) and carries its
-// 128 x 16 fp32 state block in MFMA accumulators.  blockIdx.x = vb * H + h,
-// so with H a multiple of 8 the eight workgroups of a head land on the same
-// XCD and share its L2 for the chunk inputs.
+// Two phases.
+//  A (chunk-parallel, one workgroup per (sequence, head, chunk)): conv + SiLU,
+//    L2 norms, gate and its cumulative sum, A_kk, T, A_qk and W.  Everything
+//    that does not depend on the state or on d_v is computed once per chunk
+//    and written to the workspace as matrix-core operand tiles: Q~ = Q e^Gam
+//    and K~ = K e^(Gam_C - Gam) (transposed) and A_qk and T as split bf16
+//    (hi + lo), W as bf16, e^Gam_C as fp32.
+//  B (sequential over chunks, one workgroup per (sequence, head, 16-column
+//    block of d_v)): conv + SiLU of its own v columns, then per chunk
+//      Ut = T (beta V),  U = Ut - W S,  O = Q~ S + A_qk U,
+//      S <- e^Gam_C S + K~^T U,
+//    with the 128 x 16 state block in MFMA accumulators and the operands of
+//    chunk c+1 loaded into registers while chunk c is computed.  blockIdx.x =
+//    vb * H + h, so with H a multiple of 8 the eight workgroups of a head run on
+//    one XCD and share its L2 for the operand tiles.
 //
-// Per-channel decay inside MFMA tiles.  The chunk is cut into four 16-token
-// sub-chunks anchored at their first token n(I).  Operands carry
+// Per-channel decay inside MFMA tiles (phase A).  The chunk is cut into four
+// 16-token sub-chunks anchored at their first token n(I).  Operands carry
 // e^(Gam_i - Gam_n(I)) (<= 1) on rows and e^(Gam_n(J) - Gam_j) (<= e^(15|lb|))
 // on columns, and block (I, J) of A multiplies the row operand by the
 // per-channel factor e^(Gam_n(I) - Gam_n(J)) (<= 1).  With the bounded gate
@@ -33,8 +40,8 @@
 // in plain bf16 and W S splits only S.  T is formed in fp32.
 //
 // The output RMSNorm needs all 128 columns of o, which live in eight
-// workgroups, so o (fp32) goes to the workspace and a second, bandwidth-bound
-// kernel applies the norm, weight and gate; it also writes the new conv state.
+// workgroups, so o (fp32) goes to the workspace and a third, bandwidth-bound
+// kernel applies the norm, weight and gate; a fourth writes the new conv state.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -56,16 +63,14 @@ constexpr int PS = 132;      // fp32 pitch of the transposed state block [16][12
 constexpr int PR = 280;      // bf16 pitch of the raw staging rows: q 128 | k 128 | v 16 | pad
 constexpr int RROWS = C + HALO;
 
-// LDS layout (bytes)
+// Phase A LDS layout (bytes)
 constexpr int OFF_Q = 0;                              // q^ -> QR = q e^(Gam - Gam_n)
 constexpr int OFF_KB = OFF_Q + C * PQ * 4;            // KR (bf16) -> W (bf16)
 constexpr int OFF_G = OFF_KB + C * PKB * 2;           // k^ -> KC = k e^(Gam_n - Gam)
 constexpr int OFF_STG = OFF_G + C * PQ * 4;           // raw staging | Gam | A_kk + T | A_qk
 constexpr int STG_BYTES = RROWS * PR * 2;             // 37520 >= 2 * C * PA * 4 and >= C * PQ * 4
-constexpr int OFF_VT = OFF_STG + STG_BYTES;           // beta v, transposed [16][64]
-constexpr int OFF_UT = OFF_VT + NV * PT * 4;          // U transposed [16][64]; scratch while forming T
-constexpr int OFF_ST = OFF_UT + NV * PT * 4;          // state block transposed [16][128]
-constexpr int OFF_GN = OFF_ST + NV * PS * 4;          // Gam at the four anchors + Gam_C [5][128]
+constexpr int OFF_TMP = OFF_STG + STG_BYTES;          // scratch while forming T [1024]
+constexpr int OFF_GN = OFF_TMP + 1024 * 4;            // Gam at the four anchors + Gam_C [5][128]
 constexpr int OFF_EN = OFF_GN + 5 * D * 4;            // e^(Gam_n(I)) [4][128]
 constexpr int OFF_E = OFF_EN + 4 * D * 4;             // e^(Gam_n(I) - Gam_n(J)), I > J [6][128]
 constexpr int OFF_FAC = OFF_E + 6 * D * 4;            // e^(Gam_C - Gam_n(J)) [4][128]
@@ -73,9 +78,37 @@ constexpr int OFF_GC = OFF_FAC + 4 * D * 4;           // e^(Gam_C) [128]
 constexpr int OFF_BETA = OFF_GC + D * 4;              // [64]
 constexpr int OFF_NRM = OFF_BETA + C * 4;             // q / k normalisers [2][64]
 constexpr int OFF_SEG = OFF_NRM + 2 * C * 4;          // cumulative-sum segment totals [4][128]
-constexpr int LDS_BYTES = OFF_SEG + 4 * D * 4;
+constexpr int LDS_A = OFF_SEG + 4 * D * 4;
 static_assert(STG_BYTES >= 2 * C * PA * 4 && STG_BYTES >= C * PQ * 4, "staging aliases");
-static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+static_assert(LDS_A <= 160 * 1024, "LDS budget");
+
+// Workspace tile block per (sequence, head, chunk), written by phase A and read by phase B.
+constexpr int W_QHI = 0;                   // Q~ hi  [64][128] bf16
+constexpr int W_QLO = W_QHI + C * D * 2;   // Q~ lo
+constexpr int W_KTHI = W_QLO + C * D * 2;  // K~^T hi [128][64] bf16
+constexpr int W_KTLO = W_KTHI + D * C * 2; // K~^T lo
+constexpr int W_W = W_KTLO + D * C * 2;    // W [64][128] bf16
+constexpr int W_AHI = W_W + C * D * 2;     // A_qk hi [64][64] bf16 (upper triangle zero)
+constexpr int W_ALO = W_AHI + C * C * 2;
+constexpr int W_THI = W_ALO + C * C * 2;   // T hi [64][64] bf16 (upper triangle zero)
+constexpr int W_TLO = W_THI + C * C * 2;
+constexpr int W_GC = W_TLO + C * C * 2;    // e^Gam_C [128] fp32
+constexpr int CH_BYTES = W_GC + D * 4;     // 115200
+static_assert(CH_BYTES % 256 == 0, "tile blocks stay 256-byte aligned");
+
+// Phase B LDS layout (bytes)
+constexpr int PRV = 24;                    // bf16 pitch of the staged raw v rows (16 used)
+constexpr int PVT = 72;                    // bf16 pitch of [16][64] token-major operands
+constexpr int PST = 136;                   // bf16 pitch of the [16][128] state operand
+constexpr int B_RAWV = 0;
+constexpr int B_BETA = B_RAWV + RROWS * PRV * 2;
+constexpr int B_VHI = B_BETA + C * 4;
+constexpr int B_VLO = B_VHI + NV * PVT * 2;
+constexpr int B_UHI = B_VLO + NV * PVT * 2;
+constexpr int B_ULO = B_UHI + NV * PVT * 2;
+constexpr int B_SHI = B_ULO + NV * PVT * 2;
+constexpr int B_SLO = B_SHI + NV * PST * 2;
+constexpr int LDS_B = B_SLO + NV * PST * 2;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -123,8 +156,18 @@ __device__ __forceinline__ void block_ij(int bi, int& I, int& J) {
 }
 __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
 
-template <typename OT>
-__global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(LayerArgs a, float* __restrict__ ows) {
+__device__ __forceinline__ float silu_fast(float y) { return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y)); }
+
+__device__ __forceinline__ void store_split8(__bf16* hi, __bf16* lo, const float (&x)[8]) {
+  const Split8 sp = split(x);
+  *reinterpret_cast<bf16x8*>(hi) = sp.hi;
+  *reinterpret_cast<bf16x8*>(lo) = sp.lo;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Phase A: one workgroup per (chunk, head, sequence).
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigned char* __restrict__ ws) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* sQ = reinterpret_cast<float*>(smem + OFF_Q);
   __bf16* sKb = reinterpret_cast<__bf16*>(smem + OFF_KB);
@@ -134,9 +177,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(LayerArgs a, float
   float* sAkk = reinterpret_cast<float*>(smem + OFF_STG);
   float* sT = reinterpret_cast<float*>(smem + OFF_STG + C * PA * 4);
   float* sAqk = sAkk;  // A_kk is dead once T is formed
-  float* sVT = reinterpret_cast<float*>(smem + OFF_VT);
-  float* sUT = reinterpret_cast<float*>(smem + OFF_UT);
-  float* sST = reinterpret_cast<float*>(smem + OFF_ST);
+  float* sTmp = reinterpret_cast<float*>(smem + OFF_TMP);
   float* sGn = reinterpret_cast<float*>(smem + OFF_GN);
   float* sEn = reinterpret_cast<float*>(smem + OFF_EN);
   float* sE = reinterpret_cast<float*>(smem + OFF_E);
@@ -147,9 +188,10 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(LayerArgs a, float
   float* sSeg = reinterpret_cast<float*>(smem + OFF_SEG);
 
   const int H = a.H, T = a.T, W = a.W;
-  const int h = blockIdx.x % H;
-  const int vb = blockIdx.x / H;
-  const int b = blockIdx.y;
+  const int ci = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int NC = (T + C - 1) / C;
+  const int c0 = ci * C;
+  const int L = min(C, T - c0);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;  // MFMA row/column index and k-group
@@ -160,20 +202,27 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(LayerArgs a, float
   const bf16_t* __restrict__ bin = static_cast<const bf16_t*>(a.beta) + (long long)b * T * H + h;
   const bf16_t* __restrict__ cw = static_cast<const bf16_t*>(a.conv_w);
   const bf16_t* __restrict__ cin = static_cast<const bf16_t*>(a.conv_in) + (long long)b * Cq * (W - 1);
+  unsigned char* __restrict__ blk = ws + (((long long)b * H + h) * NC + ci) * (long long)CH_BYTES;
 
-  // State block: wave w owns channel rows 16w..16w+15; lane holds rows 16w+4lg+r, column l16.
-  f32x4 Sacc;
-  {
-    const float* sp = a.state_in + ((long long)b * H + h) * D * D + vb * NV + l16;
+  // ---- P1: stage raw q | k rows for tokens c0-3 .. c0+63 (bf16) ----
+  for (int idx = tid; idx < RROWS * 32; idx += NT) {
+    const int r = idx >> 5, sg = idx & 31;
+    const int tt = c0 - HALO + r;
+    const long long ch = sg < 16 ? (long long)h * D + sg * 8 : (long long)HD + h * D + (sg - 16) * 8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (tt >= 0 && tt < T) {
+      v = *reinterpret_cast<const uint4*>(qkv + (long long)tt * Cq + ch);
+    } else if (tt < 0 && (W - 1) + tt >= 0) {
+      uint16_t e8[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Sacc[r] = sp[(16 * wave + 4 * lg + r) * D];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sST[l16 * PS + 16 * wave + 4 * lg + r] = Sacc[r];
+      for (int e = 0; e < 8; ++e) e8[e] = cin[(ch + e) * (W - 1) + (W - 1) + tt];
+      v = make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16, e8[4] | (uint32_t)e8[5] << 16,
+                     e8[6] | (uint32_t)e8[7] << 16);
+    }
+    *reinterpret_cast<uint4*>(sRaw + r * PR + sg * 8) = v;
   }
-  const float Ah = __expf(a.A_log[h]);
-  const float lb = a.lb;
-
-  // conv taps of this lane's q/k channel (P2) and v column, zero-padded on the left to 4 taps
+  if (tid < C) sBeta[tid] = tid < L ? to_f32(bin[(long long)(c0 + tid) * H]) : 0.f;
+  // conv taps of this lane's q/k channel, zero-padded on the left to 4 taps
   const int cq = tid & 255;
   const long long gqk = cq < D ? (long long)h * D + cq : (long long)HD + h * D + (cq - D);
   float tq[4];
@@ -182,37 +231,350 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(LayerArgs a, float
     const int w = j - (4 - W);
     tq[j] = w >= 0 ? to_f32(cw[gqk * W + w]) : 0.f;
   }
-  const int vj = tid & 15;
-  const long long gv = 2LL * HD + (long long)h * D + vb * NV + vj;
-  float tv[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int w = j - (4 - W);
-    tv[j] = w >= 0 ? to_f32(cw[gv * W + w]) : 0.f;
+  __syncthreads();
+
+  // ---- P2: causal conv + SiLU over q|k: lane -> channel cq, 32 tokens ----
+  {
+    const int tb = 32 * (tid >> 8);
+    const __bf16* col = sRaw + cq;
+    float r0 = (float)col[(tb + 0) * PR], r1 = (float)col[(tb + 1) * PR], r2 = (float)col[(tb + 2) * PR];
+    float* dst = cq < D ? sQ + cq : sG + (cq - D);
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) {
+      const int t = tb + i;
+      const float r3 = (float)col[(t + 3) * PR];
+      const float y = tq[0] * r0 + tq[1] * r1 + tq[2] * r2 + tq[3] * r3;
+      dst[t * PQ] = t < L ? silu_fast(y) : 0.f;
+      r0 = r1; r1 = r2; r2 = r3;
+    }
   }
-  const float dtb = a.dt_bias[h * D + (tid & 127)];
+  __syncthreads();
 
-  for (int c0 = 0; c0 < T; c0 += C) {
-    const int L = min(C, T - c0);
-    __syncthreads();  // the previous chunk is done with every aliased buffer
-
-    // ---- P1: stage raw q | k | v-block rows for tokens c0-3 .. c0+63 (bf16) ----
-    for (int idx = tid; idx < RROWS * 34; idx += NT) {
-      const int r = idx / 34, sg = idx % 34;
-      const int tt = c0 - HALO + r;
-      long long ch;
-      int col;
-      if (sg < 16) {
-        ch = (long long)h * D + sg * 8;
-        col = sg * 8;
-      } else if (sg < 32) {
-        ch = (long long)HD + h * D + (sg - 16) * 8;
-        col = D + (sg - 16) * 8;
-      } else {
-        ch = 2LL * HD + h * D + vb * NV + (sg - 32) * 8;
-        col = 2 * D + (sg - 32) * 8;
+  // ---- P3: bounded-sigmoid gate and its cumulative sum (lane -> channel, 16-token segment) ----
+  {
+    const int i = tid & 127, seg = tid >> 7;
+    const float Ah = __expf(a.A_log[h]);
+    const float dtb = a.dt_bias[h * D + i];
+    float gl[16];
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int t = 16 * seg + k;
+      float g = 0.f;
+      if (t < L) {
+        const float fv = to_f32(fin[(long long)(c0 + t) * HD + i]) + dtb;
+        g = a.lb * __builtin_amdgcn_rcpf(1.0f + __expf(-Ah * fv));
       }
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      acc += g;
+      gl[k] = acc;
+    }
+    sSeg[seg * D + i] = acc;
+    // ---- P4 (same phase): q / k L2 normalisers, one wave per 8 tokens ----
+    for (int t = wave * 8; t < wave * 8 + 8; ++t) {
+      const float q0 = sQ[t * PQ + lane], q1 = sQ[t * PQ + lane + 64];
+      const float k0 = sG[t * PQ + lane], k1 = sG[t * PQ + lane + 64];
+      const float qq = wave_sum(q0 * q0 + q1 * q1);
+      const float kk = wave_sum(k0 * k0 + k1 * k1);
+      if (lane == 0) {
+        sNrm[t] = a.scale / fmaxf(sqrtf(qq), a.l2_eps);
+        sNrm[C + t] = 1.0f / fmaxf(sqrtf(kk), a.l2_eps);
+      }
+    }
+    __syncthreads();
+    float off = 0.f;
+    for (int s = 0; s < seg; ++s) off += sSeg[s * D + i];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) sGam[(16 * seg + k) * PQ + i] = gl[k] + off;
+    sGn[seg * D + i] = gl[0] + off;
+    if (seg == 3) sGn[4 * D + i] = gl[15] + off;
+  }
+  __syncthreads();
+
+  // ---- P5: anchored operands QR, KR (bf16), KC and the per-channel factor tables ----
+  for (int idx = tid; idx < C * D; idx += NT) {
+    const int t = idx >> 7, c = idx & 127;
+    const float G = sGam[t * PQ + c];
+    const float Gn = sGn[(t >> 4) * D + c];
+    const float e1 = __expf(G - Gn);  // <= 1
+    const float e2 = __expf(Gn - G);  // in [1, e^(15|lb|)]
+    const float q = sQ[t * PQ + c] * sNrm[t];
+    const float k = sG[t * PQ + c] * sNrm[C + t];
+    sQ[t * PQ + c] = q * e1;
+    sKb[t * PKB + c] = (__bf16)(k * e1);
+    sG[t * PQ + c] = k * e2;
+  }
+  if (tid < D) {
+    const int c = tid;
+    const float GC = sGn[4 * D + c];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      const float GI = sGn[I * D + c];
+      sEn[I * D + c] = __expf(GI);
+      sFac[I * D + c] = __expf(GC - GI);
+#pragma unroll
+      for (int J = 0; J < I; ++J) sE[pair_index(I, J) * D + c] = __expf(GI - sGn[J * D + c]);
+    }
+    sGC[c] = __expf(GC);
+  }
+  __syncthreads();
+
+  // ---- P6a: A_kk = beta_i * KR_I E_IJ . KC_J^T (plain bf16), strictly lower ----
+  for (int bi = wave; bi < 10; bi += 8) {
+    int I, J;
+    block_ij(bi, I, J);
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int c = 32 * s + 8 * lg;
+      bf16x8 av = *reinterpret_cast<const bf16x8*>(sKb + (16 * I + l16) * PKB + c);
+      if (I > J) {
+        const float* ef = sE + pair_index(I, J) * D + c;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av[e] = (__bf16)((float)av[e] * ef[e]);
+      }
+      float kc[8];
+      ld8(sG + (16 * J + l16) * PQ + c, kc);
+      acc = mfma(av, round8(kc), acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * I + 4 * lg + r, j = 16 * J + l16;
+      sAkk[i * PA + j] = j < i ? sBeta[i] * acc[r] : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- P7: T = (I + A_kk)^-1 in fp32: diagonal 16x16 blocks by forward substitution ----
+  if (wave == 0) {
+    const int I = lg, cc = l16;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float v = (i == cc) ? 1.f : 0.f;
+#pragma unroll
+      for (int j = 0; j < i; ++j) v -= sAkk[(16 * I + i) * PA + 16 * I + j] * x[j];
+      x[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sT[(16 * I + i) * PA + 16 * I + cc] = x[i];
+  } else {
+    // zero the strictly-upper blocks: W = T X reads blocks (0,1) and (2,3) inside its 32-token k-steps
+    for (int idx = tid - 64; idx < 6 * 256; idx += NT - 64) {
+      const int blk6 = idx >> 8, e = idx & 255;
+      const int I = blk6 < 3 ? 0 : blk6 < 5 ? 1 : 2;
+      const int J = blk6 < 3 ? blk6 + 1 : blk6 < 5 ? blk6 - 1 : 3;
+      sT[(16 * I + (e >> 4)) * PA + 16 * J + (e & 15)] = 0.f;
+    }
+  }
+  __syncthreads();
+  // off-diagonal blocks by distance d: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ
+  for (int d = 1; d < 4; ++d) {
+    const int nb = 4 - d;
+    for (int idx = tid; idx < nb * 256; idx += NT) {
+      const int J = idx >> 8, i = (idx >> 4) & 15, jj = idx & 15, I = J + d;
+      float m = 0.f;
+      for (int K = J; K < I; ++K)
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) m += sAkk[(16 * I + i) * PA + 16 * K + kk] * sT[(16 * K + kk) * PA + 16 * J + jj];
+      sTmp[idx] = m;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < nb * 256; idx += NT) {
+      const int J = idx >> 8, i = (idx >> 4) & 15, jj = idx & 15, I = J + d;
+      float m = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk)
+        if (kk <= i) m += sT[(16 * I + i) * PA + 16 * I + kk] * sTmp[(J << 8) + (kk << 4) + jj];
+      sT[(16 * I + i) * PA + 16 * J + jj] = -m;
+    }
+    __syncthreads();
+  }
+
+  // ---- P6b: A_qk = QR_I E_IJ . KC_J^T (split bf16), lower incl. diagonal ----
+  for (int bi = wave; bi < 10; bi += 8) {
+    int I, J;
+    block_ij(bi, I, J);
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int c = 32 * s + 8 * lg;
+      float qv[8], kc[8];
+      ld8(sQ + (16 * I + l16) * PQ + c, qv);
+      if (I > J) {
+        const float* ef = sE + pair_index(I, J) * D + c;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[e] *= ef[e];
+      }
+      ld8(sG + (16 * J + l16) * PQ + c, kc);
+      acc = mfma3(split(qv), split(kc), acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sAqk[(16 * I + 4 * lg + r) * PA + 16 * J + l16] = acc[r];
+  }
+
+  // ---- P8: W = T . (beta KR e^Gam_n) (plain bf16); wave -> 16 key channels ----
+  f32x4 wacc[4] = {zero4(), zero4(), zero4(), zero4()};
+  {
+    const int c = 16 * wave + l16;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int tb = 32 * s + 8 * lg;
+      const float fac = sEn[(tb >> 4) * D + c];
+      float xv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[e] = sBeta[tb + e] * (float)sKb[(tb + e) * PKB + c] * fac;
+      const bf16x8 bx = round8(xv);
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        if (32 * s > 16 * I + 15) continue;  // T is lower triangular
+        float tvv[8];
+        ld8(sT + (16 * I + l16) * PA + 32 * s + 8 * lg, tvv);
+        wacc[I] = mfma(round8(tvv), bx, wacc[I]);
+      }
+    }
+  }
+  __syncthreads();  // every read of KR is done: W takes its place
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sKb[(16 * I + 4 * lg + r) * PKB + 16 * wave + l16] = (__bf16)wacc[I][r];
+  __syncthreads();
+
+  // ---- write the operand tiles (16-byte stores, 8 elements per lane-task) ----
+  __bf16* qhi = reinterpret_cast<__bf16*>(blk + W_QHI);
+  __bf16* qlo = reinterpret_cast<__bf16*>(blk + W_QLO);
+  __bf16* kthi = reinterpret_cast<__bf16*>(blk + W_KTHI);
+  __bf16* ktlo = reinterpret_cast<__bf16*>(blk + W_KTLO);
+  __bf16* wdst = reinterpret_cast<__bf16*>(blk + W_W);
+  __bf16* ahi = reinterpret_cast<__bf16*>(blk + W_AHI);
+  __bf16* alo = reinterpret_cast<__bf16*>(blk + W_ALO);
+  __bf16* thi = reinterpret_cast<__bf16*>(blk + W_THI);
+  __bf16* tlo = reinterpret_cast<__bf16*>(blk + W_TLO);
+  for (int task = tid; task < C * D / 8; task += NT) {
+    // Q~ = QR e^Gam_n(I), row-major [t][c]
+    const int t = task >> 4, c8 = (task & 15) * 8;
+    float v[8];
+    ld8(sQ + t * PQ + c8, v);
+    const float* en = sEn + (t >> 4) * D + c8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= en[e];
+    store_split8(qhi + t * D + c8, qlo + t * D + c8, v);
+    // W, row-major [t][c]
+    *reinterpret_cast<bf16x8*>(wdst + t * D + c8) = *reinterpret_cast<const bf16x8*>(sKb + t * PKB + c8);
+    // K~^T = (KC e^(Gam_C - Gam_n(J)))^T, channel-major [c][t]
+    const int c = task >> 3, t8 = (task & 7) * 8;
+    const float fac = sFac[(t8 >> 4) * D + c];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = sG[(t8 + e) * PQ + c] * fac;
+    store_split8(kthi + c * C + t8, ktlo + c * C + t8, v);
+  }
+  for (int task = tid; task < C * C / 8; task += NT) {
+    const int t = task >> 3, j8 = (task & 7) * 8;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (j8 + e <= t) ? sAqk[t * PA + j8 + e] : 0.f;
+    store_split8(ahi + t * C + j8, alo + t * C + j8, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (j8 + e <= t) ? sT[t * PA + j8 + e] : 0.f;
+    store_split8(thi + t * C + j8, tlo + t * C + j8, v);
+  }
+  if (tid < D) reinterpret_cast<float*>(blk + W_GC)[tid] = sGC[tid];
+}
+
+// ---------------------------------------------------------------------------------------------
+// Phase B: one workgroup per (16-column block of d_v, head, sequence), sequential over chunks.
+// ---------------------------------------------------------------------------------------------
+struct OpTiles {     // this lane's operand fragments of one chunk
+  bf16x8 x0[4];      // waves 0-3: W row tile (4 k-steps) | waves 4-7: Q~ hi (4 k-steps)
+  bf16x8 x1[4];      // waves 4-7: Q~ lo
+  bf16x8 y0[2], y1[2];  // waves 0-3: T hi / lo | waves 4-7: A_qk hi / lo   (2 k-steps)
+  bf16x8 k0[2], k1[2];  // all waves: K~^T hi / lo of channel tile = wave
+  float4 gc;            // e^Gam_C of the four state rows this lane holds
+};
+
+// Every wave fills the same fields (only the source tiles differ by role), so the fields stay
+// in registers.  Waves 0-3 leave x1 unloaded.
+__device__ __forceinline__ void load_tiles(const unsigned char* blk, int wave, int l16, int lg, OpTiles& o) {
+  const int row = 16 * (wave & 3) + l16;
+  const bool u_role = wave < 4;
+  const __bf16* x0p = reinterpret_cast<const __bf16*>(blk + (u_role ? W_W : W_QHI)) + row * D + 8 * lg;
+  const __bf16* x1p = reinterpret_cast<const __bf16*>(blk + W_QLO) + row * D + 8 * lg;
+  const __bf16* y0p = reinterpret_cast<const __bf16*>(blk + (u_role ? W_THI : W_AHI)) + row * C + 8 * lg;
+  const __bf16* y1p = reinterpret_cast<const __bf16*>(blk + (u_role ? W_TLO : W_ALO)) + row * C + 8 * lg;
+  const __bf16* khp = reinterpret_cast<const __bf16*>(blk + W_KTHI) + (16 * wave + l16) * C + 8 * lg;
+  const __bf16* klp = reinterpret_cast<const __bf16*>(blk + W_KTLO) + (16 * wave + l16) * C + 8 * lg;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) o.x0[s] = *reinterpret_cast<const bf16x8*>(x0p + 32 * s);
+  if (!u_role) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) o.x1[s] = *reinterpret_cast<const bf16x8*>(x1p + 32 * s);
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    o.y0[s] = *reinterpret_cast<const bf16x8*>(y0p + 32 * s);
+    o.y1[s] = *reinterpret_cast<const bf16x8*>(y1p + 32 * s);
+    o.k0[s] = *reinterpret_cast<const bf16x8*>(khp + 32 * s);
+    o.k1[s] = *reinterpret_cast<const bf16x8*>(klp + 32 * s);
+  }
+  o.gc = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(blk + W_GC) + 16 * wave + 4 * lg);
+}
+
+template <typename OT>
+__global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const unsigned char* __restrict__ ws,
+                                                          float* __restrict__ ows) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __bf16* sRawV = reinterpret_cast<__bf16*>(smem + B_RAWV);
+  float* sBeta = reinterpret_cast<float*>(smem + B_BETA);
+  __bf16* sVhi = reinterpret_cast<__bf16*>(smem + B_VHI);
+  __bf16* sVlo = reinterpret_cast<__bf16*>(smem + B_VLO);
+  __bf16* sUhi = reinterpret_cast<__bf16*>(smem + B_UHI);
+  __bf16* sUlo = reinterpret_cast<__bf16*>(smem + B_ULO);
+  __bf16* sShi = reinterpret_cast<__bf16*>(smem + B_SHI);
+  __bf16* sSlo = reinterpret_cast<__bf16*>(smem + B_SLO);
+
+  const int H = a.H, T = a.T, W = a.W;
+  const int h = blockIdx.x % H;
+  const int vb = blockIdx.x / H;
+  const int b = blockIdx.y;
+  const int NC = (T + C - 1) / C;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int HD = H * D, Cq = 3 * HD;
+  const bf16_t* __restrict__ qkv = static_cast<const bf16_t*>(a.qkv) + (long long)b * T * Cq;
+  const bf16_t* __restrict__ bin = static_cast<const bf16_t*>(a.beta) + (long long)b * T * H + h;
+  const bf16_t* __restrict__ cin = static_cast<const bf16_t*>(a.conv_in) + (long long)b * Cq * (W - 1);
+  const unsigned char* __restrict__ head_ws = ws + ((long long)b * H + h) * NC * (long long)CH_BYTES;
+  const long long vch = 2LL * HD + (long long)h * D + vb * NV;  // first raw v channel of this block
+
+  // State block: wave w owns channel rows 16w..16w+15; lane holds rows 16w+4lg+r, column l16.
+  f32x4 Sacc;
+  {
+    const float* sp = a.state_in + ((long long)b * H + h) * D * D + vb * NV + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Sacc[r] = sp[(16 * wave + 4 * lg + r) * D];
+  }
+  // conv taps of this lane's v column
+  const int vj = tid & 15;
+  float tv[4];
+  {
+    const bf16_t* cw = static_cast<const bf16_t*>(a.conv_w);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int w = j - (4 - W);
+      tv[j] = w >= 0 ? to_f32(cw[(vch + vj) * W + w]) : 0.f;
+    }
+  }
+
+  // raw v rows of one chunk: lane task = (row r, half) for r < RROWS
+  auto load_rawv = [&](int cidx, uint4& v, float& beta) {
+    v = make_uint4(0u, 0u, 0u, 0u);
+    beta = 0.f;
+    const int c0 = cidx * C;
+    if (tid < RROWS * 2) {
+      const int r = tid >> 1, half = tid & 1;
+      const int tt = c0 - HALO + r;
+      const long long ch = vch + 8 * half;
       if (tt >= 0 && tt < T) {
         v = *reinterpret_cast<const uint4*>(qkv + (long long)tt * Cq + ch);
       } else if (tt < 0 && (W - 1) + tt >= 0) {
@@ -222,324 +584,142 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(LayerArgs a, float
         v = make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16, e8[4] | (uint32_t)e8[5] << 16,
                        e8[6] | (uint32_t)e8[7] << 16);
       }
-      *reinterpret_cast<uint4*>(sRaw + r * PR + col) = v;
     }
-    if (tid < C) sBeta[tid] = tid < L ? to_f32(bin[(long long)(c0 + tid) * H]) : 0.f;
-    __syncthreads();
+    if (tid >= 192 && tid < 192 + C && c0 + tid - 192 < T) beta = to_f32(bin[(long long)(c0 + tid - 192) * H]);
+  };
 
-    // ---- P2: causal conv + SiLU.  q|k: lane -> channel cq, 32 tokens; v block: 2 tokens per lane ----
+  OpTiles cur, nxt;
+  uint4 rv_cur, rv_nxt;
+  float be_cur, be_nxt;
+  load_tiles(head_ws, wave, l16, lg, cur);
+  load_rawv(0, rv_cur, be_cur);
+  // the state operand (split) for the first chunk
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const __bf16 hi = (__bf16)Sacc[r];
+    sShi[l16 * PST + 16 * wave + 4 * lg + r] = hi;
+    sSlo[l16 * PST + 16 * wave + 4 * lg + r] = (__bf16)(Sacc[r] - (float)hi);
+  }
+
+  for (int ci = 0; ci < NC; ++ci) {
+    const int c0 = ci * C;
+    const int L = min(C, T - c0);
+    // B1: this chunk's raw v rows and beta into LDS; then issue the next chunk's loads
+    if (tid < RROWS * 2) *reinterpret_cast<uint4*>(sRawV + (tid >> 1) * PRV + 8 * (tid & 1)) = rv_cur;
+    if (tid >= 192 && tid < 192 + C) sBeta[tid - 192] = be_cur;
+    if (ci + 1 < NC) {
+      load_tiles(head_ws + (long long)(ci + 1) * CH_BYTES, wave, l16, lg, nxt);
+      load_rawv(ci + 1, rv_nxt, be_nxt);
+    }
+    __syncthreads();
+    // B2: conv + SiLU of the v block, times beta, as the split B operand [col][token]
     {
-      const int tb = 32 * (tid >> 8);
-      const __bf16* col = sRaw + cq;
-      float r0 = (float)col[(tb + 0) * PR], r1 = (float)col[(tb + 1) * PR], r2 = (float)col[(tb + 2) * PR];
-      float* dst = cq < D ? sQ + cq : sG + (cq - D);
-#pragma unroll 4
-      for (int i = 0; i < 32; ++i) {
-        const int t = tb + i;
-        const float r3 = (float)col[(t + 3) * PR];
-        const float y = tq[0] * r0 + tq[1] * r1 + tq[2] * r2 + tq[3] * r3;
-        dst[t * PQ] = t < L ? y / (1.0f + __expf(-y)) : 0.f;
-        r0 = r1; r1 = r2; r2 = r3;
-      }
       const int tg = tid >> 4;  // 0..31
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int t = 2 * tg + i;
-        const __bf16* vc = sRaw + 2 * D + vj;
-        const float y = tv[0] * (float)vc[t * PR] + tv[1] * (float)vc[(t + 1) * PR] + tv[2] * (float)vc[(t + 2) * PR] +
-                        tv[3] * (float)vc[(t + 3) * PR];
-        sVT[vj * PT + t] = t < L ? sBeta[t] * (y / (1.0f + __expf(-y))) : 0.f;
+        const __bf16* vc = sRawV + vj;
+        const float y = tv[0] * (float)vc[t * PRV] + tv[1] * (float)vc[(t + 1) * PRV] +
+                        tv[2] * (float)vc[(t + 2) * PRV] + tv[3] * (float)vc[(t + 3) * PRV];
+        const float x = t < L ? sBeta[t] * silu_fast(y) : 0.f;
+        const __bf16 hi = (__bf16)x;
+        sVhi[vj * PVT + t] = hi;
+        sVlo[vj * PVT + t] = (__bf16)(x - (float)hi);
       }
     }
     __syncthreads();
-
-    // ---- P3: bounded-sigmoid gate and its cumulative sum (lane -> channel, 16-token segment) ----
-    {
-      const int i = tid & 127, seg = tid >> 7;
-      float gl[16];
-      float acc = 0.f;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int t = 16 * seg + k;
-        float g = 0.f;
-        if (t < L) {
-          const float fv = to_f32(fin[(long long)(c0 + t) * HD + i]) + dtb;
-          g = lb / (1.0f + __expf(-Ah * fv));
-        }
-        acc += g;
-        gl[k] = acc;
-      }
-      sSeg[seg * D + i] = acc;
-      // ---- P4 (same phase): q / k L2 normalisers, one wave per 8 tokens ----
-      for (int t = wave * 8; t < wave * 8 + 8; ++t) {
-        const float q0 = sQ[t * PQ + lane], q1 = sQ[t * PQ + lane + 64];
-        const float k0 = sG[t * PQ + lane], k1 = sG[t * PQ + lane + 64];
-        const float qq = wave_sum(q0 * q0 + q1 * q1);
-        const float kk = wave_sum(k0 * k0 + k1 * k1);
-        if (lane == 0) {
-          sNrm[t] = a.scale / fmaxf(sqrtf(qq), a.l2_eps);
-          sNrm[C + t] = 1.0f / fmaxf(sqrtf(kk), a.l2_eps);
-        }
-      }
-      __syncthreads();
-      float off = 0.f;
-      for (int s = 0; s < seg; ++s) off += sSeg[s * D + i];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) sGam[(16 * seg + k) * PQ + i] = gl[k] + off;
-      sGn[seg * D + i] = gl[0] + off;
-      if (seg == 3) sGn[4 * D + i] = gl[15] + off;
-    }
-    __syncthreads();
-
-    // ---- P5: anchored operands QR, KR (bf16), KC and the per-channel factor tables ----
-    for (int idx = tid; idx < C * D; idx += NT) {
-      const int t = idx >> 7, c = idx & 127;
-      const float G = sGam[t * PQ + c];
-      const float Gn = sGn[(t >> 4) * D + c];
-      const float e1 = __expf(G - Gn);  // <= 1
-      const float e2 = __expf(Gn - G);  // in [1, e^(15|lb|)]
-      const float q = sQ[t * PQ + c] * sNrm[t];
-      const float k = sG[t * PQ + c] * sNrm[C + t];
-      sQ[t * PQ + c] = q * e1;
-      sKb[t * PKB + c] = (__bf16)(k * e1);
-      sG[t * PQ + c] = k * e2;
-    }
-    if (tid < D) {
-      const int c = tid;
-      const float GC = sGn[4 * D + c];
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        const float GI = sGn[I * D + c];
-        sEn[I * D + c] = __expf(GI);
-        sFac[I * D + c] = __expf(GC - GI);
-#pragma unroll
-        for (int J = 0; J < I; ++J) sE[pair_index(I, J) * D + c] = __expf(GI - sGn[J * D + c]);
-      }
-      sGC[c] = __expf(GC);
-    }
-    __syncthreads();
-
-    // ---- P6a: A_kk = beta_i * KR_I E_IJ . KC_J^T (plain bf16), strictly lower ----
-    for (int bi = wave; bi < 10; bi += 8) {
-      int I, J;
-      block_ij(bi, I, J);
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int c = 32 * s + 8 * lg;
-        bf16x8 av = *reinterpret_cast<const bf16x8*>(sKb + (16 * I + l16) * PKB + c);
-        if (I > J) {
-          const float* ef = sE + pair_index(I, J) * D + c;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) av[e] = (__bf16)((float)av[e] * ef[e]);
-        }
-        float kc[8];
-        ld8(sG + (16 * J + l16) * PQ + c, kc);
-        acc = mfma(av, round8(kc), acc);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * I + 4 * lg + r, j = 16 * J + l16;
-        sAkk[i * PA + j] = j < i ? sBeta[i] * acc[r] : 0.f;
-      }
-    }
-    __syncthreads();
-
-    // ---- P7: T = (I + A_kk)^-1 in fp32: diagonal 16x16 blocks by forward substitution ----
-    if (wave == 0) {
-      const int I = lg, cc = l16;
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v = (i == cc) ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < i; ++j) v -= sAkk[(16 * I + i) * PA + 16 * I + j] * x[j];
-        x[i] = v;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sT[(16 * I + i) * PA + 16 * I + cc] = x[i];
-    } else {
-      // zero the strictly-upper blocks of T
-      for (int idx = tid - 64; idx < 6 * 256; idx += NT - 64) {
-        const int blk = idx >> 8, e = idx & 255;
-        const int I = blk < 3 ? 0 : blk < 5 ? 1 : 2;
-        const int J = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
-        sT[(16 * I + (e >> 4)) * PA + 16 * J + (e & 15)] = 0.f;
-      }
-    }
-    __syncthreads();
-    // off-diagonal blocks by distance d: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ
-    for (int d = 1; d < 4; ++d) {
-      const int nb = 4 - d;
-      for (int idx = tid; idx < nb * 256; idx += NT) {
-        const int J = idx >> 8, i = (idx >> 4) & 15, jj = idx & 15, I = J + d;
-        float m = 0.f;
-        for (int K = J; K < I; ++K)
-#pragma unroll
-          for (int kk = 0; kk < 16; ++kk) m += sAkk[(16 * I + i) * PA + 16 * K + kk] * sT[(16 * K + kk) * PA + 16 * J + jj];
-        sUT[idx] = m;
-      }
-      __syncthreads();
-      for (int idx = tid; idx < nb * 256; idx += NT) {
-        const int J = idx >> 8, i = (idx >> 4) & 15, jj = idx & 15, I = J + d;
-        float m = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk)
-          if (kk <= i) m += sT[(16 * I + i) * PA + 16 * I + kk] * sUT[(J << 8) + (kk << 4) + jj];
-        sT[(16 * I + i) * PA + 16 * J + jj] = -m;
-      }
-      __syncthreads();
-    }
-
-    // ---- P6b: A_qk = QR_I E_IJ . KC_J^T (split bf16), lower incl. diagonal; zero upper blocks read later ----
-    for (int bi = wave; bi < 10; bi += 8) {
-      int I, J;
-      block_ij(bi, I, J);
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int c = 32 * s + 8 * lg;
-        float qv[8], kc[8];
-        ld8(sQ + (16 * I + l16) * PQ + c, qv);
-        if (I > J) {
-          const float* ef = sE + pair_index(I, J) * D + c;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qv[e] *= ef[e];
-        }
-        ld8(sG + (16 * J + l16) * PQ + c, kc);
-        acc = mfma3(split(qv), split(kc), acc);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * I + 4 * lg + r, j = 16 * J + l16;
-        sAqk[i * PA + j] = j <= i ? acc[r] : 0.f;
-      }
-    }
-    if (wave >= 6) {  // blocks (0,1) and (2,3) fall inside the 32-token k-steps of A_qk . U
-      const int e = tid - 6 * 64;  // 0..127
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int idx = e + 128 * k, blk = idx >> 8, ee = idx & 255;
-        const int I = blk == 0 ? 0 : 2, J = I + 1;
-        sAqk[(16 * I + (ee >> 4)) * PA + 16 * J + (ee & 15)] = 0.f;
-      }
-    }
-
-    // ---- P8: W = T . (beta KR e^Gam_n) (plain bf16); wave -> 16 key channels ----
-    f32x4 wacc[4] = {zero4(), zero4(), zero4(), zero4()};
-    {
-      const int c = 16 * wave + l16;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int tb = 32 * s + 8 * lg;
-        const float fac = sEn[(tb >> 4) * D + c];
-        float xv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xv[e] = sBeta[tb + e] * (float)sKb[(tb + e) * PKB + c] * fac;
-        const bf16x8 bx = round8(xv);
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          if (32 * s > 16 * I + 15) continue;  // T is lower triangular
-          float tvv[8];
-          ld8(sT + (16 * I + l16) * PA + 32 * s + 8 * lg, tvv);
-          wacc[I] = mfma(round8(tvv), bx, wacc[I]);
-        }
-      }
-    }
-    // ---- P9: Ut = T . (beta V) (split), waves 0..3 own row tile I = wave ----
-    f32x4 uacc = zero4();
+    // B3: waves 0-3: U = T (beta V) - W S for row tile I; waves 4-7: O = Q~ S for row tile I
+    f32x4 oacc = zero4();
     if (wave < 4) {
       const int I = wave;
+      f32x4 ua = zero4(), ub = zero4();
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if (32 * s > 16 * I + 15) continue;
-        float tvv[8], vv[8];
-        ld8(sT + (16 * I + l16) * PA + 32 * s + 8 * lg, tvv);
-        ld8(sVT + l16 * PT + 32 * s + 8 * lg, vv);
-        uacc = mfma3(split(tvv), split(vv), uacc);
+        const bf16x8 vh = *reinterpret_cast<const bf16x8*>(sVhi + l16 * PVT + 32 * s + 8 * lg);
+        const bf16x8 vl = *reinterpret_cast<const bf16x8*>(sVlo + l16 * PVT + 32 * s + 8 * lg);
+        ua = mfma(cur.y0[s], vh, ua);
+        ub = mfma(cur.y0[s], vl, ub);
+        ub = mfma(cur.y1[s], vh, ub);
       }
-    }
-    __syncthreads();  // every read of KR is done: W takes its place
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sKb[(16 * I + 4 * lg + r) * PKB + 16 * wave + l16] = (__bf16)wacc[I][r];
-    __syncthreads();
-
-    // ---- S1: U = Ut - W S (waves 0..3, row tile I = wave) -> sUT ----
-    if (wave < 4) {
-      const int I = wave;
-      f32x4 pacc = zero4();
+      f32x4 pa = zero4(), pb = zero4();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int c = 32 * s + 8 * lg;
-        const bf16x8 aw = *reinterpret_cast<const bf16x8*>(sKb + (16 * I + l16) * PKB + c);
-        float sv[8];
-        ld8(sST + l16 * PS + c, sv);
-        const Split8 bs = split(sv);
-        pacc = mfma(aw, bs.lo, pacc);
-        pacc = mfma(aw, bs.hi, pacc);
+        const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
+        const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSlo + l16 * PST + 32 * s + 8 * lg);
+        pa = mfma(cur.x0[s], sh, pa);
+        pb = mfma(cur.x0[s], sl, pb);
       }
-      float4 u4;
-      u4.x = uacc[0] - pacc[0];
-      u4.y = uacc[1] - pacc[1];
-      u4.z = uacc[2] - pacc[2];
-      u4.w = uacc[3] - pacc[3];
-      *reinterpret_cast<float4*>(sUT + l16 * PT + 16 * I + 4 * lg) = u4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float u = (ua[r] + ub[r]) - (pa[r] + pb[r]);
+        const __bf16 hi = (__bf16)u;
+        sUhi[l16 * PVT + 16 * I + 4 * lg + r] = hi;
+        sUlo[l16 * PVT + 16 * I + 4 * lg + r] = (__bf16)(u - (float)hi);
+      }
+    } else {
+      f32x4 ob = zero4();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
+        const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSlo + l16 * PST + 32 * s + 8 * lg);
+        oacc = mfma(cur.x0[s], sh, oacc);
+        ob = mfma(cur.x0[s], sl, ob);
+        ob = mfma(cur.x1[s], sh, ob);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) oacc[r] += ob[r];
     }
     __syncthreads();
-
-    // ---- S3: O = (QR e^Gam_n) S + A_qk U (waves 4..7, row tile I = wave - 4) -> workspace ----
+    // B4: waves 4-7: O += A_qk U and store; all waves: S <- e^Gam_C S + K~^T U
     if (wave >= 4) {
       const int I = wave - 4;
-      f32x4 oacc = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int c = 32 * s + 8 * lg;
-        float qv[8], sv[8];
-        ld8(sQ + (16 * I + l16) * PQ + c, qv);
-        const float* en = sEn + I * D + c;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qv[e] *= en[e];
-        ld8(sST + l16 * PS + c, sv);
-        oacc = mfma3(split(qv), split(sv), oacc);
-      }
+      f32x4 ob = zero4();
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if (32 * s > 16 * I + 15) continue;
-        float av[8], uv[8];
-        ld8(sAqk + (16 * I + l16) * PA + 32 * s + 8 * lg, av);
-        ld8(sUT + l16 * PT + 32 * s + 8 * lg, uv);
-        oacc = mfma3(split(av), split(uv), oacc);
+        const bf16x8 uh = *reinterpret_cast<const bf16x8*>(sUhi + l16 * PVT + 32 * s + 8 * lg);
+        const bf16x8 ul = *reinterpret_cast<const bf16x8*>(sUlo + l16 * PVT + 32 * s + 8 * lg);
+        oacc = mfma(cur.y0[s], uh, oacc);
+        ob = mfma(cur.y0[s], ul, ob);
+        ob = mfma(cur.y1[s], uh, ob);
       }
       float* op = ows + (((long long)b * T + c0) * H + h) * D + vb * NV + l16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * I + 4 * lg + r;
-        if (t < L) op[(long long)t * HD] = oacc[r];
+        if (t < L) op[(long long)t * HD] = oacc[r] + ob[r];
       }
     }
-    // ---- S4: S <- e^Gam_C S + (KC e^(Gam_C - Gam_n))^T U (all waves, channel tile = wave) ----
     {
-      f32x4 sn;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sn[r] = sGC[16 * wave + 4 * lg + r] * Sacc[r];
-      const int c = 16 * wave + l16;
+      f32x4 sa, sb = zero4();
+      sa[0] = cur.gc.x * Sacc[0];
+      sa[1] = cur.gc.y * Sacc[1];
+      sa[2] = cur.gc.z * Sacc[2];
+      sa[3] = cur.gc.w * Sacc[3];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const int tb = 32 * s + 8 * lg;
-        const float fac = sFac[(tb >> 4) * D + c];
-        float kv[8], uv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kv[e] = sG[(tb + e) * PQ + c] * fac;
-        ld8(sUT + l16 * PT + tb, uv);
-        sn = mfma3(split(kv), split(uv), sn);
+        const bf16x8 uh = *reinterpret_cast<const bf16x8*>(sUhi + l16 * PVT + 32 * s + 8 * lg);
+        const bf16x8 ul = *reinterpret_cast<const bf16x8*>(sUlo + l16 * PVT + 32 * s + 8 * lg);
+        sa = mfma(cur.k0[s], uh, sa);
+        sb = mfma(cur.k0[s], ul, sb);
+        sb = mfma(cur.k1[s], uh, sb);
       }
-      Sacc = sn;
-    }
-    __syncthreads();  // the old state block has been read by S1 and S3
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sST[l16 * PS + 16 * wave + 4 * lg + r] = Sacc[r];
+      for (int r = 0; r < 4; ++r) Sacc[r] = sa[r] + sb[r];
+    }
+    __syncthreads();  // the old state operand has been read
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const __bf16 hi = (__bf16)Sacc[r];
+      sShi[l16 * PST + 16 * wave + 4 * lg + r] = hi;
+      sSlo[l16 * PST + 16 * wave + 4 * lg + r] = (__bf16)(Sacc[r] - (float)hi);
+    }
+    if (ci + 1 < NC) {
+      cur = nxt;
+      rv_cur = rv_nxt;
+      be_cur = be_nxt;
+    }
   }
 
   {
@@ -600,24 +780,25 @@ bool prefill_mfma_supported(int Dh, int chunk, int io, int W, float lb) {
 }
 
 size_t prefill_mfma_workspace(int B, int T, int H, int Dh, int) {
-  return (size_t)B * T * H * Dh * sizeof(float);
+  const size_t nc = (size_t)(T + C - 1) / C;
+  return (size_t)B * H * nc * CH_BYTES + (size_t)B * T * H * Dh * sizeof(float);
 }
 
 hipError_t launch_prefill_mfma(const LayerArgs& a, void* ws, size_t, int ot, hipStream_t s) {
-  float* ows = static_cast<float*>(ws);
-  const dim3 grid(NBLK * a.H, a.B), block(NT);
-  hipError_t e;
-  if (ot == kBF16) {
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_prefill_mfma_kernel<bf16_t>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    if (attr != hipSuccess) return attr;
-    kda_prefill_mfma_kernel<bf16_t><<<grid, block, LDS_BYTES, s>>>(a, ows);
-  } else {
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_prefill_mfma_kernel<float>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    if (attr != hipSuccess) return attr;
-    kda_prefill_mfma_kernel<float><<<grid, block, LDS_BYTES, s>>>(a, ows);
-  }
+  unsigned char* tiles = static_cast<unsigned char*>(ws);
+  const int NC = (a.T + C - 1) / C;
+  float* ows = reinterpret_cast<float*>(tiles + (size_t)a.B * a.H * NC * CH_BYTES);
+  static const hipError_t attr_a = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_A);
+  if (attr_a != hipSuccess) return attr_a;
+  kda_chunk_prep_kernel<<<dim3(NC, a.H, a.B), NT, LDS_A, s>>>(a, tiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid_b(NBLK * a.H, a.B);
+  if (ot == kBF16)
+    kda_chunk_state_kernel<bf16_t><<<grid_b, NT, LDS_B, s>>>(a, tiles, ows);
+  else
+    kda_chunk_state_kernel<float><<<grid_b, NT, LDS_B, s>>>(a, tiles, ows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long rows = (long long)a.B * a.T * a.H;
   const dim3 ng((unsigned)((rows + 3) / 4));
