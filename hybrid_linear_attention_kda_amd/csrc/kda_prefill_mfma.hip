@@ -50,8 +50,8 @@ namespace {
 
 constexpr int D = 128;       // head size (d_k = d_v)
 constexpr int C = 64;        // chunk
-constexpr int NV = 16;       // d_v columns per workgroup
-constexpr int NBLK = D / NV; // workgroups per head
+constexpr int NVB = 16;      // d_v columns per phase-B workgroup
+constexpr int NBLK = D / NVB; // phase-B workgroups per head
 constexpr int NT = 512;      // lanes
 constexpr int HALO = 3;      // staged rows before the chunk (conv width <= 4)
 
@@ -83,7 +83,10 @@ static_assert(STG_BYTES >= 2 * C * PA * 4 && STG_BYTES >= C * PQ * 4, "staging a
 static_assert(LDS_A <= 160 * 1024, "LDS budget");
 
 // Workspace tile block per (sequence, head, chunk), written by phase A and read by phase B.
-constexpr int W_QHI = 0;                   // Q~ hi  [64][128] bf16
+// Every matrix is stored in MFMA fragment order: fragment f = (row / 16) * (K / 32) + k / 32 of a
+// [rows][K] operand holds, for lane l, the 8 elements (row 16*(f / (K/32)) + l % 16,
+// k = 32*(f % (K/32)) + 8*(l / 16) + 0..7), so a wave loads one fragment as 1 KB contiguous.
+constexpr int W_QHI = 0;                   // Q~ hi  [64][128] bf16 (16 fragments)
 constexpr int W_QLO = W_QHI + C * D * 2;   // Q~ lo
 constexpr int W_KTHI = W_QLO + C * D * 2;  // K~^T hi [128][64] bf16
 constexpr int W_KTLO = W_KTHI + D * C * 2; // K~^T lo
@@ -97,18 +100,18 @@ constexpr int CH_BYTES = W_GC + D * 4;     // 115200
 static_assert(CH_BYTES % 256 == 0, "tile blocks stay 256-byte aligned");
 
 // Phase B LDS layout (bytes)
-constexpr int PRV = 24;                    // bf16 pitch of the staged raw v rows (16 used)
-constexpr int PVT = 72;                    // bf16 pitch of [16][64] token-major operands
-constexpr int PST = 136;                   // bf16 pitch of the [16][128] state operand
+constexpr int PRV = NVB + 8;               // bf16 pitch of the staged raw v rows
+constexpr int PVT = 72;                    // bf16 pitch of [NVB][64] token-major operands
+constexpr int PST = 136;                   // bf16 pitch of the [NVB][128] state operand
 constexpr int B_RAWV = 0;
 constexpr int B_BETA = B_RAWV + RROWS * PRV * 2;
 constexpr int B_VHI = B_BETA + C * 4;
-constexpr int B_VLO = B_VHI + NV * PVT * 2;
-constexpr int B_UHI = B_VLO + NV * PVT * 2;
-constexpr int B_ULO = B_UHI + NV * PVT * 2;
-constexpr int B_SHI = B_ULO + NV * PVT * 2;
-constexpr int B_SLO = B_SHI + NV * PST * 2;
-constexpr int LDS_B = B_SLO + NV * PST * 2;
+constexpr int B_VLO = B_VHI + NVB * PVT * 2;
+constexpr int B_UHI = B_VLO + NVB * PVT * 2;
+constexpr int B_ULO = B_UHI + NVB * PVT * 2;
+constexpr int B_SHI = B_ULO + NVB * PVT * 2;
+constexpr int B_SLO = B_SHI + NVB * PST * 2;
+constexpr int LDS_B = B_SLO + NVB * PST * 2;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -148,6 +151,14 @@ __device__ __forceinline__ void ld8(const float* p, float (&x)[8]) {
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Element offset of (row, k .. k+7) (k a multiple of 8) in the fragment-order layout of a
+// [rows][K] operand.
+__device__ __forceinline__ int frag_offset(int row, int k, int K) {
+  const int f = (row >> 4) * (K >> 5) + (k >> 5);
+  const int lane = (row & 15) + 16 * ((k & 31) >> 3);
+  return (f * 64 + lane) * 8;
+}
 
 // (I, J) of the ten lower sub-chunk blocks, and the index of the factor table for I > J.
 __device__ __forceinline__ void block_ij(int bi, int& I, int& J) {
@@ -440,7 +451,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
     for (int r = 0; r < 4; ++r) sKb[(16 * I + 4 * lg + r) * PKB + 16 * wave + l16] = (__bf16)wacc[I][r];
   __syncthreads();
 
-  // ---- write the operand tiles (16-byte stores, 8 elements per lane-task) ----
+  // ---- write the operand tiles in fragment order (16-byte stores, 8 elements per lane-task) ----
   __bf16* qhi = reinterpret_cast<__bf16*>(blk + W_QHI);
   __bf16* qlo = reinterpret_cast<__bf16*>(blk + W_QLO);
   __bf16* kthi = reinterpret_cast<__bf16*>(blk + W_KTHI);
@@ -451,70 +462,75 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
   __bf16* thi = reinterpret_cast<__bf16*>(blk + W_THI);
   __bf16* tlo = reinterpret_cast<__bf16*>(blk + W_TLO);
   for (int task = tid; task < C * D / 8; task += NT) {
-    // Q~ = QR e^Gam_n(I), row-major [t][c]
+    // Q~ = QR e^Gam_n(I) and W: [64 tokens][128 channels]
     const int t = task >> 4, c8 = (task & 15) * 8;
+    const int fo = frag_offset(t, c8, D);
     float v[8];
     ld8(sQ + t * PQ + c8, v);
     const float* en = sEn + (t >> 4) * D + c8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] *= en[e];
-    store_split8(qhi + t * D + c8, qlo + t * D + c8, v);
-    // W, row-major [t][c]
-    *reinterpret_cast<bf16x8*>(wdst + t * D + c8) = *reinterpret_cast<const bf16x8*>(sKb + t * PKB + c8);
-    // K~^T = (KC e^(Gam_C - Gam_n(J)))^T, channel-major [c][t]
+    store_split8(qhi + fo, qlo + fo, v);
+    *reinterpret_cast<bf16x8*>(wdst + fo) = *reinterpret_cast<const bf16x8*>(sKb + t * PKB + c8);
+    // K~^T = (KC e^(Gam_C - Gam_n(J)))^T: [128 channels][64 tokens]
     const int c = task >> 3, t8 = (task & 7) * 8;
+    const int ko = frag_offset(c, t8, C);
     const float fac = sFac[(t8 >> 4) * D + c];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = sG[(t8 + e) * PQ + c] * fac;
-    store_split8(kthi + c * C + t8, ktlo + c * C + t8, v);
+    store_split8(kthi + ko, ktlo + ko, v);
   }
   for (int task = tid; task < C * C / 8; task += NT) {
+    // A_qk and T: [64][64], zero above the diagonal
     const int t = task >> 3, j8 = (task & 7) * 8;
+    const int fo = frag_offset(t, j8, C);
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = (j8 + e <= t) ? sAqk[t * PA + j8 + e] : 0.f;
-    store_split8(ahi + t * C + j8, alo + t * C + j8, v);
+    store_split8(ahi + fo, alo + fo, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = (j8 + e <= t) ? sT[t * PA + j8 + e] : 0.f;
-    store_split8(thi + t * C + j8, tlo + t * C + j8, v);
+    store_split8(thi + fo, tlo + fo, v);
   }
   if (tid < D) reinterpret_cast<float*>(blk + W_GC)[tid] = sGC[tid];
 }
 
 // ---------------------------------------------------------------------------------------------
-// Phase B: one workgroup per (16-column block of d_v, head, sequence), sequential over chunks.
+// Phase B: one workgroup per (NVB-column block of d_v, head, sequence), sequential over chunks.
+// Waves 0-3 form U for row tile I = wave, waves 4-7 form O for row tile I = wave - 4, and every
+// wave updates state rows 16*wave .. 16*wave+15; each role covers all NVB/16 column tiles.
 // ---------------------------------------------------------------------------------------------
-struct OpTiles {     // this lane's operand fragments of one chunk
-  bf16x8 x0[4];      // waves 0-3: W row tile (4 k-steps) | waves 4-7: Q~ hi (4 k-steps)
-  bf16x8 x1[4];      // waves 4-7: Q~ lo
+struct OpTiles {        // this lane's operand fragments of one chunk
+  bf16x8 x0[4];         // waves 0-3: W (4 k-steps) | waves 4-7: Q~ hi
+  bf16x8 x1[4];         // waves 4-7: Q~ lo
   bf16x8 y0[2], y1[2];  // waves 0-3: T hi / lo | waves 4-7: A_qk hi / lo   (2 k-steps)
   bf16x8 k0[2], k1[2];  // all waves: K~^T hi / lo of channel tile = wave
   float4 gc;            // e^Gam_C of the four state rows this lane holds
 };
 
-// Every wave fills the same fields (only the source tiles differ by role), so the fields stay
-// in registers.  Waves 0-3 leave x1 unloaded.
-__device__ __forceinline__ void load_tiles(const unsigned char* blk, int wave, int l16, int lg, OpTiles& o) {
-  const int row = 16 * (wave & 3) + l16;
+// Every field is filled by one fixed sequence of fragment loads (only the source tiles differ by
+// role), so the fields stay in registers.  Waves 0-3 leave x1 unloaded.
+__device__ __forceinline__ void load_tiles(const unsigned char* blk, int wave, int lane, int lg, OpTiles& o) {
+  const int I = wave & 3;
   const bool u_role = wave < 4;
-  const __bf16* x0p = reinterpret_cast<const __bf16*>(blk + (u_role ? W_W : W_QHI)) + row * D + 8 * lg;
-  const __bf16* x1p = reinterpret_cast<const __bf16*>(blk + W_QLO) + row * D + 8 * lg;
-  const __bf16* y0p = reinterpret_cast<const __bf16*>(blk + (u_role ? W_THI : W_AHI)) + row * C + 8 * lg;
-  const __bf16* y1p = reinterpret_cast<const __bf16*>(blk + (u_role ? W_TLO : W_ALO)) + row * C + 8 * lg;
-  const __bf16* khp = reinterpret_cast<const __bf16*>(blk + W_KTHI) + (16 * wave + l16) * C + 8 * lg;
-  const __bf16* klp = reinterpret_cast<const __bf16*>(blk + W_KTLO) + (16 * wave + l16) * C + 8 * lg;
+  const bf16x8* x0p = reinterpret_cast<const bf16x8*>(blk + (u_role ? W_W : W_QHI)) + (I * 4) * 64 + lane;
+  const bf16x8* x1p = reinterpret_cast<const bf16x8*>(blk + W_QLO) + (I * 4) * 64 + lane;
+  const bf16x8* y0p = reinterpret_cast<const bf16x8*>(blk + (u_role ? W_THI : W_AHI)) + (I * 2) * 64 + lane;
+  const bf16x8* y1p = reinterpret_cast<const bf16x8*>(blk + (u_role ? W_TLO : W_ALO)) + (I * 2) * 64 + lane;
+  const bf16x8* khp = reinterpret_cast<const bf16x8*>(blk + W_KTHI) + (wave * 2) * 64 + lane;
+  const bf16x8* klp = reinterpret_cast<const bf16x8*>(blk + W_KTLO) + (wave * 2) * 64 + lane;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) o.x0[s] = *reinterpret_cast<const bf16x8*>(x0p + 32 * s);
+  for (int s = 0; s < 4; ++s) o.x0[s] = x0p[s * 64];
   if (!u_role) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) o.x1[s] = *reinterpret_cast<const bf16x8*>(x1p + 32 * s);
+    for (int s = 0; s < 4; ++s) o.x1[s] = x1p[s * 64];
   }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    o.y0[s] = *reinterpret_cast<const bf16x8*>(y0p + 32 * s);
-    o.y1[s] = *reinterpret_cast<const bf16x8*>(y1p + 32 * s);
-    o.k0[s] = *reinterpret_cast<const bf16x8*>(khp + 32 * s);
-    o.k1[s] = *reinterpret_cast<const bf16x8*>(klp + 32 * s);
+    o.y0[s] = y0p[s * 64];
+    o.y1[s] = y1p[s * 64];
+    o.k0[s] = khp[s * 64];
+    o.k1[s] = klp[s * 64];
   }
   o.gc = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(blk + W_GC) + 16 * wave + 4 * lg);
 }
@@ -522,6 +538,7 @@ __device__ __forceinline__ void load_tiles(const unsigned char* blk, int wave, i
 template <typename OT>
 __global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const unsigned char* __restrict__ ws,
                                                           float* __restrict__ ows) {
+  constexpr int NCT = NVB / 16;  // column tiles
   extern __shared__ __align__(16) unsigned char smem[];
   __bf16* sRawV = reinterpret_cast<__bf16*>(smem + B_RAWV);
   float* sBeta = reinterpret_cast<float*>(smem + B_BETA);
@@ -545,17 +562,30 @@ __global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const 
   const bf16_t* __restrict__ bin = static_cast<const bf16_t*>(a.beta) + (long long)b * T * H + h;
   const bf16_t* __restrict__ cin = static_cast<const bf16_t*>(a.conv_in) + (long long)b * Cq * (W - 1);
   const unsigned char* __restrict__ head_ws = ws + ((long long)b * H + h) * NC * (long long)CH_BYTES;
-  const long long vch = 2LL * HD + (long long)h * D + vb * NV;  // first raw v channel of this block
+  const long long vch = 2LL * HD + (long long)h * D + vb * NVB;  // first raw v channel of this block
 
-  // State block: wave w owns channel rows 16w..16w+15; lane holds rows 16w+4lg+r, column l16.
-  f32x4 Sacc;
+  // State block: wave w owns channel rows 16w..16w+15; lane holds rows 16w+4lg+r of column
+  // 16*j + l16 of the block in Sacc[j].
+  f32x4 Sacc[NCT];
   {
-    const float* sp = a.state_in + ((long long)b * H + h) * D * D + vb * NV + l16;
+    const float* sp = a.state_in + ((long long)b * H + h) * D * D + vb * NVB + l16;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Sacc[r] = sp[(16 * wave + 4 * lg + r) * D];
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Sacc[j][r] = sp[(16 * wave + 4 * lg + r) * D + 16 * j];
   }
-  // conv taps of this lane's v column
-  const int vj = tid & 15;
+  auto write_state_operand = [&]() {
+#pragma unroll
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const __bf16 hi = (__bf16)Sacc[j][r];
+        sShi[(16 * j + l16) * PST + 16 * wave + 4 * lg + r] = hi;
+        sSlo[(16 * j + l16) * PST + 16 * wave + 4 * lg + r] = (__bf16)(Sacc[j][r] - (float)hi);
+      }
+  };
+  // conv taps of this lane's v column (column vj of the block; lanes cover 16 columns per pass)
+  const int vj = tid % NVB;
   float tv[4];
   {
     const bf16_t* cw = static_cast<const bf16_t*>(a.conv_w);
@@ -566,15 +596,16 @@ __global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const 
     }
   }
 
-  // raw v rows of one chunk: lane task = (row r, half) for r < RROWS
+  // raw v rows of one chunk: lane task = (row r, 8-channel segment) for r < RROWS
+  constexpr int SEGS = NVB / 8;
   auto load_rawv = [&](int cidx, uint4& v, float& beta) {
     v = make_uint4(0u, 0u, 0u, 0u);
     beta = 0.f;
     const int c0 = cidx * C;
-    if (tid < RROWS * 2) {
-      const int r = tid >> 1, half = tid & 1;
+    if (tid < RROWS * SEGS) {
+      const int r = tid / SEGS, sg = tid % SEGS;
       const int tt = c0 - HALO + r;
-      const long long ch = vch + 8 * half;
+      const long long ch = vch + 8 * sg;
       if (tt >= 0 && tt < T) {
         v = *reinterpret_cast<const uint4*>(qkv + (long long)tt * Cq + ch);
       } else if (tt < 0 && (W - 1) + tt >= 0) {
@@ -585,39 +616,32 @@ __global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const 
                        e8[6] | (uint32_t)e8[7] << 16);
       }
     }
-    if (tid >= 192 && tid < 192 + C && c0 + tid - 192 < T) beta = to_f32(bin[(long long)(c0 + tid - 192) * H]);
+    if (tid >= 448 && c0 + tid - 448 < T) beta = to_f32(bin[(long long)(c0 + tid - 448) * H]);
   };
 
   OpTiles cur, nxt;
   uint4 rv_cur, rv_nxt;
   float be_cur, be_nxt;
-  load_tiles(head_ws, wave, l16, lg, cur);
+  load_tiles(head_ws, wave, lane, lg, cur);
   load_rawv(0, rv_cur, be_cur);
-  // the state operand (split) for the first chunk
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const __bf16 hi = (__bf16)Sacc[r];
-    sShi[l16 * PST + 16 * wave + 4 * lg + r] = hi;
-    sSlo[l16 * PST + 16 * wave + 4 * lg + r] = (__bf16)(Sacc[r] - (float)hi);
-  }
+  write_state_operand();
 
   for (int ci = 0; ci < NC; ++ci) {
     const int c0 = ci * C;
     const int L = min(C, T - c0);
     // B1: this chunk's raw v rows and beta into LDS; then issue the next chunk's loads
-    if (tid < RROWS * 2) *reinterpret_cast<uint4*>(sRawV + (tid >> 1) * PRV + 8 * (tid & 1)) = rv_cur;
-    if (tid >= 192 && tid < 192 + C) sBeta[tid - 192] = be_cur;
+    if (tid < RROWS * SEGS) *reinterpret_cast<uint4*>(sRawV + (tid / SEGS) * PRV + 8 * (tid % SEGS)) = rv_cur;
+    if (tid >= 448) sBeta[tid - 448] = be_cur;
     if (ci + 1 < NC) {
-      load_tiles(head_ws + (long long)(ci + 1) * CH_BYTES, wave, l16, lg, nxt);
+      load_tiles(head_ws + (long long)(ci + 1) * CH_BYTES, wave, lane, lg, nxt);
       load_rawv(ci + 1, rv_nxt, be_nxt);
     }
     __syncthreads();
     // B2: conv + SiLU of the v block, times beta, as the split B operand [col][token]
     {
-      const int tg = tid >> 4;  // 0..31
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int t = 2 * tg + i;
+      for (int i = 0; i < C * NVB / NT; ++i) {
+        const int t = (tid / NVB) + (NT / NVB) * i;
         const __bf16* vc = sRawV + vj;
         const float y = tv[0] * (float)vc[t * PRV] + tv[1] * (float)vc[(t + 1) * PRV] +
                         tv[2] * (float)vc[(t + 2) * PRV] + tv[3] * (float)vc[(t + 3) * PRV];
@@ -629,92 +653,101 @@ __global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const 
     }
     __syncthreads();
     // B3: waves 0-3: U = T (beta V) - W S for row tile I; waves 4-7: O = Q~ S for row tile I
-    f32x4 oacc = zero4();
+    f32x4 oacc[NCT], ob[NCT];
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      oacc[j] = zero4();
+      ob[j] = zero4();
+    }
     if (wave < 4) {
       const int I = wave;
-      f32x4 ua = zero4(), ub = zero4();
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (32 * s > 16 * I + 15) continue;
-        const bf16x8 vh = *reinterpret_cast<const bf16x8*>(sVhi + l16 * PVT + 32 * s + 8 * lg);
-        const bf16x8 vl = *reinterpret_cast<const bf16x8*>(sVlo + l16 * PVT + 32 * s + 8 * lg);
-        ua = mfma(cur.y0[s], vh, ua);
-        ub = mfma(cur.y0[s], vl, ub);
-        ub = mfma(cur.y1[s], vh, ub);
-      }
-      f32x4 pa = zero4(), pb = zero4();
+      for (int j = 0; j < NCT; ++j) {
+        f32x4 ua = zero4(), ub = zero4(), pa = zero4(), pb = zero4();
+        const int col = 16 * j + l16;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
-        const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSlo + l16 * PST + 32 * s + 8 * lg);
-        pa = mfma(cur.x0[s], sh, pa);
-        pb = mfma(cur.x0[s], sl, pb);
-      }
+        for (int s = 0; s < 2; ++s) {
+          if (32 * s > 16 * I + 15) continue;
+          const bf16x8 vh = *reinterpret_cast<const bf16x8*>(sVhi + col * PVT + 32 * s + 8 * lg);
+          const bf16x8 vl = *reinterpret_cast<const bf16x8*>(sVlo + col * PVT + 32 * s + 8 * lg);
+          ua = mfma(cur.y0[s], vh, ua);
+          ub = mfma(cur.y0[s], vl, ub);
+          ub = mfma(cur.y1[s], vh, ub);
+        }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float u = (ua[r] + ub[r]) - (pa[r] + pb[r]);
-        const __bf16 hi = (__bf16)u;
-        sUhi[l16 * PVT + 16 * I + 4 * lg + r] = hi;
-        sUlo[l16 * PVT + 16 * I + 4 * lg + r] = (__bf16)(u - (float)hi);
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sShi + col * PST + 32 * s + 8 * lg);
+          const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSlo + col * PST + 32 * s + 8 * lg);
+          pa = mfma(cur.x0[s], sh, pa);
+          pb = mfma(cur.x0[s], sl, pb);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float u = (ua[r] + ub[r]) - (pa[r] + pb[r]);
+          const __bf16 hi = (__bf16)u;
+          sUhi[col * PVT + 16 * I + 4 * lg + r] = hi;
+          sUlo[col * PVT + 16 * I + 4 * lg + r] = (__bf16)(u - (float)hi);
+        }
       }
     } else {
-      f32x4 ob = zero4();
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
-        const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSlo + l16 * PST + 32 * s + 8 * lg);
-        oacc = mfma(cur.x0[s], sh, oacc);
-        ob = mfma(cur.x0[s], sl, ob);
-        ob = mfma(cur.x1[s], sh, ob);
+      for (int j = 0; j < NCT; ++j) {
+        const int col = 16 * j + l16;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sShi + col * PST + 32 * s + 8 * lg);
+          const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSlo + col * PST + 32 * s + 8 * lg);
+          oacc[j] = mfma(cur.x0[s], sh, oacc[j]);
+          ob[j] = mfma(cur.x0[s], sl, ob[j]);
+          ob[j] = mfma(cur.x1[s], sh, ob[j]);
+        }
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) oacc[r] += ob[r];
     }
     __syncthreads();
     // B4: waves 4-7: O += A_qk U and store; all waves: S <- e^Gam_C S + K~^T U
     if (wave >= 4) {
       const int I = wave - 4;
-      f32x4 ob = zero4();
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (32 * s > 16 * I + 15) continue;
-        const bf16x8 uh = *reinterpret_cast<const bf16x8*>(sUhi + l16 * PVT + 32 * s + 8 * lg);
-        const bf16x8 ul = *reinterpret_cast<const bf16x8*>(sUlo + l16 * PVT + 32 * s + 8 * lg);
-        oacc = mfma(cur.y0[s], uh, oacc);
-        ob = mfma(cur.y0[s], ul, ob);
-        ob = mfma(cur.y1[s], uh, ob);
-      }
-      float* op = ows + (((long long)b * T + c0) * H + h) * D + vb * NV + l16;
+      for (int j = 0; j < NCT; ++j) {
+        const int col = 16 * j + l16;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * I + 4 * lg + r;
-        if (t < L) op[(long long)t * HD] = oacc[r] + ob[r];
+        for (int s = 0; s < 2; ++s) {
+          if (32 * s > 16 * I + 15) continue;
+          const bf16x8 uh = *reinterpret_cast<const bf16x8*>(sUhi + col * PVT + 32 * s + 8 * lg);
+          const bf16x8 ul = *reinterpret_cast<const bf16x8*>(sUlo + col * PVT + 32 * s + 8 * lg);
+          oacc[j] = mfma(cur.y0[s], uh, oacc[j]);
+          ob[j] = mfma(cur.y0[s], ul, ob[j]);
+          ob[j] = mfma(cur.y1[s], uh, ob[j]);
+        }
+        float* op = ows + (((long long)b * T + c0) * H + h) * D + vb * NVB + col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * I + 4 * lg + r;
+          if (t < L) op[(long long)t * HD] = oacc[j][r] + ob[j][r];
+        }
       }
     }
-    {
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      const int col = 16 * j + l16;
       f32x4 sa, sb = zero4();
-      sa[0] = cur.gc.x * Sacc[0];
-      sa[1] = cur.gc.y * Sacc[1];
-      sa[2] = cur.gc.z * Sacc[2];
-      sa[3] = cur.gc.w * Sacc[3];
+      sa[0] = cur.gc.x * Sacc[j][0];
+      sa[1] = cur.gc.y * Sacc[j][1];
+      sa[2] = cur.gc.z * Sacc[j][2];
+      sa[3] = cur.gc.w * Sacc[j][3];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8 uh = *reinterpret_cast<const bf16x8*>(sUhi + l16 * PVT + 32 * s + 8 * lg);
-        const bf16x8 ul = *reinterpret_cast<const bf16x8*>(sUlo + l16 * PVT + 32 * s + 8 * lg);
+        const bf16x8 uh = *reinterpret_cast<const bf16x8*>(sUhi + col * PVT + 32 * s + 8 * lg);
+        const bf16x8 ul = *reinterpret_cast<const bf16x8*>(sUlo + col * PVT + 32 * s + 8 * lg);
         sa = mfma(cur.k0[s], uh, sa);
         sb = mfma(cur.k0[s], ul, sb);
         sb = mfma(cur.k1[s], uh, sb);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Sacc[r] = sa[r] + sb[r];
+      for (int r = 0; r < 4; ++r) Sacc[j][r] = sa[r] + sb[r];
     }
     __syncthreads();  // the old state operand has been read
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const __bf16 hi = (__bf16)Sacc[r];
-      sShi[l16 * PST + 16 * wave + 4 * lg + r] = hi;
-      sSlo[l16 * PST + 16 * wave + 4 * lg + r] = (__bf16)(Sacc[r] - (float)hi);
-    }
+    write_state_operand();
     if (ci + 1 < NC) {
       cur = nxt;
       rv_cur = rv_nxt;
@@ -723,9 +756,11 @@ __global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const 
   }
 
   {
-    float* sp = a.state_out + ((long long)b * H + h) * D * D + vb * NV + l16;
+    float* sp = a.state_out + ((long long)b * H + h) * D * D + vb * NVB + l16;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sp[(16 * wave + 4 * lg + r) * D] = Sacc[r];
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sp[(16 * wave + 4 * lg + r) * D + 16 * j] = Sacc[j][r];
   }
 }
 
