@@ -78,7 +78,8 @@ constexpr int OFF_GC = OFF_FAC + 4 * D * 4;           // e^(Gam_C) [128]
 constexpr int OFF_BETA = OFF_GC + D * 4;              // [64]
 constexpr int OFF_NRM = OFF_BETA + C * 4;             // q / k normalisers [2][64]
 constexpr int OFF_SEG = OFF_NRM + 2 * C * 4;          // cumulative-sum segment totals [4][128]
-constexpr int LDS_A = OFF_SEG + 4 * D * 4;
+constexpr int OFF_AQK = OFF_SEG + 4 * D * 4;           // A_qk [64][PA] (formed while T's columns are)
+constexpr int LDS_A = OFF_AQK + C * PA * 4;
 static_assert(STG_BYTES >= 2 * C * PA * 4 && STG_BYTES >= C * PQ * 4, "staging aliases");
 static_assert(LDS_A <= 160 * 1024, "LDS budget");
 
@@ -151,6 +152,16 @@ __device__ __forceinline__ void ld8(const float* p, float (&x)[8]) {
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+// fp32 matrix core step: D += A[16 x 4] B[4 x 16]; lane l holds A[l % 16][l / 16] and B[l / 16][l % 16]
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// Orders this wave's LDS writes before its later LDS reads (other waves are not waited for).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
 // Element offset of (row, k .. k+7) (k a multiple of 8) in the fragment-order layout of a
 // [rows][K] operand.
@@ -187,7 +198,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
   float* sGam = reinterpret_cast<float*>(smem + OFF_STG);
   float* sAkk = reinterpret_cast<float*>(smem + OFF_STG);
   float* sT = reinterpret_cast<float*>(smem + OFF_STG + C * PA * 4);
-  float* sAqk = sAkk;  // A_kk is dead once T is formed
+  float* sAqk = reinterpret_cast<float*>(smem + OFF_AQK);
   float* sTmp = reinterpret_cast<float*>(smem + OFF_TMP);
   float* sGn = reinterpret_cast<float*>(smem + OFF_GN);
   float* sEn = reinterpret_cast<float*>(smem + OFF_EN);
@@ -215,24 +226,18 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
   const bf16_t* __restrict__ cin = static_cast<const bf16_t*>(a.conv_in) + (long long)b * Cq * (W - 1);
   unsigned char* __restrict__ blk = ws + (((long long)b * H + h) * NC + ci) * (long long)CH_BYTES;
 
-  // ---- P1: stage raw q | k rows for tokens c0-3 .. c0+63 (bf16) ----
-  for (int idx = tid; idx < RROWS * 32; idx += NT) {
-    const int r = idx >> 5, sg = idx & 31;
-    const int tt = c0 - HALO + r;
-    const long long ch = sg < 16 ? (long long)h * D + sg * 8 : (long long)HD + h * D + (sg - 16) * 8;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (tt >= 0 && tt < T) {
-      v = *reinterpret_cast<const uint4*>(qkv + (long long)tt * Cq + ch);
-    } else if (tt < 0 && (W - 1) + tt >= 0) {
-      uint16_t e8[8];
+  // ---- P1: issue every global load of the chunk up front (addresses clamped into the sequence,
+  //      out-of-range rows replaced after the loads), then stage raw q | k rows for tokens
+  //      c0-3 .. c0+63 (bf16) ----
+  constexpr int NRAW = (RROWS * 32 + NT - 1) / NT;
+  uint4 raw[NRAW];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) e8[e] = cin[(ch + e) * (W - 1) + (W - 1) + tt];
-      v = make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16, e8[4] | (uint32_t)e8[5] << 16,
-                     e8[6] | (uint32_t)e8[7] << 16);
-    }
-    *reinterpret_cast<uint4*>(sRaw + r * PR + sg * 8) = v;
+  for (int s = 0; s < NRAW; ++s) {
+    const int r = min((tid + s * NT) >> 5, RROWS - 1), sg = tid & 31;
+    const int tt = min(max(c0 - HALO + r, 0), T - 1);
+    const long long ch = sg < 16 ? (long long)h * D + sg * 8 : (long long)HD + h * D + (sg - 16) * 8;
+    raw[s] = *reinterpret_cast<const uint4*>(qkv + (long long)tt * Cq + ch);
   }
-  if (tid < C) sBeta[tid] = tid < L ? to_f32(bin[(long long)(c0 + tid) * H]) : 0.f;
   // conv taps of this lane's q/k channel, zero-padded on the left to 4 taps
   const int cq = tid & 255;
   const long long gqk = cq < D ? (long long)h * D + cq : (long long)HD + h * D + (cq - D);
@@ -240,8 +245,43 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int w = j - (4 - W);
-    tq[j] = w >= 0 ? to_f32(cw[gqk * W + w]) : 0.f;
+    const float tv = to_f32(cw[gqk * W + max(w, 0)]);
+    tq[j] = w >= 0 ? tv : 0.f;
   }
+  const float bval = to_f32(bin[(long long)min(c0 + (tid & 63), T - 1) * H]);
+  // gate inputs: lane -> channel tid % 128, tokens 16 * (tid / 128) .. +15
+  const float alog = a.A_log[h];
+  const float dtb = a.dt_bias[h * D + (tid & 127)];
+  bf16_t fraw[16];
+  {
+    const int i = tid & 127, seg = tid >> 7;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) fraw[k] = fin[(long long)min(c0 + 16 * seg + k, T - 1) * HD + i];
+  }
+#pragma unroll
+  for (int s = 0; s < NRAW; ++s) {
+    const int idx = tid + s * NT;
+    if (idx < RROWS * 32) {
+      const int r = idx >> 5, sg = idx & 31;
+      const int tt = c0 - HALO + r;
+      *reinterpret_cast<uint4*>(sRaw + r * PR + sg * 8) = (tt >= 0 && tt < T) ? raw[s] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  if (ci == 0 && tid < HALO * 32) {
+    // rows before the sequence start come from the conv state (the same lane wrote them as zeros)
+    const int r = tid >> 5, sg = tid & 31;
+    const int tt = r - HALO;
+    if ((W - 1) + tt >= 0) {
+      const long long ch = sg < 16 ? (long long)h * D + sg * 8 : (long long)HD + h * D + (sg - 16) * 8;
+      uint16_t e8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) e8[e] = cin[(ch + e) * (W - 1) + (W - 1) + tt];
+      *reinterpret_cast<uint4*>(sRaw + r * PR + sg * 8) =
+          make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16, e8[4] | (uint32_t)e8[5] << 16,
+                     e8[6] | (uint32_t)e8[7] << 16);
+    }
+  }
+  if (tid < C) sBeta[tid] = tid < L ? bval : 0.f;
   __syncthreads();
 
   // ---- P2: causal conv + SiLU over q|k: lane -> channel cq, 32 tokens ----
@@ -264,29 +304,35 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
   // ---- P3: bounded-sigmoid gate and its cumulative sum (lane -> channel, 16-token segment) ----
   {
     const int i = tid & 127, seg = tid >> 7;
-    const float Ah = __expf(a.A_log[h]);
-    const float dtb = a.dt_bias[h * D + i];
+    const float Ah = __expf(alog);
     float gl[16];
     float acc = 0.f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const int t = 16 * seg + k;
-      float g = 0.f;
-      if (t < L) {
-        const float fv = to_f32(fin[(long long)(c0 + t) * HD + i]) + dtb;
-        g = a.lb * __builtin_amdgcn_rcpf(1.0f + __expf(-Ah * fv));
-      }
-      acc += g;
+      const float fv = to_f32(fraw[k]) + dtb;
+      const float g = a.lb * __builtin_amdgcn_rcpf(1.0f + __expf(-Ah * fv));
+      acc += 16 * seg + k < L ? g : 0.f;
       gl[k] = acc;
     }
     sSeg[seg * D + i] = acc;
-    // ---- P4 (same phase): q / k L2 normalisers, one wave per 8 tokens ----
-    for (int t = wave * 8; t < wave * 8 + 8; ++t) {
-      const float q0 = sQ[t * PQ + lane], q1 = sQ[t * PQ + lane + 64];
-      const float k0 = sG[t * PQ + lane], k1 = sG[t * PQ + lane + 64];
-      const float qq = wave_sum(q0 * q0 + q1 * q1);
-      const float kk = wave_sum(k0 * k0 + k1 * k1);
-      if (lane == 0) {
+    // ---- P4 (same phase): q / k L2 normalisers: eight lanes per token, 16 channels each ----
+    {
+      const int t = tid >> 3, p = tid & 7;
+      const float4* qp = reinterpret_cast<const float4*>(sQ + t * PQ + 16 * p);
+      const float4* kp = reinterpret_cast<const float4*>(sG + t * PQ + 16 * p);
+      float qq = 0.f, kk = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float4 x = qp[e], y = kp[e];
+        qq += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+        kk += y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
+      }
+#pragma unroll
+      for (int o = 4; o > 0; o >>= 1) {
+        qq += __shfl_xor(qq, o, 64);
+        kk += __shfl_xor(kk, o, 64);
+      }
+      if (p == 0) {
         sNrm[t] = a.scale / fmaxf(sqrtf(qq), a.l2_eps);
         sNrm[C + t] = 1.0f / fmaxf(sqrtf(kk), a.l2_eps);
       }
@@ -378,50 +424,52 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
     }
   }
   __syncthreads();
-  // off-diagonal blocks by distance d: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ
-  for (int d = 1; d < 4; ++d) {
-    const int nb = 4 - d;
-    for (int idx = tid; idx < nb * 256; idx += NT) {
-      const int J = idx >> 8, i = (idx >> 4) & 15, jj = idx & 15, I = J + d;
-      float m = 0.f;
+  // Off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, column block J = wave (0..2)
+  // top to bottom on the fp32 matrix cores, while waves 3-7 form A_qk.
+  if (wave < 3) {
+    const int J = wave;
+    float* sM = sTmp + wave * 16 * 17;
+    for (int I = J + 1; I < 4; ++I) {
+      f32x4 m = zero4();
       for (int K = J; K < I; ++K)
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) m += sAkk[(16 * I + i) * PA + 16 * K + kk] * sT[(16 * K + kk) * PA + 16 * J + jj];
-      sTmp[idx] = m;
+        for (int s = 0; s < 4; ++s)
+          m = mfma_f32(sAkk[(16 * I + l16) * PA + 16 * K + 4 * s + lg], sT[(16 * K + 4 * s + lg) * PA + 16 * J + l16], m);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sM[(4 * lg + r) * 17 + l16] = m[r];
+      wave_lds_sync();
+      f32x4 tij = zero4();
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        tij = mfma_f32(sT[(16 * I + l16) * PA + 16 * I + 4 * s + lg], sM[(4 * s + lg) * 17 + l16], tij);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * lg + r) * PA + 16 * J + l16] = -tij[r];
+      wave_lds_sync();
     }
-    __syncthreads();
-    for (int idx = tid; idx < nb * 256; idx += NT) {
-      const int J = idx >> 8, i = (idx >> 4) & 15, jj = idx & 15, I = J + d;
-      float m = 0.f;
+  } else {
+    // ---- P6b: A_qk = QR_I E_IJ . KC_J^T (split bf16), lower incl. diagonal ----
+    for (int bi = wave - 3; bi < 10; bi += 5) {
+      int I, J;
+      block_ij(bi, I, J);
+      f32x4 acc = zero4();
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk)
-        if (kk <= i) m += sT[(16 * I + i) * PA + 16 * I + kk] * sTmp[(J << 8) + (kk << 4) + jj];
-      sT[(16 * I + i) * PA + 16 * J + jj] = -m;
-    }
-    __syncthreads();
-  }
-
-  // ---- P6b: A_qk = QR_I E_IJ . KC_J^T (split bf16), lower incl. diagonal ----
-  for (int bi = wave; bi < 10; bi += 8) {
-    int I, J;
-    block_ij(bi, I, J);
-    f32x4 acc = zero4();
+      for (int s = 0; s < 4; ++s) {
+        const int c = 32 * s + 8 * lg;
+        float qv[8], kc[8];
+        ld8(sQ + (16 * I + l16) * PQ + c, qv);
+        if (I > J) {
+          const float* ef = sE + pair_index(I, J) * D + c;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int c = 32 * s + 8 * lg;
-      float qv[8], kc[8];
-      ld8(sQ + (16 * I + l16) * PQ + c, qv);
-      if (I > J) {
-        const float* ef = sE + pair_index(I, J) * D + c;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qv[e] *= ef[e];
+          for (int e = 0; e < 8; ++e) qv[e] *= ef[e];
+        }
+        ld8(sG + (16 * J + l16) * PQ + c, kc);
+        acc = mfma3(split(qv), split(kc), acc);
       }
-      ld8(sG + (16 * J + l16) * PQ + c, kc);
-      acc = mfma3(split(qv), split(kc), acc);
-    }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sAqk[(16 * I + 4 * lg + r) * PA + 16 * J + l16] = acc[r];
+      for (int r = 0; r < 4; ++r) sAqk[(16 * I + 4 * lg + r) * PA + 16 * J + l16] = acc[r];
+    }
   }
+  __syncthreads();
 
   // ---- P8: W = T . (beta KR e^Gam_n) (plain bf16); wave -> 16 key channels ----
   f32x4 wacc[4] = {zero4(), zero4(), zero4(), zero4()};
