@@ -104,9 +104,8 @@ static_assert(CH_BYTES % 256 == 0, "tile blocks stay 256-byte aligned");
 constexpr int PRV = NVB + 8;               // bf16 pitch of the staged raw v rows
 constexpr int PVT = 72;                    // bf16 pitch of [NVB][64] token-major operands
 constexpr int PST = 136;                   // bf16 pitch of the [NVB][128] state operand
-constexpr int B_RAWV = 0;
-constexpr int B_BETA = B_RAWV + RROWS * PRV * 2;
-constexpr int B_VHI = B_BETA + C * 4;
+constexpr int B_RAWV = 0;                  // RROWS raw v rows + one spare row
+constexpr int B_VHI = B_RAWV + (RROWS + 1) * PRV * 2;
 constexpr int B_VLO = B_VHI + NVB * PVT * 2;
 constexpr int B_UHI = B_VLO + NVB * PVT * 2;
 constexpr int B_ULO = B_UHI + NVB * PVT * 2;
@@ -557,21 +556,22 @@ struct OpTiles {        // this lane's operand fragments of one chunk
 };
 
 // Every field is filled by one fixed sequence of fragment loads (only the source tiles differ by
-// role), so the fields stay in registers.  Waves 0-3 leave x1 unloaded.
+// role), so the fields stay in registers and every wave issues the same loads.
 __device__ __forceinline__ void load_tiles(const unsigned char* blk, int wave, int lane, int lg, OpTiles& o) {
   const int I = wave & 3;
   const bool u_role = wave < 4;
   const bf16x8* x0p = reinterpret_cast<const bf16x8*>(blk + (u_role ? W_W : W_QHI)) + (I * 4) * 64 + lane;
-  const bf16x8* x1p = reinterpret_cast<const bf16x8*>(blk + W_QLO) + (I * 4) * 64 + lane;
+  // waves 0-3 have no second x operand: they re-read their W fragments, so every wave issues
+  // the same loads without a branch
+  const bf16x8* x1p = u_role ? x0p : reinterpret_cast<const bf16x8*>(blk + W_QLO) + (I * 4) * 64 + lane;
   const bf16x8* y0p = reinterpret_cast<const bf16x8*>(blk + (u_role ? W_THI : W_AHI)) + (I * 2) * 64 + lane;
   const bf16x8* y1p = reinterpret_cast<const bf16x8*>(blk + (u_role ? W_TLO : W_ALO)) + (I * 2) * 64 + lane;
   const bf16x8* khp = reinterpret_cast<const bf16x8*>(blk + W_KTHI) + (wave * 2) * 64 + lane;
   const bf16x8* klp = reinterpret_cast<const bf16x8*>(blk + W_KTLO) + (wave * 2) * 64 + lane;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) o.x0[s] = x0p[s * 64];
-  if (!u_role) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) o.x1[s] = x1p[s * 64];
+  for (int s = 0; s < 4; ++s) {
+    o.x0[s] = x0p[s * 64];
+    o.x1[s] = x1p[s * 64];
   }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -589,7 +589,6 @@ __global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const 
   constexpr int NCT = NVB / 16;  // column tiles
   extern __shared__ __align__(16) unsigned char smem[];
   __bf16* sRawV = reinterpret_cast<__bf16*>(smem + B_RAWV);
-  float* sBeta = reinterpret_cast<float*>(smem + B_BETA);
   __bf16* sVhi = reinterpret_cast<__bf16*>(smem + B_VHI);
   __bf16* sVlo = reinterpret_cast<__bf16*>(smem + B_VLO);
   __bf16* sUhi = reinterpret_cast<__bf16*>(smem + B_UHI);
@@ -644,45 +643,78 @@ __global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const 
     }
   }
 
-  // raw v rows of one chunk: lane task = (row r, 8-channel segment) for r < RROWS
+  // Raw v rows of one chunk: lane task = (row r, 8-channel segment); lanes past the last row
+  // stage a spare row.  beta of the two tokens this lane converts in B2.  The loads have no
+  // branches (addresses clamped into the sequence) and their registers are consumed by every
+  // lane, so nothing waits for a prefetch before its data is needed.
   constexpr int SEGS = NVB / 8;
-  auto load_rawv = [&](int cidx, uint4& v, float& beta) {
-    v = make_uint4(0u, 0u, 0u, 0u);
-    beta = 0.f;
+  const int rv_r = min(tid / SEGS, RROWS), rv_sg = tid % SEGS;
+  auto load_rawv = [&](int cidx, uint4& v, bf16_t (&bt)[2]) {
     const int c0 = cidx * C;
-    if (tid < RROWS * SEGS) {
-      const int r = tid / SEGS, sg = tid % SEGS;
-      const int tt = c0 - HALO + r;
-      const long long ch = vch + 8 * sg;
-      if (tt >= 0 && tt < T) {
-        v = *reinterpret_cast<const uint4*>(qkv + (long long)tt * Cq + ch);
-      } else if (tt < 0 && (W - 1) + tt >= 0) {
+    const int tt = min(max(c0 - HALO + rv_r, 0), T - 1);
+    v = *reinterpret_cast<const uint4*>(qkv + (long long)tt * Cq + vch + 8 * rv_sg);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) bt[i] = bin[(long long)min(c0 + tid / NVB + (NT / NVB) * i, T - 1) * H];
+  };
+  static_assert(C * NVB / NT == 2, "two tokens per lane in B2");
+
+  // Output rows of the previous chunk, held in registers until the next chunk has started so
+  // that their stores are issued before that chunk's prefetch.
+  f32x4 opend[NCT];
+  auto store_pending = [&](int pc) {
+    if (pc < 0 || wave < 4) return;
+    const int pc0 = pc * C, pL = min(C, T - pc0);
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      float* op = ows + (((long long)b * T + pc0) * H + h) * D + vb * NVB + 16 * j + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * (wave - 4) + 4 * lg + r;
+        if (t < pL) op[(long long)t * HD] = opend[j][r];
+      }
+    }
+  };
+
+  // One chunk: operands in (cur, rv_cur, be_cur), the next chunk's prefetched into (nxt, ...).
+  // Two register sets alternate between the roles, so no loaded value is ever copied.
+  auto chunk = [&](int ci, const OpTiles& cur, const uint4& rv_cur, const bf16_t (&be_cur)[2], OpTiles& nxt,
+                   uint4& rv_nxt, bf16_t (&be_nxt)[2]) __attribute__((always_inline)) {
+    const int c0 = ci * C;
+    const int L = min(C, T - c0);
+    // B1: this chunk's prefetched raw v rows into LDS and its beta into registers (every lane,
+    // no branches), then the previous chunk's output rows are stored and the next chunk's loads
+    // issued, in that order: a wait for a prefetched value then never waits for a store.
+    float bt[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      bt[i] = to_f32(be_cur[i]);
+      asm volatile("" : "+v"(bt[i]));  // keep the conversion (and its wait) ahead of the stores
+    }
+    {
+      const int tt = c0 - HALO + rv_r;
+      const uint32_t m = ((tt >= 0) & (tt < T)) ? 0xffffffffu : 0u;
+      *reinterpret_cast<uint4*>(sRawV + rv_r * PRV + 8 * rv_sg) =
+          make_uint4(rv_cur.x & m, rv_cur.y & m, rv_cur.z & m, rv_cur.w & m);
+    }
+    if (ci == 0 && W > 1 && tid < HALO * SEGS) {
+      // rows before the sequence start come from the conv state (the same lane wrote them as zeros)
+      const int tt = rv_r - HALO;
+      if ((W - 1) + tt >= 0) {
+        const long long ch = vch + 8 * rv_sg;
         uint16_t e8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) e8[e] = cin[(ch + e) * (W - 1) + (W - 1) + tt];
-        v = make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16, e8[4] | (uint32_t)e8[5] << 16,
+        *reinterpret_cast<uint4*>(sRawV + rv_r * PRV + 8 * rv_sg) =
+            make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16, e8[4] | (uint32_t)e8[5] << 16,
                        e8[6] | (uint32_t)e8[7] << 16);
       }
     }
-    if (tid >= 448 && c0 + tid - 448 < T) beta = to_f32(bin[(long long)(c0 + tid - 448) * H]);
-  };
-
-  OpTiles cur, nxt;
-  uint4 rv_cur, rv_nxt;
-  float be_cur, be_nxt;
-  load_tiles(head_ws, wave, lane, lg, cur);
-  load_rawv(0, rv_cur, be_cur);
-  write_state_operand();
-
-  for (int ci = 0; ci < NC; ++ci) {
-    const int c0 = ci * C;
-    const int L = min(C, T - c0);
-    // B1: this chunk's raw v rows and beta into LDS; then issue the next chunk's loads
-    if (tid < RROWS * SEGS) *reinterpret_cast<uint4*>(sRawV + (tid / SEGS) * PRV + 8 * (tid % SEGS)) = rv_cur;
-    if (tid >= 448) sBeta[tid - 448] = be_cur;
-    if (ci + 1 < NC) {
-      load_tiles(head_ws + (long long)(ci + 1) * CH_BYTES, wave, lane, lg, nxt);
-      load_rawv(ci + 1, rv_nxt, be_nxt);
+    store_pending(ci - 1);
+    {
+      // the last chunk prefetches itself again: the loads stay unconditional
+      const int cn = min(ci + 1, NC - 1);
+      load_tiles(head_ws + (long long)cn * CH_BYTES, wave, lane, lg, nxt);
+      load_rawv(cn, rv_nxt, be_nxt);
     }
     __syncthreads();
     // B2: conv + SiLU of the v block, times beta, as the split B operand [col][token]
@@ -693,7 +725,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const 
         const __bf16* vc = sRawV + vj;
         const float y = tv[0] * (float)vc[t * PRV] + tv[1] * (float)vc[(t + 1) * PRV] +
                         tv[2] * (float)vc[(t + 2) * PRV] + tv[3] * (float)vc[(t + 3) * PRV];
-        const float x = t < L ? sBeta[t] * silu_fast(y) : 0.f;
+        const float xv = bt[i] * silu_fast(y);
+        const float x = t < L ? xv : 0.f;
         const __bf16 hi = (__bf16)x;
         sVhi[vj * PVT + t] = hi;
         sVlo[vj * PVT + t] = (__bf16)(x - (float)hi);
@@ -767,12 +800,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const 
           ob[j] = mfma(cur.y0[s], ul, ob[j]);
           ob[j] = mfma(cur.y1[s], uh, ob[j]);
         }
-        float* op = ows + (((long long)b * T + c0) * H + h) * D + vb * NVB + col;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * I + 4 * lg + r;
-          if (t < L) op[(long long)t * HD] = oacc[j][r] + ob[j][r];
-        }
+        for (int r = 0; r < 4; ++r) opend[j][r] = oacc[j][r] + ob[j][r];
       }
     }
 #pragma unroll
@@ -796,12 +825,21 @@ __global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const 
     }
     __syncthreads();  // the old state operand has been read
     write_state_operand();
-    if (ci + 1 < NC) {
-      cur = nxt;
-      rv_cur = rv_nxt;
-      be_cur = be_nxt;
-    }
+  };
+
+  OpTiles ta, tb;
+  uint4 rva, rvb;
+  bf16_t bea[2], beb[2];
+  load_tiles(head_ws, wave, lane, lg, ta);
+  load_rawv(0, rva, bea);
+  write_state_operand();
+  int ci = 0;
+  for (; ci + 1 < NC; ci += 2) {
+    chunk(ci, ta, rva, bea, tb, rvb, beb);
+    chunk(ci + 1, tb, rvb, beb, ta, rva, bea);
   }
+  if (ci < NC) chunk(ci, ta, rva, bea, tb, rvb, beb);
+  store_pending(NC - 1);
 
   {
     float* sp = a.state_out + ((long long)b * H + h) * D * D + vb * NVB + l16;
