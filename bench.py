@@ -63,6 +63,110 @@ def rollback_bytes(accepted, H, D, W, io_b=2):
     return n * (2 * H * D * D * 4 + 2 * 3 * H * D * (W - 1) * io_b) + sum(int(m) for m in accepted) * 0
 
 
+def kernel_alg_bytes(kernel, wp, wd, wv, accepted):
+    """Algorithmic bytes of one launch of each kernel: what the launch must read and write once,
+    with the prefill call's bytes split over its four kernels (their sum is prefill_bytes)."""
+    io_b = 2
+    Hp, Dp, Wp, Tp = wp.H, wp.dk, wp.W, wp.T
+    params = 3 * Hp * Dp * Wp * io_b + Hp * 4 + Hp * Dp * 4
+    conv = 3 * Hp * Dp * (Wp - 1) * io_b
+    table = {
+        # qkv, f, beta of every token, the conv state in, conv weights, A_log, dt_bias
+        "kda_chunk_prep_kernel": Tp * (3 * Hp * Dp * io_b + Hp * Dp * io_b + Hp * io_b) + conv + params,
+        # fp32 state in and out
+        "kda_chunk_state_kernel": 2 * Hp * Dp * Dp * 4,
+        # g_out in, out written, norm weight
+        "kda_out_norm_kernel": Tp * 2 * Hp * Dp * io_b + Dp * io_b,
+        # conv state out
+        "kda_conv_state_kernel": conv,
+        "kda_recurrent_kernel[decode]": decode_bytes(wd.B, wd.H, wd.dk, wd.W),
+        "kda_recurrent_kernel[verify]": verify_bytes(wv.B, wv.T, wv.H, wv.dk, wv.W),
+        "kda_rollback_kernel": rollback_bytes(accepted or [], wv.H, wv.dk, wv.W),
+    }
+    return table.get(kernel)
+
+
+def source_fingerprint():
+    """sha256 over the HIP sources and headers of the library: counter-derived traffic is only
+    reported while the kernels are the ones it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "hybrid_linear_attention_kda_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+CALIB_BYTES = 384 << 20  # the plain copy kernel of --calib-copy reads and writes this many bytes
+
+
+def stored_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter runs, or None when there are
+    none for it or the sources changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    if rec.get("source_sha256") != source_fingerprint():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if k is None:
+        return None
+    return k["fetch_bytes"] + k["write_bytes"]
+
+
+def short_kernel_name(full):
+    import re
+    m = re.search(r"(kda_[a-z_]+_kernel)(<[^>]*>)?", full)
+    if m is None:
+        return None
+    name = m.group(1)
+    if name == "kda_recurrent_kernel" and m.group(2):
+        name += "[verify]" if ", true," in m.group(2) else "[decode]"
+    return name
+
+
+def pmc_summary(fetch_dir, write_dir, command):
+    """Scale the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of two rocprofv3 --pmc runs
+    of `bench.py ... --calib-copy` by what they read for the plain copy kernel of CALIB_BYTES,
+    and store bytes per launch per kernel in profiles/pmc_traffic.json."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        acc = {}
+        calib = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"]) * 1024.0
+                name = short_kernel_name(r["Kernel_Name"])
+                if name is not None:
+                    acc.setdefault(name, []).append(v)
+                elif "neg" in r["Kernel_Name"].lower() or "elementwise" in r["Kernel_Name"]:
+                    calib.append(v)
+        return acc, calib
+
+    fetch, fcal = per_kernel(fetch_dir, "FETCH_SIZE")
+    write, wcal = per_kernel(write_dir, "WRITE_SIZE")
+    # the calibration copy is the elementwise launch that moved about CALIB_BYTES
+    fc = max(fcal) / CALIB_BYTES
+    wc = max(wcal) / CALIB_BYTES
+    out = {"command": command, "source_sha256": source_fingerprint(),
+           "calibration": {"copy_bytes": CALIB_BYTES, "fetch_factor": fc, "write_factor": wc},
+           "kernels": {}}
+    for k in sorted(set(fetch) | set(write)):
+        f = float(np.mean(fetch.get(k, [0.0]))) / fc
+        w = float(np.mean(write.get(k, [0.0]))) / wc
+        out["kernels"][k] = {"fetch_bytes": f, "write_bytes": w, "dispatches": len(fetch.get(k, []))}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def cpu_baseline(sample_heads: int, T: int):
     """The float64 oracle, as it stands, on a bounded sample of the prefill workload:
     `sample_heads` of the 32 heads over T tokens (heads are independent, so the
@@ -97,8 +201,15 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode", "verify"], default=None,
                     help="time one call type only (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after the timed steps, run one plain copy kernel of known size (for counter scaling)")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
+                    help="turn two rocprofv3 --pmc runs into profiles/pmc_traffic.json and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer shards by head with "
               f"no communication, so per-GPU throughput at N GPUs is the single-GPU figure at H/N heads.",
@@ -139,20 +250,24 @@ def main():
                 ws=workspace(lay, 1, wp.T)))
         del tok
 
-    def prefilled(wl, inp, lay):
-        pre = TT.token_tensors(wl, inp, 0, wl.prefix_T, dev)
+    def prefilled(wl, inp):
+        # The prefix runs through the fp32-io prefill (its own kernel, the inputs are bf16 values
+        # held exactly in fp32), so the timed kernels' launches are all of the timed shapes.
+        w32 = wl.with_(io="f32")
+        lay32 = TT.make_layer(w32, inp, dev, out="f32")
+        pre = TT.token_tensors(w32, inp, 0, wl.prefix_T, dev)
         st = torch.zeros((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
-        cs = torch.zeros((wl.B, wl.c_qkv, wl.W - 1), dtype=torch.bfloat16, device=dev)
-        o = torch.empty((wl.B, wl.prefix_T, wl.H * wl.dv), dtype=torch.bfloat16, device=dev)
-        abi.kda_prefill(lay, pre["qkv"], pre["f"], pre["beta"], pre["g_out"], st, cs, o,
-                        workspace=workspace(lay, wl.B, wl.prefix_T))
+        cs = torch.zeros((wl.B, wl.c_qkv, wl.W - 1), dtype=torch.float32, device=dev)
+        o = torch.empty((wl.B, wl.prefix_T, wl.H * wl.dv), dtype=torch.float32, device=dev)
+        abi.kda_prefill(lay32, pre["qkv"], pre["f"], pre["beta"], pre["g_out"], st, cs, o,
+                        workspace=workspace(lay32, wl.B, wl.prefix_T))
         torch.cuda.synchronize()
-        return st, cs
+        return st, cs.to(torch.bfloat16)
 
     if "decode" in ops:
         inp = I.generate(wd)
         lay = TT.make_layer(wd, inp, dev, out="bf16")
-        st, cs = prefilled(wd, inp, lay)
+        st, cs = prefilled(wd, inp)
         tok = TT.token_tensors(wd, inp, wd.prefix_T, wd.prefix_T + 1, dev)
         for _ in range(nsets):
             sets["decode"].append(dict(layer=lay, tok={k: v.clone() for k, v in tok.items()}, state=st.clone(),
@@ -164,7 +279,7 @@ def main():
         inp = I.generate(wv)
         accepted = [int(m) for m in inp["accepted"]]
         lay = TT.make_layer(wv, inp, dev, out="bf16")
-        st, cs = prefilled(wv, inp, lay)
+        st, cs = prefilled(wv, inp)
         tok = TT.token_tensors(wv, inp, wv.prefix_T, wv.prefix_T + wv.T, dev)
         for _ in range(nsets):
             sets["verify"].append(dict(
@@ -203,26 +318,35 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = {op: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-          for op in seq}
+    # each call type runs K times back to back between one event pair, so the queue never drains
+    ev = {op: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for op in seq}
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    abi.timing_enable(True)  # an event pair around every kernel of the timed steps
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for i in range(K):
-        for op in seq:
-            e0, e1 = ev[op][i]
-            e0.record(stream)
+    for op in seq:
+        e0, e1 = ev[op]
+        e0.record(stream)
+        for i in range(K):
             run(op, sets[setof(op)][i % nsets])
-            e1.record(stream)
+        e1.record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    abi.timing_enable(False)
+    kernel_ms = {}
+    for name, t in abi.timing_read():
+        kernel_ms.setdefault(name, []).append(t)
+    if args.calib_copy:
+        src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     ms_total = t_start.elapsed_time(t_end)
-    ms = {op: np.array([a.elapsed_time(b) for a, b in ev[op]]) for op in seq}
-    mean = {op: float(ms[op].mean()) for op in seq}
-    med = {op: float(np.median(ms[op])) for op in seq}
+    mean = {op: ev[op][0].elapsed_time(ev[op][1]) / K for op in seq}
 
     res = {
         "metric": "KDA prefill tokens/s (H=32,128x128,T=4096) + decode state-update HBM GB/s",
@@ -235,43 +359,47 @@ def main():
         "wall_s": wall,
     }
     detail = {}
-    roof_candidates = []
     if "prefill" in ops:
         pb = prefill_bytes(1, wp.T, wp.H, wp.dk, wp.W)
         res["value"] = wp.T / (mean["prefill"] * 1e-3)
         res["unit"] = "tokens/s"
-        detail["prefill"] = {"ms_mean": mean["prefill"], "ms_median": med["prefill"],
-                             "ms_p10": float(np.percentile(ms["prefill"], 10)),
-                             "ms_p90": float(np.percentile(ms["prefill"], 90)),
-                             "tokens_per_s": res["value"], "alg_bytes": pb,
+        detail["prefill"] = {"ms_mean": mean["prefill"], "tokens_per_s": res["value"], "alg_bytes": pb,
                              "gbps": pb / (mean["prefill"] * 1e-3) / 1e9}
-        roof_candidates.append(("prefill", mean["prefill"], pb))
     if "decode" in ops:
         db = decode_bytes(wd.B, wd.H, wd.dk, wd.W)
         gb = db / (mean["decode"] * 1e-3) / 1e9
         res["decode_state_update_gbps"] = gb
-        detail["decode"] = {"ms_mean": mean["decode"], "ms_median": med["decode"], "alg_bytes": db, "gbps": gb,
+        detail["decode"] = {"ms_mean": mean["decode"], "alg_bytes": db, "gbps": gb,
                             "hbm_frac": gb / HBM_PEAK_GBPS}
-        roof_candidates.append(("decode", mean["decode"], db))
         if "value" not in res:
             res["value"], res["unit"] = gb, "GB/s"
     if "verify" in ops:
         vb = verify_bytes(wv.B, wv.T, wv.H, wv.dk, wv.W)
         rb = rollback_bytes(accepted, wv.H, wv.dk, wv.W)
         gv = vb / (mean["verify"] * 1e-3) / 1e9
-        detail["verify"] = {"ms_mean": mean["verify"], "ms_median": med["verify"], "alg_bytes": vb, "gbps": gv,
+        detail["verify"] = {"ms_mean": mean["verify"], "alg_bytes": vb, "gbps": gv,
                             "hbm_frac": gv / HBM_PEAK_GBPS}
         detail["rollback"] = {"ms_mean": mean["rollback"], "alg_bytes": rb,
                               "gbps": rb / (mean["rollback"] * 1e-3) / 1e9, "accepted": accepted}
-        roof_candidates.append(("verify", mean["verify"], vb))
         if "value" not in res:
             res["value"], res["unit"] = gv, "GB/s"
+    # per kernel: average launch duration from the library's event pairs over the timed steps
+    kern = {}
+    for name, ts in kernel_ms.items():
+        avg = float(np.mean(ts))
+        nb = kernel_alg_bytes(name, wp, wd, wv, accepted)
+        kern[name] = {"ms_mean": avg, "ms_p10": float(np.percentile(ts, 10)), "ms_p90": float(np.percentile(ts, 90)),
+                      "launches_per_step": len(ts) / K, "alg_bytes": nb,
+                      "gbps": (nb / (avg * 1e-3) / 1e9) if nb else None}
+    detail["kernels"] = kern
     res["detail"] = detail
-    # dominant kernel: the call with the largest share of the step
-    name, t_ms, nbytes = max(roof_candidates, key=lambda c: c[1])
-    achieved = nbytes / (t_ms * 1e-3) / 1e9
+    # dominant kernel: the largest share of the step
+    name = max(kern, key=lambda n: kern[n]["ms_mean"] * kern[n]["launches_per_step"])
+    k = kern[name]
+    achieved = k["gbps"]
     res["roofline"] = {"kernel": name, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                       "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None}
+                       "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": stored_traffic(name),
+                       "alg_bytes_per_launch": k["alg_bytes"], "ms_per_launch": k["ms_mean"]}
     if not args.no_cpu_baseline and "prefill" in ops:
         log("timing the oracle on the host ...")
         res["cpu_baseline"] = cpu_baseline(args.cpu_heads, wp.T)

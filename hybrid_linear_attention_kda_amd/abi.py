@@ -65,6 +65,8 @@ def load() -> ctypes.CDLL:
         "kda_decode_step": (c_int32, [D, c_int32, P, P, P, P, P, P, P, P]),
         "kda_verify_block": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P, P, P, P]),
         "kda_rollback": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P]),
+        "kda_timing_enable": (c_int32, [c_int32]),
+        "kda_timing_read": (c_int32, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(c_float), c_int32]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -222,3 +224,19 @@ def kda_rollback(layer: KdaLayer, accepted, snaps, qkv_block, state, conv_state,
     _check_state(layer, B, state, conv_state)
     _check(load().kda_rollback(ctypes.byref(layer.desc), B, T_d, ctypes.cast(acc, c_void_p), _ptr(snaps),
                                _ptr(qkv_block), _ptr(state), _ptr(conv_state), _stream(stream)))
+
+
+def timing_enable(on: bool) -> bool:
+    """Per-kernel timing of later calls on this thread (kda_timing_enable); returns the old setting."""
+    return bool(load().kda_timing_enable(1 if on else 0))
+
+
+def timing_read(cap: int = 1 << 16) -> list:
+    """(kernel name, milliseconds) of every kernel launched since timing was enabled or last read,
+    in launch order (kda_timing_read); waits for those kernels."""
+    names = (ctypes.c_char_p * cap)()
+    ms = (c_float * cap)()
+    n = load().kda_timing_read(names, ms, cap)
+    if n < 0:
+        raise KdaError(KDA_ERR_HIP, load().kda_last_error().decode())
+    return [(names[i].decode(), float(ms[i])) for i in range(min(n, cap))]

@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <vector>
 
 #include "kda_launch.h"
 
@@ -274,6 +275,77 @@ kda_status kda_rollback(const kda_layer_desc* desc, int32_t B, int32_t T_d, cons
     if (st != KDA_OK) return st;
   }
   return ok();
+}
+
+}  // extern "C"
+
+// ---- per-kernel timing ------------------------------------------------------------------------
+
+namespace {
+struct TimingRecord {
+  const char* kernel;
+  hipEvent_t start, stop;
+};
+thread_local bool g_timing = false;
+thread_local std::vector<TimingRecord> g_records;
+thread_local std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pooled_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+namespace kda {
+void timing_begin(const char* kernel, hipStream_t s) {
+  if (!g_timing) return;
+  TimingRecord r{kernel, pooled_event(), pooled_event()};
+  if (r.start != nullptr) (void)hipEventRecord(r.start, s);
+  g_records.push_back(r);
+}
+void timing_end(hipStream_t s) {
+  if (!g_timing || g_records.empty()) return;
+  if (g_records.back().stop != nullptr) (void)hipEventRecord(g_records.back().stop, s);
+}
+}  // namespace kda
+
+extern "C" {
+
+int32_t kda_timing_enable(int32_t on) {
+  const int32_t prev = g_timing ? 1 : 0;
+  g_timing = on != 0;
+  return prev;
+}
+
+int32_t kda_timing_read(const char** names, float* ms, int32_t cap) {
+  int32_t n = 0;
+  bool failed = false;
+  for (const TimingRecord& r : g_records) {
+    float t = -1.0f;
+    if (r.start == nullptr || r.stop == nullptr || hipEventSynchronize(r.stop) != hipSuccess ||
+        hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess) {
+      failed = true;
+    }
+    if (n < cap) {
+      if (names != nullptr) names[n] = r.kernel;
+      if (ms != nullptr) ms[n] = t;
+    }
+    ++n;
+    if (r.start != nullptr) g_event_pool.push_back(r.start);
+    if (r.stop != nullptr) g_event_pool.push_back(r.stop);
+  }
+  g_records.clear();
+  if (failed) {
+    fail(KDA_ERR_HIP, "kda_timing_read: a timing event could not be created, recorded or read");
+    return -1;
+  }
+  return n;
 }
 
 }  // extern "C"

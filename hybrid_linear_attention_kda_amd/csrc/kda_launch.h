@@ -42,6 +42,11 @@ struct RollbackArgs {
   uint8_t accepted[kRollbackBatch];
 };
 
+// Per-kernel timing (kda_timing_enable): the launch functions bracket each kernel launch with
+// timing_begin / timing_end; both do nothing unless timing is on for the calling thread.
+void timing_begin(const char* kernel, hipStream_t s);
+void timing_end(hipStream_t s);
+
 hipError_t launch_recurrent(const LayerArgs& a, int io, int ot, hipStream_t s);
 hipError_t launch_rollback(const RollbackArgs& a, int io, hipStream_t s);
 

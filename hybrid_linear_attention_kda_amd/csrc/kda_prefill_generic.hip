@@ -217,7 +217,9 @@ static hipError_t launch_generic_t(const LayerArgs& a, int Cc, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
+  timing_begin("kda_prefill_generic_kernel", s);
   kern<<<dim3(a.H, a.B), dim3(kGenericThreads), lds, s>>>(a, Cc);
+  timing_end(s);
   return hipGetLastError();
 }
 

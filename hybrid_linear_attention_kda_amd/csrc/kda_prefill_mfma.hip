@@ -11,17 +11,22 @@
 // max(||x||, eps), bounded-sigmoid per-channel decay on the key axis, gated
 // output RMSNorm with a plain weight).
 //
+// Expanding U in O gives O = (Q~ - A_qk W) S + A_qk Ut, so only products with the
+// chunk-start state S remain in the sequential part.
+//
 // Two phases.
-//  A (chunk-parallel, one workgroup per (sequence, head, chunk)): conv + SiLU,
-//    L2 norms, gate and its cumulative sum, A_kk, T, A_qk and W.  Everything
-//    that does not depend on the state or on d_v is computed once per chunk
-//    and written to the workspace as matrix-core operand tiles: Q~ = Q e^Gam
-//    and K~ = K e^(Gam_C - Gam) (transposed) and A_qk and T as split bf16
-//    (hi + lo), W as bf16, e^Gam_C as fp32.
+//  A (chunk-parallel, one workgroup per (sequence, head, chunk), dispatched
+//    chunk-major from the last chunk down, so that the tiles B reads first were
+//    written last and are still in the last-level cache): conv + SiLU,
+//    L2 norms, gate and its cumulative sum, A_kk, T, A_qk, W, and from them
+//      Ut = T (beta V),  Y = A_qk Ut,  P = Q~ - A_qk W,
+//    with Q~ = Q e^Gam and K~ = K e^(Gam_C - Gam).  Everything that does not
+//    depend on the state is written to the workspace once per chunk: P and K~^T
+//    (transposed) as split bf16 (hi + lo), W as bf16, Ut and Y as fp32 and
+//    e^Gam_C as fp32, each in the order the matrix cores consume it.
 //  B (sequential over chunks, one workgroup per (sequence, head, 16-column
-//    block of d_v)): conv + SiLU of its own v columns, then per chunk
-//      Ut = T (beta V),  U = Ut - W S,  O = Q~ S + A_qk U,
-//      S <- e^Gam_C S + K~^T U,
+//    block of d_v)): per chunk
+//      U = Ut - W S,  O = P S + Y,  S <- e^Gam_C S + K~^T U,
 //    with the 128 x 16 state block in MFMA accumulators and the operands of
 //    chunk c+1 loaded into registers while chunk c is computed.  blockIdx.x =
 //    vb * H + h, so with H a multiple of 8 the eight workgroups of a head run on
@@ -36,8 +41,8 @@
 //
 // Precision.  bf16 operands round to 8 bits; contractions that feed the
 // output or the state directly use split bf16 (x = hi + lo, three MFMAs:
-// hi.hi + hi.lo + lo.hi): A_qk, Ut, Q~ S, A_qk U, K~^T U.  A_kk and W run
-// in plain bf16 and W S splits only S.  T is formed in fp32.
+// hi.hi + hi.lo + lo.hi): A_qk, Ut, Y, P S, K~^T U.  A_kk and W run in plain
+// bf16; W S and A_qk W split only S and A_qk.  T is formed in fp32.
 //
 // The output RMSNorm needs all 128 columns of o, which live in eight
 // workgroups, so o (fp32) goes to the workspace and a third, bandwidth-bound
@@ -58,15 +63,13 @@ constexpr int HALO = 3;      // staged rows before the chunk (conv width <= 4)
 constexpr int PQ = 132;      // fp32 pitch of [64][128] arrays
 constexpr int PKB = 136;     // bf16 pitch of [64][128] arrays
 constexpr int PA = 68;       // fp32 pitch of [64][64] arrays
-constexpr int PT = 68;       // fp32 pitch of [16][64] (transposed token-major) arrays
-constexpr int PS = 132;      // fp32 pitch of the transposed state block [16][128]
 constexpr int PR = 280;      // bf16 pitch of the raw staging rows: q 128 | k 128 | v 16 | pad
 constexpr int RROWS = C + HALO;
 
 // Phase A LDS layout (bytes)
-constexpr int OFF_Q = 0;                              // q^ -> QR = q e^(Gam - Gam_n)
+constexpr int OFF_Q = 0;                              // q^ -> QR = q e^(Gam - Gam_n) -> P
 constexpr int OFF_KB = OFF_Q + C * PQ * 4;            // KR (bf16) -> W (bf16)
-constexpr int OFF_G = OFF_KB + C * PKB * 2;           // k^ -> KC = k e^(Gam_n - Gam)
+constexpr int OFF_G = OFF_KB + C * PKB * 2;           // k^ -> KC = k e^(Gam_n - Gam) -> raw v rows
 constexpr int OFF_STG = OFF_G + C * PQ * 4;           // raw staging | Gam | A_kk + T | A_qk
 constexpr int STG_BYTES = RROWS * PR * 2;             // 37520 >= 2 * C * PA * 4 and >= C * PQ * 4
 constexpr int OFF_TMP = OFF_STG + STG_BYTES;          // scratch while forming T [1024]
@@ -84,36 +87,34 @@ static_assert(STG_BYTES >= 2 * C * PA * 4 && STG_BYTES >= C * PQ * 4, "staging a
 static_assert(LDS_A <= 160 * 1024, "LDS budget");
 
 // Workspace tile block per (sequence, head, chunk), written by phase A and read by phase B.
-// Every matrix is stored in MFMA fragment order: fragment f = (row / 16) * (K / 32) + k / 32 of a
-// [rows][K] operand holds, for lane l, the 8 elements (row 16*(f / (K/32)) + l % 16,
+// Every bf16 matrix is stored in MFMA fragment order: fragment f = (row / 16) * (K / 32) + k / 32
+// of a [rows][K] operand holds, for lane l, the 8 elements (row 16*(f / (K/32)) + l % 16,
 // k = 32*(f % (K/32)) + 8*(l / 16) + 0..7), so a wave loads one fragment as 1 KB contiguous.
-constexpr int W_QHI = 0;                   // Q~ hi  [64][128] bf16 (16 fragments)
-constexpr int W_QLO = W_QHI + C * D * 2;   // Q~ lo
-constexpr int W_KTHI = W_QLO + C * D * 2;  // K~^T hi [128][64] bf16
+// The fp32 [64][128] matrices are stored as 16 x 16 accumulator tiles (I, j), tile-major
+// (I * 8 + j), lane l holding rows 16 I + 4 (l / 16) + 0..3 of column 16 j + l % 16.
+constexpr int W_PHI = 0;                   // P = Q~ - A_qk W, hi [64][128] bf16 (16 fragments)
+constexpr int W_PLO = W_PHI + C * D * 2;   // P lo
+constexpr int W_KTHI = W_PLO + C * D * 2;  // K~^T hi [128][64] bf16
 constexpr int W_KTLO = W_KTHI + D * C * 2; // K~^T lo
 constexpr int W_W = W_KTLO + D * C * 2;    // W [64][128] bf16
-constexpr int W_AHI = W_W + C * D * 2;     // A_qk hi [64][64] bf16 (upper triangle zero)
-constexpr int W_ALO = W_AHI + C * C * 2;
-constexpr int W_THI = W_ALO + C * C * 2;   // T hi [64][64] bf16 (upper triangle zero)
-constexpr int W_TLO = W_THI + C * C * 2;
-constexpr int W_GC = W_TLO + C * C * 2;    // e^Gam_C [128] fp32
-constexpr int CH_BYTES = W_GC + D * 4;     // 115200
+constexpr int W_UT = W_W + C * D * 2;      // Ut = T (beta V) [64][128] fp32, accumulator-fragment order
+constexpr int W_Y = W_UT + C * D * 4;      // Y = A_qk Ut [64][128] fp32, accumulator-fragment order
+constexpr int W_GC = W_Y + C * D * 4;      // e^Gam_C [128] fp32
+constexpr int CH_BYTES = W_GC + D * 4;     // 147968
 static_assert(CH_BYTES % 256 == 0, "tile blocks stay 256-byte aligned");
 
 // Phase B LDS layout (bytes)
-constexpr int PRV = NVB + 8;               // bf16 pitch of the staged raw v rows
-constexpr int PVT = 72;                    // bf16 pitch of [NVB][64] token-major operands
-constexpr int PST = 136;                   // bf16 pitch of the [NVB][128] state operand
-constexpr int B_RAWV = 0;                  // RROWS raw v rows + one spare row
-constexpr int B_VHI = B_RAWV + (RROWS + 1) * PRV * 2;
-constexpr int B_VLO = B_VHI + NVB * PVT * 2;
-constexpr int B_UHI = B_VLO + NVB * PVT * 2;
+constexpr int PVT = 72;                    // bf16 pitch of the [16][64] token-major U operand
+constexpr int PST = 136;                   // bf16 pitch of the [16][128] state operand
+constexpr int B_UHI = 0;
 constexpr int B_ULO = B_UHI + NVB * PVT * 2;
 constexpr int B_SHI = B_ULO + NVB * PVT * 2;
 constexpr int B_SLO = B_SHI + NVB * PST * 2;
 constexpr int LDS_B = B_SLO + NVB * PST * 2;
+static_assert(NVB == 16, "one accumulator column tile per phase-B workgroup");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 struct Split8 {
   bf16x8 hi, lo;
@@ -151,6 +152,10 @@ __device__ __forceinline__ void ld8(const float* p, float (&x)[8]) {
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ void ld4(const float* p, float* x) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+}
 // fp32 matrix core step: D += A[16 x 4] B[4 x 16]; lane l holds A[l % 16][l / 16] and B[l / 16][l % 16]
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -209,7 +214,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
   float* sSeg = reinterpret_cast<float*>(smem + OFF_SEG);
 
   const int H = a.H, T = a.T, W = a.W;
-  const int ci = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.x, b = blockIdx.z;
+  const int ci = (a.T + C - 1) / C - 1 - (int)blockIdx.y;
   const int NC = (T + C - 1) / C;
   const int c0 = ci * C;
   const int L = min(C, T - c0);
@@ -257,6 +263,21 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
 #pragma unroll
     for (int k = 0; k < 16; ++k) fraw[k] = fin[(long long)min(c0 + 16 * seg + k, T - 1) * HD + i];
   }
+  // raw v rows (staged late, for Ut = T (beta V)): lane task = (row, 8-channel segment)
+  constexpr int NRV = (RROWS * 16 + NT - 1) / NT;
+  uint4 rawv[NRV];
+#pragma unroll
+  for (int s = 0; s < NRV; ++s) {
+    const int r = min((tid + s * NT) >> 4, RROWS - 1), sg = tid & 15;
+    const int tt = min(max(c0 - HALO + r, 0), T - 1);
+    rawv[s] = *reinterpret_cast<const uint4*>(qkv + (long long)tt * Cq + 2LL * HD + h * D + sg * 8);
+  }
+  // conv taps of the v channel this lane converts (16 * wave + l16), raw; taps before the
+  // first of the W are masked where used
+  bf16_t tvr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    tvr[j] = cw[(2LL * HD + h * D + 16 * wave + l16) * W + max(j - (4 - W), 0)];
 #pragma unroll
   for (int s = 0; s < NRAW; ++s) {
     const int idx = tid + s * NT;
@@ -496,107 +517,206 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
   for (int I = 0; I < 4; ++I)
 #pragma unroll
     for (int r = 0; r < 4; ++r) sKb[(16 * I + 4 * lg + r) * PKB + 16 * wave + l16] = (__bf16)wacc[I][r];
+  // W as this wave's B operand over tokens, in the token order of its own accumulators: k-step s,
+  // lane group g, element e <-> token 32 s + 4 g + e (e < 4), 32 s + 16 + 4 g + e - 4 (e >= 4)
+  bf16x8 wb[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      wb[st][e] = (__bf16)wacc[2 * st][e];
+      wb[st][e + 4] = (__bf16)wacc[2 * st + 1][e];
+    }
   __syncthreads();
 
-  // ---- write the operand tiles in fragment order (16-byte stores, 8 elements per lane-task) ----
-  __bf16* qhi = reinterpret_cast<__bf16*>(blk + W_QHI);
-  __bf16* qlo = reinterpret_cast<__bf16*>(blk + W_QLO);
+  // ---- write W and K~^T in fragment order (16-byte stores, 8 elements per lane-task) ----
   __bf16* kthi = reinterpret_cast<__bf16*>(blk + W_KTHI);
   __bf16* ktlo = reinterpret_cast<__bf16*>(blk + W_KTLO);
   __bf16* wdst = reinterpret_cast<__bf16*>(blk + W_W);
-  __bf16* ahi = reinterpret_cast<__bf16*>(blk + W_AHI);
-  __bf16* alo = reinterpret_cast<__bf16*>(blk + W_ALO);
-  __bf16* thi = reinterpret_cast<__bf16*>(blk + W_THI);
-  __bf16* tlo = reinterpret_cast<__bf16*>(blk + W_TLO);
   for (int task = tid; task < C * D / 8; task += NT) {
-    // Q~ = QR e^Gam_n(I) and W: [64 tokens][128 channels]
+    // W: [64 tokens][128 channels]
     const int t = task >> 4, c8 = (task & 15) * 8;
     const int fo = frag_offset(t, c8, D);
-    float v[8];
-    ld8(sQ + t * PQ + c8, v);
-    const float* en = sEn + (t >> 4) * D + c8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] *= en[e];
-    store_split8(qhi + fo, qlo + fo, v);
     *reinterpret_cast<bf16x8*>(wdst + fo) = *reinterpret_cast<const bf16x8*>(sKb + t * PKB + c8);
     // K~^T = (KC e^(Gam_C - Gam_n(J)))^T: [128 channels][64 tokens]
     const int c = task >> 3, t8 = (task & 7) * 8;
     const int ko = frag_offset(c, t8, C);
     const float fac = sFac[(t8 >> 4) * D + c];
+    float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = sG[(t8 + e) * PQ + c] * fac;
     store_split8(kthi + ko, ktlo + ko, v);
   }
-  for (int task = tid; task < C * C / 8; task += NT) {
-    // A_qk and T: [64][64], zero above the diagonal
-    const int t = task >> 3, j8 = (task & 7) * 8;
-    const int fo = frag_offset(t, j8, C);
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (j8 + e <= t) ? sAqk[t * PA + j8 + e] : 0.f;
-    store_split8(ahi + fo, alo + fo, v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (j8 + e <= t) ? sT[t * PA + j8 + e] : 0.f;
-    store_split8(thi + fo, tlo + fo, v);
-  }
   if (tid < D) reinterpret_cast<float*>(blk + W_GC)[tid] = sGC[tid];
+  __syncthreads();  // KC is read: the raw v rows take its place
+
+  // ---- stage raw v rows for tokens c0-3 .. c0+63 (bf16, pitch PKB) ----
+  __bf16* sRv = reinterpret_cast<__bf16*>(smem + OFF_G);
+#pragma unroll
+  for (int s = 0; s < NRV; ++s) {
+    const int idx = tid + s * NT;
+    if (idx < RROWS * 16) {
+      const int r = idx >> 4, sg = idx & 15;
+      const int tt = c0 - HALO + r;
+      *reinterpret_cast<uint4*>(sRv + r * PKB + sg * 8) = (tt >= 0 && tt < T) ? rawv[s] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  if (ci == 0 && tid < HALO * 16) {
+    // rows before the sequence start come from the conv state (the same lane wrote them as zeros)
+    const int r = tid >> 4, sg = tid & 15;
+    const int tt = r - HALO;
+    if ((W - 1) + tt >= 0) {
+      const long long ch = 2LL * HD + h * D + sg * 8;
+      uint16_t e8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) e8[e] = cin[(ch + e) * (W - 1) + (W - 1) + tt];
+      *reinterpret_cast<uint4*>(sRv + r * PKB + sg * 8) =
+          make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16, e8[4] | (uint32_t)e8[5] << 16,
+                     e8[6] | (uint32_t)e8[7] << 16);
+    }
+  }
+  __syncthreads();
+
+  // ---- P9: per wave, column tile j = wave of the value axis:
+  //      Ut = T (beta V) (split bf16), Y = A_qk Ut (split bf16), P = Q~ - A_qk W (A_qk split) ----
+  {
+    const int vc = 16 * wave + l16;
+    float tv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tv[j] = j >= 4 - W ? to_f32(tvr[j]) : 0.f;
+    // beta V for tokens 32 s + 8 lg + 0..7 of channel vc: the B operand of Ut
+    Split8 bv[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int tb = 32 * st + 8 * lg;
+      float rr[11];
+#pragma unroll
+      for (int q = 0; q < 11; ++q) rr[q] = (float)sRv[(tb + q) * PKB + vc];
+      float xv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        xv[e] = sBeta[tb + e] * silu_fast(tv[0] * rr[e] + tv[1] * rr[e + 1] + tv[2] * rr[e + 2] + tv[3] * rr[e + 3]);
+      bv[st] = split(xv);
+    }
+    f32x4 ut[4];
+    f32x4* utd = reinterpret_cast<f32x4*>(blk + W_UT);
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      ut[I] = zero4();
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        if (32 * st > 16 * I + 15) continue;  // T is lower triangular
+        float tr[8];
+        ld8(sT + (16 * I + l16) * PA + 32 * st + 8 * lg, tr);
+        ut[I] = mfma3(split(tr), bv[st], ut[I]);
+      }
+      utd[(I * 8 + wave) * 64 + lane] = ut[I];
+    }
+    // Ut as the B operand over tokens in accumulator token order (see wb)
+    Split8 ub[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = ut[2 * st][e];
+        x[e + 4] = ut[2 * st + 1][e];
+      }
+      ub[st] = split(x);
+    }
+    f32x4* yd = reinterpret_cast<f32x4*>(blk + W_Y);
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      f32x4 ya = zero4(), pa = zero4();
+      const int t = 16 * I + l16;  // A_qk row of this lane
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        if (32 * st > 16 * I + 15) continue;  // A_qk is lower triangular
+        float ar[8];
+        ld4(sAqk + t * PA + 32 * st + 4 * lg, ar);
+        ld4(sAqk + t * PA + 32 * st + 16 + 4 * lg, ar + 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tok = 32 * st + 16 * (e >> 2) + 4 * lg + (e & 3);
+          ar[e] = tok <= t ? ar[e] : 0.f;
+        }
+        const Split8 as = split(ar);
+        ya = mfma3(as, ub[st], ya);
+        pa = mfma(as.lo, wb[st], pa);
+        pa = mfma(as.hi, wb[st], pa);
+      }
+      yd[(I * 8 + wave) * 64 + lane] = ya;
+      // P = QR e^Gam_n - A_qk W, in place of QR (this lane owns these elements)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tr = 16 * I + 4 * lg + r;
+        sQ[tr * PQ + vc] = sQ[tr * PQ + vc] * sEn[I * D + vc] - pa[r];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- write P in fragment order ----
+  __bf16* phi = reinterpret_cast<__bf16*>(blk + W_PHI);
+  __bf16* plo = reinterpret_cast<__bf16*>(blk + W_PLO);
+  for (int task = tid; task < C * D / 8; task += NT) {
+    const int t = task >> 4, c8 = (task & 15) * 8;
+    const int fo = frag_offset(t, c8, D);
+    float v[8];
+    ld8(sQ + t * PQ + c8, v);
+    store_split8(phi + fo, plo + fo, v);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
-// Phase B: one workgroup per (NVB-column block of d_v, head, sequence), sequential over chunks.
-// Waves 0-3 form U for row tile I = wave, waves 4-7 form O for row tile I = wave - 4, and every
-// wave updates state rows 16*wave .. 16*wave+15; each role covers all NVB/16 column tiles.
+// Phase B: one workgroup per (16-column block of d_v, head, sequence), sequential over chunks.
+// Waves 0-3 form U = Ut - W S for row tile I = wave, waves 4-7 form O = P S + Y for row tile
+// I = wave - 4, and every wave then updates state rows 16*wave .. 16*wave+15.
 // ---------------------------------------------------------------------------------------------
 struct OpTiles {        // this lane's operand fragments of one chunk
-  bf16x8 x0[4];         // waves 0-3: W (4 k-steps) | waves 4-7: Q~ hi
-  bf16x8 x1[4];         // waves 4-7: Q~ lo
-  bf16x8 y0[2], y1[2];  // waves 0-3: T hi / lo | waves 4-7: A_qk hi / lo   (2 k-steps)
+  bf16x8 x0[4];         // waves 0-3: W | waves 4-7: P hi   (row tile I, 4 k-steps)
+  bf16x8 x1[4];         // waves 4-7: P lo
+  f32x4 y;              // waves 0-3: Ut tile | waves 4-7: Y tile   (row tile I, column tile vb)
   bf16x8 k0[2], k1[2];  // all waves: K~^T hi / lo of channel tile = wave
   float4 gc;            // e^Gam_C of the four state rows this lane holds
 };
 
-// Every field is filled by one fixed sequence of fragment loads (only the source tiles differ by
-// role), so the fields stay in registers and every wave issues the same loads.
-__device__ __forceinline__ void load_tiles(const unsigned char* blk, int wave, int lane, int lg, OpTiles& o) {
+// Every field but x1 is filled by one fixed sequence of loads for all waves (only the source
+// tiles differ by role); x1 (waves 4-7 only) comes last, so a wait on any other field never
+// waits for it.
+__device__ __forceinline__ void load_tiles(const unsigned char* blk, int wave, int lane, int lg, int vb, OpTiles& o) {
   const int I = wave & 3;
   const bool u_role = wave < 4;
-  const bf16x8* x0p = reinterpret_cast<const bf16x8*>(blk + (u_role ? W_W : W_QHI)) + (I * 4) * 64 + lane;
-  // waves 0-3 have no second x operand: they re-read their W fragments, so every wave issues
-  // the same loads without a branch
-  const bf16x8* x1p = u_role ? x0p : reinterpret_cast<const bf16x8*>(blk + W_QLO) + (I * 4) * 64 + lane;
-  const bf16x8* y0p = reinterpret_cast<const bf16x8*>(blk + (u_role ? W_THI : W_AHI)) + (I * 2) * 64 + lane;
-  const bf16x8* y1p = reinterpret_cast<const bf16x8*>(blk + (u_role ? W_TLO : W_ALO)) + (I * 2) * 64 + lane;
+  const bf16x8* x0p = reinterpret_cast<const bf16x8*>(blk + (u_role ? W_W : W_PHI)) + (I * 4) * 64 + lane;
+  const bf16x8* x1p = reinterpret_cast<const bf16x8*>(blk + W_PLO) + (I * 4) * 64 + lane;
+  const f32x4* yp = reinterpret_cast<const f32x4*>(blk + (u_role ? W_UT : W_Y)) + (I * 8 + vb) * 64 + lane;
   const bf16x8* khp = reinterpret_cast<const bf16x8*>(blk + W_KTHI) + (wave * 2) * 64 + lane;
   const bf16x8* klp = reinterpret_cast<const bf16x8*>(blk + W_KTLO) + (wave * 2) * 64 + lane;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    o.x0[s] = x0p[s * 64];
-    o.x1[s] = x1p[s * 64];
-  }
+  for (int s = 0; s < 4; ++s) o.x0[s] = x0p[s * 64];
+  o.y = *yp;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    o.y0[s] = y0p[s * 64];
-    o.y1[s] = y1p[s * 64];
     o.k0[s] = khp[s * 64];
     o.k1[s] = klp[s * 64];
   }
   o.gc = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(blk + W_GC) + 16 * wave + 4 * lg);
+  if (!u_role) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) o.x1[s] = x1p[s * 64];
+  }
 }
 
 template <typename OT>
 __global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const unsigned char* __restrict__ ws,
                                                           float* __restrict__ ows) {
-  constexpr int NCT = NVB / 16;  // column tiles
   extern __shared__ __align__(16) unsigned char smem[];
-  __bf16* sRawV = reinterpret_cast<__bf16*>(smem + B_RAWV);
-  __bf16* sVhi = reinterpret_cast<__bf16*>(smem + B_VHI);
-  __bf16* sVlo = reinterpret_cast<__bf16*>(smem + B_VLO);
   __bf16* sUhi = reinterpret_cast<__bf16*>(smem + B_UHI);
   __bf16* sUlo = reinterpret_cast<__bf16*>(smem + B_ULO);
   __bf16* sShi = reinterpret_cast<__bf16*>(smem + B_SHI);
   __bf16* sSlo = reinterpret_cast<__bf16*>(smem + B_SLO);
 
-  const int H = a.H, T = a.T, W = a.W;
+  const int H = a.H, T = a.T;
   const int h = blockIdx.x % H;
   const int vb = blockIdx.x / H;
   const int b = blockIdx.y;
@@ -604,253 +724,122 @@ __global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int HD = H * D, Cq = 3 * HD;
-  const bf16_t* __restrict__ qkv = static_cast<const bf16_t*>(a.qkv) + (long long)b * T * Cq;
-  const bf16_t* __restrict__ bin = static_cast<const bf16_t*>(a.beta) + (long long)b * T * H + h;
-  const bf16_t* __restrict__ cin = static_cast<const bf16_t*>(a.conv_in) + (long long)b * Cq * (W - 1);
+  const int HD = H * D;
   const unsigned char* __restrict__ head_ws = ws + ((long long)b * H + h) * NC * (long long)CH_BYTES;
-  const long long vch = 2LL * HD + (long long)h * D + vb * NVB;  // first raw v channel of this block
 
   // State block: wave w owns channel rows 16w..16w+15; lane holds rows 16w+4lg+r of column
-  // 16*j + l16 of the block in Sacc[j].
-  f32x4 Sacc[NCT];
+  // vb*16 + l16.
+  f32x4 Sacc;
   {
     const float* sp = a.state_in + ((long long)b * H + h) * D * D + vb * NVB + l16;
 #pragma unroll
-    for (int j = 0; j < NCT; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Sacc[j][r] = sp[(16 * wave + 4 * lg + r) * D + 16 * j];
+    for (int r = 0; r < 4; ++r) Sacc[r] = sp[(16 * wave + 4 * lg + r) * D];
   }
+  // S^T as the split B operand [column][channel]; the lane's four rows are contiguous
   auto write_state_operand = [&]() {
+    bf16x4 hi, lo;
 #pragma unroll
-    for (int j = 0; j < NCT; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const __bf16 hi = (__bf16)Sacc[j][r];
-        sShi[(16 * j + l16) * PST + 16 * wave + 4 * lg + r] = hi;
-        sSlo[(16 * j + l16) * PST + 16 * wave + 4 * lg + r] = (__bf16)(Sacc[j][r] - (float)hi);
-      }
-  };
-  // conv taps of this lane's v column (column vj of the block; lanes cover 16 columns per pass)
-  const int vj = tid % NVB;
-  float tv[4];
-  {
-    const bf16_t* cw = static_cast<const bf16_t*>(a.conv_w);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int w = j - (4 - W);
-      tv[j] = w >= 0 ? to_f32(cw[(vch + vj) * W + w]) : 0.f;
+    for (int r = 0; r < 4; ++r) {
+      hi[r] = (__bf16)Sacc[r];
+      lo[r] = (__bf16)(Sacc[r] - (float)hi[r]);
     }
-  }
-
-  // Raw v rows of one chunk: lane task = (row r, 8-channel segment); lanes past the last row
-  // stage a spare row.  beta of the two tokens this lane converts in B2.  The loads have no
-  // branches (addresses clamped into the sequence) and their registers are consumed by every
-  // lane, so nothing waits for a prefetch before its data is needed.
-  constexpr int SEGS = NVB / 8;
-  const int rv_r = min(tid / SEGS, RROWS), rv_sg = tid % SEGS;
-  auto load_rawv = [&](int cidx, uint4& v, bf16_t (&bt)[2]) {
-    const int c0 = cidx * C;
-    const int tt = min(max(c0 - HALO + rv_r, 0), T - 1);
-    v = *reinterpret_cast<const uint4*>(qkv + (long long)tt * Cq + vch + 8 * rv_sg);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) bt[i] = bin[(long long)min(c0 + tid / NVB + (NT / NVB) * i, T - 1) * H];
+    *reinterpret_cast<bf16x4*>(sShi + l16 * PST + 16 * wave + 4 * lg) = hi;
+    *reinterpret_cast<bf16x4*>(sSlo + l16 * PST + 16 * wave + 4 * lg) = lo;
   };
-  static_assert(C * NVB / NT == 2, "two tokens per lane in B2");
 
   // Output rows of the previous chunk, held in registers until the next chunk has started so
   // that their stores are issued before that chunk's prefetch.
-  f32x4 opend[NCT];
+  f32x4 opend;
   auto store_pending = [&](int pc) {
     if (pc < 0 || wave < 4) return;
     const int pc0 = pc * C, pL = min(C, T - pc0);
+    float* op = ows + (((long long)b * T + pc0) * H + h) * D + vb * NVB + l16;
 #pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      float* op = ows + (((long long)b * T + pc0) * H + h) * D + vb * NVB + 16 * j + l16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * (wave - 4) + 4 * lg + r;
-        if (t < pL) op[(long long)t * HD] = opend[j][r];
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * (wave - 4) + 4 * lg + r;
+      if (t < pL) op[(long long)t * HD] = opend[r];
     }
   };
 
-  // One chunk: operands in (cur, rv_cur, be_cur), the next chunk's prefetched into (nxt, ...).
-  // Two register sets alternate between the roles, so no loaded value is ever copied.
-  auto chunk = [&](int ci, const OpTiles& cur, const uint4& rv_cur, const bf16_t (&be_cur)[2], OpTiles& nxt,
-                   uint4& rv_nxt, bf16_t (&be_nxt)[2]) __attribute__((always_inline)) {
-    const int c0 = ci * C;
-    const int L = min(C, T - c0);
-    // B1: this chunk's prefetched raw v rows into LDS and its beta into registers (every lane,
-    // no branches), then the previous chunk's output rows are stored and the next chunk's loads
-    // issued, in that order: a wait for a prefetched value then never waits for a store.
-    float bt[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      bt[i] = to_f32(be_cur[i]);
-      asm volatile("" : "+v"(bt[i]));  // keep the conversion (and its wait) ahead of the stores
-    }
-    {
-      const int tt = c0 - HALO + rv_r;
-      const uint32_t m = ((tt >= 0) & (tt < T)) ? 0xffffffffu : 0u;
-      *reinterpret_cast<uint4*>(sRawV + rv_r * PRV + 8 * rv_sg) =
-          make_uint4(rv_cur.x & m, rv_cur.y & m, rv_cur.z & m, rv_cur.w & m);
-    }
-    if (ci == 0 && W > 1 && tid < HALO * SEGS) {
-      // rows before the sequence start come from the conv state (the same lane wrote them as zeros)
-      const int tt = rv_r - HALO;
-      if ((W - 1) + tt >= 0) {
-        const long long ch = vch + 8 * rv_sg;
-        uint16_t e8[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) e8[e] = cin[(ch + e) * (W - 1) + (W - 1) + tt];
-        *reinterpret_cast<uint4*>(sRawV + rv_r * PRV + 8 * rv_sg) =
-            make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16, e8[4] | (uint32_t)e8[5] << 16,
-                       e8[6] | (uint32_t)e8[7] << 16);
-      }
-    }
+  // One chunk: operands in cur, those of chunk ci + 2 prefetched into nxt (two chunks of
+  // latency cover a miss in L2 even though loads return in order).  Three register sets rotate
+  // through the roles, so no loaded value is ever copied.
+  auto chunk = [&](int ci, const OpTiles& cur, OpTiles& nxt) __attribute__((always_inline)) {
     store_pending(ci - 1);
-    {
-      // the last chunk prefetches itself again: the loads stay unconditional
-      const int cn = min(ci + 1, NC - 1);
-      load_tiles(head_ws + (long long)cn * CH_BYTES, wave, lane, lg, nxt);
-      load_rawv(cn, rv_nxt, be_nxt);
-    }
-    __syncthreads();
-    // B2: conv + SiLU of the v block, times beta, as the split B operand [col][token]
-    {
-#pragma unroll
-      for (int i = 0; i < C * NVB / NT; ++i) {
-        const int t = (tid / NVB) + (NT / NVB) * i;
-        const __bf16* vc = sRawV + vj;
-        const float y = tv[0] * (float)vc[t * PRV] + tv[1] * (float)vc[(t + 1) * PRV] +
-                        tv[2] * (float)vc[(t + 2) * PRV] + tv[3] * (float)vc[(t + 3) * PRV];
-        const float xv = bt[i] * silu_fast(y);
-        const float x = t < L ? xv : 0.f;
-        const __bf16 hi = (__bf16)x;
-        sVhi[vj * PVT + t] = hi;
-        sVlo[vj * PVT + t] = (__bf16)(x - (float)hi);
-      }
-    }
-    __syncthreads();
-    // B3: waves 0-3: U = T (beta V) - W S for row tile I; waves 4-7: O = Q~ S for row tile I
-    f32x4 oacc[NCT], ob[NCT];
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      oacc[j] = zero4();
-      ob[j] = zero4();
-    }
+    // the last chunks prefetch the last one again: the loads stay unconditional
+    load_tiles(head_ws + (long long)min(ci + 1, NC - 1) * CH_BYTES, wave, lane, lg, vb, nxt);
+    __syncthreads();  // the state operand of this chunk is in LDS
     if (wave < 4) {
-      const int I = wave;
+      // U = Ut - W S for row tile I = wave, as the split B operand [column][token]
+      f32x4 pa = zero4(), pb = zero4();
 #pragma unroll
-      for (int j = 0; j < NCT; ++j) {
-        f32x4 ua = zero4(), ub = zero4(), pa = zero4(), pb = zero4();
-        const int col = 16 * j + l16;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          if (32 * s > 16 * I + 15) continue;
-          const bf16x8 vh = *reinterpret_cast<const bf16x8*>(sVhi + col * PVT + 32 * s + 8 * lg);
-          const bf16x8 vl = *reinterpret_cast<const bf16x8*>(sVlo + col * PVT + 32 * s + 8 * lg);
-          ua = mfma(cur.y0[s], vh, ua);
-          ub = mfma(cur.y0[s], vl, ub);
-          ub = mfma(cur.y1[s], vh, ub);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sShi + col * PST + 32 * s + 8 * lg);
-          const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSlo + col * PST + 32 * s + 8 * lg);
-          pa = mfma(cur.x0[s], sh, pa);
-          pb = mfma(cur.x0[s], sl, pb);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float u = (ua[r] + ub[r]) - (pa[r] + pb[r]);
-          const __bf16 hi = (__bf16)u;
-          sUhi[col * PVT + 16 * I + 4 * lg + r] = hi;
-          sUlo[col * PVT + 16 * I + 4 * lg + r] = (__bf16)(u - (float)hi);
-        }
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
+        const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSlo + l16 * PST + 32 * s + 8 * lg);
+        pa = mfma(cur.x0[s], sh, pa);
+        pb = mfma(cur.x0[s], sl, pb);
       }
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float u = cur.y[r] - (pa[r] + pb[r]);
+        hi[r] = (__bf16)u;
+        lo[r] = (__bf16)(u - (float)hi[r]);
+      }
+      *reinterpret_cast<bf16x4*>(sUhi + l16 * PVT + 16 * wave + 4 * lg) = hi;
+      *reinterpret_cast<bf16x4*>(sUlo + l16 * PVT + 16 * wave + 4 * lg) = lo;
     } else {
+      // O = P S + Y for row tile I = wave - 4
+      f32x4 oa = zero4(), ob = zero4();
 #pragma unroll
-      for (int j = 0; j < NCT; ++j) {
-        const int col = 16 * j + l16;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sShi + col * PST + 32 * s + 8 * lg);
-          const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSlo + col * PST + 32 * s + 8 * lg);
-          oacc[j] = mfma(cur.x0[s], sh, oacc[j]);
-          ob[j] = mfma(cur.x0[s], sl, ob[j]);
-          ob[j] = mfma(cur.x1[s], sh, ob[j]);
-        }
-      }
-    }
-    __syncthreads();
-    // B4: waves 4-7: O += A_qk U and store; all waves: S <- e^Gam_C S + K~^T U
-    if (wave >= 4) {
-      const int I = wave - 4;
-#pragma unroll
-      for (int j = 0; j < NCT; ++j) {
-        const int col = 16 * j + l16;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          if (32 * s > 16 * I + 15) continue;
-          const bf16x8 uh = *reinterpret_cast<const bf16x8*>(sUhi + col * PVT + 32 * s + 8 * lg);
-          const bf16x8 ul = *reinterpret_cast<const bf16x8*>(sUlo + col * PVT + 32 * s + 8 * lg);
-          oacc[j] = mfma(cur.y0[s], uh, oacc[j]);
-          ob[j] = mfma(cur.y0[s], ul, ob[j]);
-          ob[j] = mfma(cur.y1[s], uh, ob[j]);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) opend[j][r] = oacc[j][r] + ob[j][r];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      const int col = 16 * j + l16;
-      f32x4 sa, sb = zero4();
-      sa[0] = cur.gc.x * Sacc[j][0];
-      sa[1] = cur.gc.y * Sacc[j][1];
-      sa[2] = cur.gc.z * Sacc[j][2];
-      sa[3] = cur.gc.w * Sacc[j][3];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 uh = *reinterpret_cast<const bf16x8*>(sUhi + col * PVT + 32 * s + 8 * lg);
-        const bf16x8 ul = *reinterpret_cast<const bf16x8*>(sUlo + col * PVT + 32 * s + 8 * lg);
-        sa = mfma(cur.k0[s], uh, sa);
-        sb = mfma(cur.k0[s], ul, sb);
-        sb = mfma(cur.k1[s], uh, sb);
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
+        const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSlo + l16 * PST + 32 * s + 8 * lg);
+        oa = mfma(cur.x0[s], sh, oa);
+        ob = mfma(cur.x0[s], sl, ob);
+        ob = mfma(cur.x1[s], sh, ob);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Sacc[j][r] = sa[r] + sb[r];
+      for (int r = 0; r < 4; ++r) opend[r] = (oa[r] + ob[r]) + cur.y[r];
     }
-    __syncthreads();  // the old state operand has been read
+    __syncthreads();  // U is in LDS and every read of the state operand is done
+    // S <- e^Gam_C S + K~^T U
+    f32x4 sa, sb = zero4();
+    sa[0] = cur.gc.x * Sacc[0];
+    sa[1] = cur.gc.y * Sacc[1];
+    sa[2] = cur.gc.z * Sacc[2];
+    sa[3] = cur.gc.w * Sacc[3];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 uh = *reinterpret_cast<const bf16x8*>(sUhi + l16 * PVT + 32 * s + 8 * lg);
+      const bf16x8 ul = *reinterpret_cast<const bf16x8*>(sUlo + l16 * PVT + 32 * s + 8 * lg);
+      sa = mfma(cur.k0[s], uh, sa);
+      sb = mfma(cur.k0[s], ul, sb);
+      sb = mfma(cur.k1[s], uh, sb);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Sacc[r] = sa[r] + sb[r];
     write_state_operand();
   };
 
   OpTiles ta, tb;
-  uint4 rva, rvb;
-  bf16_t bea[2], beb[2];
-  load_tiles(head_ws, wave, lane, lg, ta);
-  load_rawv(0, rva, bea);
+  load_tiles(head_ws, wave, lane, lg, vb, ta);
   write_state_operand();
   int ci = 0;
   for (; ci + 1 < NC; ci += 2) {
-    chunk(ci, ta, rva, bea, tb, rvb, beb);
-    chunk(ci + 1, tb, rvb, beb, ta, rva, bea);
+    chunk(ci, ta, tb);
+    chunk(ci + 1, tb, ta);
   }
-  if (ci < NC) chunk(ci, ta, rva, bea, tb, rvb, beb);
+  if (ci < NC) chunk(ci, ta, tb);
   store_pending(NC - 1);
 
   {
     float* sp = a.state_out + ((long long)b * H + h) * D * D + vb * NVB + l16;
 #pragma unroll
-    for (int j = 0; j < NCT; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sp[(16 * wave + 4 * lg + r) * D + 16 * j] = Sacc[j][r];
+    for (int r = 0; r < 4; ++r) sp[(16 * wave + 4 * lg + r) * D] = Sacc[r];
   }
 }
 
-// out = o / sqrt(mean(o^2) + eps) * w * sigmoid(g_out), one wave per (token, head) row of 128.
 template <typename OT>
 __global__ __launch_bounds__(256) void kda_out_norm_kernel(const float* __restrict__ ows, const bf16_t* __restrict__ gout,
                                                         const bf16_t* __restrict__ nw, OT* __restrict__ out,
@@ -912,17 +901,22 @@ hipError_t launch_prefill_mfma(const LayerArgs& a, void* ws, size_t, int ot, hip
   static const hipError_t attr_a = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_A);
   if (attr_a != hipSuccess) return attr_a;
-  kda_chunk_prep_kernel<<<dim3(NC, a.H, a.B), NT, LDS_A, s>>>(a, tiles);
+  timing_begin("kda_chunk_prep_kernel", s);
+  kda_chunk_prep_kernel<<<dim3(a.H, NC, a.B), NT, LDS_A, s>>>(a, tiles);
+  timing_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid_b(NBLK * a.H, a.B);
+  timing_begin("kda_chunk_state_kernel", s);
   if (ot == kBF16)
     kda_chunk_state_kernel<bf16_t><<<grid_b, NT, LDS_B, s>>>(a, tiles, ows);
   else
     kda_chunk_state_kernel<float><<<grid_b, NT, LDS_B, s>>>(a, tiles, ows);
+  timing_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long rows = (long long)a.B * a.T * a.H;
   const dim3 ng((unsigned)((rows + 3) / 4));
+  timing_begin("kda_out_norm_kernel", s);
   if (ot == kBF16)
     kda_out_norm_kernel<bf16_t><<<ng, 256, 0, s>>>(ows, static_cast<const bf16_t*>(a.g_out),
                                                    static_cast<const bf16_t*>(a.norm_w), static_cast<bf16_t*>(a.out),
@@ -931,10 +925,13 @@ hipError_t launch_prefill_mfma(const LayerArgs& a, void* ws, size_t, int ot, hip
     kda_out_norm_kernel<float><<<ng, 256, 0, s>>>(ows, static_cast<const bf16_t*>(a.g_out),
                                                   static_cast<const bf16_t*>(a.norm_w), static_cast<float*>(a.out), rows,
                                                   a.rms_eps);
+  timing_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.W > 1 && a.conv_out != nullptr) {
     const int Cq = 3 * a.H * a.D;
+    timing_begin("kda_conv_state_kernel", s);
     kda_conv_state_kernel<<<dim3((Cq + 255) / 256, a.B), 256, 0, s>>>(a);
+    timing_end(s);
     e = hipGetLastError();
   }
   return e;

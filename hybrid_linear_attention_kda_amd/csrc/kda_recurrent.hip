@@ -248,6 +248,7 @@ __global__ __launch_bounds__(256) void kda_rollback_kernel(RollbackArgs a) {
 template <int D, int WMAX, bool MULTI>
 static hipError_t launch_rec_t(const LayerArgs& a, int io, int ot, hipStream_t s) {
   dim3 grid(a.H, a.B), block(RecLayout<D>::NT);
+  timing_begin(a.snapshots ? "kda_recurrent_kernel[verify]" : "kda_recurrent_kernel[decode]", s);
   if (io == kBF16) {
     if (ot == kBF16)
       kda_recurrent_kernel<D, WMAX, MULTI, bf16_t, bf16_t><<<grid, block, 0, s>>>(a);
@@ -259,6 +260,7 @@ static hipError_t launch_rec_t(const LayerArgs& a, int io, int ot, hipStream_t s
     else
       kda_recurrent_kernel<D, WMAX, MULTI, float, float><<<grid, block, 0, s>>>(a);
   }
+  timing_end(s);
   return hipGetLastError();
 }
 
@@ -284,10 +286,12 @@ hipError_t launch_rollback(const RollbackArgs& a, int io, hipStream_t s) {
   int gx = (int)((n4 + 256 * 8 - 1) / (256 * 8));  // 8 float4 per lane
   if (gx < 1) gx = 1;
   dim3 grid(gx, a.nB), block(256);
+  timing_begin("kda_rollback_kernel", s);
   if (io == kBF16)
     kda_rollback_kernel<bf16_t><<<grid, block, 0, s>>>(a);
   else
     kda_rollback_kernel<float><<<grid, block, 0, s>>>(a);
+  timing_end(s);
   return hipGetLastError();
 }
 

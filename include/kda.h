@@ -146,6 +146,23 @@ kda_status kda_verify_block(const kda_layer_desc* desc, int32_t B, int32_t T_d, 
 kda_status kda_rollback(const kda_layer_desc* desc, int32_t B, int32_t T_d, const int32_t* accepted_host,
                         const float* snaps, const void* qkv_block, float* state, void* conv_state, void* stream);
 
+/*
+ * Per-kernel timing, for benchmarks (not part of the layer).
+ * kda_timing_enable(1) makes every later call made on this host thread record
+ * a HIP event pair on the call's stream around each kernel it launches;
+ * kda_timing_enable(0) stops recording.  Off by default; recording adds two
+ * event records per kernel and changes no result.  Returns the previous
+ * setting.
+ * kda_timing_read waits for the recorded events, writes the kernel names
+ * (static strings owned by the library) and durations in milliseconds of the
+ * first `cap` records in launch order into names / ms (host arrays, either may
+ * be NULL when cap is 0), releases every record and returns how many records
+ * there were (possibly more than cap), or -1 if a HIP call failed (the records
+ * are released all the same; kda_last_error() says which).
+ */
+int32_t kda_timing_enable(int32_t on);
+int32_t kda_timing_read(const char** names, float* ms, int32_t cap);
+
 #ifdef __cplusplus
 }
 #endif

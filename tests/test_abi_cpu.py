@@ -32,7 +32,8 @@ def test_library_exports_every_header_function():
     lib = abi.load()
     names = abi.header_functions()
     assert set(names) == {"kda_abi_version", "kda_status_string", "kda_last_error", "kda_prefill_workspace_size",
-                          "kda_prefill", "kda_decode_step", "kda_verify_block", "kda_rollback"}
+                          "kda_prefill", "kda_decode_step", "kda_verify_block", "kda_rollback",
+                          "kda_timing_enable", "kda_timing_read"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.kda_abi_version() == 1
@@ -103,3 +104,12 @@ def test_workspace_size():
     assert lib.kda_prefill_workspace_size(ctypes.byref(d), 1, 64) == 0  # fp32 vector-ALU path needs none
     bad = desc(gate_lower_bound=math.nan)
     assert lib.kda_prefill_workspace_size(ctypes.byref(bad), 1, 64) == ctypes.c_size_t(-1).value
+
+
+def test_timing_read_without_records_is_empty():
+    # no GPU needed: with nothing recorded the read touches no event
+    lib = abi.load()
+    assert lib.kda_timing_read(None, None, 0) == 0
+    assert abi.timing_enable(True) is False
+    assert abi.timing_enable(False) is True
+    assert abi.timing_read() == []

@@ -175,6 +175,25 @@ def test_bf16_prefill_four_heads(T):
     _check("out (bf16 output)", out16, ref["out"], TOL_BF16_OUT)
 
 
+@pytest.mark.parametrize("T", [100, 33])
+def test_fp32_prefill_head_size_128(T):
+    # fp32 io at d = 128 runs the vector-ALU chunked prefill (internal chunk 32)
+    wl = I.WORKLOADS["prefill_t4096"].with_(T=T, H=2, B=2, io="f32", seed=12)
+    say(f"case fp32 prefill d=128 H=2 B=2 T={T}")
+    inp = I.generate(wl)
+    rng = np.random.default_rng(100 + T)
+    S0 = (rng.standard_normal(inp["state0"].shape) * 0.3).astype(np.float32)
+    C0 = rng.standard_normal(inp["conv_state0"].shape).astype(np.float32)
+    layer = TT.make_layer(wl, inp, DEV)
+    st, cs = _dev_state(wl, inp, S0, C0)
+    out = _gpu_prefill(wl, inp, layer, 0, T, st, cs)
+    torch.cuda.synchronize()
+    ref = oracle_layer(wl, inp, 0, T, S0, C0)
+    _check("out", out, ref["out"], TOL["f32"])
+    _check("state", st, ref["state"], TOL["f32"])
+    _check("conv_state", cs, ref["conv_state"], 0.0)
+
+
 # ---------------------------------------------------------------------------
 # Full-size workloads, in the benchmark's launch configuration
 # ---------------------------------------------------------------------------
