@@ -191,8 +191,88 @@ __device__ __forceinline__ void store_split8(__bf16* hi, __bf16* lo, const float
 }
 
 // ---------------------------------------------------------------------------------------------
-// Phase A: one workgroup per (chunk, head, sequence).
+// Phase A: persistent workgroups (one per CU) loop over the tasks (chunk, head, sequence); the
+// global inputs of the next task are loaded into registers while the current one is computed.
 // ---------------------------------------------------------------------------------------------
+constexpr int NRAW = (RROWS * 32 + NT - 1) / NT;  // raw q | k row loads per lane
+constexpr int NRV = (RROWS * 16 + NT - 1) / NT;   // raw v row loads per lane
+
+struct PrepTask {
+  int h, b, ci;
+};
+// Tasks run head-fastest and chunk-major from the last chunk down, so that the tiles phase B
+// reads first were written last and are still in the last-level cache.
+__device__ __forceinline__ PrepTask prep_task(int task, int H, int NC) {
+  PrepTask k;
+  k.h = task % H;
+  const int r = task / H;
+  k.ci = NC - 1 - r % NC;
+  k.b = r / NC;
+  return k;
+}
+
+// The global inputs of one task, as loaded: 16-byte loads only (addresses clamped into the
+// sequence and into the parameter blocks; rows outside the sequence are replaced when staged).
+struct PrepIn {
+  uint4 raw[NRAW];   // raw q | k rows c0-3 .. c0+63: lane task (row, 8-channel segment)
+  uint4 rawv[NRV];   // raw v rows, the same way
+  uint4 f[2];        // gate inputs of tokens c0 .. c0+63: lane task (token, 8-channel segment)
+  uint4 par;         // 16 bytes of the head's parameter block (q, k, v conv taps, dt_bias)
+  bf16_t beta;       // beta of token tid % 64
+  float alog;        // A_log of the head
+};
+
+// Parameter block of a head in LDS: q taps [128][W], k taps, v taps (bf16), dt_bias [128] (fp32).
+__device__ __forceinline__ int par_segments(int W) { return 48 * W + 32; }
+
+// The loads of one task, in three groups (0: q|k rows, 1: v rows, 2: the rest) that the kernel
+// issues at different points of the previous task, so that no phase carries all of them.
+__device__ __forceinline__ void prep_issue(const LayerArgs& a, const PrepTask& k, int tid, PrepIn& in, int part) {
+  const int H = a.H, T = a.T, W = a.W, HD = H * D, Cq = 3 * HD;
+  const int h = k.h, c0 = k.ci * C;
+  const bf16_t* __restrict__ qkv = static_cast<const bf16_t*>(a.qkv) + (long long)k.b * T * Cq;
+  if (part == 0) {
+#pragma unroll
+    for (int s = 0; s < NRAW; ++s) {
+      const int r = min((tid + s * NT) >> 5, RROWS - 1), sg = tid & 31;
+      const int tt = min(max(c0 - HALO + r, 0), T - 1);
+      const long long ch = sg < 16 ? (long long)h * D + sg * 8 : (long long)HD + h * D + (sg - 16) * 8;
+      in.raw[s] = *reinterpret_cast<const uint4*>(qkv + (long long)tt * Cq + ch);
+    }
+  } else if (part == 1) {
+#pragma unroll
+    for (int s = 0; s < NRV; ++s) {
+      const int r = min((tid + s * NT) >> 4, RROWS - 1), sg = tid & 15;
+      const int tt = min(max(c0 - HALO + r, 0), T - 1);
+      in.rawv[s] = *reinterpret_cast<const uint4*>(qkv + (long long)tt * Cq + 2LL * HD + h * D + sg * 8);
+    }
+  } else {
+    const bf16_t* __restrict__ fin = static_cast<const bf16_t*>(a.f) + (long long)k.b * T * HD + h * D;
+    const bf16_t* __restrict__ bin = static_cast<const bf16_t*>(a.beta) + (long long)k.b * T * H + h;
+    const bf16_t* __restrict__ cw = static_cast<const bf16_t*>(a.conv_w);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int t = (tid + s * NT) >> 4, sg = tid & 15;
+      in.f[s] = *reinterpret_cast<const uint4*>(fin + (long long)min(c0 + t, T - 1) * HD + sg * 8);
+    }
+    {
+      // segment p of the parameter block: 16 W segments per tap block, then 32 of dt_bias
+      const int p = min(tid, par_segments(W) - 1);
+      const int blkw = 16 * W;
+      const uint4* src;
+      if (p < 3 * blkw) {
+        const int which = p / blkw, o = p - which * blkw;
+        src = reinterpret_cast<const uint4*>(cw + ((long long)which * HD + h * D) * W) + o;
+      } else {
+        src = reinterpret_cast<const uint4*>(a.dt_bias + h * D) + (p - 3 * blkw);
+      }
+      in.par = *src;
+    }
+    in.beta = bin[(long long)min(c0 + (tid & 63), T - 1) * H];
+    in.alog = a.A_log[h];
+  }
+}
+
 __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigned char* __restrict__ ws) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* sQ = reinterpret_cast<float*>(smem + OFF_Q);
@@ -214,457 +294,455 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
   float* sSeg = reinterpret_cast<float*>(smem + OFF_SEG);
 
   const int H = a.H, T = a.T, W = a.W;
-  const int h = blockIdx.x, b = blockIdx.z;
-  const int ci = (a.T + C - 1) / C - 1 - (int)blockIdx.y;
   const int NC = (T + C - 1) / C;
-  const int c0 = ci * C;
-  const int L = min(C, T - c0);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, lg = lane >> 4;  // MFMA row/column index and k-group
+  const int ntask = a.B * NC * H;
   const int HD = H * D, Cq = 3 * HD;
 
-  const bf16_t* __restrict__ qkv = static_cast<const bf16_t*>(a.qkv) + (long long)b * T * Cq;
-  const bf16_t* __restrict__ fin = static_cast<const bf16_t*>(a.f) + (long long)b * T * HD + h * D;
-  const bf16_t* __restrict__ bin = static_cast<const bf16_t*>(a.beta) + (long long)b * T * H + h;
-  const bf16_t* __restrict__ cw = static_cast<const bf16_t*>(a.conv_w);
-  const bf16_t* __restrict__ cin = static_cast<const bf16_t*>(a.conv_in) + (long long)b * Cq * (W - 1);
-  unsigned char* __restrict__ blk = ws + (((long long)b * H + h) * NC + ci) * (long long)CH_BYTES;
-
-  // ---- P1: issue every global load of the chunk up front (addresses clamped into the sequence,
-  //      out-of-range rows replaced after the loads), then stage raw q | k rows for tokens
-  //      c0-3 .. c0+63 (bf16) ----
-  constexpr int NRAW = (RROWS * 32 + NT - 1) / NT;
-  uint4 raw[NRAW];
-#pragma unroll
-  for (int s = 0; s < NRAW; ++s) {
-    const int r = min((tid + s * NT) >> 5, RROWS - 1), sg = tid & 31;
-    const int tt = min(max(c0 - HALO + r, 0), T - 1);
-    const long long ch = sg < 16 ? (long long)h * D + sg * 8 : (long long)HD + h * D + (sg - 16) * 8;
-    raw[s] = *reinterpret_cast<const uint4*>(qkv + (long long)tt * Cq + ch);
-  }
-  // conv taps of this lane's q/k channel, zero-padded on the left to 4 taps
-  const int cq = tid & 255;
-  const long long gqk = cq < D ? (long long)h * D + cq : (long long)HD + h * D + (cq - D);
-  float tq[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int w = j - (4 - W);
-    const float tv = to_f32(cw[gqk * W + max(w, 0)]);
-    tq[j] = w >= 0 ? tv : 0.f;
-  }
-  const float bval = to_f32(bin[(long long)min(c0 + (tid & 63), T - 1) * H]);
-  // gate inputs: lane -> channel tid % 128, tokens 16 * (tid / 128) .. +15
-  const float alog = a.A_log[h];
-  const float dtb = a.dt_bias[h * D + (tid & 127)];
-  bf16_t fraw[16];
+  PrepIn cur;
   {
-    const int i = tid & 127, seg = tid >> 7;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) fraw[k] = fin[(long long)min(c0 + 16 * seg + k, T - 1) * HD + i];
+    const PrepTask k0 = prep_task(min((int)blockIdx.x, ntask - 1), H, NC);
+    prep_issue(a, k0, (int)threadIdx.x, cur, 0);
+    prep_issue(a, k0, (int)threadIdx.x, cur, 1);
+    prep_issue(a, k0, (int)threadIdx.x, cur, 2);
   }
-  // raw v rows (staged late, for Ut = T (beta V)): lane task = (row, 8-channel segment)
-  constexpr int NRV = (RROWS * 16 + NT - 1) / NT;
-  uint4 rawv[NRV];
-#pragma unroll
-  for (int s = 0; s < NRV; ++s) {
-    const int r = min((tid + s * NT) >> 4, RROWS - 1), sg = tid & 15;
-    const int tt = min(max(c0 - HALO + r, 0), T - 1);
-    rawv[s] = *reinterpret_cast<const uint4*>(qkv + (long long)tt * Cq + 2LL * HD + h * D + sg * 8);
-  }
-  // conv taps of the v channel this lane converts (16 * wave + l16), raw; taps before the
-  // first of the W are masked where used
-  bf16_t tvr[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    tvr[j] = cw[(2LL * HD + h * D + 16 * wave + l16) * W + max(j - (4 - W), 0)];
-#pragma unroll
-  for (int s = 0; s < NRAW; ++s) {
-    const int idx = tid + s * NT;
-    if (idx < RROWS * 32) {
-      const int r = idx >> 5, sg = idx & 31;
-      const int tt = c0 - HALO + r;
-      *reinterpret_cast<uint4*>(sRaw + r * PR + sg * 8) = (tt >= 0 && tt < T) ? raw[s] : make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-  if (ci == 0 && tid < HALO * 32) {
-    // rows before the sequence start come from the conv state (the same lane wrote them as zeros)
-    const int r = tid >> 5, sg = tid & 31;
-    const int tt = r - HALO;
-    if ((W - 1) + tt >= 0) {
-      const long long ch = sg < 16 ? (long long)h * D + sg * 8 : (long long)HD + h * D + (sg - 16) * 8;
-      uint16_t e8[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) e8[e] = cin[(ch + e) * (W - 1) + (W - 1) + tt];
-      *reinterpret_cast<uint4*>(sRaw + r * PR + sg * 8) =
-          make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16, e8[4] | (uint32_t)e8[5] << 16,
-                     e8[6] | (uint32_t)e8[7] << 16);
-    }
-  }
-  if (tid < C) sBeta[tid] = tid < L ? bval : 0.f;
-  __syncthreads();
+  for (int tk = blockIdx.x; tk < ntask; tk += gridDim.x) {
+    // lane indices are re-derived per task from an opaque copy, so that the address arithmetic
+    // built on them is not hoisted out of the loop and held in registers across it
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;  // MFMA row/column index and k-group
+    const PrepTask ktask = prep_task(tk, H, NC);
+    const int h = ktask.h, b = ktask.b, ci = ktask.ci;
+    const int c0 = ci * C;
+    const int L = min(C, T - c0);
+    const bf16_t* __restrict__ cin = static_cast<const bf16_t*>(a.conv_in) + (long long)b * Cq * (W - 1);
+    unsigned char* __restrict__ blk = ws + (((long long)b * H + h) * NC + ci) * (long long)CH_BYTES;
 
-  // ---- P2: causal conv + SiLU over q|k: lane -> channel cq, 32 tokens ----
-  {
-    const int tb = 32 * (tid >> 8);
-    const __bf16* col = sRaw + cq;
-    float r0 = (float)col[(tb + 0) * PR], r1 = (float)col[(tb + 1) * PR], r2 = (float)col[(tb + 2) * PR];
-    float* dst = cq < D ? sQ + cq : sG + (cq - D);
-#pragma unroll 4
-    for (int i = 0; i < 32; ++i) {
-      const int t = tb + i;
-      const float r3 = (float)col[(t + 3) * PR];
-      const float y = tq[0] * r0 + tq[1] * r1 + tq[2] * r2 + tq[3] * r3;
-      dst[t * PQ] = t < L ? silu_fast(y) : 0.f;
-      r0 = r1; r1 = r2; r2 = r3;
-    }
-  }
-  __syncthreads();
-
-  // ---- P3: bounded-sigmoid gate and its cumulative sum (lane -> channel, 16-token segment) ----
-  {
-    const int i = tid & 127, seg = tid >> 7;
-    const float Ah = __expf(alog);
-    float gl[16];
-    float acc = 0.f;
+    // ---- P1: stage this task's raw q | k rows for tokens c0-3 .. c0+63, its gate inputs and
+    //      its head's parameter block (bf16) from the registers loaded during the previous task ----
+    __bf16* sF = reinterpret_cast<__bf16*>(smem + OFF_AQK);  // f [64][PKB] until A_qk is formed
+    unsigned char* sPar = smem + OFF_TMP;                    // parameter block until T is formed
+    const float alog = cur.alog;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float fv = to_f32(fraw[k]) + dtb;
-      const float g = a.lb * __builtin_amdgcn_rcpf(1.0f + __expf(-Ah * fv));
-      acc += 16 * seg + k < L ? g : 0.f;
-      gl[k] = acc;
+    for (int s = 0; s < NRAW; ++s) {
+      const int idx = tid + s * NT;
+      if (idx < RROWS * 32) {
+        const int r = idx >> 5, sg = idx & 31;
+        const int tt = c0 - HALO + r;
+        *reinterpret_cast<uint4*>(sRaw + r * PR + sg * 8) = (tt >= 0 && tt < T) ? cur.raw[s] : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
-    sSeg[seg * D + i] = acc;
-    // ---- P4 (same phase): q / k L2 normalisers: eight lanes per token, 16 channels each ----
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int t = (tid + s * NT) >> 4, sg = tid & 15;
+      *reinterpret_cast<uint4*>(sF + t * PKB + sg * 8) = cur.f[s];
+    }
+    if (tid < par_segments(W)) reinterpret_cast<uint4*>(sPar)[tid] = cur.par;
+    if (ci == 0 && tid < HALO * 32) {
+      // rows before the sequence start come from the conv state (the same lane wrote them as zeros)
+      const int r = tid >> 5, sg = tid & 31;
+      const int tt = r - HALO;
+      if ((W - 1) + tt >= 0) {
+        const long long ch = sg < 16 ? (long long)h * D + sg * 8 : (long long)HD + h * D + (sg - 16) * 8;
+        uint16_t e8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) e8[e] = cin[(ch + e) * (W - 1) + (W - 1) + tt];
+        *reinterpret_cast<uint4*>(sRaw + r * PR + sg * 8) =
+            make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16, e8[4] | (uint32_t)e8[5] << 16,
+                       e8[6] | (uint32_t)e8[7] << 16);
+      }
+    }
+    if (tid < C) sBeta[tid] = tid < L ? to_f32(cur.beta) : 0.f;
+    __syncthreads();
+    // conv taps of this lane's q|k channel (tid % 256) and of the v channel it converts in P9
+    // (16 * wave + lane % 16), zero-padded on the left to 4 taps; read before T reuses the block
+    float tq[4], tv[4];
     {
-      const int t = tid >> 3, p = tid & 7;
-      const float4* qp = reinterpret_cast<const float4*>(sQ + t * PQ + 16 * p);
-      const float4* kp = reinterpret_cast<const float4*>(sG + t * PQ + 16 * p);
-      float qq = 0.f, kk = 0.f;
+      const __bf16* taps = reinterpret_cast<const __bf16*>(sPar);
+      const int cq = tid & 255;  // q channels then k channels: the block rows in that order
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float4 x = qp[e], y = kp[e];
-        qq += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
-        kk += y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
+      for (int j = 0; j < 4; ++j) {
+        const int w = max(j - (4 - W), 0);
+        tq[j] = j >= 4 - W ? (float)taps[cq * W + w] : 0.f;
+        tv[j] = j >= 4 - W ? (float)taps[(2 * D + 16 * wave + l16) * W + w] : 0.f;
       }
-#pragma unroll
-      for (int o = 4; o > 0; o >>= 1) {
-        qq += __shfl_xor(qq, o, 64);
-        kk += __shfl_xor(kk, o, 64);
-      }
-      if (p == 0) {
-        sNrm[t] = a.scale / fmaxf(sqrtf(qq), a.l2_eps);
-        sNrm[C + t] = 1.0f / fmaxf(sqrtf(kk), a.l2_eps);
+    }
+    const float* sDtb = reinterpret_cast<const float*>(sPar + 3 * D * W * 2);
+
+    // ---- P2: causal conv + SiLU over q|k: lane -> channel cq, 32 tokens ----
+    {
+      const int tb = 32 * (tid >> 8), cq = tid & 255;
+      const __bf16* col = sRaw + cq;
+      float r0 = (float)col[(tb + 0) * PR], r1 = (float)col[(tb + 1) * PR], r2 = (float)col[(tb + 2) * PR];
+      float* dst = cq < D ? sQ + cq : sG + (cq - D);
+#pragma unroll 4
+      for (int i = 0; i < 32; ++i) {
+        const int t = tb + i;
+        const float r3 = (float)col[(t + 3) * PR];
+        const float y = tq[0] * r0 + tq[1] * r1 + tq[2] * r2 + tq[3] * r3;
+        dst[t * PQ] = t < L ? silu_fast(y) : 0.f;
+        r0 = r1; r1 = r2; r2 = r3;
       }
     }
     __syncthreads();
-    float off = 0.f;
-    for (int s = 0; s < seg; ++s) off += sSeg[s * D + i];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) sGam[(16 * seg + k) * PQ + i] = gl[k] + off;
-    sGn[seg * D + i] = gl[0] + off;
-    if (seg == 3) sGn[4 * D + i] = gl[15] + off;
-  }
-  __syncthreads();
 
-  // ---- P5: anchored operands QR, KR (bf16), KC and the per-channel factor tables ----
-  for (int idx = tid; idx < C * D; idx += NT) {
-    const int t = idx >> 7, c = idx & 127;
-    const float G = sGam[t * PQ + c];
-    const float Gn = sGn[(t >> 4) * D + c];
-    const float e1 = __expf(G - Gn);  // <= 1
-    const float e2 = __expf(Gn - G);  // in [1, e^(15|lb|)]
-    const float q = sQ[t * PQ + c] * sNrm[t];
-    const float k = sG[t * PQ + c] * sNrm[C + t];
-    sQ[t * PQ + c] = q * e1;
-    sKb[t * PKB + c] = (__bf16)(k * e1);
-    sG[t * PQ + c] = k * e2;
-  }
-  if (tid < D) {
-    const int c = tid;
-    const float GC = sGn[4 * D + c];
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      const float GI = sGn[I * D + c];
-      sEn[I * D + c] = __expf(GI);
-      sFac[I * D + c] = __expf(GC - GI);
-#pragma unroll
-      for (int J = 0; J < I; ++J) sE[pair_index(I, J) * D + c] = __expf(GI - sGn[J * D + c]);
-    }
-    sGC[c] = __expf(GC);
-  }
-  __syncthreads();
+    // the next task's inputs (the last task loads its own again: the loads stay unconditional),
+    // issued in three groups spread over this task
+    const PrepTask knext = prep_task(min(tk + (int)gridDim.x, ntask - 1), H, NC);
+    PrepIn nxt;
+    prep_issue(a, knext, tid, nxt, 0);
 
-  // ---- P6a: A_kk = beta_i * KR_I E_IJ . KC_J^T (plain bf16), strictly lower ----
-  for (int bi = wave; bi < 10; bi += 8) {
-    int I, J;
-    block_ij(bi, I, J);
-    f32x4 acc = zero4();
+    // ---- P3: bounded-sigmoid gate and its cumulative sum (lane -> channel, 16-token segment) ----
+    {
+      const int i = tid & 127, seg = tid >> 7;
+      const float Ah = __expf(alog);
+      const float dtb = sDtb[i];
+      float gl[16];
+      float acc = 0.f;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int c = 32 * s + 8 * lg;
-      bf16x8 av = *reinterpret_cast<const bf16x8*>(sKb + (16 * I + l16) * PKB + c);
-      if (I > J) {
-        const float* ef = sE + pair_index(I, J) * D + c;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) av[e] = (__bf16)((float)av[e] * ef[e]);
+      for (int k = 0; k < 16; ++k) {
+        const float fv = (float)sF[(16 * seg + k) * PKB + i] + dtb;
+        const float g = a.lb * __builtin_amdgcn_rcpf(1.0f + __expf(-Ah * fv));
+        acc += 16 * seg + k < L ? g : 0.f;
+        gl[k] = acc;
       }
-      float kc[8];
-      ld8(sG + (16 * J + l16) * PQ + c, kc);
-      acc = mfma(av, round8(kc), acc);
-    }
+      sSeg[seg * D + i] = acc;
+      // ---- P4 (same phase): q / k L2 normalisers: eight lanes per token, 16 channels each ----
+      {
+        const int t = tid >> 3, p = tid & 7;
+        const float4* qp = reinterpret_cast<const float4*>(sQ + t * PQ + 16 * p);
+        const float4* kp = reinterpret_cast<const float4*>(sG + t * PQ + 16 * p);
+        float qq = 0.f, kk = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * I + 4 * lg + r, j = 16 * J + l16;
-      sAkk[i * PA + j] = j < i ? sBeta[i] * acc[r] : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const float4 x = qp[e], y = kp[e];
+          qq += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+          kk += y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
+        }
+#pragma unroll
+        for (int o = 4; o > 0; o >>= 1) {
+          qq += __shfl_xor(qq, o, 64);
+          kk += __shfl_xor(kk, o, 64);
+        }
+        if (p == 0) {
+          sNrm[t] = a.scale / fmaxf(sqrtf(qq), a.l2_eps);
+          sNrm[C + t] = 1.0f / fmaxf(sqrtf(kk), a.l2_eps);
+        }
+      }
+      __syncthreads();
+      float off = 0.f;
+      for (int s = 0; s < seg; ++s) off += sSeg[s * D + i];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) sGam[(16 * seg + k) * PQ + i] = gl[k] + off;
+      sGn[seg * D + i] = gl[0] + off;
+      if (seg == 3) sGn[4 * D + i] = gl[15] + off;
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // ---- P7: T = (I + A_kk)^-1 in fp32: diagonal 16x16 blocks by forward substitution ----
-  if (wave == 0) {
-    const int I = lg, cc = l16;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float v = (i == cc) ? 1.f : 0.f;
-#pragma unroll
-      for (int j = 0; j < i; ++j) v -= sAkk[(16 * I + i) * PA + 16 * I + j] * x[j];
-      x[i] = v;
+    prep_issue(a, knext, tid, nxt, 1);
+
+    // ---- P5: anchored operands QR, KR (bf16), KC and the per-channel factor tables ----
+    for (int idx = tid; idx < C * D; idx += NT) {
+      const int t = idx >> 7, c = idx & 127;
+      const float G = sGam[t * PQ + c];
+      const float Gn = sGn[(t >> 4) * D + c];
+      const float e1 = __expf(G - Gn);  // <= 1
+      const float e2 = __expf(Gn - G);  // in [1, e^(15|lb|)]
+      const float q = sQ[t * PQ + c] * sNrm[t];
+      const float k = sG[t * PQ + c] * sNrm[C + t];
+      sQ[t * PQ + c] = q * e1;
+      sKb[t * PKB + c] = (__bf16)(k * e1);
+      sG[t * PQ + c] = k * e2;
     }
+    if (tid < D) {
+      const int c = tid;
+      const float GC = sGn[4 * D + c];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sT[(16 * I + i) * PA + 16 * I + cc] = x[i];
-  } else {
-    // zero the strictly-upper blocks: W = T X reads blocks (0,1) and (2,3) inside its 32-token k-steps
-    for (int idx = tid - 64; idx < 6 * 256; idx += NT - 64) {
-      const int blk6 = idx >> 8, e = idx & 255;
-      const int I = blk6 < 3 ? 0 : blk6 < 5 ? 1 : 2;
-      const int J = blk6 < 3 ? blk6 + 1 : blk6 < 5 ? blk6 - 1 : 3;
-      sT[(16 * I + (e >> 4)) * PA + 16 * J + (e & 15)] = 0.f;
+      for (int I = 0; I < 4; ++I) {
+        const float GI = sGn[I * D + c];
+        sEn[I * D + c] = __expf(GI);
+        sFac[I * D + c] = __expf(GC - GI);
+#pragma unroll
+        for (int J = 0; J < I; ++J) sE[pair_index(I, J) * D + c] = __expf(GI - sGn[J * D + c]);
+      }
+      sGC[c] = __expf(GC);
     }
-  }
-  __syncthreads();
-  // Off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, column block J = wave (0..2)
-  // top to bottom on the fp32 matrix cores, while waves 3-7 form A_qk.
-  if (wave < 3) {
-    const int J = wave;
-    float* sM = sTmp + wave * 16 * 17;
-    for (int I = J + 1; I < 4; ++I) {
-      f32x4 m = zero4();
-      for (int K = J; K < I; ++K)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          m = mfma_f32(sAkk[(16 * I + l16) * PA + 16 * K + 4 * s + lg], sT[(16 * K + 4 * s + lg) * PA + 16 * J + l16], m);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sM[(4 * lg + r) * 17 + l16] = m[r];
-      wave_lds_sync();
-      f32x4 tij = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        tij = mfma_f32(sT[(16 * I + l16) * PA + 16 * I + 4 * s + lg], sM[(4 * s + lg) * 17 + l16], tij);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * lg + r) * PA + 16 * J + l16] = -tij[r];
-      wave_lds_sync();
-    }
-  } else {
-    // ---- P6b: A_qk = QR_I E_IJ . KC_J^T (split bf16), lower incl. diagonal ----
-    for (int bi = wave - 3; bi < 10; bi += 5) {
+    __syncthreads();
+
+    // ---- P6a: A_kk = beta_i * KR_I E_IJ . KC_J^T (plain bf16), strictly lower ----
+    for (int bi = wave; bi < 10; bi += 8) {
       int I, J;
       block_ij(bi, I, J);
       f32x4 acc = zero4();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int c = 32 * s + 8 * lg;
-        float qv[8], kc[8];
-        ld8(sQ + (16 * I + l16) * PQ + c, qv);
+        bf16x8 av = *reinterpret_cast<const bf16x8*>(sKb + (16 * I + l16) * PKB + c);
         if (I > J) {
           const float* ef = sE + pair_index(I, J) * D + c;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) qv[e] *= ef[e];
+          for (int e = 0; e < 8; ++e) av[e] = (__bf16)((float)av[e] * ef[e]);
         }
+        float kc[8];
         ld8(sG + (16 * J + l16) * PQ + c, kc);
-        acc = mfma3(split(qv), split(kc), acc);
+        acc = mfma(av, round8(kc), acc);
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sAqk[(16 * I + 4 * lg + r) * PA + 16 * J + l16] = acc[r];
-    }
-  }
-  __syncthreads();
-
-  // ---- P8: W = T . (beta KR e^Gam_n) (plain bf16); wave -> 16 key channels ----
-  f32x4 wacc[4] = {zero4(), zero4(), zero4(), zero4()};
-  {
-    const int c = 16 * wave + l16;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int tb = 32 * s + 8 * lg;
-      const float fac = sEn[(tb >> 4) * D + c];
-      float xv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xv[e] = sBeta[tb + e] * (float)sKb[(tb + e) * PKB + c] * fac;
-      const bf16x8 bx = round8(xv);
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        if (32 * s > 16 * I + 15) continue;  // T is lower triangular
-        float tvv[8];
-        ld8(sT + (16 * I + l16) * PA + 32 * s + 8 * lg, tvv);
-        wacc[I] = mfma(round8(tvv), bx, wacc[I]);
-      }
-    }
-  }
-  __syncthreads();  // every read of KR is done: W takes its place
-#pragma unroll
-  for (int I = 0; I < 4; ++I)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sKb[(16 * I + 4 * lg + r) * PKB + 16 * wave + l16] = (__bf16)wacc[I][r];
-  // W as this wave's B operand over tokens, in the token order of its own accumulators: k-step s,
-  // lane group g, element e <-> token 32 s + 4 g + e (e < 4), 32 s + 16 + 4 g + e - 4 (e >= 4)
-  bf16x8 wb[2];
-#pragma unroll
-  for (int st = 0; st < 2; ++st)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      wb[st][e] = (__bf16)wacc[2 * st][e];
-      wb[st][e + 4] = (__bf16)wacc[2 * st + 1][e];
-    }
-  __syncthreads();
-
-  // ---- write W and K~^T in fragment order (16-byte stores, 8 elements per lane-task) ----
-  __bf16* kthi = reinterpret_cast<__bf16*>(blk + W_KTHI);
-  __bf16* ktlo = reinterpret_cast<__bf16*>(blk + W_KTLO);
-  __bf16* wdst = reinterpret_cast<__bf16*>(blk + W_W);
-  for (int task = tid; task < C * D / 8; task += NT) {
-    // W: [64 tokens][128 channels]
-    const int t = task >> 4, c8 = (task & 15) * 8;
-    const int fo = frag_offset(t, c8, D);
-    *reinterpret_cast<bf16x8*>(wdst + fo) = *reinterpret_cast<const bf16x8*>(sKb + t * PKB + c8);
-    // K~^T = (KC e^(Gam_C - Gam_n(J)))^T: [128 channels][64 tokens]
-    const int c = task >> 3, t8 = (task & 7) * 8;
-    const int ko = frag_offset(c, t8, C);
-    const float fac = sFac[(t8 >> 4) * D + c];
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = sG[(t8 + e) * PQ + c] * fac;
-    store_split8(kthi + ko, ktlo + ko, v);
-  }
-  if (tid < D) reinterpret_cast<float*>(blk + W_GC)[tid] = sGC[tid];
-  __syncthreads();  // KC is read: the raw v rows take its place
-
-  // ---- stage raw v rows for tokens c0-3 .. c0+63 (bf16, pitch PKB) ----
-  __bf16* sRv = reinterpret_cast<__bf16*>(smem + OFF_G);
-#pragma unroll
-  for (int s = 0; s < NRV; ++s) {
-    const int idx = tid + s * NT;
-    if (idx < RROWS * 16) {
-      const int r = idx >> 4, sg = idx & 15;
-      const int tt = c0 - HALO + r;
-      *reinterpret_cast<uint4*>(sRv + r * PKB + sg * 8) = (tt >= 0 && tt < T) ? rawv[s] : make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-  if (ci == 0 && tid < HALO * 16) {
-    // rows before the sequence start come from the conv state (the same lane wrote them as zeros)
-    const int r = tid >> 4, sg = tid & 15;
-    const int tt = r - HALO;
-    if ((W - 1) + tt >= 0) {
-      const long long ch = 2LL * HD + h * D + sg * 8;
-      uint16_t e8[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) e8[e] = cin[(ch + e) * (W - 1) + (W - 1) + tt];
-      *reinterpret_cast<uint4*>(sRv + r * PKB + sg * 8) =
-          make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16, e8[4] | (uint32_t)e8[5] << 16,
-                     e8[6] | (uint32_t)e8[7] << 16);
-    }
-  }
-  __syncthreads();
-
-  // ---- P9: per wave, column tile j = wave of the value axis:
-  //      Ut = T (beta V) (split bf16), Y = A_qk Ut (split bf16), P = Q~ - A_qk W (A_qk split) ----
-  {
-    const int vc = 16 * wave + l16;
-    float tv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) tv[j] = j >= 4 - W ? to_f32(tvr[j]) : 0.f;
-    // beta V for tokens 32 s + 8 lg + 0..7 of channel vc: the B operand of Ut
-    Split8 bv[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int tb = 32 * st + 8 * lg;
-      float rr[11];
-#pragma unroll
-      for (int q = 0; q < 11; ++q) rr[q] = (float)sRv[(tb + q) * PKB + vc];
-      float xv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        xv[e] = sBeta[tb + e] * silu_fast(tv[0] * rr[e] + tv[1] * rr[e + 1] + tv[2] * rr[e + 2] + tv[3] * rr[e + 3]);
-      bv[st] = split(xv);
-    }
-    f32x4 ut[4];
-    f32x4* utd = reinterpret_cast<f32x4*>(blk + W_UT);
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      ut[I] = zero4();
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        if (32 * st > 16 * I + 15) continue;  // T is lower triangular
-        float tr[8];
-        ld8(sT + (16 * I + l16) * PA + 32 * st + 8 * lg, tr);
-        ut[I] = mfma3(split(tr), bv[st], ut[I]);
-      }
-      utd[(I * 8 + wave) * 64 + lane] = ut[I];
-    }
-    // Ut as the B operand over tokens in accumulator token order (see wb)
-    Split8 ub[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = ut[2 * st][e];
-        x[e + 4] = ut[2 * st + 1][e];
-      }
-      ub[st] = split(x);
-    }
-    f32x4* yd = reinterpret_cast<f32x4*>(blk + W_Y);
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      f32x4 ya = zero4(), pa = zero4();
-      const int t = 16 * I + l16;  // A_qk row of this lane
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        if (32 * st > 16 * I + 15) continue;  // A_qk is lower triangular
-        float ar[8];
-        ld4(sAqk + t * PA + 32 * st + 4 * lg, ar);
-        ld4(sAqk + t * PA + 32 * st + 16 + 4 * lg, ar + 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tok = 32 * st + 16 * (e >> 2) + 4 * lg + (e & 3);
-          ar[e] = tok <= t ? ar[e] : 0.f;
-        }
-        const Split8 as = split(ar);
-        ya = mfma3(as, ub[st], ya);
-        pa = mfma(as.lo, wb[st], pa);
-        pa = mfma(as.hi, wb[st], pa);
-      }
-      yd[(I * 8 + wave) * 64 + lane] = ya;
-      // P = QR e^Gam_n - A_qk W, in place of QR (this lane owns these elements)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int tr = 16 * I + 4 * lg + r;
-        sQ[tr * PQ + vc] = sQ[tr * PQ + vc] * sEn[I * D + vc] - pa[r];
+        const int i = 16 * I + 4 * lg + r, j = 16 * J + l16;
+        sAkk[i * PA + j] = j < i ? sBeta[i] * acc[r] : 0.f;
       }
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // ---- write P in fragment order ----
-  __bf16* phi = reinterpret_cast<__bf16*>(blk + W_PHI);
-  __bf16* plo = reinterpret_cast<__bf16*>(blk + W_PLO);
-  for (int task = tid; task < C * D / 8; task += NT) {
-    const int t = task >> 4, c8 = (task & 15) * 8;
-    const int fo = frag_offset(t, c8, D);
-    float v[8];
-    ld8(sQ + t * PQ + c8, v);
-    store_split8(phi + fo, plo + fo, v);
+    // ---- P7: T = (I + A_kk)^-1 in fp32: diagonal 16x16 blocks by forward substitution ----
+    if (wave == 0) {
+      const int I = lg, cc = l16;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float v = (i == cc) ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < i; ++j) v -= sAkk[(16 * I + i) * PA + 16 * I + j] * x[j];
+        x[i] = v;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sT[(16 * I + i) * PA + 16 * I + cc] = x[i];
+    } else {
+      // zero the strictly-upper blocks: W = T X reads blocks (0,1) and (2,3) inside its 32-token k-steps
+      for (int idx = tid - 64; idx < 6 * 256; idx += NT - 64) {
+        const int blk6 = idx >> 8, e = idx & 255;
+        const int I = blk6 < 3 ? 0 : blk6 < 5 ? 1 : 2;
+        const int J = blk6 < 3 ? blk6 + 1 : blk6 < 5 ? blk6 - 1 : 3;
+        sT[(16 * I + (e >> 4)) * PA + 16 * J + (e & 15)] = 0.f;
+      }
+    }
+    __syncthreads();
+    // Off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, column block J = wave (0..2)
+    // top to bottom on the fp32 matrix cores, while waves 3-7 form A_qk.
+    if (wave < 3) {
+      const int J = wave;
+      float* sM = sTmp + wave * 16 * 17;
+      for (int I = J + 1; I < 4; ++I) {
+        f32x4 m = zero4();
+        for (int K = J; K < I; ++K)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            m = mfma_f32(sAkk[(16 * I + l16) * PA + 16 * K + 4 * s + lg], sT[(16 * K + 4 * s + lg) * PA + 16 * J + l16], m);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sM[(4 * lg + r) * 17 + l16] = m[r];
+        wave_lds_sync();
+        f32x4 tij = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          tij = mfma_f32(sT[(16 * I + l16) * PA + 16 * I + 4 * s + lg], sM[(4 * s + lg) * 17 + l16], tij);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * lg + r) * PA + 16 * J + l16] = -tij[r];
+        wave_lds_sync();
+      }
+    } else {
+      // ---- P6b: A_qk = QR_I E_IJ . KC_J^T (split bf16), lower incl. diagonal ----
+      for (int bi = wave - 3; bi < 10; bi += 5) {
+        int I, J;
+        block_ij(bi, I, J);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int c = 32 * s + 8 * lg;
+          float qv[8], kc[8];
+          ld8(sQ + (16 * I + l16) * PQ + c, qv);
+          if (I > J) {
+            const float* ef = sE + pair_index(I, J) * D + c;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[e] *= ef[e];
+          }
+          ld8(sG + (16 * J + l16) * PQ + c, kc);
+          acc = mfma3(split(qv), split(kc), acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sAqk[(16 * I + 4 * lg + r) * PA + 16 * J + l16] = acc[r];
+      }
+    }
+    __syncthreads();
+
+    prep_issue(a, knext, tid, nxt, 2);
+
+    // ---- P8: W = T . (beta KR e^Gam_n) (plain bf16); wave -> 16 key channels ----
+    f32x4 wacc[4] = {zero4(), zero4(), zero4(), zero4()};
+    {
+      const int c = 16 * wave + l16;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int tb = 32 * s + 8 * lg;
+        const float fac = sEn[(tb >> 4) * D + c];
+        float xv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[e] = sBeta[tb + e] * (float)sKb[(tb + e) * PKB + c] * fac;
+        const bf16x8 bx = round8(xv);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          if (32 * s > 16 * I + 15) continue;  // T is lower triangular
+          float tvv[8];
+          ld8(sT + (16 * I + l16) * PA + 32 * s + 8 * lg, tvv);
+          wacc[I] = mfma(round8(tvv), bx, wacc[I]);
+        }
+      }
+    }
+    __syncthreads();  // every read of KR is done: W takes its place
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sKb[(16 * I + 4 * lg + r) * PKB + 16 * wave + l16] = (__bf16)wacc[I][r];
+    // W as this wave's B operand over tokens, in the token order of its own accumulators: k-step s,
+    // lane group g, element e <-> token 32 s + 4 g + e (e < 4), 32 s + 16 + 4 g + e - 4 (e >= 4)
+    bf16x8 wb[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wb[st][e] = (__bf16)wacc[2 * st][e];
+        wb[st][e + 4] = (__bf16)wacc[2 * st + 1][e];
+      }
+    __syncthreads();
+
+    // ---- write W and K~^T in fragment order (16-byte stores, 8 elements per lane-task) ----
+    __bf16* kthi = reinterpret_cast<__bf16*>(blk + W_KTHI);
+    __bf16* ktlo = reinterpret_cast<__bf16*>(blk + W_KTLO);
+    __bf16* wdst = reinterpret_cast<__bf16*>(blk + W_W);
+    for (int task = tid; task < C * D / 8; task += NT) {
+      // W: [64 tokens][128 channels]
+      const int t = task >> 4, c8 = (task & 15) * 8;
+      const int fo = frag_offset(t, c8, D);
+      *reinterpret_cast<bf16x8*>(wdst + fo) = *reinterpret_cast<const bf16x8*>(sKb + t * PKB + c8);
+      // K~^T = (KC e^(Gam_C - Gam_n(J)))^T: [128 channels][64 tokens]
+      const int c = task >> 3, t8 = (task & 7) * 8;
+      const int ko = frag_offset(c, t8, C);
+      const float fac = sFac[(t8 >> 4) * D + c];
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = sG[(t8 + e) * PQ + c] * fac;
+      store_split8(kthi + ko, ktlo + ko, v);
+    }
+    // every lane stores (four lanes per value, the same value) so that the number of stores is fixed
+    reinterpret_cast<float*>(blk + W_GC)[tid & 127] = sGC[tid & 127];
+    __syncthreads();  // KC is read: the raw v rows take its place
+
+    // ---- stage raw v rows for tokens c0-3 .. c0+63 (bf16, pitch PKB) ----
+    __bf16* sRv = reinterpret_cast<__bf16*>(smem + OFF_G);
+#pragma unroll
+    for (int s = 0; s < NRV; ++s) {
+      const int idx = tid + s * NT;
+      if (idx < RROWS * 16) {
+        const int r = idx >> 4, sg = idx & 15;
+        const int tt = c0 - HALO + r;
+        *reinterpret_cast<uint4*>(sRv + r * PKB + sg * 8) = (tt >= 0 && tt < T) ? cur.rawv[s] : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    if (ci == 0 && tid < HALO * 16) {
+      // rows before the sequence start come from the conv state (the same lane wrote them as zeros)
+      const int r = tid >> 4, sg = tid & 15;
+      const int tt = r - HALO;
+      if ((W - 1) + tt >= 0) {
+        const long long ch = 2LL * HD + h * D + sg * 8;
+        uint16_t e8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) e8[e] = cin[(ch + e) * (W - 1) + (W - 1) + tt];
+        *reinterpret_cast<uint4*>(sRv + r * PKB + sg * 8) =
+            make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16, e8[4] | (uint32_t)e8[5] << 16,
+                       e8[6] | (uint32_t)e8[7] << 16);
+      }
+    }
+    __syncthreads();
+
+    // ---- P9: per wave, column tile j = wave of the value axis:
+    //      Ut = T (beta V) (split bf16), Y = A_qk Ut (split bf16), P = Q~ - A_qk W (A_qk split) ----
+    {
+      const int vc = 16 * wave + l16;
+      // beta V for tokens 32 s + 8 lg + 0..7 of channel vc: the B operand of Ut
+      Split8 bv[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int tb = 32 * st + 8 * lg;
+        float rr[11];
+#pragma unroll
+        for (int q = 0; q < 11; ++q) rr[q] = (float)sRv[(tb + q) * PKB + vc];
+        float xv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          xv[e] = sBeta[tb + e] * silu_fast(tv[0] * rr[e] + tv[1] * rr[e + 1] + tv[2] * rr[e + 2] + tv[3] * rr[e + 3]);
+        bv[st] = split(xv);
+      }
+      f32x4 ut[4];
+      f32x4* utd = reinterpret_cast<f32x4*>(blk + W_UT);
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        ut[I] = zero4();
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          if (32 * st > 16 * I + 15) continue;  // T is lower triangular
+          float tr[8];
+          ld8(sT + (16 * I + l16) * PA + 32 * st + 8 * lg, tr);
+          ut[I] = mfma3(split(tr), bv[st], ut[I]);
+        }
+        utd[(I * 8 + wave) * 64 + lane] = ut[I];
+      }
+      // Ut as the B operand over tokens in accumulator token order (see wb)
+      Split8 ub[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = ut[2 * st][e];
+          x[e + 4] = ut[2 * st + 1][e];
+        }
+        ub[st] = split(x);
+      }
+      f32x4* yd = reinterpret_cast<f32x4*>(blk + W_Y);
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        f32x4 ya = zero4(), pa = zero4();
+        const int t = 16 * I + l16;  // A_qk row of this lane
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          if (32 * st > 16 * I + 15) continue;  // A_qk is lower triangular
+          float ar[8];
+          ld4(sAqk + t * PA + 32 * st + 4 * lg, ar);
+          ld4(sAqk + t * PA + 32 * st + 16 + 4 * lg, ar + 4);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int tok = 32 * st + 16 * (e >> 2) + 4 * lg + (e & 3);
+            ar[e] = tok <= t ? ar[e] : 0.f;
+          }
+          const Split8 as = split(ar);
+          ya = mfma3(as, ub[st], ya);
+          pa = mfma(as.lo, wb[st], pa);
+          pa = mfma(as.hi, wb[st], pa);
+        }
+        yd[(I * 8 + wave) * 64 + lane] = ya;
+        // P = QR e^Gam_n - A_qk W, in place of QR (this lane owns these elements)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tr = 16 * I + 4 * lg + r;
+          sQ[tr * PQ + vc] = sQ[tr * PQ + vc] * sEn[I * D + vc] - pa[r];
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- write P in fragment order ----
+    __bf16* phi = reinterpret_cast<__bf16*>(blk + W_PHI);
+    __bf16* plo = reinterpret_cast<__bf16*>(blk + W_PLO);
+    for (int task = tid; task < C * D / 8; task += NT) {
+      const int t = task >> 4, c8 = (task & 15) * 8;
+      const int fo = frag_offset(t, c8, D);
+      float v[8];
+      ld8(sQ + t * PQ + c8, v);
+      store_split8(phi + fo, plo + fo, v);
+    }
+    __syncthreads();  // the next task overwrites the staging rows and tables
+    cur = nxt;
   }
 }
 
@@ -901,8 +979,17 @@ hipError_t launch_prefill_mfma(const LayerArgs& a, void* ws, size_t, int ot, hip
   static const hipError_t attr_a = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_A);
   if (attr_a != hipSuccess) return attr_a;
+  // persistent: one workgroup per CU (the LDS use admits one), each looping over tasks
+  static const int ncu = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    return n;
+  }();
+  const int ntask = a.B * NC * a.H;
   timing_begin("kda_chunk_prep_kernel", s);
-  kda_chunk_prep_kernel<<<dim3(a.H, NC, a.B), NT, LDS_A, s>>>(a, tiles);
+  kda_chunk_prep_kernel<<<dim3(ntask < ncu ? ntask : ncu), NT, LDS_A, s>>>(a, tiles);
   timing_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
