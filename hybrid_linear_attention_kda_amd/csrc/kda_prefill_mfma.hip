@@ -63,6 +63,7 @@ constexpr int HALO = 3;      // staged rows before the chunk (conv width <= 4)
 constexpr int PQ = 132;      // fp32 pitch of [64][128] arrays
 constexpr int PKB = 136;     // bf16 pitch of [64][128] arrays
 constexpr int PA = 68;       // fp32 pitch of [64][64] arrays
+constexpr int PTB = 68;      // bf16 pitch of the [64][64] split planes (8-byte aligned rows)
 constexpr int PR = 280;      // bf16 pitch of the raw staging rows: q 128 | k 128 | v 16 | pad
 constexpr int RROWS = C + HALO;
 
@@ -81,7 +82,7 @@ constexpr int OFF_GC = OFF_FAC + 4 * D * 4;           // e^(Gam_C) [128]
 constexpr int OFF_BETA = OFF_GC + D * 4;              // [64]
 constexpr int OFF_NRM = OFF_BETA + C * 4;             // q / k normalisers [2][64]
 constexpr int OFF_SEG = OFF_NRM + 2 * C * 4;          // cumulative-sum segment totals [4][128]
-constexpr int OFF_AQK = OFF_SEG + 4 * D * 4;           // A_qk [64][PA] (formed while T's columns are)
+constexpr int OFF_AQK = OFF_SEG + 4 * D * 4;           // A_qk hi | lo [64][PTB] bf16 (formed while T is)
 constexpr int LDS_A = OFF_AQK + C * PA * 4;
 static_assert(STG_BYTES >= 2 * C * PA * 4 && STG_BYTES >= C * PQ * 4, "staging aliases");
 static_assert(LDS_A <= 160 * 1024, "LDS budget");
@@ -152,9 +153,11 @@ __device__ __forceinline__ void ld8(const float* p, float (&x)[8]) {
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-__device__ __forceinline__ void ld4(const float* p, float* x) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+// 8 bf16 at p and at p + off2 (4 + 4 elements), rows of 8-byte alignment
+__device__ __forceinline__ bf16x8 ld4x2(const __bf16* p, int off2) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + off2);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 // fp32 matrix core step: D += A[16 x 4] B[4 x 16]; lane l holds A[l % 16][l / 16] and B[l / 16][l % 16]
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
@@ -282,7 +285,10 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
   float* sGam = reinterpret_cast<float*>(smem + OFF_STG);
   float* sAkk = reinterpret_cast<float*>(smem + OFF_STG);
   float* sT = reinterpret_cast<float*>(smem + OFF_STG + C * PA * 4);
-  float* sAqk = reinterpret_cast<float*>(smem + OFF_AQK);
+  __bf16* sAhi = reinterpret_cast<__bf16*>(smem + OFF_AQK);  // A_qk split planes [64][PTB]
+  __bf16* sAlo = sAhi + C * PTB;
+  __bf16* sThi = reinterpret_cast<__bf16*>(smem + OFF_STG);  // T split planes, in place of A_kk
+  __bf16* sTlo = sThi + C * PTB;
   float* sTmp = reinterpret_cast<float*>(smem + OFF_TMP);
   float* sGn = reinterpret_cast<float*>(smem + OFF_GN);
   float* sEn = reinterpret_cast<float*>(smem + OFF_EN);
@@ -496,7 +502,36 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
     }
     __syncthreads();
 
-    // ---- P7: T = (I + A_kk)^-1 in fp32: diagonal 16x16 blocks by forward substitution ----
+    // ---- P6b: A_qk = QR_I E_IJ . KC_J^T (split bf16), lower incl. diagonal: one 16 x 16 block ----
+    auto aqk_block = [&](int bi) {
+      int I, J;
+      block_ij(bi, I, J);
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int c = 32 * s + 8 * lg;
+        float qv[8], kc[8];
+        ld8(sQ + (16 * I + l16) * PQ + c, qv);
+        if (I > J) {
+          const float* ef = sE + pair_index(I, J) * D + c;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qv[e] *= ef[e];
+        }
+        ld8(sG + (16 * J + l16) * PQ + c, kc);
+        acc = mfma3(split(qv), split(kc), acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * lg + r, j = 16 * J + l16;
+        const float v = j <= i ? acc[r] : 0.f;  // zero above the diagonal
+        const __bf16 hi = (__bf16)v;
+        sAhi[i * PTB + j] = hi;
+        sAlo[i * PTB + j] = (__bf16)(v - (float)hi);
+      }
+    };
+
+    // ---- P7: T = (I + A_kk)^-1 in fp32: diagonal 16x16 blocks by forward substitution on wave 0,
+    //      while waves 1-7 clear T's strictly-upper blocks and form A_qk blocks 0..6 ----
     if (wave == 0) {
       const int I = lg, cc = l16;
       float x[16];
@@ -517,10 +552,18 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
         const int J = blk6 < 3 ? blk6 + 1 : blk6 < 5 ? blk6 - 1 : 3;
         sT[(16 * I + (e >> 4)) * PA + 16 * J + (e & 15)] = 0.f;
       }
+      // A_qk blocks (0,1) and (2,3) lie inside the 32-token k-steps that P9 reads
+      for (int idx = tid - 64; idx < 2 * 256; idx += NT - 64) {
+        const int I = 2 * (idx >> 8), e = idx & 255;
+        const int o = (16 * I + (e >> 4)) * PTB + 16 * (I + 1) + (e & 15);
+        sAhi[o] = (__bf16)0.f;
+        sAlo[o] = (__bf16)0.f;
+      }
+      aqk_block(wave - 1);
     }
     __syncthreads();
     // Off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, column block J = wave (0..2)
-    // top to bottom on the fp32 matrix cores, while waves 3-7 form A_qk.
+    // top to bottom on the fp32 matrix cores, while waves 3-5 form A_qk blocks 7..9.
     if (wave < 3) {
       const int J = wave;
       float* sM = sTmp + wave * 16 * 17;
@@ -541,28 +584,20 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
         for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * lg + r) * PA + 16 * J + l16] = -tij[r];
         wave_lds_sync();
       }
-    } else {
-      // ---- P6b: A_qk = QR_I E_IJ . KC_J^T (split bf16), lower incl. diagonal ----
-      for (int bi = wave - 3; bi < 10; bi += 5) {
-        int I, J;
-        block_ij(bi, I, J);
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int c = 32 * s + 8 * lg;
-          float qv[8], kc[8];
-          ld8(sQ + (16 * I + l16) * PQ + c, qv);
-          if (I > J) {
-            const float* ef = sE + pair_index(I, J) * D + c;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qv[e] *= ef[e];
-          }
-          ld8(sG + (16 * J + l16) * PQ + c, kc);
-          acc = mfma3(split(qv), split(kc), acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sAqk[(16 * I + 4 * lg + r) * PA + 16 * J + l16] = acc[r];
-      }
+    } else if (wave < 6) {
+      aqk_block(wave + 4);
+    }
+    __syncthreads();
+    // T as split bf16 planes in place of A_kk: eight elements per lane
+    {
+      const int t = tid >> 3, j8 = (tid & 7) * 8;
+      float v[8];
+      ld8(sT + t * PA + j8, v);
+      const Split8 sp = split(v);
+      *reinterpret_cast<bf16x4*>(sThi + t * PTB + j8) = bf16x4{sp.hi[0], sp.hi[1], sp.hi[2], sp.hi[3]};
+      *reinterpret_cast<bf16x4*>(sThi + t * PTB + j8 + 4) = bf16x4{sp.hi[4], sp.hi[5], sp.hi[6], sp.hi[7]};
+      *reinterpret_cast<bf16x4*>(sTlo + t * PTB + j8) = bf16x4{sp.lo[0], sp.lo[1], sp.lo[2], sp.lo[3]};
+      *reinterpret_cast<bf16x4*>(sTlo + t * PTB + j8 + 4) = bf16x4{sp.lo[4], sp.lo[5], sp.lo[6], sp.lo[7]};
     }
     __syncthreads();
 
@@ -583,9 +618,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
           if (32 * s > 16 * I + 15) continue;  // T is lower triangular
-          float tvv[8];
-          ld8(sT + (16 * I + l16) * PA + 32 * s + 8 * lg, tvv);
-          wacc[I] = mfma(round8(tvv), bx, wacc[I]);
+          wacc[I] = mfma(ld4x2(sThi + (16 * I + l16) * PTB + 32 * s + 8 * lg, 4), bx, wacc[I]);
         }
       }
     }
@@ -681,9 +714,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           if (32 * st > 16 * I + 15) continue;  // T is lower triangular
-          float tr[8];
-          ld8(sT + (16 * I + l16) * PA + 32 * st + 8 * lg, tr);
-          ut[I] = mfma3(split(tr), bv[st], ut[I]);
+          const int o = (16 * I + l16) * PTB + 32 * st + 8 * lg;
+          ut[I] = mfma3(Split8{ld4x2(sThi + o, 4), ld4x2(sTlo + o, 4)}, bv[st], ut[I]);
         }
         utd[(I * 8 + wave) * 64 + lane] = ut[I];
       }
@@ -707,15 +739,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           if (32 * st > 16 * I + 15) continue;  // A_qk is lower triangular
-          float ar[8];
-          ld4(sAqk + t * PA + 32 * st + 4 * lg, ar);
-          ld4(sAqk + t * PA + 32 * st + 16 + 4 * lg, ar + 4);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int tok = 32 * st + 16 * (e >> 2) + 4 * lg + (e & 3);
-            ar[e] = tok <= t ? ar[e] : 0.f;
-          }
-          const Split8 as = split(ar);
+          const int o = t * PTB + 32 * st + 4 * lg;
+          const Split8 as{ld4x2(sAhi + o, 16), ld4x2(sAlo + o, 16)};
           ya = mfma3(as, ub[st], ya);
           pa = mfma(as.lo, wb[st], pa);
           pa = mfma(as.hi, wb[st], pa);
