@@ -104,15 +104,29 @@ constexpr int W_GC = W_Y + C * D * 4;      // e^Gam_C [128] fp32
 constexpr int CH_BYTES = W_GC + D * 4;     // 147968
 static_assert(CH_BYTES % 256 == 0, "tile blocks stay 256-byte aligned");
 
-// Phase B LDS layout (bytes)
+// Phase B: 8 compute waves and 4 loader waves per workgroup.
+constexpr int NTB = 768;
 constexpr int PVT = 72;                    // bf16 pitch of the [16][64] token-major U operand
 constexpr int PST = 136;                   // bf16 pitch of the [16][128] state operand
+// Phase B LDS layout (bytes): U and S operands, a scratch line for cache-warming loads, then two
+// buffers of the tiles the loader waves bring in (W, this block's Ut, K~^T hi / lo, e^Gam_C), each
+// byte-for-byte as in the workspace (1 KB fragments).
 constexpr int B_UHI = 0;
 constexpr int B_ULO = B_UHI + NVB * PVT * 2;
 constexpr int B_SHI = B_ULO + NVB * PVT * 2;
 constexpr int B_SLO = B_SHI + NVB * PST * 2;
-constexpr int LDS_B = B_SLO + NVB * PST * 2;
+constexpr int B_TRASH = B_SLO + NVB * PST * 2;   // 256 B, written by warming loads, never read
+constexpr int TB_W = 0;
+constexpr int TB_UT = TB_W + C * D * 2;
+constexpr int TB_KHI = TB_UT + 4 * 1024;
+constexpr int TB_KLO = TB_KHI + D * C * 2;
+constexpr int TB_GC = TB_KLO + D * C * 2;
+constexpr int TB_BYTES = TB_GC + D * 4;          // 53760
+constexpr int B_TB0 = B_TRASH + 256;
+constexpr int LDS_B = B_TB0 + 2 * TB_BYTES;
 static_assert(NVB == 16, "one accumulator column tile per phase-B workgroup");
+static_assert(B_TB0 % 16 == 0 && TB_BYTES % 16 == 0, "16-byte aligned tile buffers");
+static_assert(LDS_B <= 160 * 1024, "LDS budget");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -774,45 +788,46 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
 // ---------------------------------------------------------------------------------------------
 // Phase B: one workgroup per (16-column block of d_v, head, sequence), sequential over chunks.
 // Waves 0-3 form U = Ut - W S for row tile I = wave, waves 4-7 form O = P S + Y for row tile
-// I = wave - 4, and every wave then updates state rows 16*wave .. 16*wave+15.
+// I = wave - 4, and waves 0-7 then update state rows 16*wave .. 16*wave+15.  Waves 8-11 only
+// move data: while chunk c is computed they copy the tiles of chunk c+1 that waves 0-7 read
+// (W, Ut, K~^T, e^Gam_C) straight into LDS and touch chunk c+2 so that it is in L2; waves 4-7
+// load their own P and Y into registers a chunk ahead.
 // ---------------------------------------------------------------------------------------------
-struct OpTiles {        // this lane's operand fragments of one chunk
-  bf16x8 x0[4];         // waves 0-3: W | waves 4-7: P hi   (row tile I, 4 k-steps)
-  bf16x8 x1[4];         // waves 4-7: P lo
-  f32x4 y;              // waves 0-3: Ut tile | waves 4-7: Y tile   (row tile I, column tile vb)
-  bf16x8 k0[2], k1[2];  // all waves: K~^T hi / lo of channel tile = wave
-  float4 gc;            // e^Gam_C of the four state rows this lane holds
+// Operands the output waves (4-7) keep in registers: P hi / lo of their row tile and their Y tile.
+struct OpTiles {
+  bf16x8 x0[4], x1[4];  // P hi / lo, row tile I = wave - 4 (4 k-steps)
+  f32x4 y;              // Y tile (I, column tile vb)
 };
 
-// Every field but x1 is filled by one fixed sequence of loads for all waves (only the source
-// tiles differ by role); x1 (waves 4-7 only) comes last, so a wait on any other field never
-// waits for it.
-__device__ __forceinline__ void load_tiles(const unsigned char* blk, int wave, int lane, int lg, int vb, OpTiles& o) {
-  const int I = wave & 3;
-  const bool u_role = wave < 4;
-  const bf16x8* x0p = reinterpret_cast<const bf16x8*>(blk + (u_role ? W_W : W_PHI)) + (I * 4) * 64 + lane;
+__device__ __forceinline__ void load_out_tiles(const unsigned char* blk, int I, int lane, int vb, OpTiles& o) {
+  const bf16x8* x0p = reinterpret_cast<const bf16x8*>(blk + W_PHI) + (I * 4) * 64 + lane;
   const bf16x8* x1p = reinterpret_cast<const bf16x8*>(blk + W_PLO) + (I * 4) * 64 + lane;
-  const f32x4* yp = reinterpret_cast<const f32x4*>(blk + (u_role ? W_UT : W_Y)) + (I * 8 + vb) * 64 + lane;
-  const bf16x8* khp = reinterpret_cast<const bf16x8*>(blk + W_KTHI) + (wave * 2) * 64 + lane;
-  const bf16x8* klp = reinterpret_cast<const bf16x8*>(blk + W_KTLO) + (wave * 2) * 64 + lane;
 #pragma unroll
   for (int s = 0; s < 4; ++s) o.x0[s] = x0p[s * 64];
-  o.y = *yp;
+  o.y = reinterpret_cast<const f32x4*>(blk + W_Y)[(I * 8 + vb) * 64 + lane];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    o.k0[s] = khp[s * 64];
-    o.k1[s] = klp[s * 64];
-  }
-  o.gc = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(blk + W_GC) + 16 * wave + 4 * lg);
-  if (!u_role) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) o.x1[s] = x1p[s * 64];
-  }
+  for (int s = 0; s < 4; ++s) o.x1[s] = x1p[s * 64];
 }
 
-template <typename OT>
-__global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const unsigned char* __restrict__ ws,
-                                                          float* __restrict__ ows) {
+// Direct global -> LDS copies (gfx950 global_load_lds): lane l's bytes land at lds + l * size.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+// Workgroup barrier for LDS only: this wave's LDS operations complete, then s_barrier; the asm is
+// a compiler memory barrier.  Unlike __syncthreads it does not wait for outstanding global loads
+// (phase B shares no global memory between waves), so copies into LDS may stay in flight across
+// it; their issuing waves wait for them explicitly before the barrier that publishes them.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
+#define KDA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+__global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, const unsigned char* __restrict__ ws,
+                                                           float* __restrict__ ows) {
   extern __shared__ __align__(16) unsigned char smem[];
   __bf16* sUhi = reinterpret_cast<__bf16*>(smem + B_UHI);
   __bf16* sUlo = reinterpret_cast<__bf16*>(smem + B_ULO);
@@ -825,13 +840,71 @@ __global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const 
   const int b = blockIdx.y;
   const int NC = (T + C - 1) / C;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: role branches are uniform
   const int l16 = lane & 15, lg = lane >> 4;
   const int HD = H * D;
   const unsigned char* __restrict__ head_ws = ws + ((long long)b * H + h) * NC * (long long)CH_BYTES;
+  auto tbuf = [&](int c) { return smem + B_TB0 + (c & 1) * TB_BYTES; };
 
-  // State block: wave w owns channel rows 16w..16w+15; lane holds rows 16w+4lg+r of column
-  // vb*16 + l16.
+  // ---- loader waves: tiles of chunk cn into its LDS buffer; cache lines of chunk cw touched ----
+  const int lw = wave - 8;
+  auto issue_chunk = [&](int cn) {
+    const unsigned char* blk = head_ws + (long long)cn * CH_BYTES;
+    unsigned char* tb = tbuf(cn);
+    if (lw == 0) {
+#pragma unroll
+      for (int f = 0; f < 16; ++f) dma16(blk + W_W + f * 1024 + lane * 16, tb + TB_W + f * 1024);
+    } else if (lw == 1) {
+#pragma unroll
+      for (int f = 0; f < 16; ++f) dma16(blk + W_KTHI + f * 1024 + lane * 16, tb + TB_KHI + f * 1024);
+    } else if (lw == 2) {
+#pragma unroll
+      for (int f = 0; f < 16; ++f) dma16(blk + W_KTLO + f * 1024 + lane * 16, tb + TB_KLO + f * 1024);
+    } else {
+#pragma unroll
+      for (int I = 0; I < 4; ++I) dma16(blk + W_UT + (I * 8 + vb) * 1024 + lane * 16, tb + TB_UT + I * 1024);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) dma4(blk + W_GC + q * 256 + lane * 4, tb + TB_GC + q * 256);
+    }
+  };
+  // the 8 workgroups of a head touch one eighth each of a chunk's 128-byte lines (one 4-byte copy
+  // per line), so that the chunk is in L2 when its tiles are fetched a chunk later
+  constexpr int LINES = CH_BYTES / 128;
+  constexpr int LINES_PER_WG = (LINES + NBLK - 1) / NBLK;
+  constexpr int TOUCH_PER_WAVE = (LINES_PER_WG + 4 * 64 - 1) / (4 * 64);
+  auto touch_chunk = [&](int cw) {
+    const unsigned char* blk = head_ws + (long long)cw * CH_BYTES;
+#pragma unroll
+    for (int q = 0; q < TOUCH_PER_WAVE; ++q) {
+      const int line = min(vb * LINES_PER_WG + min((q * 4 + lw) * 64 + lane, LINES_PER_WG - 1), LINES - 1);
+      dma4(blk + line * 128, smem + B_TRASH);
+    }
+  };
+
+  if (wave >= 8) {
+    // Loader waves: their own loop, with the same two barriers per chunk as the compute waves.
+    // While chunk ci is computed they copy chunk ci+1 into the other buffer (free: its previous
+    // chunk's last reads came before barrier (a)) and touch chunk ci+2; before the barrier that
+    // opens chunk ci+1 they wait for the copies (the touches may stay in flight).
+    issue_chunk(0);
+    if (NC > 1) touch_chunk(1);
+    KDA_WAIT_VMCNT(0);
+    for (int ci = 0; ci < NC; ++ci) {
+      lds_barrier();  // (a)
+      if (ci + 1 < NC) issue_chunk(ci + 1);
+      if (ci + 2 < NC) touch_chunk(ci + 2);
+      lds_barrier();  // (b)
+      if (ci + 2 < NC)
+        KDA_WAIT_VMCNT(TOUCH_PER_WAVE);
+      else
+        KDA_WAIT_VMCNT(0);
+    }
+    return;
+  }
+
+  // ---- compute waves: state block, wave w owns channel rows 16w..16w+15; lane holds rows
+  //      16w+4lg+r of column vb*16 + l16 ----
   f32x4 Sacc;
   {
     const float* sp = a.state_in + ((long long)b * H + h) * D * D + vb * NVB + l16;
@@ -850,49 +923,91 @@ __global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const 
     *reinterpret_cast<bf16x4*>(sSlo + l16 * PST + 16 * wave + 4 * lg) = lo;
   };
 
-  // Output rows of the previous chunk, held in registers until the next chunk has started so
-  // that their stores are issued before that chunk's prefetch.
-  f32x4 opend;
+  // Output rows of the previous chunk (waves 4-7), held in registers until the next chunk has
+  // started so that their stores are issued before that chunk's prefetch.
+  // Rows past the end of the sequence go to a scratch slot after o, so that every lane issues the
+  // same stores.
+  f32x4 opend = zero4();
+  float* scratch = ows + (long long)a.B * T * HD + lane * 4;
   auto store_pending = [&](int pc) {
-    if (pc < 0 || wave < 4) return;
+    if (pc < 0) return;
     const int pc0 = pc * C, pL = min(C, T - pc0);
     float* op = ows + (((long long)b * T + pc0) * H + h) * D + vb * NVB + l16;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * (wave - 4) + 4 * lg + r;
-      if (t < pL) op[(long long)t * HD] = opend[r];
+      *(t < pL ? op + (long long)t * HD : scratch + r) = opend[r];
     }
   };
 
-  // One chunk: operands in cur, those of chunk ci + 2 prefetched into nxt (two chunks of
-  // latency cover a miss in L2 even though loads return in order).  Three register sets rotate
-  // through the roles, so no loaded value is ever copied.
-  auto chunk = [&](int ci, const OpTiles& cur, OpTiles& nxt) __attribute__((always_inline)) {
-    store_pending(ci - 1);
-    // the last chunks prefetch the last one again: the loads stay unconditional
-    load_tiles(head_ws + (long long)min(ci + 1, NC - 1) * CH_BYTES, wave, lane, lg, vb, nxt);
-    __syncthreads();  // the state operand of this chunk is in LDS
-    if (wave < 4) {
-      // U = Ut - W S for row tile I = wave, as the split B operand [column][token]
+  // S <- e^Gam_C S + K~^T U from chunk ci's buffer, then the state operand for the next chunk
+  // (every read of the old one came before barrier (b)).
+  auto state_update = [&](const unsigned char* tb) {
+    const float4 gc = *reinterpret_cast<const float4*>(tb + TB_GC + (16 * wave + 4 * lg) * 4);
+    f32x4 sa, sb = zero4();
+    sa[0] = gc.x * Sacc[0];
+    sa[1] = gc.y * Sacc[1];
+    sa[2] = gc.z * Sacc[2];
+    sa[3] = gc.w * Sacc[3];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(tb + TB_KHI + ((wave * 2 + s) * 64 + lane) * 16);
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(tb + TB_KLO + ((wave * 2 + s) * 64 + lane) * 16);
+      const bf16x8 uh = *reinterpret_cast<const bf16x8*>(sUhi + l16 * PVT + 32 * s + 8 * lg);
+      const bf16x8 ul = *reinterpret_cast<const bf16x8*>(sUlo + l16 * PVT + 32 * s + 8 * lg);
+      sa = mfma(k0, uh, sa);
+      sb = mfma(k0, ul, sb);
+      sb = mfma(k1, uh, sb);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Sacc[r] = sa[r] + sb[r];
+    write_state_operand();
+  };
+
+  // Each role runs its own loop (so that no wave's waits are derived from another role's loads),
+  // with the same two barriers per chunk: (a) the state operand and chunk ci's tile buffer
+  // (complete: the loaders waited before it) are in LDS; (b) U is in LDS and every read of the
+  // state operand is done.
+  write_state_operand();
+  if (wave < 4) {
+    // U = Ut - W S for row tile I = wave, as the split B operand [column][token]
+    const int I = wave;
+    for (int ci = 0; ci < NC; ++ci) {
+      const unsigned char* tb = tbuf(ci);
+      lds_barrier();  // (a)
       f32x4 pa = zero4(), pb = zero4();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
+        const bf16x8 w = *reinterpret_cast<const bf16x8*>(tb + TB_W + ((I * 4 + s) * 64 + lane) * 16);
         const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
         const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSlo + l16 * PST + 32 * s + 8 * lg);
-        pa = mfma(cur.x0[s], sh, pa);
-        pb = mfma(cur.x0[s], sl, pb);
+        pa = mfma(w, sh, pa);
+        pb = mfma(w, sl, pb);
       }
+      const f32x4 ut = *reinterpret_cast<const f32x4*>(tb + TB_UT + (I * 64 + lane) * 16);
       bf16x4 hi, lo;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float u = cur.y[r] - (pa[r] + pb[r]);
+        const float u = ut[r] - (pa[r] + pb[r]);
         hi[r] = (__bf16)u;
         lo[r] = (__bf16)(u - (float)hi[r]);
       }
-      *reinterpret_cast<bf16x4*>(sUhi + l16 * PVT + 16 * wave + 4 * lg) = hi;
-      *reinterpret_cast<bf16x4*>(sUlo + l16 * PVT + 16 * wave + 4 * lg) = lo;
-    } else {
-      // O = P S + Y for row tile I = wave - 4
+      *reinterpret_cast<bf16x4*>(sUhi + l16 * PVT + 16 * I + 4 * lg) = hi;
+      *reinterpret_cast<bf16x4*>(sUlo + l16 * PVT + 16 * I + 4 * lg) = lo;
+      lds_barrier();  // (b)
+      state_update(tb);
+    }
+  } else {
+    // O = P S + Y for row tile I = wave - 4, P and Y in registers a chunk ahead (two register
+    // sets alternate, so no loaded value is copied); the output rows of chunk ci are stored at
+    // the start of chunk ci + 1, before its prefetch.
+    const int I = wave - 4;
+    auto chunk_o = [&](int ci, const OpTiles& cur, OpTiles& nxt) __attribute__((always_inline)) {
+      const unsigned char* tb = tbuf(ci);
+      store_pending(ci - 1);
+      // the last chunk prefetches itself again: the loads stay unconditional
+      load_out_tiles(head_ws + (long long)min(ci + 1, NC - 1) * CH_BYTES, I, lane, vb, nxt);
+      lds_barrier();  // (a)
       f32x4 oa = zero4(), ob = zero4();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -904,37 +1019,19 @@ __global__ __launch_bounds__(NT) void kda_chunk_state_kernel(LayerArgs a, const 
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) opend[r] = (oa[r] + ob[r]) + cur.y[r];
+      lds_barrier();  // (b)
+      state_update(tb);
+    };
+    OpTiles ta, tb2;
+    load_out_tiles(head_ws, I, lane, vb, ta);
+    int ci = 0;
+    for (; ci + 1 < NC; ci += 2) {
+      chunk_o(ci, ta, tb2);
+      chunk_o(ci + 1, tb2, ta);
     }
-    __syncthreads();  // U is in LDS and every read of the state operand is done
-    // S <- e^Gam_C S + K~^T U
-    f32x4 sa, sb = zero4();
-    sa[0] = cur.gc.x * Sacc[0];
-    sa[1] = cur.gc.y * Sacc[1];
-    sa[2] = cur.gc.z * Sacc[2];
-    sa[3] = cur.gc.w * Sacc[3];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bf16x8 uh = *reinterpret_cast<const bf16x8*>(sUhi + l16 * PVT + 32 * s + 8 * lg);
-      const bf16x8 ul = *reinterpret_cast<const bf16x8*>(sUlo + l16 * PVT + 32 * s + 8 * lg);
-      sa = mfma(cur.k0[s], uh, sa);
-      sb = mfma(cur.k0[s], ul, sb);
-      sb = mfma(cur.k1[s], uh, sb);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Sacc[r] = sa[r] + sb[r];
-    write_state_operand();
-  };
-
-  OpTiles ta, tb;
-  load_tiles(head_ws, wave, lane, lg, vb, ta);
-  write_state_operand();
-  int ci = 0;
-  for (; ci + 1 < NC; ci += 2) {
-    chunk(ci, ta, tb);
-    chunk(ci + 1, tb, ta);
+    if (ci < NC) chunk_o(ci, ta, tb2);
+    store_pending(NC - 1);
   }
-  if (ci < NC) chunk(ci, ta, tb);
-  store_pending(NC - 1);
 
   {
     float* sp = a.state_out + ((long long)b * H + h) * D * D + vb * NVB + l16;
@@ -994,7 +1091,7 @@ bool prefill_mfma_supported(int Dh, int chunk, int io, int W, float lb) {
 
 size_t prefill_mfma_workspace(int B, int T, int H, int Dh, int) {
   const size_t nc = (size_t)(T + C - 1) / C;
-  return (size_t)B * H * nc * CH_BYTES + (size_t)B * T * H * Dh * sizeof(float);
+  return (size_t)B * H * nc * CH_BYTES + (size_t)B * T * H * Dh * sizeof(float) + 64 * 4 * sizeof(float);
 }
 
 hipError_t launch_prefill_mfma(const LayerArgs& a, void* ws, size_t, int ot, hipStream_t s) {
@@ -1018,12 +1115,12 @@ hipError_t launch_prefill_mfma(const LayerArgs& a, void* ws, size_t, int ot, hip
   timing_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  static const hipError_t attr_b = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_state_kernel),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_B);
+  if (attr_b != hipSuccess) return attr_b;
   const dim3 grid_b(NBLK * a.H, a.B);
   timing_begin("kda_chunk_state_kernel", s);
-  if (ot == kBF16)
-    kda_chunk_state_kernel<bf16_t><<<grid_b, NT, LDS_B, s>>>(a, tiles, ows);
-  else
-    kda_chunk_state_kernel<float><<<grid_b, NT, LDS_B, s>>>(a, tiles, ows);
+  kda_chunk_state_kernel<<<grid_b, NTB, LDS_B, s>>>(a, tiles, ows);
   timing_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long rows = (long long)a.B * a.T * a.H;
