@@ -849,21 +849,20 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, const
 
   // ---- loader waves: tiles of chunk cn into its LDS buffer; cache lines of chunk cw touched ----
   const int lw = wave - 8;
-  auto issue_chunk = [&](int cn) {
+  // half 0 / 1 of this wave's copies for chunk cn (issued in the two halves of the chunk before,
+  // so that no burst holds a barrier)
+  auto issue_chunk = [&](int cn, int half) {
     const unsigned char* blk = head_ws + (long long)cn * CH_BYTES;
     unsigned char* tb = tbuf(cn);
-    if (lw == 0) {
+    if (lw < 3) {
+      const int src = lw == 0 ? W_W : lw == 1 ? W_KTHI : W_KTLO;
+      const int dst = lw == 0 ? TB_W : lw == 1 ? TB_KHI : TB_KLO;
 #pragma unroll
-      for (int f = 0; f < 16; ++f) dma16(blk + W_W + f * 1024 + lane * 16, tb + TB_W + f * 1024);
-    } else if (lw == 1) {
-#pragma unroll
-      for (int f = 0; f < 16; ++f) dma16(blk + W_KTHI + f * 1024 + lane * 16, tb + TB_KHI + f * 1024);
-    } else if (lw == 2) {
-#pragma unroll
-      for (int f = 0; f < 16; ++f) dma16(blk + W_KTLO + f * 1024 + lane * 16, tb + TB_KLO + f * 1024);
-    } else {
+      for (int f = 8 * half; f < 8 * half + 8; ++f) dma16(blk + src + f * 1024 + lane * 16, tb + dst + f * 1024);
+    } else if (half == 0) {
 #pragma unroll
       for (int I = 0; I < 4; ++I) dma16(blk + W_UT + (I * 8 + vb) * 1024 + lane * 16, tb + TB_UT + I * 1024);
+    } else {
 #pragma unroll
       for (int q = 0; q < 2; ++q) dma4(blk + W_GC + q * 256 + lane * 4, tb + TB_GC + q * 256);
     }
@@ -887,18 +886,17 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, const
     // While chunk ci is computed they copy chunk ci+1 into the other buffer (free: its previous
     // chunk's last reads came before barrier (a)) and touch chunk ci+2; before the barrier that
     // opens chunk ci+1 they wait for the copies (the touches may stay in flight).
-    issue_chunk(0);
+    issue_chunk(0, 0);
+    issue_chunk(0, 1);
     if (NC > 1) touch_chunk(1);
     KDA_WAIT_VMCNT(0);
     for (int ci = 0; ci < NC; ++ci) {
       lds_barrier();  // (a)
-      if (ci + 1 < NC) issue_chunk(ci + 1);
+      if (ci + 1 < NC) issue_chunk(ci + 1, 0);
       if (ci + 2 < NC) touch_chunk(ci + 2);
       lds_barrier();  // (b)
-      if (ci + 2 < NC)
-        KDA_WAIT_VMCNT(TOUCH_PER_WAVE);
-      else
-        KDA_WAIT_VMCNT(0);
+      if (ci + 1 < NC) issue_chunk(ci + 1, 1);
+      KDA_WAIT_VMCNT(0);
     }
     return;
   }
