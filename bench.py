@@ -73,12 +73,10 @@ def kernel_alg_bytes(kernel, wp, wd, wv, accepted):
     table = {
         # qkv, f, beta of every token, the conv state in, conv weights, A_log, dt_bias
         "kda_chunk_prep_kernel": Tp * (3 * Hp * Dp * io_b + Hp * Dp * io_b + Hp * io_b) + conv + params,
-        # fp32 state in and out
-        "kda_chunk_state_kernel": 2 * Hp * Dp * Dp * 4,
+        # fp32 state in and out, conv state out
+        "kda_chunk_state_kernel": 2 * Hp * Dp * Dp * 4 + conv,
         # g_out in, out written, norm weight
         "kda_out_norm_kernel": Tp * 2 * Hp * Dp * io_b + Dp * io_b,
-        # conv state out
-        "kda_conv_state_kernel": conv,
         "kda_recurrent_kernel[decode]": decode_bytes(wd.B, wd.H, wd.dk, wd.W),
         "kda_recurrent_kernel[verify]": verify_bytes(wv.B, wv.T, wv.H, wv.dk, wv.W),
         "kda_rollback_kernel": rollback_bytes(accepted or [], wv.H, wv.dk, wv.W),

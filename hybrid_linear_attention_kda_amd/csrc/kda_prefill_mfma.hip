@@ -46,7 +46,7 @@
 //
 // The output RMSNorm needs all 128 columns of o, which live in eight
 // workgroups, so o (fp32) goes to the workspace and a third, bandwidth-bound
-// kernel applies the norm, weight and gate; a fourth writes the new conv state.
+// kernel applies the norm, weight and gate.  Phase B's loader waves also write the new conv state.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -898,6 +898,25 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, const
       if (ci + 1 < NC) issue_chunk(ci + 1, 1);
       KDA_WAIT_VMCNT(0);
     }
+    // The new conv state of this workgroup's 48 channels (16 each of q, k and v): the last W-1
+    // raw inputs, from the conv state passed in where the call has fewer tokens.
+    const int j = tid - 8 * 64;
+    if (a.W > 1 && a.conv_out != nullptr && j < 48) {
+      const int W = a.W, Cq = 3 * HD;
+      const long long c = (long long)(j >> 4) * HD + h * D + vb * NVB + (j & 15);
+      const bf16_t* x = static_cast<const bf16_t*>(a.qkv);
+      const bf16_t* cin = static_cast<const bf16_t*>(a.conv_in) + ((long long)b * Cq + c) * (W - 1);
+      bf16_t* cout = static_cast<bf16_t*>(a.conv_out) + ((long long)b * Cq + c) * (W - 1);
+      bf16_t win[3];
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+        const int tt = T - (W - 1) + w;
+        if (w < W - 1) win[w] = tt >= 0 ? x[((long long)b * T + tt) * Cq + c] : cin[(W - 1) + tt];
+      }
+#pragma unroll
+      for (int w = 0; w < 3; ++w)
+        if (w < W - 1) cout[w] = win[w];
+    }
     return;
   }
 
@@ -1057,27 +1076,6 @@ __global__ __launch_bounds__(256) void kda_out_norm_kernel(const float* __restri
 }
 
 // New conv state: the last W-1 raw inputs of (conv state || this call's tokens), per channel.
-__global__ __launch_bounds__(256) void kda_conv_state_kernel(LayerArgs a) {
-  const int Cq = 3 * a.H * a.D;
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  const int b = blockIdx.y;
-  if (c >= Cq) return;
-  const int W = a.W, T = a.T;
-  const bf16_t* x = static_cast<const bf16_t*>(a.qkv);
-  bf16_t* cs = static_cast<bf16_t*>(a.conv_out);
-  const bf16_t* ci = static_cast<const bf16_t*>(a.conv_in);
-  bf16_t win[3];
-#pragma unroll
-  for (int w = 0; w < 3; ++w) {
-    if (w < W - 1) {
-      const int tt = T - (W - 1) + w;
-      win[w] = tt >= 0 ? x[((long long)b * T + tt) * Cq + c] : ci[((long long)b * Cq + c) * (W - 1) + (W - 1) + tt];
-    }
-  }
-#pragma unroll
-  for (int w = 0; w < 3; ++w)
-    if (w < W - 1) cs[((long long)b * Cq + c) * (W - 1) + w] = win[w];
-}
 
 }  // namespace
 
@@ -1133,15 +1131,7 @@ hipError_t launch_prefill_mfma(const LayerArgs& a, void* ws, size_t, int ot, hip
                                                   static_cast<const bf16_t*>(a.norm_w), static_cast<float*>(a.out), rows,
                                                   a.rms_eps);
   timing_end(s);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (a.W > 1 && a.conv_out != nullptr) {
-    const int Cq = 3 * a.H * a.D;
-    timing_begin("kda_conv_state_kernel", s);
-    kda_conv_state_kernel<<<dim3((Cq + 255) / 256, a.B), 256, 0, s>>>(a);
-    timing_end(s);
-    e = hipGetLastError();
-  }
-  return e;
+  return hipGetLastError();
 }
 
 }  // namespace kda
