@@ -1057,22 +1057,50 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, const
   }
 }
 
+// Gated output RMSNorm over the 128 columns of each (token, head) row of o: 16 lanes per row,
+// 8 columns per lane, 16-byte loads and stores.
+__device__ __forceinline__ void store8(bf16_t* p, const float (&v)[8]) {
+  uint4 u;
+  u.x = f32_to_bf16(v[0]) | (uint32_t)f32_to_bf16(v[1]) << 16;
+  u.y = f32_to_bf16(v[2]) | (uint32_t)f32_to_bf16(v[3]) << 16;
+  u.z = f32_to_bf16(v[4]) | (uint32_t)f32_to_bf16(v[5]) << 16;
+  u.w = f32_to_bf16(v[6]) | (uint32_t)f32_to_bf16(v[7]) << 16;
+  *reinterpret_cast<uint4*>(p) = u;
+}
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void unpack8(const uint4 u, float (&v)[8]) {
+  v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+  v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+  v[4] = __uint_as_float(u.z << 16); v[5] = __uint_as_float(u.z & 0xffff0000u);
+  v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+
 template <typename OT>
 __global__ __launch_bounds__(256) void kda_out_norm_kernel(const float* __restrict__ ows, const bf16_t* __restrict__ gout,
                                                         const bf16_t* __restrict__ nw, OT* __restrict__ out,
                                                         long long rows, float eps) {
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const float2 o = *reinterpret_cast<const float2*>(ows + row * D + 2 * lane);
-  const float ss = wave_sum(o.x * o.x + o.y * o.y);
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int c8 = (threadIdx.x & 15) * 8;
+  if (row >= rows) return;  // the 16 lanes of a row leave together
+  const float4 a0 = *reinterpret_cast<const float4*>(ows + row * D + c8);
+  const float4 a1 = *reinterpret_cast<const float4*>(ows + row * D + c8 + 4);
+  const uint4 g = *reinterpret_cast<const uint4*>(gout + row * D + c8);
+  const uint4 w = *reinterpret_cast<const uint4*>(nw + c8);
+  const float o[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += o[e] * o[e];
+  ss = group_sum<16>(ss);
   const float rr = rsqrtf(ss / (float)D + eps);
-  const uint32_t g2 = *reinterpret_cast<const uint32_t*>(gout + row * D + 2 * lane);
-  const uint32_t w2 = *reinterpret_cast<const uint32_t*>(nw + 2 * lane);
-  const float g0 = __uint_as_float(g2 << 16), g1 = __uint_as_float(g2 & 0xffff0000u);
-  const float w0 = __uint_as_float(w2 << 16), w1 = __uint_as_float(w2 & 0xffff0000u);
-  store_as(out + row * D + 2 * lane, o.x * rr * w0 / (1.0f + __expf(-g0)));
-  store_as(out + row * D + 2 * lane + 1, o.y * rr * w1 / (1.0f + __expf(-g1)));
+  float gv[8], wv[8], r[8];
+  unpack8(g, gv);
+  unpack8(w, wv);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = o[e] * rr * wv[e] / (1.0f + __expf(-gv[e]));
+  store8(out + row * D + c8, r);
 }
 
 // New conv state: the last W-1 raw inputs of (conv state || this call's tokens), per channel.
@@ -1120,7 +1148,7 @@ hipError_t launch_prefill_mfma(const LayerArgs& a, void* ws, size_t, int ot, hip
   timing_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long rows = (long long)a.B * a.T * a.H;
-  const dim3 ng((unsigned)((rows + 3) / 4));
+  const dim3 ng((unsigned)((rows + 15) / 16));
   timing_begin("kda_out_norm_kernel", s);
   if (ot == kBF16)
     kda_out_norm_kernel<bf16_t><<<ng, 256, 0, s>>>(ows, static_cast<const bf16_t*>(a.g_out),
