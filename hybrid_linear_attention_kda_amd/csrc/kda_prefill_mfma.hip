@@ -71,7 +71,7 @@ constexpr int RROWS = C + HALO;
 constexpr int OFF_Q = 0;                              // q^ -> QR = q e^(Gam - Gam_n) -> P
 constexpr int OFF_KB = OFF_Q + C * PQ * 4;            // KR (bf16) -> W (bf16)
 constexpr int OFF_G = OFF_KB + C * PKB * 2;           // k^ -> KC = k e^(Gam_n - Gam) -> raw v rows
-constexpr int OFF_STG = OFF_G + C * PQ * 4;           // raw staging | Gam | A_kk + T | A_qk
+constexpr int OFF_STG = OFF_G + C * PQ * 4;           // raw q|k staging | A_kk + T (-> T split planes)
 constexpr int STG_BYTES = RROWS * PR * 2;             // 37520 >= 2 * C * PA * 4 and >= C * PQ * 4
 constexpr int OFF_TMP = OFF_STG + STG_BYTES;          // scratch while forming T [1024]
 constexpr int OFF_GN = OFF_TMP + 1024 * 4;            // Gam at the four anchors + Gam_C [5][128]
@@ -84,7 +84,7 @@ constexpr int OFF_NRM = OFF_BETA + C * 4;             // q / k normalisers [2][6
 constexpr int OFF_SEG = OFF_NRM + 2 * C * 4;          // cumulative-sum segment totals [4][128]
 constexpr int OFF_AQK = OFF_SEG + 4 * D * 4;           // A_qk hi | lo [64][PTB] bf16 (formed while T is)
 constexpr int LDS_A = OFF_AQK + C * PA * 4;
-static_assert(STG_BYTES >= 2 * C * PA * 4 && STG_BYTES >= C * PQ * 4, "staging aliases");
+static_assert(STG_BYTES >= 2 * C * PA * 4, "staging aliases");
 static_assert(LDS_A <= 160 * 1024, "LDS budget");
 
 // Workspace tile block per (sequence, head, chunk), written by phase A and read by phase B.
@@ -296,7 +296,6 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
   __bf16* sKb = reinterpret_cast<__bf16*>(smem + OFF_KB);
   float* sG = reinterpret_cast<float*>(smem + OFF_G);
   __bf16* sRaw = reinterpret_cast<__bf16*>(smem + OFF_STG);
-  float* sGam = reinterpret_cast<float*>(smem + OFF_STG);
   float* sAkk = reinterpret_cast<float*>(smem + OFF_STG);
   float* sT = reinterpret_cast<float*>(smem + OFF_STG + C * PA * 4);
   __bf16* sAhi = reinterpret_cast<__bf16*>(smem + OFF_AQK);  // A_qk split planes [64][PTB]
@@ -413,12 +412,13 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
     PrepIn nxt;
     prep_issue(a, knext, tid, nxt, 0);
 
-    // ---- P3: bounded-sigmoid gate and its cumulative sum (lane -> channel, 16-token segment) ----
+    // ---- P3: bounded-sigmoid gate and its cumulative sum (lane -> channel, 16-token segment);
+    //      gl[k] = Gam(16 seg + k) - Gam(16 seg - 1) stays in registers for P5 ----
+    float gl[16];
     {
       const int i = tid & 127, seg = tid >> 7;
       const float Ah = __expf(alog);
       const float dtb = sDtb[i];
-      float gl[16];
       float acc = 0.f;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
@@ -453,8 +453,6 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
       __syncthreads();
       float off = 0.f;
       for (int s = 0; s < seg; ++s) off += sSeg[s * D + i];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) sGam[(16 * seg + k) * PQ + i] = gl[k] + off;
       sGn[seg * D + i] = gl[0] + off;
       if (seg == 3) sGn[4 * D + i] = gl[15] + off;
     }
@@ -462,18 +460,26 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
 
     prep_issue(a, knext, tid, nxt, 1);
 
-    // ---- P5: anchored operands QR, KR (bf16), KC and the per-channel factor tables ----
-    for (int idx = tid; idx < C * D; idx += NT) {
-      const int t = idx >> 7, c = idx & 127;
-      const float G = sGam[t * PQ + c];
-      const float Gn = sGn[(t >> 4) * D + c];
-      const float e1 = __expf(G - Gn);  // <= 1
-      const float e2 = __expf(Gn - G);  // in [1, e^(15|lb|)]
-      const float q = sQ[t * PQ + c] * sNrm[t];
-      const float k = sG[t * PQ + c] * sNrm[C + t];
-      sQ[t * PQ + c] = q * e1;
-      sKb[t * PKB + c] = (__bf16)(k * e1);
-      sG[t * PQ + c] = k * e2;
+    // ---- P5: anchored operands QR, KR (bf16), KC (lane -> channel, 16-token segment, as in P3:
+    //      Gam_t - Gam_n(I) = gl[k] - gl[0]) and the per-channel factor tables ----
+    {
+      const int i = tid & 127, seg = tid >> 7;
+      float* qp = sQ + 16 * seg * PQ + i;
+      float* kp = sG + 16 * seg * PQ + i;
+      __bf16* rp = sKb + 16 * seg * PKB + i;
+      const float* nq = sNrm + 16 * seg;
+      const float* nk = sNrm + C + 16 * seg;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float d = gl[k] - gl[0];
+        const float e1 = __expf(d);   // <= 1
+        const float e2 = __expf(-d);  // in [1, e^(15|lb|)]
+        const float q = qp[k * PQ] * nq[k];
+        const float kv = kp[k * PQ] * nk[k];
+        qp[k * PQ] = q * e1;
+        rp[k * PKB] = (__bf16)(kv * e1);
+        kp[k * PQ] = kv * e2;
+      }
     }
     if (tid < D) {
       const int c = tid;
@@ -547,15 +553,18 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
     // ---- P7: T = (I + A_kk)^-1 in fp32: diagonal 16x16 blocks by forward substitution on wave 0,
     //      while waves 1-7 clear T's strictly-upper blocks and form A_qk blocks 0..6 ----
     if (wave == 0) {
+      // lane: column cc of diagonal block I.  Column-oriented: once x[j] is final it is folded
+      // into every row below at once, so the dependent chain is 16 steps long; each x[i] still
+      // accumulates its terms in the order j = 0, 1, ...
       const int I = lg, cc = l16;
+      const float* aI = sAkk + 16 * I * PA + 16 * I;
       float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v = (i == cc) ? 1.f : 0.f;
+      for (int i = 0; i < 16; ++i) x[i] = (i == cc) ? 1.f : 0.f;
 #pragma unroll
-        for (int j = 0; j < i; ++j) v -= sAkk[(16 * I + i) * PA + 16 * I + j] * x[j];
-        x[i] = v;
-      }
+      for (int j = 0; j < 15; ++j)
+#pragma unroll
+        for (int i = j + 1; i < 16; ++i) x[i] -= aI[i * PA + j] * x[j];
 #pragma unroll
       for (int i = 0; i < 16; ++i) sT[(16 * I + i) * PA + 16 * I + cc] = x[i];
     } else {
