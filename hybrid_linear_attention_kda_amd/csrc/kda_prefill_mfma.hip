@@ -108,7 +108,7 @@ static_assert(CH_BYTES % 256 == 0, "tile blocks stay 256-byte aligned");
 constexpr int NTB = 768;
 constexpr int PVT = 72;                    // bf16 pitch of the [16][64] token-major U operand
 constexpr int PST = 136;                   // bf16 pitch of the [16][128] state operand
-// Phase B LDS layout (bytes): U and S operands, a scratch line for cache-warming loads, then two
+// Phase B LDS layout (bytes): U and S operands, a scratch line for cache-warming loads, then the
 // buffers of the tiles the loader waves bring in (W, this block's Ut, K~^T hi / lo, e^Gam_C), each
 // byte-for-byte as in the workspace (1 KB fragments).
 constexpr int B_UHI = 0;
@@ -116,16 +116,20 @@ constexpr int B_ULO = B_UHI + NVB * PVT * 2;
 constexpr int B_SHI = B_ULO + NVB * PVT * 2;
 constexpr int B_SLO = B_SHI + NVB * PST * 2;
 constexpr int B_TRASH = B_SLO + NVB * PST * 2;   // 256 B, written by warming loads, never read
-constexpr int TB_W = 0;
-constexpr int TB_UT = TB_W + C * D * 2;
-constexpr int TB_KHI = TB_UT + 4 * 1024;
-constexpr int TB_KLO = TB_KHI + D * C * 2;
-constexpr int TB_GC = TB_KLO + D * C * 2;
-constexpr int TB_BYTES = TB_GC + D * 4;          // 53760
-constexpr int B_TB0 = B_TRASH + 256;
-constexpr int LDS_B = B_TB0 + 2 * TB_BYTES;
+// W and Ut are read before barrier (b), K~^T and e^Gam_C after it, so they sit in separate
+// buffers: three of W | Ut (copied two chunks ahead) and two of K~^T | e^Gam_C.
+constexpr int WU_W = 0;
+constexpr int WU_UT = WU_W + C * D * 2;
+constexpr int WU_BYTES = WU_UT + 4 * 1024;       // 20480
+constexpr int KB_KHI = 0;
+constexpr int KB_KLO = KB_KHI + D * C * 2;
+constexpr int KB_GC = KB_KLO + D * C * 2;
+constexpr int KB_BYTES = KB_GC + D * 4;          // 33280
+constexpr int B_WU0 = B_TRASH + 256;
+constexpr int B_KB0 = B_WU0 + 3 * WU_BYTES;
+constexpr int LDS_B = B_KB0 + 2 * KB_BYTES;
 static_assert(NVB == 16, "one accumulator column tile per phase-B workgroup");
-static_assert(B_TB0 % 16 == 0 && TB_BYTES % 16 == 0, "16-byte aligned tile buffers");
+static_assert(B_WU0 % 16 == 0 && WU_BYTES % 16 == 0 && KB_BYTES % 16 == 0, "16-byte aligned tile buffers");
 static_assert(LDS_B <= 160 * 1024, "LDS budget");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -796,11 +800,11 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
 
 // ---------------------------------------------------------------------------------------------
 // Phase B: one workgroup per (16-column block of d_v, head, sequence), sequential over chunks.
-// Waves 0-3 form U = Ut - W S for row tile I = wave, waves 4-7 form O = P S + Y for row tile
-// I = wave - 4, and waves 0-7 then update state rows 16*wave .. 16*wave+15.  Waves 8-11 only
-// move data: while chunk c is computed they copy the tiles of chunk c+1 that waves 0-7 read
-// (W, Ut, K~^T, e^Gam_C) straight into LDS and touch chunk c+2 so that it is in L2; waves 4-7
-// load their own P and Y into registers a chunk ahead.
+// Waves 0-3 form U = Ut - W S for row tile I = wave and then update state row tiles wave and
+// wave + 4; waves 4-7 form O = P S + Y for row tile I = wave - 4 and, while the state is
+// updated, store it and load their P and Y of two chunks later into registers.  Waves 8-11 only
+// move data: they copy the tiles that waves 0-3 read (W, Ut, K~^T, e^Gam_C) straight into LDS
+// ahead of use and touch later chunks so that they are in L2.
 // ---------------------------------------------------------------------------------------------
 // Operands the output waves (4-7) keep in registers: P hi / lo of their row tile and their Y tile.
 struct OpTiles {
@@ -854,26 +858,34 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, const
   const int l16 = lane & 15, lg = lane >> 4;
   const int HD = H * D;
   const unsigned char* __restrict__ head_ws = ws + ((long long)b * H + h) * NC * (long long)CH_BYTES;
-  auto tbuf = [&](int c) { return smem + B_TB0 + (c & 1) * TB_BYTES; };
+  auto wubuf = [&](int c) { return smem + B_WU0 + (c % 3) * WU_BYTES; };
+  auto kbuf = [&](int c) { return smem + B_KB0 + (c & 1) * KB_BYTES; };
 
-  // ---- loader waves: tiles of chunk cn into its LDS buffer; cache lines of chunk cw touched ----
+  // ---- loader waves (lw = 0..3): each copies 5 of the 20 W | Ut fragments and 8 of the 32
+  //      K~^T fragments of a chunk (wave 3 also e^Gam_C); cache lines of later chunks touched ----
   const int lw = wave - 8;
-  // half 0 / 1 of this wave's copies for chunk cn (issued in the two halves of the chunk before,
-  // so that no burst holds a barrier)
-  auto issue_chunk = [&](int cn, int half) {
+  constexpr int N_WU = 5, N_K = 8;
+  auto issue_wu = [&](int cn) {
     const unsigned char* blk = head_ws + (long long)cn * CH_BYTES;
-    unsigned char* tb = tbuf(cn);
-    if (lw < 3) {
-      const int src = lw == 0 ? W_W : lw == 1 ? W_KTHI : W_KTLO;
-      const int dst = lw == 0 ? TB_W : lw == 1 ? TB_KHI : TB_KLO;
+    unsigned char* wb = wubuf(cn);
 #pragma unroll
-      for (int f = 8 * half; f < 8 * half + 8; ++f) dma16(blk + src + f * 1024 + lane * 16, tb + dst + f * 1024);
-    } else if (half == 0) {
+    for (int q = 0; q < N_WU; ++q) {
+      const int f = lw * N_WU + q;  // 0..15: W fragment f; 16..19: Ut row tile f - 16 of column tile vb
+      const unsigned char* src = f < 16 ? blk + W_W + f * 1024 : blk + W_UT + ((f - 16) * 8 + vb) * 1024;
+      dma16(src + lane * 16, wb + WU_W + f * 1024);
+    }
+  };
+  auto issue_k = [&](int cn) {
+    const unsigned char* blk = head_ws + (long long)cn * CH_BYTES;
+    unsigned char* kb = kbuf(cn);
 #pragma unroll
-      for (int I = 0; I < 4; ++I) dma16(blk + W_UT + (I * 8 + vb) * 1024 + lane * 16, tb + TB_UT + I * 1024);
-    } else {
+    for (int q = 0; q < N_K; ++q) {
+      const int f = lw * N_K + q;  // 0..15: K~^T hi fragment f; 16..31: lo fragment f - 16
+      dma16(blk + W_KTHI + f * 1024 + lane * 16, kb + KB_KHI + f * 1024);
+    }
+    if (lw == 3) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) dma4(blk + W_GC + q * 256 + lane * 4, tb + TB_GC + q * 256);
+      for (int q = 0; q < 2; ++q) dma4(blk + W_GC + q * 256 + lane * 4, kb + KB_GC + q * 256);
     }
   };
   // the 8 workgroups of a head touch one eighth each of a chunk's 128-byte lines (one 4-byte copy
@@ -892,20 +904,34 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, const
 
   if (wave >= 8) {
     // Loader waves: their own loop, with the same two barriers per chunk as the compute waves.
-    // While chunk ci is computed they copy chunk ci+1 into the other buffer (free: its previous
-    // chunk's last reads came before barrier (a)) and touch chunk ci+2; before the barrier that
-    // opens chunk ci+1 they wait for the copies (the touches may stay in flight).
-    issue_chunk(0, 0);
-    issue_chunk(0, 1);
-    if (NC > 1) touch_chunk(1);
+    // During chunk ci they copy W | Ut of chunk ci+2 (its buffer last served chunk ci-1, whose
+    // reads ended before barrier (b) of ci-1) and K~^T of chunk ci+1 (its buffer last served
+    // chunk ci-1, read before barrier (a) of ci), and touch chunk ci+3.  Before barrier (b) of
+    // chunk ci they wait for K~^T of ci (issued during chunk ci-1); W | Ut of ci+1, issued before
+    // it, is then complete too, ahead of the barrier (a) that publishes it.
+    issue_wu(0);
+    issue_k(0);
+    if (NC > 1) issue_wu(1);
+    if (NC > 2) touch_chunk(2);
     KDA_WAIT_VMCNT(0);
     for (int ci = 0; ci < NC; ++ci) {
       lds_barrier();  // (a)
-      if (ci + 1 < NC) issue_chunk(ci + 1, 0);
-      if (ci + 2 < NC) touch_chunk(ci + 2);
+      const bool full = ci + 3 < NC;
+      if (ci + 2 < NC) issue_wu(ci + 2);
+      if (ci + 1 < NC) issue_k(ci + 1);
+      if (full) touch_chunk(ci + 3);
+      // K~^T(0) was waited for before the loop.  Later, the ops this wave issued after the last
+      // copy of K~^T(ci) are the touch of chunk ci+2 (during chunk ci-1), then W | Ut(ci+2),
+      // K~^T(ci+1) and the touch of ci+3 (this chunk); near the end everything is waited for.
+      if (full && ci > 0) {
+        if (lw == 3)
+          KDA_WAIT_VMCNT(TOUCH_PER_WAVE + N_WU + N_K + 2 + TOUCH_PER_WAVE);
+        else
+          KDA_WAIT_VMCNT(TOUCH_PER_WAVE + N_WU + N_K + TOUCH_PER_WAVE);
+      } else if (ci > 0) {
+        KDA_WAIT_VMCNT(0);
+      }
       lds_barrier();  // (b)
-      if (ci + 1 < NC) issue_chunk(ci + 1, 1);
-      KDA_WAIT_VMCNT(0);
     }
     // The new conv state of this workgroup's 48 channels (16 each of q, k and v): the last W-1
     // raw inputs, from the conv state passed in where the call has fewer tokens.
@@ -929,88 +955,86 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, const
     return;
   }
 
-  // ---- compute waves: state block, wave w owns channel rows 16w..16w+15; lane holds rows
-  //      16w+4lg+r of column vb*16 + l16 ----
-  f32x4 Sacc;
-  {
-    const float* sp = a.state_in + ((long long)b * H + h) * D * D + vb * NVB + l16;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Sacc[r] = sp[(16 * wave + 4 * lg + r) * D];
-  }
+  // ---- state waves (0-3): wave w owns state row tiles w and w + 4 (channels 16t..16t+15); the
+  //      lane holds rows 16t+4lg+r of column vb*16 + l16 ----
+  f32x4 Sacc[2];
+  const float* s_in = a.state_in + ((long long)b * H + h) * D * D + vb * NVB + l16;
+  float* s_out = a.state_out + ((long long)b * H + h) * D * D + vb * NVB + l16;
   // S^T as the split B operand [column][channel]; the lane's four rows are contiguous
   auto write_state_operand = [&]() {
-    bf16x4 hi, lo;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      hi[r] = (__bf16)Sacc[r];
-      lo[r] = (__bf16)(Sacc[r] - (float)hi[r]);
-    }
-    *reinterpret_cast<bf16x4*>(sShi + l16 * PST + 16 * wave + 4 * lg) = hi;
-    *reinterpret_cast<bf16x4*>(sSlo + l16 * PST + 16 * wave + 4 * lg) = lo;
-  };
-
-  // Output rows of the previous chunk (waves 4-7), held in registers until the next chunk has
-  // started so that their stores are issued before that chunk's prefetch.
-  // Rows past the end of the sequence go to a scratch slot after o, so that every lane issues the
-  // same stores.
-  f32x4 opend = zero4();
-  float* scratch = ows + (long long)a.B * T * HD + lane * 4;
-  auto store_pending = [&](int pc) {
-    if (pc < 0) return;
-    const int pc0 = pc * C, pL = min(C, T - pc0);
-    float* op = ows + (((long long)b * T + pc0) * H + h) * D + vb * NVB + l16;
+    for (int u = 0; u < 2; ++u) {
+      const int t = wave + 4 * u;
+      bf16x4 hi, lo;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * (wave - 4) + 4 * lg + r;
-      *(t < pL ? op + (long long)t * HD : scratch + r) = opend[r];
+      for (int r = 0; r < 4; ++r) {
+        hi[r] = (__bf16)Sacc[u][r];
+        lo[r] = (__bf16)(Sacc[u][r] - (float)hi[r]);
+      }
+      *reinterpret_cast<bf16x4*>(sShi + l16 * PST + 16 * t + 4 * lg) = hi;
+      *reinterpret_cast<bf16x4*>(sSlo + l16 * PST + 16 * t + 4 * lg) = lo;
     }
   };
 
   // S <- e^Gam_C S + K~^T U from chunk ci's buffer, then the state operand for the next chunk
   // (every read of the old one came before barrier (b)).
-  auto state_update = [&](const unsigned char* tb) {
-    const float4 gc = *reinterpret_cast<const float4*>(tb + TB_GC + (16 * wave + 4 * lg) * 4);
-    f32x4 sa, sb = zero4();
-    sa[0] = gc.x * Sacc[0];
-    sa[1] = gc.y * Sacc[1];
-    sa[2] = gc.z * Sacc[2];
-    sa[3] = gc.w * Sacc[3];
+  auto state_update = [&](const unsigned char* kb) {
+    f32x4 sa[2], sb[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(tb + TB_KHI + ((wave * 2 + s) * 64 + lane) * 16);
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(tb + TB_KLO + ((wave * 2 + s) * 64 + lane) * 16);
-      const bf16x8 uh = *reinterpret_cast<const bf16x8*>(sUhi + l16 * PVT + 32 * s + 8 * lg);
-      const bf16x8 ul = *reinterpret_cast<const bf16x8*>(sUlo + l16 * PVT + 32 * s + 8 * lg);
-      sa = mfma(k0, uh, sa);
-      sb = mfma(k0, ul, sb);
-      sb = mfma(k1, uh, sb);
+    for (int u = 0; u < 2; ++u) {
+      const int t = wave + 4 * u;
+      const float4 gc = *reinterpret_cast<const float4*>(kb + KB_GC + (16 * t + 4 * lg) * 4);
+      sa[u][0] = gc.x * Sacc[u][0];
+      sa[u][1] = gc.y * Sacc[u][1];
+      sa[u][2] = gc.z * Sacc[u][2];
+      sa[u][3] = gc.w * Sacc[u][3];
+      sb[u] = zero4();
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Sacc[r] = sa[r] + sb[r];
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 uh = *reinterpret_cast<const bf16x8*>(sUhi + l16 * PVT + 32 * s + 8 * lg);
+      const bf16x8 ul = *reinterpret_cast<const bf16x8*>(sUlo + l16 * PVT + 32 * s + 8 * lg);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t = wave + 4 * u;
+        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kb + KB_KHI + ((t * 2 + s) * 64 + lane) * 16);
+        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kb + KB_KLO + ((t * 2 + s) * 64 + lane) * 16);
+        sa[u] = mfma(k0, uh, sa[u]);
+        sb[u] = mfma(k0, ul, sb[u]);
+        sb[u] = mfma(k1, uh, sb[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Sacc[u][r] = sa[u][r] + sb[u][r];
     write_state_operand();
   };
 
   // Each role runs its own loop (so that no wave's waits are derived from another role's loads),
-  // with the same two barriers per chunk: (a) the state operand and chunk ci's tile buffer
-  // (complete: the loaders waited before it) are in LDS; (b) U is in LDS and every read of the
-  // state operand is done.
-  write_state_operand();
+  // with the same two barriers per chunk: (a) the state operand and chunk ci's W | Ut are in
+  // LDS; (b) U and chunk ci's K~^T are in LDS and every read of the state operand is done.
   if (wave < 4) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Sacc[u][r] = s_in[(16 * (wave + 4 * u) + 4 * lg + r) * D];
+    write_state_operand();
     // U = Ut - W S for row tile I = wave, as the split B operand [column][token]
     const int I = wave;
     for (int ci = 0; ci < NC; ++ci) {
-      const unsigned char* tb = tbuf(ci);
+      const unsigned char* wb = wubuf(ci);
       lds_barrier();  // (a)
       f32x4 pa = zero4(), pb = zero4();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 w = *reinterpret_cast<const bf16x8*>(tb + TB_W + ((I * 4 + s) * 64 + lane) * 16);
+        const bf16x8 w = *reinterpret_cast<const bf16x8*>(wb + WU_W + ((I * 4 + s) * 64 + lane) * 16);
         const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
         const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSlo + l16 * PST + 32 * s + 8 * lg);
         pa = mfma(w, sh, pa);
         pb = mfma(w, sl, pb);
       }
-      const f32x4 ut = *reinterpret_cast<const f32x4*>(tb + TB_UT + (I * 64 + lane) * 16);
+      const f32x4 ut = *reinterpret_cast<const f32x4*>(wb + WU_UT + (I * 64 + lane) * 16);
       bf16x4 hi, lo;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -1021,18 +1045,21 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, const
       *reinterpret_cast<bf16x4*>(sUhi + l16 * PVT + 16 * I + 4 * lg) = hi;
       *reinterpret_cast<bf16x4*>(sUlo + l16 * PVT + 16 * I + 4 * lg) = lo;
       lds_barrier();  // (b)
-      state_update(tb);
+      state_update(kbuf(ci));
     }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_out[(16 * (wave + 4 * u) + 4 * lg + r) * D] = Sacc[u][r];
   } else {
-    // O = P S + Y for row tile I = wave - 4, P and Y in registers a chunk ahead (two register
-    // sets alternate, so no loaded value is copied); the output rows of chunk ci are stored at
-    // the start of chunk ci + 1, before its prefetch.
+    // O = P S + Y for row tile I = wave - 4 from P and Y in registers; after barrier (b) the rows
+    // are stored and the register set is refilled with the tiles of chunk ci + 2 (two sets
+    // alternate, so no loaded value is copied, and a load has two chunks to arrive).  Rows past
+    // the end of the sequence go to a scratch slot after o, so that every lane issues the same
+    // stores; the last chunk's tiles are loaded again in place of chunks past the end.
     const int I = wave - 4;
-    auto chunk_o = [&](int ci, const OpTiles& cur, OpTiles& nxt) __attribute__((always_inline)) {
-      const unsigned char* tb = tbuf(ci);
-      store_pending(ci - 1);
-      // the last chunk prefetches itself again: the loads stay unconditional
-      load_out_tiles(head_ws + (long long)min(ci + 1, NC - 1) * CH_BYTES, I, lane, vb, nxt);
+    float* scratch = ows + (long long)a.B * T * HD + lane * 4;
+    auto chunk_o = [&](int ci, OpTiles& cur) __attribute__((always_inline)) {
       lds_barrier();  // (a)
       f32x4 oa = zero4(), ob = zero4();
 #pragma unroll
@@ -1043,26 +1070,28 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, const
         ob = mfma(cur.x0[s], sl, ob);
         ob = mfma(cur.x1[s], sh, ob);
       }
+      f32x4 o;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) opend[r] = (oa[r] + ob[r]) + cur.y[r];
+      for (int r = 0; r < 4; ++r) o[r] = (oa[r] + ob[r]) + cur.y[r];
       lds_barrier();  // (b)
-      state_update(tb);
+      const int c0 = ci * C, L = min(C, T - c0);
+      float* op = ows + (((long long)b * T + c0) * H + h) * D + vb * NVB + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * I + 4 * lg + r;
+        *(t < L ? op + (long long)t * HD : scratch + r) = o[r];
+      }
+      load_out_tiles(head_ws + (long long)min(ci + 2, NC - 1) * CH_BYTES, I, lane, vb, cur);
     };
     OpTiles ta, tb2;
     load_out_tiles(head_ws, I, lane, vb, ta);
+    load_out_tiles(head_ws + (long long)min(1, NC - 1) * CH_BYTES, I, lane, vb, tb2);
     int ci = 0;
     for (; ci + 1 < NC; ci += 2) {
-      chunk_o(ci, ta, tb2);
-      chunk_o(ci + 1, tb2, ta);
+      chunk_o(ci, ta);
+      chunk_o(ci + 1, tb2);
     }
-    if (ci < NC) chunk_o(ci, ta, tb2);
-    store_pending(NC - 1);
-  }
-
-  {
-    float* sp = a.state_out + ((long long)b * H + h) * D * D + vb * NVB + l16;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sp[(16 * wave + 4 * lg + r) * D] = Sacc[r];
+    if (ci < NC) chunk_o(ci, ta);
   }
 }
 
