@@ -4,7 +4,8 @@ One step = one pass over every call of the path on its layer-shaped workload:
   prefill   B=1, T=4096, H=32, d_k=d_v=128, chunk 64, bf16 io, fp32 state
   decode    64 sequences x 32 heads x 128x128 fp32 state, one token each
   verify    16 sequences x 8 draft tokens with per-token snapshots, then rollback
-            to a seeded accepted prefix (0..8) per sequence
+            to a seeded accepted prefix (0..8) per sequence; and the same block
+            verified with a replay tape, then committed from the tape
 Inputs are seeded synthetic tensors (hybrid_linear_attention_kda_amd.inputs);
 the decode / verify states are pre-filled on the GPU by running 256 / 2048
 random tokens through kda_prefill first.  Every call rotates over --sets
@@ -60,7 +61,17 @@ def verify_bytes(B, T_d, H, D, W, io_b=2, out_b=2):
 
 def rollback_bytes(accepted, H, D, W, io_b=2):
     n = sum(1 for m in accepted if m > 0)
-    return n * (2 * H * D * D * 4 + 2 * 3 * H * D * (W - 1) * io_b) + sum(int(m) for m in accepted) * 0
+    return n * (2 * H * D * D * 4 + 2 * 3 * H * D * (W - 1) * io_b)
+
+
+def verify_tape_bytes(B, T_d, H, D, W, io_b=2, out_b=2):
+    """verify with a replay tape: the snapshots are replaced by 3*D floats per token and head"""
+    return verify_bytes(B, T_d, H, D, W, io_b, out_b) - B * T_d * H * D * D * 4 + B * T_d * H * 3 * D * 4
+
+
+def commit_bytes(accepted, H, D, W, io_b=2):
+    """tape commit: the state of every sequence with m > 0 read and written, its m tape rows read"""
+    return rollback_bytes(accepted, H, D, W, io_b) + sum(int(m) for m in accepted) * H * 3 * D * 4
 
 
 def kernel_alg_bytes(kernel, wp, wd, wv, accepted):
@@ -80,6 +91,8 @@ def kernel_alg_bytes(kernel, wp, wd, wv, accepted):
         "kda_recurrent_kernel[decode]": decode_bytes(wd.B, wd.H, wd.dk, wd.W),
         "kda_recurrent_kernel[verify]": verify_bytes(wv.B, wv.T, wv.H, wv.dk, wv.W),
         "kda_rollback_kernel": rollback_bytes(accepted or [], wv.H, wv.dk, wv.W),
+        "kda_recurrent_kernel[verify_tape]": verify_tape_bytes(wv.B, wv.T, wv.H, wv.dk, wv.W),
+        "kda_commit_tape_kernel": commit_bytes(accepted or [], wv.H, wv.dk, wv.W),
     }
     return table.get(kernel)
 
@@ -122,7 +135,8 @@ def short_kernel_name(full):
         return None
     name = m.group(1)
     if name == "kda_recurrent_kernel" and m.group(2):
-        name += "[verify]" if ", true," in m.group(2) else "[decode]"
+        targs = m.group(2)
+        name += "[verify_tape]" if ", true, true," in targs else "[verify]" if ", true," in targs else "[decode]"
     return name
 
 
@@ -283,6 +297,7 @@ def main():
             sets["verify"].append(dict(
                 layer=lay, tok={k: v.clone() for k, v in tok.items()}, state=st.clone(), conv=cs.clone(),
                 snaps=torch.empty((wv.B, wv.T, wv.H, wv.dk, wv.dv), dtype=torch.float32, device=dev),
+                tape=torch.empty((wv.B, wv.T, wv.H, 3, wv.dk), dtype=torch.float32, device=dev),
                 out=torch.empty((wv.B, wv.T, wv.H * wv.dv), dtype=torch.bfloat16, device=dev)))
         del st, cs
     torch.cuda.synchronize()
@@ -300,15 +315,20 @@ def main():
                                  s["snaps"], s["out"], stream=stream)
         elif op == "rollback":
             abi.kda_rollback(s["layer"], accepted, s["snaps"], t["qkv"], s["state"], s["conv"], stream=stream)
+        elif op == "verify_tape":
+            abi.kda_verify_block_tape(s["layer"], t["qkv"], t["f"], t["beta"], t["g_out"], s["state"], s["conv"],
+                                      s["tape"], s["out"], stream=stream)
+        elif op == "commit":
+            abi.kda_commit_tape(s["layer"], accepted, s["tape"], t["qkv"], s["state"], s["conv"], stream=stream)
 
     seq = []
     for op in ops:
         seq.append(op)
         if op == "verify":
-            seq.append("rollback")
+            seq += ["rollback", "verify_tape", "commit"]
 
     def setof(op):
-        return "verify" if op == "rollback" else op
+        return "verify" if op in ("rollback", "verify_tape", "commit") else op
 
     for i in range(args.warmup):
         for op in seq:
@@ -379,6 +399,14 @@ def main():
                             "hbm_frac": gv / HBM_PEAK_GBPS}
         detail["rollback"] = {"ms_mean": mean["rollback"], "alg_bytes": rb,
                               "gbps": rb / (mean["rollback"] * 1e-3) / 1e9, "accepted": accepted}
+        vtb = verify_tape_bytes(wv.B, wv.T, wv.H, wv.dk, wv.W)
+        cb = commit_bytes(accepted, wv.H, wv.dk, wv.W)
+        detail["verify_tape"] = {"ms_mean": mean["verify_tape"], "alg_bytes": vtb,
+                                 "gbps": vtb / (mean["verify_tape"] * 1e-3) / 1e9}
+        detail["commit_tape"] = {"ms_mean": mean["commit"], "alg_bytes": cb,
+                                 "gbps": cb / (mean["commit"] * 1e-3) / 1e9}
+        detail["speculative_block_ms"] = {"snapshots_verify_plus_rollback": mean["verify"] + mean["rollback"],
+                                          "tape_verify_plus_commit": mean["verify_tape"] + mean["commit"]}
         if "value" not in res:
             res["value"], res["unit"] = gv, "GB/s"
     # per kernel: average launch duration from the library's event pairs over the timed steps

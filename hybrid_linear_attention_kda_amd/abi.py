@@ -65,6 +65,9 @@ def load() -> ctypes.CDLL:
         "kda_decode_step": (c_int32, [D, c_int32, P, P, P, P, P, P, P, P]),
         "kda_verify_block": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P, P, P, P]),
         "kda_rollback": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P]),
+        "kda_verify_tape_size": (c_size_t, [D, c_int32, c_int32]),
+        "kda_verify_block_tape": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P, P, P, P]),
+        "kda_commit_tape": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P]),
         "kda_timing_enable": (c_int32, [c_int32]),
         "kda_timing_read": (c_int32, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(c_float), c_int32]),
     }
@@ -224,6 +227,36 @@ def kda_rollback(layer: KdaLayer, accepted, snaps, qkv_block, state, conv_state,
     _check_state(layer, B, state, conv_state)
     _check(load().kda_rollback(ctypes.byref(layer.desc), B, T_d, ctypes.cast(acc, c_void_p), _ptr(snaps),
                                _ptr(qkv_block), _ptr(state), _ptr(conv_state), _stream(stream)))
+
+
+def kda_verify_tape_size(layer: KdaLayer, B: int, T_d: int) -> int:
+    n = load().kda_verify_tape_size(ctypes.byref(layer.desc), B, T_d)
+    if n == ctypes.c_size_t(-1).value:
+        raise KdaError(KDA_ERR_INVALID_ARGUMENT, load().kda_last_error().decode())
+    return n
+
+
+def kda_verify_block_tape(layer: KdaLayer, qkv, f, beta, g_out, state, conv_state, tape, out, stream=None):
+    B, T_d = qkv.shape[0], qkv.shape[1]
+    _check_tokens(layer, B, T_d, qkv, f, beta, g_out)
+    _check_state(layer, B, state, conv_state)
+    _expect(tape, (B, T_d, layer.H, 3, layer.D), torch.float32, "tape")
+    _expect(out, (B, T_d, layer.H * layer.D), layer.out_torch, "out")
+    _check(load().kda_verify_block_tape(ctypes.byref(layer.desc), B, T_d, _ptr(qkv), _ptr(f), _ptr(beta),
+                                        _ptr(g_out), _ptr(state), _ptr(conv_state), _ptr(tape), _ptr(out),
+                                        _stream(stream)))
+
+
+def kda_commit_tape(layer: KdaLayer, accepted, tape, qkv_block, state, conv_state, stream=None):
+    B, T_d = qkv_block.shape[0], qkv_block.shape[1]
+    if len(accepted) != B:
+        raise ValueError(f"accepted has {len(accepted)} entries, expected {B}")
+    acc = (ctypes.c_int32 * B)(*[int(m) for m in accepted])
+    _expect(qkv_block, (B, T_d, layer.c_qkv), layer.io_torch, "qkv_block")
+    _expect(tape, (B, T_d, layer.H, 3, layer.D), torch.float32, "tape")
+    _check_state(layer, B, state, conv_state)
+    _check(load().kda_commit_tape(ctypes.byref(layer.desc), B, T_d, ctypes.cast(acc, c_void_p), _ptr(tape),
+                                  _ptr(qkv_block), _ptr(state), _ptr(conv_state), _stream(stream)))
 
 
 def timing_enable(on: bool) -> bool:

@@ -277,6 +277,78 @@ kda_status kda_rollback(const kda_layer_desc* desc, int32_t B, int32_t T_d, cons
   return ok();
 }
 
+size_t kda_verify_tape_size(const kda_layer_desc* desc, int32_t B, int32_t T_d) {
+  if (check_desc(desc) != KDA_OK || check_batch(B, T_d) != KDA_OK) return (size_t)-1;
+  return (size_t)B * (size_t)T_d * (size_t)desc->num_heads * 3u * (size_t)desc->head_dim_k * sizeof(float);
+}
+
+kda_status kda_verify_block_tape(const kda_layer_desc* desc, int32_t B, int32_t T_d, const void* qkv,
+                                 const void* f, const void* beta, const void* g_out, const float* state,
+                                 const void* conv_state, float* tape, void* out, void* stream) {
+  KDA_TRY(check_desc(desc));
+  KDA_TRY(check_batch(B, T_d));
+  if (T_d > 255) return fail(KDA_ERR_UNSUPPORTED, "draft block T_d = %d > 255", T_d);
+  if (B == 0 || T_d == 0) return ok();
+  KDA_TRY(check_token_tensors(qkv, f, beta, g_out));
+  KDA_TRY(check_ptr(state, "state"));
+  if (desc->conv_width > 1) KDA_TRY(check_ptr(conv_state, "conv_state"));
+  KDA_TRY(check_ptr(tape, "tape"));
+  KDA_TRY(check_ptr(out, "out"));
+  kda::LayerArgs a = make_args(desc, B, T_d);
+  a.qkv = qkv;
+  a.f = f;
+  a.beta = beta;
+  a.g_out = g_out;
+  a.state_in = state;
+  a.state_out = nullptr;
+  a.conv_in = conv_state;
+  a.conv_out = nullptr;
+  a.out = out;
+  a.snapshots = 0;
+  a.tape = tape;
+  return launched(kda::launch_recurrent(a, desc->io_dtype, desc->out_dtype, static_cast<hipStream_t>(stream)),
+                  "kda_verify_block_tape");
+}
+
+kda_status kda_commit_tape(const kda_layer_desc* desc, int32_t B, int32_t T_d, const int32_t* accepted_host,
+                           const float* tape, const void* qkv_block, float* state, void* conv_state,
+                           void* stream) {
+  KDA_TRY(check_desc(desc));
+  KDA_TRY(check_batch(B, T_d));
+  if (T_d > 255) return fail(KDA_ERR_UNSUPPORTED, "draft block T_d = %d > 255", T_d);
+  if (B == 0) return ok();
+  if (accepted_host == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "accepted_host is null");
+  bool any = false;
+  for (int32_t b = 0; b < B; ++b) {
+    if (accepted_host[b] < 0 || accepted_host[b] > T_d)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "accepted[%d] = %d outside 0..%d", b, accepted_host[b], T_d);
+    any = any || accepted_host[b] > 0;
+  }
+  if (!any) return ok();
+  KDA_TRY(check_ptr(tape, "tape"));
+  KDA_TRY(check_ptr(qkv_block, "qkv_block"));
+  KDA_TRY(check_ptr(state, "state"));
+  if (desc->conv_width > 1) KDA_TRY(check_ptr(conv_state, "conv_state"));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t b0 = 0; b0 < B; b0 += kda::kRollbackBatch) {
+    kda::CommitArgs c{};
+    c.B0 = b0;
+    c.nB = (B - b0) < kda::kRollbackBatch ? (B - b0) : kda::kRollbackBatch;
+    c.T_d = T_d;
+    c.H = desc->num_heads;
+    c.D = desc->head_dim_k;
+    c.W = desc->conv_width;
+    c.tape = tape;
+    c.qkv = qkv_block;
+    c.state = state;
+    c.conv_state = conv_state;
+    for (int i = 0; i < c.nB; ++i) c.accepted[i] = (uint8_t)accepted_host[b0 + i];
+    kda_status st = launched(kda::launch_commit_tape(c, desc->io_dtype, s), "kda_commit_tape");
+    if (st != KDA_OK) return st;
+  }
+  return ok();
+}
+
 }  // extern "C"
 
 // ---- per-kernel timing ------------------------------------------------------------------------

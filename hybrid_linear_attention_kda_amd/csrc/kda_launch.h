@@ -31,11 +31,22 @@ struct LayerArgs {
   void* conv_out;       // may alias conv_in; nullptr: conv state not written (verify)
   void* out;            // [B, T, H*D] out type
   int snapshots;        // 1: write the state after every token to state_out (verify)
+  float* tape;          // verify with a replay tape: [B, T, H, 3, D] = (alpha, k, u) per token and
+                        // head, written instead of any state (state_out unused); nullptr otherwise
 };
 
 struct RollbackArgs {
   int B0, nB, T_d, H, D, W;
   const float* snaps;   // [B, T_d, H, D, D]
+  const void* qkv;      // [B, T_d, 3*H*D] io
+  float* state;         // [B, H, D, D]
+  void* conv_state;     // [B, 3*H*D, W-1] io
+  uint8_t accepted[kRollbackBatch];
+};
+
+struct CommitArgs {
+  int B0, nB, T_d, H, D, W;
+  const float* tape;    // [B, T_d, H, 3, D]: alpha, k, u of every draft token
   const void* qkv;      // [B, T_d, 3*H*D] io
   float* state;         // [B, H, D, D]
   void* conv_state;     // [B, 3*H*D, W-1] io
@@ -49,6 +60,7 @@ void timing_end(hipStream_t s);
 
 hipError_t launch_recurrent(const LayerArgs& a, int io, int ot, hipStream_t s);
 hipError_t launch_rollback(const RollbackArgs& a, int io, hipStream_t s);
+hipError_t launch_commit_tape(const CommitArgs& a, int io, hipStream_t s);
 
 // Chunked prefill, fp32 VALU form (any supported head size; internal chunk <= 4096 / D).
 hipError_t launch_prefill_generic(const LayerArgs& a, int chunk, int io, int ot, hipStream_t s);

@@ -397,15 +397,17 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
     {
       const int tb = 32 * (tid >> 8), cq = tid & 255;
       const __bf16* col = sRaw + cq;
-      float r0 = (float)col[(tb + 0) * PR], r1 = (float)col[(tb + 1) * PR], r2 = (float)col[(tb + 2) * PR];
       float* dst = cq < D ? sQ + cq : sG + (cq - D);
-#pragma unroll 4
+      // the lane's 35 raw rows are read before any arithmetic, so that the reads overlap instead of
+      // each output waiting on the latency of its own read
+      float x[32 + 3];
+#pragma unroll
+      for (int i = 0; i < 35; ++i) x[i] = (float)col[(tb + i) * PR];
+#pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int t = tb + i;
-        const float r3 = (float)col[(t + 3) * PR];
-        const float y = tq[0] * r0 + tq[1] * r1 + tq[2] * r2 + tq[3] * r3;
+        const float y = tq[0] * x[i] + tq[1] * x[i + 1] + tq[2] * x[i + 2] + tq[3] * x[i + 3];
         dst[t * PQ] = t < L ? silu_fast(y) : 0.f;
-        r0 = r1; r1 = r2; r2 = r3;
       }
     }
     __syncthreads();

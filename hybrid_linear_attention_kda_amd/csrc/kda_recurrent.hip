@@ -1,9 +1,11 @@
-// Token-recurrent KDA kernels: decode step, speculative verify block, rollback.
+// Token-recurrent KDA kernels: decode step, speculative verify block, rollback,
+// and the replay-tape commit.
 //
 // One workgroup owns one (sequence, head).  Its d_k x d_v fp32 state is read
 // from HBM once into registers (float4 per lane, coalesced along d_v), kept
 // there across the tokens of the call, and written once per token (verify:
-// one snapshot per token) or once at the end (decode).  There is no
+// one snapshot per token), once at the end (decode), or not at all (verify
+// with a replay tape: per token only alpha, k and u, 3 x d floats).  There is no
 // contraction worth a matrix core here: every state element takes part in
 // three multiply-adds per token, so these kernels are HBM-bound and the
 // design goal is one streaming read plus one streaming write of the state.
@@ -34,8 +36,9 @@ struct RecLayout {
 };
 
 // MULTI: the call carries several tokens (verify); otherwise exactly one (decode).
+// TAPE: verify that records the replay tape and writes no state.
 // WMAX: compile-time bound on the conv width, so taps and window stay in registers.
-template <int D, int WMAX, bool MULTI, typename IO, typename OT>
+template <int D, int WMAX, bool MULTI, bool TAPE, typename IO, typename OT>
 __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerArgs a) {
   using L = RecLayout<D>;
   constexpr int NT = L::NT;
@@ -64,8 +67,14 @@ __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerAr
   //    ahead of the state lets the prologue below run while the state is still in flight.
   //    Conv taps are held right-aligned (tapr[0] multiplies the current token) and the window
   //    newest-first (win[j] = input j tokens back), so no register is indexed at run time.
+  //    A snapshot verify loads the inputs of PF tokens ahead (a whole draft block of 8 at
+  //    once), so no token waits on the latency of its own loads.  The tape verify, which has
+  //    no state stores to hide them behind, keeps the registers for occupancy instead (two
+  //    workgroups per CU) and loads one token ahead.
+  constexpr int PF = (MULTI && !TAPE) ? 8 : 1;
   int choff[NCH];
-  float tapr[NCH][WMAX], win[NCH][WMAX], xin[NCH];
+  float tapr[NCH][WMAX], win[NCH][WMAX];
+  float xs[PF][NCH], fs[PF], gs[PF], bs[PF];
 #pragma unroll
   for (int n = 0; n < NCH; ++n) {
     const int c = tid + n * NT;
@@ -79,12 +88,19 @@ __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerAr
       tapr[n][j] = (j < W) ? to_f32(cwp[W - 1 - j]) : 0.f;
       win[n][j] = (j >= 1 && j < W) ? to_f32(csp[W - 1 - j]) : 0.f;
     }
-    xin[n] = to_f32(xq[choff[n]]);
   }
   const int ci = tid < D ? tid : 0;
-  float fin = to_f32(xf[ci]);
-  float gin = to_f32(xg[ci]);
-  float bin = to_f32(xb[0]);
+  // token tl's inputs into slot j (j is a compile-time index wherever this is called)
+  auto load_token = [&](int j, int tl) {
+#pragma unroll
+    for (int n = 0; n < NCH; ++n) xs[j][n] = to_f32(xq[(long long)tl * Cqkv + choff[n]]);
+    fs[j] = to_f32(xf[(long long)tl * HD + ci]);
+    gs[j] = to_f32(xg[(long long)tl * HD + ci]);
+    bs[j] = to_f32(xb[(long long)tl * H]);
+  };
+  // tokens past the end re-read the last one: the loads stay unconditional
+#pragma unroll
+  for (int j = 0; j < PF; ++j) load_token(j, min(j, T - 1));
   const float dtb = a.dt_bias[h * D + ci];
   const float nwj = to_f32(static_cast<const IO*>(a.norm_w)[ci]);
   const float Ah = __expf(a.A_log[h]);
@@ -103,17 +119,21 @@ __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerAr
     }
   }
 
-  for (int t = 0; t < T; ++t) {
+  for (int t0 = 0; t0 < T; t0 += PF) {
+#pragma unroll
+  for (int pj = 0; pj < PF; ++pj) {
+    const int t = t0 + pj;
+    if (t >= T) break;
     // conv + SiLU over this lane's channels; advance the window
 #pragma unroll
     for (int n = 0; n < NCH; ++n) {
       const int c = tid + n * NT;
-      float y = tapr[n][0] * xin[n];
+      float y = tapr[n][0] * xs[pj][n];
 #pragma unroll
       for (int j = 1; j < WMAX; ++j) y += tapr[n][j] * win[n][j];
 #pragma unroll
       for (int j = WMAX - 1; j >= 2; --j) win[n][j] = win[n][j - 1];
-      win[n][1 % WMAX] = (WMAX > 1) ? xin[n] : win[n][0];
+      win[n][1 % WMAX] = (WMAX > 1) ? xs[pj][n] : win[n][0];
       if (c < C3) {
         const float z = y / (1.0f + expf(-y));
         const int part = c / D, i = c % D;
@@ -121,16 +141,9 @@ __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerAr
       }
     }
     // bounded-sigmoid decay gate (log-decay in (lb, 0)), per key channel
-    if (tid < D) s_alpha[tid] = expf(a.lb / (1.0f + expf(-Ah * (fin + dtb))));
-    const float bt = bin, gcur = gin;
-    if (MULTI && t + 1 < T) {  // next token's inputs: issued before this token's stores
-      const int tn = t + 1;
-#pragma unroll
-      for (int n = 0; n < NCH; ++n) xin[n] = to_f32(xq[(long long)tn * Cqkv + choff[n]]);
-      fin = to_f32(xf[(long long)tn * HD + ci]);
-      gin = to_f32(xg[(long long)tn * HD + ci]);
-      bin = to_f32(xb[(long long)tn * H]);
-    }
+    if (tid < D) s_alpha[tid] = expf(a.lb / (1.0f + expf(-Ah * (fs[pj] + dtb))));
+    const float bt = bs[pj], gcur = gs[pj];
+    if (MULTI && t + PF < T) load_token(pj, t + PF);  // refill the slot: issued before this token's stores
     __syncthreads();
     // q/k norms and q.k, computed redundantly by every wave (no extra barrier)
     float qq = 0.f, kk = 0.f, qk = 0.f;
@@ -172,19 +185,32 @@ __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerAr
     }
     __syncthreads();
 
-    // 4. Rank-1 update in registers; verify streams a snapshot per token, decode the final state.
+    // 4. Rank-1 update in registers (one fused multiply-add per element, as the tape replay does);
+    //    verify streams a snapshot per token, or the token's replay tape, decode the final state.
     {
       const float4 u4 = *reinterpret_cast<const float4*>(&s_u[4 * cg]);
 #pragma unroll
       for (int r = 0; r < L::RPT; ++r) {
         const float ki = s_k[rg * L::RPT + r] * rk;
-        S[r].x += ki * u4.x; S[r].y += ki * u4.y; S[r].z += ki * u4.z; S[r].w += ki * u4.w;
+        S[r].x = __builtin_fmaf(ki, u4.x, S[r].x);
+        S[r].y = __builtin_fmaf(ki, u4.y, S[r].y);
+        S[r].z = __builtin_fmaf(ki, u4.z, S[r].z);
+        S[r].w = __builtin_fmaf(ki, u4.w, S[r].w);
       }
-      float* dst = a.snapshots ? a.state_out + (((long long)b * T + t) * H + h) * D * D
-                               : a.state_out + bh * D * D;
-      if (a.snapshots || t + 1 == T) {
+      if (TAPE) {
+        if (tid < D) {
+          float* tp = a.tape + (((long long)b * T + t) * H + h) * 3 * D;
+          tp[tid] = s_alpha[tid];
+          tp[D + tid] = s_k[tid] * rk;
+          tp[2 * D + tid] = s_u[tid];
+        }
+      } else {
+        float* dst = a.snapshots ? a.state_out + (((long long)b * T + t) * H + h) * D * D
+                                 : a.state_out + bh * D * D;
+        if (a.snapshots || t + 1 == T) {
 #pragma unroll
-        for (int r = 0; r < L::RPT; ++r) store_nt(dst + soff + r * D, S[r]);
+          for (int r = 0; r < L::RPT; ++r) store_nt(dst + soff + r * D, S[r]);
+        }
       }
     }
 
@@ -197,6 +223,7 @@ __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerAr
       store_as(&out[(long long)t * HD + tid], s_o[tid] * rr * nwj / (1.0f + expf(-gcur)));
     }
     if (MULTI && t + 1 < T) __syncthreads();  // s_q/s_k/s_o are rewritten by the next token
+  }
   }
 
   if (a.conv_out != nullptr) {
@@ -245,30 +272,126 @@ __global__ __launch_bounds__(256) void kda_rollback_kernel(RollbackArgs a) {
   }
 }
 
-template <int D, int WMAX, bool MULTI>
+// Commit the accepted prefix of a draft block verified with a replay tape: for t < m,
+//   S <- Diag(alpha_t) S + k_t u_t^T
+// with the (alpha, k, u) the verify call recorded.  The verify call computed u_t from exactly the
+// state this replay reaches before token t, and performs the same multiply and fused multiply-add
+// per element, so the committed state is bit-identical to its state after token m.  The conv
+// state takes the last W-1 raw inputs, as in the rollback.  grid = (head x row block, sequence):
+// a d = 128 state is split into four blocks of 32 rows, so that enough workgroups stream at once.
+constexpr int kCommitNT = 256;
+constexpr int kCommitTok = 8;  // tape tokens staged in LDS at a time
+template <int D>
+struct CommitLayout {
+  static constexpr int NS = D == 128 ? 4 : 1;  // row blocks per head
+  static constexpr int RW = D / NS;            // rows per workgroup
+};
+template <int D, typename IO>
+__global__ __launch_bounds__(kCommitNT) void kda_commit_tape_kernel(CommitArgs a) {
+  constexpr int NT = kCommitNT;
+  constexpr int NS = CommitLayout<D>::NS;
+  constexpr int CG = D / 4;                          // float4 per state row
+  constexpr int NV = CommitLayout<D>::RW * D / 4;    // float4 in this workgroup's rows
+  constexpr int PER = (NV + NT - 1) / NT;            // float4 per lane
+  __shared__ float s_tp[kCommitTok * 3 * D];
+  const int h = blockIdx.x / NS;
+  const int part = blockIdx.x % NS;
+  const int lbi = blockIdx.y;
+  const int m = a.accepted[lbi];
+  if (m == 0) return;
+  const int b = a.B0 + lbi;
+  const int tid = threadIdx.x;
+  const int H = a.H;
+  const int r0 = part * CommitLayout<D>::RW;
+  float* S = a.state + ((long long)b * H + h) * D * D + (long long)r0 * D;
+  float4 v[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = tid + k * NT;
+    if (NV % NT == 0 || i < NV) {
+      const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S) + i);
+      v[k] = make_float4(x.x, x.y, x.z, x.w);
+    }
+  }
+  const float* tp = a.tape + ((long long)b * a.T_d * H + h) * 3 * D;  // token t at tp + t * H * 3 * D
+  for (int t0 = 0; t0 < m; t0 += kCommitTok) {
+    const int nt = min(kCommitTok, m - t0);
+    __syncthreads();  // the previous tokens' reads are done
+    for (int i = tid; i < nt * 3 * D; i += NT) s_tp[i] = tp[(long long)(t0 + i / (3 * D)) * H * 3 * D + i % (3 * D)];
+    __syncthreads();
+    for (int t = 0; t < nt; ++t) {
+      const float* al = s_tp + t * 3 * D;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int i = tid + k * NT;
+        if (NV % NT == 0 || i < NV) {
+          const int row = r0 + i / CG, c4 = i % CG;
+          const float alr = al[row], kr = al[D + row];
+          const float4 u4 = *reinterpret_cast<const float4*>(al + 2 * D + 4 * c4);
+          v[k].x *= alr; v[k].y *= alr; v[k].z *= alr; v[k].w *= alr;
+          v[k].x = __builtin_fmaf(kr, u4.x, v[k].x);
+          v[k].y = __builtin_fmaf(kr, u4.y, v[k].y);
+          v[k].z = __builtin_fmaf(kr, u4.z, v[k].z);
+          v[k].w = __builtin_fmaf(kr, u4.w, v[k].w);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = tid + k * NT;
+    if (NV % NT == 0 || i < NV) store_nt(S + 4 * i, v[k]);
+  }
+
+  // conv window of this head's q, k and v channels
+  const long long HD = (long long)H * D, Cqkv = 3 * HD;
+  const int Wm1 = a.W - 1;
+  IO* cs = static_cast<IO*>(a.conv_state);
+  const IO* x = static_cast<const IO*>(a.qkv);
+  for (int j = part * NT + tid; Wm1 > 0 && j < 3 * D; j += NS * NT) {
+    const long long c = (long long)(j / D) * HD + (long long)h * D + (j % D);
+    IO win[kMaxConvWidth - 1];
+    // position p of (old window || accepted tokens), length Wm1 + m; keep p = m .. m + Wm1 - 1
+    for (int w = 0; w < Wm1; ++w) {
+      const int p = m + w;
+      win[w] = (p < Wm1) ? cs[(b * Cqkv + c) * Wm1 + p] : x[((long long)b * a.T_d + (p - Wm1)) * Cqkv + c];
+    }
+    for (int w = 0; w < Wm1; ++w) cs[(b * Cqkv + c) * Wm1 + w] = win[w];
+  }
+}
+
+template <int D, int WMAX, bool MULTI, bool TAPE>
 static hipError_t launch_rec_t(const LayerArgs& a, int io, int ot, hipStream_t s) {
   dim3 grid(a.H, a.B), block(RecLayout<D>::NT);
-  timing_begin(a.snapshots ? "kda_recurrent_kernel[verify]" : "kda_recurrent_kernel[decode]", s);
+  timing_begin(TAPE ? "kda_recurrent_kernel[verify_tape]"
+               : a.snapshots ? "kda_recurrent_kernel[verify]"
+                             : "kda_recurrent_kernel[decode]",
+               s);
   if (io == kBF16) {
     if (ot == kBF16)
-      kda_recurrent_kernel<D, WMAX, MULTI, bf16_t, bf16_t><<<grid, block, 0, s>>>(a);
+      kda_recurrent_kernel<D, WMAX, MULTI, TAPE, bf16_t, bf16_t><<<grid, block, 0, s>>>(a);
     else
-      kda_recurrent_kernel<D, WMAX, MULTI, bf16_t, float><<<grid, block, 0, s>>>(a);
+      kda_recurrent_kernel<D, WMAX, MULTI, TAPE, bf16_t, float><<<grid, block, 0, s>>>(a);
   } else {
     if (ot == kBF16)
-      kda_recurrent_kernel<D, WMAX, MULTI, float, bf16_t><<<grid, block, 0, s>>>(a);
+      kda_recurrent_kernel<D, WMAX, MULTI, TAPE, float, bf16_t><<<grid, block, 0, s>>>(a);
     else
-      kda_recurrent_kernel<D, WMAX, MULTI, float, float><<<grid, block, 0, s>>>(a);
+      kda_recurrent_kernel<D, WMAX, MULTI, TAPE, float, float><<<grid, block, 0, s>>>(a);
   }
   timing_end(s);
   return hipGetLastError();
 }
 
+// A one-token tape call runs the multi-token instance (its loop covers T = 1).
+template <int D, int WMAX>
+static hipError_t launch_rec_w(const LayerArgs& a, int io, int ot, hipStream_t s) {
+  if (a.tape != nullptr) return launch_rec_t<D, WMAX, true, true>(a, io, ot, s);
+  return a.T > 1 ? launch_rec_t<D, WMAX, true, false>(a, io, ot, s) : launch_rec_t<D, WMAX, false, false>(a, io, ot, s);
+}
+
 template <int D>
 static hipError_t launch_rec_d(const LayerArgs& a, int io, int ot, hipStream_t s) {
-  const bool multi = a.T > 1;
-  if (a.W <= 4) return multi ? launch_rec_t<D, 4, true>(a, io, ot, s) : launch_rec_t<D, 4, false>(a, io, ot, s);
-  return multi ? launch_rec_t<D, kMaxConvWidth, true>(a, io, ot, s) : launch_rec_t<D, kMaxConvWidth, false>(a, io, ot, s);
+  return a.W <= 4 ? launch_rec_w<D, 4>(a, io, ot, s) : launch_rec_w<D, kMaxConvWidth>(a, io, ot, s);
 }
 
 hipError_t launch_recurrent(const LayerArgs& a, int io, int ot, hipStream_t s) {
@@ -291,6 +414,28 @@ hipError_t launch_rollback(const RollbackArgs& a, int io, hipStream_t s) {
     kda_rollback_kernel<bf16_t><<<grid, block, 0, s>>>(a);
   else
     kda_rollback_kernel<float><<<grid, block, 0, s>>>(a);
+  timing_end(s);
+  return hipGetLastError();
+}
+
+template <int D>
+static void commit_d(const CommitArgs& a, int io, hipStream_t s) {
+  dim3 grid(a.H * CommitLayout<D>::NS, a.nB), block(kCommitNT);
+  if (io == kBF16)
+    kda_commit_tape_kernel<D, bf16_t><<<grid, block, 0, s>>>(a);
+  else
+    kda_commit_tape_kernel<D, float><<<grid, block, 0, s>>>(a);
+}
+
+hipError_t launch_commit_tape(const CommitArgs& a, int io, hipStream_t s) {
+  timing_begin("kda_commit_tape_kernel", s);
+  switch (a.D) {
+    case 16: commit_d<16>(a, io, s); break;
+    case 32: commit_d<32>(a, io, s); break;
+    case 64: commit_d<64>(a, io, s); break;
+    case 128: commit_d<128>(a, io, s); break;
+    default: timing_end(s); return hipErrorInvalidValue;
+  }
   timing_end(s);
   return hipGetLastError();
 }

@@ -147,6 +147,39 @@ kda_status kda_rollback(const kda_layer_desc* desc, int32_t B, int32_t T_d, cons
                         const float* snaps, const void* qkv_block, float* state, void* conv_state, void* stream);
 
 /*
+ * Speculative verify with a replay tape instead of snapshots.  The state after
+ * draft token t is Diag(alpha_t) S_{t-1} + k_t u_t^T, where alpha_t is the
+ * token's decay, k_t its normalised key and u_t = beta_t (v_t - (Diag(alpha_t)
+ * S_{t-1})^T k_t) its delta-rule update; all three are known once the verify
+ * pass has computed u_t.  Recording them (3*d floats per token and head)
+ * instead of the d*d state lets the commit replay the accepted prefix on the
+ * live state, so a block costs about three state passes (verify read, commit
+ * read and write) instead of 1 + T_d + 1.
+ *
+ * kda_verify_tape_size: bytes of the tape for (desc, B, T_d),
+ *   B * T_d * H * 3 * d * 4; (size_t)-1 if the arguments are invalid.
+ * kda_verify_block_tape: as kda_verify_block (same outputs, bit-identical),
+ *   but writes
+ *     tape [B, T_d, H, 3, d] fp32: tape[b, t, h] = (alpha, k, u) of token t
+ *   and no state at all.  state and conv_state are read only.
+ * kda_commit_tape: commits the accepted prefix from the tape.  accepted_host
+ *   is a HOST array of B counts m_b in 0..T_d (outside that range the call
+ *   fails; no clamping).  For each b with m_b > 0 it replays tokens 0..m_b-1
+ *   on state[b] (the state the verify call read), which gives the verify
+ *   pass's own state after token m_b bit for bit, and sets conv_state[b] to
+ *   the last W-1 raw inputs of (conv_state[b] || qkv_block[b, :m_b]).
+ *   Sequences with m_b = 0 are left untouched.  qkv_block is the verify call's
+ *   qkv; tape the verify call's tape, unchanged.
+ */
+size_t kda_verify_tape_size(const kda_layer_desc* desc, int32_t B, int32_t T_d);
+kda_status kda_verify_block_tape(const kda_layer_desc* desc, int32_t B, int32_t T_d, const void* qkv,
+                                 const void* f, const void* beta, const void* g_out, const float* state,
+                                 const void* conv_state, float* tape, void* out, void* stream);
+kda_status kda_commit_tape(const kda_layer_desc* desc, int32_t B, int32_t T_d, const int32_t* accepted_host,
+                           const float* tape, const void* qkv_block, float* state, void* conv_state,
+                           void* stream);
+
+/*
  * Per-kernel timing, for benchmarks (not part of the layer).
  * kda_timing_enable(1) makes every later call made on this host thread record
  * a HIP event pair on the call's stream around each kernel it launches;

@@ -228,6 +228,34 @@ def recurrence_token(q, k, v, g, beta, S0, record_states: bool = False):
     return o, S, states
 
 
+def recurrence_token_tape(q, k, v, g, beta, S0):
+    """The token recurrence of recurrence_token, also returning each token's
+    replay tape: alpha_t = exp(g_t) [H, dk] and u_t = beta_t (v_t - S'^T k_t)
+    [H, dv], with S' the decayed state the update reads.
+
+    With these the state after token t is Diag(alpha_t) S_{t-1} + k_t u_t^T, so
+    an accepted prefix of a draft block can be re-applied to the live state
+    without storing the state after every token (dflash-mlx issue #63, "What
+    the backend needs": rollback of a speculative block).
+    Returns (o [T,H,dv], S_T [H,dk,dv], alpha [T,H,dk], u [T,H,dv]).
+    """
+    q, k, v, g, beta = (_f64(a) for a in (q, k, v, g, beta))
+    S = _f64(S0).copy()
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    o = np.zeros((T, H, dv))
+    alpha = np.exp(g)
+    us = np.zeros((T, H, dv))
+    for t in range(T):
+        S = alpha[t][:, :, None] * S
+        kS = np.einsum("hk,hkv->hv", k[t], S)
+        u = beta[t][:, None] * (v[t] - kS)
+        S = S + k[t][:, :, None] * u[:, None, :]
+        o[t] = np.einsum("hk,hkv->hv", q[t], S)
+        us[t] = u
+    return o, S, alpha, us
+
+
 def ut_forward_substitution(A: np.ndarray, rhs: np.ndarray) -> np.ndarray:
     """Solve (I + A) X = rhs for strictly lower-triangular A by forward substitution.
 
@@ -397,6 +425,63 @@ def kda_rollback(p: KdaParams, accepted, snaps, qkv_block, state, conv_state):
         if m == 0:
             continue
         state[b] = snaps[b, m - 1]
+        xt = np.concatenate([conv_state[b].T, qkv_block[b, :m]], axis=0)
+        conv_state[b] = xt[xt.shape[0] - (W - 1):].T
+    return state, conv_state
+
+
+def kda_verify_tape(p: KdaParams, qkv, f, beta, g_out, state, conv_state):
+    """Verify a draft block recording a replay tape instead of snapshots.
+
+    Same outputs as kda_verify.  tape[b, t, h] = (alpha_t, k_t, u_t): the
+    token's decay exp(g_t), its normalised key and its delta-rule update, each
+    of length d (d_k == d_v).  The live state and conv state are not modified.
+    Returns dict(out [B,T_d,H*dv], tape [B,T_d,H,3,d]).
+    """
+    _check_lb(p)
+    if p.dk != p.dv:
+        raise ValueError("the replay tape needs d_k == d_v")
+    qkv, f, beta, g_out = (_f64(a) for a in (qkv, f, beta, g_out))
+    state, conv_state = _f64(state), _f64(conv_state)
+    B, T, _ = qkv.shape
+    H, d = p.H, p.dk
+    out = np.zeros((B, T, H * d))
+    tape = np.zeros((B, T, H, 3, d))
+    for b in range(B):
+        q, k, v, g, _cs = prologue(p, qkv[b], f[b], conv_state[b])
+        o, _S, alpha, u = recurrence_token_tape(q, k, v, g, beta[b], state[b])
+        tape[b, :, :, 0] = alpha
+        tape[b, :, :, 1] = k
+        tape[b, :, :, 2] = u
+        out[b] = gated_rmsnorm(o, g_out[b].reshape(T, H, d), p.norm_w, p.rms_eps).reshape(T, H * d)
+    return {"out": out, "tape": tape}
+
+
+def kda_commit_tape(p: KdaParams, accepted, tape, qkv_block, state, conv_state):
+    """Commit the accepted prefix of a block verified with a replay tape.
+
+    For each sequence b with m = accepted[b] in 0..T_d:
+        for t < m:  state[b] <- Diag(alpha_t) state[b] + k_t u_t^T
+        conv_state[b] <- the last W-1 rows of (conv_state[b] || qkv_block[b, :m])
+    state must be the state the verify call read.  Returns (state, conv_state)
+    as new float64 arrays.
+    """
+    tape, qkv_block = _f64(tape), _f64(qkv_block)
+    state, conv_state = _f64(state).copy(), _f64(conv_state).copy()
+    W = p.W
+    T_d = tape.shape[1]
+    for b, m in enumerate(accepted):
+        m = int(m)
+        if m < 0 or m > T_d:
+            raise ValueError("accepted prefix length out of range")
+        if m == 0:
+            continue
+        S = state[b]
+        for t in range(m):
+            alpha, k, u = tape[b, t, :, 0], tape[b, t, :, 1], tape[b, t, :, 2]
+            S = alpha[:, :, None] * S
+            S = S + k[:, :, None] * u[:, None, :]
+        state[b] = S
         xt = np.concatenate([conv_state[b].T, qkv_block[b, :m]], axis=0)
         conv_state[b] = xt[xt.shape[0] - (W - 1):].T
     return state, conv_state

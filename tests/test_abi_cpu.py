@@ -33,6 +33,7 @@ def test_library_exports_every_header_function():
     names = abi.header_functions()
     assert set(names) == {"kda_abi_version", "kda_status_string", "kda_last_error", "kda_prefill_workspace_size",
                           "kda_prefill", "kda_decode_step", "kda_verify_block", "kda_rollback",
+                          "kda_verify_tape_size", "kda_verify_block_tape", "kda_commit_tape",
                           "kda_timing_enable", "kda_timing_read"}
     for n in names:
         assert hasattr(lib, n), n
@@ -96,6 +97,30 @@ def test_verify_and_rollback_validation():
         assert st == abi.KDA_ERR_INVALID_ARGUMENT
         assert f"accepted[1] = {bad} outside 0..8".encode() in lib.kda_last_error()
     assert lib.kda_rollback(ctypes.byref(d), 2, 8, None, P, P, P, P, None) == abi.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_verify_tape_and_commit_validation():
+    lib = abi.load()
+    d = desc()
+    P = FAKE
+    assert lib.kda_verify_block_tape(ctypes.byref(d), 3, 0, 0, 0, 0, 0, 0, 0, 0, 0, None) == abi.KDA_OK
+    assert lib.kda_verify_block_tape(ctypes.byref(d), 1, 256, P, P, P, P, P, P, P, P, None) == abi.KDA_ERR_UNSUPPORTED
+    assert lib.kda_verify_block_tape(ctypes.byref(d), 1, 8, P, P, P, P, P, P, 0, P, None) == abi.KDA_ERR_INVALID_ARGUMENT
+    assert b"tape is null" in lib.kda_last_error()
+    acc = (ctypes.c_int32 * 2)(0, 0)  # nothing accepted: no-op, no pointer looked at
+    assert lib.kda_commit_tape(ctypes.byref(d), 2, 8, ctypes.cast(acc, ctypes.c_void_p), 0, 0, 0, 0, None) == abi.KDA_OK
+    for bad in (-1, 9):
+        acc = (ctypes.c_int32 * 2)(3, bad)
+        st = lib.kda_commit_tape(ctypes.byref(d), 2, 8, ctypes.cast(acc, ctypes.c_void_p), P, P, P, P, None)
+        assert st == abi.KDA_ERR_INVALID_ARGUMENT
+        assert f"accepted[1] = {bad} outside 0..8".encode() in lib.kda_last_error()
+    acc = (ctypes.c_int32 * 2)(3, 0)
+    st = lib.kda_commit_tape(ctypes.byref(d), 2, 8, ctypes.cast(acc, ctypes.c_void_p), 0, P, P, P, None)
+    assert st == abi.KDA_ERR_INVALID_ARGUMENT and b"tape is null" in lib.kda_last_error()
+    # B * T_d * H * 3 * d fp32 (the test descriptor: H = 2, d = 16)
+    assert lib.kda_verify_tape_size(ctypes.byref(d), 4, 8) == 4 * 8 * d.num_heads * 3 * d.head_dim_k * 4
+    bad = desc(gate_lower_bound=math.nan)
+    assert lib.kda_verify_tape_size(ctypes.byref(bad), 4, 8) == ctypes.c_size_t(-1).value
 
 
 def test_workspace_size():

@@ -13,6 +13,8 @@ import torch
 from hybrid_linear_attention_kda_amd import abi
 from hybrid_linear_attention_kda_amd import inputs as I
 from hybrid_linear_attention_kda_amd import tensors as TT
+import parity_util as pu
+from oracle import kda_oracle as O
 from parity_util import TOL, TOL_BF16_OUT, head_channels, oracle_layer, oracle_prefilled, rel_err, say
 
 pytestmark = pytest.mark.gpu
@@ -145,6 +147,83 @@ def test_tiny_fp32_verify_rollback_replay():
             sub[k] = inp[k][b:b + 1]
         ref_c = oracle_layer(wl, sub, 6, 6 + m, S0[b:b + 1], C0[b:b + 1])["conv_state"][0]
         _check(f"rolled-back conv b={b} m={m}", cs[b], ref_c, 0.0)
+
+
+def _bit_equal(name, a, b):
+    same = torch.equal(a, b)
+    say(f"  {name}: bit-identical {same}")
+    assert same, name
+
+
+def test_tiny_fp32_verify_tape_and_commit():
+    wl = I.WORKLOADS["tiny_fp32"].with_(T=8, B=4, prefix_T=6)
+    say("case tiny_fp32 verify with replay tape + commit")
+    inp = I.generate(wl)
+    pre = oracle_layer(wl, inp, 0, 6, inp["state0"], inp["conv_state0"])
+    S0, C0 = pre["state"].astype(np.float32), pre["conv_state"].astype(np.float32)
+    layer = TT.make_layer(wl, inp, DEV)
+    tok = TT.token_tensors(wl, inp, 6, 14, DEV)
+    # snapshot path
+    st1, cs1 = _dev_state(wl, inp, S0, C0)
+    snaps = torch.empty((4, 8, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=DEV)
+    out1 = torch.empty((4, 8, wl.H * wl.dv), dtype=torch.float32, device=DEV)
+    abi.kda_verify_block(layer, tok["qkv"], tok["f"], tok["beta"], tok["g_out"], st1, cs1, snaps, out1)
+    # tape path
+    st2, cs2 = _dev_state(wl, inp, S0, C0)
+    assert abi.kda_verify_tape_size(layer, 4, 8) == 4 * 8 * wl.H * 3 * wl.dk * 4
+    tape = torch.empty((4, 8, wl.H, 3, wl.dk), dtype=torch.float32, device=DEV)
+    out2 = torch.empty_like(out1)
+    abi.kda_verify_block_tape(layer, tok["qkv"], tok["f"], tok["beta"], tok["g_out"], st2, cs2, tape, out2)
+    torch.cuda.synchronize()
+    _bit_equal("verify out, tape vs snapshot path", out2, out1)
+    _check("live state untouched", st2, S0, 0.0)
+    sub = I.split_tokens(inp, 6, 14)
+    ref = O.kda_verify_tape(pu.params(wl, inp), sub["qkv"], sub["f"], sub["beta"], sub["g_out"], S0, C0)
+    _check("verify out", out2, ref["out"], TOL["f32"])
+    for j, name in enumerate(("alpha", "k", "u")):
+        _check(f"tape {name}", tape[:, :, :, j], ref["tape"][:, :, :, j], TOL["f32"])
+    accepted = [0, 3, 8, 5]
+    abi.kda_rollback(layer, accepted, snaps, tok["qkv"], st1, cs1)
+    abi.kda_commit_tape(layer, accepted, tape, tok["qkv"], st2, cs2)
+    torch.cuda.synchronize()
+    _bit_equal("committed state, tape vs snapshot path", st2, st1)
+    _bit_equal("committed conv state, tape vs snapshot path", cs2, cs1)
+    ref_s, ref_c = O.kda_commit_tape(pu.params(wl, inp), accepted, ref["tape"], sub["qkv"], S0, C0)
+    _check("committed state", st2, ref_s, TOL["f32"])
+    _check("committed conv state", cs2, ref_c, 0.0)
+
+
+def test_verify_tape_b16_full_size_with_commit():
+    wl = I.WORKLOADS["verify_b16"]
+    say("case verify_b16 full size (B=16, T_d=8, H=32, d=128) with replay tape + commit")
+    inp = I.generate(wl)
+    S0, C0 = oracle_prefilled(wl, inp, n_pre=2)
+    layer = TT.make_layer(wl, inp, DEV)
+    t0 = wl.prefix_T
+    tok = TT.token_tensors(wl, inp, t0, t0 + wl.T, DEV)
+    st1, cs1 = _dev_state(wl, inp, S0, C0)
+    snaps = torch.empty((wl.B, wl.T, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=DEV)
+    out1 = torch.empty((wl.B, wl.T, wl.H * wl.dv), dtype=torch.float32, device=DEV)
+    abi.kda_verify_block(layer, tok["qkv"], tok["f"], tok["beta"], tok["g_out"], st1, cs1, snaps, out1)
+    st2, cs2 = _dev_state(wl, inp, S0, C0)
+    tape = torch.empty((wl.B, wl.T, wl.H, 3, wl.dk), dtype=torch.float32, device=DEV)
+    out2 = torch.empty_like(out1)
+    abi.kda_verify_block_tape(layer, tok["qkv"], tok["f"], tok["beta"], tok["g_out"], st2, cs2, tape, out2)
+    torch.cuda.synchronize()
+    _bit_equal("verify out, tape vs snapshot path", out2, out1)
+    accepted = [int(m) for m in inp["accepted"]]
+    say(f"  accepted = {accepted}")
+    abi.kda_rollback(layer, accepted, snaps, tok["qkv"], st1, cs1)
+    abi.kda_commit_tape(layer, accepted, tape, tok["qkv"], st2, cs2)
+    torch.cuda.synchronize()
+    _bit_equal("committed state, tape vs snapshot path", st2, st1)
+    _bit_equal("committed conv state, tape vs snapshot path", cs2, cs1)
+    sub = I.split_tokens(inp, t0, t0 + wl.T)
+    ref = O.kda_verify_tape(pu.params(wl, inp), sub["qkv"], sub["f"], sub["beta"], sub["g_out"], S0, C0)
+    _check("verify out", out2, ref["out"], TOL["bf16"])
+    ref_s, ref_c = O.kda_commit_tape(pu.params(wl, inp), accepted, ref["tape"], sub["qkv"], S0, C0)
+    _check("committed state", st2, ref_s, TOL["bf16"])
+    _check("committed conv state", cs2, ref_c, 0.0)
 
 
 # ---------------------------------------------------------------------------

@@ -399,6 +399,60 @@ def test_rollback_rejects_out_of_range():
         O.kda_rollback(p, [9], snaps, inp["qkv"], inp["state0"], inp["conv_state0"])
 
 
+def test_verify_tape_outputs_equal_snapshot_verify():
+    wl, inp, p = _tiny(8, B=2)
+    S0 = RNG.standard_normal((2, wl.H, wl.dk, wl.dv))
+    cs0 = RNG.standard_normal(inp["conv_state0"].shape)
+    v = O.kda_verify(p, inp["qkv"], inp["f"], inp["beta"], inp["g_out"], S0, cs0)
+    vt = O.kda_verify_tape(p, inp["qkv"], inp["f"], inp["beta"], inp["g_out"], S0, cs0)
+    np.testing.assert_array_equal(vt["out"], v["out"])
+    # the tape's key is the normalised key and its decay exp(g), straight from the prologue
+    q, k, vv, g, _ = O.prologue(p, inp["qkv"][0], inp["f"][0], cs0[0])
+    np.testing.assert_array_equal(vt["tape"][0, :, :, 1], k)
+    np.testing.assert_array_equal(vt["tape"][0, :, :, 0], np.exp(g))
+
+
+@pytest.mark.parametrize("m", list(range(9)))
+def test_tape_commit_equals_snapshot_rollback(m):
+    # The replayed state is the verify pass's own state after m tokens (same operations in the
+    # same order), and the conv window is the rollback's.
+    wl, inp, p = _tiny(8, B=2)
+    S0 = RNG.standard_normal((2, wl.H, wl.dk, wl.dv))
+    cs0 = RNG.standard_normal(inp["conv_state0"].shape)
+    v = O.kda_verify(p, inp["qkv"], inp["f"], inp["beta"], inp["g_out"], S0, cs0)
+    vt = O.kda_verify_tape(p, inp["qkv"], inp["f"], inp["beta"], inp["g_out"], S0, cs0)
+    acc = [m, 8 - m]
+    S1, c1 = O.kda_rollback(p, acc, v["snaps"], inp["qkv"], S0, cs0)
+    S2, c2 = O.kda_commit_tape(p, acc, vt["tape"], inp["qkv"], S0, cs0)
+    np.testing.assert_array_equal(S2, S1)
+    np.testing.assert_array_equal(c2, c1)
+
+
+def test_tape_closed_forms():
+    # beta = 0: every u is zero and the commit is the pure key-axis decay prod_t alpha_t of S0;
+    # one token from a zero state: u = beta v.
+    wl, inp, p = _tiny(6, B=1)
+    S0 = RNG.standard_normal((1, wl.H, wl.dk, wl.dv))
+    cs0 = inp["conv_state0"]
+    z = np.zeros_like(inp["beta"])
+    vt = O.kda_verify_tape(p, inp["qkv"], inp["f"], z, inp["g_out"], S0, cs0)
+    assert np.all(vt["tape"][:, :, :, 2] == 0.0)
+    S, _ = O.kda_commit_tape(p, [6], vt["tape"], inp["qkv"], S0, cs0)
+    decay = np.prod(vt["tape"][0, :, :, 0], axis=0)  # [H, dk]
+    np.testing.assert_allclose(S[0], decay[:, :, None] * S0[0], rtol=1e-13, atol=0)
+    vt1 = O.kda_verify_tape(p, inp["qkv"][:, :1], inp["f"][:, :1], inp["beta"][:, :1], inp["g_out"][:, :1],
+                            np.zeros_like(S0), cs0)
+    _, _, vv, _, _ = O.prologue(p, inp["qkv"][0, :1], inp["f"][0, :1], cs0[0])
+    np.testing.assert_allclose(vt1["tape"][0, 0, :, 2], inp["beta"][0, 0][:, None] * vv[0], rtol=1e-15, atol=0)
+
+
+def test_commit_tape_rejects_out_of_range():
+    wl, inp, p = _tiny(8)
+    tape = np.zeros((1, 8, wl.H, 3, wl.dk))
+    with pytest.raises(ValueError):
+        O.kda_commit_tape(p, [9], tape, inp["qkv"], inp["state0"], inp["conv_state0"])
+
+
 def test_missing_gate_lower_bound_is_an_error():
     wl, inp, p = _tiny(4)
     p.lb = float("nan")
