@@ -52,8 +52,12 @@ __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerAr
   const int HD = H * D;
   const int Cqkv = 3 * HD;
 
-  __shared__ float s_q[D], s_k[D], s_v[D], s_alpha[D], s_u[D], s_o[D];
+  // q, k, v and alpha alternate between two buffers by token parity, so that the next token's
+  // conv can write them while this token's update still reads k (no end-of-token barrier)
+  __shared__ float s_q[2][D], s_k[2][D], s_v[2][D], s_alpha[2][D], s_u[D], s_o[D];
   __shared__ float s_part[2][L::RG][D];
+  __shared__ float s_nrm[3][L::RG];  // per row group: sum q^2, sum k^2, sum q k (raw q, k)
+  __shared__ float s_rk;
 
   // Uniform (per-workgroup) base pointers; lanes add 32-bit offsets.
   const long long bh = (long long)b * H + h;
@@ -124,6 +128,7 @@ __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerAr
   for (int pj = 0; pj < PF; ++pj) {
     const int t = t0 + pj;
     if (t >= T) break;
+    const int pb = t & 1;
     // conv + SiLU over this lane's channels; advance the window
 #pragma unroll
     for (int n = 0; n < NCH; ++n) {
@@ -137,53 +142,56 @@ __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerAr
       if (c < C3) {
         const float z = y / (1.0f + expf(-y));
         const int part = c / D, i = c % D;
-        (part == 0 ? s_q : part == 1 ? s_k : s_v)[i] = z;
+        (part == 0 ? s_q[pb] : part == 1 ? s_k[pb] : s_v[pb])[i] = z;
       }
     }
     // bounded-sigmoid decay gate (log-decay in (lb, 0)), per key channel
-    if (tid < D) s_alpha[tid] = expf(a.lb / (1.0f + expf(-Ah * (fs[pj] + dtb))));
+    if (tid < D) s_alpha[pb][tid] = expf(a.lb / (1.0f + expf(-Ah * (fs[pj] + dtb))));
     const float bt = bs[pj], gcur = gs[pj];
     if (MULTI && t + PF < T) load_token(pj, t + PF);  // refill the slot: issued before this token's stores
     __syncthreads();
-    // q/k norms and q.k, computed redundantly by every wave (no extra barrier)
-    float qq = 0.f, kk = 0.f, qk = 0.f;
-    for (int i = lane; i < D; i += 64) {
-      qq += s_q[i] * s_q[i];
-      kk += s_k[i] * s_k[i];
-      qk += s_q[i] * s_k[i];
-    }
-    qq = wave_sum(qq);
-    kk = wave_sum(kk);
-    qk = wave_sum(qk);
-    const float rq = a.scale / fmaxf(sqrtf(qq), a.l2_eps);
-    const float rk = 1.0f / fmaxf(sqrtf(kk), a.l2_eps);
-    const float qkn = qk * rq * rk;
 
-    // 3. One sweep over this lane's rows: decay, then partial S'^T k and S'^T q.
+    // 3. One sweep over this lane's rows with the raw (unnormalised) q and k: decay, partial
+    //    S'^T k and S'^T q, and the row group's share of |q|^2, |k|^2 and q.k.  The L2 scales
+    //    are applied to the reduced sums, so no reduction stands between the conv and the sweep.
     float4 kS = make_float4(0.f, 0.f, 0.f, 0.f), qS = kS;
+    float nq = 0.f, nk = 0.f, nqk = 0.f;
 #pragma unroll
     for (int r = 0; r < L::RPT; ++r) {
       const int i = rg * L::RPT + r;
-      const float al = s_alpha[i], ki = s_k[i] * rk, qi = s_q[i] * rq;
+      const float al = s_alpha[pb][i], ki = s_k[pb][i], qi = s_q[pb][i];
       S[r].x *= al; S[r].y *= al; S[r].z *= al; S[r].w *= al;
       kS.x += ki * S[r].x; kS.y += ki * S[r].y; kS.z += ki * S[r].z; kS.w += ki * S[r].w;
       qS.x += qi * S[r].x; qS.y += qi * S[r].y; qS.z += qi * S[r].z; qS.w += qi * S[r].w;
+      nq += qi * qi; nk += ki * ki; nqk += qi * ki;
     }
     *reinterpret_cast<float4*>(&s_part[0][rg][4 * cg]) = kS;
     *reinterpret_cast<float4*>(&s_part[1][rg][4 * cg]) = qS;
+    if (cg == 0) {
+      s_nrm[0][rg] = nq;
+      s_nrm[1][rg] = nk;
+      s_nrm[2][rg] = nqk;
+    }
     __syncthreads();
     if (tid < D) {
-      float ks = 0.f, qs = 0.f;
+      float ks = 0.f, qs = 0.f, qq = 0.f, kk = 0.f, qk = 0.f;
 #pragma unroll
       for (int g = 0; g < L::RG; ++g) {
         ks += s_part[0][g][tid];
         qs += s_part[1][g][tid];
+        qq += s_nrm[0][g];
+        kk += s_nrm[1][g];
+        qk += s_nrm[2][g];
       }
-      const float u = bt * (s_v[tid] - ks);
+      const float rq = a.scale / fmaxf(sqrtf(qq), a.l2_eps);
+      const float rk = 1.0f / fmaxf(sqrtf(kk), a.l2_eps);
+      const float u = bt * (s_v[pb][tid] - rk * ks);
       s_u[tid] = u;
-      s_o[tid] = qs + qkn * u;
+      s_o[tid] = rq * qs + (qk * rq * rk) * u;
+      if (tid == 0) s_rk = rk;
     }
     __syncthreads();
+    const float rk = s_rk;
 
     // 4. Rank-1 update in registers (one fused multiply-add per element, as the tape replay does);
     //    verify streams a snapshot per token, or the token's replay tape, decode the final state.
@@ -191,7 +199,7 @@ __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerAr
       const float4 u4 = *reinterpret_cast<const float4*>(&s_u[4 * cg]);
 #pragma unroll
       for (int r = 0; r < L::RPT; ++r) {
-        const float ki = s_k[rg * L::RPT + r] * rk;
+        const float ki = s_k[pb][rg * L::RPT + r] * rk;
         S[r].x = __builtin_fmaf(ki, u4.x, S[r].x);
         S[r].y = __builtin_fmaf(ki, u4.y, S[r].y);
         S[r].z = __builtin_fmaf(ki, u4.z, S[r].z);
@@ -200,8 +208,8 @@ __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerAr
       if (TAPE) {
         if (tid < D) {
           float* tp = a.tape + (((long long)b * T + t) * H + h) * 3 * D;
-          tp[tid] = s_alpha[tid];
-          tp[D + tid] = s_k[tid] * rk;
+          tp[tid] = s_alpha[pb][tid];
+          tp[D + tid] = s_k[pb][tid] * rk;
           tp[2 * D + tid] = s_u[tid];
         }
       } else {
@@ -214,15 +222,18 @@ __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerAr
       }
     }
 
-    // 5. Gated RMSNorm over d_v (every wave reduces; lanes < D write).
-    float oo = 0.f;
-    for (int j = lane; j < D; j += 64) oo += s_o[j] * s_o[j];
-    oo = wave_sum(oo);
-    if (tid < D) {
-      const float rr = rsqrtf(oo / (float)D + a.rms_eps);
-      store_as(&out[(long long)t * HD + tid], s_o[tid] * rr * nwj / (1.0f + expf(-gcur)));
+    // 5. Gated RMSNorm over d_v (the waves holding lanes < D reduce and write).  s_o and s_u
+    //    are rewritten only after the next token's second barrier, which every lane reaches
+    //    after this point.
+    if (tid < ((D + 63) / 64) * 64) {
+      float oo = 0.f;
+      for (int j = lane; j < D; j += 64) oo += s_o[j] * s_o[j];
+      oo = wave_sum(oo);
+      if (tid < D) {
+        const float rr = rsqrtf(oo / (float)D + a.rms_eps);
+        store_as(&out[(long long)t * HD + tid], s_o[tid] * rr * nwj / (1.0f + expf(-gcur)));
+      }
     }
-    if (MULTI && t + 1 < T) __syncthreads();  // s_q/s_k/s_o are rewritten by the next token
   }
   }
 
