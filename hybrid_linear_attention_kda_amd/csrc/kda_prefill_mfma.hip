@@ -502,8 +502,10 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
     }
     __syncthreads();
 
-    // ---- P6a: A_kk = beta_i * KR_I E_IJ . KC_J^T (plain bf16), strictly lower ----
-    for (int bi = wave; bi < 10; bi += 8) {
+    // ---- P6a: A_kk = beta_i * KR_I E_IJ . KC_J^T (plain bf16), strictly lower: one 16 x 16 block.
+    //      The diagonal blocks and four below them here, one per wave; blocks (3,1) and (3,2),
+    //      which only the off-diagonal T chains read, during the diagonal solve ----
+    auto akk_block = [&](int bi) {
       int I, J;
       block_ij(bi, I, J);
       f32x4 acc = zero4();
@@ -525,7 +527,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
         const int i = 16 * I + 4 * lg + r, j = 16 * J + l16;
         sAkk[i * PA + j] = j < i ? sBeta[i] * acc[r] : 0.f;
       }
-    }
+    };
+    akk_block(wave < 7 ? wave : 9);
     __syncthreads();
 
     // ---- P6b: A_qk = QR_I E_IJ . KC_J^T (split bf16), lower incl. diagonal: one 16 x 16 block ----
@@ -557,7 +560,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
     };
 
     // ---- P7: T = (I + A_kk)^-1 in fp32: diagonal 16x16 blocks by forward substitution on wave 0,
-    //      while waves 1-7 clear T's strictly-upper blocks and form A_qk blocks 0..6 ----
+    //      while waves 1-7 clear T's strictly-upper blocks, waves 1-2 form A_kk blocks (3,1) and
+    //      (3,2) and waves 3-7 A_qk blocks 0..4 ----
     if (wave == 0) {
       // lane: column cc of diagonal block I.  Column-oriented: once x[j] is final it is folded
       // into every row below at once, so the dependent chain is 16 steps long; each x[i] still
@@ -588,11 +592,14 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
         sAhi[o] = (__bf16)0.f;
         sAlo[o] = (__bf16)0.f;
       }
-      aqk_block(wave - 1);
+      if (wave < 3)
+        akk_block(wave + 6);
+      else
+        aqk_block(wave - 3);
     }
     __syncthreads();
     // Off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, column block J = wave (0..2)
-    // top to bottom on the fp32 matrix cores, while waves 3-5 form A_qk blocks 7..9.
+    // top to bottom on the fp32 matrix cores, while waves 3-7 form A_qk blocks 5..9.
     if (wave < 3) {
       const int J = wave;
       float* sM = sTmp + wave * 16 * 17;
@@ -613,8 +620,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
         for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * lg + r) * PA + 16 * J + l16] = -tij[r];
         wave_lds_sync();
       }
-    } else if (wave < 6) {
-      aqk_block(wave + 4);
+    } else {
+      aqk_block(wave + 2);
     }
     __syncthreads();
     // T as split bf16 planes in place of A_kk: eight elements per lane
@@ -677,8 +684,9 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
       const int t = task >> 4, c8 = (task & 15) * 8;
       const int fo = frag_offset(t, c8, D);
       *reinterpret_cast<bf16x8*>(wdst + fo) = *reinterpret_cast<const bf16x8*>(sKb + t * PKB + c8);
-      // K~^T = (KC e^(Gam_C - Gam_n(J)))^T: [128 channels][64 tokens]
-      const int c = task >> 3, t8 = (task & 7) * 8;
+      // K~^T = (KC e^(Gam_C - Gam_n(J)))^T: [128 channels][64 tokens]; the lanes of a wave take
+      // 64 consecutive channels of one 8-token group, so the column reads of KC hit 64 banks
+      const int c = task & 127, t8 = (task >> 7) * 8;
       const int ko = frag_offset(c, t8, C);
       const float fac = sFac[(t8 >> 4) * D + c];
       float v[8];
