@@ -66,6 +66,8 @@ def load() -> ctypes.CDLL:
         "kda_verify_block": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P, P, P, P]),
         "kda_rollback": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P]),
         "kda_verify_tape_size": (c_size_t, [D, c_int32, c_int32]),
+        "kda_prefill_varlen_workspace_size": (c_size_t, [D, c_int32, P]),
+        "kda_prefill_varlen": (c_int32, [D, c_int32, P, P, c_int32, P, P, P, P, P, P, P, P, c_size_t, P]),
         "kda_verify_block_tape": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P, P, P, P]),
         "kda_commit_tape": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P]),
         "kda_timing_enable": (c_int32, [c_int32]),
@@ -227,6 +229,46 @@ def kda_rollback(layer: KdaLayer, accepted, snaps, qkv_block, state, conv_state,
     _check_state(layer, B, state, conv_state)
     _check(load().kda_rollback(ctypes.byref(layer.desc), B, T_d, ctypes.cast(acc, c_void_p), _ptr(snaps),
                                _ptr(qkv_block), _ptr(state), _ptr(conv_state), _stream(stream)))
+
+
+def _int32_array(values):
+    vals = [int(v) for v in values]
+    return (ctypes.c_int32 * max(len(vals), 1))(*vals), len(vals)
+
+
+def kda_prefill_varlen_workspace_size(layer: KdaLayer, cu_seqlens) -> int:
+    cu, n = _int32_array(cu_seqlens)
+    size = load().kda_prefill_varlen_workspace_size(ctypes.byref(layer.desc), n - 1, ctypes.cast(cu, c_void_p))
+    if size == ctypes.c_size_t(-1).value:
+        raise KdaError(KDA_ERR_INVALID_ARGUMENT, load().kda_last_error().decode())
+    return size
+
+
+def kda_prefill_varlen(layer: KdaLayer, cu_seqlens, slots, qkv, f, beta, g_out, state, conv_state, out,
+                       workspace=None, stream=None):
+    """Sequences packed along the token axis (cu_seqlens, host list of N+1 offsets), each continuing
+    the state in its own slot (slots: host list of N, or None for slot i)."""
+    cu, n1 = _int32_array(cu_seqlens)
+    N = n1 - 1
+    total = int(cu_seqlens[-1]) if N >= 0 else 0
+    num_slots = state.shape[0]
+    sl = None
+    if slots is not None:
+        if len(slots) != N:
+            raise ValueError(f"slots has {len(slots)} entries, expected {N}")
+        sl, _ = _int32_array(slots)
+    _check_tokens(layer, 1, total, qkv.view(1, total, -1), f.view(1, total, -1), beta.view(1, total, -1),
+                  g_out.view(1, total, -1))
+    _check_state(layer, num_slots, state, conv_state)
+    _expect(out.view(1, total, -1), (1, total, layer.H * layer.D), layer.out_torch, "out")
+    need = kda_prefill_varlen_workspace_size(layer, cu_seqlens)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if ws_bytes < need:
+        raise ValueError(f"workspace of {ws_bytes} bytes, {need} needed")
+    _check(load().kda_prefill_varlen(ctypes.byref(layer.desc), N, ctypes.cast(cu, c_void_p),
+                                     ctypes.cast(sl, c_void_p) if sl is not None else None, num_slots,
+                                     _ptr(qkv), _ptr(f), _ptr(beta), _ptr(g_out), _ptr(state), _ptr(conv_state),
+                                     _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def kda_verify_tape_size(layer: KdaLayer, B: int, T_d: int) -> int:

@@ -117,6 +117,64 @@ kda_status launched(hipError_t e, const char* what) {
   return ok();
 }
 
+// One launch of a variable-length prefill: up to kVarlenBatch sequences of length >= 1, packed from
+// token t0 of the call on (the table's token offsets are relative to t0).
+struct Launch {
+  long long t0;
+  kda::SeqTab tab;
+};
+
+// Validate a variable-length call and cut it into launches.  cu_seqlens[0] = 0 and non-decreasing;
+// slots (NULL: sequence i uses slot i) in 0..num_slots-1 and distinct.  Sequences of length 0 are
+// no-ops and get no table entry.
+kda_status plan_varlen(int32_t N, const int32_t* cu, const int32_t* slots, int32_t num_slots, std::vector<Launch>& plan) {
+  plan.clear();
+  if (N < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "N must be >= 0");
+  if (N == 0) return KDA_OK;
+  if (cu == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host is null");
+  if (cu[0] != 0) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens[0] = %d, must be 0", cu[0]);
+  if (num_slots < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "num_slots must be >= 1");
+  std::vector<char> used((size_t)num_slots, 0);
+  Launch cur{};
+  for (int32_t i = 0; i < N; ++i) {
+    if (cu[i + 1] < cu[i])
+      return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens decreases at %d (%d -> %d)", i, cu[i], cu[i + 1]);
+    const int32_t slot = slots != nullptr ? slots[i] : i;
+    if (slot < 0 || slot >= num_slots)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "slot of sequence %d = %d outside 0..%d", i, slot, num_slots - 1);
+    if (used[(size_t)slot]) return fail(KDA_ERR_INVALID_ARGUMENT, "slot %d is used by two sequences", slot);
+    used[(size_t)slot] = 1;
+    const int32_t len = cu[i + 1] - cu[i];
+    if (len == 0) continue;
+    if (cur.tab.n == kda::kVarlenBatch) {
+      plan.push_back(cur);
+      cur = Launch{};
+    }
+    kda::SeqTab& t = cur.tab;
+    if (t.n == 0) {
+      cur.t0 = cu[i];
+      t.tok0[0] = 0;
+      t.chunk0[0] = 0;
+    }
+    t.slot[t.n] = slot;
+    t.tok0[t.n + 1] = cu[i + 1] - (int32_t)cur.t0;
+    t.chunk0[t.n + 1] = t.chunk0[t.n] + (len + kda::kMfmaChunk - 1) / kda::kMfmaChunk;
+    t.total_chunks = t.chunk0[t.n + 1];
+    ++t.n;
+  }
+  if (cur.tab.n > 0) plan.push_back(cur);
+  return KDA_OK;
+}
+
+size_t varlen_workspace(const std::vector<Launch>& plan, int H) {
+  size_t need = 0;
+  for (const Launch& l : plan) {
+    const size_t n = kda::prefill_mfma_workspace(l.tab.total_chunks, l.tab.tok0[l.tab.n], H);
+    if (n > need) need = n;
+  }
+  return need;
+}
+
 kda_status check_token_tensors(const void* qkv, const void* f, const void* beta, const void* g_out) {
   KDA_TRY(check_ptr(qkv, "qkv"));
   KDA_TRY(check_ptr(f, "f"));
@@ -146,7 +204,8 @@ const char* kda_last_error(void) { return g_last_error; }
 size_t kda_prefill_workspace_size(const kda_layer_desc* desc, int32_t B, int32_t T) {
   if (check_desc(desc) != KDA_OK || check_batch(B, T) != KDA_OK || check_chunk(desc) != KDA_OK) return (size_t)-1;
   if (!mfma_path(desc)) return 0;
-  return kda::prefill_mfma_workspace(B, T, desc->num_heads, desc->head_dim_k, desc->chunk_size);
+  const long long nc = ((long long)T + kda::kMfmaChunk - 1) / kda::kMfmaChunk;
+  return kda::prefill_mfma_workspace((long long)B * nc, (long long)B * T, desc->num_heads);
 }
 
 kda_status kda_prefill(const kda_layer_desc* desc, int32_t B, int32_t T, const void* qkv, const void* f,
@@ -173,7 +232,7 @@ kda_status kda_prefill(const kda_layer_desc* desc, int32_t B, int32_t T, const v
   a.snapshots = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (mfma_path(desc)) {
-    const size_t need = kda::prefill_mfma_workspace(B, T, a.H, a.D, desc->chunk_size);
+    const size_t need = kda_prefill_workspace_size(desc, B, T);
     if (need > 0) {
       if (workspace == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is null (%zu bytes needed)", need);
       if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -181,10 +240,66 @@ kda_status kda_prefill(const kda_layer_desc* desc, int32_t B, int32_t T, const v
       if (workspace_bytes < need)
         return fail(KDA_ERR_INVALID_ARGUMENT, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
     }
-    return launched(kda::launch_prefill_mfma(a, workspace, workspace_bytes, desc->out_dtype, s), "kda_prefill");
+    return launched(kda::launch_prefill_mfma(a, kda::SeqTab{}, workspace, workspace_bytes, desc->out_dtype, s),
+                    "kda_prefill");
   }
-  return launched(kda::launch_prefill_generic(a, desc->chunk_size, desc->io_dtype, desc->out_dtype, s),
+  return launched(kda::launch_prefill_generic(a, kda::SeqTab{}, desc->chunk_size, desc->io_dtype, desc->out_dtype, s),
                   "kda_prefill");
+}
+
+size_t kda_prefill_varlen_workspace_size(const kda_layer_desc* desc, int32_t N, const int32_t* cu_seqlens_host) {
+  if (check_desc(desc) != KDA_OK || check_chunk(desc) != KDA_OK) return (size_t)-1;
+  std::vector<Launch> plan;
+  // slots do not change the size: check the offsets with slot i for sequence i
+  if (plan_varlen(N, cu_seqlens_host, nullptr, N > 0 ? N : 1, plan) != KDA_OK) return (size_t)-1;
+  if (!mfma_path(desc)) return 0;
+  return varlen_workspace(plan, desc->num_heads);
+}
+
+kda_status kda_prefill_varlen(const kda_layer_desc* desc, int32_t N, const int32_t* cu_seqlens_host,
+                              const int32_t* slots_host, int32_t num_slots, const void* qkv, const void* f,
+                              const void* beta, const void* g_out, float* state, void* conv_state, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  KDA_TRY(check_desc(desc));
+  KDA_TRY(check_chunk(desc));
+  std::vector<Launch> plan;
+  KDA_TRY(plan_varlen(N, cu_seqlens_host, slots_host, num_slots, plan));
+  if (plan.empty()) return ok();  // no sequence has a token
+  KDA_TRY(check_token_tensors(qkv, f, beta, g_out));
+  KDA_TRY(check_ptr(state, "state"));
+  if (desc->conv_width > 1) KDA_TRY(check_ptr(conv_state, "conv_state"));
+  KDA_TRY(check_ptr(out, "out"));
+  const bool mfma = mfma_path(desc);
+  if (mfma) {
+    const size_t need = varlen_workspace(plan, desc->num_heads);
+    if (workspace == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is null (%zu bytes needed)", need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t io = desc->io_dtype == KDA_BF16 ? 2 : 4, ob = desc->out_dtype == KDA_BF16 ? 2 : 4;
+  const long long H = desc->num_heads, HD = H * desc->head_dim_k;
+  for (const Launch& l : plan) {
+    // each launch sees its tokens from its first one on; slots stay absolute
+    kda::LayerArgs a = make_args(desc, l.tab.n, 0);
+    a.qkv = static_cast<const char*>(qkv) + l.t0 * 3 * HD * io;
+    a.f = static_cast<const char*>(f) + l.t0 * HD * io;
+    a.beta = static_cast<const char*>(beta) + l.t0 * H * io;
+    a.g_out = static_cast<const char*>(g_out) + l.t0 * HD * io;
+    a.out = static_cast<char*>(out) + l.t0 * HD * ob;
+    a.state_in = state;
+    a.state_out = state;
+    a.conv_in = conv_state;
+    a.conv_out = desc->conv_width > 1 ? conv_state : nullptr;
+    a.snapshots = 0;
+    const hipError_t e = mfma ? kda::launch_prefill_mfma(a, l.tab, workspace, workspace_bytes, desc->out_dtype, s)
+                              : kda::launch_prefill_generic(a, l.tab, desc->chunk_size, desc->io_dtype,
+                                                            desc->out_dtype, s);
+    KDA_TRY(launched(e, "kda_prefill_varlen"));
+  }
+  return ok();
 }
 
 kda_status kda_decode_step(const kda_layer_desc* desc, int32_t B, const void* qkv, const void* f,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda_launch.h"
+
 namespace kda {
 
 // bf16 values travel as raw 16-bit patterns; fp32 as float.
@@ -48,6 +50,27 @@ template <int WIDTH>
 __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
   for (int off = WIDTH / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Sequence b of a prefill launch: first packed token, length, first chunk block, state slot.
+struct SeqView {
+  long long tok0;
+  int len, chunk0, slot;
+};
+__device__ __forceinline__ SeqView seq_view(const SeqTab& st, int b, int T, int NC) {
+  SeqView v;
+  if (st.n == 0) {
+    v.tok0 = (long long)b * T;
+    v.len = T;
+    v.chunk0 = b * NC;
+    v.slot = b;
+  } else {
+    v.tok0 = st.tok0[b];
+    v.len = st.tok0[b + 1] - st.tok0[b];
+    v.chunk0 = st.chunk0[b];
+    v.slot = st.slot[b];
+  }
   return v;
 }
 

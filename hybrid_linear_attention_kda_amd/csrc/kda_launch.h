@@ -10,6 +10,7 @@ namespace kda {
 
 constexpr int kMaxConvWidth = 8;       // conv taps supported (W - 1 <= 7 raw inputs of state)
 constexpr int kRollbackBatch = 256;    // sequences per rollback launch (accepted counts ride in the args)
+constexpr int kVarlenBatch = 128;      // sequences per variable-length prefill launch (their table rides in the args)
 
 enum IoType { kF32 = 0, kBF16 = 1 };
 
@@ -33,6 +34,17 @@ struct LayerArgs {
   int snapshots;        // 1: write the state after every token to state_out (verify)
   float* tape;          // verify with a replay tape: [B, T, H, 3, D] = (alpha, k, u) per token and
                         // head, written instead of any state (state_out unused); nullptr otherwise
+};
+
+// The sequences of one prefill launch.  n == 0: a.B sequences of a.T tokens each (sequence b at
+// packed tokens b*T.., chunk blocks b*NC.., state and conv-state slot b).  n > 0: the n sequences
+// of the table, each of length >= 1, packed along the token axis.
+struct SeqTab {
+  int n;
+  int total_chunks;                // sum over the table of ceil(len / 64) (the matrix-core path's chunks)
+  int tok0[kVarlenBatch + 1];      // first packed token of sequence i; tok0[n] = tokens of the launch
+  int chunk0[kVarlenBatch + 1];    // first chunk block of sequence i
+  int slot[kVarlenBatch];          // state / conv-state slot of sequence i
 };
 
 struct RollbackArgs {
@@ -63,11 +75,14 @@ hipError_t launch_rollback(const RollbackArgs& a, int io, hipStream_t s);
 hipError_t launch_commit_tape(const CommitArgs& a, int io, hipStream_t s);
 
 // Chunked prefill, fp32 VALU form (any supported head size; internal chunk <= 4096 / D).
-hipError_t launch_prefill_generic(const LayerArgs& a, int chunk, int io, int ot, hipStream_t s);
+hipError_t launch_prefill_generic(const LayerArgs& a, const SeqTab& st, int chunk, int io, int ot, hipStream_t s);
 
 // Chunked prefill on bf16 MFMA (D = 128, chunk 64, bf16 io, conv width <= 4, -5.5 <= lb <= 0).
+// Workspace: chunk blocks for `chunks` chunks of H heads, o for `tokens` tokens, a scratch slot.
+constexpr int kMfmaChunk = 64;
 bool prefill_mfma_supported(int D, int chunk, int io, int W, float lb);
-size_t prefill_mfma_workspace(int B, int T, int H, int D, int chunk);
-hipError_t launch_prefill_mfma(const LayerArgs& a, void* ws, size_t ws_bytes, int ot, hipStream_t s);
+size_t prefill_mfma_workspace(long long chunks, long long tokens, int H);
+hipError_t launch_prefill_mfma(const LayerArgs& a, const SeqTab& st, void* ws, size_t ws_bytes, int ot,
+                               hipStream_t s);
 
 }  // namespace kda

@@ -30,7 +30,7 @@ __host__ __device__ constexpr size_t generic_lds_floats(int D, int Cc) {
 }
 
 template <int D, typename IO, typename OT>
-__global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(LayerArgs a, int Cc) {
+__global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(LayerArgs a, SeqTab st, int Cc) {
   constexpr int NT = kGenericThreads;
   constexpr int NW = NT / 64;
   constexpr int LP = D + 1;
@@ -47,11 +47,14 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
   float* sgl = sbeta + Cc;          // [D]       Gam at the chunk's last token
   float* snrm = sgl + D;            // [2*Cc]    per-token q / k normalisers
 
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int h = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int H = a.H, W = a.W, T = a.T;
+  const SeqView sq0 = seq_view(st, blockIdx.y, a.T, 0);
+  const long long tok0 = sq0.tok0;  // packed token of the sequence's first token
+  const long long b = sq0.slot;     // state and conv-state slot
+  const int H = a.H, W = a.W, T = sq0.len;
   const long long Cqkv = 3LL * H * D;
-  const long long bh = (long long)b * H + h;
+  const long long bh = b * H + h;
   const IO* qkv = static_cast<const IO*>(a.qkv);
   const IO* fin = static_cast<const IO*>(a.f);
   const IO* bin = static_cast<const IO*>(a.beta);
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
       float y = 0.f;
       for (int w = 0; w < W; ++w) {
         const int tt = c0 + t - (W - 1) + w;
-        const float x = tt >= 0 ? to_f32(qkv[((long long)b * T + tt) * Cqkv + gc])
+        const float x = tt >= 0 ? to_f32(qkv[(tok0 + tt) * Cqkv + gc])
                                 : to_f32(cin[(b * Cqkv + gc) * (W - 1) + (W - 1) + tt]);
         y += to_f32(cw[gc * W + w]) * x;
       }
@@ -82,11 +85,11 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
     }
     for (int idx = tid; idx < L * D; idx += NT) {
       const int t = idx / D, i = idx % D;
-      const float fv = to_f32(fin[((long long)b * T + c0 + t) * H * D + (long long)h * D + i]) +
+      const float fv = to_f32(fin[(tok0 + c0 + t) * H * D + (long long)h * D + i]) +
                        a.dt_bias[(long long)h * D + i];
       sg[t * LP + i] = a.lb / (1.0f + expf(-Ah * fv));
     }
-    for (int t = tid; t < L; t += NT) sbeta[t] = to_f32(bin[((long long)b * T + c0 + t) * H + h]);
+    for (int t = tid; t < L; t += NT) sbeta[t] = to_f32(bin[(tok0 + c0 + t) * H + h]);
     __syncthreads();
     // -- q/k L2 normalisation (one wave per token), q scale
     for (int t = wave; t < L; t += NW) {
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
       for (int i = lane; i < D; i += 64) oo += sg[t * LP + i] * sg[t * LP + i];
       oo = wave_sum(oo);
       const float rr = rsqrtf(oo / (float)D + a.rms_eps);
-      const long long ob = ((long long)b * T + c0 + t) * H * D + (long long)h * D;
+      const long long ob = (tok0 + c0 + t) * H * D + (long long)h * D;
       for (int i = lane; i < D; i += 64) {
         const float gv = to_f32(gin[ob + i]);
         store_as(&out[ob + i], sg[t * LP + i] * rr * to_f32(nw[i]) / (1.0f + expf(-gv)));
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
       IO win[kMaxConvWidth - 1];
       for (int w = 0; w < W - 1; ++w) {
         const int tt = T - (W - 1) + w;
-        win[w] = tt >= 0 ? qkv[((long long)b * T + tt) * Cqkv + gc] : cin[(b * Cqkv + gc) * (W - 1) + (W - 1) + tt];
+        win[w] = tt >= 0 ? qkv[(tok0 + tt) * Cqkv + gc] : cin[(b * Cqkv + gc) * (W - 1) + (W - 1) + tt];
       }
       for (int w = 0; w < W - 1; ++w) cs[(b * Cqkv + gc) * (W - 1) + w] = win[w];
     }
@@ -211,32 +214,32 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
 }
 
 template <int D, typename IO, typename OT>
-static hipError_t launch_generic_t(const LayerArgs& a, int Cc, hipStream_t s) {
+static hipError_t launch_generic_t(const LayerArgs& a, const SeqTab& st, int Cc, hipStream_t s) {
   const size_t lds = generic_lds_floats(D, Cc) * sizeof(float);
   auto kern = kda_prefill_generic_kernel<D, IO, OT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   timing_begin("kda_prefill_generic_kernel", s);
-  kern<<<dim3(a.H, a.B), dim3(kGenericThreads), lds, s>>>(a, Cc);
+  kern<<<dim3(a.H, st.n > 0 ? st.n : a.B), dim3(kGenericThreads), lds, s>>>(a, st, Cc);
   timing_end(s);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_generic_d(const LayerArgs& a, int Cc, int io, int ot, hipStream_t s) {
+static hipError_t launch_generic_d(const LayerArgs& a, const SeqTab& st, int Cc, int io, int ot, hipStream_t s) {
   if (io == kBF16)
-    return ot == kBF16 ? launch_generic_t<D, bf16_t, bf16_t>(a, Cc, s) : launch_generic_t<D, bf16_t, float>(a, Cc, s);
-  return ot == kBF16 ? launch_generic_t<D, float, bf16_t>(a, Cc, s) : launch_generic_t<D, float, float>(a, Cc, s);
+    return ot == kBF16 ? launch_generic_t<D, bf16_t, bf16_t>(a, st, Cc, s) : launch_generic_t<D, bf16_t, float>(a, st, Cc, s);
+  return ot == kBF16 ? launch_generic_t<D, float, bf16_t>(a, st, Cc, s) : launch_generic_t<D, float, float>(a, st, Cc, s);
 }
 
-hipError_t launch_prefill_generic(const LayerArgs& a, int chunk, int io, int ot, hipStream_t s) {
+hipError_t launch_prefill_generic(const LayerArgs& a, const SeqTab& st, int chunk, int io, int ot, hipStream_t s) {
   const int Cc = generic_chunk(a.D, chunk);
   switch (a.D) {
-    case 16: return launch_generic_d<16>(a, Cc, io, ot, s);
-    case 32: return launch_generic_d<32>(a, Cc, io, ot, s);
-    case 64: return launch_generic_d<64>(a, Cc, io, ot, s);
-    case 128: return launch_generic_d<128>(a, Cc, io, ot, s);
+    case 16: return launch_generic_d<16>(a, st, Cc, io, ot, s);
+    case 32: return launch_generic_d<32>(a, st, Cc, io, ot, s);
+    case 64: return launch_generic_d<64>(a, st, Cc, io, ot, s);
+    case 128: return launch_generic_d<128>(a, st, Cc, io, ot, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -221,14 +221,28 @@ constexpr int NRV = (RROWS * 16 + NT - 1) / NT;   // raw v row loads per lane
 struct PrepTask {
   int h, b, ci;
 };
-// Tasks run head-fastest and chunk-major from the last chunk down, so that the tiles phase B
-// reads first were written last and are still in the last-level cache.
-__device__ __forceinline__ PrepTask prep_task(int task, int H, int NC) {
+// Tasks run head-fastest and, within a sequence, chunk-major from the last chunk down, so that
+// the tiles phase B reads first were written last and are still in the last-level cache.
+__device__ __forceinline__ PrepTask prep_task(int task, int H, int NC, const SeqTab& st) {
   PrepTask k;
   k.h = task % H;
   const int r = task / H;
-  k.ci = NC - 1 - r % NC;
-  k.b = r / NC;
+  if (st.n == 0) {
+    k.ci = NC - 1 - r % NC;
+    k.b = r / NC;
+  } else {
+    // the sequence holding chunk r: the last i with chunk0[i] <= r
+    int lo = 0, hi = st.n - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (st.chunk0[mid] <= r)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    k.b = lo;
+    k.ci = st.chunk0[lo + 1] - 1 - r;  // the sequence's chunks from its last one down
+  }
   return k;
 }
 
@@ -248,10 +262,12 @@ __device__ __forceinline__ int par_segments(int W) { return 48 * W + 32; }
 
 // The loads of one task, in three groups (0: q|k rows, 1: v rows, 2: the rest) that the kernel
 // issues at different points of the previous task, so that no phase carries all of them.
-__device__ __forceinline__ void prep_issue(const LayerArgs& a, const PrepTask& k, int tid, PrepIn& in, int part) {
-  const int H = a.H, T = a.T, W = a.W, HD = H * D, Cq = 3 * HD;
+__device__ __forceinline__ void prep_issue(const LayerArgs& a, const SeqTab& st, const PrepTask& k, int tid, PrepIn& in,
+                                           int part) {
+  const SeqView sv = seq_view(st, k.b, a.T, 0);
+  const int H = a.H, T = sv.len, W = a.W, HD = H * D, Cq = 3 * HD;
   const int h = k.h, c0 = k.ci * C;
-  const bf16_t* __restrict__ qkv = static_cast<const bf16_t*>(a.qkv) + (long long)k.b * T * Cq;
+  const bf16_t* __restrict__ qkv = static_cast<const bf16_t*>(a.qkv) + sv.tok0 * Cq;
   if (part == 0) {
 #pragma unroll
     for (int s = 0; s < NRAW; ++s) {
@@ -268,8 +284,8 @@ __device__ __forceinline__ void prep_issue(const LayerArgs& a, const PrepTask& k
       in.rawv[s] = *reinterpret_cast<const uint4*>(qkv + (long long)tt * Cq + 2LL * HD + h * D + sg * 8);
     }
   } else {
-    const bf16_t* __restrict__ fin = static_cast<const bf16_t*>(a.f) + (long long)k.b * T * HD + h * D;
-    const bf16_t* __restrict__ bin = static_cast<const bf16_t*>(a.beta) + (long long)k.b * T * H + h;
+    const bf16_t* __restrict__ fin = static_cast<const bf16_t*>(a.f) + sv.tok0 * HD + h * D;
+    const bf16_t* __restrict__ bin = static_cast<const bf16_t*>(a.beta) + sv.tok0 * H + h;
     const bf16_t* __restrict__ cw = static_cast<const bf16_t*>(a.conv_w);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -294,7 +310,7 @@ __device__ __forceinline__ void prep_issue(const LayerArgs& a, const PrepTask& k
   }
 }
 
-__global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigned char* __restrict__ ws) {
+__global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab st, unsigned char* __restrict__ ws) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* sQ = reinterpret_cast<float*>(smem + OFF_Q);
   __bf16* sKb = reinterpret_cast<__bf16*>(smem + OFF_KB);
@@ -316,17 +332,17 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
   float* sNrm = reinterpret_cast<float*>(smem + OFF_NRM);
   float* sSeg = reinterpret_cast<float*>(smem + OFF_SEG);
 
-  const int H = a.H, T = a.T, W = a.W;
-  const int NC = (T + C - 1) / C;
-  const int ntask = a.B * NC * H;
+  const int H = a.H, W = a.W;
+  const int NC = (a.T + C - 1) / C;  // chunks per sequence of a uniform launch
+  const int ntask = (st.n == 0 ? a.B * NC : st.total_chunks) * H;
   const int HD = H * D, Cq = 3 * HD;
 
   PrepIn cur;
   {
-    const PrepTask k0 = prep_task(min((int)blockIdx.x, ntask - 1), H, NC);
-    prep_issue(a, k0, (int)threadIdx.x, cur, 0);
-    prep_issue(a, k0, (int)threadIdx.x, cur, 1);
-    prep_issue(a, k0, (int)threadIdx.x, cur, 2);
+    const PrepTask k0 = prep_task(min((int)blockIdx.x, ntask - 1), H, NC, st);
+    prep_issue(a, st, k0, (int)threadIdx.x, cur, 0);
+    prep_issue(a, st, k0, (int)threadIdx.x, cur, 1);
+    prep_issue(a, st, k0, (int)threadIdx.x, cur, 2);
   }
   for (int tk = blockIdx.x; tk < ntask; tk += gridDim.x) {
     // lane indices are re-derived per task from an opaque copy, so that the address arithmetic
@@ -335,12 +351,16 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;  // MFMA row/column index and k-group
-    const PrepTask ktask = prep_task(tk, H, NC);
-    const int h = ktask.h, b = ktask.b, ci = ktask.ci;
+    const PrepTask ktask = prep_task(tk, H, NC, st);
+    const int h = ktask.h, ci = ktask.ci;
+    const SeqView sv = seq_view(st, ktask.b, a.T, NC);
+    const int T = sv.len;  // this sequence's tokens
     const int c0 = ci * C;
     const int L = min(C, T - c0);
-    const bf16_t* __restrict__ cin = static_cast<const bf16_t*>(a.conv_in) + (long long)b * Cq * (W - 1);
-    unsigned char* __restrict__ blk = ws + (((long long)b * H + h) * NC + ci) * (long long)CH_BYTES;
+    const bf16_t* __restrict__ cin = static_cast<const bf16_t*>(a.conv_in) + (long long)sv.slot * Cq * (W - 1);
+    // chunk blocks of a sequence: head-major, then chunk
+    unsigned char* __restrict__ blk =
+        ws + ((long long)sv.chunk0 * H + (long long)h * ((T + C - 1) / C) + ci) * (long long)CH_BYTES;
 
     // ---- P1: stage this task's raw q | k rows for tokens c0-3 .. c0+63, its gate inputs and
     //      its head's parameter block (bf16) from the registers loaded during the previous task ----
@@ -414,9 +434,9 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
 
     // the next task's inputs (the last task loads its own again: the loads stay unconditional),
     // issued in three groups spread over this task
-    const PrepTask knext = prep_task(min(tk + (int)gridDim.x, ntask - 1), H, NC);
+    const PrepTask knext = prep_task(min(tk + (int)gridDim.x, ntask - 1), H, NC, st);
     PrepIn nxt;
-    prep_issue(a, knext, tid, nxt, 0);
+    prep_issue(a, st, knext, tid, nxt, 0);
 
     // ---- P3: bounded-sigmoid gate and its cumulative sum (lane -> channel, 16-token segment);
     //      gl[k] = Gam(16 seg + k) - Gam(16 seg - 1) stays in registers for P5 ----
@@ -464,7 +484,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
     }
     __syncthreads();
 
-    prep_issue(a, knext, tid, nxt, 1);
+    prep_issue(a, st, knext, tid, nxt, 1);
 
     // ---- P5: anchored operands QR, KR (bf16), KC (lane -> channel, 16-token segment, as in P3:
     //      Gam_t - Gam_n(I) = gl[k] - gl[0]) and the per-channel factor tables ----
@@ -637,7 +657,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, unsigne
     }
     __syncthreads();
 
-    prep_issue(a, knext, tid, nxt, 2);
+    prep_issue(a, st, knext, tid, nxt, 2);
 
     // ---- P8: W = T . (beta KR e^Gam_n) (plain bf16); wave -> 16 key channels ----
     f32x4 wacc[4] = {zero4(), zero4(), zero4(), zero4()};
@@ -849,7 +869,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
 #define KDA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-__global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, const unsigned char* __restrict__ ws,
+__global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTab st, const unsigned char* __restrict__ ws,
                                                            float* __restrict__ ows) {
   extern __shared__ __align__(16) unsigned char smem[];
   __bf16* sUhi = reinterpret_cast<__bf16*>(smem + B_UHI);
@@ -857,17 +877,19 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, const
   __bf16* sShi = reinterpret_cast<__bf16*>(smem + B_SHI);
   __bf16* sSlo = reinterpret_cast<__bf16*>(smem + B_SLO);
 
-  const int H = a.H, T = a.T;
+  const int H = a.H;
   const int h = blockIdx.x % H;
   const int vb = blockIdx.x / H;
-  const int b = blockIdx.y;
+  const SeqView sv = seq_view(st, blockIdx.y, a.T, (a.T + C - 1) / C);
+  const int T = sv.len;  // this sequence's tokens (>= 1)
+  const long long tok0 = sv.tok0, slot = sv.slot;
   const int NC = (T + C - 1) / C;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: role branches are uniform
   const int l16 = lane & 15, lg = lane >> 4;
   const int HD = H * D;
-  const unsigned char* __restrict__ head_ws = ws + ((long long)b * H + h) * NC * (long long)CH_BYTES;
+  const unsigned char* __restrict__ head_ws = ws + ((long long)sv.chunk0 * H + (long long)h * NC) * CH_BYTES;
   auto wubuf = [&](int c) { return smem + B_WU0 + (c % 3) * WU_BYTES; };
   auto kbuf = [&](int c) { return smem + B_KB0 + (c & 1) * KB_BYTES; };
 
@@ -950,13 +972,13 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, const
       const int W = a.W, Cq = 3 * HD;
       const long long c = (long long)(j >> 4) * HD + h * D + vb * NVB + (j & 15);
       const bf16_t* x = static_cast<const bf16_t*>(a.qkv);
-      const bf16_t* cin = static_cast<const bf16_t*>(a.conv_in) + ((long long)b * Cq + c) * (W - 1);
-      bf16_t* cout = static_cast<bf16_t*>(a.conv_out) + ((long long)b * Cq + c) * (W - 1);
+      const bf16_t* cin = static_cast<const bf16_t*>(a.conv_in) + (slot * Cq + c) * (W - 1);
+      bf16_t* cout = static_cast<bf16_t*>(a.conv_out) + (slot * Cq + c) * (W - 1);
       bf16_t win[3];
 #pragma unroll
       for (int w = 0; w < 3; ++w) {
         const int tt = T - (W - 1) + w;
-        if (w < W - 1) win[w] = tt >= 0 ? x[((long long)b * T + tt) * Cq + c] : cin[(W - 1) + tt];
+        if (w < W - 1) win[w] = tt >= 0 ? x[(tok0 + tt) * Cq + c] : cin[(W - 1) + tt];
       }
 #pragma unroll
       for (int w = 0; w < 3; ++w)
@@ -968,8 +990,8 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, const
   // ---- state waves (0-3): wave w owns state row tiles w and w + 4 (channels 16t..16t+15); the
   //      lane holds rows 16t+4lg+r of column vb*16 + l16 ----
   f32x4 Sacc[2];
-  const float* s_in = a.state_in + ((long long)b * H + h) * D * D + vb * NVB + l16;
-  float* s_out = a.state_out + ((long long)b * H + h) * D * D + vb * NVB + l16;
+  const float* s_in = a.state_in + (slot * H + h) * D * D + vb * NVB + l16;
+  float* s_out = a.state_out + (slot * H + h) * D * D + vb * NVB + l16;
   // S^T as the split B operand [column][channel]; the lane's four rows are contiguous
   auto write_state_operand = [&]() {
 #pragma unroll
@@ -1068,7 +1090,7 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, const
     // the end of the sequence go to a scratch slot after o, so that every lane issues the same
     // stores; the last chunk's tiles are loaded again in place of chunks past the end.
     const int I = wave - 4;
-    float* scratch = ows + (long long)a.B * T * HD + lane * 4;
+    float* scratch = ows + (st.n == 0 ? (long long)a.B * a.T : (long long)st.tok0[st.n]) * HD + lane * 4;
     auto chunk_o = [&](int ci, OpTiles& cur) __attribute__((always_inline)) {
       lds_barrier();  // (a)
       f32x4 oa = zero4(), ob = zero4();
@@ -1085,7 +1107,7 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, const
       for (int r = 0; r < 4; ++r) o[r] = (oa[r] + ob[r]) + cur.y[r];
       lds_barrier();  // (b)
       const int c0 = ci * C, L = min(C, T - c0);
-      float* op = ows + (((long long)b * T + c0) * H + h) * D + vb * NVB + l16;
+      float* op = ows + ((tok0 + c0) * H + h) * D + vb * NVB + l16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * I + 4 * lg + r;
@@ -1151,8 +1173,6 @@ __global__ __launch_bounds__(256) void kda_out_norm_kernel(const float* __restri
   store8(out + row * D + c8, r);
 }
 
-// New conv state: the last W-1 raw inputs of (conv state || this call's tokens), per channel.
-
 }  // namespace
 
 // The anchored decay factors stay finite only for a bounded gate (15 |lb| < 87), and the
@@ -1161,15 +1181,17 @@ bool prefill_mfma_supported(int Dh, int chunk, int io, int W, float lb) {
   return Dh == D && chunk == C && io == kBF16 && W >= 1 && W <= HALO + 1 && lb <= 0.f && lb >= -5.5f;
 }
 
-size_t prefill_mfma_workspace(int B, int T, int H, int Dh, int) {
-  const size_t nc = (size_t)(T + C - 1) / C;
-  return (size_t)B * H * nc * CH_BYTES + (size_t)B * T * H * Dh * sizeof(float) + 64 * 4 * sizeof(float);
+size_t prefill_mfma_workspace(long long chunks, long long tokens, int H) {
+  return (size_t)chunks * H * CH_BYTES + (size_t)tokens * H * D * sizeof(float) + 64 * 4 * sizeof(float);
 }
 
-hipError_t launch_prefill_mfma(const LayerArgs& a, void* ws, size_t, int ot, hipStream_t s) {
+hipError_t launch_prefill_mfma(const LayerArgs& a, const SeqTab& st, void* ws, size_t, int ot, hipStream_t s) {
+  static_assert(C == kMfmaChunk, "chunk of the sequence tables");
   unsigned char* tiles = static_cast<unsigned char*>(ws);
   const int NC = (a.T + C - 1) / C;
-  float* ows = reinterpret_cast<float*>(tiles + (size_t)a.B * a.H * NC * CH_BYTES);
+  const long long chunks = st.n == 0 ? (long long)a.B * NC : st.total_chunks;
+  const long long tokens = st.n == 0 ? (long long)a.B * a.T : st.tok0[st.n];
+  float* ows = reinterpret_cast<float*>(tiles + (size_t)chunks * a.H * CH_BYTES);
   static const hipError_t attr_a = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_A);
   if (attr_a != hipSuccess) return attr_a;
@@ -1181,21 +1203,21 @@ hipError_t launch_prefill_mfma(const LayerArgs& a, void* ws, size_t, int ot, hip
       n = 256;
     return n;
   }();
-  const int ntask = a.B * NC * a.H;
+  const int ntask = (int)(chunks * a.H);
   timing_begin("kda_chunk_prep_kernel", s);
-  kda_chunk_prep_kernel<<<dim3(ntask < ncu ? ntask : ncu), NT, LDS_A, s>>>(a, tiles);
+  kda_chunk_prep_kernel<<<dim3(ntask < ncu ? ntask : ncu), NT, LDS_A, s>>>(a, st, tiles);
   timing_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   static const hipError_t attr_b = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_state_kernel),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_B);
   if (attr_b != hipSuccess) return attr_b;
-  const dim3 grid_b(NBLK * a.H, a.B);
+  const dim3 grid_b(NBLK * a.H, st.n == 0 ? a.B : st.n);
   timing_begin("kda_chunk_state_kernel", s);
-  kda_chunk_state_kernel<<<grid_b, NTB, LDS_B, s>>>(a, tiles, ows);
+  kda_chunk_state_kernel<<<grid_b, NTB, LDS_B, s>>>(a, st, tiles, ows);
   timing_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const long long rows = (long long)a.B * a.T * a.H;
+  const long long rows = tokens * a.H;
   const dim3 ng((unsigned)((rows + 15) / 16));
   timing_begin("kda_out_norm_kernel", s);
   if (ot == kBF16)

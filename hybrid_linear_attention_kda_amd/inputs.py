@@ -175,3 +175,28 @@ def select_heads(wl: Workload, inp: dict, heads) -> tuple:
     sub["state0"] = inp["state0"][:, heads]
     sub["conv_state0"] = inp["conv_state0"][:, ch]
     return wl.with_(H=len(heads)), sub
+
+
+def varlen_lengths(total: int, n: int, seed: int, zeros: int = 0) -> list:
+    """n sequence lengths summing to `total`, for packed variable-length calls: a seeded
+    log-normal mix (spread of about 4x between short and long sequences), `zeros` of them
+    empty, rounded so that the sum is exact."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    w = rng.lognormal(mean=0.0, sigma=0.7, size=n)
+    w[:zeros] = 0.0
+    rng.shuffle(w)
+    raw = w / w.sum() * total
+    lens = np.floor(raw).astype(np.int64)
+    rest = total - int(lens.sum())
+    order = np.argsort(-(raw - lens))
+    for i in order[:rest]:
+        lens[i] += 1
+    return [int(x) for x in lens]
+
+
+def cu_seqlens(lengths) -> list:
+    """Packed offsets [0, l0, l0+l1, ...] of a list of sequence lengths."""
+    out = [0]
+    for n in lengths:
+        out.append(out[-1] + int(n))
+    return out

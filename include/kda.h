@@ -117,6 +117,34 @@ kda_status kda_prefill(const kda_layer_desc* desc, int32_t B, int32_t T, const v
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Variable-length prefill: N sequences of different lengths packed along the
+ * token axis in one call, each continuing the state held in its own slot of a
+ * state pool (the serving shape of a hybrid memory with one recurrent-state
+ * cell per sequence, llama.cpp PR #27754, KDA commit: n_rs_seq).  Each
+ * sequence gives exactly what kda_prefill gives for it alone.
+ *   cu_seqlens_host [N+1] HOST int32: cu_seqlens[0] = 0, non-decreasing;
+ *                   sequence i owns packed tokens cu_seqlens[i] .. cu_seqlens[i+1]-1
+ *   slots_host      [N] HOST int32, distinct, in 0..num_slots-1: the state /
+ *                   conv-state slot of sequence i (NULL: slot i)
+ *   qkv   [total, 3*H*d], f [total, H*d], beta [total, H], g_out [total, H*d]
+ *         with total = cu_seqlens[N]                                 (in)
+ *   state      [num_slots, H, d, d] fp32                             (in/out)
+ *   conv_state [num_slots, 3*H*d, W-1]                               (in/out)
+ *   out        [total, H*d]                                          (out)
+ *   workspace  >= kda_prefill_varlen_workspace_size(desc, N, cu_seqlens_host)
+ *              bytes, 256-byte aligned (0 bytes for the fp32 path)
+ * Only the slots of sequences with at least one token are read or written;
+ * a sequence of length 0 is a no-op.  An invalid table (decreasing offsets,
+ * a slot out of range or used twice) fails before anything runs.
+ * kda_prefill_varlen_workspace_size returns (size_t)-1 for invalid arguments.
+ */
+size_t kda_prefill_varlen_workspace_size(const kda_layer_desc* desc, int32_t N, const int32_t* cu_seqlens_host);
+kda_status kda_prefill_varlen(const kda_layer_desc* desc, int32_t N, const int32_t* cu_seqlens_host,
+                              const int32_t* slots_host, int32_t num_slots, const void* qkv, const void* f,
+                              const void* beta, const void* g_out, float* state, void* conv_state, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One decode step: one new token per sequence, state and conv_state updated
  * in place.  Tensor shapes as kda_prefill with T = 1.
  */

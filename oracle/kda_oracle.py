@@ -485,3 +485,39 @@ def kda_commit_tape(p: KdaParams, accepted, tape, qkv_block, state, conv_state):
         xt = np.concatenate([conv_state[b].T, qkv_block[b, :m]], axis=0)
         conv_state[b] = xt[xt.shape[0] - (W - 1):].T
     return state, conv_state
+
+
+def kda_prefill_varlen(p: KdaParams, cu_seqlens, slots, qkv, f, beta, g_out, state, conv_state, *,
+                       form: str = "token", chunk: int = 64):
+    """Sequences of different lengths packed along the token axis, each
+    continuing the state held in its own slot of a state pool (the hybrid
+    memory keeps one recurrent-state cell per sequence: llama.cpp PR #27754,
+    KDA commit, n_rs_seq).  Sequence i is tokens cu_seqlens[i] ..
+    cu_seqlens[i+1]-1 and is exactly one kda_layer call on its own.
+
+    qkv [total, C_qkv], f [total, H*dk], beta [total, H], g_out [total, H*dv];
+    state [num_slots, H, dk, dv], conv_state [num_slots, C_qkv, W-1];
+    slots [N] distinct slot indices (None: slot i).  Slots not named, and the
+    slots of empty sequences, are returned unchanged.
+    Returns dict(out [total, H*dv], state, conv_state) as new float64 arrays.
+    """
+    cu = [int(c) for c in cu_seqlens]
+    N = len(cu) - 1
+    if N < 0 or cu[0] != 0 or any(cu[i + 1] < cu[i] for i in range(N)):
+        raise ValueError("cu_seqlens must start at 0 and not decrease")
+    state, conv_state = _f64(state).copy(), _f64(conv_state).copy()
+    slots = list(range(N)) if slots is None else [int(s) for s in slots]
+    if len(slots) != N or len(set(slots)) != N or any(s < 0 or s >= state.shape[0] for s in slots):
+        raise ValueError("slots must be N distinct indices into the state pool")
+    qkv, f, beta, g_out = (_f64(a) for a in (qkv, f, beta, g_out))
+    out = np.zeros((cu[-1], p.H * p.dv))
+    for i in range(N):
+        a, e, s = cu[i], cu[i + 1], slots[i]
+        if e == a:
+            continue
+        r = kda_layer(p, qkv[None, a:e], f[None, a:e], beta[None, a:e], g_out[None, a:e], state[None, s],
+                      conv_state[None, s], form=form, chunk=chunk)
+        out[a:e] = r["out"][0]
+        state[s] = r["state"][0]
+        conv_state[s] = r["conv_state"][0]
+    return {"out": out, "state": state, "conv_state": conv_state}

@@ -34,6 +34,7 @@ def test_library_exports_every_header_function():
     assert set(names) == {"kda_abi_version", "kda_status_string", "kda_last_error", "kda_prefill_workspace_size",
                           "kda_prefill", "kda_decode_step", "kda_verify_block", "kda_rollback",
                           "kda_verify_tape_size", "kda_verify_block_tape", "kda_commit_tape",
+                          "kda_prefill_varlen_workspace_size", "kda_prefill_varlen",
                           "kda_timing_enable", "kda_timing_read"}
     for n in names:
         assert hasattr(lib, n), n
@@ -121,6 +122,33 @@ def test_verify_tape_and_commit_validation():
     assert lib.kda_verify_tape_size(ctypes.byref(d), 4, 8) == 4 * 8 * d.num_heads * 3 * d.head_dim_k * 4
     bad = desc(gate_lower_bound=math.nan)
     assert lib.kda_verify_tape_size(ctypes.byref(bad), 4, 8) == ctypes.c_size_t(-1).value
+
+
+def test_varlen_validation_and_workspace_size():
+    lib = abi.load()
+    d = desc()
+    P = FAKE
+
+    def call(cu, slots=None, num_slots=4, ptr=P):
+        c = (ctypes.c_int32 * len(cu))(*cu)
+        sl = (ctypes.c_int32 * len(slots))(*slots) if slots is not None else None
+        return lib.kda_prefill_varlen(ctypes.byref(d), len(cu) - 1, ctypes.cast(c, ctypes.c_void_p),
+                                      ctypes.cast(sl, ctypes.c_void_p) if sl is not None else None, num_slots,
+                                      ptr, ptr, ptr, ptr, ptr, ptr, ptr, 0, 0, None)
+
+    assert lib.kda_prefill_varlen(ctypes.byref(d), 0, None, None, 1, 0, 0, 0, 0, 0, 0, 0, 0, 0, None) == abi.KDA_OK
+    assert call([0, 0, 0], ptr=0) == abi.KDA_OK  # every sequence empty: nothing runs, no pointer looked at
+    assert call([1, 3]) == abi.KDA_ERR_INVALID_ARGUMENT and b"cu_seqlens[0]" in lib.kda_last_error()
+    assert call([0, 4, 2]) == abi.KDA_ERR_INVALID_ARGUMENT and b"decreases" in lib.kda_last_error()
+    assert call([0, 2, 4], [1, 1]) == abi.KDA_ERR_INVALID_ARGUMENT and b"used by two" in lib.kda_last_error()
+    assert call([0, 2, 4], [0, 4]) == abi.KDA_ERR_INVALID_ARGUMENT and b"outside 0..3" in lib.kda_last_error()
+    assert call([0, 2, 4], num_slots=0) == abi.KDA_ERR_INVALID_ARGUMENT
+    assert call([0, 2, 4], ptr=0) == abi.KDA_ERR_INVALID_ARGUMENT  # non-empty: pointers are checked
+    c = (ctypes.c_int32 * 3)(0, 2, 4)
+    assert lib.kda_prefill_varlen_workspace_size(ctypes.byref(d), 2, ctypes.cast(c, ctypes.c_void_p)) == 0  # fp32 path
+    bad = (ctypes.c_int32 * 3)(0, 4, 2)
+    assert lib.kda_prefill_varlen_workspace_size(ctypes.byref(d), 2, ctypes.cast(bad, ctypes.c_void_p)) == \
+        ctypes.c_size_t(-1).value
 
 
 def test_workspace_size():

@@ -254,6 +254,95 @@ def test_bf16_prefill_four_heads(T):
     _check("out (bf16 output)", out16, ref["out"], TOL_BF16_OUT)
 
 
+# ---------------------------------------------------------------------------
+# Variable-length prefill over a state pool (every element)
+# ---------------------------------------------------------------------------
+
+def _varlen_case(wl, lens, slots, num_slots, seed, out_dtype=torch.float32):
+    """Run kda_prefill_varlen on a packed batch and the oracle per sequence; returns both."""
+    total = sum(lens)
+    cu = I.cu_seqlens(lens)
+    inp = I.generate(wl.with_(B=1, T=total))
+    rng = np.random.default_rng(seed)
+    pool = (rng.standard_normal((num_slots, wl.H, wl.dk, wl.dv)) * 0.3).astype(np.float32)
+    cpool = I.round_to_io(rng.standard_normal((num_slots, wl.c_qkv, wl.W - 1)), wl.io)
+    layer = TT.make_layer(wl, inp, DEV, out="bf16" if out_dtype == torch.bfloat16 else "f32")
+    st = torch.from_numpy(pool).to(DEV)
+    cs = TT.to_device(cpool, wl.io, DEV)
+    tok = {k: v[0] for k, v in TT.token_tensors(wl, inp, 0, total, DEV).items()}
+    out = torch.empty((total, wl.H * wl.dv), dtype=out_dtype, device=DEV)
+    n = abi.kda_prefill_varlen_workspace_size(layer, cu)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV) if n else None
+    abi.kda_prefill_varlen(layer, cu, slots, tok["qkv"], tok["f"], tok["beta"], tok["g_out"], st, cs, out,
+                           workspace=ws)
+    torch.cuda.synchronize()
+    pk = {k: inp[k][0] for k in ("qkv", "f", "beta", "g_out")}
+    ref = O.kda_prefill_varlen(pu.params(wl, inp), cu, slots, pk["qkv"], pk["f"], pk["beta"], pk["g_out"],
+                               pool, cpool)
+    return out, st, cs, ref, pool, cpool
+
+
+def test_bf16_varlen_prefill_mixed_lengths_and_slots():
+    # ragged lengths (empty, one token, exactly one chunk, partial chunks, several chunks), a slot
+    # permutation and a pool slot no sequence names
+    wl = I.WORKLOADS["prefill_t4096"].with_(H=4, seed=21)
+    lens = [0, 1, 64, 100, 257, 3]
+    slots = [2, 5, 0, 3, 1, 4]
+    say(f"case bf16 varlen H=4 lengths {lens} slots {slots} (pool of 7)")
+    out, st, cs, ref, pool, cpool = _varlen_case(wl, lens, slots, 7, seed=5)
+    _check("out", out, ref["out"], TOL["bf16"])
+    _check("state pool", st, ref["state"], TOL["bf16"])
+    _check("conv-state pool", cs, ref["conv_state"], 0.0)
+    _check("unnamed slot and empty sequence's slot untouched", st[[6, 2]], pool[[6, 2]], 0.0)
+
+
+def test_bf16_varlen_equals_batched_prefill():
+    # equal lengths: the packed call is bit-identical to kda_prefill on B sequences
+    wl = I.WORKLOADS["prefill_t4096"].with_(H=4, B=3, T=150, seed=22)
+    say("case bf16 varlen 3 x 150 tokens vs batched prefill")
+    inp = I.generate(wl)
+    rng = np.random.default_rng(9)
+    S0 = (rng.standard_normal(inp["state0"].shape) * 0.3).astype(np.float32)
+    C0 = I.round_to_io(rng.standard_normal(inp["conv_state0"].shape), "bf16")
+    layer = TT.make_layer(wl, inp, DEV)
+    st1, cs1 = _dev_state(wl, inp, S0, C0)
+    out1 = _gpu_prefill(wl, inp, layer, 0, 150, st1, cs1)
+    st2, cs2 = _dev_state(wl, inp, S0, C0)
+    tok = TT.token_tensors(wl, inp, 0, 150, DEV)
+    out2 = torch.empty((450, wl.H * wl.dv), dtype=torch.float32, device=DEV)
+    cu = [0, 150, 300, 450]
+    ws = torch.empty(abi.kda_prefill_varlen_workspace_size(layer, cu), dtype=torch.uint8, device=DEV)
+    abi.kda_prefill_varlen(layer, cu, None, tok["qkv"].reshape(450, -1), tok["f"].reshape(450, -1),
+                           tok["beta"].reshape(450, -1), tok["g_out"].reshape(450, -1), st2, cs2, out2, workspace=ws)
+    torch.cuda.synchronize()
+    _bit_equal("out", out2, out1.reshape(450, -1))
+    _bit_equal("state", st2, st1)
+    _bit_equal("conv state", cs2, cs1)
+
+
+def test_bf16_varlen_more_sequences_than_one_launch_holds():
+    # 150 short sequences (over the 128 of one launch's table), two heads
+    wl = I.WORKLOADS["prefill_t4096"].with_(H=2, seed=23)
+    rng = np.random.default_rng(3)
+    lens = [int(x) for x in rng.integers(0, 6, size=150)]
+    slots = [int(x) for x in rng.permutation(160)[:150]]
+    say(f"case bf16 varlen 150 sequences, {sum(lens)} tokens, pool of 160")
+    out, st, cs, ref, pool, cpool = _varlen_case(wl, lens, slots, 160, seed=6)
+    _check("out", out, ref["out"], TOL["bf16"])
+    _check("state pool", st, ref["state"], TOL["bf16"])
+    _check("conv-state pool", cs, ref["conv_state"], 0.0)
+
+
+def test_tiny_fp32_varlen_prefill():
+    wl = I.WORKLOADS["tiny_fp32"]
+    lens = [5, 0, 17, 64, 1]
+    say(f"case fp32 varlen H=2 d=16 lengths {lens}")
+    out, st, cs, ref, pool, cpool = _varlen_case(wl, lens, [4, 0, 1, 3, 2], 6, seed=7)
+    _check("out", out, ref["out"], TOL["f32"])
+    _check("state pool", st, ref["state"], TOL["f32"])
+    _check("conv-state pool", cs, ref["conv_state"], 0.0)
+
+
 @pytest.mark.parametrize("T", [100, 33])
 def test_fp32_prefill_head_size_128(T):
     # fp32 io at d = 128 runs the vector-ALU chunked prefill (internal chunk 32)

@@ -453,6 +453,60 @@ def test_commit_tape_rejects_out_of_range():
         O.kda_commit_tape(p, [9], tape, inp["qkv"], inp["state0"], inp["conv_state0"])
 
 
+def _packed(inp, B, T):
+    return {k: inp[k].reshape(B * T, -1) for k in ("qkv", "f", "beta", "g_out")}
+
+
+def test_varlen_equal_lengths_equals_batched_layer():
+    wl, inp, p = _tiny(12, B=3)
+    S0 = RNG.standard_normal((3, wl.H, wl.dk, wl.dv))
+    cs0 = RNG.standard_normal(inp["conv_state0"].shape)
+    full = O.kda_layer(p, inp["qkv"], inp["f"], inp["beta"], inp["g_out"], S0, cs0)
+    pk = _packed(inp, 3, 12)
+    v = O.kda_prefill_varlen(p, [0, 12, 24, 36], None, pk["qkv"], pk["f"], pk["beta"], pk["g_out"], S0, cs0)
+    np.testing.assert_array_equal(v["out"], full["out"].reshape(36, -1))
+    np.testing.assert_array_equal(v["state"], full["state"])
+    np.testing.assert_array_equal(v["conv_state"], full["conv_state"])
+
+
+def test_varlen_sequences_are_independent_of_order_and_slots():
+    # each sequence is one call on its own slot: permuting the packing and the slot assignment
+    # moves results around and changes nothing else; empty sequences and unnamed slots are untouched
+    wl, inp, p = _tiny(30, B=1)
+    pool = RNG.standard_normal((5, wl.H, wl.dk, wl.dv))
+    cpool = RNG.standard_normal((5, wl.c_qkv, wl.W - 1))
+    pk = _packed(inp, 1, 30)
+    lens = [7, 0, 16, 7]
+    cu = I.cu_seqlens(lens)
+    v1 = O.kda_prefill_varlen(p, cu, [3, 1, 0, 4], pk["qkv"], pk["f"], pk["beta"], pk["g_out"], pool, cpool)
+    np.testing.assert_array_equal(v1["state"][[1, 2]], pool[[1, 2]])
+    np.testing.assert_array_equal(v1["conv_state"][[1, 2]], cpool[[1, 2]])
+    # sequence 2 (tokens 7..22, slot 0) alone, as a plain layer call
+    r = O.kda_layer(p, inp["qkv"][:, 7:23], inp["f"][:, 7:23], inp["beta"][:, 7:23], inp["g_out"][:, 7:23],
+                    pool[None, 0], cpool[None, 0])
+    np.testing.assert_array_equal(v1["out"][7:23], r["out"][0])
+    np.testing.assert_array_equal(v1["state"][0], r["state"][0])
+    # reversed packing order with the same slots per sequence
+    order = [3, 2, 1, 0]
+    idx = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in order])
+    cu2 = I.cu_seqlens([lens[i] for i in order])
+    v2 = O.kda_prefill_varlen(p, cu2, [[3, 1, 0, 4][i] for i in order], pk["qkv"][idx], pk["f"][idx],
+                              pk["beta"][idx], pk["g_out"][idx], pool, cpool)
+    np.testing.assert_array_equal(v2["out"], v1["out"][idx])
+    np.testing.assert_array_equal(v2["state"], v1["state"])
+    np.testing.assert_array_equal(v2["conv_state"], v1["conv_state"])
+
+
+@pytest.mark.parametrize("cu,slots", [([1, 3], None), ([0, 4, 2], None), ([0, 2, 4], [0, 0]), ([0, 2, 4], [0, 9])])
+def test_varlen_rejects_bad_tables(cu, slots):
+    wl, inp, p = _tiny(4, B=1)
+    pk = _packed(inp, 1, 4)
+    pool = np.zeros((3, wl.H, wl.dk, wl.dv))
+    with pytest.raises(ValueError):
+        O.kda_prefill_varlen(p, cu, slots, pk["qkv"], pk["f"], pk["beta"], pk["g_out"], pool,
+                             np.zeros((3, wl.c_qkv, wl.W - 1)))
+
+
 def test_missing_gate_lower_bound_is_an_error():
     wl, inp, p = _tiny(4)
     p.lb = float("nan")
