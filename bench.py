@@ -2,6 +2,8 @@
 
 One step = one pass over every call of the path on its layer-shaped workload:
   prefill   B=1, T=4096, H=32, d_k=d_v=128, chunk 64, bf16 io, fp32 state
+  varlen    the same 4096 tokens as 16 packed sequences of a seeded length mix
+            (123..628 tokens), each from its own zero state slot
   decode    64 sequences x 32 heads x 128x128 fp32 state, one token each
   verify    16 sequences x 8 draft tokens with per-token snapshots, then rollback
             to a seeded accepted prefix (0..8) per sequence; and the same block
@@ -74,6 +76,10 @@ def commit_bytes(accepted, H, D, W, io_b=2):
     return rollback_bytes(accepted, H, D, W, io_b) + sum(int(m) for m in accepted) * H * 3 * D * 4
 
 
+VARLEN_SEQS = 16
+VARLEN_SEED = 8
+
+
 def kernel_alg_bytes(kernel, wp, wd, wv, accepted):
     """Algorithmic bytes of one launch of each kernel: what the launch must read and write once,
     with the prefill call's bytes split over its four kernels (their sum is prefill_bytes)."""
@@ -88,6 +94,11 @@ def kernel_alg_bytes(kernel, wp, wd, wv, accepted):
         "kda_chunk_state_kernel": 2 * Hp * Dp * Dp * 4 + conv,
         # g_out in, out written, norm weight
         "kda_out_norm_kernel": Tp * 2 * Hp * Dp * io_b + Dp * io_b,
+        # the variable-length call: the same tokens, a state and conv state per sequence
+        "kda_chunk_prep_kernel[varlen]": Tp * (3 * Hp * Dp * io_b + Hp * Dp * io_b + Hp * io_b)
+                                         + VARLEN_SEQS * conv + params,
+        "kda_chunk_state_kernel[varlen]": VARLEN_SEQS * (2 * Hp * Dp * Dp * 4 + conv),
+        "kda_out_norm_kernel[varlen]": Tp * 2 * Hp * Dp * io_b + Dp * io_b,
         "kda_recurrent_kernel[decode]": decode_bytes(wd.B, wd.H, wd.dk, wd.W),
         "kda_recurrent_kernel[verify]": verify_bytes(wv.B, wv.T, wv.H, wv.dk, wv.W),
         "kda_rollback_kernel": rollback_bytes(accepted or [], wv.H, wv.dk, wv.W),
@@ -134,6 +145,8 @@ def short_kernel_name(full):
     if m is None:
         return None
     name = m.group(1)
+    if name in ("kda_chunk_prep_kernel", "kda_chunk_state_kernel") and m.group(2) == "<true>":
+        name += "[varlen]"
     if name == "kda_recurrent_kernel" and m.group(2):
         targs = m.group(2)
         name += "[verify_tape]" if ", true, true," in targs else "[verify]" if ", true," in targs else "[decode]"
@@ -210,7 +223,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sets", type=int, default=4)
-    ap.add_argument("--only", choices=["prefill", "decode", "verify"], default=None,
+    ap.add_argument("--only", choices=["prefill", "varlen", "decode", "verify"], default=None,
                     help="time one call type only (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
@@ -241,7 +254,7 @@ def main():
     nsets = max(1, args.sets)
 
     wp, wd, wv = I.WORKLOADS["prefill_t4096"], I.WORKLOADS["decode_b64"], I.WORKLOADS["verify_b16"]
-    ops = ["prefill", "decode", "verify"] if args.only is None else [args.only]
+    ops = ["prefill", "varlen", "decode", "verify"] if args.only is None else [args.only]
 
     def workspace(layer, B, T):
         n = abi.kda_prefill_workspace_size(layer, B, T)
@@ -260,6 +273,22 @@ def main():
                 conv=torch.zeros((1, wp.c_qkv, wp.W - 1), dtype=torch.bfloat16, device=dev),
                 out=torch.empty((1, wp.T, wp.H * wp.dv), dtype=torch.bfloat16, device=dev),
                 ws=workspace(lay, 1, wp.T)))
+        del tok
+    # --- variable-length sets: the prefill tokens as packed sequences of a seeded length mix
+    var_lens = I.varlen_lengths(wp.T, VARLEN_SEQS, VARLEN_SEED)
+    var_cu = I.cu_seqlens(var_lens)
+    if "varlen" in ops:
+        inp = I.generate(wp)
+        lay = TT.make_layer(wp, inp, dev, out="bf16")
+        tok = TT.token_tensors(wp, inp, 0, wp.T, dev)
+        nvs = abi.kda_prefill_varlen_workspace_size(lay, var_cu)
+        for _ in range(nsets):
+            sets["varlen"].append(dict(
+                layer=lay, tok={k: v[0].clone() for k, v in tok.items()},
+                state=torch.zeros((VARLEN_SEQS, wp.H, wp.dk, wp.dv), dtype=torch.float32, device=dev),
+                conv=torch.zeros((VARLEN_SEQS, wp.c_qkv, wp.W - 1), dtype=torch.bfloat16, device=dev),
+                out=torch.empty((wp.T, wp.H * wp.dv), dtype=torch.bfloat16, device=dev),
+                ws=torch.empty(nvs, dtype=torch.uint8, device=dev)))
         del tok
 
     def prefilled(wl, inp):
@@ -307,6 +336,9 @@ def main():
         if op == "prefill":
             abi.kda_prefill(s["layer"], t["qkv"], t["f"], t["beta"], t["g_out"], s["state"], s["conv"], s["out"],
                             workspace=s["ws"], stream=stream)
+        elif op == "varlen":
+            abi.kda_prefill_varlen(s["layer"], var_cu, None, t["qkv"], t["f"], t["beta"], t["g_out"], s["state"],
+                                   s["conv"], s["out"], workspace=s["ws"], stream=stream)
         elif op == "decode":
             abi.kda_decode_step(s["layer"], t["qkv"], t["f"], t["beta"], t["g_out"], s["state"], s["conv"],
                                 s["out"], stream=stream)
@@ -341,7 +373,6 @@ def main():
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    abi.timing_enable(True)  # an event pair around every kernel of the timed steps
     wall0 = time.perf_counter()
     t_start.record(stream)
     for op in seq:
@@ -353,6 +384,13 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    # the same K steps again with an event pair around every kernel (the library's timing hook),
+    # for the per-kernel durations; kept out of the timed steps above so its events add no gaps
+    abi.timing_enable(True)
+    for op in seq:
+        for i in range(K):
+            run(op, sets[setof(op)][i % nsets])
+    torch.cuda.synchronize()
     abi.timing_enable(False)
     kernel_ms = {}
     for name, t in abi.timing_read():
@@ -371,8 +409,9 @@ def main():
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_total / K,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "prefill_t4096 (B=1,T=4096,H=32,d=128,chunk 64) + decode_b64 (B=64,H=32,d=128) + "
-                               "verify_b16 (B=16,T_d=8,H=32,d=128) with rollback",
+        "config": {"workload": "prefill_t4096 (B=1,T=4096,H=32,d=128,chunk 64) + the same tokens as 16 packed "
+                               "sequences + decode_b64 (B=64,H=32,d=128) + verify_b16 (B=16,T_d=8,H=32,d=128) "
+                               "with rollback and with the replay tape",
                    "io": "bf16 inputs and outputs, fp32 state and accumulation", "buffer_sets": nsets},
         "wall_s": wall,
     }
@@ -383,6 +422,14 @@ def main():
         res["unit"] = "tokens/s"
         detail["prefill"] = {"ms_mean": mean["prefill"], "tokens_per_s": res["value"], "alg_bytes": pb,
                              "gbps": pb / (mean["prefill"] * 1e-3) / 1e9}
+    if "varlen" in ops:
+        vb_ = sum(kernel_alg_bytes(k, wp, wd, wv, accepted) for k in
+                  ("kda_chunk_prep_kernel[varlen]", "kda_chunk_state_kernel[varlen]", "kda_out_norm_kernel[varlen]"))
+        detail["prefill_varlen"] = {"ms_mean": mean["varlen"], "tokens_per_s": wp.T / (mean["varlen"] * 1e-3),
+                                    "alg_bytes": vb_, "gbps": vb_ / (mean["varlen"] * 1e-3) / 1e9,
+                                    "sequences": VARLEN_SEQS, "lengths": var_lens}
+        if "value" not in res:
+            res["value"], res["unit"] = wp.T / (mean["varlen"] * 1e-3), "tokens/s"
     if "decode" in ops:
         db = decode_bytes(wd.B, wd.H, wd.dk, wd.W)
         gb = db / (mean["decode"] * 1e-3) / 1e9
@@ -409,7 +456,7 @@ def main():
                                           "tape_verify_plus_commit": mean["verify_tape"] + mean["commit"]}
         if "value" not in res:
             res["value"], res["unit"] = gv, "GB/s"
-    # per kernel: average launch duration from the library's event pairs over the timed steps
+    # per kernel: average launch duration from the library's event pairs over the second pass
     kern = {}
     for name, ts in kernel_ms.items():
         avg = float(np.mean(ts))
@@ -419,8 +466,10 @@ def main():
                       "gbps": (nb / (avg * 1e-3) / 1e9) if nb else None}
     detail["kernels"] = kern
     res["detail"] = detail
-    # dominant kernel: the largest share of the step
-    name = max(kern, key=lambda n: kern[n]["ms_mean"] * kern[n]["launches_per_step"])
+    # dominant kernel: the largest share of the step among the headline workloads' kernels (the
+    # variable-length line runs the same kernels on another table and is reported beside them)
+    name = max((n for n in kern if not n.endswith("[varlen]")),
+               key=lambda n: kern[n]["ms_mean"] * kern[n]["launches_per_step"])
     k = kern[name]
     achieved = k["gbps"]
     res["roofline"] = {"kernel": name, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,

@@ -58,9 +58,11 @@ struct SeqView {
   long long tok0;
   int len, chunk0, slot;
 };
+// TABLE: the launch carries a sequence table (st.n >= 1); otherwise the uniform layout.
+template <bool TABLE>
 __device__ __forceinline__ SeqView seq_view(const SeqTab& st, int b, int T, int NC) {
   SeqView v;
-  if (st.n == 0) {
+  if (!TABLE) {
     v.tok0 = (long long)b * T;
     v.len = T;
     v.chunk0 = b * NC;

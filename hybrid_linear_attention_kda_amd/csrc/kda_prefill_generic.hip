@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
 
   const int h = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const SeqView sq0 = seq_view(st, blockIdx.y, a.T, 0);
+  const SeqView sq0 = st.n > 0 ? seq_view<true>(st, blockIdx.y, a.T, 0) : seq_view<false>(st, blockIdx.y, a.T, 0);
   const long long tok0 = sq0.tok0;  // packed token of the sequence's first token
   const long long b = sq0.slot;     // state and conv-state slot
   const int H = a.H, W = a.W, T = sq0.len;

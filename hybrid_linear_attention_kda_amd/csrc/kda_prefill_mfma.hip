@@ -223,11 +223,12 @@ struct PrepTask {
 };
 // Tasks run head-fastest and, within a sequence, chunk-major from the last chunk down, so that
 // the tiles phase B reads first were written last and are still in the last-level cache.
+template <bool VL>
 __device__ __forceinline__ PrepTask prep_task(int task, int H, int NC, const SeqTab& st) {
   PrepTask k;
   k.h = task % H;
   const int r = task / H;
-  if (st.n == 0) {
+  if (!VL) {
     k.ci = NC - 1 - r % NC;
     k.b = r / NC;
   } else {
@@ -262,9 +263,10 @@ __device__ __forceinline__ int par_segments(int W) { return 48 * W + 32; }
 
 // The loads of one task, in three groups (0: q|k rows, 1: v rows, 2: the rest) that the kernel
 // issues at different points of the previous task, so that no phase carries all of them.
+template <bool VL>
 __device__ __forceinline__ void prep_issue(const LayerArgs& a, const SeqTab& st, const PrepTask& k, int tid, PrepIn& in,
                                            int part) {
-  const SeqView sv = seq_view(st, k.b, a.T, 0);
+  const SeqView sv = seq_view<VL>(st, k.b, a.T, 0);
   const int H = a.H, T = sv.len, W = a.W, HD = H * D, Cq = 3 * HD;
   const int h = k.h, c0 = k.ci * C;
   const bf16_t* __restrict__ qkv = static_cast<const bf16_t*>(a.qkv) + sv.tok0 * Cq;
@@ -310,6 +312,8 @@ __device__ __forceinline__ void prep_issue(const LayerArgs& a, const SeqTab& st,
   }
 }
 
+// VL: the launch carries a sequence table (variable-length call); otherwise a.B sequences of a.T.
+template <bool VL>
 __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab st, unsigned char* __restrict__ ws) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* sQ = reinterpret_cast<float*>(smem + OFF_Q);
@@ -334,15 +338,15 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 
   const int H = a.H, W = a.W;
   const int NC = (a.T + C - 1) / C;  // chunks per sequence of a uniform launch
-  const int ntask = (st.n == 0 ? a.B * NC : st.total_chunks) * H;
+  const int ntask = (VL ? st.total_chunks : a.B * NC) * H;
   const int HD = H * D, Cq = 3 * HD;
 
   PrepIn cur;
   {
-    const PrepTask k0 = prep_task(min((int)blockIdx.x, ntask - 1), H, NC, st);
-    prep_issue(a, st, k0, (int)threadIdx.x, cur, 0);
-    prep_issue(a, st, k0, (int)threadIdx.x, cur, 1);
-    prep_issue(a, st, k0, (int)threadIdx.x, cur, 2);
+    const PrepTask k0 = prep_task<VL>(min((int)blockIdx.x, ntask - 1), H, NC, st);
+    prep_issue<VL>(a, st, k0, (int)threadIdx.x, cur, 0);
+    prep_issue<VL>(a, st, k0, (int)threadIdx.x, cur, 1);
+    prep_issue<VL>(a, st, k0, (int)threadIdx.x, cur, 2);
   }
   for (int tk = blockIdx.x; tk < ntask; tk += gridDim.x) {
     // lane indices are re-derived per task from an opaque copy, so that the address arithmetic
@@ -351,9 +355,9 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;  // MFMA row/column index and k-group
-    const PrepTask ktask = prep_task(tk, H, NC, st);
+    const PrepTask ktask = prep_task<VL>(tk, H, NC, st);
     const int h = ktask.h, ci = ktask.ci;
-    const SeqView sv = seq_view(st, ktask.b, a.T, NC);
+    const SeqView sv = seq_view<VL>(st, ktask.b, a.T, NC);
     const int T = sv.len;  // this sequence's tokens
     const int c0 = ci * C;
     const int L = min(C, T - c0);
@@ -434,9 +438,9 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 
     // the next task's inputs (the last task loads its own again: the loads stay unconditional),
     // issued in three groups spread over this task
-    const PrepTask knext = prep_task(min(tk + (int)gridDim.x, ntask - 1), H, NC, st);
+    const PrepTask knext = prep_task<VL>(min(tk + (int)gridDim.x, ntask - 1), H, NC, st);
     PrepIn nxt;
-    prep_issue(a, st, knext, tid, nxt, 0);
+    prep_issue<VL>(a, st, knext, tid, nxt, 0);
 
     // ---- P3: bounded-sigmoid gate and its cumulative sum (lane -> channel, 16-token segment);
     //      gl[k] = Gam(16 seg + k) - Gam(16 seg - 1) stays in registers for P5 ----
@@ -484,7 +488,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     }
     __syncthreads();
 
-    prep_issue(a, st, knext, tid, nxt, 1);
+    prep_issue<VL>(a, st, knext, tid, nxt, 1);
 
     // ---- P5: anchored operands QR, KR (bf16), KC (lane -> channel, 16-token segment, as in P3:
     //      Gam_t - Gam_n(I) = gl[k] - gl[0]) and the per-channel factor tables ----
@@ -657,7 +661,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     }
     __syncthreads();
 
-    prep_issue(a, st, knext, tid, nxt, 2);
+    prep_issue<VL>(a, st, knext, tid, nxt, 2);
 
     // ---- P8: W = T . (beta KR e^Gam_n) (plain bf16); wave -> 16 key channels ----
     f32x4 wacc[4] = {zero4(), zero4(), zero4(), zero4()};
@@ -869,6 +873,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
 #define KDA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
+template <bool VL>
 __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTab st, const unsigned char* __restrict__ ws,
                                                            float* __restrict__ ows) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -880,7 +885,7 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
   const int H = a.H;
   const int h = blockIdx.x % H;
   const int vb = blockIdx.x / H;
-  const SeqView sv = seq_view(st, blockIdx.y, a.T, (a.T + C - 1) / C);
+  const SeqView sv = seq_view<VL>(st, blockIdx.y, a.T, (a.T + C - 1) / C);
   const int T = sv.len;  // this sequence's tokens (>= 1)
   const long long tok0 = sv.tok0, slot = sv.slot;
   const int NC = (T + C - 1) / C;
@@ -1090,7 +1095,7 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
     // the end of the sequence go to a scratch slot after o, so that every lane issues the same
     // stores; the last chunk's tiles are loaded again in place of chunks past the end.
     const int I = wave - 4;
-    float* scratch = ows + (st.n == 0 ? (long long)a.B * a.T : (long long)st.tok0[st.n]) * HD + lane * 4;
+    float* scratch = ows + (VL ? (long long)st.tok0[st.n] : (long long)a.B * a.T) * HD + lane * 4;
     auto chunk_o = [&](int ci, OpTiles& cur) __attribute__((always_inline)) {
       lds_barrier();  // (a)
       f32x4 oa = zero4(), ob = zero4();
@@ -1185,14 +1190,14 @@ size_t prefill_mfma_workspace(long long chunks, long long tokens, int H) {
   return (size_t)chunks * H * CH_BYTES + (size_t)tokens * H * D * sizeof(float) + 64 * 4 * sizeof(float);
 }
 
-hipError_t launch_prefill_mfma(const LayerArgs& a, const SeqTab& st, void* ws, size_t, int ot, hipStream_t s) {
-  static_assert(C == kMfmaChunk, "chunk of the sequence tables");
+template <bool VL>
+static hipError_t launch_mfma_t(const LayerArgs& a, const SeqTab& st, void* ws, int ot, hipStream_t s) {
   unsigned char* tiles = static_cast<unsigned char*>(ws);
   const int NC = (a.T + C - 1) / C;
-  const long long chunks = st.n == 0 ? (long long)a.B * NC : st.total_chunks;
-  const long long tokens = st.n == 0 ? (long long)a.B * a.T : st.tok0[st.n];
+  const long long chunks = VL ? st.total_chunks : (long long)a.B * NC;
+  const long long tokens = VL ? st.tok0[st.n] : (long long)a.B * a.T;
   float* ows = reinterpret_cast<float*>(tiles + (size_t)chunks * a.H * CH_BYTES);
-  static const hipError_t attr_a = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel),
+  static const hipError_t attr_a = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_A);
   if (attr_a != hipSuccess) return attr_a;
   // persistent: one workgroup per CU (the LDS use admits one), each looping over tasks
@@ -1204,22 +1209,22 @@ hipError_t launch_prefill_mfma(const LayerArgs& a, const SeqTab& st, void* ws, s
     return n;
   }();
   const int ntask = (int)(chunks * a.H);
-  timing_begin("kda_chunk_prep_kernel", s);
-  kda_chunk_prep_kernel<<<dim3(ntask < ncu ? ntask : ncu), NT, LDS_A, s>>>(a, st, tiles);
+  timing_begin(VL ? "kda_chunk_prep_kernel[varlen]" : "kda_chunk_prep_kernel", s);
+  kda_chunk_prep_kernel<VL><<<dim3(ntask < ncu ? ntask : ncu), NT, LDS_A, s>>>(a, st, tiles);
   timing_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  static const hipError_t attr_b = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_state_kernel),
+  static const hipError_t attr_b = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_state_kernel<VL>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_B);
   if (attr_b != hipSuccess) return attr_b;
-  const dim3 grid_b(NBLK * a.H, st.n == 0 ? a.B : st.n);
-  timing_begin("kda_chunk_state_kernel", s);
-  kda_chunk_state_kernel<<<grid_b, NTB, LDS_B, s>>>(a, st, tiles, ows);
+  const dim3 grid_b(NBLK * a.H, VL ? st.n : a.B);
+  timing_begin(VL ? "kda_chunk_state_kernel[varlen]" : "kda_chunk_state_kernel", s);
+  kda_chunk_state_kernel<VL><<<grid_b, NTB, LDS_B, s>>>(a, st, tiles, ows);
   timing_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long rows = tokens * a.H;
   const dim3 ng((unsigned)((rows + 15) / 16));
-  timing_begin("kda_out_norm_kernel", s);
+  timing_begin(VL ? "kda_out_norm_kernel[varlen]" : "kda_out_norm_kernel", s);
   if (ot == kBF16)
     kda_out_norm_kernel<bf16_t><<<ng, 256, 0, s>>>(ows, static_cast<const bf16_t*>(a.g_out),
                                                    static_cast<const bf16_t*>(a.norm_w), static_cast<bf16_t*>(a.out),
@@ -1230,6 +1235,11 @@ hipError_t launch_prefill_mfma(const LayerArgs& a, const SeqTab& st, void* ws, s
                                                   a.rms_eps);
   timing_end(s);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill_mfma(const LayerArgs& a, const SeqTab& st, void* ws, size_t, int ot, hipStream_t s) {
+  static_assert(C == kMfmaChunk, "chunk of the sequence tables");
+  return st.n > 0 ? launch_mfma_t<true>(a, st, ws, ot, s) : launch_mfma_t<false>(a, st, ws, ot, s);
 }
 
 }  // namespace kda
