@@ -134,6 +134,17 @@ static_assert(LDS_B <= 160 * 1024, "LDS budget");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// The depthwise conv on bf16 pairs: a.x * b.x + a.y * b.y + c (products exact in fp32).
+__device__ __forceinline__ float dot2(bf16x2 a, bf16x2 b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+// (x.y, y.x): the pair between two consecutive pairs of a column
+__device__ __forceinline__ bf16x2 mid_pair(bf16x2 x, bf16x2 y) {
+  return __builtin_bit_cast(bf16x2, __builtin_amdgcn_alignbit(__builtin_bit_cast(uint32_t, y),
+                                                               __builtin_bit_cast(uint32_t, x), 16));
+}
 
 struct Split8 {
   bf16x8 hi, lo;
@@ -404,16 +415,22 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     __syncthreads();
     // conv taps of this lane's q|k channel (tid % 256) and of the v channel it converts in P9
     // (16 * wave + lane % 16), zero-padded on the left to 4 taps; read before T reuses the block
-    float tq[4], tv[4];
+    // taps as bf16 pairs (tap of the older token first): {t0, t1} and {t2, t3}
+    bf16x2 tq01, tq23, tv01, tv23;
     {
       const __bf16* taps = reinterpret_cast<const __bf16*>(sPar);
       const int cq = tid & 255;  // q channels then k channels: the block rows in that order
+      __bf16 tq[4], tv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int w = max(j - (4 - W), 0);
-        tq[j] = j >= 4 - W ? (float)taps[cq * W + w] : 0.f;
-        tv[j] = j >= 4 - W ? (float)taps[(2 * D + 16 * wave + l16) * W + w] : 0.f;
+        tq[j] = j >= 4 - W ? taps[cq * W + w] : (__bf16)0.f;
+        tv[j] = j >= 4 - W ? taps[(2 * D + 16 * wave + l16) * W + w] : (__bf16)0.f;
       }
+      tq01 = bf16x2{tq[0], tq[1]};
+      tq23 = bf16x2{tq[2], tq[3]};
+      tv01 = bf16x2{tv[0], tv[1]};
+      tv23 = bf16x2{tv[2], tv[3]};
     }
     const float* sDtb = reinterpret_cast<const float*>(sPar + 3 * D * W * 2);
 
@@ -422,15 +439,20 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       const int tb = 32 * (tid >> 8), cq = tid & 255;
       const __bf16* col = sRaw + cq;
       float* dst = cq < D ? sQ + cq : sG + (cq - D);
-      // the lane's 35 raw rows are read before any arithmetic, so that the reads overlap instead of
-      // each output waiting on the latency of its own read
-      float x[32 + 3];
+      // the lane's 35 raw rows are read before any arithmetic (so that the reads overlap) as pairs
+      // pe[m] = (row 2m, row 2m+1) and, between them, po[m] = (row 2m+1, row 2m+2); output row i
+      // takes pairs i and i+2
+      bf16x2 pe[18], po[17];
 #pragma unroll
-      for (int i = 0; i < 35; ++i) x[i] = (float)col[(tb + i) * PR];
+      for (int m = 0; m < 17; ++m) pe[m] = bf16x2{col[(tb + 2 * m) * PR], col[(tb + 2 * m + 1) * PR]};
+      pe[17] = bf16x2{col[(tb + 34) * PR], (__bf16)0.f};
+#pragma unroll
+      for (int m = 0; m < 17; ++m) po[m] = mid_pair(pe[m], pe[m + 1]);
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        const int t = tb + i;
-        const float y = tq[0] * x[i] + tq[1] * x[i + 1] + tq[2] * x[i + 2] + tq[3] * x[i + 3];
+        const int t = tb + i, m = i >> 1;
+        const float y = (i & 1) ? dot2(tq23, po[m + 1], dot2(tq01, po[m], 0.f))
+                                : dot2(tq23, pe[m + 1], dot2(tq01, pe[m], 0.f));
         dst[t * PQ] = t < L ? silu_fast(y) : 0.f;
       }
     }
@@ -758,13 +780,21 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int tb = 32 * st + 8 * lg;
-        float rr[11];
+        // rows tb .. tb+10 of channel vc as pairs, as in the q|k conv
+        bf16x2 pe[6], po[5];
 #pragma unroll
-        for (int q = 0; q < 11; ++q) rr[q] = (float)sRv[(tb + q) * PKB + vc];
+        for (int m = 0; m < 5; ++m) pe[m] = bf16x2{sRv[(tb + 2 * m) * PKB + vc], sRv[(tb + 2 * m + 1) * PKB + vc]};
+        pe[5] = bf16x2{sRv[(tb + 10) * PKB + vc], (__bf16)0.f};
+#pragma unroll
+        for (int m = 0; m < 5; ++m) po[m] = mid_pair(pe[m], pe[m + 1]);
         float xv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          xv[e] = sBeta[tb + e] * silu_fast(tv[0] * rr[e] + tv[1] * rr[e + 1] + tv[2] * rr[e + 2] + tv[3] * rr[e + 3]);
+        for (int e = 0; e < 8; ++e) {
+          const int m = e >> 1;
+          const float y = (e & 1) ? dot2(tv23, po[m + 1], dot2(tv01, po[m], 0.f))
+                                  : dot2(tv23, pe[m + 1], dot2(tv01, pe[m], 0.f));
+          xv[e] = sBeta[tb + e] * silu_fast(y);
+        }
         bv[st] = split(xv);
       }
       f32x4 ut[4];
