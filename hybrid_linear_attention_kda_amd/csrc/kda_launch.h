@@ -77,7 +77,7 @@ hipError_t launch_commit_tape(const CommitArgs& a, int io, hipStream_t s);
 // Chunked prefill, fp32 VALU form (any supported head size; internal chunk <= 4096 / D).
 hipError_t launch_prefill_generic(const LayerArgs& a, const SeqTab& st, int chunk, int io, int ot, hipStream_t s);
 
-// Chunked prefill on bf16 MFMA (D = 128, chunk 64, bf16 io, conv width <= 4, -5.5 <= lb <= 0).
+// Chunked prefill on bf16 MFMA (D = 128, chunk 64, bf16 io, conv width <= 4, -5.5 <= lb <= -0.25).
 // Workspace: chunk blocks for `chunks` chunks of H heads, o for `tokens` tokens, a scratch slot.
 constexpr int kMfmaChunk = 64;
 bool prefill_mfma_supported(int D, int chunk, int io, int W, float lb);

@@ -39,8 +39,11 @@
  *     the snapshots, A_log and dt_bias are always fp32.
  *   - Supported: d_k == d_v in {16, 32, 64, 128}; conv_width 1..8;
  *     prefill chunk_size in {16, 32, 64}.  Other shapes return
- *     KDA_ERR_UNSUPPORTED.  bf16 io with d = 128 and chunk 64 runs the bf16
- *     matrix-core prefill; every other prefill runs the fp32 vector-ALU form.
+ *     KDA_ERR_UNSUPPORTED.  bf16 io with d = 128, chunk 64, conv width <= 4
+ *     and a gate bound in [-5.5, -0.25] runs the bf16 matrix-core prefill;
+ *     every other prefill runs the fp32 vector-ALU form (weaker decay keeps
+ *     more of the state, which the matrix-core path's bf16 operands would
+ *     carry past the 2e-3 tolerance over long sequences).
  */
 #ifndef KDA_H_
 #define KDA_H_

@@ -254,6 +254,64 @@ def test_bf16_prefill_four_heads(T):
     _check("out (bf16 output)", out16, ref["out"], TOL_BF16_OUT)
 
 
+@pytest.mark.parametrize("W,lb", [(1, -5.0), (2, -5.0), (3, -5.0), (4, -0.25), (4, -5.5), (4, 0.0), (4, -8.0)])
+def test_bf16_prefill_conv_widths_and_gate_bounds(W, lb):
+    # the matrix-core path takes conv widths 1..4 and gate bounds in [-5.5, -0.25]; lb = 0 (no decay)
+    # and lb = -8 (outside the anchoring bound) run the fp32 path on the same bf16 inputs
+    wl = I.WORKLOADS["prefill_t4096"].with_(T=150, H=2, B=2, W=W, lb=lb, seed=30 + W)
+    say(f"case bf16 prefill W={W} lb={lb} H=2 B=2 T=150")
+    inp = I.generate(wl)
+    rng = np.random.default_rng(W)
+    S0 = (rng.standard_normal(inp["state0"].shape) * 0.3).astype(np.float32)
+    C0 = I.round_to_io(rng.standard_normal(inp["conv_state0"].shape), "bf16")
+    layer = TT.make_layer(wl, inp, DEV)
+    st, cs = _dev_state(wl, inp, S0, C0)
+    out = _gpu_prefill(wl, inp, layer, 0, 150, st, cs)
+    torch.cuda.synchronize()
+    ref = oracle_layer(wl, inp, 0, 150, S0, C0)
+    _check("out", out, ref["out"], TOL["bf16"])
+    _check("state", st, ref["state"], TOL["bf16"])
+    if W > 1:
+        _check("conv_state", cs, ref["conv_state"], 0.0)
+
+
+@pytest.mark.parametrize("W", [1, 8])
+def test_tiny_fp32_conv_width_extremes_prefill_decode_tape(W):
+    # conv widths 1 (no conv state) and 8 (the widest supported): fp32 prefill of a prefix, then a
+    # decode step, then a tape verify of 8 tokens and its commit
+    wl = I.WORKLOADS["tiny_fp32"].with_(T=8, B=2, W=W, prefix_T=6, seed=40 + W)
+    say(f"case tiny_fp32 W={W}: prefill 5, decode 1, tape verify 8 + commit")
+    inp = I.generate(wl)
+    layer = TT.make_layer(wl, inp, DEV)
+    st, cs = _dev_state(wl, inp)
+    out = _gpu_prefill(wl, inp, layer, 0, 5, st, cs)
+    tok = TT.token_tensors(wl, inp, 5, 6, DEV)
+    out1 = torch.empty((2, 1, wl.H * wl.dv), dtype=torch.float32, device=DEV)
+    abi.kda_decode_step(layer, tok["qkv"], tok["f"], tok["beta"], tok["g_out"], st, cs, out1)
+    torch.cuda.synchronize()
+    ref = oracle_layer(wl, inp, 0, 6, inp["state0"], inp["conv_state0"])
+    _check("prefill out", out, ref["out"][:, :5], TOL["f32"])
+    _check("decode out", out1, ref["out"][:, 5:6], TOL["f32"])
+    _check("state", st, ref["state"], TOL["f32"])
+    if W > 1:
+        _check("conv_state", cs, ref["conv_state"], 0.0)
+    S6, C6 = ref["state"].astype(np.float32), ref["conv_state"].astype(np.float32)
+    tok = TT.token_tensors(wl, inp, 6, 14, DEV)
+    tape = torch.empty((2, 8, wl.H, 3, wl.dk), dtype=torch.float32, device=DEV)
+    out8 = torch.empty((2, 8, wl.H * wl.dv), dtype=torch.float32, device=DEV)
+    abi.kda_verify_block_tape(layer, tok["qkv"], tok["f"], tok["beta"], tok["g_out"], st, cs, tape, out8)
+    accepted = [3, 8]
+    abi.kda_commit_tape(layer, accepted, tape, tok["qkv"], st, cs)
+    torch.cuda.synchronize()
+    sub = I.split_tokens(inp, 6, 14)
+    rv = O.kda_verify_tape(pu.params(wl, inp), sub["qkv"], sub["f"], sub["beta"], sub["g_out"], S6, C6)
+    _check("tape verify out", out8, rv["out"], TOL["f32"])
+    ref_s, ref_c = O.kda_commit_tape(pu.params(wl, inp), accepted, rv["tape"], sub["qkv"], S6, C6)
+    _check("committed state", st, ref_s, TOL["f32"])
+    if W > 1:
+        _check("committed conv state", cs, ref_c, 0.0)
+
+
 # ---------------------------------------------------------------------------
 # Variable-length prefill over a state pool (every element)
 # ---------------------------------------------------------------------------
