@@ -5,6 +5,8 @@ One step = one pass over every call of the path on its layer-shaped workload:
   varlen    the same 4096 tokens as 16 packed sequences of a seeded length mix
             (123..628 tokens), each from its own zero state slot
   decode    64 sequences x 32 heads x 128x128 fp32 state, one token each
+  projection  the layer's input projection for those 4096 tokens: hidden 4096 -> q|k|v, f, beta,
+            g_out (H=32, d=128, rank 128; the q|k|v|f_a|g_a|b projections as one GEMM)
   verify    16 sequences x 8 draft tokens with per-token snapshots, then rollback
             to a seeded accepted prefix (0..8) per sequence; and the same block
             verified with a replay tape, then committed from the tape
@@ -139,8 +141,24 @@ def stored_traffic(kernel):
     return k["fetch_bytes"] + k["write_bytes"]
 
 
+def projection_flops(wl):
+    """useful flops of one input projection: the fused GEMM and the two rank-r up-projections"""
+    HD = wl.H * wl.d
+    return 2 * wl.T * wl.hidden * (3 * HD + 2 * wl.rank + wl.H) + 2 * 2 * wl.T * wl.rank * HD
+
+
+def kernel_alg_flops(kernel, wj):
+    """Useful flops of one launch of the input projection's kernels (matrix-core bound, no bytes)."""
+    HD = wj.H * wj.d
+    return {"hipblaslt_gemm[qkv]": 2 * wj.T * wj.hidden * 3 * HD,
+            "hipblaslt_gemm[rank|beta]": 2 * wj.T * wj.hidden * (2 * wj.rank + wj.H),
+            "kda_proj_lowrank_kernel": 2 * 2 * wj.T * wj.rank * HD}.get(kernel)
+
+
 def short_kernel_name(full):
     import re
+    if "Cijk_" in full:  # the GEMM library's kernels (the input projection's two GEMMs)
+        return "hipblaslt_gemm"
     m = re.search(r"(kda_[a-z_]+_kernel)(<[^>]*>)?", full)
     if m is None:
         return None
@@ -223,7 +241,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sets", type=int, default=4)
-    ap.add_argument("--only", choices=["prefill", "varlen", "decode", "verify"], default=None,
+    ap.add_argument("--only", choices=["prefill", "varlen", "projection", "decode", "verify"], default=None,
                     help="time one call type only (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
@@ -254,7 +272,7 @@ def main():
     nsets = max(1, args.sets)
 
     wp, wd, wv = I.WORKLOADS["prefill_t4096"], I.WORKLOADS["decode_b64"], I.WORKLOADS["verify_b16"]
-    ops = ["prefill", "varlen", "decode", "verify"] if args.only is None else [args.only]
+    ops = ["prefill", "varlen", "projection", "decode", "verify"] if args.only is None else [args.only]
 
     def workspace(layer, B, T):
         n = abi.kda_prefill_workspace_size(layer, B, T)
@@ -290,6 +308,24 @@ def main():
                 out=torch.empty((wp.T, wp.H * wp.dv), dtype=torch.bfloat16, device=dev),
                 ws=torch.empty(nvs, dtype=torch.uint8, device=dev)))
         del tok
+
+    wj = I.PROJ_WORKLOADS["projection_t4096"]
+    if "projection" in ops:
+        pin = I.generate_projection(wj)
+        HDj = wj.H * wj.d
+        pw = {k: TT.to_device(pin[k], "bf16", dev) for k in ("w_in", "w_fb", "w_gb")}
+        proj = abi.KdaProjection(H=wj.H, D=wj.d, hidden=wj.hidden, rank=wj.rank, out_dtype=abi.KDA_BF16, **pw)
+        x = TT.to_device(pin["x"], "bf16", dev)
+        npw = abi.kda_input_projection_workspace_size(proj, wj.T)
+        for _ in range(nsets):
+            sets["projection"].append(dict(
+                proj=proj, x=x.clone(),
+                qkv=torch.empty((wj.T, 3 * HDj), dtype=torch.bfloat16, device=dev),
+                f=torch.empty((wj.T, HDj), dtype=torch.bfloat16, device=dev),
+                beta=torch.empty((wj.T, wj.H), dtype=torch.bfloat16, device=dev),
+                g=torch.empty((wj.T, HDj), dtype=torch.bfloat16, device=dev),
+                ws=torch.empty(npw, dtype=torch.uint8, device=dev)))
+        del pin, x
 
     def prefilled(wl, inp):
         # The prefix runs through the fp32-io prefill (its own kernel, the inputs are bf16 values
@@ -339,6 +375,8 @@ def main():
         elif op == "varlen":
             abi.kda_prefill_varlen(s["layer"], var_cu, None, t["qkv"], t["f"], t["beta"], t["g_out"], s["state"],
                                    s["conv"], s["out"], workspace=s["ws"], stream=stream)
+        elif op == "projection":
+            abi.kda_input_projection(s["proj"], s["x"], s["qkv"], s["f"], s["beta"], s["g"], s["ws"], stream=stream)
         elif op == "decode":
             abi.kda_decode_step(s["layer"], t["qkv"], t["f"], t["beta"], t["g_out"], s["state"], s["conv"],
                                 s["out"], stream=stream)
@@ -410,8 +448,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "prefill_t4096 (B=1,T=4096,H=32,d=128,chunk 64) + the same tokens as 16 packed "
-                               "sequences + decode_b64 (B=64,H=32,d=128) + verify_b16 (B=16,T_d=8,H=32,d=128) "
-                               "with rollback and with the replay tape",
+                               "sequences + their input projection (hidden 4096) + decode_b64 (B=64,H=32,d=128) "
+                               "+ verify_b16 (B=16,T_d=8,H=32,d=128) with rollback and with the replay tape",
                    "io": "bf16 inputs and outputs, fp32 state and accumulation", "buffer_sets": nsets},
         "wall_s": wall,
     }
@@ -430,6 +468,13 @@ def main():
                                     "sequences": VARLEN_SEQS, "lengths": var_lens}
         if "value" not in res:
             res["value"], res["unit"] = wp.T / (mean["varlen"] * 1e-3), "tokens/s"
+    if "projection" in ops:
+        fl = projection_flops(wj)
+        tf = fl / (mean["projection"] * 1e-3) / 1e12
+        detail["input_projection"] = {"ms_mean": mean["projection"], "flops": fl, "tflops": tf,
+                                      "mfma_frac": tf / BF16_MFMA_PEAK_TFLOPS,
+                                      "tokens_per_s": wj.T / (mean["projection"] * 1e-3),
+                                      "workload": "T=4096, hidden=4096, H=32, d=128, rank 128, bf16 in and out"}
     if "decode" in ops:
         db = decode_bytes(wd.B, wd.H, wd.dk, wd.W)
         gb = db / (mean["decode"] * 1e-3) / 1e9
@@ -464,11 +509,16 @@ def main():
         kern[name] = {"ms_mean": avg, "ms_p10": float(np.percentile(ts, 10)), "ms_p90": float(np.percentile(ts, 90)),
                       "launches_per_step": len(ts) / K, "alg_bytes": nb,
                       "gbps": (nb / (avg * 1e-3) / 1e9) if nb else None}
+        fl = kernel_alg_flops(name, wj)
+        if fl:
+            kern[name].update(flops=fl, tflops=fl / (avg * 1e-3) / 1e12,
+                              mfma_frac=fl / (avg * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS)
     detail["kernels"] = kern
     res["detail"] = detail
-    # dominant kernel: the largest share of the step among the headline workloads' kernels (the
-    # variable-length line runs the same kernels on another table and is reported beside them)
-    name = max((n for n in kern if not n.endswith("[varlen]")),
+    # dominant kernel: the largest share of the step among the attention kernels of the headline
+    # workloads (the variable-length line runs the same kernels on another table, and the input
+    # projection is a matrix-core GEMM line ahead of the layer: both are reported beside them)
+    name = max((n for n in kern if not n.endswith("[varlen]") and kern[n]["alg_bytes"]),
                key=lambda n: kern[n]["ms_mean"] * kern[n]["launches_per_step"])
     k = kern[name]
     achieved = k["gbps"]

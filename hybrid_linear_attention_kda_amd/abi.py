@@ -42,6 +42,13 @@ class KdaLayerDesc(ctypes.Structure):
     ]
 
 
+class KdaProjDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", c_int32), ("head_dim", c_int32), ("hidden", c_int32), ("rank", c_int32),
+        ("out_dtype", c_int32), ("w_in", c_void_p), ("w_fb", c_void_p), ("w_gb", c_void_p),
+    ]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -67,6 +74,8 @@ def load() -> ctypes.CDLL:
         "kda_rollback": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P]),
         "kda_verify_tape_size": (c_size_t, [D, c_int32, c_int32]),
         "kda_prefill_varlen_workspace_size": (c_size_t, [D, c_int32, P]),
+        "kda_input_projection_workspace_size": (c_size_t, [ctypes.POINTER(KdaProjDesc), c_int32]),
+        "kda_input_projection": (c_int32, [ctypes.POINTER(KdaProjDesc), c_int32, P, P, P, P, P, P, c_size_t, P]),
         "kda_prefill_varlen": (c_int32, [D, c_int32, P, P, c_int32, P, P, P, P, P, P, P, P, c_size_t, P]),
         "kda_verify_block_tape": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P, P, P, P]),
         "kda_commit_tape": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P]),
@@ -145,6 +154,31 @@ class KdaLayer:
     @property
     def io_torch(self):
         return _TORCH_OF[self.io_dtype]
+
+    @property
+    def out_torch(self):
+        return _TORCH_OF[self.out_dtype]
+
+
+@dataclass
+class KdaProjection:
+    """An input-projection description plus its device weight tensors (Linear weights, [out, in])."""
+    H: int
+    D: int
+    hidden: int
+    rank: int
+    out_dtype: int
+    w_in: torch.Tensor  # [3*H*D + 2*rank + H, hidden] bf16
+    w_fb: torch.Tensor  # [H*D, rank] bf16
+    w_gb: torch.Tensor  # [H*D, rank] bf16
+
+    def __post_init__(self):
+        n = 3 * self.H * self.D + 2 * self.rank + self.H
+        _expect(self.w_in, (n, self.hidden), torch.bfloat16, "w_in")
+        _expect(self.w_fb, (self.H * self.D, self.rank), torch.bfloat16, "w_fb")
+        _expect(self.w_gb, (self.H * self.D, self.rank), torch.bfloat16, "w_gb")
+        self.desc = KdaProjDesc(self.H, self.D, self.hidden, self.rank, self.out_dtype, _ptr(self.w_in),
+                                _ptr(self.w_fb), _ptr(self.w_gb))
 
     @property
     def out_torch(self):
@@ -269,6 +303,31 @@ def kda_prefill_varlen(layer: KdaLayer, cu_seqlens, slots, qkv, f, beta, g_out, 
                                      ctypes.cast(sl, c_void_p) if sl is not None else None, num_slots,
                                      _ptr(qkv), _ptr(f), _ptr(beta), _ptr(g_out), _ptr(state), _ptr(conv_state),
                                      _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kda_input_projection_workspace_size(proj: KdaProjection, T: int) -> int:
+    n = load().kda_input_projection_workspace_size(ctypes.byref(proj.desc), T)
+    if n == ctypes.c_size_t(-1).value:
+        raise KdaError(KDA_ERR_INVALID_ARGUMENT, load().kda_last_error().decode())
+    return n
+
+
+def kda_input_projection(proj: KdaProjection, x, qkv, f, beta, g_out, workspace, stream=None):
+    """x [T, hidden] bf16 -> qkv [T, 3*H*D], f [T, H*D], beta [T, H], g_out [T, H*D]."""
+    T = x.shape[0]
+    _expect(x, (T, proj.hidden), torch.bfloat16, "x")
+    ot = proj.out_torch
+    HD = proj.H * proj.D
+    _expect(qkv, (T, 3 * HD), ot, "qkv")
+    _expect(f, (T, HD), ot, "f")
+    _expect(beta, (T, proj.H), ot, "beta")
+    _expect(g_out, (T, HD), ot, "g_out")
+    need = kda_input_projection_workspace_size(proj, T)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if ws_bytes < need:
+        raise ValueError(f"workspace of {ws_bytes} bytes, {need} needed")
+    _check(load().kda_input_projection(ctypes.byref(proj.desc), T, _ptr(x), _ptr(qkv), _ptr(f), _ptr(beta),
+                                       _ptr(g_out), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def kda_verify_tape_size(layer: KdaLayer, B: int, T_d: int) -> int:

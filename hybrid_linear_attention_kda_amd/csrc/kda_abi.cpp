@@ -175,6 +175,22 @@ size_t varlen_workspace(const std::vector<Launch>& plan, int H) {
   return need;
 }
 
+kda_status check_proj(const kda_proj_desc* d) {
+  if (d == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is null");
+  if (d->num_heads < 1 || d->head_dim < 1 || d->hidden < 1 || d->rank < 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "num_heads, head_dim, hidden and rank must be >= 1");
+  if (d->rank != kda::kProjRank) return fail(KDA_ERR_UNSUPPORTED, "rank %d != %d", d->rank, kda::kProjRank);
+  if ((d->num_heads * d->head_dim) % 128 != 0)
+    return fail(KDA_ERR_UNSUPPORTED, "H*d = %d is not a multiple of 128", d->num_heads * d->head_dim);
+  if (d->hidden % 8 != 0) return fail(KDA_ERR_UNSUPPORTED, "hidden = %d is not a multiple of 8", d->hidden);
+  if (d->out_dtype != KDA_F32 && d->out_dtype != KDA_BF16)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "out_dtype must be KDA_F32 or KDA_BF16");
+  KDA_TRY(check_ptr(d->w_in, "desc.w_in"));
+  KDA_TRY(check_ptr(d->w_fb, "desc.w_fb"));
+  KDA_TRY(check_ptr(d->w_gb, "desc.w_gb"));
+  return KDA_OK;
+}
+
 kda_status check_token_tensors(const void* qkv, const void* f, const void* beta, const void* g_out) {
   KDA_TRY(check_ptr(qkv, "qkv"));
   KDA_TRY(check_ptr(f, "f"));
@@ -460,6 +476,52 @@ kda_status kda_commit_tape(const kda_layer_desc* desc, int32_t B, int32_t T_d, c
     for (int i = 0; i < c.nB; ++i) c.accepted[i] = (uint8_t)accepted_host[b0 + i];
     kda_status st = launched(kda::launch_commit_tape(c, desc->io_dtype, s), "kda_commit_tape");
     if (st != KDA_OK) return st;
+  }
+  return ok();
+}
+
+size_t kda_input_projection_workspace_size(const kda_proj_desc* desc, int32_t T) {
+  if (check_proj(desc) != KDA_OK || check_batch(1, T) != KDA_OK) return (size_t)-1;
+  return kda::projection_workspace(T, desc->num_heads, desc->head_dim);
+}
+
+kda_status kda_input_projection(const kda_proj_desc* desc, int32_t T, const void* x, void* qkv, void* f,
+                                void* beta, void* g_out, void* workspace, size_t workspace_bytes, void* stream) {
+  KDA_TRY(check_proj(desc));
+  KDA_TRY(check_batch(1, T));
+  if (T == 0) return ok();
+  KDA_TRY(check_ptr(x, "x"));
+  KDA_TRY(check_ptr(qkv, "qkv"));
+  KDA_TRY(check_ptr(f, "f"));
+  KDA_TRY(check_ptr(beta, "beta"));
+  KDA_TRY(check_ptr(g_out, "g_out"));
+  const size_t need = kda::projection_workspace(T, desc->num_heads, desc->head_dim);
+  if (workspace == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is null (%zu bytes needed)", need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  kda::ProjArgs p{};
+  p.T = T;
+  p.hidden = desc->hidden;
+  p.H = desc->num_heads;
+  p.D = desc->head_dim;
+  p.out_type = desc->out_dtype;
+  p.x = x;
+  p.w_in = desc->w_in;
+  p.w_fb = desc->w_fb;
+  p.w_gb = desc->w_gb;
+  p.qkv = qkv;
+  p.f = f;
+  p.beta = beta;
+  p.g = g_out;
+  p.ws = workspace;
+  p.ws_bytes = workspace_bytes;
+  char err[256] = "";
+  const hipError_t e = kda::launch_projection(p, static_cast<hipStream_t>(stream), err, sizeof(err));
+  if (e != hipSuccess) {
+    if (err[0] != '\0') return fail(KDA_ERR_HIP, "kda_input_projection: %s", err);
+    return fail(KDA_ERR_HIP, "kda_input_projection: %s", hipGetErrorString(e));
   }
   return ok();
 }

@@ -74,6 +74,27 @@ hipError_t launch_recurrent(const LayerArgs& a, int io, int ot, hipStream_t s);
 hipError_t launch_rollback(const RollbackArgs& a, int io, hipStream_t s);
 hipError_t launch_commit_tape(const CommitArgs& a, int io, hipStream_t s);
 
+// Input projection (hipBLASLt GEMMs + the low-rank / beta kernel).  Rank r = 128; H*D a multiple
+// of 128; bf16 weights and hidden states; outputs bf16 or fp32.
+constexpr int kProjRank = 128;
+constexpr size_t kProjGemmWorkspace = 32u << 20;  // hipBLASLt workspace inside the caller's workspace
+struct ProjArgs {
+  int T, hidden, H, D, out_type;
+  const void* x;      // [T, hidden] bf16
+  const void* w_in;   // [3*H*D + 2*r + H, hidden] bf16: rows q | k | v | f_a | g_a | b
+  const void* w_fb;   // [H*D, r] bf16
+  const void* w_gb;   // [H*D, r] bf16
+  void* qkv;          // [T, 3*H*D]
+  void* f;            // [T, H*D]
+  void* beta;         // [T, H]
+  void* g;            // [T, H*D]
+  void* ws;
+  size_t ws_bytes;
+};
+size_t projection_workspace(int T, int H, int D);
+// On failure returns an error and writes a description into err.
+hipError_t launch_projection(const ProjArgs& p, hipStream_t s, char* err, size_t errlen);
+
 // Chunked prefill, fp32 VALU form (any supported head size; internal chunk <= 4096 / D).
 hipError_t launch_prefill_generic(const LayerArgs& a, const SeqTab& st, int chunk, int io, int ot, hipStream_t s);
 

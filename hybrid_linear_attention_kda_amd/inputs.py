@@ -200,3 +200,37 @@ def cu_seqlens(lengths) -> list:
     for n in lengths:
         out.append(out[-1] + int(n))
     return out
+
+
+@dataclass(frozen=True)
+class ProjWorkload:
+    name: str
+    T: int
+    hidden: int
+    H: int
+    d: int
+    rank: int
+    seed: int
+
+
+PROJ_WORKLOADS = {
+    # the input projection ahead of prefill_t4096: 4096 tokens of a 4096-wide model (the pages give
+    # no model width; 4096 = H*d is the reading taken), H=32, d=128, f/g rank 128
+    "projection_t4096": ProjWorkload("projection_t4096", T=4096, hidden=4096, H=32, d=128, rank=128, seed=6),
+}
+
+
+def generate_projection(wl: ProjWorkload) -> dict:
+    """Hidden states x ~ N(0, 1) and Linear weights ~ N(0, 1/in_features), all rounded to bf16
+    (so the projected q, k, v, f and gate logits come out near N(0, 1), as in the layer's own
+    synthetic inputs).  Keys: x [T, hidden], w_in [3Hd + 2r + H, hidden], w_fb, w_gb [Hd, r]."""
+    children = np.random.SeedSequence(wl.seed).spawn(4)
+    r = [np.random.Generator(np.random.PCG64(c)) for c in children]
+    HD = wl.H * wl.d
+    n = 3 * HD + 2 * wl.rank + wl.H
+    return {
+        "x": round_to_io(_normal(r[0], (wl.T, wl.hidden)), "bf16"),
+        "w_in": round_to_io(_normal(r[1], (n, wl.hidden), wl.hidden ** -0.5), "bf16"),
+        "w_fb": round_to_io(_normal(r[2], (HD, wl.rank), wl.rank ** -0.5), "bf16"),
+        "w_gb": round_to_io(_normal(r[3], (HD, wl.rank), wl.rank ** -0.5), "bf16"),
+    }

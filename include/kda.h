@@ -211,6 +211,45 @@ kda_status kda_commit_tape(const kda_layer_desc* desc, int32_t B, int32_t T_d, c
                            void* stream);
 
 /*
+ * Input projection of a KDA layer: the step before the layer.  The q, k, v,
+ * f_a, g_a and b projections of the hidden states are one weight matrix (the
+ * runtime fuses the six KDA input projections into one matmul, glm53-flash-mlx
+ * README, quantization recipe); f and the output gate are low rank,
+ * f = f_b(f_a x), g_out = g_b(g_a x) (llama.cpp PR #27754, KDA commit), and
+ * beta = sigmoid(b x).  Weights are Linear weights ([out, in], row-major):
+ *   w_in [3*H*d + 2*rank + H, hidden] bf16, rows q | k | v | f_a | g_a | b
+ *   w_fb [H*d, rank] bf16,  w_gb [H*d, rank] bf16
+ * Supported: rank = 128, H*d a multiple of 128, hidden a multiple of 8.
+ */
+typedef struct kda_proj_desc {
+  int32_t num_heads;   /* H */
+  int32_t head_dim;    /* d */
+  int32_t hidden;      /* model width of the hidden states */
+  int32_t rank;        /* f_a / g_a width (128) */
+  int32_t out_dtype;   /* KDA_BF16 or KDA_F32: type of qkv, f, beta, g_out */
+  const void* w_in;
+  const void* w_fb;
+  const void* w_gb;
+} kda_proj_desc;
+
+/*
+ * Workspace bytes kda_input_projection needs for T tokens ((size_t)-1 if the
+ * arguments are invalid): the rank / beta activations in fp32 and the GEMM
+ * library's workspace.
+ */
+size_t kda_input_projection_workspace_size(const kda_proj_desc* desc, int32_t T);
+
+/*
+ * x [T, hidden] bf16 (in) -> qkv [T, 3*H*d], f [T, H*d], beta [T, H],
+ * g_out [T, H*d] (out, desc->out_dtype): exactly the token inputs of
+ * kda_prefill.  workspace: >= kda_input_projection_workspace_size bytes,
+ * 256-byte aligned.  Accumulation is fp32; the rank activations stay fp32
+ * until the up-projections (which split them into bf16 hi + lo).
+ */
+kda_status kda_input_projection(const kda_proj_desc* desc, int32_t T, const void* x, void* qkv, void* f,
+                                void* beta, void* g_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Per-kernel timing, for benchmarks (not part of the layer).
  * kda_timing_enable(1) makes every later call made on this host thread record
  * a HIP event pair on the call's stream around each kernel it launches;

@@ -521,3 +521,21 @@ def kda_prefill_varlen(p: KdaParams, cu_seqlens, slots, qkv, f, beta, g_out, sta
         state[s] = r["state"][0]
         conv_state[s] = r["conv_state"][0]
     return {"out": out, "state": state, "conv_state": conv_state}
+
+
+def kda_input_projection(x, w_in, w_fb, w_gb, H: int, d: int, rank: int):
+    """The step before the layer: the six input projections of the hidden states x [T, hidden].
+
+    w_in [3*H*d + 2*rank + H, hidden] holds the q, k, v, f_a, g_a and b projections as one
+    weight (rows in that order; the runtime fuses them into one matmul, glm53-flash-mlx README,
+    quantization recipe).  f and the output gate are low rank, f = f_b(f_a x) and
+    g_out = g_b(g_a x) (llama.cpp PR #27754, KDA commit); beta = sigmoid(b x).  Weights are
+    Linear weights [out, in].  Returns dict(qkv [T, 3Hd], f [T, Hd], beta [T, H], g_out [T, Hd]).
+    """
+    x, w_in, w_fb, w_gb = (_f64(a) for a in (x, w_in, w_fb, w_gb))
+    HD = H * d
+    y = x @ w_in.T
+    fa = y[:, 3 * HD:3 * HD + rank]
+    ga = y[:, 3 * HD + rank:3 * HD + 2 * rank]
+    return {"qkv": y[:, :3 * HD], "f": fa @ w_fb.T, "beta": sigmoid(y[:, 3 * HD + 2 * rank:]),
+            "g_out": ga @ w_gb.T}

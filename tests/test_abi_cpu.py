@@ -35,6 +35,7 @@ def test_library_exports_every_header_function():
                           "kda_prefill", "kda_decode_step", "kda_verify_block", "kda_rollback",
                           "kda_verify_tape_size", "kda_verify_block_tape", "kda_commit_tape",
                           "kda_prefill_varlen_workspace_size", "kda_prefill_varlen",
+                          "kda_input_projection_workspace_size", "kda_input_projection",
                           "kda_timing_enable", "kda_timing_read"}
     for n in names:
         assert hasattr(lib, n), n
@@ -149,6 +150,31 @@ def test_varlen_validation_and_workspace_size():
     bad = (ctypes.c_int32 * 3)(0, 4, 2)
     assert lib.kda_prefill_varlen_workspace_size(ctypes.byref(d), 2, ctypes.cast(bad, ctypes.c_void_p)) == \
         ctypes.c_size_t(-1).value
+
+
+def test_input_projection_validation():
+    lib = abi.load()
+    P = FAKE
+
+    def pd(**kw):
+        v = dict(num_heads=32, head_dim=128, hidden=4096, rank=128, out_dtype=abi.KDA_BF16, w_in=P, w_fb=P, w_gb=P)
+        v.update(kw)
+        return abi.KdaProjDesc(**v)
+
+    def call(d, T=16, ptr=P, ws=0):
+        return lib.kda_input_projection(ctypes.byref(d), T, ptr, ptr, ptr, ptr, ptr, ws, 1 << 30, None)
+
+    assert call(pd(), T=0, ptr=0) == abi.KDA_OK
+    assert call(pd(rank=64)) == abi.KDA_ERR_UNSUPPORTED and b"rank 64" in lib.kda_last_error()
+    assert call(pd(num_heads=3, head_dim=16)) == abi.KDA_ERR_UNSUPPORTED
+    assert call(pd(hidden=4100)) == abi.KDA_ERR_UNSUPPORTED
+    assert call(pd(w_fb=0)) == abi.KDA_ERR_INVALID_ARGUMENT and b"desc.w_fb is null" in lib.kda_last_error()
+    assert call(pd(out_dtype=5)) == abi.KDA_ERR_INVALID_ARGUMENT
+    assert call(pd()) == abi.KDA_ERR_INVALID_ARGUMENT and b"workspace is null" in lib.kda_last_error()
+    need = lib.kda_input_projection_workspace_size(ctypes.byref(pd()), 4096)
+    act = (4096 * (2 * 128 + 32) * 4 + 255) // 256 * 256
+    assert need == act + (32 << 20)
+    assert lib.kda_input_projection_workspace_size(ctypes.byref(pd(rank=3)), 16) == ctypes.c_size_t(-1).value
 
 
 def test_workspace_size():

@@ -518,3 +518,50 @@ def test_long_prefill_chained_equals_single_shot():
     oc, ch = head_channels(wl, heads)
     _check("out (head 9)", chained[..., oc], ref["out"], TOL["bf16"])
     _check("state (head 9)", st[:, heads], ref["state"], TOL["bf16"])
+
+
+# ---------------------------------------------------------------------------
+# Input projection ahead of the layer
+# ---------------------------------------------------------------------------
+
+def _gpu_projection(wl, inp, out_dtype, rows=None):
+    ot = abi.KDA_BF16 if out_dtype == torch.bfloat16 else abi.KDA_F32
+    dev = {k: TT.to_device(v, "bf16", DEV) for k, v in inp.items()}
+    proj = abi.KdaProjection(H=wl.H, D=wl.d, hidden=wl.hidden, rank=wl.rank, out_dtype=ot, w_in=dev["w_in"],
+                             w_fb=dev["w_fb"], w_gb=dev["w_gb"])
+    HD = wl.H * wl.d
+    out = {"qkv": torch.empty((wl.T, 3 * HD), dtype=out_dtype, device=DEV),
+           "f": torch.empty((wl.T, HD), dtype=out_dtype, device=DEV),
+           "beta": torch.empty((wl.T, wl.H), dtype=out_dtype, device=DEV),
+           "g_out": torch.empty((wl.T, HD), dtype=out_dtype, device=DEV)}
+    ws = torch.empty(abi.kda_input_projection_workspace_size(proj, wl.T), dtype=torch.uint8, device=DEV)
+    abi.kda_input_projection(proj, dev["x"], out["qkv"], out["f"], out["beta"], out["g_out"], ws)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("T", [100, 1, 64])
+def test_input_projection_small(T):
+    from dataclasses import replace
+    wl = replace(I.PROJ_WORKLOADS["projection_t4096"], T=T, hidden=256, H=4, seed=60 + T)
+    say(f"case input projection T={T} hidden=256 H=4 d=128 rank=128")
+    inp = I.generate_projection(wl)
+    ref = O.kda_input_projection(inp["x"], inp["w_in"], inp["w_fb"], inp["w_gb"], wl.H, wl.d, wl.rank)
+    out = _gpu_projection(wl, inp, torch.float32)
+    for k in ("qkv", "f", "beta", "g_out"):
+        _check(k, out[k], ref[k], TOL["bf16"])
+    out16 = _gpu_projection(wl, inp, torch.bfloat16)
+    for k in ("qkv", "f", "beta", "g_out"):
+        _check(f"{k} (bf16 output)", out16[k], ref[k], TOL_BF16_OUT)
+
+
+def test_input_projection_full_size_sampled_rows():
+    wl = I.PROJ_WORKLOADS["projection_t4096"]
+    say("case input projection full size (T=4096, hidden=4096, H=32, d=128, rank=128), 48 sampled rows")
+    inp = I.generate_projection(wl)
+    out = _gpu_projection(wl, inp, torch.float32)
+    rows = np.random.default_rng(0).choice(wl.T, 48, replace=False)
+    ref = O.kda_input_projection(inp["x"][rows], inp["w_in"], inp["w_fb"], inp["w_gb"], wl.H, wl.d, wl.rank)
+    idx = torch.from_numpy(rows).to(DEV)
+    for k in ("qkv", "f", "beta", "g_out"):
+        _check(k, out[k].index_select(0, idx), ref[k], TOL["bf16"])

@@ -507,6 +507,41 @@ def test_varlen_rejects_bad_tables(cu, slots):
                              np.zeros((3, wl.c_qkv, wl.W - 1)))
 
 
+def _proj_weights(H, d, r, hidden, rng):
+    n = 3 * H * d + 2 * r + H
+    return (rng.standard_normal((n, hidden)), rng.standard_normal((H * d, r)), rng.standard_normal((H * d, r)))
+
+
+def test_projection_one_hot_rows_select_weight_columns():
+    # x = identity: row i of every output is what weight column i maps to; the low-rank path equals
+    # the product of its two Linear maps taken the other way round (associativity)
+    H, d, r, hidden = 2, 16, 8, 12
+    rng = np.random.default_rng(5)
+    w_in, w_fb, w_gb = _proj_weights(H, d, r, hidden, rng)
+    out = O.kda_input_projection(np.eye(hidden), w_in, w_fb, w_gb, H, d, r)
+    HD = H * d
+    np.testing.assert_array_equal(out["qkv"], w_in[:3 * HD].T)
+    np.testing.assert_allclose(out["f"], (w_fb @ w_in[3 * HD:3 * HD + r]).T, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out["g_out"], (w_gb @ w_in[3 * HD + r:3 * HD + 2 * r]).T, rtol=1e-12, atol=1e-12)
+    b = w_in[3 * HD + 2 * r:].T
+    np.testing.assert_allclose(out["beta"], 0.5 + 0.5 * np.tanh(b / 2), rtol=1e-14)
+
+
+def test_projection_zero_and_linearity():
+    H, d, r, hidden = 2, 16, 8, 12
+    rng = np.random.default_rng(6)
+    w_in, w_fb, w_gb = _proj_weights(H, d, r, hidden, rng)
+    z = O.kda_input_projection(np.zeros((3, hidden)), w_in, w_fb, w_gb, H, d, r)
+    for k in ("qkv", "f", "g_out"):
+        assert np.all(z[k] == 0.0)
+    assert np.all(z["beta"] == 0.5)
+    x = rng.standard_normal((5, hidden))
+    a = O.kda_input_projection(x, w_in, w_fb, w_gb, H, d, r)
+    b = O.kda_input_projection(2.0 * x, w_in, w_fb, w_gb, H, d, r)
+    for k in ("qkv", "f", "g_out"):
+        np.testing.assert_allclose(b[k], 2.0 * a[k], rtol=1e-13, atol=1e-13)
+
+
 def test_missing_gate_lower_bound_is_an_error():
     wl, inp, p = _tiny(4)
     p.lb = float("nan")
