@@ -14,12 +14,14 @@ typedef uint16_t bf16_t;
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
 
-__device__ __forceinline__ bf16_t f32_to_bf16(float x) {
-  // round to nearest even; NaN stays NaN (quiet bit forced)
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+// Round to nearest even on the hardware conversion (v_cvt_pk_bf16_f32); NaN stays NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float x) { return __builtin_bit_cast(bf16_t, (__bf16)x); }
+
+// Two values rounded as above into one 32-bit word, a in the low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ void store_as(float* p, float v) { *p = v; }

@@ -1166,10 +1166,10 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
 // 8 columns per lane, 16-byte loads and stores.
 __device__ __forceinline__ void store8(bf16_t* p, const float (&v)[8]) {
   uint4 u;
-  u.x = f32_to_bf16(v[0]) | (uint32_t)f32_to_bf16(v[1]) << 16;
-  u.y = f32_to_bf16(v[2]) | (uint32_t)f32_to_bf16(v[3]) << 16;
-  u.z = f32_to_bf16(v[4]) | (uint32_t)f32_to_bf16(v[5]) << 16;
-  u.w = f32_to_bf16(v[6]) | (uint32_t)f32_to_bf16(v[7]) << 16;
+  u.x = pack_bf16x2(v[0], v[1]);
+  u.y = pack_bf16x2(v[2], v[3]);
+  u.z = pack_bf16x2(v[4], v[5]);
+  u.w = pack_bf16x2(v[6], v[7]);
   *reinterpret_cast<uint4*>(p) = u;
 }
 __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {

@@ -27,7 +27,7 @@ constexpr int PJ_ROWS = 64;    // token rows per workgroup (16 per wave)
 constexpr int PJ_COLS = 128;   // output columns per workgroup
 constexpr int PJ_NT = 256;
 constexpr int PJ_PB = kProjRank + 8;    // LDS pitch of a weight row (bf16), spreads the banks
-constexpr int PJ_PO = PJ_COLS + 4;      // LDS pitch of an output row (fp32)
+constexpr int PJ_XCD = 8;               // L2 domains the workgroups are dealt over, round robin
 
 __device__ __forceinline__ f32x4 pj_mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -35,95 +35,110 @@ __device__ __forceinline__ f32x4 pj_mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ void pj_store(float* p, float v) { *p = v; }
 __device__ __forceinline__ void pj_store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
-__device__ __forceinline__ void pj_store8(float* p, const float* v) {
+// four consecutive outputs of one token
+__device__ __forceinline__ void pj_store4(float* p, f32x4 v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
-__device__ __forceinline__ void pj_store8(bf16_t* p, const float* v) {
-  uint4 u;
-  u.x = f32_to_bf16(v[0]) | (uint32_t)f32_to_bf16(v[1]) << 16;
-  u.y = f32_to_bf16(v[2]) | (uint32_t)f32_to_bf16(v[3]) << 16;
-  u.z = f32_to_bf16(v[4]) | (uint32_t)f32_to_bf16(v[5]) << 16;
-  u.w = f32_to_bf16(v[6]) | (uint32_t)f32_to_bf16(v[7]) << 16;
-  *reinterpret_cast<uint4*>(p) = u;
+__device__ __forceinline__ void pj_store4(bf16_t* p, f32x4 v) {
+  uint2 u;
+  u.x = pack_bf16x2(v[0], v[1]);
+  u.y = pack_bf16x2(v[2], v[3]);
+  *reinterpret_cast<uint2*>(p) = u;
 }
 
 // out[T, HD] = act[T, R] . W^T for W [HD, R] (a Linear weight), act the fp32 rank activations
-// (columns act_col .. act_col + R - 1 of the workspace rows, leading dimension ld).  blockIdx.z
-// selects f (0) or g (1); the z = 0 workgroups of column block 0 also write beta.
+// (columns which*R .. which*R + R - 1 of the workspace rows, leading dimension ld), f for which = 0
+// and g for which = 1.  A workgroup multiplies one 64-token tile by one 128-column block of W held
+// in LDS.  The product is taken transposed (out^T tile = W tile . act^T) so that each lane ends
+// with four consecutive output columns of one token and stores them directly.
+//
+// Workgroup b runs on L2 domain b % 8 and takes a row tile = b % 8 modulo 8, so one domain's L2
+// holds the activations of its own row tiles only, beside the 2 MB of weights; within a domain
+// the (column block, which) pairs run fastest.  The workgroups of column block 0 of f also write
+// beta = sigmoid(b x) for their tile.
 template <typename OT>
 __global__ __launch_bounds__(PJ_NT) void kda_proj_lowrank_kernel(const float* __restrict__ act, int ld, int T,
                                                                  int HD, int H, const bf16_t* __restrict__ w_fb,
                                                                  const bf16_t* __restrict__ w_gb, OT* __restrict__ f,
                                                                  OT* __restrict__ g, OT* __restrict__ beta) {
   constexpr int R = kProjRank;
-  // the weight block, then (after every read of it) the output rows
-  static_assert(PJ_ROWS * PJ_PO * 4 <= PJ_COLS * PJ_PB * 2, "output rows fit in the weight block");
   __shared__ __align__(16) __bf16 sW[PJ_COLS * PJ_PB];
-  float* sO = reinterpret_cast<float*>(sW);
-  const int which = blockIdx.z;
-  const int r0 = blockIdx.y * PJ_ROWS, c0 = blockIdx.x * PJ_COLS;
+  const int ncb2 = 2 * (HD / PJ_COLS);
+  const int xcd = blockIdx.x % PJ_XCD, k = blockIdx.x / PJ_XCD;
+  const int r0 = ((k / ncb2) * PJ_XCD + xcd) * PJ_ROWS;
+  if (r0 >= T) return;  // the spare workgroups of the last domains
+  const int which = k % 2, c0 = ((k % ncb2) / 2) * PJ_COLS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const bf16_t* W = which == 0 ? w_fb : w_gb;
   OT* out = which == 0 ? f : g;
-  const int acol = which * R;
 
-  // the weight rows of this column block into LDS: 16-byte pieces, 16 per row
-  for (int i = tid; i < PJ_COLS * (R / 8); i += PJ_NT) {
-    const int row = i / (R / 8), seg = i % (R / 8);
-    *reinterpret_cast<uint4*>(sW + row * PJ_PB + seg * 8) =
-        *reinterpret_cast<const uint4*>(W + (long long)(c0 + row) * R + seg * 8);
+  // the weight rows of this column block, 16-byte pieces (16 per row): all loads, then the LDS writes
+  constexpr int NW = PJ_COLS * (R / 8) / PJ_NT;
+  uint4 wv[NW];
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const int i = tid + j * PJ_NT, row = i / (R / 8), seg = i % (R / 8);
+    wv[j] = *reinterpret_cast<const uint4*>(W + (long long)(c0 + row) * R + seg * 8);
   }
-  // this wave's 16 activation rows as split A operands (rows past T read row T-1; not stored)
-  const int arow = min(r0 + 16 * wave + l16, T - 1);
-  const float* ap = act + (long long)arow * ld + acol + 8 * lg;
-  bf16x8 ahi[R / 32], alo[R / 32];
+  // this wave's 16 activation rows (rows past T read row T-1 and are not stored)
+  const int trow = r0 + 16 * wave + l16;
+  const float* ap = act + (long long)min(trow, T - 1) * ld + which * R + 8 * lg;
+  float4 xv[R / 32][2];
 #pragma unroll
   for (int s = 0; s < R / 32; ++s) {
-    const float4 x0 = *reinterpret_cast<const float4*>(ap + 32 * s);
-    const float4 x1 = *reinterpret_cast<const float4*>(ap + 32 * s + 4);
-    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    xv[s][0] = *reinterpret_cast<const float4*>(ap + 32 * s);
+    xv[s][1] = *reinterpret_cast<const float4*>(ap + 32 * s + 4);
+  }
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const int i = tid + j * PJ_NT, row = i / (R / 8), seg = i % (R / 8);
+    *reinterpret_cast<uint4*>(sW + row * PJ_PB + seg * 8) = wv[j];
+  }
+  // split B operands: fp32 activations as bf16 hi + lo
+  bf16x8 xhi[R / 32], xlo[R / 32];
+#pragma unroll
+  for (int s = 0; s < R / 32; ++s) {
+    const float x[8] = {xv[s][0].x, xv[s][0].y, xv[s][0].z, xv[s][0].w,
+                        xv[s][1].x, xv[s][1].y, xv[s][1].z, xv[s][1].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const __bf16 hi = (__bf16)x[e];
-      ahi[s][e] = hi;
-      alo[s][e] = (__bf16)(x[e] - (float)hi);
+      xhi[s][e] = hi;
+      xlo[s][e] = (__bf16)(x[e] - (float)hi);
     }
   }
   __syncthreads();
   f32x4 acc[PJ_COLS / 16];
 #pragma unroll
-  for (int ct = 0; ct < PJ_COLS / 16; ++ct) {
-    acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < PJ_COLS / 16; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < R / 32; ++s) {
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(sW + (16 * ct + l16) * PJ_PB + 32 * s + 8 * lg);
-      acc[ct] = pj_mfma(alo[s], b, acc[ct]);
-      acc[ct] = pj_mfma(ahi[s], b, acc[ct]);
+  for (int s = 0; s < R / 32; ++s)
+#pragma unroll
+    for (int ct = 0; ct < PJ_COLS / 16; ++ct) {
+      const bf16x8 w = *reinterpret_cast<const bf16x8*>(sW + (16 * ct + l16) * PJ_PB + 32 * s + 8 * lg);
+      acc[ct] = pj_mfma(w, xlo[s], acc[ct]);
+      acc[ct] = pj_mfma(w, xhi[s], acc[ct]);
     }
+  // lane: output columns 16 ct + 4 lg .. + 3 of token trow
+  if (trow < T) {
+    OT* orow = out + (long long)trow * HD + c0 + 4 * lg;
+#pragma unroll
+    for (int ct = 0; ct < PJ_COLS / 16; ++ct) pj_store4(orow + 16 * ct, acc[ct]);
   }
-  // accumulator tiles (lane: rows 4 lg .. 4 lg + 3 of column l16) -> LDS rows -> 16-byte stores
-  __syncthreads();  // every read of the weight block is done
+  if (which == 0 && c0 == 0) {
+    for (int i0 = 0; i0 < PJ_ROWS * H; i0 += 4 * PJ_NT) {
+      float z[4];
 #pragma unroll
-  for (int ct = 0; ct < PJ_COLS / 16; ++ct)
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + tid + e * PJ_NT, row = r0 + i / H;
+        z[e] = (i < PJ_ROWS * H && row < T) ? act[(long long)row * ld + 2 * R + i % H] : 0.f;
+      }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sO[(16 * wave + 4 * lg + r) * PJ_PO + 16 * ct + l16] = acc[ct][r];
-  __syncthreads();
-  for (int i = tid; i < PJ_ROWS * (PJ_COLS / 8); i += PJ_NT) {
-    const int row = i / (PJ_COLS / 8), c8 = (i % (PJ_COLS / 8)) * 8;
-    if (r0 + row >= T) continue;
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = sO[row * PJ_PO + c8 + e];
-    pj_store8(out + (long long)(r0 + row) * HD + c0 + c8, v);
-  }
-  if (which == 0 && blockIdx.x == 0) {
-    for (int i = tid; i < PJ_ROWS * H; i += PJ_NT) {
-      const int row = i / H, hh = i % H;
-      if (r0 + row >= T) continue;
-      const float z = act[(long long)(r0 + row) * ld + 2 * R + hh];
-      pj_store(beta + (long long)(r0 + row) * H + hh, 1.0f / (1.0f + __expf(-z)));
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + tid + e * PJ_NT, row = r0 + i / H;
+        if (i < PJ_ROWS * H && row < T) pj_store(beta + (long long)row * H + i % H, 1.0f / (1.0f + __expf(-z[e])));
+      }
     }
   }
 }
@@ -237,7 +252,9 @@ hipError_t launch_projection(const ProjArgs& p, hipStream_t s, char* err, size_t
   if (!gemm_xwt(p.T, p.hidden, NS, p.x, w + (long long)N3 * p.hidden, HIP_R_32F, act, NS, gws, gwsb, s,
                 "hipblaslt_gemm[rank|beta]", err, errlen))
     return hipErrorUnknown;
-  const dim3 grid(HD / PJ_COLS, (p.T + PJ_ROWS - 1) / PJ_ROWS, 2);
+  // per domain ceil(tiles / 8) row tiles, times the (column block, which) pairs
+  const int tiles = (p.T + PJ_ROWS - 1) / PJ_ROWS;
+  const dim3 grid(((tiles + PJ_XCD - 1) / PJ_XCD) * PJ_XCD * 2 * (HD / PJ_COLS));
   timing_begin("kda_proj_lowrank_kernel", s);
   if (p.out_type == kBF16)
     kda_proj_lowrank_kernel<bf16_t><<<grid, PJ_NT, 0, s>>>(
