@@ -47,6 +47,7 @@ class Workload:
     prefix_T: int = 0  # tokens run before the step under test (pre-filled state)
     splits: int = 1    # number of chained calls the T tokens are split into
     lb: float = -5.0
+    gate: str = "sigmoid"  # "sigmoid" (bounded by lb) or "softplus" (no bound: lb is absent, NaN)
 
     @property
     def c_qkv(self) -> int:
@@ -136,7 +137,8 @@ def generate(wl: Workload) -> dict:
         "g_out": round_to_io(_normal(r["g_out"], (B, TT, H * dv)), io),
         "norm_w": round_to_io(r["norm_w"].random(size=(dv,), dtype=np.float32) + np.float32(0.5), io),
         "accepted": r["accepted"].integers(0, wl.T + 1, size=(B,)).astype(np.int32),
-        "lb": float(wl.lb),
+        "lb": float(wl.lb) if wl.gate == "sigmoid" else float("nan"),
+        "gate": wl.gate,
         "scale": float(dk) ** -0.5,
         "state0": np.zeros((B, H, dk, dv), dtype=np.float32),
         "conv_state0": np.zeros((B, wl.c_qkv, W - 1), dtype=np.float32),

@@ -36,6 +36,11 @@ design notes):
 
 * gate:   g = lb * sigmoid(exp(A_log[h]) * (f + dt_bias)), alpha = exp(g),
           so the per-step log-decay lies in (lb, 0).
+* softplus branch (llama.cpp PR #27754, metadata commit: kimi-k3 takes a
+          softplus branch, a different function, when kda.gate_lower_bound is
+          absent; the page gives no formula): g = -exp(A_log[h]) *
+          softplus(f + dt_bias), the same parameters with the softplus in place
+          of the bounded sigmoid and A as the decay rate; unbounded below.
 * update: S <- Diag(alpha) S ; u = beta * (v - S^T k) ; S <- S + k u^T ;
           o = S^T q  (output read after the update).
 * conv:   causal, no bias, tap W-1 multiplies the current token; the conv
@@ -57,6 +62,7 @@ __all__ = [
     "causal_depthwise_conv",
     "silu",
     "sigmoid",
+    "softplus",
     "l2_normalize",
     "decay_gate",
     "gated_rmsnorm",
@@ -78,7 +84,9 @@ class KdaParams:
     A_log   [H]          per-head log of the decay rate A
     dt_bias [H*dk]       per-channel bias added to f before the head reshape
     norm_w  [dv]         output RMSNorm weight (plain weight, not 1 + w)
-    lb                   kda.gate_lower_bound (must be finite)
+    lb                   kda.gate_lower_bound (finite for the bounded gate; NaN,
+                         i.e. absent, for the softplus branch)
+    gate                 "sigmoid" (the bounded gate) or "softplus"
     """
 
     H: int
@@ -90,6 +98,7 @@ class KdaParams:
     norm_w: np.ndarray
     lb: float
     scale: float = 1.0
+    gate: str = "sigmoid"
     l2_eps: float = 1e-6
     rms_eps: float = 1e-5
     extra: dict = field(default_factory=dict)
@@ -116,6 +125,13 @@ def sigmoid(x: np.ndarray) -> np.ndarray:
     x = _f64(x)
     with np.errstate(over="ignore"):
         return 1.0 / (1.0 + np.exp(-x))
+
+
+def softplus(x: np.ndarray) -> np.ndarray:
+    """ln(1 + e^x) in float64, written as max(x, 0) + ln(1 + e^-|x|) so that neither
+    tail overflows (the two forms are equal for every x)."""
+    x = _f64(x)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
 
 
 def silu(y: np.ndarray) -> np.ndarray:
@@ -162,21 +178,28 @@ def l2_normalize(x: np.ndarray, eps: float) -> np.ndarray:
     return x / np.maximum(n, eps)
 
 
-def decay_gate(f: np.ndarray, A_log: np.ndarray, dt_bias: np.ndarray, lb: float, H: int, dk: int):
-    """Per-channel log-decay g and decay alpha = exp(g) for one sequence.
+def decay_gate(f: np.ndarray, A_log: np.ndarray, dt_bias: np.ndarray, lb: float, H: int, dk: int,
+               kind: str = "sigmoid"):
+    """Per-channel log-decay g (the decay is alpha = exp(g)) for one sequence.
 
     llama.cpp PR #27754, KDA commit: a bounded-sigmoid decay gate; dt_bias is
     added per channel before the reshape to heads; A is per head and
     broadcast over the head's channels; kda.gate_lower_bound bounds it.
 
     f [T, H*dk] -> g [T, H, dk] with g = lb * sigmoid(exp(A_log[h]) * (f + dt_bias)),
-    which lies in (lb, 0) for lb < 0.
+    which lies in (lb, 0) for lb < 0.  kind "softplus" (the branch taken when
+    the bound is absent, metadata commit): g = -exp(A_log[h]) * softplus(f + dt_bias),
+    in (-inf, 0).
     """
     f = _f64(f)
     T = f.shape[0]
     z = (f + _f64(dt_bias)[None, :]).reshape(T, H, dk)
     A = np.exp(_f64(A_log))[None, :, None]
-    return float(lb) * sigmoid(A * z)
+    if kind == "sigmoid":
+        return float(lb) * sigmoid(A * z)
+    if kind == "softplus":
+        return -A * softplus(z)
+    raise ValueError(f"unknown gate kind {kind!r}")
 
 
 def gated_rmsnorm(o: np.ndarray, g_out: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
@@ -340,13 +363,21 @@ def prologue(p: KdaParams, qkv, f, conv_state):
     v = z[:, 2 * H * dk:].reshape(T, H, dv)
     q = p.scale * l2_normalize(q_hat, p.l2_eps)
     k = l2_normalize(k_hat, p.l2_eps)
-    g = decay_gate(f, p.A_log, p.dt_bias, p.lb, H, dk)
+    g = decay_gate(f, p.A_log, p.dt_bias, p.lb, H, dk, p.gate)
     return q, k, v, g, new_cs
 
 
 def _check_lb(p: KdaParams):
-    if not np.isfinite(p.lb):
-        raise ValueError("gate_lower_bound is required and must be finite")
+    """The branch follows the bound's presence (metadata commit): the bounded gate needs a
+    finite kda.gate_lower_bound; the softplus branch is the one taken when it is absent (NaN)."""
+    if p.gate == "sigmoid":
+        if not np.isfinite(p.lb):
+            raise ValueError("gate_lower_bound is required and must be finite")
+    elif p.gate == "softplus":
+        if not np.isnan(p.lb):
+            raise ValueError("the softplus branch is the one without gate_lower_bound (pass NaN)")
+    else:
+        raise ValueError(f"unknown gate kind {p.gate!r}")
 
 
 def kda_layer(p: KdaParams, qkv, f, beta, g_out, state, conv_state, *,

@@ -38,7 +38,8 @@ def rel_err(x, ref) -> float:
 
 def params(wl: I.Workload, inp: dict) -> O.KdaParams:
     return O.KdaParams(H=wl.H, dk=wl.dk, dv=wl.dv, conv_w=inp["conv_w"], A_log=inp["A_log"],
-                       dt_bias=inp["dt_bias"], norm_w=inp["norm_w"], lb=inp["lb"], scale=inp["scale"])
+                       dt_bias=inp["dt_bias"], norm_w=inp["norm_w"], lb=inp["lb"], scale=inp["scale"],
+                       gate=inp["gate"])
 
 
 def oracle_layer(wl, inp, t0, t1, state, conv_state, form="token", record_states=False):

@@ -11,6 +11,8 @@ import json
 import math
 import os
 
+from dataclasses import replace
+
 import mpmath
 import numpy as np
 import pytest
@@ -38,7 +40,8 @@ def rand_recurrence_inputs(T, H, dk, dv, rng, lb=-5.0):
 
 def params_for(wl, inp):
     return O.KdaParams(H=wl.H, dk=wl.dk, dv=wl.dv, conv_w=inp["conv_w"], A_log=inp["A_log"],
-                       dt_bias=inp["dt_bias"], norm_w=inp["norm_w"], lb=inp["lb"], scale=inp["scale"])
+                       dt_bias=inp["dt_bias"], norm_w=inp["norm_w"], lb=inp["lb"], scale=inp["scale"],
+                       gate=inp["gate"])
 
 
 # ---------------------------------------------------------------------------
@@ -125,6 +128,89 @@ def test_decay_gate_range_bias_order_and_head_broadcast():
     np.testing.assert_array_equal(g0, np.full((1, H, dk), -2.5))
     # lb = 0 switches the decay off exactly (alpha = 1).
     assert np.all(np.exp(O.decay_gate(f, A_log, dt, 0.0, H, dk)) == 1.0)
+
+
+def test_softplus_against_mpmath_and_tails():
+    mpmath.mp.dps = 40
+    for xv in (-700.0, -40.0, -5.0, -1.0, 0.0, 1e-8, 0.5, 3.0, 30.0, 700.0):
+        ref = mpmath.log1p(mpmath.exp(mpmath.mpf(xv)))
+        assert abs(O.softplus(np.array([xv]))[0] - float(ref)) <= 1e-15 * float(ref)
+    # softplus(x) - softplus(-x) = x (the function is x plus its mirror image)
+    x = RNG.standard_normal(50) * 20
+    np.testing.assert_allclose(O.softplus(x) - O.softplus(-x), x, rtol=1e-13, atol=1e-13)
+
+
+def test_softplus_gate_closed_forms_bias_order_and_head_broadcast():
+    # The branch taken without a lower bound (llama.cpp PR #27754, metadata commit); reading:
+    # g = -exp(A_log[h]) * softplus(f + dt_bias).
+    H, dk, T = 3, 4, 5
+    A_log = RNG.uniform(0, math.log(16), H)
+    A = np.exp(A_log)
+    # f + dt_bias = 0: g = -A ln 2 (A outside the softplus: -softplus(A z) would give -ln 2)
+    g0 = O.decay_gate(np.zeros((1, H * dk)), A_log, np.zeros(H * dk), float("nan"), H, dk, "softplus")
+    np.testing.assert_allclose(g0[0], np.repeat(-A * math.log(2.0), dk).reshape(H, dk), rtol=1e-15)
+    # large arguments: g = -A (z + e^-z) to rounding; unbounded below (no clamp at any lb)
+    z = 30.0
+    gz = O.decay_gate(np.full((1, H * dk), z), A_log, np.zeros(H * dk), float("nan"), H, dk, "softplus")
+    np.testing.assert_allclose(gz[0], np.repeat(-A * (z + math.exp(-z)), dk).reshape(H, dk), rtol=1e-15)
+    g500 = O.decay_gate(np.full((1, H * dk), 500.0), A_log, np.zeros(H * dk), float("nan"), H, dk, "softplus")
+    assert np.all(g500 <= -500.0)
+    # very negative arguments: g = -A e^z (nearly no decay, still strictly negative)
+    gn = O.decay_gate(np.full((1, H * dk), -40.0), A_log, np.zeros(H * dk), float("nan"), H, dk, "softplus")
+    np.testing.assert_allclose(gn[0], np.repeat(-A * math.exp(-40.0), dk).reshape(H, dk), rtol=1e-12)
+    assert np.all(gn < 0)
+    # dt_bias per channel before the reshape; A per head
+    f = RNG.standard_normal((T, H * dk))
+    dt = RNG.normal(0, 0.1, H * dk)
+    g = O.decay_gate(f, A_log, dt, float("nan"), H, dk, "softplus")
+    dt2 = dt.copy()
+    dt2[2 * dk + 1] -= 2.0
+    g2 = O.decay_gate(f, A_log, dt2, float("nan"), H, dk, "softplus")
+    assert np.argwhere(np.any(g2 != g, axis=0)).tolist() == [[2, 1]]
+    A2 = A_log.copy()
+    A2[0] += 0.25
+    g3 = O.decay_gate(f, A2, dt, float("nan"), H, dk, "softplus")
+    assert np.all(g3[:, 1:] == g[:, 1:]) and np.all(g3[:, 0] < g[:, 0])
+
+
+def test_softplus_branch_follows_the_bound_being_absent():
+    wl, inp, p = _tiny(6, gate="softplus")
+    assert math.isnan(p.lb) and p.gate == "softplus"
+    O.kda_layer(p, inp["qkv"], inp["f"], inp["beta"], inp["g_out"], inp["state0"], inp["conv_state0"])
+    for bad in (replace(p, lb=-5.0), replace(p, gate="tanh"), replace(p, gate="sigmoid")):
+        with pytest.raises(ValueError):
+            O.kda_layer(bad, inp["qkv"], inp["f"], inp["beta"], inp["g_out"], inp["state0"], inp["conv_state0"])
+
+
+def test_softplus_strong_decay_forgets_the_state():
+    # f + dt_bias = 300: g = -300 A <= -300 per token, alpha ~ 1e-130: each token starts from an empty
+    # state, so o_t = scale * beta_t (q^_t . k^_t) v_t with the normalised q^, k (the one-token closed form)
+    wl, inp, p = _tiny(7, gate="softplus")
+    f = np.full_like(inp["f"], 300.0)
+    S0 = RNG.standard_normal(inp["state0"].shape)
+    r = O.kda_layer(p, inp["qkv"], f, inp["beta"], inp["g_out"], S0, inp["conv_state0"])
+    q, k, v, g, _ = O.prologue(p, inp["qkv"][0], f[0], inp["conv_state0"][0])
+    assert np.all(g <= -300.0)
+    beta = inp["beta"][0]
+    o_ref = np.einsum("thc,thc->th", q, k)[:, :, None] * beta[:, :, None] * v
+    np.testing.assert_allclose(r["o"][0], o_ref, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_softplus_chunked_equals_token_and_split_is_exact(chunk):
+    # the chunked spelling with pairwise decay factors stays finite under unbounded decay
+    wl, inp, p = _tiny(45, gate="softplus")
+    S0 = RNG.standard_normal(inp["state0"].shape)
+    tok = O.kda_layer(p, inp["qkv"], inp["f"], inp["beta"], inp["g_out"], S0, inp["conv_state0"])
+    ch = O.kda_layer(p, inp["qkv"], inp["f"], inp["beta"], inp["g_out"], S0, inp["conv_state0"],
+                     form="chunked", chunk=chunk)
+    assert np.all(np.isfinite(ch["out"]))
+    np.testing.assert_allclose(ch["out"], tok["out"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(ch["state"], tok["state"], rtol=1e-10, atol=1e-12)
+    a, b = I.split_tokens(inp, 0, 20), I.split_tokens(inp, 20, 45)
+    r1 = O.kda_layer(p, a["qkv"], a["f"], a["beta"], a["g_out"], S0, inp["conv_state0"])
+    r2 = O.kda_layer(p, b["qkv"], b["f"], b["beta"], b["g_out"], r1["state"], r1["conv_state"])
+    np.testing.assert_array_equal(np.concatenate([r1["out"], r2["out"]], axis=1), tok["out"])
 
 
 def test_gated_rmsnorm_closed_forms():
