@@ -24,6 +24,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "kda.h")
 
 KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
 KDA_F32, KDA_BF16 = 0, 1
+KDA_GATE_BOUNDED_SIGMOID, KDA_GATE_SOFTPLUS = 0, 1
 _TORCH_OF = {KDA_F32: torch.float32, KDA_BF16: torch.bfloat16}
 
 
@@ -39,6 +40,7 @@ class KdaLayerDesc(ctypes.Structure):
         ("chunk_size", c_int32), ("io_dtype", c_int32), ("out_dtype", c_int32),
         ("gate_lower_bound", c_float), ("l2_eps", c_float), ("rms_eps", c_float), ("scale", c_float),
         ("conv_w", c_void_p), ("A_log", c_void_p), ("dt_bias", c_void_p), ("norm_w", c_void_p),
+        ("gate_kind", c_int32),
     ]
 
 
@@ -135,6 +137,7 @@ class KdaLayer:
     norm_w: torch.Tensor
     l2_eps: float = 1e-6
     rms_eps: float = 1e-5
+    gate_kind: int = 0  # KDA_GATE_BOUNDED_SIGMOID; KDA_GATE_SOFTPLUS (1) takes lb = NaN
 
     def __post_init__(self):
         io = _TORCH_OF[self.io_dtype]
@@ -145,7 +148,7 @@ class KdaLayer:
         _expect(self.norm_w, (self.D,), io, "norm_w")
         self.desc = KdaLayerDesc(self.H, self.D, self.D, self.W, self.chunk, self.io_dtype, self.out_dtype,
                                  self.lb, self.l2_eps, self.rms_eps, self.scale, _ptr(self.conv_w),
-                                 _ptr(self.A_log), _ptr(self.dt_bias), _ptr(self.norm_w))
+                                 _ptr(self.A_log), _ptr(self.dt_bias), _ptr(self.norm_w), self.gate_kind)
 
     @property
     def c_qkv(self) -> int:

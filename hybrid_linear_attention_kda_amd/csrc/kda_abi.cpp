@@ -63,9 +63,19 @@ kda_status check_desc(const kda_layer_desc* d) {
     return fail(KDA_ERR_UNSUPPORTED, "conv_width %d > %d", d->conv_width, kda::kMaxConvWidth);
   if ((d->io_dtype != KDA_F32 && d->io_dtype != KDA_BF16) || (d->out_dtype != KDA_F32 && d->out_dtype != KDA_BF16))
     return fail(KDA_ERR_INVALID_ARGUMENT, "io_dtype / out_dtype must be KDA_F32 or KDA_BF16");
-  if (std::isnan(d->gate_lower_bound))
-    return fail(KDA_ERR_INVALID_ARGUMENT, "gate_lower_bound is absent (NaN); it is required");
-  if (!std::isfinite(d->gate_lower_bound)) return fail(KDA_ERR_INVALID_ARGUMENT, "gate_lower_bound is not finite");
+  if (d->gate_kind == KDA_GATE_BOUNDED_SIGMOID) {
+    if (std::isnan(d->gate_lower_bound))
+      return fail(KDA_ERR_INVALID_ARGUMENT,
+                  "gate_lower_bound is absent (NaN); the bounded gate requires it (the softplus branch is "
+                  "gate_kind KDA_GATE_SOFTPLUS)");
+    if (!std::isfinite(d->gate_lower_bound)) return fail(KDA_ERR_INVALID_ARGUMENT, "gate_lower_bound is not finite");
+  } else if (d->gate_kind == KDA_GATE_SOFTPLUS) {
+    if (!std::isnan(d->gate_lower_bound))
+      return fail(KDA_ERR_INVALID_ARGUMENT,
+                  "gate_kind KDA_GATE_SOFTPLUS is the branch without a lower bound: gate_lower_bound must be NaN");
+  } else {
+    return fail(KDA_ERR_INVALID_ARGUMENT, "gate_kind %d is not a kda_gate_kind", d->gate_kind);
+  }
   if (!std::isfinite(d->l2_eps) || !(d->l2_eps > 0.f)) return fail(KDA_ERR_INVALID_ARGUMENT, "l2_eps must be > 0");
   if (!std::isfinite(d->rms_eps) || d->rms_eps < 0.f) return fail(KDA_ERR_INVALID_ARGUMENT, "rms_eps must be >= 0");
   if (!std::isfinite(d->scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
@@ -96,7 +106,8 @@ kda::LayerArgs make_args(const kda_layer_desc* d, int B, int T) {
   a.H = d->num_heads;
   a.D = d->head_dim_k;
   a.W = d->conv_width;
-  a.lb = d->gate_lower_bound;
+  a.gate = d->gate_kind;
+  a.lb = d->gate_kind == KDA_GATE_SOFTPLUS ? 0.f : d->gate_lower_bound;
   a.l2_eps = d->l2_eps;
   a.rms_eps = d->rms_eps;
   a.scale = d->scale;
@@ -109,7 +120,8 @@ kda::LayerArgs make_args(const kda_layer_desc* d, int B, int T) {
 
 // bf16 io at the model's head size runs the matrix-core prefill; everything else the fp32 form.
 bool mfma_path(const kda_layer_desc* d) {
-  return kda::prefill_mfma_supported(d->head_dim_k, d->chunk_size, d->io_dtype, d->conv_width, d->gate_lower_bound);
+  return d->gate_kind == KDA_GATE_BOUNDED_SIGMOID &&
+         kda::prefill_mfma_supported(d->head_dim_k, d->chunk_size, d->io_dtype, d->conv_width, d->gate_lower_bound);
 }
 
 kda_status launched(hipError_t e, const char* what) {

@@ -40,6 +40,14 @@ __device__ __forceinline__ void store_nt(float* p, float4 v) {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
+// Per-channel log-decay from x = f + dt_bias and A = exp(A_log[h]) (llama.cpp PR #27754, KDA and
+// metadata commits): gate 0, the bounded sigmoid lb * sigmoid(A x) in (lb, 0); gate 1, the softplus
+// branch -A * softplus(x) in (-inf, 0), softplus(x) = max(x, 0) + log(1 + e^-|x|).
+__device__ __forceinline__ float log_decay(int gate, float lb, float A, float x) {
+  if (gate == 0) return lb / (1.0f + expf(-A * x));
+  return -A * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))));
+}
+
 // Sum over the 64 lanes of a wavefront; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

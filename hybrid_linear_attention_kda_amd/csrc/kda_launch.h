@@ -17,6 +17,7 @@ enum IoType { kF32 = 0, kBF16 = 1 };
 // Arguments shared by the recurrent (decode / verify) kernels and the prefill kernels.
 struct LayerArgs {
   int B, T, H, D, W;
+  int gate;             // 0: bounded sigmoid with bound lb; 1: softplus branch (lb unused)
   float lb, l2_eps, rms_eps, scale;
   const void* qkv;      // [B, T, 3*H*D] io
   const void* f;        // [B, T, H*D] io

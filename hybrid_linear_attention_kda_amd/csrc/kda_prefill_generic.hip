@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
       const int t = idx / D, i = idx % D;
       const float fv = to_f32(fin[(tok0 + c0 + t) * H * D + (long long)h * D + i]) +
                        a.dt_bias[(long long)h * D + i];
-      sg[t * LP + i] = a.lb / (1.0f + expf(-Ah * fv));
+      sg[t * LP + i] = log_decay(a.gate, a.lb, Ah, fv);
     }
     for (int t = tid; t < L; t += NT) sbeta[t] = to_f32(bin[(tok0 + c0 + t) * H + h]);
     __syncthreads();

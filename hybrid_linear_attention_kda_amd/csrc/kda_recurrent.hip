@@ -12,8 +12,9 @@
 //
 // Per token (the layer as described in llama.cpp PR #27754, KDA commit):
 //   conv over this head's q|k|v channels from the rolling conv window, SiLU,
-//   q/k L2 normalisation with max(||x||, eps), q scale, bounded-sigmoid decay
-//   alpha = exp(lb * sigmoid(exp(A_log[h]) * (f + dt_bias))),
+//   q/k L2 normalisation with max(||x||, eps), q scale, decay
+//   alpha = exp(lb * sigmoid(exp(A_log[h]) * (f + dt_bias))) (bounded gate) or
+//   alpha = exp(-exp(A_log[h]) * softplus(f + dt_bias)) (softplus branch),
 //   S' = Diag(alpha) S  (key axis = rows),  u = beta (v - S'^T k),
 //   o = S'^T q + (q.k) u  (= (S' + k u^T)^T q, so S is swept only once),
 //   S = S' + k u^T,  out = o / sqrt(mean(o^2) + eps) * w * sigmoid(g_out).
@@ -145,8 +146,8 @@ __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerAr
         (part == 0 ? s_q[pb] : part == 1 ? s_k[pb] : s_v[pb])[i] = z;
       }
     }
-    // bounded-sigmoid decay gate (log-decay in (lb, 0)), per key channel
-    if (tid < D) s_alpha[pb][tid] = expf(a.lb / (1.0f + expf(-Ah * (fs[pj] + dtb))));
+    // decay gate (bounded sigmoid or the softplus branch), per key channel
+    if (tid < D) s_alpha[pb][tid] = expf(log_decay(a.gate, a.lb, Ah, fs[pj] + dtb));
     const float bt = bs[pj], gcur = gs[pj];
     if (MULTI && t + PF < T) load_token(pj, t + PF);  // refill the slot: issued before this token's stores
     __syncthreads();

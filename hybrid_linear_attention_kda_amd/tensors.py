@@ -30,7 +30,7 @@ def make_layer(wl: Workload, inp: dict, device, out: str = "f32", chunk: int = N
     """A KdaLayer whose parameters are the workload's, on `device`."""
     return abi.KdaLayer(
         H=wl.H, D=wl.dk, W=wl.W, chunk=chunk or wl.chunk, io_dtype=io_code(wl.io), out_dtype=io_code(out),
-        lb=inp["lb"], scale=inp["scale"],
+        lb=inp["lb"], scale=inp["scale"], gate_kind={"sigmoid": 0, "softplus": 1}[inp.get("gate", "sigmoid")],
         conv_w=to_device(inp["conv_w"], wl.io, device),
         A_log=torch.from_numpy(np.ascontiguousarray(inp["A_log"], dtype=np.float32)).to(device),
         dt_bias=torch.from_numpy(np.ascontiguousarray(inp["dt_bias"], dtype=np.float32)).to(device),

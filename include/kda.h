@@ -11,6 +11,10 @@
  *   4. a bounded-sigmoid per-channel log-decay
  *        g = gate_lower_bound * sigmoid(exp(A_log[h]) * (f + dt_bias)),
  *      dt_bias added per channel before the reshape to heads, A per head;
+ *      or, where kda.gate_lower_bound is absent, the softplus branch
+ *      (metadata commit of the same PR: a different function, not a missing
+ *      clamp; read here as g = -exp(A_log[h]) * softplus(f + dt_bias), no
+ *      lower bound), selected by gate_kind;
  *   5. per head a d_k x d_v fp32 state S (row = key channel) that decays on
  *      the key axis and takes a beta-weighted delta-rule update per token:
  *        S <- Diag(exp(g_t)) S;  u = beta_t (v_t - S^T k_t);  S <- S + k_t u^T;
@@ -40,10 +44,12 @@
  *   - Supported: d_k == d_v in {16, 32, 64, 128}; conv_width 1..8;
  *     prefill chunk_size in {16, 32, 64}.  Other shapes return
  *     KDA_ERR_UNSUPPORTED.  bf16 io with d = 128, chunk 64, conv width <= 4
- *     and a gate bound in [-5.5, -0.25] runs the bf16 matrix-core prefill;
- *     every other prefill runs the fp32 vector-ALU form (weaker decay keeps
- *     more of the state, which the matrix-core path's bf16 operands would
- *     carry past the 2e-3 tolerance over long sequences).
+ *     and a bounded gate with its bound in [-5.5, -0.25] runs the bf16
+ *     matrix-core prefill; every other prefill, the softplus branch included,
+ *     runs the fp32 vector-ALU form (weaker decay keeps more of the state,
+ *     which the matrix-core path's bf16 operands would carry past the 2e-3
+ *     tolerance over long sequences; unbounded decay breaks its sub-chunk
+ *     factoring, while the fp32 form uses pairwise decay factors).
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -55,7 +61,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum kda_status {
   KDA_OK = 0,
@@ -66,6 +72,11 @@ typedef enum kda_status {
 
 typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
+/* Decay gate (step 4).  KDA_GATE_BOUNDED_SIGMOID needs a finite gate_lower_bound;
+ * KDA_GATE_SOFTPLUS is the branch for a model without one, and takes
+ * gate_lower_bound = NaN (absent); any other combination is an error. */
+typedef enum kda_gate_kind { KDA_GATE_BOUNDED_SIGMOID = 0, KDA_GATE_SOFTPLUS = 1 } kda_gate_kind;
+
 /* Per-layer description.  Parameter pointers are device pointers. */
 typedef struct kda_layer_desc {
   int32_t num_heads;        /* H */
@@ -75,7 +86,7 @@ typedef struct kda_layer_desc {
   int32_t chunk_size;       /* prefill chunk length C */
   int32_t io_dtype;         /* kda_dtype */
   int32_t out_dtype;        /* kda_dtype */
-  float gate_lower_bound;   /* kda.gate_lower_bound: required, finite (NaN = absent -> error) */
+  float gate_lower_bound;   /* kda.gate_lower_bound: finite for the bounded gate, NaN (absent) for softplus */
   float l2_eps;             /* q/k L2 clamp, > 0 (1e-6 in the model) */
   float rms_eps;            /* output RMSNorm eps, >= 0 (1e-5 in the model) */
   float scale;              /* query scale applied after the L2 norm */
@@ -83,6 +94,7 @@ typedef struct kda_layer_desc {
   const float* A_log;       /* [H] fp32 */
   const float* dt_bias;     /* [H*d_k] fp32 */
   const void* norm_w;       /* [d_v] io_dtype, plain weight (not 1 + w) */
+  int32_t gate_kind;        /* kda_gate_kind (0, the bounded gate, when zero-initialised) */
 } kda_layer_desc;
 
 /* Version of this ABI (KDA_ABI_VERSION). */

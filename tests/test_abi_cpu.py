@@ -17,7 +17,7 @@ FAKE = 0x10000  # aligned, never dereferenced: validation fails or returns befor
 def desc(**kw):
     d = dict(num_heads=2, head_dim_k=16, head_dim_v=16, conv_width=4, chunk_size=16, io_dtype=0, out_dtype=0,
              gate_lower_bound=-5.0, l2_eps=1e-6, rms_eps=1e-5, scale=0.25, conv_w=FAKE, A_log=FAKE,
-             dt_bias=FAKE, norm_w=FAKE)
+             dt_bias=FAKE, norm_w=FAKE, gate_kind=0)
     d.update(kw)
     return abi.KdaLayerDesc(*[d[n] for n, _ in abi.KdaLayerDesc._fields_])
 
@@ -39,13 +39,19 @@ def test_library_exports_every_header_function():
                           "kda_timing_enable", "kda_timing_read"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     assert lib.kda_status_string(0) == b"ok"
 
 
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(gate_lower_bound=math.nan), abi.KDA_ERR_INVALID_ARGUMENT, b"gate_lower_bound is absent"),
     (dict(gate_lower_bound=math.inf), abi.KDA_ERR_INVALID_ARGUMENT, b"not finite"),
+    # the softplus branch is the one without a bound: a finite bound with it is an error, and so is
+    # a gate kind the header does not define
+    (dict(gate_kind=1), abi.KDA_ERR_INVALID_ARGUMENT, b"must be NaN"),
+    (dict(gate_kind=1, gate_lower_bound=math.inf), abi.KDA_ERR_INVALID_ARGUMENT, b"must be NaN"),
+    (dict(gate_kind=2), abi.KDA_ERR_INVALID_ARGUMENT, b"not a kda_gate_kind"),
+    (dict(gate_kind=-1, gate_lower_bound=math.nan), abi.KDA_ERR_INVALID_ARGUMENT, b"not a kda_gate_kind"),
     (dict(head_dim_v=8), abi.KDA_ERR_UNSUPPORTED, b"head_dim_k"),
     (dict(head_dim_k=48, head_dim_v=48), abi.KDA_ERR_UNSUPPORTED, b"head dim 48"),
     (dict(conv_width=9), abi.KDA_ERR_UNSUPPORTED, b"conv_width"),
@@ -62,6 +68,11 @@ def test_library_exports_every_header_function():
 def test_prefill_rejects_bad_descriptor(kw, status, needle):
     assert prefill(desc(**kw)) == status
     assert needle in abi.load().kda_last_error()
+
+
+def test_softplus_descriptor_passes_validation():
+    # a NaN bound with the softplus kind passes validation; B = 0 leaves nothing to launch
+    assert prefill(desc(gate_kind=1, gate_lower_bound=math.nan), B=0) == abi.KDA_OK
 
 
 def test_null_descriptor_and_bad_sizes():

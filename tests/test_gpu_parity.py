@@ -313,6 +313,77 @@ def test_tiny_fp32_conv_width_extremes_prefill_decode_tape(W):
 
 
 # ---------------------------------------------------------------------------
+# The softplus decay branch (no lower bound)
+# ---------------------------------------------------------------------------
+
+def test_softplus_tiny_fp32_prefill_decode_verify_rollback_tape():
+    # fp32 io: prefill 5 tokens, one decode step, then an 8-token draft block through the snapshot
+    # verify + rollback and through the tape verify + commit, all with the softplus gate
+    wl = I.WORKLOADS["tiny_fp32"].with_(T=8, B=4, prefix_T=6, gate="softplus", seed=50)
+    say("case tiny_fp32 softplus: prefill 5, decode 1, verify 8 + rollback, tape verify 8 + commit")
+    inp = I.generate(wl)
+    layer = TT.make_layer(wl, inp, DEV)
+    assert layer.gate_kind == abi.KDA_GATE_SOFTPLUS and np.isnan(layer.lb)
+    st, cs = _dev_state(wl, inp)
+    out = _gpu_prefill(wl, inp, layer, 0, 5, st, cs)
+    tok = TT.token_tensors(wl, inp, 5, 6, DEV)
+    out1 = torch.empty((4, 1, wl.H * wl.dv), dtype=torch.float32, device=DEV)
+    abi.kda_decode_step(layer, tok["qkv"], tok["f"], tok["beta"], tok["g_out"], st, cs, out1)
+    torch.cuda.synchronize()
+    ref = oracle_layer(wl, inp, 0, 6, inp["state0"], inp["conv_state0"])
+    _check("prefill out", out, ref["out"][:, :5], TOL["f32"])
+    _check("decode out", out1, ref["out"][:, 5:6], TOL["f32"])
+    _check("state", st, ref["state"], TOL["f32"])
+    _check("conv_state", cs, ref["conv_state"], 0.0)
+    S6, C6 = ref["state"].astype(np.float32), ref["conv_state"].astype(np.float32)
+    tok = TT.token_tensors(wl, inp, 6, 14, DEV)
+    snaps = torch.empty((4, 8, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=DEV)
+    out8 = torch.empty((4, 8, wl.H * wl.dv), dtype=torch.float32, device=DEV)
+    st2, cs2 = _dev_state(wl, inp, S6, C6)
+    abi.kda_verify_block(layer, tok["qkv"], tok["f"], tok["beta"], tok["g_out"], st2, cs2, snaps, out8)
+    accepted = [0, 3, 8, 5]
+    abi.kda_rollback(layer, accepted, snaps, tok["qkv"], st2, cs2)
+    torch.cuda.synchronize()
+    ver = oracle_layer(wl, inp, 6, 14, S6, C6, record_states=True)
+    _check("verify out", out8, ver["out"], TOL["f32"])
+    _check("snapshots", snaps, ver["states"], TOL["f32"])
+    for b, m in enumerate(accepted):
+        _check(f"rolled-back state b={b} m={m}", st2[b], S6[b] if m == 0 else ver["states"][b, m - 1], TOL["f32"])
+    st3, cs3 = _dev_state(wl, inp, S6, C6)
+    tape = torch.empty((4, 8, wl.H, 3, wl.dk), dtype=torch.float32, device=DEV)
+    out8t = torch.empty_like(out8)
+    abi.kda_verify_block_tape(layer, tok["qkv"], tok["f"], tok["beta"], tok["g_out"], st3, cs3, tape, out8t)
+    abi.kda_commit_tape(layer, accepted, tape, tok["qkv"], st3, cs3)
+    torch.cuda.synchronize()
+    _bit_equal("tape verify out == snapshot verify out", out8t, out8)
+    _bit_equal("committed state == rolled-back state", st3, st2)
+    _bit_equal("committed conv state == rolled-back conv state", cs3, cs2)
+
+
+def test_softplus_bf16_prefill_then_decode():
+    # bf16 io at the model's head size: the softplus branch takes the fp32 prefill (pairwise decay
+    # factors), then a decode step continues each sequence
+    wl = I.WORKLOADS["prefill_t4096"].with_(T=151, H=2, B=2, gate="softplus", prefix_T=0, seed=51)
+    say("case bf16 softplus prefill 150 + decode 1 (H=2 B=2 d=128)")
+    inp = I.generate(wl)
+    rng = np.random.default_rng(51)
+    S0 = (rng.standard_normal(inp["state0"].shape) * 0.3).astype(np.float32)
+    C0 = I.round_to_io(rng.standard_normal(inp["conv_state0"].shape), "bf16")
+    layer = TT.make_layer(wl, inp, DEV)
+    st, cs = _dev_state(wl, inp, S0, C0)
+    out = _gpu_prefill(wl, inp, layer, 0, 150, st, cs)
+    tok = TT.token_tensors(wl, inp, 150, 151, DEV)
+    out1 = torch.empty((2, 1, wl.H * wl.dv), dtype=torch.float32, device=DEV)
+    abi.kda_decode_step(layer, tok["qkv"], tok["f"], tok["beta"], tok["g_out"], st, cs, out1)
+    torch.cuda.synchronize()
+    ref = oracle_layer(wl, inp, 0, 151, S0, C0)
+    _check("prefill out", out, ref["out"][:, :150], TOL["bf16"])
+    _check("decode out", out1, ref["out"][:, 150:], TOL["bf16"])
+    _check("state", st, ref["state"], TOL["bf16"])
+    _check("conv_state", cs, ref["conv_state"], 0.0)
+
+
+# ---------------------------------------------------------------------------
 # Variable-length prefill over a state pool (every element)
 # ---------------------------------------------------------------------------
 
@@ -391,6 +462,16 @@ def test_bf16_varlen_more_sequences_than_one_launch_holds():
     _check("conv-state pool", cs, ref["conv_state"], 0.0)
 
 
+def test_bf16_varlen_prefill_softplus():
+    wl = I.WORKLOADS["prefill_t4096"].with_(H=2, seed=24, gate="softplus")
+    lens = [0, 1, 70, 130]
+    say(f"case bf16 varlen softplus H=2 lengths {lens}")
+    out, st, cs, ref, pool, cpool = _varlen_case(wl, lens, [1, 3, 0, 2], 4, seed=8)
+    _check("out", out, ref["out"], TOL["bf16"])
+    _check("state pool", st, ref["state"], TOL["bf16"])
+    _check("conv-state pool", cs, ref["conv_state"], 0.0)
+
+
 def test_tiny_fp32_varlen_prefill():
     wl = I.WORKLOADS["tiny_fp32"]
     lens = [5, 0, 17, 64, 1]
@@ -401,11 +482,11 @@ def test_tiny_fp32_varlen_prefill():
     _check("conv-state pool", cs, ref["conv_state"], 0.0)
 
 
-@pytest.mark.parametrize("T", [100, 33])
-def test_fp32_prefill_head_size_128(T):
+@pytest.mark.parametrize("T,gate", [(100, "sigmoid"), (33, "sigmoid"), (100, "softplus")])
+def test_fp32_prefill_head_size_128(T, gate):
     # fp32 io at d = 128 runs the vector-ALU chunked prefill (internal chunk 32)
-    wl = I.WORKLOADS["prefill_t4096"].with_(T=T, H=2, B=2, io="f32", seed=12)
-    say(f"case fp32 prefill d=128 H=2 B=2 T={T}")
+    wl = I.WORKLOADS["prefill_t4096"].with_(T=T, H=2, B=2, io="f32", seed=12, gate=gate)
+    say(f"case fp32 prefill d=128 H=2 B=2 T={T} gate {gate}")
     inp = I.generate(wl)
     rng = np.random.default_rng(100 + T)
     S0 = (rng.standard_normal(inp["state0"].shape) * 0.3).astype(np.float32)
