@@ -5,6 +5,7 @@ One step = one pass over every call of the path on its layer-shaped workload:
   varlen    the same 4096 tokens as 16 packed sequences of a seeded length mix
             (123..628 tokens), each from its own zero state slot
   decode    64 sequences x 32 heads x 128x128 fp32 state, one token each
+  softplus  prefill_t4096 and decode_b64 again with the softplus decay branch (no lower bound)
   projection  the layer's input projection for those 4096 tokens: hidden 4096 -> q|k|v, f, beta,
             g_out (H=32, d=128, rank 128; the q|k|v|f_a|g_a|b projections as one GEMM)
   verify    16 sequences x 8 draft tokens with per-token snapshots, then rollback
@@ -102,11 +103,14 @@ def kernel_alg_bytes(kernel, wp, wd, wv, accepted):
         "kda_chunk_state_kernel[varlen]": VARLEN_SEQS * (2 * Hp * Dp * Dp * 4 + conv),
         "kda_out_norm_kernel[varlen]": Tp * 2 * Hp * Dp * io_b + Dp * io_b,
         "kda_recurrent_kernel[decode]": decode_bytes(wd.B, wd.H, wd.dk, wd.W),
+        "kda_recurrent_kernel[decode][softplus]": decode_bytes(wd.B, wd.H, wd.dk, wd.W),
         "kda_recurrent_kernel[verify]": verify_bytes(wv.B, wv.T, wv.H, wv.dk, wv.W),
         "kda_rollback_kernel": rollback_bytes(accepted or [], wv.H, wv.dk, wv.W),
         "kda_recurrent_kernel[verify_tape]": verify_tape_bytes(wv.B, wv.T, wv.H, wv.dk, wv.W),
         "kda_commit_tape_kernel": commit_bytes(accepted or [], wv.H, wv.dk, wv.W),
     }
+    for k in ("kda_chunk_prep_kernel", "kda_chunk_state_kernel", "kda_out_norm_kernel"):
+        table[k + "[softplus]"] = table[k]  # the softplus decay branch: the same bytes
     return table.get(kernel)
 
 
@@ -163,8 +167,11 @@ def short_kernel_name(full):
     if m is None:
         return None
     name = m.group(1)
-    if name in ("kda_chunk_prep_kernel", "kda_chunk_state_kernel") and m.group(2) == "<true>":
+    targs = m.group(2) or ""
+    if name in ("kda_chunk_prep_kernel", "kda_chunk_state_kernel") and targs.startswith("<true"):
         name += "[varlen]"
+    if name == "kda_chunk_prep_kernel" and targs.endswith(", true>"):
+        name += "[softplus]"
     if name == "kda_recurrent_kernel" and m.group(2):
         targs = m.group(2)
         name += "[verify_tape]" if ", true, true," in targs else "[verify]" if ", true," in targs else "[decode]"
@@ -274,6 +281,13 @@ def main():
     wp, wd, wv = I.WORKLOADS["prefill_t4096"], I.WORKLOADS["decode_b64"], I.WORKLOADS["verify_b16"]
     ops = ["prefill", "varlen", "projection", "decode", "verify"] if args.only is None else [args.only]
 
+    def softplus_layer(lay):
+        """The same layer parameters on the softplus decay branch (no lower bound)."""
+        return abi.KdaLayer(H=lay.H, D=lay.D, W=lay.W, chunk=lay.chunk, io_dtype=lay.io_dtype,
+                            out_dtype=lay.out_dtype, lb=float("nan"), scale=lay.scale, conv_w=lay.conv_w,
+                            A_log=lay.A_log, dt_bias=lay.dt_bias, norm_w=lay.norm_w,
+                            gate_kind=abi.KDA_GATE_SOFTPLUS)
+
     def workspace(layer, B, T):
         n = abi.kda_prefill_workspace_size(layer, B, T)
         return torch.empty(n, dtype=torch.uint8, device=dev) if n else None
@@ -284,9 +298,10 @@ def main():
         inp = I.generate(wp)
         lay = TT.make_layer(wp, inp, dev, out="bf16")
         tok = TT.token_tensors(wp, inp, 0, wp.T, dev)
+        lay_sp = softplus_layer(lay)
         for _ in range(nsets):
             sets["prefill"].append(dict(
-                layer=lay, tok={k: v.clone() for k, v in tok.items()},
+                layer=lay, layer_sp=lay_sp, tok={k: v.clone() for k, v in tok.items()},
                 state=torch.zeros((1, wp.H, wp.dk, wp.dv), dtype=torch.float32, device=dev),
                 conv=torch.zeros((1, wp.c_qkv, wp.W - 1), dtype=torch.bfloat16, device=dev),
                 out=torch.empty((1, wp.T, wp.H * wp.dv), dtype=torch.bfloat16, device=dev),
@@ -346,8 +361,10 @@ def main():
         lay = TT.make_layer(wd, inp, dev, out="bf16")
         st, cs = prefilled(wd, inp)
         tok = TT.token_tensors(wd, inp, wd.prefix_T, wd.prefix_T + 1, dev)
+        lay_sp = softplus_layer(lay)
         for _ in range(nsets):
-            sets["decode"].append(dict(layer=lay, tok={k: v.clone() for k, v in tok.items()}, state=st.clone(),
+            sets["decode"].append(dict(layer=lay, layer_sp=lay_sp, tok={k: v.clone() for k, v in tok.items()},
+                                       state=st.clone(),
                                        conv=cs.clone(),
                                        out=torch.empty((wd.B, 1, wd.H * wd.dv), dtype=torch.bfloat16, device=dev)))
         del st, cs
@@ -369,17 +386,17 @@ def main():
 
     def run(op, s):
         t = s.get("tok")
-        if op == "prefill":
-            abi.kda_prefill(s["layer"], t["qkv"], t["f"], t["beta"], t["g_out"], s["state"], s["conv"], s["out"],
-                            workspace=s["ws"], stream=stream)
+        if op in ("prefill", "prefill_softplus"):
+            abi.kda_prefill(s["layer" if op == "prefill" else "layer_sp"], t["qkv"], t["f"], t["beta"], t["g_out"],
+                            s["state"], s["conv"], s["out"], workspace=s["ws"], stream=stream)
         elif op == "varlen":
             abi.kda_prefill_varlen(s["layer"], var_cu, None, t["qkv"], t["f"], t["beta"], t["g_out"], s["state"],
                                    s["conv"], s["out"], workspace=s["ws"], stream=stream)
         elif op == "projection":
             abi.kda_input_projection(s["proj"], s["x"], s["qkv"], s["f"], s["beta"], s["g"], s["ws"], stream=stream)
-        elif op == "decode":
-            abi.kda_decode_step(s["layer"], t["qkv"], t["f"], t["beta"], t["g_out"], s["state"], s["conv"],
-                                s["out"], stream=stream)
+        elif op in ("decode", "decode_softplus"):
+            abi.kda_decode_step(s["layer" if op == "decode" else "layer_sp"], t["qkv"], t["f"], t["beta"],
+                                t["g_out"], s["state"], s["conv"], s["out"], stream=stream)
         elif op == "verify":
             abi.kda_verify_block(s["layer"], t["qkv"], t["f"], t["beta"], t["g_out"], s["state"], s["conv"],
                                  s["snaps"], s["out"], stream=stream)
@@ -396,8 +413,12 @@ def main():
         seq.append(op)
         if op == "verify":
             seq += ["rollback", "verify_tape", "commit"]
+        if op in ("prefill", "decode"):
+            seq.append(op + "_softplus")
 
     def setof(op):
+        if op.endswith("_softplus"):
+            return op[: -len("_softplus")]
         return "verify" if op in ("rollback", "verify_tape", "commit") else op
 
     for i in range(args.warmup):
@@ -449,7 +470,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "prefill_t4096 (B=1,T=4096,H=32,d=128,chunk 64) + the same tokens as 16 packed "
                                "sequences + their input projection (hidden 4096) + decode_b64 (B=64,H=32,d=128) "
-                               "+ verify_b16 (B=16,T_d=8,H=32,d=128) with rollback and with the replay tape",
+                               "+ verify_b16 (B=16,T_d=8,H=32,d=128) with rollback and with the replay tape; "
+                               "prefill_t4096 and decode_b64 again on the softplus decay branch",
                    "io": "bf16 inputs and outputs, fp32 state and accumulation", "buffer_sets": nsets},
         "wall_s": wall,
     }
@@ -477,12 +499,21 @@ def main():
                                       "workload": "T=4096, hidden=4096, H=32, d=128, rank 128, bf16 in and out"}
         if "value" not in res:
             res["value"], res["unit"] = wj.T / (mean["projection"] * 1e-3), "tokens/s"
+    if "prefill" in ops:
+        ms = mean["prefill_softplus"]
+        detail["prefill_softplus"] = {"ms_mean": ms, "tokens_per_s": wp.T / (ms * 1e-3), "alg_bytes": pb,
+                                      "gbps": pb / (ms * 1e-3) / 1e9,
+                                      "workload": "prefill_t4096 with the softplus decay branch (no lower bound)"}
     if "decode" in ops:
         db = decode_bytes(wd.B, wd.H, wd.dk, wd.W)
         gb = db / (mean["decode"] * 1e-3) / 1e9
         res["decode_state_update_gbps"] = gb
         detail["decode"] = {"ms_mean": mean["decode"], "alg_bytes": db, "gbps": gb,
                             "hbm_frac": gb / HBM_PEAK_GBPS}
+        ms = mean["decode_softplus"]
+        detail["decode_softplus"] = {"ms_mean": ms, "alg_bytes": db, "gbps": db / (ms * 1e-3) / 1e9,
+                                     "hbm_frac": db / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                     "workload": "decode_b64 with the softplus decay branch"}
         if "value" not in res:
             res["value"], res["unit"] = gb, "GB/s"
     if "verify" in ops:
@@ -518,10 +549,11 @@ def main():
     detail["kernels"] = kern
     res["detail"] = detail
     # dominant kernel: the largest share of the step among the attention kernels of the headline
-    # workloads (the variable-length line runs the same kernels on another table, and the input
-    # projection is a matrix-core GEMM line ahead of the layer: both are reported beside them)
+    # workloads (the variable-length and softplus lines run the same kernels on another table or
+    # gate, and the input projection is a matrix-core GEMM line ahead of the layer: all are
+    # reported beside them)
     share = lambda n: kern[n]["ms_mean"] * kern[n]["launches_per_step"]
-    hbm = [n for n in kern if not n.endswith("[varlen]") and kern[n]["alg_bytes"]]
+    hbm = [n for n in kern if "[varlen]" not in n and "[softplus]" not in n and kern[n]["alg_bytes"]]
     if hbm:
         name = max(hbm, key=share)
         k = kern[name]

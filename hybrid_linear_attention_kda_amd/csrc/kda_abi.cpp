@@ -120,8 +120,8 @@ kda::LayerArgs make_args(const kda_layer_desc* d, int B, int T) {
 
 // bf16 io at the model's head size runs the matrix-core prefill; everything else the fp32 form.
 bool mfma_path(const kda_layer_desc* d) {
-  return d->gate_kind == KDA_GATE_BOUNDED_SIGMOID &&
-         kda::prefill_mfma_supported(d->head_dim_k, d->chunk_size, d->io_dtype, d->conv_width, d->gate_lower_bound);
+  return kda::prefill_mfma_supported(d->head_dim_k, d->chunk_size, d->io_dtype, d->conv_width, d->gate_lower_bound,
+                                     d->gate_kind);
 }
 
 kda_status launched(hipError_t e, const char* what) {

@@ -99,10 +99,11 @@ hipError_t launch_projection(const ProjArgs& p, hipStream_t s, char* err, size_t
 // Chunked prefill, fp32 VALU form (any supported head size; internal chunk <= 4096 / D).
 hipError_t launch_prefill_generic(const LayerArgs& a, const SeqTab& st, int chunk, int io, int ot, hipStream_t s);
 
-// Chunked prefill on bf16 MFMA (D = 128, chunk 64, bf16 io, conv width <= 4, -5.5 <= lb <= -0.25).
+// Chunked prefill on bf16 MFMA (D = 128, chunk 64, bf16 io, conv width <= 4; the bounded gate with
+// -5.5 <= lb <= -0.25, or the softplus branch).
 // Workspace: chunk blocks for `chunks` chunks of H heads, o for `tokens` tokens, a scratch slot.
 constexpr int kMfmaChunk = 64;
-bool prefill_mfma_supported(int D, int chunk, int io, int W, float lb);
+bool prefill_mfma_supported(int D, int chunk, int io, int W, float lb, int gate);
 size_t prefill_mfma_workspace(long long chunks, long long tokens, int H);
 hipError_t launch_prefill_mfma(const LayerArgs& a, const SeqTab& st, void* ws, size_t ws_bytes, int ot,
                                hipStream_t s);

@@ -83,7 +83,8 @@ constexpr int OFF_BETA = OFF_GC + D * 4;              // [64]
 constexpr int OFF_NRM = OFF_BETA + C * 4;             // q / k normalisers [2][64]
 constexpr int OFF_SEG = OFF_NRM + 2 * C * 4;          // cumulative-sum segment totals [4][128]
 constexpr int OFF_AQK = OFF_SEG + 4 * D * 4;           // A_qk hi | lo [64][PTB] bf16 (formed while T is)
-constexpr int LDS_A = OFF_AQK + C * PA * 4;
+constexpr int OFF_GA = OFF_AQK + C * PA * 4;           // softplus branch: Gam at the sub-chunk ends [4][128]
+constexpr int LDS_A = OFF_GA + 4 * D * 4;
 static_assert(STG_BYTES >= 2 * C * PA * 4, "staging aliases");
 static_assert(LDS_A <= 160 * 1024, "LDS budget");
 
@@ -197,6 +198,56 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Cross-lane steps of the wave reduce-scatter below.
+__device__ __forceinline__ float dpp_ror8(float x) {  // lane l <- lane l ^ 8 (rotation by 8 in a row of 16)
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_xor2(float x) {  // quad_perm [2, 3, 0, 1]
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_xor1(float x) {  // quad_perm [1, 0, 3, 2]
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float swz_xor4(float x) {  // ds_swizzle bit mode, xor mask 4
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (4 << 10) | 0x1f));
+}
+// Reduce-scatter over the wave: every lane holds v[0..63]; lane l returns the sum over the 64
+// lanes of v[l].  Each step halves the values a lane holds: the lanes whose step bit is set keep
+// the upper half, and add the partner's copy of it (permlane32 / permlane16 swaps exchange two
+// registers' halves at once; the steps inside a row of 16 use DPP and swizzle).
+__device__ __forceinline__ float reduce_scatter64(float (&v)[64], int lane) {
+#pragma unroll
+  for (int m = 0; m < 32; ++m) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[m]), __float_as_uint(v[m + 32]), false, false);
+    v[m] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[m]), __float_as_uint(v[m + 16]), false, false);
+    v[m] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) v[m] = (b3 ? v[m + 8] : v[m]) + dpp_ror8(b3 ? v[m] : v[m + 8]);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) v[m] = (b2 ? v[m + 4] : v[m]) + swz_xor4(b2 ? v[m] : v[m + 4]);
+#pragma unroll
+  for (int m = 0; m < 2; ++m) v[m] = (b1 ? v[m + 2] : v[m]) + dpp_xor2(b1 ? v[m] : v[m + 2]);
+  return (b0 ? v[1] : v[0]) + dpp_xor1(b0 ? v[0] : v[1]);
+}
+
+// Softplus branch, exact diagonal sub-chunk blocks: the values of one 16-token sub-chunk are
+// enumerated column by column, n = 0..255: for column j, A_qk(j, j), then for each row i > j
+// A_kk(i, j) and A_qk(i, j).  Column j starts at n = 32 j - j^2.
+__device__ __forceinline__ void diag_entry(int n, bool& qk, int& i, int& j) {
+  j = 0;
+#pragma unroll
+  for (int jj = 1; jj < 16; ++jj) j += (32 * jj - jj * jj <= n) ? 1 : 0;
+  const int r = n - (32 * j - j * j);
+  i = r == 0 ? j : j + 1 + ((r - 1) >> 1);
+  qk = r == 0 || ((r - 1) & 1);
 }
 
 // Element offset of (row, k .. k+7) (k a multiple of 8) in the fragment-order layout of a
@@ -324,7 +375,12 @@ __device__ __forceinline__ void prep_issue(const LayerArgs& a, const SeqTab& st,
 }
 
 // VL: the launch carries a sequence table (variable-length call); otherwise a.B sequences of a.T.
-template <bool VL>
+// SP: the softplus decay branch (no lower bound).  Its decay is unbounded, so the sub-chunk
+// factoring changes: key columns are anchored at the END of their sub-chunk (every off-diagonal
+// factor is then <= 1, whatever the gate), and the four diagonal 16 x 16 blocks of A_kk and A_qk,
+// which no single anchor keeps finite, are summed exactly per channel (pairwise decay as running
+// products of the per-token decays) and reduced across the channels' lanes.
+template <bool VL, bool SP>
 __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab st, unsigned char* __restrict__ ws) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* sQ = reinterpret_cast<float*>(smem + OFF_Q);
@@ -346,6 +402,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
   float* sBeta = reinterpret_cast<float*>(smem + OFF_BETA);
   float* sNrm = reinterpret_cast<float*>(smem + OFF_NRM);
   float* sSeg = reinterpret_cast<float*>(smem + OFF_SEG);
+  float* sGa = reinterpret_cast<float*>(smem + OFF_GA);
 
   const int H = a.H, W = a.W;
   const int NC = (a.T + C - 1) / C;  // chunks per sequence of a uniform launch
@@ -467,6 +524,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     // ---- P3: bounded-sigmoid gate and its cumulative sum (lane -> channel, 16-token segment);
     //      gl[k] = Gam(16 seg + k) - Gam(16 seg - 1) stays in registers for P5 ----
     float gl[16];
+    float graw[16];  // softplus branch: this token's own log-decay, for the exact diagonal blocks
     {
       const int i = tid & 127, seg = tid >> 7;
       const float Ah = __expf(alog);
@@ -475,9 +533,14 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const float fv = (float)sF[(16 * seg + k) * PKB + i] + dtb;
-        const float g = a.lb * __builtin_amdgcn_rcpf(1.0f + __expf(-Ah * fv));
-        acc += 16 * seg + k < L ? g : 0.f;
+        // bounded sigmoid; or softplus, floored at -100 (a decay below e^-100 is zero at fp32
+        // precision either way), which keeps the 16-token sums of the log-decay well scaled
+        const float g = SP ? fmaxf(-Ah * (fmaxf(fv, 0.f) + __logf(1.0f + __expf(-fabsf(fv)))), -100.f)
+                           : a.lb * __builtin_amdgcn_rcpf(1.0f + __expf(-Ah * fv));
+        const float gv = 16 * seg + k < L ? g : 0.f;
+        acc += gv;
         gl[k] = acc;
+        graw[k] = gv;
       }
       sSeg[seg * D + i] = acc;
       // ---- P4 (same phase): q / k L2 normalisers: eight lanes per token, 16 channels each ----
@@ -507,6 +570,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       for (int s = 0; s < seg; ++s) off += sSeg[s * D + i];
       sGn[seg * D + i] = gl[0] + off;
       if (seg == 3) sGn[4 * D + i] = gl[15] + off;
+      if (SP) sGa[seg * D + i] = gl[15] + off;
     }
     __syncthreads();
 
@@ -514,6 +578,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 
     // ---- P5: anchored operands QR, KR (bf16), KC (lane -> channel, 16-token segment, as in P3:
     //      Gam_t - Gam_n(I) = gl[k] - gl[0]) and the per-channel factor tables ----
+    float dpart[4];  // softplus branch: this lane's share of its wave's diagonal-block sums
     {
       const int i = tid & 127, seg = tid >> 7;
       float* qp = sQ + 16 * seg * PQ + i;
@@ -521,16 +586,62 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       __bf16* rp = sKb + 16 * seg * PKB + i;
       const float* nq = sNrm + 16 * seg;
       const float* nk = sNrm + C + 16 * seg;
+      if (!SP) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float d = gl[k] - gl[0];
-        const float e1 = __expf(d);   // <= 1
-        const float e2 = __expf(-d);  // in [1, e^(15|lb|)]
-        const float q = qp[k * PQ] * nq[k];
-        const float kv = kp[k * PQ] * nk[k];
-        qp[k * PQ] = q * e1;
-        rp[k * PKB] = (__bf16)(kv * e1);
-        kp[k * PQ] = kv * e2;
+        for (int k = 0; k < 16; ++k) {
+          const float d = gl[k] - gl[0];
+          const float e1 = __expf(d);   // <= 1
+          const float e2 = __expf(-d);  // in [1, e^(15|lb|)]
+          const float q = qp[k * PQ] * nq[k];
+          const float kv = kp[k * PQ] * nk[k];
+          qp[k * PQ] = q * e1;
+          rp[k * PKB] = (__bf16)(kv * e1);
+          kp[k * PQ] = kv * e2;
+        }
+      } else {
+        float qn[16], kn[16], al[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          qn[k] = qp[k * PQ] * nq[k];
+          kn[k] = kp[k * PQ] * nk[k];
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float e1 = __expf(gl[k] - gl[0]);   // <= 1
+          const float e2 = __expf(gl[15] - gl[k]);  // <= 1: key columns anchored at the sub-chunk's end
+          qp[k * PQ] = qn[k] * e1;
+          rp[k * PKB] = (__bf16)(kn[k] * e1);
+          kp[k * PQ] = kn[k] * e2;
+          al[k] = __expf(graw[k]);  // this token's decay
+        }
+        // the diagonal block entries of this channel (enumerated as in diag_entry), 64 at a time,
+        // each batch summed over the wave's 64 channels; the pairwise decay e^(Gam_i - Gam_j) is
+        // the running product of the decays of tokens j+1 .. i
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          float v[64];
+          int n = 0;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            float w = kn[j];
+            if (n >= 64 * b && n < 64 * b + 64) v[n - 64 * b] = qn[j] * kn[j];
+            ++n;
+#pragma unroll
+            for (int ii = j + 1; ii < 16; ++ii) {
+              w *= al[ii];
+              if (n >= 64 * b && n < 64 * b + 64) v[n - 64 * b] = kn[ii] * w;
+              ++n;
+              if (n >= 64 * b && n < 64 * b + 64) v[n - 64 * b] = qn[ii] * w;
+              ++n;
+            }
+          }
+          dpart[b] = reduce_scatter64(v, lane);
+        }
+        // the first wave of each sub-chunk (channels 0..63) hands its sums to the second
+        if ((wave & 1) == 0) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) sTmp[seg * 256 + 64 * b + lane] = dpart[b];
+        }
       }
     }
     if (tid < D) {
@@ -540,9 +651,10 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       for (int I = 0; I < 4; ++I) {
         const float GI = sGn[I * D + c];
         sEn[I * D + c] = __expf(GI);
-        sFac[I * D + c] = __expf(GC - GI);
+        // column anchors: the sub-chunk's first token, or its last one for the softplus branch
+        sFac[I * D + c] = __expf(GC - (SP ? sGa[I * D + c] : GI));
 #pragma unroll
-        for (int J = 0; J < I; ++J) sE[pair_index(I, J) * D + c] = __expf(GI - sGn[J * D + c]);
+        for (int J = 0; J < I; ++J) sE[pair_index(I, J) * D + c] = __expf(GI - (SP ? sGa[J * D + c] : sGn[J * D + c]));
       }
       sGC[c] = __expf(GC);
     }
@@ -554,6 +666,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     auto akk_block = [&](int bi) {
       int I, J;
       block_ij(bi, I, J);
+      if (SP && I == J) return;  // formed exactly from the per-channel sums
       f32x4 acc = zero4();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -575,12 +688,43 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       }
     };
     akk_block(wave < 7 ? wave : 9);
+    if (SP && (wave & 1)) {
+      // diagonal block of sub-chunk seg: this wave's sums plus the partner wave's, as A_kk (times
+      // beta, strictly lower) and A_qk (split planes, lower with the diagonal); then the upper
+      // triangles, lane -> row l16, columns 4 lg .. 4 lg + 3
+      const int base = 16 * (wave >> 1);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float tot = dpart[b] + sTmp[(wave >> 1) * 256 + 64 * b + lane];
+        bool qk;
+        int i, j;
+        diag_entry(64 * b + lane, qk, i, j);
+        const int R = base + i, Cc = base + j;
+        if (qk) {
+          const __bf16 hi = (__bf16)tot;
+          sAhi[R * PTB + Cc] = hi;
+          sAlo[R * PTB + Cc] = (__bf16)(tot - (float)hi);
+        } else {
+          sAkk[R * PA + Cc] = sBeta[R] * tot;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * lg + e, R = base + l16, Cc = base + j;
+        if (j >= l16) sAkk[R * PA + Cc] = 0.f;
+        if (j > l16) {
+          sAhi[R * PTB + Cc] = (__bf16)0.f;
+          sAlo[R * PTB + Cc] = (__bf16)0.f;
+        }
+      }
+    }
     __syncthreads();
 
     // ---- P6b: A_qk = QR_I E_IJ . KC_J^T (split bf16), lower incl. diagonal: one 16 x 16 block ----
     auto aqk_block = [&](int bi) {
       int I, J;
       block_ij(bi, I, J);
+      if (SP && I == J) return;  // formed exactly from the per-channel sums
       f32x4 acc = zero4();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -1210,13 +1354,15 @@ __global__ __launch_bounds__(256) void kda_out_norm_kernel(const float* __restri
 
 }  // namespace
 
-// The anchored decay factors stay finite only for a bounded gate (15 |lb| < 87), and the
-// staging halo covers conv widths up to 4.  A gate bound above -0.25 lets the state decay too
+// The staging halo covers conv widths up to 4.  For the bounded gate the start-anchored decay
+// factors stay finite only for 15 |lb| < 87, and a gate bound above -0.25 lets the state decay too
 // little to keep this path's bf16 operands (W and the key rows behind it) inside the 2e-3 bar over
 // thousands of tokens (measured at T = 4096: state error 1.6e-3 at lb = -0.1, 2.0e-3 at -0.05,
-// 9e-4 at -0.25, 4e-4 at -5), so such gates take the fp32 path.
-bool prefill_mfma_supported(int Dh, int chunk, int io, int W, float lb) {
-  return Dh == D && chunk == C && io == kBF16 && W >= 1 && W <= HALO + 1 && lb <= -0.25f && lb >= -5.5f;
+// 9e-4 at -0.25, 4e-4 at -5), so such gates take the fp32 path.  The softplus branch has its own
+// factoring (end anchors and exact diagonal blocks) and no bound to check.
+bool prefill_mfma_supported(int Dh, int chunk, int io, int W, float lb, int gate) {
+  if (!(Dh == D && chunk == C && io == kBF16 && W >= 1 && W <= HALO + 1)) return false;
+  return gate == 1 || (lb <= -0.25f && lb >= -5.5f);
 }
 
 size_t prefill_mfma_workspace(long long chunks, long long tokens, int H) {
@@ -1230,9 +1376,12 @@ static hipError_t launch_mfma_t(const LayerArgs& a, const SeqTab& st, void* ws, 
   const long long chunks = VL ? st.total_chunks : (long long)a.B * NC;
   const long long tokens = VL ? st.tok0[st.n] : (long long)a.B * a.T;
   float* ows = reinterpret_cast<float*>(tiles + (size_t)chunks * a.H * CH_BYTES);
-  static const hipError_t attr_a = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL>),
+  static const hipError_t attr_a = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL, false>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_A);
   if (attr_a != hipSuccess) return attr_a;
+  static const hipError_t attr_sp = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL, true>),
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_A);
+  if (attr_sp != hipSuccess) return attr_sp;
   // persistent: one workgroup per CU (the LDS use admits one), each looping over tasks
   static const int ncu = [] {
     int dev = 0, n = 0;
@@ -1242,8 +1391,21 @@ static hipError_t launch_mfma_t(const LayerArgs& a, const SeqTab& st, void* ws, 
     return n;
   }();
   const int ntask = (int)(chunks * a.H);
-  timing_begin(VL ? "kda_chunk_prep_kernel[varlen]" : "kda_chunk_prep_kernel", s);
-  kda_chunk_prep_kernel<VL><<<dim3(ntask < ncu ? ntask : ncu), NT, LDS_A, s>>>(a, st, tiles);
+  // timing names (kept apart per call kind: [varlen] table mode, [softplus] decay branch)
+  static const char* const kname[3][4] = {
+      {"kda_chunk_prep_kernel", "kda_chunk_prep_kernel[softplus]", "kda_chunk_prep_kernel[varlen]",
+       "kda_chunk_prep_kernel[varlen][softplus]"},
+      {"kda_chunk_state_kernel", "kda_chunk_state_kernel[softplus]", "kda_chunk_state_kernel[varlen]",
+       "kda_chunk_state_kernel[varlen][softplus]"},
+      {"kda_out_norm_kernel", "kda_out_norm_kernel[softplus]", "kda_out_norm_kernel[varlen]",
+       "kda_out_norm_kernel[varlen][softplus]"}};
+  const int kn = (VL ? 2 : 0) + (a.gate != 0 ? 1 : 0);
+  const dim3 grid_a(ntask < ncu ? ntask : ncu);
+  timing_begin(kname[0][kn], s);
+  if (a.gate == 0)
+    kda_chunk_prep_kernel<VL, false><<<grid_a, NT, LDS_A, s>>>(a, st, tiles);
+  else
+    kda_chunk_prep_kernel<VL, true><<<grid_a, NT, LDS_A, s>>>(a, st, tiles);
   timing_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1251,13 +1413,13 @@ static hipError_t launch_mfma_t(const LayerArgs& a, const SeqTab& st, void* ws, 
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_B);
   if (attr_b != hipSuccess) return attr_b;
   const dim3 grid_b(NBLK * a.H, VL ? st.n : a.B);
-  timing_begin(VL ? "kda_chunk_state_kernel[varlen]" : "kda_chunk_state_kernel", s);
+  timing_begin(kname[1][kn], s);
   kda_chunk_state_kernel<VL><<<grid_b, NTB, LDS_B, s>>>(a, st, tiles, ows);
   timing_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long rows = tokens * a.H;
   const dim3 ng((unsigned)((rows + 15) / 16));
-  timing_begin(VL ? "kda_out_norm_kernel[varlen]" : "kda_out_norm_kernel", s);
+  timing_begin(kname[2][kn], s);
   if (ot == kBF16)
     kda_out_norm_kernel<bf16_t><<<ng, 256, 0, s>>>(ows, static_cast<const bf16_t*>(a.g_out),
                                                    static_cast<const bf16_t*>(a.norm_w), static_cast<bf16_t*>(a.out),

@@ -375,10 +375,12 @@ __global__ __launch_bounds__(kCommitNT) void kda_commit_tape_kernel(CommitArgs a
 template <int D, int WMAX, bool MULTI, bool TAPE>
 static hipError_t launch_rec_t(const LayerArgs& a, int io, int ot, hipStream_t s) {
   dim3 grid(a.H, a.B), block(RecLayout<D>::NT);
-  timing_begin(TAPE ? "kda_recurrent_kernel[verify_tape]"
-               : a.snapshots ? "kda_recurrent_kernel[verify]"
-                             : "kda_recurrent_kernel[decode]",
-               s);
+  // timing names per call kind, [softplus] for the decay branch without a bound
+  static const char* const kname[2][3] = {
+      {"kda_recurrent_kernel[decode]", "kda_recurrent_kernel[verify]", "kda_recurrent_kernel[verify_tape]"},
+      {"kda_recurrent_kernel[decode][softplus]", "kda_recurrent_kernel[verify][softplus]",
+       "kda_recurrent_kernel[verify_tape][softplus]"}};
+  timing_begin(kname[a.gate != 0][TAPE ? 2 : a.snapshots ? 1 : 0], s);
   if (io == kBF16) {
     if (ot == kBF16)
       kda_recurrent_kernel<D, WMAX, MULTI, TAPE, bf16_t, bf16_t><<<grid, block, 0, s>>>(a);

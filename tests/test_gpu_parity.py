@@ -361,8 +361,8 @@ def test_softplus_tiny_fp32_prefill_decode_verify_rollback_tape():
 
 
 def test_softplus_bf16_prefill_then_decode():
-    # bf16 io at the model's head size: the softplus branch takes the fp32 prefill (pairwise decay
-    # factors), then a decode step continues each sequence
+    # bf16 io at the model's head size: the softplus branch on the matrix-core prefill (end-anchored
+    # key columns, exact diagonal sub-chunk blocks), then a decode step continues each sequence
     wl = I.WORKLOADS["prefill_t4096"].with_(T=151, H=2, B=2, gate="softplus", prefix_T=0, seed=51)
     say("case bf16 softplus prefill 150 + decode 1 (H=2 B=2 d=128)")
     inp = I.generate(wl)
@@ -381,6 +381,29 @@ def test_softplus_bf16_prefill_then_decode():
     _check("decode out", out1, ref["out"][:, 150:], TOL["bf16"])
     _check("state", st, ref["state"], TOL["bf16"])
     _check("conv_state", cs, ref["conv_state"], 0.0)
+
+
+@pytest.mark.parametrize("shift", [-12.0, 8.0, 60.0])
+def test_softplus_bf16_prefill_extreme_decays(shift):
+    # f + dt_bias shifted so the decay is nearly absent (-12: g ~ -A e^-12), strong (8: g ~ -8 A)
+    # or far past any sub-chunk bound (60: g ~ -60 A, floored at -100), with every fourth token
+    # unshifted so strong and weak decays mix inside the sub-chunks; T = 150 (a partial chunk)
+    wl = I.WORKLOADS["prefill_t4096"].with_(T=150, H=2, B=1, gate="softplus", seed=52)
+    say(f"case bf16 softplus prefill, f shifted by {shift} on three tokens of four")
+    inp = dict(I.generate(wl))
+    f = inp["f"].astype(np.float64)
+    f[:, np.arange(150) % 4 != 0] += shift
+    inp["f"] = I.round_to_io(f, "bf16")
+    rng = np.random.default_rng(53)
+    S0 = (rng.standard_normal(inp["state0"].shape) * 0.3).astype(np.float32)
+    layer = TT.make_layer(wl, inp, DEV)
+    st, cs = _dev_state(wl, inp, S0)
+    out = _gpu_prefill(wl, inp, layer, 0, 150, st, cs)
+    torch.cuda.synchronize()
+    ref = oracle_layer(wl, inp, 0, 150, S0, inp["conv_state0"])
+    assert torch.isfinite(out).all()
+    _check("out", out, ref["out"], TOL["bf16"])
+    _check("state", st, ref["state"], TOL["bf16"])
 
 
 # ---------------------------------------------------------------------------
@@ -553,9 +576,10 @@ def test_verify_b16_full_size_with_rollback():
     _check("rolled-back conv", cs, np.stack(ref_c), 0.0)
 
 
-def test_prefill_t4096_full_size_sampled_heads():
-    wl = I.WORKLOADS["prefill_t4096"]
-    say("case prefill_t4096 full size (B=1, T=4096, H=32, d=128), oracle on heads 0 and 21")
+@pytest.mark.parametrize("gate", ["sigmoid", "softplus"])
+def test_prefill_t4096_full_size_sampled_heads(gate):
+    wl = I.WORKLOADS["prefill_t4096"].with_(gate=gate)
+    say(f"case prefill_t4096 full size (B=1, T=4096, H=32, d=128), gate {gate}, oracle on heads 0 and 21")
     inp = I.generate(wl)
     layer = TT.make_layer(wl, inp, DEV)
     st, cs = _dev_state(wl, inp)
