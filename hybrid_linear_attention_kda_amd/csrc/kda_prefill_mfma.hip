@@ -37,7 +37,11 @@
 // e^(Gam_i - Gam_n(I)) (<= 1) on rows and e^(Gam_n(J) - Gam_j) (<= e^(15|lb|))
 // on columns, and block (I, J) of A multiplies the row operand by the
 // per-channel factor e^(Gam_n(I) - Gam_n(J)) (<= 1).  With the bounded gate
-// (|lb| <= 5.5) every factor stays a finite fp32 / bf16 number.
+// (|lb| <= 5.5) every factor stays a finite fp32 / bf16 number.  The softplus decay
+// branch (llama.cpp PR #27754, metadata commit: the function taken without a lower
+// bound) has no such bound; its instance anchors the columns at the end of their
+// sub-chunk instead, which keeps every off-diagonal factor <= 1, and sums the four
+// diagonal blocks exactly per channel (see kda_chunk_prep_kernel).
 //
 // Precision.  bf16 operands round to 8 bits; contractions that feed the
 // output or the state directly use split bf16 (x = hi + lo, three MFMAs:
