@@ -86,9 +86,13 @@ kda_status check_desc(const kda_layer_desc* d) {
   return KDA_OK;
 }
 
-kda_status check_batch(int32_t B, int32_t T) {
+// B sequences of T tokens over H heads; the launches index token-heads (and their 64-token
+// chunks) with 32-bit integers, so one call covers at most 2^31 - 1 token-heads.
+kda_status check_batch(int32_t B, int32_t T, int32_t H) {
   if (B < 0 || T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B and T must be >= 0");
   if (B > 65535) return fail(KDA_ERR_UNSUPPORTED, "B > 65535");
+  if ((long long)B * T * H > 0x7fffffffLL)
+    return fail(KDA_ERR_UNSUPPORTED, "B * T * H = %lld token-heads exceeds 2^31 - 1 per call", (long long)B * T * H);
   return KDA_OK;
 }
 
@@ -139,7 +143,8 @@ struct Launch {
 // Validate a variable-length call and cut it into launches.  cu_seqlens[0] = 0 and non-decreasing;
 // slots (NULL: sequence i uses slot i) in 0..num_slots-1 and distinct.  Sequences of length 0 are
 // no-ops and get no table entry.
-kda_status plan_varlen(int32_t N, const int32_t* cu, const int32_t* slots, int32_t num_slots, std::vector<Launch>& plan) {
+kda_status plan_varlen(int32_t N, const int32_t* cu, const int32_t* slots, int32_t num_slots, int32_t H,
+                       std::vector<Launch>& plan) {
   plan.clear();
   if (N < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "N must be >= 0");
   if (N == 0) return KDA_OK;
@@ -175,6 +180,8 @@ kda_status plan_varlen(int32_t N, const int32_t* cu, const int32_t* slots, int32
     ++t.n;
   }
   if (cur.tab.n > 0) plan.push_back(cur);
+  if ((long long)cu[N] * H > 0x7fffffffLL)
+    return fail(KDA_ERR_UNSUPPORTED, "%d packed tokens x %d heads exceeds 2^31 - 1 token-heads per call", cu[N], H);
   return KDA_OK;
 }
 
@@ -192,6 +199,8 @@ kda_status check_proj(const kda_proj_desc* d) {
   if (d->num_heads < 1 || d->head_dim < 1 || d->hidden < 1 || d->rank < 1)
     return fail(KDA_ERR_INVALID_ARGUMENT, "num_heads, head_dim, hidden and rank must be >= 1");
   if (d->rank != kda::kProjRank) return fail(KDA_ERR_UNSUPPORTED, "rank %d != %d", d->rank, kda::kProjRank);
+  if ((long long)d->num_heads * d->head_dim > 65536 || d->hidden > 65536)
+    return fail(KDA_ERR_UNSUPPORTED, "H*d and hidden must be <= 65536");
   if ((d->num_heads * d->head_dim) % 128 != 0)
     return fail(KDA_ERR_UNSUPPORTED, "H*d = %d is not a multiple of 128", d->num_heads * d->head_dim);
   if (d->hidden % 8 != 0) return fail(KDA_ERR_UNSUPPORTED, "hidden = %d is not a multiple of 8", d->hidden);
@@ -230,7 +239,7 @@ const char* kda_status_string(kda_status s) {
 const char* kda_last_error(void) { return g_last_error; }
 
 size_t kda_prefill_workspace_size(const kda_layer_desc* desc, int32_t B, int32_t T) {
-  if (check_desc(desc) != KDA_OK || check_batch(B, T) != KDA_OK || check_chunk(desc) != KDA_OK) return (size_t)-1;
+  if (check_desc(desc) != KDA_OK || check_batch(B, T, desc->num_heads) != KDA_OK || check_chunk(desc) != KDA_OK) return (size_t)-1;
   if (!mfma_path(desc)) return 0;
   const long long nc = ((long long)T + kda::kMfmaChunk - 1) / kda::kMfmaChunk;
   return kda::prefill_mfma_workspace((long long)B * nc, (long long)B * T, desc->num_heads);
@@ -240,7 +249,7 @@ kda_status kda_prefill(const kda_layer_desc* desc, int32_t B, int32_t T, const v
                        const void* beta, const void* g_out, float* state, void* conv_state, void* out,
                        void* workspace, size_t workspace_bytes, void* stream) {
   KDA_TRY(check_desc(desc));
-  KDA_TRY(check_batch(B, T));
+  KDA_TRY(check_batch(B, T, desc->num_heads));
   KDA_TRY(check_chunk(desc));
   if (B == 0 || T == 0) return ok();
   KDA_TRY(check_token_tensors(qkv, f, beta, g_out));
@@ -279,7 +288,7 @@ size_t kda_prefill_varlen_workspace_size(const kda_layer_desc* desc, int32_t N, 
   if (check_desc(desc) != KDA_OK || check_chunk(desc) != KDA_OK) return (size_t)-1;
   std::vector<Launch> plan;
   // slots do not change the size: check the offsets with slot i for sequence i
-  if (plan_varlen(N, cu_seqlens_host, nullptr, N > 0 ? N : 1, plan) != KDA_OK) return (size_t)-1;
+  if (plan_varlen(N, cu_seqlens_host, nullptr, N > 0 ? N : 1, desc->num_heads, plan) != KDA_OK) return (size_t)-1;
   if (!mfma_path(desc)) return 0;
   return varlen_workspace(plan, desc->num_heads);
 }
@@ -291,7 +300,7 @@ kda_status kda_prefill_varlen(const kda_layer_desc* desc, int32_t N, const int32
   KDA_TRY(check_desc(desc));
   KDA_TRY(check_chunk(desc));
   std::vector<Launch> plan;
-  KDA_TRY(plan_varlen(N, cu_seqlens_host, slots_host, num_slots, plan));
+  KDA_TRY(plan_varlen(N, cu_seqlens_host, slots_host, num_slots, desc->num_heads, plan));
   if (plan.empty()) return ok();  // no sequence has a token
   KDA_TRY(check_token_tensors(qkv, f, beta, g_out));
   KDA_TRY(check_ptr(state, "state"));
@@ -334,7 +343,7 @@ kda_status kda_decode_step(const kda_layer_desc* desc, int32_t B, const void* qk
                            const void* beta, const void* g_out, float* state, void* conv_state, void* out,
                            void* stream) {
   KDA_TRY(check_desc(desc));
-  KDA_TRY(check_batch(B, 1));
+  KDA_TRY(check_batch(B, 1, desc->num_heads));
   if (B == 0) return ok();
   KDA_TRY(check_token_tensors(qkv, f, beta, g_out));
   KDA_TRY(check_ptr(state, "state"));
@@ -359,7 +368,7 @@ kda_status kda_verify_block(const kda_layer_desc* desc, int32_t B, int32_t T_d, 
                             const void* beta, const void* g_out, const float* state, const void* conv_state,
                             float* snaps, void* out, void* stream) {
   KDA_TRY(check_desc(desc));
-  KDA_TRY(check_batch(B, T_d));
+  KDA_TRY(check_batch(B, T_d, desc->num_heads));
   if (T_d > 255) return fail(KDA_ERR_UNSUPPORTED, "draft block T_d = %d > 255", T_d);
   if (B == 0 || T_d == 0) return ok();
   KDA_TRY(check_token_tensors(qkv, f, beta, g_out));
@@ -385,7 +394,7 @@ kda_status kda_verify_block(const kda_layer_desc* desc, int32_t B, int32_t T_d, 
 kda_status kda_rollback(const kda_layer_desc* desc, int32_t B, int32_t T_d, const int32_t* accepted_host,
                         const float* snaps, const void* qkv_block, float* state, void* conv_state, void* stream) {
   KDA_TRY(check_desc(desc));
-  KDA_TRY(check_batch(B, T_d));
+  KDA_TRY(check_batch(B, T_d, desc->num_heads));
   if (T_d > 255) return fail(KDA_ERR_UNSUPPORTED, "draft block T_d = %d > 255", T_d);
   if (B == 0) return ok();
   if (accepted_host == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "accepted_host is null");
@@ -421,7 +430,7 @@ kda_status kda_rollback(const kda_layer_desc* desc, int32_t B, int32_t T_d, cons
 }
 
 size_t kda_verify_tape_size(const kda_layer_desc* desc, int32_t B, int32_t T_d) {
-  if (check_desc(desc) != KDA_OK || check_batch(B, T_d) != KDA_OK) return (size_t)-1;
+  if (check_desc(desc) != KDA_OK || check_batch(B, T_d, desc->num_heads) != KDA_OK) return (size_t)-1;
   return (size_t)B * (size_t)T_d * (size_t)desc->num_heads * 3u * (size_t)desc->head_dim_k * sizeof(float);
 }
 
@@ -429,7 +438,7 @@ kda_status kda_verify_block_tape(const kda_layer_desc* desc, int32_t B, int32_t 
                                  const void* f, const void* beta, const void* g_out, const float* state,
                                  const void* conv_state, float* tape, void* out, void* stream) {
   KDA_TRY(check_desc(desc));
-  KDA_TRY(check_batch(B, T_d));
+  KDA_TRY(check_batch(B, T_d, desc->num_heads));
   if (T_d > 255) return fail(KDA_ERR_UNSUPPORTED, "draft block T_d = %d > 255", T_d);
   if (B == 0 || T_d == 0) return ok();
   KDA_TRY(check_token_tensors(qkv, f, beta, g_out));
@@ -457,7 +466,7 @@ kda_status kda_commit_tape(const kda_layer_desc* desc, int32_t B, int32_t T_d, c
                            const float* tape, const void* qkv_block, float* state, void* conv_state,
                            void* stream) {
   KDA_TRY(check_desc(desc));
-  KDA_TRY(check_batch(B, T_d));
+  KDA_TRY(check_batch(B, T_d, desc->num_heads));
   if (T_d > 255) return fail(KDA_ERR_UNSUPPORTED, "draft block T_d = %d > 255", T_d);
   if (B == 0) return ok();
   if (accepted_host == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "accepted_host is null");
@@ -493,14 +502,14 @@ kda_status kda_commit_tape(const kda_layer_desc* desc, int32_t B, int32_t T_d, c
 }
 
 size_t kda_input_projection_workspace_size(const kda_proj_desc* desc, int32_t T) {
-  if (check_proj(desc) != KDA_OK || check_batch(1, T) != KDA_OK) return (size_t)-1;
+  if (check_proj(desc) != KDA_OK || check_batch(1, T, desc->num_heads) != KDA_OK) return (size_t)-1;
   return kda::projection_workspace(T, desc->num_heads, desc->head_dim);
 }
 
 kda_status kda_input_projection(const kda_proj_desc* desc, int32_t T, const void* x, void* qkv, void* f,
                                 void* beta, void* g_out, void* workspace, size_t workspace_bytes, void* stream) {
   KDA_TRY(check_proj(desc));
-  KDA_TRY(check_batch(1, T));
+  KDA_TRY(check_batch(1, T, desc->num_heads));
   if (T == 0) return ok();
   KDA_TRY(check_ptr(x, "x"));
   KDA_TRY(check_ptr(qkv, "qkv"));

@@ -41,6 +41,8 @@
  *   - io_dtype (KDA_F32 or KDA_BF16) is the type of qkv, f, beta, g_out,
  *     conv_w, norm_w and conv_state; out_dtype the type of out; the state,
  *     the snapshots, A_log and dt_bias are always fp32.
+ *   - One call covers at most 2^31 - 1 token-heads (B * T * H, or the packed
+ *     tokens times H); larger requests return KDA_ERR_UNSUPPORTED.
  *   - Supported: d_k == d_v in {16, 32, 64, 128}; conv_width 1..8;
  *     prefill chunk_size in {16, 32, 64}.  Other shapes return
  *     KDA_ERR_UNSUPPORTED.  bf16 io with d = 128, chunk 64, conv width <= 4

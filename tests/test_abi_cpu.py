@@ -83,6 +83,9 @@ def test_null_descriptor_and_bad_sizes():
     assert prefill(desc(), ptr=0) == abi.KDA_ERR_INVALID_ARGUMENT
     assert prefill(desc(), ptr=FAKE + 2) == abi.KDA_ERR_INVALID_ARGUMENT
     assert b"not 16-byte aligned" in lib.kda_last_error()
+    # one call indexes token-heads with 32-bit integers: 2 heads x 2^30 tokens is refused up front
+    assert prefill(desc(), B=1, T=(1 << 30)) == abi.KDA_ERR_UNSUPPORTED
+    assert b"token-heads" in lib.kda_last_error()
 
 
 def test_empty_calls_are_no_ops():
@@ -156,6 +159,7 @@ def test_varlen_validation_and_workspace_size():
     assert call([0, 2, 4], [0, 4]) == abi.KDA_ERR_INVALID_ARGUMENT and b"outside 0..3" in lib.kda_last_error()
     assert call([0, 2, 4], num_slots=0) == abi.KDA_ERR_INVALID_ARGUMENT
     assert call([0, 2, 4], ptr=0) == abi.KDA_ERR_INVALID_ARGUMENT  # non-empty: pointers are checked
+    assert call([0, 1 << 30]) == abi.KDA_ERR_UNSUPPORTED and b"token-heads" in lib.kda_last_error()
     c = (ctypes.c_int32 * 3)(0, 2, 4)
     assert lib.kda_prefill_varlen_workspace_size(ctypes.byref(d), 2, ctypes.cast(c, ctypes.c_void_p)) == 0  # fp32 path
     bad = (ctypes.c_int32 * 3)(0, 4, 2)
@@ -179,6 +183,9 @@ def test_input_projection_validation():
     assert call(pd(rank=64)) == abi.KDA_ERR_UNSUPPORTED and b"rank 64" in lib.kda_last_error()
     assert call(pd(num_heads=3, head_dim=16)) == abi.KDA_ERR_UNSUPPORTED
     assert call(pd(hidden=4100)) == abi.KDA_ERR_UNSUPPORTED
+    assert call(pd(hidden=1 << 17)) == abi.KDA_ERR_UNSUPPORTED
+    assert call(pd(num_heads=1024, head_dim=128)) == abi.KDA_ERR_UNSUPPORTED
+    assert call(pd(), T=(1 << 26)) == abi.KDA_ERR_UNSUPPORTED and b"token-heads" in lib.kda_last_error()
     assert call(pd(w_fb=0)) == abi.KDA_ERR_INVALID_ARGUMENT and b"desc.w_fb is null" in lib.kda_last_error()
     assert call(pd(out_dtype=5)) == abi.KDA_ERR_INVALID_ARGUMENT
     assert call(pd()) == abi.KDA_ERR_INVALID_ARGUMENT and b"workspace is null" in lib.kda_last_error()

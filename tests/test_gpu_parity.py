@@ -383,6 +383,33 @@ def test_softplus_bf16_prefill_then_decode():
     _check("conv_state", cs, ref["conv_state"], 0.0)
 
 
+@pytest.mark.parametrize("W", [1, 3])
+def test_softplus_bf16_prefill_conv_widths_chained(W):
+    # the softplus instance of the matrix-core prefill at conv widths 1 and 3, as two chained calls
+    # (100 + 50 tokens) against one call and the oracle
+    wl = I.WORKLOADS["prefill_t4096"].with_(T=150, H=2, B=2, W=W, gate="softplus", seed=54 + W)
+    say(f"case bf16 softplus prefill W={W}, 100 + 50 chained vs single-shot")
+    inp = I.generate(wl)
+    rng = np.random.default_rng(60 + W)
+    S0 = (rng.standard_normal(inp["state0"].shape) * 0.3).astype(np.float32)
+    C0 = I.round_to_io(rng.standard_normal(inp["conv_state0"].shape), "bf16")
+    layer = TT.make_layer(wl, inp, DEV)
+    st, cs = _dev_state(wl, inp, S0, C0)
+    o1 = _gpu_prefill(wl, inp, layer, 0, 100, st, cs)
+    o2 = _gpu_prefill(wl, inp, layer, 100, 150, st, cs)
+    st1, cs1 = _dev_state(wl, inp, S0, C0)
+    o = _gpu_prefill(wl, inp, layer, 0, 150, st1, cs1)
+    torch.cuda.synchronize()
+    ref = oracle_layer(wl, inp, 0, 150, S0, C0)
+    _check("chained out", torch.cat([o1, o2], dim=1), ref["out"], TOL["bf16"])
+    _check("single-shot out", o, ref["out"], TOL["bf16"])
+    _check("chained state", st, ref["state"], TOL["bf16"])
+    _check("single-shot state", st1, ref["state"], TOL["bf16"])
+    if W > 1:
+        _check("conv_state", cs, ref["conv_state"], 0.0)
+        assert torch.equal(cs, cs1)
+
+
 @pytest.mark.parametrize("shift", [-12.0, 8.0, 60.0])
 def test_softplus_bf16_prefill_extreme_decays(shift):
     # f + dt_bias shifted so the decay is nearly absent (-12: g ~ -A e^-12), strong (8: g ~ -8 A)
