@@ -474,47 +474,64 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     }
     if (tid < C) sBeta[tid] = tid < L ? to_f32(cur.beta) : 0.f;
     __syncthreads();
-    // conv taps of this lane's q|k channel (tid % 256) and of the v channel it converts in P9
-    // (16 * wave + lane % 16), zero-padded on the left to 4 taps; read before T reuses the block
-    // taps as bf16 pairs (tap of the older token first): {t0, t1} and {t2, t3}
-    bf16x2 tq01, tq23, tv01, tv23;
+    // conv taps of this lane's two q|k channels 2 (tid % 128) and 2 (tid % 128) + 1 and of the v
+    // channel it converts in P9 (16 * wave + lane % 16), zero-padded on the left to 4 taps; read
+    // before T reuses the block; taps as bf16 pairs (tap of the older token first): {t0, t1}, {t2, t3}
+    bf16x2 ta01, ta23, tb01, tb23, tv01, tv23;
     {
       const __bf16* taps = reinterpret_cast<const __bf16*>(sPar);
-      const int cq = tid & 255;  // q channels then k channels: the block rows in that order
-      __bf16 tq[4], tv[4];
+      const int ca = 2 * (tid & 127);  // q channels then k channels: the block rows in that order
+      __bf16 ta[4], tb[4], tv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int w = max(j - (4 - W), 0);
-        tq[j] = j >= 4 - W ? taps[cq * W + w] : (__bf16)0.f;
+        ta[j] = j >= 4 - W ? taps[ca * W + w] : (__bf16)0.f;
+        tb[j] = j >= 4 - W ? taps[(ca + 1) * W + w] : (__bf16)0.f;
         tv[j] = j >= 4 - W ? taps[(2 * D + 16 * wave + l16) * W + w] : (__bf16)0.f;
       }
-      tq01 = bf16x2{tq[0], tq[1]};
-      tq23 = bf16x2{tq[2], tq[3]};
+      ta01 = bf16x2{ta[0], ta[1]};
+      ta23 = bf16x2{ta[2], ta[3]};
+      tb01 = bf16x2{tb[0], tb[1]};
+      tb23 = bf16x2{tb[2], tb[3]};
       tv01 = bf16x2{tv[0], tv[1]};
       tv23 = bf16x2{tv[2], tv[3]};
     }
     const float* sDtb = reinterpret_cast<const float*>(sPar + 3 * D * W * 2);
 
-    // ---- P2: causal conv + SiLU over q|k: lane -> channel cq, 32 tokens ----
+    // ---- P2: causal conv + SiLU over q|k: lane -> channels 2 (tid % 128) + {0, 1}, 16 tokens.
+    //      Tokens past the sequence's end are not masked: beta is 0 there, so their rows of W and
+    //      Ut, and with them their share of the state update, are exactly 0, and their outputs are
+    //      not stored ----
     {
-      const int tb = 32 * (tid >> 8), cq = tid & 255;
-      const __bf16* col = sRaw + cq;
-      float* dst = cq < D ? sQ + cq : sG + (cq - D);
-      // the lane's 35 raw rows are read before any arithmetic (so that the reads overlap) as pairs
-      // pe[m] = (row 2m, row 2m+1) and, between them, po[m] = (row 2m+1, row 2m+2); output row i
-      // takes pairs i and i+2
-      bf16x2 pe[18], po[17];
+      const int tb = 16 * (tid >> 7), ca = 2 * (tid & 127);
+      const uint32_t* col = reinterpret_cast<const uint32_t*>(sRaw + ca);  // both channels of a row
+      float* dst = ca < D ? sQ + ca : sG + (ca - D);
+      // the lane's 19 raw rows (one 32-bit word: channel ca low, ca + 1 high) are read before any
+      // arithmetic, then regrouped per channel as pairs pe[m] = (row 2m, row 2m+1) and, between
+      // them, po[m] = (row 2m+1, row 2m+2); output row i takes pairs i and i+2
+      uint32_t w[20];
 #pragma unroll
-      for (int m = 0; m < 17; ++m) pe[m] = bf16x2{col[(tb + 2 * m) * PR], col[(tb + 2 * m + 1) * PR]};
-      pe[17] = bf16x2{col[(tb + 34) * PR], (__bf16)0.f};
+      for (int r = 0; r < 19; ++r) w[r] = col[(tb + r) * (PR / 2)];
+      w[19] = 0u;
+      bf16x2 pa[10], pb[10], qa[9], qb[9];
 #pragma unroll
-      for (int m = 0; m < 17; ++m) po[m] = mid_pair(pe[m], pe[m + 1]);
+      for (int m = 0; m < 10; ++m) {
+        pa[m] = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(w[2 * m + 1], w[2 * m], 0x05040100u));
+        pb[m] = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(w[2 * m + 1], w[2 * m], 0x07060302u));
+      }
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int t = tb + i, m = i >> 1;
-        const float y = (i & 1) ? dot2(tq23, po[m + 1], dot2(tq01, po[m], 0.f))
-                                : dot2(tq23, pe[m + 1], dot2(tq01, pe[m], 0.f));
-        dst[t * PQ] = t < L ? silu_fast(y) : 0.f;
+      for (int m = 0; m < 9; ++m) {
+        qa[m] = mid_pair(pa[m], pa[m + 1]);
+        qb[m] = mid_pair(pb[m], pb[m + 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = i >> 1;
+        const float ya = (i & 1) ? dot2(ta23, qa[m + 1], dot2(ta01, qa[m], 0.f))
+                                 : dot2(ta23, pa[m + 1], dot2(ta01, pa[m], 0.f));
+        const float yb = (i & 1) ? dot2(tb23, qb[m + 1], dot2(tb01, qb[m], 0.f))
+                                 : dot2(tb23, pb[m + 1], dot2(tb01, pb[m], 0.f));
+        *reinterpret_cast<float2*>(dst + (tb + i) * PQ) = make_float2(silu_fast(ya), silu_fast(yb));
       }
     }
     __syncthreads();
@@ -541,7 +558,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
         // precision either way), which keeps the 16-token sums of the log-decay well scaled
         const float g = SP ? fmaxf(-Ah * (fmaxf(fv, 0.f) + __logf(1.0f + __expf(-fabsf(fv)))), -100.f)
                            : a.lb * __builtin_amdgcn_rcpf(1.0f + __expf(-Ah * fv));
-        const float gv = 16 * seg + k < L ? g : 0.f;
+        const float gv = (L == C || 16 * seg + k < L) ? g : 0.f;
         acc += gv;
         gl[k] = acc;
         graw[k] = gv;
@@ -565,8 +582,10 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
           kk += __shfl_xor(kk, o, 64);
         }
         if (p == 0) {
-          sNrm[t] = a.scale / fmaxf(sqrtf(qq), a.l2_eps);
-          sNrm[C + t] = 1.0f / fmaxf(sqrtf(kk), a.l2_eps);
+          // 1 / max(||x||, eps) = min(1 / ||x||, 1 / eps) (rsq(0) is +inf)
+          const float inv_eps = 1.0f / a.l2_eps;
+          sNrm[t] = a.scale * fminf(__builtin_amdgcn_rsqf(qq), inv_eps);
+          sNrm[C + t] = fminf(__builtin_amdgcn_rsqf(kk), inv_eps);
         }
       }
       __syncthreads();
