@@ -271,6 +271,10 @@ __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2
 
 __device__ __forceinline__ float silu_fast(float y) { return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y)); }
 
+// 2^x on v_exp_f32 (the decay factors of phase A are formed from base-2 log-decays)
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp2f_(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ void store_split8(__bf16* hi, __bf16* lo, const float (&x)[8]) {
   const Split8 sp = split(x);
   *reinterpret_cast<bf16x8*>(hi) = sp.hi;
@@ -543,21 +547,23 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     prep_issue<VL>(a, st, knext, tid, nxt, 0);
 
     // ---- P3: bounded-sigmoid gate and its cumulative sum (lane -> channel, 16-token segment);
-    //      gl[k] = Gam(16 seg + k) - Gam(16 seg - 1) stays in registers for P5 ----
+    //      gl[k] = Gam(16 seg + k) - Gam(16 seg - 1) stays in registers for P5.  From here on every
+    //      log-decay is held in base-2 units (Gam log2 e), so each decay factor is one v_exp_f32 ----
     float gl[16];
     float graw[16];  // softplus branch: this token's own log-decay, for the exact diagonal blocks
     {
       const int i = tid & 127, seg = tid >> 7;
       const float Ah = __expf(alog);
       const float dtb = sDtb[i];
+      const float Ah2 = Ah * kLog2e, lb2 = a.lb * kLog2e;
       float acc = 0.f;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const float fv = (float)sF[(16 * seg + k) * PKB + i] + dtb;
         // bounded sigmoid; or softplus, floored at -100 (a decay below e^-100 is zero at fp32
         // precision either way), which keeps the 16-token sums of the log-decay well scaled
-        const float g = SP ? fmaxf(-Ah * (fmaxf(fv, 0.f) + __logf(1.0f + __expf(-fabsf(fv)))), -100.f)
-                           : a.lb * __builtin_amdgcn_rcpf(1.0f + __expf(-Ah * fv));
+        const float g = SP ? fmaxf(-Ah2 * (fmaxf(fv, 0.f) + __logf(1.0f + __expf(-fabsf(fv)))), -100.f * kLog2e)
+                           : lb2 * __builtin_amdgcn_rcpf(1.0f + __expf(-Ah * fv));
         const float gv = (L == C || 16 * seg + k < L) ? g : 0.f;
         acc += gv;
         gl[k] = acc;
@@ -613,8 +619,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
           const float d = gl[k] - gl[0];
-          const float e1 = __expf(d);   // <= 1
-          const float e2 = __expf(-d);  // in [1, e^(15|lb|)]
+          const float e1 = exp2f_(d);   // <= 1
+          const float e2 = exp2f_(-d);  // in [1, e^(15|lb|)]
           const float q = qp[k * PQ] * nq[k];
           const float kv = kp[k * PQ] * nk[k];
           qp[k * PQ] = q * e1;
@@ -630,12 +636,12 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
         }
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          const float e1 = __expf(gl[k] - gl[0]);   // <= 1
-          const float e2 = __expf(gl[15] - gl[k]);  // <= 1: key columns anchored at the sub-chunk's end
+          const float e1 = exp2f_(gl[k] - gl[0]);   // <= 1
+          const float e2 = exp2f_(gl[15] - gl[k]);  // <= 1: key columns anchored at the sub-chunk's end
           qp[k * PQ] = qn[k] * e1;
           rp[k * PKB] = (__bf16)(kn[k] * e1);
           kp[k * PQ] = kn[k] * e2;
-          al[k] = __expf(graw[k]);  // this token's decay
+          al[k] = exp2f_(graw[k]);  // this token's decay
         }
         // the diagonal block entries of this channel (enumerated as in diag_entry), 64 at a time,
         // each batch summed over the wave's 64 channels; the pairwise decay e^(Gam_i - Gam_j) is
@@ -673,13 +679,13 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
         const float GI = sGn[I * D + c];
-        sEn[I * D + c] = __expf(GI);
+        sEn[I * D + c] = exp2f_(GI);
         // column anchors: the sub-chunk's first token, or its last one for the softplus branch
-        sFac[I * D + c] = __expf(GC - (SP ? sGa[I * D + c] : GI));
+        sFac[I * D + c] = exp2f_(GC - (SP ? sGa[I * D + c] : GI));
 #pragma unroll
-        for (int J = 0; J < I; ++J) sE[pair_index(I, J) * D + c] = __expf(GI - (SP ? sGa[J * D + c] : sGn[J * D + c]));
+        for (int J = 0; J < I; ++J) sE[pair_index(I, J) * D + c] = exp2f_(GI - (SP ? sGa[J * D + c] : sGn[J * D + c]));
       }
-      sGC[c] = __expf(GC);
+      sGC[c] = exp2f_(GC);
     }
     __syncthreads();
 
@@ -1371,7 +1377,7 @@ __global__ __launch_bounds__(256) void kda_out_norm_kernel(const float* __restri
   unpack8(g, gv);
   unpack8(w, wv);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = o[e] * rr * wv[e] / (1.0f + __expf(-gv[e]));
+  for (int e = 0; e < 8; ++e) r[e] = o[e] * rr * wv[e] * __builtin_amdgcn_rcpf(1.0f + __expf(-gv[e]));
   store8(out + row * D + c8, r);
 }
 
