@@ -554,6 +554,8 @@ def main():
     # reported beside them)
     share = lambda n: kern[n]["ms_mean"] * kern[n]["launches_per_step"]
     hbm = [n for n in kern if "[varlen]" not in n and "[softplus]" not in n and kern[n]["alg_bytes"]]
+    if not hbm:  # a run of one side line (--only varlen): its own kernels
+        hbm = [n for n in kern if kern[n]["alg_bytes"]]
     if hbm:
         name = max(hbm, key=share)
         k = kern[name]

@@ -11,6 +11,7 @@ namespace kda {
 constexpr int kMaxConvWidth = 8;       // conv taps supported (W - 1 <= 7 raw inputs of state)
 constexpr int kRollbackBatch = 256;    // sequences per rollback launch (accepted counts ride in the args)
 constexpr int kVarlenBatch = 128;      // sequences per variable-length prefill launch (their table rides in the args)
+constexpr int kVarlenGroups = 64;      // sequence groups of a launch's matrix-core state pass
 
 enum IoType { kF32 = 0, kBF16 = 1 };
 
@@ -46,6 +47,10 @@ struct SeqTab {
   int tok0[kVarlenBatch + 1];      // first packed token of sequence i; tok0[n] = tokens of the launch
   int chunk0[kVarlenBatch + 1];    // first chunk block of sequence i
   int slot[kVarlenBatch];          // state / conv-state slot of sequence i
+  // set by the matrix-core launch: its state pass runs one workgroup per (column block, head,
+  // group of consecutive sequences), group g being sequences grp0[g] .. grp0[g + 1] - 1
+  int ngroups;
+  int grp0[kVarlenGroups + 1];
 };
 
 struct RollbackArgs {

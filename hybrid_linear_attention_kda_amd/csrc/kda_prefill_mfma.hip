@@ -302,17 +302,19 @@ __device__ __forceinline__ PrepTask prep_task(int task, int H, int NC, const Seq
     k.ci = NC - 1 - r % NC;
     k.b = r / NC;
   } else {
-    // the sequence holding chunk r: the last i with chunk0[i] <= r
+    // the launch's chunks from its last one down: the sequence holding chunk gc is the last i
+    // with chunk0[i] <= gc (the state pass reads each group of sequences from its first chunk up)
+    const int gc = st.total_chunks - 1 - r;
     int lo = 0, hi = st.n - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (st.chunk0[mid] <= r)
+      if (st.chunk0[mid] <= gc)
         lo = mid;
       else
         hi = mid - 1;
     }
     k.b = lo;
-    k.ci = st.chunk0[lo + 1] - 1 - r;  // the sequence's chunks from its last one down
+    k.ci = gc - st.chunk0[lo];
   }
   return k;
 }
@@ -1088,16 +1090,55 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
   const int H = a.H;
   const int h = blockIdx.x % H;
   const int vb = blockIdx.x / H;
-  const SeqView sv = seq_view<VL>(st, blockIdx.y, a.T, (a.T + C - 1) / C);
-  const int T = sv.len;  // this sequence's tokens (>= 1)
-  const long long tok0 = sv.tok0, slot = sv.slot;
-  const int NC = (T + C - 1) / C;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: role branches are uniform
   const int l16 = lane & 15, lg = lane >> 4;
   const int HD = H * D;
-  const unsigned char* __restrict__ head_ws = ws + ((long long)sv.chunk0 * H + (long long)h * NC) * CH_BYTES;
+  // The workgroup's sequences: group blockIdx.y of the table (consecutive sequences, whose chunks
+  // it runs as one stream, so the tile pipeline stays full across sequence boundaries), or
+  // sequence blockIdx.y of a uniform batch.  Chunk g of the stream is chunk ci of sequence s.
+  const int s_first = VL ? st.grp0[blockIdx.y] : (int)blockIdx.y;
+  const int s_end = VL ? st.grp0[blockIdx.y + 1] : (int)blockIdx.y + 1;
+  const int NCu = (a.T + C - 1) / C;  // chunks per sequence of a uniform batch
+  const int g0 = VL ? st.chunk0[s_first] : 0;
+  const int NG = VL ? st.chunk0[s_end] - g0 : NCu;
+  struct ChunkRef {
+    int s, ci, nc, base;  // sequence, chunk in it, its chunk count, its first chunk in the launch
+    long long tok0;       // the sequence's first packed token
+    int len;              // and its length
+  };
+  // Each call site walks the stream forward through its own cursor: the sequence it reached with
+  // its chunk range and tokens, so the table is read only when a sequence boundary is crossed.
+  struct Cursor {
+    int s, base, next, len;
+    long long tok0;
+  };
+  auto cursor0 = [&]() {
+    return VL ? Cursor{s_first, st.chunk0[s_first], st.chunk0[s_first + 1], st.tok0[s_first + 1] - st.tok0[s_first],
+                       (long long)st.tok0[s_first]}
+              : Cursor{s_first, 0, NCu, a.T, (long long)s_first * a.T};
+  };
+  auto locate = [&](Cursor& cu, int g) -> ChunkRef {
+    if (!VL) return ChunkRef{s_first, g, NCu, s_first * NCu, (long long)s_first * a.T, a.T};
+    const int gc = g0 + g;
+    while (gc >= cu.next && cu.s + 1 < s_end) {
+      ++cu.s;
+      cu.base = cu.next;
+      cu.next = st.chunk0[cu.s + 1];
+      cu.tok0 = st.tok0[cu.s];
+      cu.len = st.tok0[cu.s + 1] - st.tok0[cu.s];
+    }
+    return ChunkRef{cu.s, gc - cu.base, cu.next - cu.base, cu.base, cu.tok0, cu.len};
+  };
+  // tile block of a chunk: sequence-major, then head, then chunk
+  auto chunk_ptr = [&](Cursor& cu, int g) -> const unsigned char* {
+    const ChunkRef r = locate(cu, g);
+    return ws + (((long long)r.base * H + (long long)h * r.nc) + r.ci) * CH_BYTES;
+  };
+  auto seq_tok0 = [&](int sq) -> long long { return VL ? (long long)st.tok0[sq] : (long long)sq * a.T; };
+  auto seq_len = [&](int sq) -> int { return VL ? st.tok0[sq + 1] - st.tok0[sq] : a.T; };
+  auto seq_slot = [&](int sq) -> long long { return VL ? st.slot[sq] : sq; };
   auto wubuf = [&](int c) { return smem + B_WU0 + (c % 3) * WU_BYTES; };
   auto kbuf = [&](int c) { return smem + B_KB0 + (c & 1) * KB_BYTES; };
 
@@ -1105,8 +1146,9 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
   //      K~^T fragments of a chunk (wave 3 also e^Gam_C); cache lines of later chunks touched ----
   const int lw = wave - 8;
   constexpr int N_WU = 5, N_K = 8;
+  Cursor cur_wu = cursor0(), cur_k = cursor0(), cur_t = cursor0();
   auto issue_wu = [&](int cn) {
-    const unsigned char* blk = head_ws + (long long)cn * CH_BYTES;
+    const unsigned char* blk = chunk_ptr(cur_wu, cn);
     unsigned char* wb = wubuf(cn);
 #pragma unroll
     for (int q = 0; q < N_WU; ++q) {
@@ -1116,7 +1158,7 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
     }
   };
   auto issue_k = [&](int cn) {
-    const unsigned char* blk = head_ws + (long long)cn * CH_BYTES;
+    const unsigned char* blk = chunk_ptr(cur_k, cn);
     unsigned char* kb = kbuf(cn);
 #pragma unroll
     for (int q = 0; q < N_K; ++q) {
@@ -1134,7 +1176,7 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
   constexpr int LINES_PER_WG = (LINES + NBLK - 1) / NBLK;
   constexpr int TOUCH_PER_WAVE = (LINES_PER_WG + 4 * 64 - 1) / (4 * 64);
   auto touch_chunk = [&](int cw) {
-    const unsigned char* blk = head_ws + (long long)cw * CH_BYTES;
+    const unsigned char* blk = chunk_ptr(cur_t, cw);
 #pragma unroll
     for (int q = 0; q < TOUCH_PER_WAVE; ++q) {
       const int line = min(vb * LINES_PER_WG + min((q * 4 + lw) * 64 + lane, LINES_PER_WG - 1), LINES - 1);
@@ -1151,14 +1193,14 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
     // it, is then complete too, ahead of the barrier (a) that publishes it.
     issue_wu(0);
     issue_k(0);
-    if (NC > 1) issue_wu(1);
-    if (NC > 2) touch_chunk(2);
+    if (NG > 1) issue_wu(1);
+    if (NG > 2) touch_chunk(2);
     KDA_WAIT_VMCNT(0);
-    for (int ci = 0; ci < NC; ++ci) {
+    for (int ci = 0; ci < NG; ++ci) {
       lds_barrier();  // (a)
-      const bool full = ci + 3 < NC;
-      if (ci + 2 < NC) issue_wu(ci + 2);
-      if (ci + 1 < NC) issue_k(ci + 1);
+      const bool full = ci + 3 < NG;
+      if (ci + 2 < NG) issue_wu(ci + 2);
+      if (ci + 1 < NG) issue_k(ci + 1);
       if (full) touch_chunk(ci + 3);
       // K~^T(0) was waited for before the loop.  Later, the ops this wave issued after the last
       // copy of K~^T(ci) are the touch of chunk ci+2 (during chunk ci-1), then W | Ut(ci+2),
@@ -1173,24 +1215,44 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
       }
       lds_barrier();  // (b)
     }
-    // The new conv state of this workgroup's 48 channels (16 each of q, k and v): the last W-1
-    // raw inputs, from the conv state passed in where the call has fewer tokens.
-    const int j = tid - 8 * 64;
-    if (a.W > 1 && a.conv_out != nullptr && j < 48) {
+    // The new conv state of this workgroup's 48 channels (16 each of q, k and v) for each of its
+    // sequences: the last W-1 raw inputs, from the conv state passed in where a sequence is shorter.
+    // The 256 loader lanes take (sequence, channel) pairs, four at a time with every load issued
+    // before the first store, so a group of sequences costs about one memory round trip.
+    if (a.W > 1 && a.conv_out != nullptr) {
       const int W = a.W, Cq = 3 * HD;
-      const long long c = (long long)(j >> 4) * HD + h * D + vb * NVB + (j & 15);
+      const int npairs = (s_end - s_first) * 48;
       const bf16_t* x = static_cast<const bf16_t*>(a.qkv);
-      const bf16_t* cin = static_cast<const bf16_t*>(a.conv_in) + (slot * Cq + c) * (W - 1);
-      bf16_t* cout = static_cast<bf16_t*>(a.conv_out) + (slot * Cq + c) * (W - 1);
-      bf16_t win[3];
+      for (int p0 = tid - 8 * 64; p0 < npairs; p0 += 4 * 256) {
+        bf16_t win[4][3];
+        long long dst[4];
 #pragma unroll
-      for (int w = 0; w < 3; ++w) {
-        const int tt = T - (W - 1) + w;
-        if (w < W - 1) win[w] = tt >= 0 ? x[(tok0 + tt) * Cq + c] : cin[(W - 1) + tt];
+        for (int q = 0; q < 4; ++q) {
+          const int p = p0 + q * 256;
+          dst[q] = -1;
+          if (p < npairs) {
+            const int sq = s_first + p / 48, j = p % 48;
+            const long long slot = seq_slot(sq), tok0 = seq_tok0(sq);
+            const int T = seq_len(sq);
+            const long long c = (long long)(j >> 4) * HD + h * D + vb * NVB + (j & 15);
+            const bf16_t* cin = static_cast<const bf16_t*>(a.conv_in) + (slot * Cq + c) * (W - 1);
+            dst[q] = (slot * Cq + c) * (W - 1);
+#pragma unroll
+            for (int w = 0; w < 3; ++w) {
+              const int tt = T - (W - 1) + w;
+              if (w < W - 1) win[q][w] = tt >= 0 ? x[(tok0 + tt) * Cq + c] : cin[(W - 1) + tt];
+            }
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (dst[q] < 0) continue;
+          bf16_t* cout = static_cast<bf16_t*>(a.conv_out) + dst[q];
+#pragma unroll
+          for (int w = 0; w < 3; ++w)
+            if (w < W - 1) cout[w] = win[q][w];
+        }
       }
-#pragma unroll
-      for (int w = 0; w < 3; ++w)
-        if (w < W - 1) cout[w] = win[w];
     }
     return;
   }
@@ -1198,8 +1260,8 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
   // ---- state waves (0-3): wave w owns state row tiles w and w + 4 (channels 16t..16t+15); the
   //      lane holds rows 16t+4lg+r of column vb*16 + l16 ----
   f32x4 Sacc[2];
-  const float* s_in = a.state_in + (slot * H + h) * D * D + vb * NVB + l16;
-  float* s_out = a.state_out + (slot * H + h) * D * D + vb * NVB + l16;
+  auto s_in = [&](int sq) { return a.state_in + (seq_slot(sq) * H + h) * D * D + vb * NVB + l16; };
+  auto s_out = [&](int sq) { return a.state_out + (seq_slot(sq) * H + h) * D * D + vb * NVB + l16; };
   // S^T as the split B operand [column][channel]; the lane's four rows are contiguous
   auto write_state_operand = [&]() {
 #pragma unroll
@@ -1255,14 +1317,28 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
   // with the same two barriers per chunk: (a) the state operand and chunk ci's W | Ut are in
   // LDS; (b) U and chunk ci's K~^T are in LDS and every read of the state operand is done.
   if (wave < 4) {
+    {
+      const float* si = s_in(s_first);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Sacc[u][r] = s_in[(16 * (wave + 4 * u) + 4 * lg + r) * D];
+        for (int r = 0; r < 4; ++r) Sacc[u][r] = si[(16 * (wave + 4 * u) + 4 * lg + r) * D];
+    }
     write_state_operand();
     // U = Ut - W S for row tile I = wave, as the split B operand [column][token]
     const int I = wave;
-    for (int ci = 0; ci < NC; ++ci) {
+    Cursor cur_s = cursor0();
+    f32x4 Snext[2];  // the next sequence's state, loaded during the current one's last chunk
+    for (int ci = 0; ci < NG; ++ci) {
+      const ChunkRef rc = locate(cur_s, ci);
+      const bool seq_last = rc.ci == rc.nc - 1, more = ci + 1 < NG;
+      if (seq_last && more) {
+        const float* si = s_in(rc.s + 1);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Snext[u][r] = si[(16 * (wave + 4 * u) + 4 * lg + r) * D];
+      }
       const unsigned char* wb = wubuf(ci);
       lds_barrier();  // (a)
       f32x4 pa = zero4(), pb = zero4();
@@ -1286,11 +1362,21 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
       *reinterpret_cast<bf16x4*>(sUlo + l16 * PVT + 16 * I + 4 * lg) = lo;
       lds_barrier();  // (b)
       state_update(kbuf(ci));
+      if (seq_last) {
+        // the sequence's final state; the next sequence starts from its own slot's state (its
+        // operand replaces the one state_update just wrote, before barrier (a) publishes it)
+        float* so = s_out(rc.s);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) so[(16 * (wave + 4 * u) + 4 * lg + r) * D] = Sacc[u][r];
+        if (more) {
+          Sacc[0] = Snext[0];
+          Sacc[1] = Snext[1];
+          write_state_operand();
+        }
+      }
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s_out[(16 * (wave + 4 * u) + 4 * lg + r) * D] = Sacc[u][r];
   } else {
     // O = P S + Y for row tile I = wave - 4 from P and Y in registers; after barrier (b) the rows
     // are stored and the register set is refilled with the tiles of chunk ci + 2 (two sets
@@ -1299,7 +1385,9 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
     // stores; the last chunk's tiles are loaded again in place of chunks past the end.
     const int I = wave - 4;
     float* scratch = ows + (VL ? (long long)st.tok0[st.n] : (long long)a.B * a.T) * HD + lane * 4;
+    Cursor cur_o = cursor0(), cur_l = cursor0();
     auto chunk_o = [&](int ci, OpTiles& cur) __attribute__((always_inline)) {
+      const ChunkRef rc = locate(cur_o, ci);
       lds_barrier();  // (a)
       f32x4 oa = zero4(), ob = zero4();
 #pragma unroll
@@ -1314,24 +1402,24 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[r] = (oa[r] + ob[r]) + cur.y[r];
       lds_barrier();  // (b)
-      const int c0 = ci * C, L = min(C, T - c0);
-      float* op = ows + ((tok0 + c0) * H + h) * D + vb * NVB + l16;
+      const int c0 = rc.ci * C, L = min(C, rc.len - c0);
+      float* op = ows + ((rc.tok0 + c0) * H + h) * D + vb * NVB + l16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * I + 4 * lg + r;
         *(t < L ? op + (long long)t * HD : scratch + r) = o[r];
       }
-      load_out_tiles(head_ws + (long long)min(ci + 2, NC - 1) * CH_BYTES, I, lane, vb, cur);
+      load_out_tiles(chunk_ptr(cur_l, min(ci + 2, NG - 1)), I, lane, vb, cur);
     };
     OpTiles ta, tb2;
-    load_out_tiles(head_ws, I, lane, vb, ta);
-    load_out_tiles(head_ws + (long long)min(1, NC - 1) * CH_BYTES, I, lane, vb, tb2);
+    load_out_tiles(chunk_ptr(cur_l, 0), I, lane, vb, ta);
+    load_out_tiles(chunk_ptr(cur_l, min(1, NG - 1)), I, lane, vb, tb2);
     int ci = 0;
-    for (; ci + 1 < NC; ci += 2) {
+    for (; ci + 1 < NG; ci += 2) {
       chunk_o(ci, ta);
       chunk_o(ci + 1, tb2);
     }
-    if (ci < NC) chunk_o(ci, ta);
+    if (ci < NG) chunk_o(ci, ta);
   }
 }
 
@@ -1441,9 +1529,26 @@ static hipError_t launch_mfma_t(const LayerArgs& a, const SeqTab& st, void* ws, 
   static const hipError_t attr_b = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_state_kernel<VL>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_B);
   if (attr_b != hipSuccess) return attr_b;
-  const dim3 grid_b(NBLK * a.H, VL ? st.n : a.B);
+  // table mode: the sequences split into groups of consecutive sequences with about equal chunk
+  // counts, as many groups as keep every CU busy with one (column block, head, group) workgroup
+  SeqTab stb = st;
+  if (VL) {
+    int G = (ncu + NBLK * a.H - 1) / (NBLK * a.H);
+    G = G < 1 ? 1 : G > kVarlenGroups ? kVarlenGroups : G;
+    G = G > st.n ? st.n : G;
+    stb.grp0[0] = 0;
+    for (int g = 1; g < G; ++g) {
+      const long long target = (long long)st.total_chunks * g / G;
+      int e = stb.grp0[g - 1] + 1;  // every group keeps at least one sequence
+      while (e < st.n - (G - g) && st.chunk0[e] < target) ++e;
+      stb.grp0[g] = e;
+    }
+    stb.grp0[G] = st.n;
+    stb.ngroups = G;
+  }
+  const dim3 grid_b(NBLK * a.H, VL ? stb.ngroups : a.B);
   timing_begin(kname[1][kn], s);
-  kda_chunk_state_kernel<VL><<<grid_b, NTB, LDS_B, s>>>(a, st, tiles, ows);
+  kda_chunk_state_kernel<VL><<<grid_b, NTB, LDS_B, s>>>(a, stb, tiles, ows);
   timing_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long rows = tokens * a.H;
