@@ -15,9 +15,10 @@
 // chunk-start state S remain in the sequential part.
 //
 // Two phases.
-//  A (chunk-parallel, one workgroup per (sequence, head, chunk), dispatched
-//    chunk-major from the last chunk down, so that the tiles B reads first were
-//    written last and are still in the last-level cache): conv + SiLU,
+//  A (chunk-parallel: persistent workgroups, one per CU, looping over the
+//    (sequence, head, chunk) tasks chunk-major from the last chunk down, so that
+//    the tiles B reads first were written last and are still in the last-level
+//    cache): conv + SiLU,
 //    L2 norms, gate and its cumulative sum, A_kk, T, A_qk, W, and from them
 //      Ut = T (beta V),  Y = A_qk Ut,  P = Q~ - A_qk W,
 //    with Q~ = Q e^Gam and K~ = K e^(Gam_C - Gam).  Everything that does not
@@ -25,7 +26,8 @@
 //    (transposed) as split bf16 (hi + lo), W as bf16, Ut and Y as fp32 and
 //    e^Gam_C as fp32, each in the order the matrix cores consume it.
 //  B (sequential over chunks, one workgroup per (sequence, head, 16-column
-//    block of d_v)): per chunk
+//    block of d_v); with a sequence table, per group of consecutive sequences,
+//    whose chunks it runs as one stream): per chunk
 //      U = Ut - W S,  O = P S + Y,  S <- e^Gam_C S + K~^T U,
 //    with the 128 x 16 state block in MFMA accumulators and the operands of
 //    chunk c+1 loaded into registers while chunk c is computed.  blockIdx.x =
@@ -291,8 +293,9 @@ constexpr int NRV = (RROWS * 16 + NT - 1) / NT;   // raw v row loads per lane
 struct PrepTask {
   int h, b, ci;
 };
-// Tasks run head-fastest and, within a sequence, chunk-major from the last chunk down, so that
-// the tiles phase B reads first were written last and are still in the last-level cache.
+// Tasks run head-fastest and chunk-major from the last chunk down (within each sequence of a
+// uniform batch; over the whole launch with a table), so that the tiles phase B reads first were
+// written last and are still in the last-level cache.
 template <bool VL>
 __device__ __forceinline__ PrepTask prep_task(int task, int H, int NC, const SeqTab& st) {
   PrepTask k;
@@ -1038,7 +1041,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 }
 
 // ---------------------------------------------------------------------------------------------
-// Phase B: one workgroup per (16-column block of d_v, head, sequence), sequential over chunks.
+// Phase B: one workgroup per (16-column block of d_v, head, sequence or group of sequences),
+// sequential over chunks.
 // Waves 0-3 form U = Ut - W S for row tile I = wave and then update state row tiles wave and
 // wave + 4; waves 4-7 form O = P S + Y for row tile I = wave - 4 and, while the state is
 // updated, store it and load their P and Y of two chunks later into registers.  Waves 8-11 only
