@@ -1455,9 +1455,13 @@ __global__ __launch_bounds__(256) void kda_out_norm_kernel(const float* __restri
   const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int c8 = (threadIdx.x & 15) * 8;
   if (row >= rows) return;  // the 16 lanes of a row leave together
-  const float4 a0 = *reinterpret_cast<const float4*>(ows + row * D + c8);
-  const float4 a1 = *reinterpret_cast<const float4*>(ows + row * D + c8 + 4);
-  const uint4 g = *reinterpret_cast<const uint4*>(gout + row * D + c8);
+  // o and the gate are read once: non-temporal loads keep them from displacing cached lines
+  const f32x4 a0v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ows + row * D + c8));
+  const f32x4 a1v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ows + row * D + c8 + 4));
+  const float4 a0 = make_float4(a0v.x, a0v.y, a0v.z, a0v.w), a1 = make_float4(a1v.x, a1v.y, a1v.z, a1v.w);
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 gq = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gout + row * D + c8));
+  const uint4 g = make_uint4(gq.x, gq.y, gq.z, gq.w);
   const uint4 w = *reinterpret_cast<const uint4*>(nw + c8);
   const float o[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
   float ss = 0.f;
