@@ -522,6 +522,39 @@ def test_bf16_varlen_prefill_softplus():
     _check("conv-state pool", cs, ref["conv_state"], 0.0)
 
 
+def test_varlen_full_size_bench_packing_sampled_heads():
+    # the packed call the benchmark times: the 4096 tokens of prefill_t4096 as 16 sequences of the
+    # seeded length mix, all 32 heads, bf16 output, one slot per sequence; the oracle runs every
+    # sequence on heads 3 and 30 (heads are independent)
+    wl = I.WORKLOADS["prefill_t4096"]
+    lens = I.varlen_lengths(wl.T, 16, 8)
+    total = sum(lens)
+    cu = I.cu_seqlens(lens)
+    say(f"case varlen full size: H=32, 16 sequences {lens}, bf16 out, oracle on heads 3 and 30")
+    inp = I.generate(wl.with_(B=1, T=total))
+    rng = np.random.default_rng(11)
+    pool = (rng.standard_normal((16, wl.H, wl.dk, wl.dv)) * 0.3).astype(np.float32)
+    cpool = I.round_to_io(rng.standard_normal((16, wl.c_qkv, wl.W - 1)), wl.io)
+    layer = TT.make_layer(wl, inp, DEV, out="bf16")
+    st = torch.from_numpy(pool).to(DEV)
+    cs = TT.to_device(cpool, wl.io, DEV)
+    tok = {k: v[0] for k, v in TT.token_tensors(wl, inp, 0, total, DEV).items()}
+    out = torch.empty((total, wl.H * wl.dv), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(abi.kda_prefill_varlen_workspace_size(layer, cu), dtype=torch.uint8, device=DEV)
+    abi.kda_prefill_varlen(layer, cu, None, tok["qkv"], tok["f"], tok["beta"], tok["g_out"], st, cs, out,
+                           workspace=ws)
+    torch.cuda.synchronize()
+    heads = [3, 30]
+    swl, sinp = I.select_heads(wl.with_(T=total), inp, heads)
+    oc, ch = head_channels(wl, heads)
+    pk = {k: sinp[k][0] for k in ("qkv", "f", "beta", "g_out")}
+    ref = O.kda_prefill_varlen(pu.params(swl, sinp), cu, None, pk["qkv"], pk["f"], pk["beta"], pk["g_out"],
+                               pool[:, heads], cpool[:, ch])
+    _check("out (sampled heads)", out[:, oc], ref["out"], TOL_BF16_OUT)
+    _check("state pool (sampled heads)", st[:, heads], ref["state"], TOL["bf16"])
+    _check("conv-state pool (sampled heads)", cs[:, ch], ref["conv_state"], 0.0)
+
+
 def test_tiny_fp32_varlen_prefill():
     wl = I.WORKLOADS["tiny_fp32"]
     lens = [5, 0, 17, 64, 1]
