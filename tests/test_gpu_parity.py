@@ -193,6 +193,47 @@ def test_tiny_fp32_verify_tape_and_commit():
     _check("committed conv state", cs2, ref_c, 0.0)
 
 
+def test_tiny_fp32_verify_max_draft_length():
+    # the longest draft block the boundary takes (T_d = 255): 31 full groups of the verify kernel's
+    # 8-token input prefetch and a partial one, and the tape commit's 8-token staging with a partial
+    # last group; snapshots, rollback, tape and commit against the oracle
+    Td = 255
+    wl = I.WORKLOADS["tiny_fp32"].with_(T=Td, B=3, prefix_T=6, seed=77)
+    say(f"case tiny_fp32 verify T_d={Td} (the maximum) + rollback, tape + commit")
+    inp = I.generate(wl)
+    pre = oracle_layer(wl, inp, 0, 6, inp["state0"], inp["conv_state0"])
+    S0, C0 = pre["state"].astype(np.float32), pre["conv_state"].astype(np.float32)
+    layer = TT.make_layer(wl, inp, DEV)
+    tok = TT.token_tensors(wl, inp, 6, 6 + Td, DEV)
+    st1, cs1 = _dev_state(wl, inp, S0, C0)
+    snaps = torch.empty((3, Td, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=DEV)
+    out1 = torch.empty((3, Td, wl.H * wl.dv), dtype=torch.float32, device=DEV)
+    abi.kda_verify_block(layer, tok["qkv"], tok["f"], tok["beta"], tok["g_out"], st1, cs1, snaps, out1)
+    st2, cs2 = _dev_state(wl, inp, S0, C0)
+    tape = torch.empty((3, Td, wl.H, 3, wl.dk), dtype=torch.float32, device=DEV)
+    out2 = torch.empty_like(out1)
+    abi.kda_verify_block_tape(layer, tok["qkv"], tok["f"], tok["beta"], tok["g_out"], st2, cs2, tape, out2)
+    torch.cuda.synchronize()
+    ver = oracle_layer(wl, inp, 6, 6 + Td, S0, C0, record_states=True)
+    _check("verify out", out1, ver["out"], TOL["f32"])
+    _check("snapshots", snaps, ver["states"], TOL["f32"])
+    _bit_equal("verify out, tape vs snapshot path", out2, out1)
+    accepted = [0, Td, 131]
+    abi.kda_rollback(layer, accepted, snaps, tok["qkv"], st1, cs1)
+    abi.kda_commit_tape(layer, accepted, tape, tok["qkv"], st2, cs2)
+    torch.cuda.synchronize()
+    _bit_equal("committed state, tape vs snapshot path", st2, st1)
+    _bit_equal("committed conv state, tape vs snapshot path", cs2, cs1)
+    for b, m in enumerate(accepted):
+        ref_s = S0[b] if m == 0 else ver["states"][b, m - 1]
+        _check(f"state b={b} m={m}", st1[b], ref_s, TOL["f32"])
+        sub = dict(inp)
+        for k in ("qkv", "f", "beta", "g_out"):
+            sub[k] = inp[k][b:b + 1]
+        ref_c = oracle_layer(wl, sub, 6, 6 + m, S0[b:b + 1], C0[b:b + 1])["conv_state"][0]
+        _check(f"conv state b={b} m={m}", cs1[b], ref_c, 0.0)
+
+
 def test_verify_tape_b16_full_size_with_commit():
     wl = I.WORKLOADS["verify_b16"]
     say("case verify_b16 full size (B=16, T_d=8, H=32, d=128) with replay tape + commit")
