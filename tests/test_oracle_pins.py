@@ -130,6 +130,53 @@ def test_decay_gate_range_bias_order_and_head_broadcast():
     assert np.all(np.exp(O.decay_gate(f, A_log, dt, 0.0, H, dk)) == 1.0)
 
 
+def _gate_hand_worked_passes(gate_fn):
+    # tests/golden/gate_hand_worked.json: A = exp(A_log) an integer, A (f + dt_bias) an integer
+    d = json.load(open(os.path.join(GOLDEN, "gate_hand_worked.json")))
+    for c in d["cases"]:
+        g = gate_fn(np.array([[c["f"]]]), np.array([c["A_log"]]), np.array([c["dt_bias"]]), c["lb"], 1, 1)
+        if not abs(float(g[0, 0, 0]) - c["g"]) <= 1e-14 * abs(c["g"]):
+            return False
+    return True
+
+
+def _gate_monotone_passes(gate_fn):
+    # With lb < 0 and a positive rate A: a larger f + dt_bias decays more (g falls towards lb), a
+    # smaller one decays less (g rises towards 0); for f + dt_bias > 0 a larger A_log decays more.
+    z = np.linspace(-3.0, 3.0, 25)[:, None]
+    g = gate_fn(z, np.array([0.7]), np.zeros(1), -5.0, 1, 1)[:, 0, 0]
+    if not np.all(np.diff(g) < 0):
+        return False
+    A_logs = np.linspace(-1.0, 2.5, 8)
+    gA = np.array([gate_fn(np.array([[0.4]]), np.array([a]), np.zeros(1), -5.0, 1, 1)[0, 0, 0] for a in A_logs])
+    return bool(np.all(np.diff(gA) < 0))
+
+
+def _gate_through_layer_passes():
+    # beta = 0 leaves only the decay: one token from S0 = 1 gives S1 = exp(g) with g the hand-worked
+    # case 0 value (A_log = ln 2, f + dt_bias = 0.5, lb = -5) on every channel
+    d = json.load(open(os.path.join(GOLDEN, "gate_hand_worked.json")))["cases"][0]
+    H, dk, dv, W = 1, 4, 4, 1
+    c = 2 * H * dk + H * dv
+    p = O.KdaParams(H=H, dk=dk, dv=dv, conv_w=np.ones((c, W)), A_log=np.array([d["A_log"]]),
+                    dt_bias=np.full(H * dk, d["dt_bias"]), norm_w=np.ones(dv), lb=d["lb"], scale=1.0)
+    r = O.kda_layer(p, RNG.standard_normal((1, 1, c)), np.full((1, 1, H * dk), d["f"]), np.zeros((1, 1, H)),
+                    np.zeros((1, 1, H * dv)), np.ones((1, H, dk, dv)), np.zeros((1, c, 0)))
+    return bool(np.allclose(r["state"], math.exp(d["g"]), rtol=1e-14, atol=0))
+
+
+def test_decay_gate_hand_worked_values():
+    assert _gate_hand_worked_passes(O.decay_gate)
+
+
+def test_decay_gate_is_monotone_in_the_pre_activation_and_the_rate():
+    assert _gate_monotone_passes(O.decay_gate)
+
+
+def test_decay_gate_hand_worked_value_through_the_layer():
+    assert _gate_through_layer_passes()
+
+
 def test_softplus_against_mpmath_and_tails():
     mpmath.mp.dps = 40
     for xv in (-700.0, -40.0, -5.0, -1.0, 0.0, 1e-8, 0.5, 3.0, 30.0, 700.0):
@@ -255,25 +302,49 @@ def test_one_token_from_zero_state(scale):
     np.testing.assert_allclose(S, beta[0][:, None, None] * k[0][:, :, None] * v[0][:, None, :], rtol=1e-15)
 
 
-def test_one_token_from_zero_state_through_the_layer():
-    # Identity conv (only the current-token tap = 1): q = silu(x_q)/||.||, same for k; v = silu(x_v).
+def _one_token_layer_passes(scale):
+    # Identity conv (only the current-token tap = 1): q = scale silu(x_q)/||.||, k = silu(x_k)/||.||,
+    # v = silu(x_v); one token from a zero state gives o = beta (q.k) v = scale beta cos(q^, k^) v, so
+    # the scale shows in o only when it is applied after the normalisation
     H, dk, dv, W = 2, 8, 8, 4
     c = 2 * H * dk + H * dv
     conv_w = np.zeros((c, W))
     conv_w[:, W - 1] = 1.0
     p = O.KdaParams(H=H, dk=dk, dv=dv, conv_w=conv_w, A_log=np.zeros(H), dt_bias=np.zeros(H * dk),
-                    norm_w=np.ones(dv), lb=-5.0, scale=1.0)
-    x = RNG.standard_normal((1, 1, c))
+                    norm_w=np.ones(dv), lb=-5.0, scale=scale)
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((1, 1, c))
     beta = np.array([[[0.3, 0.8]]])
-    r = O.kda_layer(p, x, RNG.standard_normal((1, 1, H * dk)), beta, np.zeros((1, 1, H * dv)),
+    r = O.kda_layer(p, x, rng.standard_normal((1, 1, H * dk)), beta, np.zeros((1, 1, H * dv)),
                     np.zeros((1, H, dk, dv)), np.zeros((1, c, W - 1)))
     s = x[0, 0] / (1 + np.exp(-x[0, 0]))
     for h in range(H):
         qh = s[h * dk:(h + 1) * dk]
         kh = s[H * dk + h * dk: H * dk + (h + 1) * dk]
         vh = s[2 * H * dk + h * dv: 2 * H * dk + (h + 1) * dv]
-        expect = beta[0, 0, h] * (qh @ kh) / (np.linalg.norm(qh) * np.linalg.norm(kh)) * vh
-        np.testing.assert_allclose(r["o"][0, 0, h], expect, rtol=1e-13, atol=1e-15)
+        expect = scale * beta[0, 0, h] * (qh @ kh) / (np.linalg.norm(qh) * np.linalg.norm(kh)) * vh
+        if not np.allclose(r["o"][0, 0, h], expect, rtol=1e-13, atol=1e-15):
+            return False
+    return True
+
+
+def _query_norm_passes():
+    # after the prologue every query has length `scale` and every key length 1 (conv outputs far
+    # above the 1e-6 clamp)
+    wl, inp, p = _tiny(9)
+    p = replace(p, scale=0.3)
+    q, k, _, _, _ = O.prologue(p, inp["qkv"][0], inp["f"][0], inp["conv_state0"][0])
+    return bool(np.allclose(np.linalg.norm(q, axis=-1), 0.3, rtol=1e-14, atol=0)
+                and np.allclose(np.linalg.norm(k, axis=-1), 1.0, rtol=1e-14, atol=0))
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.3])
+def test_one_token_from_zero_state_through_the_layer(scale):
+    assert _one_token_layer_passes(scale)
+
+
+def test_prologue_query_length_is_the_scale():
+    assert _query_norm_passes()
 
 
 def test_beta_zero_decay_zero_leaves_state_bit_exact():
@@ -689,6 +760,44 @@ def test_pins_catch_planted_mistakes(kind):
     rec = _mutant(kind)
     assert not _hand_worked_passes(rec)
     assert not _brute_force_passes(rec)
+
+
+def _mutant_gate(kind):
+    # copies of the bounded gate with a planted mistake in the rate A
+    def gate(f, A_log, dt_bias, lb, H, dk, kind_=None):
+        f = np.asarray(f, dtype=np.float64)
+        z = (f + np.asarray(dt_bias, dtype=np.float64)[None, :]).reshape(f.shape[0], H, dk)
+        A_log = np.asarray(A_log, dtype=np.float64)
+        A = {"A_is_A_log": A_log, "A_negative": -np.exp(A_log)}[kind][None, :, None]
+        return float(lb) / (1.0 + np.exp(-A * z))
+    return gate
+
+
+def _mutant_prologue_scale_before_norm():
+    real = O.prologue
+
+    def prologue(p, qkv, f, conv_state):
+        q, k, v, g, cs = real(replace(p, scale=1.0), qkv, f, conv_state)
+        # the mistake: scale the raw query, then normalise it (the scale cancels)
+        return O.l2_normalize(p.scale * q, p.l2_eps), k, v, g, cs
+    return prologue
+
+
+@pytest.mark.parametrize("kind", ["A_is_A_log", "A_negative"])
+def test_gate_pins_catch_planted_mistakes(kind, monkeypatch):
+    mut = _mutant_gate(kind)
+    assert not _gate_hand_worked_passes(mut)
+    if kind == "A_negative":
+        assert not _gate_monotone_passes(mut)
+    monkeypatch.setattr(O, "decay_gate", mut)
+    assert not _gate_through_layer_passes()
+
+
+def test_scale_pins_catch_scale_before_the_norm(monkeypatch):
+    assert _one_token_layer_passes(0.3) and _query_norm_passes()
+    monkeypatch.setattr(O, "prologue", _mutant_prologue_scale_before_norm())
+    assert not _one_token_layer_passes(0.3)
+    assert not _query_norm_passes()
 
 
 def test_scalar_gate_makes_key_and_value_axis_agree():
