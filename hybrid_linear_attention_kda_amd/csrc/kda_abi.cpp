@@ -431,6 +431,10 @@ kda_status kda_rollback(const kda_layer_desc* desc, int32_t B, int32_t T_d, cons
 
 size_t kda_verify_tape_size(const kda_layer_desc* desc, int32_t B, int32_t T_d) {
   if (check_desc(desc) != KDA_OK || check_batch(B, T_d, desc->num_heads) != KDA_OK) return (size_t)-1;
+  if (T_d > 255) {
+    fail(KDA_ERR_UNSUPPORTED, "draft block T_d = %d > 255", T_d);
+    return (size_t)-1;
+  }
   return (size_t)B * (size_t)T_d * (size_t)desc->num_heads * 3u * (size_t)desc->head_dim_k * sizeof(float);
 }
 

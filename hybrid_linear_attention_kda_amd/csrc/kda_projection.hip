@@ -168,8 +168,26 @@ thread_local LtState g_lt;
 
 // D [T, m] (row-major, leading dimension ldd) = X [T, k] . Wr^T, Wr the m rows of a row-major [*, k]
 // bf16 weight starting at Wr.  Column-major view: D^T (m x T) = op_T(Wr as k x m) . (X as k x T).
-bool gemm_xwt(int T, int k, int m, const void* X, const void* Wr, hipDataType dtype, void* D, int ldd, void* ws,
-              size_t wsb, hipStream_t s, const char* name, char* err, size_t errlen) {
+// A GEMM is resolved (descriptors and algorithm) before anything is launched, so that a call whose
+// second GEMM has no algorithm fails with no buffer touched.  The algorithm is chosen within
+// kProjGemmWorkspace bytes, the library's share of every valid workspace, so an algorithm cached
+// under one call fits every later call of the same shape.
+struct Gemm {
+  hipblasLtMatmulDesc_t op = nullptr;
+  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
+  hipblasLtMatmulAlgo_t algo{};
+  Gemm() = default;
+  Gemm(const Gemm&) = delete;
+  Gemm& operator=(const Gemm&) = delete;
+  ~Gemm() {
+    if (ld) hipblasLtMatrixLayoutDestroy(ld);
+    if (lb) hipblasLtMatrixLayoutDestroy(lb);
+    if (la) hipblasLtMatrixLayoutDestroy(la);
+    if (op) hipblasLtMatmulDescDestroy(op);
+  }
+};
+
+bool lt_handle(char* err, size_t errlen) {
   bool ok = true;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
@@ -183,52 +201,56 @@ bool gemm_xwt(int T, int k, int m, const void* X, const void* Wr, hipDataType dt
     if (!ok) return false;
     g_lt.device = dev;
   }
-  hipblasLtMatmulDesc_t op = nullptr;
-  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
-  hipblasLtMatmulPreference_t pref = nullptr;
-  LT_TRY(hipblasLtMatmulDescCreate(&op, HIPBLAS_COMPUTE_32F, HIP_R_32F), "desc");
+  return true;
+}
+
+bool gemm_resolve(Gemm& g, int T, int k, int m, hipDataType dtype, int ldd, char* err, size_t errlen) {
+  bool ok = true;
+  LT_TRY(hipblasLtMatmulDescCreate(&g.op, HIPBLAS_COMPUTE_32F, HIP_R_32F), "desc");
   const hipblasOperation_t opT = HIPBLAS_OP_T, opN = HIPBLAS_OP_N;
-  if (ok) LT_TRY(hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof(opT)), "transa");
-  if (ok) LT_TRY(hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof(opN)), "transb");
-  if (ok) LT_TRY(hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, k, m, k), "layout A");
-  if (ok) LT_TRY(hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, k, T, k), "layout B");
-  if (ok) LT_TRY(hipblasLtMatrixLayoutCreate(&ld, dtype, m, T, ldd), "layout D");
-  hipblasLtMatmulAlgo_t algo{};
-  if (ok) {
-    const GemmKey key{m, T, k, ldd, (int)dtype};
-    auto it = g_lt.algos.find(key);
-    if (it != g_lt.algos.end()) {
-      algo = it->second;
-    } else {
-      LT_TRY(hipblasLtMatmulPreferenceCreate(&pref), "preference");
-      const uint64_t cap = wsb;
-      if (ok)
-        LT_TRY(hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &cap, sizeof(cap)),
-               "workspace preference");
-      hipblasLtMatmulHeuristicResult_t res{};
-      int nres = 0;
-      if (ok) LT_TRY(hipblasLtMatmulAlgoGetHeuristic(g_lt.handle, op, la, lb, ld, ld, pref, 1, &res, &nres), "heuristic");
-      if (ok && (nres < 1 || res.state != HIPBLAS_STATUS_SUCCESS || res.workspaceSize > wsb)) {
-        snprintf(err, errlen, "hipBLASLt has no algorithm for this GEMM within %zu workspace bytes", wsb);
-        ok = false;
-      }
-      if (ok) {
-        algo = res.algo;
-        g_lt.algos[key] = algo;
-      }
-    }
+  if (ok) LT_TRY(hipblasLtMatmulDescSetAttribute(g.op, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof(opT)), "transa");
+  if (ok) LT_TRY(hipblasLtMatmulDescSetAttribute(g.op, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof(opN)), "transb");
+  if (ok) LT_TRY(hipblasLtMatrixLayoutCreate(&g.la, HIP_R_16BF, k, m, k), "layout A");
+  if (ok) LT_TRY(hipblasLtMatrixLayoutCreate(&g.lb, HIP_R_16BF, k, T, k), "layout B");
+  if (ok) LT_TRY(hipblasLtMatrixLayoutCreate(&g.ld, dtype, m, T, ldd), "layout D");
+  if (!ok) return false;
+  const GemmKey key{m, T, k, ldd, (int)dtype};
+  auto it = g_lt.algos.find(key);
+  if (it != g_lt.algos.end()) {
+    g.algo = it->second;
+    return true;
   }
-  if (ok) {
-    const float one = 1.f, zero = 0.f;
-    timing_begin(name, s);
-    LT_TRY(hipblasLtMatmul(g_lt.handle, op, &one, Wr, la, X, lb, &zero, D, ld, D, ld, &algo, ws, wsb, s), "matmul");
-    timing_end(s);
-  }
+  hipblasLtMatmulPreference_t pref = nullptr;
+  LT_TRY(hipblasLtMatmulPreferenceCreate(&pref), "preference");
+  const uint64_t cap = kProjGemmWorkspace;
+  if (ok)
+    LT_TRY(hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &cap, sizeof(cap)),
+           "workspace preference");
+  hipblasLtMatmulHeuristicResult_t res{};
+  int nres = 0;
+  if (ok) LT_TRY(hipblasLtMatmulAlgoGetHeuristic(g_lt.handle, g.op, g.la, g.lb, g.ld, g.ld, pref, 1, &res, &nres),
+                 "heuristic");
   if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-  if (ld) hipblasLtMatrixLayoutDestroy(ld);
-  if (lb) hipblasLtMatrixLayoutDestroy(lb);
-  if (la) hipblasLtMatrixLayoutDestroy(la);
-  if (op) hipblasLtMatmulDescDestroy(op);
+  if (ok && (nres < 1 || res.state != HIPBLAS_STATUS_SUCCESS || res.workspaceSize > kProjGemmWorkspace)) {
+    snprintf(err, errlen, "hipBLASLt has no algorithm for this GEMM within %zu workspace bytes", kProjGemmWorkspace);
+    ok = false;
+  }
+  if (ok) {
+    g.algo = res.algo;
+    g_lt.algos[key] = g.algo;
+  }
+  return ok;
+}
+
+bool gemm_run(const Gemm& g, const void* X, const void* Wr, void* D, void* ws, hipStream_t s, const char* name,
+              char* err, size_t errlen) {
+  bool ok = true;
+  const float one = 1.f, zero = 0.f;
+  timing_begin(name, s);
+  LT_TRY(hipblasLtMatmul(g_lt.handle, g.op, &one, Wr, g.la, X, g.lb, &zero, D, g.ld, D, g.ld, &g.algo, ws,
+                         kProjGemmWorkspace, s),
+         "matmul");
+  timing_end(s);
   return ok;
 }
 
@@ -244,13 +266,15 @@ hipError_t launch_projection(const ProjArgs& p, hipStream_t s, char* err, size_t
   float* act = static_cast<float*>(p.ws);
   const size_t act_bytes = ((size_t)p.T * NS * sizeof(float) + 255) / 256 * 256;
   void* gws = static_cast<char*>(p.ws) + act_bytes;
-  const size_t gwsb = p.ws_bytes - act_bytes;
   const bf16_t* w = static_cast<const bf16_t*>(p.w_in);
   const hipDataType dt = p.out_type == kBF16 ? HIP_R_16BF : HIP_R_32F;
-  if (!gemm_xwt(p.T, p.hidden, N3, p.x, w, dt, p.qkv, N3, gws, gwsb, s, "hipblaslt_gemm[qkv]", err, errlen))
-    return hipErrorUnknown;
-  if (!gemm_xwt(p.T, p.hidden, NS, p.x, w + (long long)N3 * p.hidden, HIP_R_32F, act, NS, gws, gwsb, s,
-                "hipblaslt_gemm[rank|beta]", err, errlen))
+  // both GEMMs are resolved before the first launch
+  if (!lt_handle(err, errlen)) return hipErrorUnknown;
+  Gemm g_qkv, g_rank;
+  if (!gemm_resolve(g_qkv, p.T, p.hidden, N3, dt, N3, err, errlen)) return hipErrorUnknown;
+  if (!gemm_resolve(g_rank, p.T, p.hidden, NS, HIP_R_32F, NS, err, errlen)) return hipErrorUnknown;
+  if (!gemm_run(g_qkv, p.x, w, p.qkv, gws, s, "hipblaslt_gemm[qkv]", err, errlen)) return hipErrorUnknown;
+  if (!gemm_run(g_rank, p.x, w + (long long)N3 * p.hidden, act, gws, s, "hipblaslt_gemm[rank|beta]", err, errlen))
     return hipErrorUnknown;
   // per domain ceil(tiles / 8) row tiles, times the (column block, which) pairs
   const int tiles = (p.T + PJ_ROWS - 1) / PJ_ROWS;

@@ -29,6 +29,10 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller, row-major,
  *     16-byte aligned.  The library allocates no device memory and keeps no
  *     state between calls; prefill scratch comes from the caller's workspace.
+ *     One exception, invisible in results: kda_input_projection keeps a
+ *     per-thread hipBLASLt handle (created on the first call on a device, so
+ *     whatever the GEMM library allocates for it stays until the thread ends)
+ *     and the algorithm it chose per GEMM shape.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream).  The returned status covers argument validation and launch
  *     errors only.  Validation runs before any launch: a call that returns an
@@ -116,7 +120,10 @@ size_t kda_prefill_workspace_size(const kda_layer_desc* desc, int32_t B, int32_t
 
 /*
  * Chunked prefill of T tokens on each of B sequences (steps 1-6 above; the
- * recurrence in chunked WY/UT form with chunk desc->chunk_size).
+ * recurrence in chunked WY/UT form with chunk desc->chunk_size).  It plays
+ * the role of the "chunked fallback" delta net of llama.cpp PR #27754, KDA
+ * commit; chained calls carrying state and conv_state equal one call, as the
+ * glm53-flash-mlx README's tests require of split prefills (5 + 7 tokens).
  *   qkv        [B, T, 3*H*d]   raw pre-conv projections        (in)
  *   f          [B, T, H*d]     gate pre-activation             (in)
  *   beta       [B, T, H]       delta-rule step, in (0, 1)      (in)
@@ -163,7 +170,10 @@ kda_status kda_prefill_varlen(const kda_layer_desc* desc, int32_t N, const int32
 
 /*
  * One decode step: one new token per sequence, state and conv_state updated
- * in place.  Tensor shapes as kda_prefill with T = 1.
+ * in place.  Tensor shapes as kda_prefill with T = 1.  It plays the role of
+ * build_delta_net_autoregressive (llama.cpp PR #27754, KDA commit: the
+ * token-by-token path, key-axis decay); decoding token by token equals one
+ * prefill over the same tokens (glm53-flash-mlx README, tests).
  */
 kda_status kda_decode_step(const kda_layer_desc* desc, int32_t B, const void* qkv, const void* f,
                            const void* beta, const void* g_out, float* state, void* conv_state, void* out,
@@ -171,7 +181,14 @@ kda_status kda_decode_step(const kda_layer_desc* desc, int32_t B, const void* qk
 
 /*
  * Verify a draft block of T_d tokens per sequence from the live state,
- * recording the state after every token.  state and conv_state are read only.
+ * recording the state after every token, so that the state can roll back to
+ * any accepted prefix (dflash-mlx issue #63, "What the backend needs": KDA
+ * state rollback; "Context": the DFlash2 drafter proposes blocks of 8; the
+ * conv state is one contiguous block so that it can be snapshotted, llama.cpp
+ * PR #27754, KDA commit).  state and conv_state are read only.
+ * 1 <= T_d <= 255 (T_d = 0 or B = 0 is a no-op; T_d > 255 returns
+ * KDA_ERR_UNSUPPORTED); the same limit holds for kda_rollback,
+ * kda_verify_block_tape, kda_commit_tape and kda_verify_tape_size.
  *   qkv, f, beta, g_out  [B, T_d, ...] as kda_prefill
  *   snaps  [B, T_d, H, d, d] fp32: snaps[b, t] = state after draft token t+1 (out)
  *   out    [B, T_d, H*d] (out)
@@ -181,7 +198,9 @@ kda_status kda_verify_block(const kda_layer_desc* desc, int32_t B, int32_t T_d, 
                             float* snaps, void* out, void* stream);
 
 /*
- * Commit the accepted prefix of a verified block.  accepted_host is a HOST
+ * Commit the accepted prefix of a verified block (dflash-mlx issue #63, "What
+ * the backend needs"; a rollback depth must never be silently clamped,
+ * llama.cpp PR #27754, KDA commit on n_rs_seq).  accepted_host is a HOST
  * array of B counts m_b in 0..T_d (outside that range the call fails; no
  * clamping).  For each b with m_b > 0:
  *   state[b]      <- snaps[b, m_b - 1]
@@ -202,7 +221,8 @@ kda_status kda_rollback(const kda_layer_desc* desc, int32_t B, int32_t T_d, cons
  * read and write) instead of 1 + T_d + 1.
  *
  * kda_verify_tape_size: bytes of the tape for (desc, B, T_d),
- *   B * T_d * H * 3 * d * 4; (size_t)-1 if the arguments are invalid.
+ *   B * T_d * H * 3 * d * 4; (size_t)-1 if the arguments are invalid or
+ *   T_d > 255.
  * kda_verify_block_tape: as kda_verify_block (same outputs, bit-identical),
  *   but writes
  *     tape [B, T_d, H, 3, d] fp32: tape[b, t, h] = (alpha, k, u) of token t

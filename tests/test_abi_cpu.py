@@ -139,6 +139,32 @@ def test_verify_tape_and_commit_validation():
     assert lib.kda_verify_tape_size(ctypes.byref(bad), 4, 8) == ctypes.c_size_t(-1).value
 
 
+def test_draft_block_limit_is_refused_by_every_call():
+    # T_d <= 255 is the documented limit of the verify, rollback, tape and commit calls and of the
+    # tape-size query; T_d = 256 is refused up front with KDA_ERR_UNSUPPORTED, never clamped
+    lib = abi.load()
+    d = desc()
+    P = FAKE
+    acc = (ctypes.c_int32 * 1)(3)
+    accp = ctypes.cast(acc, ctypes.c_void_p)
+    calls = {
+        "kda_verify_block": lambda T_d: lib.kda_verify_block(ctypes.byref(d), 1, T_d, P, P, P, P, P, P, P, P, None),
+        "kda_verify_block_tape": lambda T_d: lib.kda_verify_block_tape(ctypes.byref(d), 1, T_d, P, P, P, P, P, P, P, P,
+                                                                       None),
+        "kda_rollback": lambda T_d: lib.kda_rollback(ctypes.byref(d), 1, T_d, accp, P, P, P, P, None),
+        "kda_commit_tape": lambda T_d: lib.kda_commit_tape(ctypes.byref(d), 1, T_d, accp, P, P, P, P, None),
+    }
+    for name, call in calls.items():
+        assert call(256) == abi.KDA_ERR_UNSUPPORTED, name
+        assert b"T_d = 256 > 255" in lib.kda_last_error(), name
+    assert lib.kda_verify_tape_size(ctypes.byref(d), 2, 256) == ctypes.c_size_t(-1).value
+    assert b"T_d = 256 > 255" in lib.kda_last_error()
+    # the largest block is sized exactly: B * T_d * H * 3 * d fp32
+    assert lib.kda_verify_tape_size(ctypes.byref(d), 2, 255) == 2 * 255 * 2 * 3 * 16 * 4
+    assert lib.kda_verify_tape_size(ctypes.byref(d), 0, 8) == 0
+    assert lib.kda_verify_tape_size(ctypes.byref(d), -1, 8) == ctypes.c_size_t(-1).value
+
+
 def test_varlen_validation_and_workspace_size():
     lib = abi.load()
     d = desc()
