@@ -6,6 +6,8 @@ One step = one pass over every call of the path on its layer-shaped workload:
             (123..628 tokens), each from its own zero state slot
   decode    64 sequences x 32 heads x 128x128 fp32 state, one token each
   softplus  prefill_t4096 and decode_b64 again with the softplus decay branch (no lower bound)
+  strong    prefill_t4096 again with the bounded gate at gate_lower_bound = -8 (below the range of
+            start-anchored sub-chunks: end-anchored ones with exact diagonal blocks)
   projection  the layer's input projection for those 4096 tokens: hidden 4096 -> q|k|v, f, beta,
             g_out (H=32, d=128, rank 128; the q|k|v|f_a|g_a|b projections as one GEMM)
   verify    16 sequences x 8 draft tokens with per-token snapshots, then rollback
@@ -111,6 +113,7 @@ def kernel_alg_bytes(kernel, wp, wd, wv, accepted):
     }
     for k in ("kda_chunk_prep_kernel", "kda_chunk_state_kernel", "kda_out_norm_kernel"):
         table[k + "[softplus]"] = table[k]  # the softplus decay branch: the same bytes
+        table[k + "[strong]"] = table[k]    # the bounded gate below -5.5: the same bytes
     return table.get(kernel)
 
 
@@ -170,8 +173,9 @@ def short_kernel_name(full):
     targs = m.group(2) or ""
     if name in ("kda_chunk_prep_kernel", "kda_chunk_state_kernel") and targs.startswith("<true"):
         name += "[varlen]"
-    if name == "kda_chunk_prep_kernel" and targs.endswith(", true>"):
-        name += "[softplus]"
+    if name == "kda_chunk_prep_kernel":
+        gk = targs.rstrip(">").split(",")[-1].strip()
+        name += {"1": "[softplus]", "2": "[strong]"}.get(gk, "")
     if name == "kda_recurrent_kernel" and m.group(2):
         targs = m.group(2)
         name += "[verify_tape]" if ", true, true," in targs else "[verify]" if ", true," in targs else "[decode]"
@@ -217,29 +221,129 @@ def pmc_summary(fetch_dir, write_dir, command):
     print(json.dumps(out, indent=1))
 
 
-def cpu_baseline(sample_heads: int, T: int):
-    """The float64 oracle, as it stands, on a bounded sample of the prefill workload:
-    `sample_heads` of the 32 heads over T tokens (heads are independent, so the
-    full layer costs 32 / sample_heads times as much)."""
-    from threadpoolctl import threadpool_limits
+def mfma_summary(pmc_dir, command, n_cu=256):
+    """Per-kernel matrix-core busy fraction from one rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES,
+    GRBM_GUI_ACTIVE, SQ_INSTS_MFMA and SQ_INSTS_VALU: busy / (GRBM_GUI_ACTIVE x 4 SIMDs x CUs), the
+    mean over the kernel's dispatches; stored in profiles/pmc_mfma.json with the sources' sha256."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            name = short_kernel_name(r["Kernel_Name"])
+            if name is None:
+                continue
+            key = (name, r.get("Dispatch_Id", r.get("Correlation_Id", "")))
+            vals.setdefault(name, {}).setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    out = {"command": command, "source_sha256": source_fingerprint(), "n_cu": n_cu, "kernels": {}}
+    for name, disp in sorted(vals.items()):
+        fr, mf, va = [], [], []
+        for c in disp.values():
+            if c.get("GRBM_GUI_ACTIVE", 0) > 0 and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                fr.append(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * 4 * n_cu))
+            if "SQ_INSTS_MFMA" in c:
+                mf.append(c["SQ_INSTS_MFMA"])
+            if "SQ_INSTS_VALU" in c:
+                va.append(c["SQ_INSTS_VALU"])
+        out["kernels"][name] = {"mfma_busy_frac": float(np.mean(fr)) if fr else None,
+                                "insts_mfma": float(np.mean(mf)) if mf else None,
+                                "insts_valu": float(np.mean(va)) if va else None, "dispatches": len(disp)}
+    json.dump(out, open(SQ_FILE, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def cpu_baseline(sample_heads: int, T: int, chunked_heads: int = 8):
+    """The float64 oracle, as it stands, on a bounded sample of the prefill workload, with its BLAS
+    on every host core this process may use: the token recurrence (the definition) on
+    `sample_heads` of the 32 heads over T tokens, and the chunked WY/UT spelling on `chunked_heads`
+    heads (heads are independent, so the full layer costs 32 / heads times as much)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from hybrid_linear_attention_kda_amd import inputs as I
     from oracle import kda_oracle as O
 
+    cores = len(os.sched_getaffinity(0))
     wl = I.WORKLOADS["prefill_t4096"].with_(T=T)
     inp = I.generate(wl)
-    heads = list(range(sample_heads))
-    swl, sinp = I.select_heads(wl, inp, heads)
-    p = O.KdaParams(H=swl.H, dk=swl.dk, dv=swl.dv, conv_w=sinp["conv_w"], A_log=sinp["A_log"],
-                    dt_bias=sinp["dt_bias"], norm_w=sinp["norm_w"], lb=sinp["lb"], scale=sinp["scale"])
-    with threadpool_limits(limits=1):
+
+    def run(nh, form):
+        swl, sinp = I.select_heads(wl, inp, list(range(nh)))
+        p = O.KdaParams(H=swl.H, dk=swl.dk, dv=swl.dv, conv_w=sinp["conv_w"], A_log=sinp["A_log"],
+                        dt_bias=sinp["dt_bias"], norm_w=sinp["norm_w"], lb=sinp["lb"], scale=sinp["scale"])
         t0 = time.perf_counter()
-        O.kda_layer(p, sinp["qkv"], sinp["f"], sinp["beta"], sinp["g_out"], sinp["state0"], sinp["conv_state0"])
-        dt = time.perf_counter() - t0
-    full_layer_s = dt * wl.H / sample_heads
-    return {"value": T / full_layer_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"float64 token-recurrence oracle, {sample_heads} of 32 heads x {T} tokens of the "
-                      f"T=4096 prefill workload ({dt:.1f} s), scaled to 32 heads; BLAS limited to 1 thread"}
+        O.kda_layer(p, sinp["qkv"], sinp["f"], sinp["beta"], sinp["g_out"], sinp["state0"], sinp["conv_state0"],
+                    form=form, chunk=wl.chunk)
+        return time.perf_counter() - t0
+
+    with threadpool_limits(limits=cores):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        dt_tok = run(sample_heads, "token")
+        dt_chk = run(chunked_heads, "chunked")
+    tok_s = T / (dt_tok * wl.H / sample_heads)
+    chk_s = T / (dt_chk * wl.H / chunked_heads)
+    return {"value": tok_s, "unit": "tokens/s", "cores": min(cores, threads), "kind": "oracle",
+            "sample": f"float64 token-recurrence oracle, {sample_heads} of 32 heads x {T} tokens of the T=4096 "
+                      f"prefill workload ({dt_tok:.1f} s), scaled to 32 heads; BLAS on {min(cores, threads)} "
+                      f"threads ({cores} cores in this process's affinity mask)",
+            "chunked": {"value": chk_s, "unit": "tokens/s",
+                        "sample": f"float64 chunked WY/UT oracle (chunk 64), {chunked_heads} of 32 heads x {T} "
+                                  f"tokens ({dt_chk:.1f} s), scaled to 32 heads"}}
+
+
+PREFILL_CHUNK = 64
+
+
+def prefill_alg_flops(T, H, D, C=PREFILL_CHUNK):
+    """Algorithmic flops of one chunked prefill call, dense tiles (triangular products counted whole):
+    per chunk-head A_kk, A_qk, W = T X, Ut = T (beta V) and A_qk U (2 C^2 D each), the UT inverse
+    (C^3 / 3 x 2) and the three products with the state U = Ut - W S, Q~ S, K~^T U (2 C D^2 each)."""
+    nch = (T + C - 1) // C
+    per = 5 * 2 * C * C * D + 2 * C ** 3 // 3 + 3 * 2 * C * D * D
+    return nch * H * per
+
+
+SQ_FILE = os.path.join(ROOT, "profiles", "pmc_mfma.json")
+
+
+def stored_mfma_busy(kernel):
+    """Fraction of the chip's matrix-core cycles busy during `kernel` from the committed counter run
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x 4 SIMDs x CUs), or None when there is none or
+    the sources changed since."""
+    if not os.path.exists(SQ_FILE):
+        return None
+    rec = json.load(open(SQ_FILE))
+    if rec.get("source_sha256") != source_fingerprint():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("mfma_busy_frac")
+
+
+def hbm_ceilings(dev, nbytes=1 << 30, reps=5):
+    """Measured HBM ceilings on this GPU: a plain copy (torch copy_: nbytes read + nbytes written),
+    a write-only fill (torch fill_) and a read-only reduction (torch sum, a few bytes out), each the
+    median of `reps` runs on buffers well beyond the 256 MB last-level cache."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),
+                            ("write", lambda: dst.fill_(2.0), nbytes),
+                            ("read", lambda: src.sum(), nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        out[name] = {"gbps": moved / (ms * 1e-3) / 1e9, "bytes": moved, "ms_median": ms}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -256,9 +360,14 @@ def main():
                     help="after the timed steps, run one plain copy kernel of known size (for counter scaling)")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
                     help="turn two rocprofv3 --pmc runs into profiles/pmc_traffic.json and exit")
+    ap.add_argument("--mfma-summary", nargs=2, metavar=("PMC_DIR", "COMMAND"),
+                    help="turn a rocprofv3 --pmc run of the matrix-core counters into profiles/pmc_mfma.json and exit")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.mfma_summary:
+        mfma_summary(*args.mfma_summary)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer shards by head with "
@@ -281,6 +390,12 @@ def main():
     wp, wd, wv = I.WORKLOADS["prefill_t4096"], I.WORKLOADS["decode_b64"], I.WORKLOADS["verify_b16"]
     ops = ["prefill", "varlen", "projection", "decode", "verify"] if args.only is None else [args.only]
 
+    def strong_layer(lay):
+        """The same layer parameters with the bounded gate at gate_lower_bound = -8."""
+        return abi.KdaLayer(H=lay.H, D=lay.D, W=lay.W, chunk=lay.chunk, io_dtype=lay.io_dtype,
+                            out_dtype=lay.out_dtype, lb=-8.0, scale=lay.scale, conv_w=lay.conv_w,
+                            A_log=lay.A_log, dt_bias=lay.dt_bias, norm_w=lay.norm_w)
+
     def softplus_layer(lay):
         """The same layer parameters on the softplus decay branch (no lower bound)."""
         return abi.KdaLayer(H=lay.H, D=lay.D, W=lay.W, chunk=lay.chunk, io_dtype=lay.io_dtype,
@@ -299,9 +414,10 @@ def main():
         lay = TT.make_layer(wp, inp, dev, out="bf16")
         tok = TT.token_tensors(wp, inp, 0, wp.T, dev)
         lay_sp = softplus_layer(lay)
+        lay_st = strong_layer(lay)
         for _ in range(nsets):
             sets["prefill"].append(dict(
-                layer=lay, layer_sp=lay_sp, tok={k: v.clone() for k, v in tok.items()},
+                layer=lay, layer_sp=lay_sp, layer_st=lay_st, tok={k: v.clone() for k, v in tok.items()},
                 state=torch.zeros((1, wp.H, wp.dk, wp.dv), dtype=torch.float32, device=dev),
                 conv=torch.zeros((1, wp.c_qkv, wp.W - 1), dtype=torch.bfloat16, device=dev),
                 out=torch.empty((1, wp.T, wp.H * wp.dv), dtype=torch.bfloat16, device=dev),
@@ -386,8 +502,9 @@ def main():
 
     def run(op, s):
         t = s.get("tok")
-        if op in ("prefill", "prefill_softplus"):
-            abi.kda_prefill(s["layer" if op == "prefill" else "layer_sp"], t["qkv"], t["f"], t["beta"], t["g_out"],
+        if op in ("prefill", "prefill_softplus", "prefill_strong"):
+            lay = {"prefill": "layer", "prefill_softplus": "layer_sp", "prefill_strong": "layer_st"}[op]
+            abi.kda_prefill(s[lay], t["qkv"], t["f"], t["beta"], t["g_out"],
                             s["state"], s["conv"], s["out"], workspace=s["ws"], stream=stream)
         elif op == "varlen":
             abi.kda_prefill_varlen(s["layer"], var_cu, None, t["qkv"], t["f"], t["beta"], t["g_out"], s["state"],
@@ -415,10 +532,14 @@ def main():
             seq += ["rollback", "verify_tape", "commit"]
         if op in ("prefill", "decode"):
             seq.append(op + "_softplus")
+        if op == "prefill":
+            seq.append("prefill_strong")
 
     def setof(op):
         if op.endswith("_softplus"):
             return op[: -len("_softplus")]
+        if op == "prefill_strong":
+            return "prefill"
         return "verify" if op in ("rollback", "verify_tape", "commit") else op
 
     for i in range(args.warmup):
@@ -460,6 +581,32 @@ def main():
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    # each call on its own event pair, max(K, 50) calls per type: median and p10 / p90 per call
+    KD = max(K, 50)
+    dist = {}
+    for op in seq:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(KD)]
+        for i in range(KD):
+            evs[i][0].record(stream)
+            run(op, sets[setof(op)][i % nsets])
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) for a, b in evs]
+        dist[op] = {"ms_median": float(np.median(ts)), "ms_p10": float(np.percentile(ts, 10)),
+                    "ms_p90": float(np.percentile(ts, 90)), "calls": KD}
+    # cache-warm figure: the prefill on one buffer set, K calls back to back (inputs partly resident in
+    # the 256 MB last-level cache), labelled as such and kept apart from the rotated-set numbers
+    warm = None
+    if "prefill" in ops:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        run("prefill", sets["prefill"][0])
+        e0.record(stream)
+        for i in range(K):
+            run("prefill", sets["prefill"][0])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        warm = e0.elapsed_time(e1) / K
+    ceil = hbm_ceilings(dev)
     ms_total = t_start.elapsed_time(t_end)
     mean = {op: ev[op][0].elapsed_time(ev[op][1]) / K for op in seq}
 
@@ -471,17 +618,28 @@ def main():
         "config": {"workload": "prefill_t4096 (B=1,T=4096,H=32,d=128,chunk 64) + the same tokens as 16 packed "
                                "sequences + their input projection (hidden 4096) + decode_b64 (B=64,H=32,d=128) "
                                "+ verify_b16 (B=16,T_d=8,H=32,d=128) with rollback and with the replay tape; "
-                               "prefill_t4096 and decode_b64 again on the softplus decay branch",
+                               "prefill_t4096 and decode_b64 again on the softplus decay branch; prefill_t4096 "
+                               "with gate_lower_bound -8",
                    "io": "bf16 inputs and outputs, fp32 state and accumulation", "buffer_sets": nsets},
         "wall_s": wall,
     }
     detail = {}
+    res["hbm_ceilings"] = {k: v["gbps"] for k, v in ceil.items()}
+    res["hbm_ceilings"]["how"] = ("measured in this run: torch copy_ (1 GiB read + 1 GiB written), fill_ (1 GiB "
+                                  "written) and sum (1 GiB read), median of 5")
+    copy_ceil = ceil["copy"]["gbps"]
     if "prefill" in ops:
         pb = prefill_bytes(1, wp.T, wp.H, wp.dk, wp.W)
+        pf = prefill_alg_flops(wp.T, wp.H, wp.dk)
         res["value"] = wp.T / (mean["prefill"] * 1e-3)
         res["unit"] = "tokens/s"
         detail["prefill"] = {"ms_mean": mean["prefill"], "tokens_per_s": res["value"], "alg_bytes": pb,
-                             "gbps": pb / (mean["prefill"] * 1e-3) / 1e9}
+                             "gbps": pb / (mean["prefill"] * 1e-3) / 1e9,
+                             "hbm_frac": pb / (mean["prefill"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                             "alg_flops": pf, "alg_tflops": pf / (mean["prefill"] * 1e-3) / 1e12,
+                             "cache_warm_ms": warm,
+                             "cache_warm_note": "one buffer set, calls back to back: inputs partly in the last-level "
+                                                "cache; not the headline (which rotates 4 sets)"}
     if "varlen" in ops:
         vb_ = sum(kernel_alg_bytes(k, wp, wd, wv, accepted) for k in
                   ("kda_chunk_prep_kernel[varlen]", "kda_chunk_state_kernel[varlen]", "kda_out_norm_kernel[varlen]"))
@@ -504,6 +662,10 @@ def main():
         detail["prefill_softplus"] = {"ms_mean": ms, "tokens_per_s": wp.T / (ms * 1e-3), "alg_bytes": pb,
                                       "gbps": pb / (ms * 1e-3) / 1e9,
                                       "workload": "prefill_t4096 with the softplus decay branch (no lower bound)"}
+        ms = mean["prefill_strong"]
+        detail["prefill_strong"] = {"ms_mean": ms, "tokens_per_s": wp.T / (ms * 1e-3), "alg_bytes": pb,
+                                    "gbps": pb / (ms * 1e-3) / 1e9, "vs_prefill": ms / mean["prefill"],
+                                    "workload": "prefill_t4096 with the bounded gate at gate_lower_bound = -8"}
     if "decode" in ops:
         db = decode_bytes(wd.B, wd.H, wd.dk, wd.W)
         gb = db / (mean["decode"] * 1e-3) / 1e9
@@ -534,6 +696,17 @@ def main():
                                           "tape_verify_plus_commit": mean["verify_tape"] + mean["commit"]}
         if "value" not in res:
             res["value"], res["unit"] = gv, "GB/s"
+    line_of = {"prefill": "prefill", "varlen": "prefill_varlen", "projection": "input_projection",
+               "prefill_softplus": "prefill_softplus", "prefill_strong": "prefill_strong", "decode": "decode",
+               "decode_softplus": "decode_softplus",
+               "verify": "verify", "rollback": "rollback", "verify_tape": "verify_tape", "commit": "commit_tape"}
+    for op, line in line_of.items():
+        if op in dist and line in detail:
+            detail[line].update(dist[op])
+            if "alg_bytes" in detail[line] and detail[line]["alg_bytes"]:
+                gm = detail[line]["alg_bytes"] / (dist[op]["ms_median"] * 1e-3) / 1e9
+                detail[line]["gbps_median_call"] = gm
+                detail[line]["frac_of_copy_ceiling"] = gm / copy_ceil
     # per kernel: average launch duration from the library's event pairs over the second pass
     kern = {}
     for name, ts in kernel_ms.items():
@@ -553,16 +726,32 @@ def main():
     # gate, and the input projection is a matrix-core GEMM line ahead of the layer: all are
     # reported beside them)
     share = lambda n: kern[n]["ms_mean"] * kern[n]["launches_per_step"]
-    hbm = [n for n in kern if "[varlen]" not in n and "[softplus]" not in n and kern[n]["alg_bytes"]]
+    hbm = [n for n in kern if "[varlen]" not in n and "[softplus]" not in n and "[strong]" not in n
+           and kern[n]["alg_bytes"]]
     if not hbm:  # a run of one side line (--only varlen): its own kernels
         hbm = [n for n in kern if kern[n]["alg_bytes"]]
     if hbm:
         name = max(hbm, key=share)
         k = kern[name]
         achieved = k["gbps"]
+        tr = stored_traffic(name)
         res["roofline"] = {"kernel": name, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": stored_traffic(name),
+                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": tr,
+                           "traffic_source": ("profiles/pmc_traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE runs "
+                                              "on these sources, scaled by a plain copy of known size; not measured "
+                                              "in this run") if tr is not None else None,
+                           "frac_of_measured_copy_ceiling": achieved / copy_ceil,
                            "alg_bytes_per_launch": k["alg_bytes"], "ms_per_launch": k["ms_mean"]}
+        if "prefill" in detail:
+            pl = detail["prefill"]
+            res["roofline"]["prefill_mfma"] = {
+                "alg_tflops": pl["alg_tflops"], "peak": BF16_MFMA_PEAK_TFLOPS,
+                "frac": pl["alg_tflops"] / BF16_MFMA_PEAK_TFLOPS,
+                "busy_frac_by_kernel": {kn: stored_mfma_busy(kn) for kn in
+                                        ("kda_chunk_prep_kernel", "kda_chunk_state_kernel")},
+                "note": "algorithmic dense-tile flops of the prefill call over its mean call time; busy fraction "
+                        "from profiles/pmc_mfma.json (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 4 x CUs)), "
+                        "null when those counters were taken on other sources"}
     else:  # --only projection: its GEMM against the dense bf16 matrix-core peak
         name = max((n for n in kern if kern[n].get("flops")), key=share)
         k = kern[name]

@@ -105,7 +105,7 @@ hipError_t launch_projection(const ProjArgs& p, hipStream_t s, char* err, size_t
 hipError_t launch_prefill_generic(const LayerArgs& a, const SeqTab& st, int chunk, int io, int ot, hipStream_t s);
 
 // Chunked prefill on bf16 MFMA (D = 128, chunk 64, bf16 io, conv width <= 4; the bounded gate with
-// -5.5 <= lb <= -0.25, or the softplus branch).
+// lb <= 0, or the softplus branch).
 // Workspace: chunk blocks for `chunks` chunks of H heads, o for `tokens` tokens, a scratch slot.
 constexpr int kMfmaChunk = 64;
 bool prefill_mfma_supported(int D, int chunk, int io, int W, float lb, int gate);

@@ -104,11 +104,12 @@ constexpr int W_PHI = 0;                   // P = Q~ - A_qk W, hi [64][128] bf16
 constexpr int W_PLO = W_PHI + C * D * 2;   // P lo
 constexpr int W_KTHI = W_PLO + C * D * 2;  // K~^T hi [128][64] bf16
 constexpr int W_KTLO = W_KTHI + D * C * 2; // K~^T lo
-constexpr int W_W = W_KTLO + D * C * 2;    // W [64][128] bf16
-constexpr int W_UT = W_W + C * D * 2;      // Ut = T (beta V) [64][128] fp32, accumulator-fragment order
+constexpr int W_W = W_KTLO + D * C * 2;    // W hi [64][128] bf16
+constexpr int W_WLO = W_W + C * D * 2;     // W lo
+constexpr int W_UT = W_WLO + C * D * 2;    // Ut = T (beta V) [64][128] fp32, accumulator-fragment order
 constexpr int W_Y = W_UT + C * D * 4;      // Y = A_qk Ut [64][128] fp32, accumulator-fragment order
 constexpr int W_GC = W_Y + C * D * 4;      // e^Gam_C [128] fp32
-constexpr int CH_BYTES = W_GC + D * 4;     // 147968
+constexpr int CH_BYTES = W_GC + D * 4;     // 164352
 static_assert(CH_BYTES % 256 == 0, "tile blocks stay 256-byte aligned");
 
 // Phase B: 8 compute waves and 4 loader waves per workgroup.
@@ -124,16 +125,17 @@ constexpr int B_SHI = B_ULO + NVB * PVT * 2;
 constexpr int B_SLO = B_SHI + NVB * PST * 2;
 constexpr int B_TRASH = B_SLO + NVB * PST * 2;   // 256 B, written by warming loads, never read
 // W and Ut are read before barrier (b), K~^T and e^Gam_C after it, so they sit in separate
-// buffers: three of W | Ut (copied two chunks ahead) and two of K~^T | e^Gam_C.
+// buffers: two of W hi | W lo | Ut (each copied a chunk and a half ahead) and two of K~^T | e^Gam_C.
 constexpr int WU_W = 0;
-constexpr int WU_UT = WU_W + C * D * 2;
-constexpr int WU_BYTES = WU_UT + 4 * 1024;       // 20480
+constexpr int WU_WLO = WU_W + C * D * 2;
+constexpr int WU_UT = WU_WLO + C * D * 2;
+constexpr int WU_BYTES = WU_UT + 4 * 1024;       // 36864
 constexpr int KB_KHI = 0;
 constexpr int KB_KLO = KB_KHI + D * C * 2;
 constexpr int KB_GC = KB_KLO + D * C * 2;
 constexpr int KB_BYTES = KB_GC + D * 4;          // 33280
 constexpr int B_WU0 = B_TRASH + 256;
-constexpr int B_KB0 = B_WU0 + 3 * WU_BYTES;
+constexpr int B_KB0 = B_WU0 + 2 * WU_BYTES;
 constexpr int LDS_B = B_KB0 + 2 * KB_BYTES;
 static_assert(NVB == 16, "one accumulator column tile per phase-B workgroup");
 static_assert(B_WU0 % 16 == 0 && WU_BYTES % 16 == 0 && KB_BYTES % 16 == 0, "16-byte aligned tile buffers");
@@ -388,13 +390,16 @@ __device__ __forceinline__ void prep_issue(const LayerArgs& a, const SeqTab& st,
 }
 
 // VL: the launch carries a sequence table (variable-length call); otherwise a.B sequences of a.T.
-// SP: the softplus decay branch (no lower bound).  Its decay is unbounded, so the sub-chunk
+// GK: the gate and its factoring.  0: the bounded sigmoid with -5.5 <= lb <= 0, start-anchored
+// sub-chunks.  1: the softplus decay branch (no lower bound).  2: the bounded sigmoid with lb < -5.5.
+// Under kinds 1 and 2 a 16-token sub-chunk can decay past the range of fp32 (e^-88), so the
 // factoring changes: key columns are anchored at the END of their sub-chunk (every off-diagonal
 // factor is then <= 1, whatever the gate), and the four diagonal 16 x 16 blocks of A_kk and A_qk,
 // which no single anchor keeps finite, are summed exactly per channel (pairwise decay as running
 // products of the per-token decays) and reduced across the channels' lanes.
-template <bool VL, bool SP>
+template <bool VL, int GK>
 __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab st, unsigned char* __restrict__ ws) {
+  constexpr bool SP = GK != 0;  // end-anchored columns, exact diagonal blocks
   extern __shared__ __align__(16) unsigned char smem[];
   float* sQ = reinterpret_cast<float*>(smem + OFF_Q);
   __bf16* sKb = reinterpret_cast<__bf16*>(smem + OFF_KB);
@@ -556,6 +561,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     //      log-decay is held in base-2 units (Gam log2 e), so each decay factor is one v_exp_f32 ----
     float gl[16];
     float graw[16];  // softplus branch: this token's own log-decay, for the exact diagonal blocks
+    float gn0;       // Gam at this lane's segment anchor (base-2 units)
     {
       const int i = tid & 127, seg = tid >> 7;
       const float Ah = __expf(alog);
@@ -565,10 +571,13 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const float fv = (float)sF[(16 * seg + k) * PKB + i] + dtb;
-        // bounded sigmoid; or softplus, floored at -100 (a decay below e^-100 is zero at fp32
-        // precision either way), which keeps the 16-token sums of the log-decay well scaled
-        const float g = SP ? fmaxf(-Ah2 * (fmaxf(fv, 0.f) + __logf(1.0f + __expf(-fabsf(fv)))), -100.f * kLog2e)
-                           : lb2 * __builtin_amdgcn_rcpf(1.0f + __expf(-Ah * fv));
+        // bounded sigmoid or softplus; under the end-anchored factoring floored at -100 (a decay
+        // below e^-100 is zero at fp32 precision either way), which keeps the 16-token sums of the
+        // log-decay well scaled
+        const float gb = lb2 * __builtin_amdgcn_rcpf(1.0f + __expf(-Ah * fv));
+        const float g = GK == 1 ? fmaxf(-Ah2 * (fmaxf(fv, 0.f) + __logf(1.0f + __expf(-fabsf(fv)))), -100.f * kLog2e)
+                      : GK == 2 ? fmaxf(gb, -100.f * kLog2e)
+                                : gb;
         const float gv = (L == C || 16 * seg + k < L) ? g : 0.f;
         acc += gv;
         gl[k] = acc;
@@ -602,7 +611,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       __syncthreads();
       float off = 0.f;
       for (int s = 0; s < seg; ++s) off += sSeg[s * D + i];
-      sGn[seg * D + i] = gl[0] + off;
+      gn0 = gl[0] + off;
+      sGn[seg * D + i] = gn0;
       if (seg == 3) sGn[4 * D + i] = gl[15] + off;
       if (SP) sGa[seg * D + i] = gl[15] + off;
     }
@@ -613,8 +623,12 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     // ---- P5: anchored operands QR, KR (bf16), KC (lane -> channel, 16-token segment, as in P3:
     //      Gam_t - Gam_n(I) = gl[k] - gl[0]) and the per-channel factor tables ----
     float dpart[4];  // softplus branch: this lane's share of its wave's diagonal-block sums
+    // X = beta K e^Gam (Gam from the chunk start) of this lane's channel and 16 tokens, in fp32: the
+    // right-hand side of W = T X, kept in registers until T is formed
+    float xk[16];
     {
       const int i = tid & 127, seg = tid >> 7;
+      const float egn = exp2f_(gn0);
       float* qp = sQ + 16 * seg * PQ + i;
       float* kp = sG + 16 * seg * PQ + i;
       __bf16* rp = sKb + 16 * seg * PKB + i;
@@ -631,6 +645,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
           qp[k * PQ] = q * e1;
           rp[k * PKB] = (__bf16)(kv * e1);
           kp[k * PQ] = kv * e2;
+          xk[k] = sBeta[16 * seg + k] * (kv * e1) * egn;
         }
       } else {
         float qn[16], kn[16], al[16];
@@ -646,6 +661,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
           qp[k * PQ] = qn[k] * e1;
           rp[k * PKB] = (__bf16)(kn[k] * e1);
           kp[k * PQ] = kn[k] * e2;
+          xk[k] = sBeta[16 * seg + k] * (kn[k] * e1) * egn;
           al[k] = exp2f_(graw[k]);  // this token's decay
         }
         // the diagonal block entries of this channel (enumerated as in diag_entry), 64 at a time,
@@ -863,39 +879,66 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 
     prep_issue<VL>(a, st, knext, tid, nxt, 2);
 
-    // ---- P8: W = T . (beta KR e^Gam_n) (plain bf16); wave -> 16 key channels ----
+    // ---- P8: W = T X on split bf16 (T hi.X hi + T hi.X lo + T lo.X hi): W sits beside the state in
+    //      U = Ut - W S, a small difference of large terms when little decays, so it keeps ~16 bits.
+    //      X goes to LDS as split planes in place of KR (no longer read) and of the fp32 T (split
+    //      above); wave -> 16 key channels ----
+    __bf16* sXlo = reinterpret_cast<__bf16*>(smem + OFF_STG + C * PA * 4);  // [64][PKB], old fp32 T
+    {
+      const int i = tid & 127, seg = tid >> 7;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const __bf16 hi = (__bf16)xk[k];
+        sKb[(16 * seg + k) * PKB + i] = hi;
+        sXlo[(16 * seg + k) * PKB + i] = (__bf16)(xk[k] - (float)hi);
+      }
+    }
+    __syncthreads();
     f32x4 wacc[4] = {zero4(), zero4(), zero4(), zero4()};
     {
       const int c = 16 * wave + l16;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int tb = 32 * s + 8 * lg;
-        const float fac = sEn[(tb >> 4) * D + c];
-        float xv[8];
+        bf16x8 xh, xl;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xv[e] = sBeta[tb + e] * (float)sKb[(tb + e) * PKB + c] * fac;
-        const bf16x8 bx = round8(xv);
+        for (int e = 0; e < 8; ++e) {
+          xh[e] = sKb[(tb + e) * PKB + c];
+          xl[e] = sXlo[(tb + e) * PKB + c];
+        }
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
           if (32 * s > 16 * I + 15) continue;  // T is lower triangular
-          wacc[I] = mfma(ld4x2(sThi + (16 * I + l16) * PTB + 32 * s + 8 * lg, 4), bx, wacc[I]);
+          const int o = (16 * I + l16) * PTB + 32 * s + 8 * lg;
+          const bf16x8 th = ld4x2(sThi + o, 4), tl = ld4x2(sTlo + o, 4);
+          wacc[I] = mfma(tl, xh, wacc[I]);
+          wacc[I] = mfma(th, xl, wacc[I]);
+          wacc[I] = mfma(th, xh, wacc[I]);
         }
       }
     }
-    __syncthreads();  // every read of KR is done: W takes its place
+    __syncthreads();  // every read of X is done: W hi / lo take its place
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sKb[(16 * I + 4 * lg + r) * PKB + 16 * wave + l16] = (__bf16)wacc[I][r];
-    // W as this wave's B operand over tokens, in the token order of its own accumulators: k-step s,
-    // lane group g, element e <-> token 32 s + 4 g + e (e < 4), 32 s + 16 + 4 g + e - 4 (e >= 4)
-    bf16x8 wb[2];
+      for (int r = 0; r < 4; ++r) {
+        const int o = (16 * I + 4 * lg + r) * PKB + 16 * wave + l16;
+        const __bf16 hi = (__bf16)wacc[I][r];
+        sKb[o] = hi;
+        sXlo[o] = (__bf16)(wacc[I][r] - (float)hi);
+      }
+    // W as this wave's split B operand over tokens, in the token order of its own accumulators: k-step
+    // s, lane group g, element e <-> token 32 s + 4 g + e (e < 4), 32 s + 16 + 4 g + e - 4 (e >= 4)
+    bf16x8 wb[2], wbl[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        wb[st][e] = (__bf16)wacc[2 * st][e];
-        wb[st][e + 4] = (__bf16)wacc[2 * st + 1][e];
+        const float a0 = wacc[2 * st][e], a1 = wacc[2 * st + 1][e];
+        wb[st][e] = (__bf16)a0;
+        wb[st][e + 4] = (__bf16)a1;
+        wbl[st][e] = (__bf16)(a0 - (float)wb[st][e]);
+        wbl[st][e + 4] = (__bf16)(a1 - (float)wb[st][e + 4]);
       }
     __syncthreads();
 
@@ -903,11 +946,13 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     __bf16* kthi = reinterpret_cast<__bf16*>(blk + W_KTHI);
     __bf16* ktlo = reinterpret_cast<__bf16*>(blk + W_KTLO);
     __bf16* wdst = reinterpret_cast<__bf16*>(blk + W_W);
+    __bf16* wldst = reinterpret_cast<__bf16*>(blk + W_WLO);
     for (int task = tid; task < C * D / 8; task += NT) {
-      // W: [64 tokens][128 channels]
+      // W hi and lo: [64 tokens][128 channels]
       const int t = task >> 4, c8 = (task & 15) * 8;
       const int fo = frag_offset(t, c8, D);
       *reinterpret_cast<bf16x8*>(wdst + fo) = *reinterpret_cast<const bf16x8*>(sKb + t * PKB + c8);
+      *reinterpret_cast<bf16x8*>(wldst + fo) = *reinterpret_cast<const bf16x8*>(sXlo + t * PKB + c8);
       // K~^T = (KC e^(Gam_C - Gam_n(J)))^T: [128 channels][64 tokens]; the lanes of a wave take
       // 64 consecutive channels of one 8-token group, so the column reads of KC hit 64 banks
       const int c = task & 127, t8 = (task >> 7) * 8;
@@ -1011,8 +1056,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
           const int o = t * PTB + 32 * st + 4 * lg;
           const Split8 as{ld4x2(sAhi + o, 16), ld4x2(sAlo + o, 16)};
           ya = mfma3(as, ub[st], ya);
-          pa = mfma(as.lo, wb[st], pa);
-          pa = mfma(as.hi, wb[st], pa);
+          pa = mfma3(as, Split8{wb[st], wbl[st]}, pa);
         }
         yd[(I * 8 + wave) * 64 + lane] = ya;
         // P = QR e^Gam_n - A_qk W, in place of QR (this lane owns these elements)
@@ -1143,21 +1187,22 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
   auto seq_tok0 = [&](int sq) -> long long { return VL ? (long long)st.tok0[sq] : (long long)sq * a.T; };
   auto seq_len = [&](int sq) -> int { return VL ? st.tok0[sq + 1] - st.tok0[sq] : a.T; };
   auto seq_slot = [&](int sq) -> long long { return VL ? st.slot[sq] : sq; };
-  auto wubuf = [&](int c) { return smem + B_WU0 + (c % 3) * WU_BYTES; };
+  auto wubuf = [&](int c) { return smem + B_WU0 + (c & 1) * WU_BYTES; };
   auto kbuf = [&](int c) { return smem + B_KB0 + (c & 1) * KB_BYTES; };
 
-  // ---- loader waves (lw = 0..3): each copies 5 of the 20 W | Ut fragments and 8 of the 32
-  //      K~^T fragments of a chunk (wave 3 also e^Gam_C); cache lines of later chunks touched ----
+  // ---- loader waves (lw = 0..3): each copies 9 of the 36 W hi | W lo | Ut fragments and 8 of the
+  //      32 K~^T fragments of a chunk (wave 3 also e^Gam_C); cache lines of later chunks touched ----
   const int lw = wave - 8;
-  constexpr int N_WU = 5, N_K = 8;
+  constexpr int N_WU = 9, N_K = 8;
   Cursor cur_wu = cursor0(), cur_k = cursor0(), cur_t = cursor0();
   auto issue_wu = [&](int cn) {
     const unsigned char* blk = chunk_ptr(cur_wu, cn);
     unsigned char* wb = wubuf(cn);
 #pragma unroll
     for (int q = 0; q < N_WU; ++q) {
-      const int f = lw * N_WU + q;  // 0..15: W fragment f; 16..19: Ut row tile f - 16 of column tile vb
-      const unsigned char* src = f < 16 ? blk + W_W + f * 1024 : blk + W_UT + ((f - 16) * 8 + vb) * 1024;
+      // 0..15: W hi fragment f; 16..31: W lo fragment f - 16; 32..35: Ut row tile f - 32 of column tile vb
+      const int f = lw * N_WU + q;
+      const unsigned char* src = f < 32 ? blk + W_W + f * 1024 : blk + W_UT + ((f - 32) * 8 + vb) * 1024;
       dma16(src + lane * 16, wb + WU_W + f * 1024);
     }
   };
@@ -1190,34 +1235,45 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
 
   if (wave >= 8) {
     // Loader waves: their own loop, with the same two barriers per chunk as the compute waves.
-    // During chunk ci they copy W | Ut of chunk ci+2 (its buffer last served chunk ci-1, whose
-    // reads ended before barrier (b) of ci-1) and K~^T of chunk ci+1 (its buffer last served
-    // chunk ci-1, read before barrier (a) of ci), and touch chunk ci+3.  Before barrier (b) of
-    // chunk ci they wait for K~^T of ci (issued during chunk ci-1); W | Ut of ci+1, issued before
-    // it, is then complete too, ahead of the barrier (a) that publishes it.
+    // W | Ut of chunk c goes to buffer c & 1, whose last reader (chunk c-2's U waves) is done at
+    // barrier (b) of chunk c-2: it is copied right after that barrier.  K~^T of chunk c goes to
+    // buffer c & 1 after barrier (a) of chunk c-1 (its last reader, chunk c-2's state update, is done
+    // by then), and chunk c+3 is touched into L2 then too.  Before barrier (a) of chunk c this wave
+    // waits for its W | Ut copies of c, before barrier (b) for its K~^T copies of c; each wait counts
+    // the copies issued after the awaited ones, and near the end waits for everything.
     issue_wu(0);
     issue_k(0);
     if (NG > 1) issue_wu(1);
     if (NG > 2) touch_chunk(2);
     KDA_WAIT_VMCNT(0);
     for (int ci = 0; ci < NG; ++ci) {
+      if (ci >= 2) {
+        // after W | Ut(ci): K~^T(ci) and the touch of ci+2 (chunk ci-1, after (a)), W | Ut(ci+1) (after (b))
+        if (ci + 2 < NG) {
+          if (lw == 3)
+            KDA_WAIT_VMCNT(N_K + 2 + TOUCH_PER_WAVE + N_WU);
+          else
+            KDA_WAIT_VMCNT(N_K + TOUCH_PER_WAVE + N_WU);
+        } else {
+          KDA_WAIT_VMCNT(0);
+        }
+      }
       lds_barrier();  // (a)
-      const bool full = ci + 3 < NG;
-      if (ci + 2 < NG) issue_wu(ci + 2);
       if (ci + 1 < NG) issue_k(ci + 1);
-      if (full) touch_chunk(ci + 3);
-      // K~^T(0) was waited for before the loop.  Later, the ops this wave issued after the last
-      // copy of K~^T(ci) are the touch of chunk ci+2 (during chunk ci-1), then W | Ut(ci+2),
-      // K~^T(ci+1) and the touch of ci+3 (this chunk); near the end everything is waited for.
-      if (full && ci > 0) {
-        if (lw == 3)
-          KDA_WAIT_VMCNT(TOUCH_PER_WAVE + N_WU + N_K + 2 + TOUCH_PER_WAVE);
-        else
-          KDA_WAIT_VMCNT(TOUCH_PER_WAVE + N_WU + N_K + TOUCH_PER_WAVE);
-      } else if (ci > 0) {
-        KDA_WAIT_VMCNT(0);
+      if (ci + 3 < NG) touch_chunk(ci + 3);
+      if (ci >= 1) {
+        // after K~^T(ci): the touch of ci+2, W | Ut(ci+1), K~^T(ci+1) and the touch of ci+3
+        if (ci + 3 < NG) {
+          if (lw == 3)
+            KDA_WAIT_VMCNT(TOUCH_PER_WAVE + N_WU + N_K + 2 + TOUCH_PER_WAVE);
+          else
+            KDA_WAIT_VMCNT(TOUCH_PER_WAVE + N_WU + N_K + TOUCH_PER_WAVE);
+        } else {
+          KDA_WAIT_VMCNT(0);
+        }
       }
       lds_barrier();  // (b)
+      if (ci + 2 < NG) issue_wu(ci + 2);
     }
     // The new conv state of this workgroup's 48 channels (16 each of q, k and v) for each of its
     // sequences: the last W-1 raw inputs, from the conv state passed in where a sequence is shorter.
@@ -1349,10 +1405,12 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const bf16x8 w = *reinterpret_cast<const bf16x8*>(wb + WU_W + ((I * 4 + s) * 64 + lane) * 16);
+        const bf16x8 wl = *reinterpret_cast<const bf16x8*>(wb + WU_WLO + ((I * 4 + s) * 64 + lane) * 16);
         const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
         const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSlo + l16 * PST + 32 * s + 8 * lg);
         pa = mfma(w, sh, pa);
         pb = mfma(w, sl, pb);
+        pb = mfma(wl, sh, pb);
       }
       const f32x4 ut = *reinterpret_cast<const f32x4*>(wb + WU_UT + (I * 64 + lane) * 16);
       bf16x4 hi, lo;
@@ -1479,15 +1537,15 @@ __global__ __launch_bounds__(256) void kda_out_norm_kernel(const float* __restri
 
 }  // namespace
 
-// The staging halo covers conv widths up to 4.  For the bounded gate the start-anchored decay
-// factors stay finite only for 15 |lb| < 87, and a gate bound above -0.25 lets the state decay too
-// little to keep this path's bf16 operands (W and the key rows behind it) inside the 2e-3 bar over
-// thousands of tokens (measured at T = 4096: state error 1.6e-3 at lb = -0.1, 2.0e-3 at -0.05,
-// 9e-4 at -0.25, 4e-4 at -5), so such gates take the fp32 path.  The softplus branch has its own
-// factoring (end anchors and exact diagonal blocks) and no bound to check.
+// The staging halo covers conv widths up to 4.  Every gate whose log-decay is <= 0 runs here: the
+// bounded gate with -5.5 <= lb <= 0 on start-anchored sub-chunks (its factors stay finite while
+// 15 |lb| < 87), with lb < -5.5 and the softplus branch on end-anchored ones with exact diagonal
+// blocks.  W is formed and used as split bf16, so weak decay (lb near 0, or pre-activations that
+// keep the gate near 0) keeps the state within the tolerance.  A positive bound (log-decay above
+// 0, a growing state) takes the fp32 path.
 bool prefill_mfma_supported(int Dh, int chunk, int io, int W, float lb, int gate) {
   if (!(Dh == D && chunk == C && io == kBF16 && W >= 1 && W <= HALO + 1)) return false;
-  return gate == 1 || (lb <= -0.25f && lb >= -5.5f);
+  return gate == 1 || lb <= 0.f;
 }
 
 size_t prefill_mfma_workspace(long long chunks, long long tokens, int H) {
@@ -1501,12 +1559,15 @@ static hipError_t launch_mfma_t(const LayerArgs& a, const SeqTab& st, void* ws, 
   const long long chunks = VL ? st.total_chunks : (long long)a.B * NC;
   const long long tokens = VL ? st.tok0[st.n] : (long long)a.B * a.T;
   float* ows = reinterpret_cast<float*>(tiles + (size_t)chunks * a.H * CH_BYTES);
-  static const hipError_t attr_a = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL, false>),
+  static const hipError_t attr_a = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL, 0>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_A);
   if (attr_a != hipSuccess) return attr_a;
-  static const hipError_t attr_sp = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL, true>),
+  static const hipError_t attr_sp = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL, 1>),
                                                         hipFuncAttributeMaxDynamicSharedMemorySize, LDS_A);
   if (attr_sp != hipSuccess) return attr_sp;
+  static const hipError_t attr_st = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL, 2>),
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_A);
+  if (attr_st != hipSuccess) return attr_st;
   // persistent: one workgroup per CU (the LDS use admits one), each looping over tasks
   static const int ncu = [] {
     int dev = 0, n = 0;
@@ -1516,21 +1577,28 @@ static hipError_t launch_mfma_t(const LayerArgs& a, const SeqTab& st, void* ws, 
     return n;
   }();
   const int ntask = (int)(chunks * a.H);
-  // timing names (kept apart per call kind: [varlen] table mode, [softplus] decay branch)
-  static const char* const kname[3][4] = {
-      {"kda_chunk_prep_kernel", "kda_chunk_prep_kernel[softplus]", "kda_chunk_prep_kernel[varlen]",
-       "kda_chunk_prep_kernel[varlen][softplus]"},
-      {"kda_chunk_state_kernel", "kda_chunk_state_kernel[softplus]", "kda_chunk_state_kernel[varlen]",
-       "kda_chunk_state_kernel[varlen][softplus]"},
-      {"kda_out_norm_kernel", "kda_out_norm_kernel[softplus]", "kda_out_norm_kernel[varlen]",
-       "kda_out_norm_kernel[varlen][softplus]"}};
-  const int kn = (VL ? 2 : 0) + (a.gate != 0 ? 1 : 0);
+  // the gate's phase-A instance: 0 bounded with -5.5 <= lb <= 0, 1 softplus, 2 bounded with lb < -5.5
+  const int gk = a.gate != 0 ? 1 : (a.lb < -5.5f ? 2 : 0);
+  // timing names (kept apart per call kind: [varlen] table mode, [softplus] decay branch, [strong]
+  // the bounded gate below -5.5)
+  static const char* const kname[3][6] = {
+      {"kda_chunk_prep_kernel", "kda_chunk_prep_kernel[softplus]", "kda_chunk_prep_kernel[strong]",
+       "kda_chunk_prep_kernel[varlen]", "kda_chunk_prep_kernel[varlen][softplus]",
+       "kda_chunk_prep_kernel[varlen][strong]"},
+      {"kda_chunk_state_kernel", "kda_chunk_state_kernel[softplus]", "kda_chunk_state_kernel[strong]",
+       "kda_chunk_state_kernel[varlen]", "kda_chunk_state_kernel[varlen][softplus]",
+       "kda_chunk_state_kernel[varlen][strong]"},
+      {"kda_out_norm_kernel", "kda_out_norm_kernel[softplus]", "kda_out_norm_kernel[strong]",
+       "kda_out_norm_kernel[varlen]", "kda_out_norm_kernel[varlen][softplus]", "kda_out_norm_kernel[varlen][strong]"}};
+  const int kn = (VL ? 3 : 0) + gk;
   const dim3 grid_a(ntask < ncu ? ntask : ncu);
   timing_begin(kname[0][kn], s);
-  if (a.gate == 0)
-    kda_chunk_prep_kernel<VL, false><<<grid_a, NT, LDS_A, s>>>(a, st, tiles);
+  if (gk == 0)
+    kda_chunk_prep_kernel<VL, 0><<<grid_a, NT, LDS_A, s>>>(a, st, tiles);
+  else if (gk == 1)
+    kda_chunk_prep_kernel<VL, 1><<<grid_a, NT, LDS_A, s>>>(a, st, tiles);
   else
-    kda_chunk_prep_kernel<VL, true><<<grid_a, NT, LDS_A, s>>>(a, st, tiles);
+    kda_chunk_prep_kernel<VL, 2><<<grid_a, NT, LDS_A, s>>>(a, st, tiles);
   timing_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -50,12 +50,10 @@
  *   - Supported: d_k == d_v in {16, 32, 64, 128}; conv_width 1..8;
  *     prefill chunk_size in {16, 32, 64}.  Other shapes return
  *     KDA_ERR_UNSUPPORTED.  bf16 io with d = 128, chunk 64, conv width <= 4
- *     and a bounded gate with its bound in [-5.5, -0.25] runs the bf16
- *     matrix-core prefill; every other prefill, the softplus branch included,
- *     runs the fp32 vector-ALU form (weaker decay keeps more of the state,
- *     which the matrix-core path's bf16 operands would carry past the 2e-3
- *     tolerance over long sequences; unbounded decay breaks its sub-chunk
- *     factoring, while the fp32 form uses pairwise decay factors).
+ *     and a decaying gate (the softplus branch, or the bounded gate with
+ *     gate_lower_bound <= 0) runs the bf16 matrix-core prefill; every other
+ *     prefill (fp32 io, other head sizes or chunks, conv width > 4, a positive
+ *     bound, under which the state grows) runs the fp32 vector-ALU form.
  */
 #ifndef KDA_H_
 #define KDA_H_

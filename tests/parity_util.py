@@ -39,7 +39,7 @@ def rel_err(x, ref) -> float:
 def params(wl: I.Workload, inp: dict) -> O.KdaParams:
     return O.KdaParams(H=wl.H, dk=wl.dk, dv=wl.dv, conv_w=inp["conv_w"], A_log=inp["A_log"],
                        dt_bias=inp["dt_bias"], norm_w=inp["norm_w"], lb=inp["lb"], scale=inp["scale"],
-                       gate=inp["gate"])
+                       gate=inp["gate"], rms_eps=inp.get("rms_eps", 1e-5))
 
 
 def oracle_layer(wl, inp, t0, t1, state, conv_state, form="token", record_states=False):
@@ -48,17 +48,25 @@ def oracle_layer(wl, inp, t0, t1, state, conv_state, form="token", record_states
                        form=form, chunk=wl.chunk, record_states=record_states)
 
 
+_PREFILLED = {}
+
+
 def oracle_prefilled(wl, inp, n_pre: int):
     """State and conv state after the workload's prefix tokens, computed by the
     oracle for the first n_pre sequences and assigned to sequence b from
     sequence b % n_pre (the step under test then continues that sequence
-    with sequence b's own new tokens)."""
-    sub_inp = dict(inp)
-    for k in ("qkv", "f", "beta", "g_out"):
-        sub_inp[k] = inp[k][:n_pre]
-    r = oracle_layer(wl, sub_inp, 0, wl.prefix_T, inp["state0"][:n_pre], inp["conv_state0"][:n_pre])
+    with sequence b's own new tokens).  Kept per (workload, n_pre) for the
+    other tests of the same session."""
+    key = (wl, n_pre)
+    if key not in _PREFILLED:
+        sub_inp = dict(inp)
+        for k in ("qkv", "f", "beta", "g_out"):
+            sub_inp[k] = inp[k][:n_pre]
+        r = oracle_layer(wl, sub_inp, 0, wl.prefix_T, inp["state0"][:n_pre], inp["conv_state0"][:n_pre])
+        _PREFILLED[key] = (r["state"].astype(np.float32), r["conv_state"].astype(np.float32))
+    st, cs = _PREFILLED[key]
     idx = np.arange(wl.B) % n_pre
-    return r["state"][idx].astype(np.float32), r["conv_state"][idx].astype(np.float32)
+    return st[idx], cs[idx]
 
 
 def head_channels(wl, heads):
