@@ -71,6 +71,7 @@ def load() -> ctypes.CDLL:
         "kda_last_error": (ctypes.c_char_p, []),
         "kda_prefill_workspace_size": (c_size_t, [D, c_int32, c_int32]),
         "kda_prefill": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P, P, P, c_size_t, P]),
+        "kda_prefill_noalloc": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P, P, P]),
         "kda_decode_step": (c_int32, [D, c_int32, P, P, P, P, P, P, P, P]),
         "kda_verify_block": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P, P, P, P]),
         "kda_rollback": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P]),
@@ -234,6 +235,16 @@ def kda_prefill(layer: KdaLayer, qkv, f, beta, g_out, state, conv_state, out, wo
     _check(load().kda_prefill(ctypes.byref(layer.desc), B, T, _ptr(qkv), _ptr(f), _ptr(beta), _ptr(g_out),
                               _ptr(state), _ptr(conv_state), _ptr(out), _ptr(workspace), ws_bytes,
                               _stream(stream)))
+
+
+def kda_prefill_noalloc(layer: KdaLayer, qkv, f, beta, g_out, state, conv_state, out, stream=None):
+    """kda_prefill with the library's fixed scratch instead of a caller workspace."""
+    B, T = qkv.shape[0], qkv.shape[1]
+    _check_tokens(layer, B, T, qkv, f, beta, g_out)
+    _check_state(layer, B, state, conv_state)
+    _expect(out, (B, T, layer.H * layer.D), layer.out_torch, "out")
+    _check(load().kda_prefill_noalloc(ctypes.byref(layer.desc), B, T, _ptr(qkv), _ptr(f), _ptr(beta), _ptr(g_out),
+                                      _ptr(state), _ptr(conv_state), _ptr(out), _stream(stream)))
 
 
 def kda_decode_step(layer: KdaLayer, qkv, f, beta, g_out, state, conv_state, out, stream=None):

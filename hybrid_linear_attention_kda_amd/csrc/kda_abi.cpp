@@ -284,6 +284,31 @@ kda_status kda_prefill(const kda_layer_desc* desc, int32_t B, int32_t T, const v
                   "kda_prefill");
 }
 
+kda_status kda_prefill_noalloc(const kda_layer_desc* desc, int32_t B, int32_t T, const void* qkv, const void* f,
+                               const void* beta, const void* g_out, float* state, void* conv_state, void* out,
+                               void* stream) {
+  KDA_TRY(check_desc(desc));
+  KDA_TRY(check_batch(B, T, desc->num_heads));
+  KDA_TRY(check_chunk(desc));
+  if (B == 0 || T == 0) return ok();
+  const size_t need = kda_prefill_workspace_size(desc, B, T);
+  if (need > kda::kNoallocScratchBytes)
+    return fail(KDA_ERR_UNSUPPORTED,
+                "kda_prefill_noalloc: B = %d, T = %d, H = %d needs %zu scratch bytes, more than the library's fixed "
+                "%zu; use kda_prefill with a workspace, or fewer tokens per call",
+                B, T, desc->num_heads, need, kda::kNoallocScratchBytes);
+  KDA_TRY(check_token_tensors(qkv, f, beta, g_out));
+  KDA_TRY(check_ptr(state, "state"));
+  if (desc->conv_width > 1) KDA_TRY(check_ptr(conv_state, "conv_state"));
+  KDA_TRY(check_ptr(out, "out"));
+  void* scratch = nullptr;
+  if (need > 0) {
+    const hipError_t e = kda::noalloc_scratch(&scratch);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "kda_prefill_noalloc: scratch lookup: %s", hipGetErrorString(e));
+  }
+  return kda_prefill(desc, B, T, qkv, f, beta, g_out, state, conv_state, out, scratch, need, stream);
+}
+
 size_t kda_prefill_varlen_workspace_size(const kda_layer_desc* desc, int32_t N, const int32_t* cu_seqlens_host) {
   if (check_desc(desc) != KDA_OK || check_chunk(desc) != KDA_OK) return (size_t)-1;
   std::vector<Launch> plan;

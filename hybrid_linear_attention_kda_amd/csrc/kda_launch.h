@@ -113,4 +113,10 @@ size_t prefill_mfma_workspace(long long chunks, long long tokens, int H);
 hipError_t launch_prefill_mfma(const LayerArgs& a, const SeqTab& st, void* ws, size_t ws_bytes, int ot,
                                hipStream_t s);
 
+// kda_prefill_noalloc: the matrix-core prefill's workspace from a fixed device array of the library
+// (kNoallocScratchBytes per GPU, held until the process ends).  noalloc_scratch returns the
+// current device's address of that array, looked up on the first call on each device.
+constexpr size_t kNoallocScratchBytes = 64u << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace kda

@@ -29,10 +29,11 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller, row-major,
  *     16-byte aligned.  The library allocates no device memory and keeps no
  *     state between calls; prefill scratch comes from the caller's workspace.
- *     One exception, invisible in results: kda_input_projection keeps a
+ *     Two exceptions, both invisible in results: kda_input_projection keeps a
  *     per-thread hipBLASLt handle (created on the first call on a device, so
  *     whatever the GEMM library allocates for it stays until the thread ends)
- *     and the algorithm it chose per GEMM shape.
+ *     and the algorithm it chose per GEMM shape; kda_prefill_noalloc takes its
+ *     scratch from a fixed device array of the library (see there).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream).  The returned status covers argument validation and launch
  *     errors only.  Validation runs before any launch: a call that returns an
@@ -65,7 +66,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum kda_status {
   KDA_OK = 0,
@@ -137,6 +138,24 @@ size_t kda_prefill_workspace_size(const kda_layer_desc* desc, int32_t B, int32_t
 kda_status kda_prefill(const kda_layer_desc* desc, int32_t B, int32_t T, const void* qkv, const void* f,
                        const void* beta, const void* g_out, float* state, void* conv_state, void* out,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_prefill without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the scratch the matrix-core prefill needs comes from
+ * a fixed array inside the library, 64 MiB on each GPU the call runs on (held
+ * from the first such call on that GPU until the process ends).  Arguments
+ * and results are those of kda_prefill; no device memory is allocated or
+ * freed.  A request whose scratch, kda_prefill_workspace_size(desc, B, T),
+ * exceeds 64 MiB returns KDA_ERR_UNSUPPORTED before anything runs (at H = 32,
+ * B = 1 that is T up to 640 tokens; chain calls for longer prompts).  Every
+ * call on one GPU uses the same array: calls that overlap in time on one GPU
+ * (on different streams, or from different threads) race and must not be
+ * issued; calls in one stream's order are safe.
+ */
+kda_status kda_prefill_noalloc(const kda_layer_desc* desc, int32_t B, int32_t T, const void* qkv, const void* f,
+                               const void* beta, const void* g_out, float* state, void* conv_state, void* out,
+                               void* stream);
 
 /*
  * Variable-length prefill: N sequences of different lengths packed along the
