@@ -166,10 +166,12 @@ def short_kernel_name(full):
     import re
     if "Cijk_" in full:  # the GEMM library's kernels (the input projection's two GEMMs)
         return "hipblaslt_gemm"
-    m = re.search(r"(kda_[a-z_]+_kernel)(<[^>]*>)?", full)
+    m = re.search(r"(kda_[a-z0-9_]+_kernel)(<[^>]*>)?", full)
     if m is None:
         return None
     name = m.group(1)
+    if name == "kda_chunk_state64_kernel":  # the uniform-batch state pass (the library's timing name)
+        name = "kda_chunk_state_kernel"
     targs = m.group(2) or ""
     if name in ("kda_chunk_prep_kernel", "kda_chunk_state_kernel") and targs.startswith("<true"):
         name += "[varlen]"
