@@ -9,7 +9,7 @@ One step = one pass over every call of the path on its layer-shaped workload:
   strong    prefill_t4096 again with the bounded gate at gate_lower_bound = -8 (below the range of
             start-anchored sub-chunks: end-anchored ones with exact diagonal blocks)
   projection  the layer's input projection for those 4096 tokens: hidden 4096 -> q|k|v, f, beta,
-            g_out (H=32, d=128, rank 128; the q|k|v|f_a|g_a|b projections as one GEMM)
+            g_out (H=32, d=128, rank 128; the q|k|v|f_a|g_a|b projections as one matmul)
   verify    16 sequences x 8 draft tokens with per-token snapshots, then rollback
             to a seeded accepted prefix (0..8) per sequence; and the same block
             verified with a replay tape, then committed from the tape
@@ -157,15 +157,12 @@ def projection_flops(wl):
 def kernel_alg_flops(kernel, wj):
     """Useful flops of one launch of the input projection's kernels (matrix-core bound, no bytes)."""
     HD = wj.H * wj.d
-    return {"hipblaslt_gemm[qkv]": 2 * wj.T * wj.hidden * 3 * HD,
-            "hipblaslt_gemm[rank|beta]": 2 * wj.T * wj.hidden * (2 * wj.rank + wj.H),
+    return {"kda_proj_gemm_kernel": 2 * wj.T * wj.hidden * (3 * HD + 2 * wj.rank + wj.H),
             "kda_proj_lowrank_kernel": 2 * 2 * wj.T * wj.rank * HD}.get(kernel)
 
 
 def short_kernel_name(full):
     import re
-    if "Cijk_" in full:  # the GEMM library's kernels (the input projection's two GEMMs)
-        return "hipblaslt_gemm"
     m = re.search(r"(kda_[a-z0-9_]+_kernel)(<[^>]*>)?", full)
     if m is None:
         return None

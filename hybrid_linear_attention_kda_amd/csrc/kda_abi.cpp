@@ -203,7 +203,7 @@ kda_status check_proj(const kda_proj_desc* d) {
     return fail(KDA_ERR_UNSUPPORTED, "H*d and hidden must be <= 65536");
   if ((d->num_heads * d->head_dim) % 128 != 0)
     return fail(KDA_ERR_UNSUPPORTED, "H*d = %d is not a multiple of 128", d->num_heads * d->head_dim);
-  if (d->hidden % 8 != 0) return fail(KDA_ERR_UNSUPPORTED, "hidden = %d is not a multiple of 8", d->hidden);
+  if (d->hidden % 128 != 0) return fail(KDA_ERR_UNSUPPORTED, "hidden = %d is not a multiple of 128", d->hidden);
   if (d->out_dtype != KDA_F32 && d->out_dtype != KDA_BF16)
     return fail(KDA_ERR_INVALID_ARGUMENT, "out_dtype must be KDA_F32 or KDA_BF16");
   KDA_TRY(check_ptr(d->w_in, "desc.w_in"));

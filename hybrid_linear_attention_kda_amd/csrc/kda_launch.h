@@ -80,10 +80,9 @@ hipError_t launch_recurrent(const LayerArgs& a, int io, int ot, hipStream_t s);
 hipError_t launch_rollback(const RollbackArgs& a, int io, hipStream_t s);
 hipError_t launch_commit_tape(const CommitArgs& a, int io, hipStream_t s);
 
-// Input projection (hipBLASLt GEMMs + the low-rank / beta kernel).  Rank r = 128; H*D a multiple
-// of 128; bf16 weights and hidden states; outputs bf16 or fp32.
+// Input projection (the fused-rows matmul + the low-rank / beta kernel).  Rank r = 128; H*D a
+// multiple of 128; hidden a multiple of 128; bf16 weights and hidden states; outputs bf16 or fp32.
 constexpr int kProjRank = 128;
-constexpr size_t kProjGemmWorkspace = 32u << 20;  // hipBLASLt workspace inside the caller's workspace
 struct ProjArgs {
   int T, hidden, H, D, out_type;
   const void* x;      // [T, hidden] bf16

@@ -1,19 +1,16 @@
 // KDA input projection: the q, k, v, f_a, g_a and b projections of the hidden states as one
-// weight matrix (one matmul over the concatenated output rows, glm53-flash-mlx README,
-// quantization recipe: the runtime fuses the six KDA input projections into one matmul), then
-// the low-rank up-projections f = f_b(f_a x) and g = g_b(g_a x) (the output gate is low rank,
-// llama.cpp PR #27754, KDA commit) and beta = sigmoid(b x) in one kernel of our own.
+// weight matrix and one matmul over the concatenated output rows (glm53-flash-mlx README,
+// quantization recipe: the runtime fuses the six KDA input projections into one matmul), then the
+// low-rank up-projections f = f_b(f_a x) and g = g_b(g_a x) (the output gate is low rank,
+// llama.cpp PR #27754, KDA commit) and beta = sigmoid(b x).
 //
-// The big matmul is a plain bf16 GEMM with fp32 accumulation and runs on hipBLASLt: the q|k|v
-// rows write straight into the layer's qkv input, the 2r + H rank / beta rows into an fp32
-// workspace.  The low-rank kernel splits the fp32 rank-r activations into bf16 hi + lo (two
-// matrix-core products per k-step, ~16 mantissa bits) so the only bf16 rounding an output sees is
-// its own.
-#include <hipblaslt/hipblaslt.h>
-
+// Both steps are kernels of this library on the bf16 matrix cores with fp32 accumulation.  The
+// fused matmul (kda_proj_gemm_kernel) writes the q|k|v columns straight into the layer's qkv input
+// and the 2r + H rank / beta columns in fp32 into the workspace.  The low-rank kernel splits those
+// fp32 rank-r activations into bf16 hi + lo (two matrix-core products per k-step, ~16 mantissa
+// bits) so the only bf16 rounding an output sees is its own.
+#include <algorithm>
 #include <cstdio>
-#include <map>
-#include <tuple>
 
 #include "kda_device.h"
 #include "kda_launch.h"
@@ -143,139 +140,323 @@ __global__ __launch_bounds__(PJ_NT) void kda_proj_lowrank_kernel(const float* __
   }
 }
 
-struct GemmKey {
-  int m, n, k, ldd, dtype;
-  bool operator<(const GemmKey& o) const {
-    return std::tie(m, n, k, ldd, dtype) < std::tie(o.m, o.n, o.k, o.ldd, o.dtype);
-  }
-};
+// ---------------------------------------------------------------------------------------------
+// The fused projection matmul: D [T, N] = X [T, hidden] . W^T for the N = 3Hd + 2r + H rows of the
+// fused weight.  It is taken transposed, D^T tile = W tile . X tile^T, so that each lane's
+// accumulator holds four consecutive output columns of one token and stores them at once.
+//
+// One workgroup computes a 256-column x 256-token tile with 4 waves, one per SIMD, in a 2 x 2
+// arrangement: each wave owns 128 columns x 128 tokens, 8 x 8 accumulator tiles of 16 x 16 (256
+// fp32 per lane, pinned in the accumulation registers).  K advances in stages of 64 through two
+// LDS slots of 64 KiB: stage s + 1 is copied global -> LDS (global_load_lds, 16 bytes a lane) while
+// stage s is multiplied.  Each copy instruction moves 8 whole 128-byte rows (64 k) of one operand,
+// so every request is a full cache line; within a row the eight 16-byte chunks are stored in an
+// XOR-permuted order chosen so that an MFMA fragment read (16 rows x 32 k, lane l reading row
+// l % 16, k 8 (l / 16) .. + 7) hits 16 different 16-byte bank groups per 16 lanes (and 8 per 8
+// lanes): conflict-free 16-byte LDS reads.  Each wave reads the next half-stage's fragments into a
+// second register set while the matrix cores work on the current one.
+//
+// Tiles are dealt to the 8 L2 domains (XCDs) so that the 32 tiles a domain runs at once are a
+// compact block (4 token tiles x 8 column tiles sharing their operand rows in that L2).
+// ---------------------------------------------------------------------------------------------
+constexpr int GM = 256;                        // tokens per tile (X rows)
+constexpr int GN = 256;                        // output columns per tile (W rows)
+constexpr int GK = 64;                         // K per stage: one 128-byte row segment
+constexpr int G_NT = 256;                      // 4 waves
+constexpr int G_BLOCKS = (GM + GN) / 8;        // 64 copy blocks (8 rows x 128 bytes) per stage: W then X
+constexpr int G_CPW = G_BLOCKS / (G_NT / 64);  // 16 copies per wave per stage
+constexpr int G_STAGE = G_BLOCKS * 1024;       // 64 KiB
+constexpr int G_XOFF = (GN / 8) * 1024;        // X blocks after the W blocks
+constexpr int G_LDS = 2 * G_STAGE;             // 128 KiB
+constexpr int G_MGROUP = 4;                    // token tiles per group of the tile order
+constexpr int G_KSPLIT = 8;                    // K pieces of a rank / beta tile
+static_assert(G_LDS <= 160 * 1024, "LDS budget");
+static_assert(G_CPW == 16, "the wait counts below assume 16 copies per wave per stage");
 
-struct LtState {
-  int device = -1;
-  hipblasLtHandle_t handle = nullptr;
-  std::map<GemmKey, hipblasLtMatmulAlgo_t> algos;
-};
-thread_local LtState g_lt;
-
-#define LT_TRY(expr, what)                                                                 \
-  do {                                                                                     \
-    const hipblasStatus_t _st = (expr);                                                    \
-    if (_st != HIPBLAS_STATUS_SUCCESS) {                                                   \
-      snprintf(err, errlen, "hipBLASLt %s failed (status %d)", what, (int)_st);            \
-      ok = false;                                                                          \
-    }                                                                                      \
-  } while (0)
-
-// D [T, m] (row-major, leading dimension ldd) = X [T, k] . Wr^T, Wr the m rows of a row-major [*, k]
-// bf16 weight starting at Wr.  Column-major view: D^T (m x T) = op_T(Wr as k x m) . (X as k x T).
-// A GEMM is resolved (descriptors and algorithm) before anything is launched, so that a call whose
-// second GEMM has no algorithm fails with no buffer touched.  The algorithm is chosen within
-// kProjGemmWorkspace bytes, the library's share of every valid workspace, so an algorithm cached
-// under one call fits every later call of the same shape.
-struct Gemm {
-  hipblasLtMatmulDesc_t op = nullptr;
-  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
-  hipblasLtMatmulAlgo_t algo{};
-  Gemm() = default;
-  Gemm(const Gemm&) = delete;
-  Gemm& operator=(const Gemm&) = delete;
-  ~Gemm() {
-    if (ld) hipblasLtMatrixLayoutDestroy(ld);
-    if (lb) hipblasLtMatrixLayoutDestroy(lb);
-    if (la) hipblasLtMatrixLayoutDestroy(la);
-    if (op) hipblasLtMatmulDescDestroy(op);
-  }
-};
-
-bool lt_handle(char* err, size_t errlen) {
-  bool ok = true;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) {
-    snprintf(err, errlen, "hipGetDevice failed");
-    return false;
-  }
-  if (g_lt.handle == nullptr || g_lt.device != dev) {
-    if (g_lt.handle != nullptr) hipblasLtDestroy(g_lt.handle);
-    g_lt = LtState{};
-    LT_TRY(hipblasLtCreate(&g_lt.handle), "create");
-    if (!ok) return false;
-    g_lt.device = dev;
-  }
-  return true;
+__device__ __forceinline__ void g_dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void g_store4(float* p, f32x4 v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void g_store4(bf16_t* p, f32x4 v) {
+  uint2 u;
+  u.x = pack_bf16x2(v[0], v[1]);
+  u.y = pack_bf16x2(v[2], v[3]);
+  *reinterpret_cast<uint2*>(p) = u;
 }
 
-bool gemm_resolve(Gemm& g, int T, int k, int m, hipDataType dtype, int ldd, char* err, size_t errlen) {
-  bool ok = true;
-  LT_TRY(hipblasLtMatmulDescCreate(&g.op, HIPBLAS_COMPUTE_32F, HIP_R_32F), "desc");
-  const hipblasOperation_t opT = HIPBLAS_OP_T, opN = HIPBLAS_OP_N;
-  if (ok) LT_TRY(hipblasLtMatmulDescSetAttribute(g.op, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof(opT)), "transa");
-  if (ok) LT_TRY(hipblasLtMatmulDescSetAttribute(g.op, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof(opN)), "transb");
-  if (ok) LT_TRY(hipblasLtMatrixLayoutCreate(&g.la, HIP_R_16BF, k, m, k), "layout A");
-  if (ok) LT_TRY(hipblasLtMatrixLayoutCreate(&g.lb, HIP_R_16BF, k, T, k), "layout B");
-  if (ok) LT_TRY(hipblasLtMatrixLayoutCreate(&g.ld, dtype, m, T, ldd), "layout D");
-  if (!ok) return false;
-  const GemmKey key{m, T, k, ldd, (int)dtype};
-  auto it = g_lt.algos.find(key);
-  if (it != g_lt.algos.end()) {
-    g.algo = it->second;
-    return true;
-  }
-  hipblasLtMatmulPreference_t pref = nullptr;
-  LT_TRY(hipblasLtMatmulPreferenceCreate(&pref), "preference");
-  const uint64_t cap = kProjGemmWorkspace;
-  if (ok)
-    LT_TRY(hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &cap, sizeof(cap)),
-           "workspace preference");
-  hipblasLtMatmulHeuristicResult_t res{};
-  int nres = 0;
-  if (ok) LT_TRY(hipblasLtMatmulAlgoGetHeuristic(g_lt.handle, g.op, g.la, g.lb, g.ld, g.ld, pref, 1, &res, &nres),
-                 "heuristic");
-  if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-  if (ok && (nres < 1 || res.state != HIPBLAS_STATUS_SUCCESS || res.workspaceSize > kProjGemmWorkspace)) {
-    snprintf(err, errlen, "hipBLASLt has no algorithm for this GEMM within %zu workspace bytes", kProjGemmWorkspace);
-    ok = false;
-  }
-  if (ok) {
-    g.algo = res.algo;
-    g_lt.algos[key] = g.algo;
-  }
-  return ok;
+// acc += a . b^T on the matrix cores with the accumulator pinned in the accumulation registers:
+// 256 fp32 per lane live across the K loop, which the register allocator otherwise splits between
+// the two register files and shuffles every trip.
+__device__ __forceinline__ void g_mfma(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// the first product of an accumulator: acc = a . b^T (a zero constant for the addend, so no
+// register is read before it is written)
+__device__ __forceinline__ void g_mfma0(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
 }
 
-bool gemm_run(const Gemm& g, const void* X, const void* Wr, void* D, void* ws, hipStream_t s, const char* name,
-              char* err, size_t errlen) {
-  bool ok = true;
-  const float one = 1.f, zero = 0.f;
-  timing_begin(name, s);
-  LT_TRY(hipblasLtMatmul(g_lt.handle, g.op, &one, Wr, g.la, X, g.lb, &zero, D, g.ld, D, g.ld, &g.algo, ws,
-                         kProjGemmWorkspace, s),
-         "matmul");
-  timing_end(s);
-  return ok;
+// Wait until this wave's copies have all landed and its LDS reads have returned, then meet the
+// other waves.  (The LDS wait repeated as a builtin tells the compiler that the operand registers
+// have arrived, so it adds no wait of its own before the products, which would also wait on reads
+// of the next half-stage issued in between.)
+__device__ __forceinline__ void g_meet() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt not waited on
+}
+
+// position of 16-byte chunk c of row r (0..15 within a 16-row fragment) inside its 128-byte row
+__device__ __forceinline__ int g_pos(int r, int c) { return c ^ (r & 7) ^ (r >> 3); }
+
+// Work items of one launch (g_items): first the q|k|v tiles, full K each, dealt to the 8 L2 domains
+// (block % 8) in 8 * ceil(tiles / 8) blocks; then the tiles of the 2r + H rank / beta columns, each
+// split into `ksplit` K pieces that write fp32 partial sums to part[piece] [T, g_pitch(N - N3)],
+// summed by kda_proj_act_reduce_kernel.  The rank / beta columns are 2.3% of the work at the layer's sizes:
+// as whole tiles they would be the only work of a fourth round of tiles (768 q|k|v tiles fill three
+// rounds of 256 CUs exactly); as pieces they add an eighth of one.
+// row pitch of a partial-sum block: a multiple of 4 floats, so each lane stores its four columns
+// as one 16-byte store (4-byte stores of the 37 MB of partial sums left partly written lines that
+// took ~25 us more to write back when the launch ends)
+__host__ __device__ inline int g_pitch(int ns) { return (ns + 3) & ~3; }
+
+struct GItems {
+  int MT, NQ, NA, ksplit, qblocks, nblocks;
+};
+__host__ __device__ inline GItems g_items(int T, int K, int N, int N3) {
+  GItems g;
+  g.MT = (T + GM - 1) / GM;
+  g.NQ = (N3 + GN - 1) / GN;
+  g.NA = (N - N3 + GN - 1) / GN;
+  g.ksplit = min(G_KSPLIT, K / GK);
+  g.qblocks = 8 * ((g.MT * g.NQ + 7) / 8);
+  g.nblocks = g.qblocks + g.MT * g.NA * g.ksplit;
+  return g;
+}
+
+// X [T, K] bf16, W [N, K] bf16 (rows of the fused weight), K a multiple of 128, N3 a multiple of 16.
+// Columns n < N3 go to qkv [T, N3] (OT); columns N3 <= n < N go, as partial sums over K piece p, to
+// part + p * T * P ([T, P] fp32 each, P = g_pitch(N - N3), columns past N - N3 unused).
+template <typename OT>
+__global__ __launch_bounds__(G_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void kda_proj_gemm_kernel(
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ Wt, int T, int K, int N, int N3, OT* __restrict__ qkv,
+    float* __restrict__ part) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const GItems gi = g_items(T, K, N, N3);
+  const int KS = K / GK;  // >= 2
+  int m0, n0, s0, s1, piece = -1;
+  if ((int)blockIdx.x < gi.qblocks) {
+    const int G = gi.MT * gi.NQ;
+    // logical tile: the blocks of one L2 domain (block % 8) take consecutive logical tiles
+    const int per = gi.qblocks / 8;
+    const int L = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    if (L >= G) return;
+    // logical tiles run in groups of G_MGROUP token tiles x all column tiles, the token tile
+    // fastest within a group, so a domain's 32 concurrent (consecutive) logical tiles span 4 x 8
+    const int gsz = G_MGROUP * gi.NQ;
+    const int grp = L / gsz, r = L % gsz;
+    const int mrows = min(G_MGROUP, gi.MT - grp * G_MGROUP);
+    m0 = (grp * G_MGROUP + r % mrows) * GM;
+    n0 = (r / mrows) * GN;
+    s0 = 0;
+    s1 = KS;
+  } else {
+    // rank / beta piece: the K piece fastest, so one tile's pieces run side by side
+    const int a = blockIdx.x - gi.qblocks;
+    piece = a % gi.ksplit;
+    const int t = a / gi.ksplit;
+    m0 = (t / gi.NA) * GM;
+    n0 = N3 + (t % gi.NA) * GN;
+    s0 = KS * piece / gi.ksplit;
+    s1 = KS * (piece + 1) / gi.ksplit;
+  }
+  const int nst = s1 - s0;  // >= 1 stages of this item
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 1, wm = wave >> 1;  // columns 128 wn .., tokens 128 wm ..
+
+  // copies: this wave moves blocks q = wave + 4 i (q < 32: W rows n0 + 8 q .., else X rows
+  // m0 + 8 (q - 32) ..); lane l takes row 8 q + l / 8 and stores at position l % 8 of it the chunk
+  // that belongs there.  Byte offsets from the matrix base (both matrices are under 4 GiB); rows
+  // past the end are clamped (computed, never stored).
+  unsigned ofs[G_CPW];
+  {
+    const int rr = lane >> 3, p = lane & 7;
+#pragma unroll
+    for (int i = 0; i < G_CPW; ++i) {
+      const int q = wave + 4 * i;
+      const int c = p ^ rr ^ (q & 1);  // g_pos(8 (q & 1) + rr, c) == p
+      const int row = q < GN / 8 ? min(n0 + 8 * q + rr, N - 1) : min(m0 + 8 * (q - GN / 8) + rr, T - 1);
+      ofs[i] = (unsigned)row * (unsigned)(2 * K) + 16u * c;
+    }
+  }
+  const unsigned char* wbase = reinterpret_cast<const unsigned char*>(Wt);
+  const unsigned char* xbase = reinterpret_cast<const unsigned char*>(X);
+  // copy i of the item's stage s (stages past its last re-copy the last one into a slot no later
+  // read uses)
+  auto dma = [&](int s, int slot, int i) __attribute__((always_inline)) {
+    const int sk = (s0 + min(s, nst - 1)) * (2 * GK);
+    g_dma16((i < G_CPW / 2 ? wbase : xbase) + sk + ofs[i], smem + slot * G_STAGE + (wave + 4 * i) * 1024);
+  };
+  // fragment reads: lane l reads row l % 16 of a fragment, chunk 4 h + l / 16 of half h
+  const int fr = lane & 15;
+  const unsigned char* rb0 = smem + (fr >> 3) * 1024 + 128 * (fr & 7) + 16 * g_pos(fr, lane >> 4);
+  const unsigned char* rb1 = smem + (fr >> 3) * 1024 + 128 * (fr & 7) + 16 * g_pos(fr, 4 + (lane >> 4));
+  // read r of a half-stage: r < 8 the W fragment 8 wn + r, else the X fragment 8 wm + r - 8
+  auto rd = [&](int slot, int h, int r) __attribute__((always_inline)) -> bf16x8 {
+    const unsigned char* b = (h ? rb1 : rb0) + slot * G_STAGE;
+    const int off = r < 8 ? (8 * wn + r) * 2048 : G_XOFF + (8 * wm + r - 8) * 2048;
+    return *reinterpret_cast<const bf16x8*>(b + off);
+  };
+
+  f32x4 acc[8][8];
+
+  // one half-stage: the 64 products of register set (ca, cb), with the 16 reads of the next
+  // half-stage (slot rs, half rh) into (na, nb) and (do_copy) the 16 copies of stage ds into slot
+  // dsl spread evenly between them, one read or copy after every second product; the order is
+  // kept as written.  (Copies any denser than one per four products stall the products: bunched
+  // into the first half of the products, the same 16 copies cost 15% more cycles per tile.)
+  auto half = [&](const bf16x8 (&ca)[8], const bf16x8 (&cb)[8], bf16x8 (&na)[8], bf16x8 (&nb)[8], int rs, int rh,
+                  bool do_read, bool do_copy, int ds, int dsl, bool first = false) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 64; ++k) {
+      if (first)
+        g_mfma0(acc[k >> 3][k & 7], ca[k >> 3], cb[k & 7]);
+      else
+        g_mfma(acc[k >> 3][k & 7], ca[k >> 3], cb[k & 7]);
+      if (do_read && k % 4 == 0) {
+        const int r = k / 4;
+        if (r < 8)
+          na[r] = rd(rs, rh, r);
+        else
+          nb[r - 8] = rd(rs, rh, r);
+      }
+      if (do_copy && k % 4 == 2) dma(ds, dsl, k / 4);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  bf16x8 a0[8], b0[8], a1[8], b1[8];
+  // stage 0 -> slot 0, stage 1 -> slot 1 (stages counted from the item's first)
+#pragma unroll
+  for (int i = 0; i < G_CPW; ++i) dma(0, 0, i);
+#pragma unroll
+  for (int i = 0; i < G_CPW; ++i) dma(1, 1, i);
+  asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < 8; ++r) a0[r] = rd(0, 0, r);
+#pragma unroll
+  for (int r = 0; r < 8; ++r) b0[r] = rd(0, 0, 8 + r);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  half(a0, b0, a1, b1, 0, 1, true, false, 0, 0, true);  // stage 0 half 0, reading stage 0 half 1
+  // Stage s (slot s % 2): its half 1 is in (a1, b1).  The meeting: every wave's copies of stage
+  // s + 1 have landed and every wave's reads of stage s have returned, so slot s % 2 takes stage
+  // s + 2 while half 1 of stage s is multiplied and half 0 of stage s + 1 read, then half 0 of
+  // stage s + 1 is multiplied while its half 1 is read.
+  auto stage = [&](int s, int sl) __attribute__((always_inline)) {
+    g_meet();
+    half(a1, b1, a0, b0, sl ^ 1, 0, true, true, s + 2, sl);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    half(a0, b0, a1, b1, sl ^ 1, 1, true, false, 0, 0);
+  };
+  int j = 0;
+  for (; j + 1 <= nst - 2; j += 2) {
+    stage(j, 0);
+    stage(j + 1, 1);
+  }
+  if (j == nst - 2) stage(j, 0);  // its copies re-copy the last stage into slot 0
+  g_meet();
+  half(a1, b1, a0, b0, 0, 0, false, false, 0, 0);  // the last stage's half 1
+  // the no-ops cover the matrix cores' result latency before the accumulators are read
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+  // acc[i][j]: columns n0 + 16 (8 wn + i) + 4 lg .. + 3 of token m0 + 16 (8 wm + j) + l16
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int NP = g_pitch(N - N3);
+  float* pp = piece >= 0 ? part + (long long)piece * T * NP : nullptr;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int m = m0 + 16 * (8 * wm + jj) + l16;
+    if (m >= T) continue;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = n0 + 16 * (8 * wn + i) + 4 * lg;
+      if (piece < 0) {
+        if (n < N3) g_store4(qkv + (long long)m * N3 + n, acc[i][jj]);  // N3 a multiple of 16: n + 3 < N3
+      } else if (n < N) {
+        // the four columns n .. n + 3 lie inside the pitch (n - N3 < N - N3 <= P, P a multiple of 4)
+        *reinterpret_cast<float4*>(pp + (long long)m * NP + (n - N3)) =
+            make_float4(acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]);
+      }
+    }
+  }
+}
+
+// act [T, ns] = sum over the K pieces of part [p] [T, np] (np = g_pitch(ns))
+__global__ __launch_bounds__(256) void kda_proj_act_reduce_kernel(const float* __restrict__ part, int pieces,
+                                                                 int T, int ns, float* __restrict__ act) {
+  const int np = g_pitch(ns);
+  const long long n = (long long)T * ns, pstride = (long long)T * np;
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const long long t = i / ns, c = i - t * ns;
+    float v = 0.f;
+    for (int p = 0; p < pieces; ++p) v += part[p * pstride + t * np + c];
+    act[i] = v;
+  }
 }
 
 }  // namespace
 
+// workspace: the rank / beta activations act [T, 2r + H] fp32, then room for G_KSPLIT partial sums
+// of them at a row pitch of g_pitch(2r + H) (the launch uses min(G_KSPLIT, hidden / 64) of them)
+static size_t proj_act_bytes(int T, int H) {
+  return ((size_t)T * g_pitch(2 * kProjRank + H) * sizeof(float) + 255) / 256 * 256;
+}
 size_t projection_workspace(int T, int H, int D) {
-  const size_t act = ((size_t)T * (2 * kProjRank + H) * sizeof(float) + 255) / 256 * 256;
-  return act + kProjGemmWorkspace;
+  (void)D;
+  return (1 + G_KSPLIT) * proj_act_bytes(T, H);
 }
 
 hipError_t launch_projection(const ProjArgs& p, hipStream_t s, char* err, size_t errlen) {
-  const int HD = p.H * p.D, N3 = 3 * HD, NS = 2 * kProjRank + p.H;
+  (void)err;
+  (void)errlen;
+  const int HD = p.H * p.D, N3 = 3 * HD, NS = 2 * kProjRank + p.H, N = N3 + NS;
+  const size_t one = proj_act_bytes(p.T, p.H);
   float* act = static_cast<float*>(p.ws);
-  const size_t act_bytes = ((size_t)p.T * NS * sizeof(float) + 255) / 256 * 256;
-  void* gws = static_cast<char*>(p.ws) + act_bytes;
-  const bf16_t* w = static_cast<const bf16_t*>(p.w_in);
-  const hipDataType dt = p.out_type == kBF16 ? HIP_R_16BF : HIP_R_32F;
-  // both GEMMs are resolved before the first launch
-  if (!lt_handle(err, errlen)) return hipErrorUnknown;
-  Gemm g_qkv, g_rank;
-  if (!gemm_resolve(g_qkv, p.T, p.hidden, N3, dt, N3, err, errlen)) return hipErrorUnknown;
-  if (!gemm_resolve(g_rank, p.T, p.hidden, NS, HIP_R_32F, NS, err, errlen)) return hipErrorUnknown;
-  if (!gemm_run(g_qkv, p.x, w, p.qkv, gws, s, "hipblaslt_gemm[qkv]", err, errlen)) return hipErrorUnknown;
-  if (!gemm_run(g_rank, p.x, w + (long long)N3 * p.hidden, act, gws, s, "hipblaslt_gemm[rank|beta]", err, errlen))
-    return hipErrorUnknown;
+  float* part = reinterpret_cast<float*>(static_cast<unsigned char*>(p.ws) + one);
+  static const hipError_t attr_f = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_proj_gemm_kernel<float>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, G_LDS);
+  if (attr_f != hipSuccess) return attr_f;
+  static const hipError_t attr_b = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_proj_gemm_kernel<bf16_t>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, G_LDS);
+  if (attr_b != hipSuccess) return attr_b;
+  const GItems gi = g_items(p.T, p.hidden, N, N3);
+  {
+    timing_begin("kda_proj_gemm_kernel", s);
+    if (p.out_type == kBF16)
+      kda_proj_gemm_kernel<bf16_t><<<gi.nblocks, G_NT, G_LDS, s>>>(static_cast<const bf16_t*>(p.x),
+                                                                   static_cast<const bf16_t*>(p.w_in), p.T, p.hidden,
+                                                                   N, N3, static_cast<bf16_t*>(p.qkv), part);
+    else
+      kda_proj_gemm_kernel<float><<<gi.nblocks, G_NT, G_LDS, s>>>(static_cast<const bf16_t*>(p.x),
+                                                                  static_cast<const bf16_t*>(p.w_in), p.T, p.hidden,
+                                                                  N, N3, static_cast<float*>(p.qkv), part);
+    timing_end(s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const long long n = (long long)p.T * NS;
+    timing_begin("kda_proj_act_reduce_kernel", s);
+    kda_proj_act_reduce_kernel<<<(unsigned)std::min<long long>((n + 255) / 256, 2048), 256, 0, s>>>(part, gi.ksplit,
+                                                                                                   p.T, NS, act);
+    timing_end(s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // per domain ceil(tiles / 8) row tiles, times the (column block, which) pairs
   const int tiles = (p.T + PJ_ROWS - 1) / PJ_ROWS;
   const dim3 grid(((tiles + PJ_XCD - 1) / PJ_XCD) * PJ_XCD * 2 * (HD / PJ_COLS));

@@ -29,11 +29,8 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller, row-major,
  *     16-byte aligned.  The library allocates no device memory and keeps no
  *     state between calls; prefill scratch comes from the caller's workspace.
- *     Two exceptions, both invisible in results: kda_input_projection keeps a
- *     per-thread hipBLASLt handle (created on the first call on a device, so
- *     whatever the GEMM library allocates for it stays until the thread ends)
- *     and the algorithm it chose per GEMM shape; kda_prefill_noalloc takes its
- *     scratch from a fixed device array of the library (see there).
+ *     One exception: kda_prefill_noalloc takes its scratch from a fixed
+ *     device array of the library (see there).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream).  The returned status covers argument validation and launch
  *     errors only.  Validation runs before any launch: a call that returns an
@@ -270,7 +267,7 @@ kda_status kda_commit_tape(const kda_layer_desc* desc, int32_t B, int32_t T_d, c
  * beta = sigmoid(b x).  Weights are Linear weights ([out, in], row-major):
  *   w_in [3*H*d + 2*rank + H, hidden] bf16, rows q | k | v | f_a | g_a | b
  *   w_fb [H*d, rank] bf16,  w_gb [H*d, rank] bf16
- * Supported: rank = 128, H*d a multiple of 128, hidden a multiple of 8.
+ * Supported: rank = 128, H*d a multiple of 128, hidden a multiple of 128.
  */
 typedef struct kda_proj_desc {
   int32_t num_heads;   /* H */
@@ -285,8 +282,9 @@ typedef struct kda_proj_desc {
 
 /*
  * Workspace bytes kda_input_projection needs for T tokens ((size_t)-1 if the
- * arguments are invalid): the rank / beta activations in fp32 and the GEMM
- * library's workspace.
+ * arguments are invalid): 9 blocks of T * P * 4 bytes, each rounded up to 256,
+ * P = 2 * rank + H rounded up to a multiple of 4: the rank / beta activations
+ * in fp32 and 8 partial sums of them over pieces of the hidden dimension.
  */
 size_t kda_input_projection_workspace_size(const kda_proj_desc* desc, int32_t T);
 

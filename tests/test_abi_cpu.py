@@ -209,6 +209,7 @@ def test_input_projection_validation():
     assert call(pd(rank=64)) == abi.KDA_ERR_UNSUPPORTED and b"rank 64" in lib.kda_last_error()
     assert call(pd(num_heads=3, head_dim=16)) == abi.KDA_ERR_UNSUPPORTED
     assert call(pd(hidden=4100)) == abi.KDA_ERR_UNSUPPORTED
+    assert call(pd(hidden=4160)) == abi.KDA_ERR_UNSUPPORTED and b"multiple of 128" in lib.kda_last_error()
     assert call(pd(hidden=1 << 17)) == abi.KDA_ERR_UNSUPPORTED
     assert call(pd(num_heads=1024, head_dim=128)) == abi.KDA_ERR_UNSUPPORTED
     assert call(pd(), T=(1 << 26)) == abi.KDA_ERR_UNSUPPORTED and b"token-heads" in lib.kda_last_error()
@@ -216,8 +217,12 @@ def test_input_projection_validation():
     assert call(pd(out_dtype=5)) == abi.KDA_ERR_INVALID_ARGUMENT
     assert call(pd()) == abi.KDA_ERR_INVALID_ARGUMENT and b"workspace is null" in lib.kda_last_error()
     need = lib.kda_input_projection_workspace_size(ctypes.byref(pd()), 4096)
-    act = (4096 * (2 * 128 + 32) * 4 + 255) // 256 * 256
-    assert need == act + (32 << 20)
+    act = (4096 * (2 * 128 + 32) * 4 + 255) // 256 * 256  # the rank / beta activations in fp32
+    assert need == 9 * act  # ... and 8 K-piece partial sums of them
+    # an odd 2r + H pads each partial-sum row to a multiple of 4 floats
+    pitch = (4 * (2 * 128 + 1) + 15) // 16 * 16
+    assert lib.kda_input_projection_workspace_size(ctypes.byref(pd(num_heads=1, head_dim=128)), 100) == \
+        9 * ((100 * pitch + 255) // 256 * 256)
     assert lib.kda_input_projection_workspace_size(ctypes.byref(pd(rank=3)), 16) == ctypes.c_size_t(-1).value
 
 
