@@ -84,6 +84,7 @@ def load() -> ctypes.CDLL:
         "kda_commit_tape": (c_int32, [D, c_int32, c_int32, P, P, P, P, P, P]),
         "kda_timing_enable": (c_int32, [c_int32]),
         "kda_timing_read": (c_int32, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(c_float), c_int32]),
+        "kda_measure_stream": (c_int32, [P, P, c_size_t, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -388,3 +389,12 @@ def timing_read(cap: int = 1 << 16) -> list:
     if n < 0:
         raise KdaError(KDA_ERR_HIP, load().kda_last_error().decode())
     return [(names[i].decode(), float(ms[i])) for i in range(min(n, cap))]
+
+
+def measure_stream(dst, src=None, stream=None):
+    """The library's streaming copy of src into dst (kda_measure_stream; src None: a zero fill of
+    dst), for measuring HBM ceilings: contiguous device tensors, the byte size of dst."""
+    nbytes = dst.numel() * dst.element_size()
+    if src is not None and src.numel() * src.element_size() != nbytes:
+        raise ValueError("src and dst differ in size")
+    _check(load().kda_measure_stream(_ptr(dst), None if src is None else _ptr(src), nbytes, _stream(stream)))

@@ -13,9 +13,48 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
+#include <mutex>
+#include <utility>
 #include <vector>
 
 #include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+std::mutex g_dev_mu;
+std::map<int, int> g_cus;
+std::map<std::pair<int, const void*>, hipError_t> g_lds;
+}  // namespace
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  auto it = g_cus.find(dev);
+  if (it != g_cus.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  g_cus[dev] = n;
+  return n;
+}
+
+hipError_t set_lds_limit(const void* fn, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  const auto key = std::make_pair(dev, fn);
+  auto it = g_lds.find(key);
+  if (it != g_lds.end()) return it->second;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  g_lds[key] = e;
+  return e;
+}
+
+}  // namespace kda
+
 
 namespace {
 
@@ -645,6 +684,15 @@ int32_t kda_timing_read(const char** names, float* ms, int32_t cap) {
     return -1;
   }
   return n;
+}
+
+kda_status kda_measure_stream(void* dst, const void* src, size_t bytes, void* stream) {
+  KDA_TRY(check_ptr(dst, "dst"));
+  if (src != nullptr && !aligned16(src)) return fail(KDA_ERR_INVALID_ARGUMENT, "src is not 16-byte aligned");
+  if (bytes % 16 != 0) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes = %zu is not a multiple of 16", bytes);
+  const hipError_t e = kda::launch_stream_copy(dst, src, bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "kda_measure_stream: %s", hipGetErrorString(e));
+  return ok();
 }
 
 }  // extern "C"

@@ -71,6 +71,12 @@ struct CommitArgs {
   uint8_t accepted[kRollbackBatch];
 };
 
+// The current device's compute-unit count (looked up once per device; 256 if the query fails).
+int device_cus();
+// Allow `bytes` of dynamic LDS for kernel `fn` on the current device (set once per device and
+// kernel; the status of that first attempt is returned on every later call).
+hipError_t set_lds_limit(const void* fn, int bytes);
+
 // Per-kernel timing (kda_timing_enable): the launch functions bracket each kernel launch with
 // timing_begin / timing_end; both do nothing unless timing is on for the calling thread.
 void timing_begin(const char* kernel, hipStream_t s);
@@ -117,5 +123,8 @@ hipError_t launch_prefill_mfma(const LayerArgs& a, const SeqTab& st, void* ws, s
 // current device's address of that array, looked up on the first call on each device.
 constexpr size_t kNoallocScratchBytes = 64u << 20;
 hipError_t noalloc_scratch(void** ptr);
+
+// kda_measure_stream: a streaming copy (src == nullptr: a zero fill) of bytes / 16 16-byte words.
+hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
 
 }  // namespace kda

@@ -1559,23 +1559,15 @@ static hipError_t launch_mfma_t(const LayerArgs& a, const SeqTab& st, void* ws, 
   const long long chunks = VL ? st.total_chunks : (long long)a.B * NC;
   const long long tokens = VL ? st.tok0[st.n] : (long long)a.B * a.T;
   float* ows = reinterpret_cast<float*>(tiles + (size_t)chunks * a.H * CH_BYTES);
-  static const hipError_t attr_a = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL, 0>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_A);
-  if (attr_a != hipSuccess) return attr_a;
-  static const hipError_t attr_sp = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL, 1>),
-                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_A);
-  if (attr_sp != hipSuccess) return attr_sp;
-  static const hipError_t attr_st = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL, 2>),
-                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_A);
-  if (attr_st != hipSuccess) return attr_st;
+  {
+    hipError_t e0 = set_lds_limit(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL, 0>), LDS_A);
+    if (e0 == hipSuccess) e0 = set_lds_limit(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL, 1>), LDS_A);
+    if (e0 == hipSuccess) e0 = set_lds_limit(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL, 2>), LDS_A);
+    if (e0 == hipSuccess) e0 = set_lds_limit(reinterpret_cast<const void*>(kda_chunk_state_kernel<VL>), LDS_B);
+    if (e0 != hipSuccess) return e0;
+  }
   // persistent: one workgroup per CU (the LDS use admits one), each looping over tasks
-  static const int ncu = [] {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    return n;
-  }();
+  const int ncu = device_cus();
   const int ntask = (int)(chunks * a.H);
   // the gate's phase-A instance: 0 bounded with -5.5 <= lb <= 0, 1 softplus, 2 bounded with lb < -5.5
   const int gk = a.gate != 0 ? 1 : (a.lb < -5.5f ? 2 : 0);
@@ -1602,9 +1594,6 @@ static hipError_t launch_mfma_t(const LayerArgs& a, const SeqTab& st, void* ws, 
   timing_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  static const hipError_t attr_b = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_chunk_state_kernel<VL>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_B);
-  if (attr_b != hipSuccess) return attr_b;
   // table mode: the sequences split into groups of consecutive sequences with about equal chunk
   // counts, as many groups as keep every CU busy with one (column block, head, group) workgroup
   SeqTab stb = st;

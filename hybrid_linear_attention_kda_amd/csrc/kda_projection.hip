@@ -427,12 +427,11 @@ hipError_t launch_projection(const ProjArgs& p, hipStream_t s, char* err, size_t
   const size_t one = proj_act_bytes(p.T, p.H);
   float* act = static_cast<float*>(p.ws);
   float* part = reinterpret_cast<float*>(static_cast<unsigned char*>(p.ws) + one);
-  static const hipError_t attr_f = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_proj_gemm_kernel<float>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, G_LDS);
-  if (attr_f != hipSuccess) return attr_f;
-  static const hipError_t attr_b = hipFuncSetAttribute(reinterpret_cast<const void*>(kda_proj_gemm_kernel<bf16_t>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, G_LDS);
-  if (attr_b != hipSuccess) return attr_b;
+  {
+    hipError_t e0 = set_lds_limit(reinterpret_cast<const void*>(kda_proj_gemm_kernel<float>), G_LDS);
+    if (e0 == hipSuccess) e0 = set_lds_limit(reinterpret_cast<const void*>(kda_proj_gemm_kernel<bf16_t>), G_LDS);
+    if (e0 != hipSuccess) return e0;
+  }
   const GItems gi = g_items(p.T, p.hidden, N, N3);
   {
     timing_begin("kda_proj_gemm_kernel", s);

@@ -315,6 +315,16 @@ kda_status kda_input_projection(const kda_proj_desc* desc, int32_t T, const void
 int32_t kda_timing_enable(int32_t on);
 int32_t kda_timing_read(const char** names, float* ms, int32_t cap);
 
+/*
+ * A streaming copy, for benchmarks (not part of the layer): the HBM ceilings the
+ * layer's bandwidth-bound calls are reported against.  Copies `bytes` from src to
+ * dst (device pointers, 16-byte aligned, bytes a multiple of 16, the ranges
+ * disjoint), or writes zeros to dst when src is NULL, with 16-byte non-temporal
+ * loads and stores, asynchronously on `stream`.  KDA_ERR_INVALID_ARGUMENT on a
+ * null dst, misaligned pointers or a size that is not a multiple of 16.
+ */
+kda_status kda_measure_stream(void* dst, const void* src, size_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,7 @@ def test_library_exports_every_header_function():
                           "kda_verify_tape_size", "kda_verify_block_tape", "kda_commit_tape",
                           "kda_prefill_varlen_workspace_size", "kda_prefill_varlen",
                           "kda_input_projection_workspace_size", "kda_input_projection",
-                          "kda_timing_enable", "kda_timing_read", "kda_prefill_noalloc"}
+                          "kda_timing_enable", "kda_timing_read", "kda_prefill_noalloc", "kda_measure_stream"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.kda_abi_version() == 3
@@ -262,3 +262,15 @@ def test_noalloc_prefill_refuses_requests_beyond_its_scratch():
     assert call(0, 5000, ptr=0) == abi.KDA_OK and call(1, 0, ptr=0) == abi.KDA_OK  # empty calls are no-ops
     assert lib.kda_prefill_noalloc(ctypes.byref(desc(gate_lower_bound=math.nan)), 1, 8, FAKE, FAKE, FAKE, FAKE,
                                    FAKE, FAKE, FAKE, None) == abi.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_measure_stream_validation():
+    lib = abi.load()
+    P = ctypes.c_void_p
+    assert lib.kda_measure_stream(None, None, 16, None) == abi.KDA_ERR_INVALID_ARGUMENT
+    assert b"dst is null" in lib.kda_last_error()
+    assert lib.kda_measure_stream(P(8), None, 16, None) == abi.KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_measure_stream(P(16), P(24), 16, None) == abi.KDA_ERR_INVALID_ARGUMENT
+    assert b"src is not 16-byte aligned" in lib.kda_last_error()
+    assert lib.kda_measure_stream(P(16), P(32), 15, None) == abi.KDA_ERR_INVALID_ARGUMENT
+    assert b"multiple of 16" in lib.kda_last_error()
