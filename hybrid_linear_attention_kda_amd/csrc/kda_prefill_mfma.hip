@@ -22,9 +22,9 @@
 //    L2 norms, gate and its cumulative sum, A_kk, T, A_qk, W, and from them
 //      Ut = T (beta V),  Y = A_qk Ut,  P = Q~ - A_qk W,
 //    with Q~ = Q e^Gam and K~ = K e^(Gam_C - Gam).  Everything that does not
-//    depend on the state is written to the workspace once per chunk: P and K~^T
-//    (transposed) as split bf16 (hi + lo), W as bf16, Ut and Y as fp32 and
-//    e^Gam_C as fp32, each in the order the matrix cores consume it.
+//    depend on the state is written to the workspace once per chunk: P, W and K~^T
+//    (transposed) as fp16, Ut and Y as fp32 and e^Gam_C as fp32, each in the order
+//    the matrix cores consume it.
 //  B (sequential over chunks, one workgroup per (sequence, head, 16-column
 //    block of d_v); with a sequence table, per group of consecutive sequences,
 //    whose chunks it runs as one stream): per chunk
@@ -45,10 +45,16 @@
 // sub-chunk instead, which keeps every off-diagonal factor <= 1, and sums the four
 // diagonal blocks exactly per channel (see kda_chunk_prep_kernel).
 //
-// Precision.  bf16 operands round to 8 bits; contractions that feed the
-// output or the state directly use split bf16 (x = hi + lo, three MFMAs:
-// hi.hi + hi.lo + lo.hi): A_qk, Ut, Y, P S, K~^T U.  A_kk and W run in plain
-// bf16; W S and A_qk W split only S and A_qk.  T is formed in fp32.
+// Precision.  bf16 operands round to 8 bits; phase A's contractions that feed
+// the output or the state use split bf16 (x = hi + lo, three MFMAs: hi.hi +
+// hi.lo + lo.hi): A_qk, Ut, Y, W = T X, A_qk W; A_kk runs in plain bf16 and T is
+// formed in fp32.  Phase B's three products with the state (W S, P S, K~^T U) take
+// W, P and K~^T as fp16 (11 significant bits, half the bytes of a split bf16 pair
+// on the per-chunk operand path) and S or U split into fp16 hi + lo (~22 bits),
+// two MFMAs each.  fp16's range holds these values: |q| and |k| are at most
+// 1 after the L2 norm, and the delta rule keeps every state entry within the
+// value vectors' scale (the largest |S| over the 4096- and 32768-token workloads
+// is below 2).
 //
 // The output RMSNorm needs all 128 columns of o, which live in eight
 // workgroups, so o (fp32) goes to the workspace and a third, bandwidth-bound
@@ -95,45 +101,40 @@ static_assert(STG_BYTES >= 2 * C * PA * 4, "staging aliases");
 static_assert(LDS_A <= 160 * 1024, "LDS budget");
 
 // Workspace tile block per (sequence, head, chunk), written by phase A and read by phase B.
-// Every bf16 matrix is stored in MFMA fragment order: fragment f = (row / 16) * (K / 32) + k / 32
+// Every fp16 matrix is stored in MFMA fragment order: fragment f = (row / 16) * (K / 32) + k / 32
 // of a [rows][K] operand holds, for lane l, the 8 elements (row 16*(f / (K/32)) + l % 16,
 // k = 32*(f % (K/32)) + 8*(l / 16) + 0..7), so a wave loads one fragment as 1 KB contiguous.
 // The fp32 [64][128] matrices are stored as 16 x 16 accumulator tiles (I, j), tile-major
 // (I * 8 + j), lane l holding rows 16 I + 4 (l / 16) + 0..3 of column 16 j + l % 16.
-constexpr int W_PHI = 0;                   // P = Q~ - A_qk W, hi [64][128] bf16 (16 fragments)
-constexpr int W_PLO = W_PHI + C * D * 2;   // P lo
-constexpr int W_KTHI = W_PLO + C * D * 2;  // K~^T hi [128][64] bf16
-constexpr int W_KTLO = W_KTHI + D * C * 2; // K~^T lo
-constexpr int W_W = W_KTLO + D * C * 2;    // W hi [64][128] bf16
-constexpr int W_WLO = W_W + C * D * 2;     // W lo
-constexpr int W_UT = W_WLO + C * D * 2;    // Ut = T (beta V) [64][128] fp32, accumulator-fragment order
+constexpr int W_PHI = 0;                   // P = Q~ - A_qk W [64][128] fp16 (16 fragments)
+constexpr int W_KTHI = W_PHI + C * D * 2;  // K~^T [128][64] fp16
+constexpr int W_W = W_KTHI + D * C * 2;    // W [64][128] fp16
+constexpr int W_UT = W_W + C * D * 2;      // Ut = T (beta V) [64][128] fp32, accumulator-fragment order
 constexpr int W_Y = W_UT + C * D * 4;      // Y = A_qk Ut [64][128] fp32, accumulator-fragment order
 constexpr int W_GC = W_Y + C * D * 4;      // e^Gam_C [128] fp32
-constexpr int CH_BYTES = W_GC + D * 4;     // 164352
+constexpr int CH_BYTES = W_GC + D * 4;     // 115200
 static_assert(CH_BYTES % 256 == 0, "tile blocks stay 256-byte aligned");
 
 // Phase B: 8 compute waves and 4 loader waves per workgroup.
 constexpr int NTB = 768;
-constexpr int PVT = 72;                    // bf16 pitch of the [16][64] token-major U operand
-constexpr int PST = 136;                   // bf16 pitch of the [16][128] state operand
-// Phase B LDS layout (bytes): U and S operands, a scratch line for cache-warming loads, then the
-// buffers of the tiles the loader waves bring in (W, this block's Ut, K~^T hi / lo, e^Gam_C), each
-// byte-for-byte as in the workspace (1 KB fragments).
+constexpr int PVT = 72;                    // fp16 pitch of the [16][64] token-major U operand
+constexpr int PST = 136;                   // fp16 pitch of the [16][128] state operand
+// Phase B LDS layout (bytes): U and S operands (fp16 hi / lo), a scratch line for cache-warming
+// loads, then the buffers of the tiles the loader waves bring in (W, this block's Ut, K~^T,
+// e^Gam_C), each byte-for-byte as in the workspace (1 KB fragments).
 constexpr int B_UHI = 0;
 constexpr int B_ULO = B_UHI + NVB * PVT * 2;
 constexpr int B_SHI = B_ULO + NVB * PVT * 2;
 constexpr int B_SLO = B_SHI + NVB * PST * 2;
 constexpr int B_TRASH = B_SLO + NVB * PST * 2;   // 256 B, written by warming loads, never read
 // W and Ut are read before barrier (b), K~^T and e^Gam_C after it, so they sit in separate
-// buffers: two of W hi | W lo | Ut (each copied a chunk and a half ahead) and two of K~^T | e^Gam_C.
+// buffers: two of W | Ut (each copied a chunk and a half ahead) and two of K~^T | e^Gam_C.
 constexpr int WU_W = 0;
-constexpr int WU_WLO = WU_W + C * D * 2;
-constexpr int WU_UT = WU_WLO + C * D * 2;
-constexpr int WU_BYTES = WU_UT + 4 * 1024;       // 36864
+constexpr int WU_UT = WU_W + C * D * 2;
+constexpr int WU_BYTES = WU_UT + 4 * 1024;       // 20480
 constexpr int KB_KHI = 0;
-constexpr int KB_KLO = KB_KHI + D * C * 2;
-constexpr int KB_GC = KB_KLO + D * C * 2;
-constexpr int KB_BYTES = KB_GC + D * 4;          // 33280
+constexpr int KB_GC = KB_KHI + D * C * 2;
+constexpr int KB_BYTES = KB_GC + D * 4;          // 16896
 constexpr int B_WU0 = B_TRASH + 256;
 constexpr int B_KB0 = B_WU0 + 2 * WU_BYTES;
 constexpr int LDS_B = B_KB0 + 2 * KB_BYTES;
@@ -144,6 +145,8 @@ static_assert(LDS_B <= 160 * 1024, "LDS budget");
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // The depthwise conv on bf16 pairs: a.x * b.x + a.y * b.y + c (products exact in fp32).
 __device__ __forceinline__ float dot2(bf16x2 a, bf16x2 b, float c) {
@@ -161,6 +164,16 @@ struct Split8 {
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// fp16 operands (the phase-B products): 11 significant bits, with the state-side operand split
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x8 to_f16x8(const float (&x)[8]) {
+  f16x8 h;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = (_Float16)x[e];
+  return h;
 }
 // hi.hi + hi.lo + lo.hi: about 16 significant bits per operand
 __device__ __forceinline__ f32x4 mfma3(const Split8& a, const Split8& b, f32x4 c) {
@@ -279,11 +292,6 @@ __device__ __forceinline__ float silu_fast(float y) { return y * __builtin_amdgc
 constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp2f_(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ void store_split8(__bf16* hi, __bf16* lo, const float (&x)[8]) {
-  const Split8 sp = split(x);
-  *reinterpret_cast<bf16x8*>(hi) = sp.hi;
-  *reinterpret_cast<bf16x8*>(lo) = sp.lo;
-}
 
 // ---------------------------------------------------------------------------------------------
 // Phase A: persistent workgroups (one per CU) loop over the tasks (chunk, head, sequence); the
@@ -917,15 +925,13 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
         }
       }
     }
-    __syncthreads();  // every read of X is done: W hi / lo take its place
+    __syncthreads();  // every read of X is done: W (fp16) takes X hi's place
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int o = (16 * I + 4 * lg + r) * PKB + 16 * wave + l16;
-        const __bf16 hi = (__bf16)wacc[I][r];
-        sKb[o] = hi;
-        sXlo[o] = (__bf16)(wacc[I][r] - (float)hi);
+        reinterpret_cast<_Float16*>(sKb)[o] = (_Float16)wacc[I][r];
       }
     // W as this wave's split B operand over tokens, in the token order of its own accumulators: k-step
     // s, lane group g, element e <-> token 32 s + 4 g + e (e < 4), 32 s + 16 + 4 g + e - 4 (e >= 4)
@@ -942,17 +948,14 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       }
     __syncthreads();
 
-    // ---- write W and K~^T in fragment order (16-byte stores, 8 elements per lane-task) ----
-    __bf16* kthi = reinterpret_cast<__bf16*>(blk + W_KTHI);
-    __bf16* ktlo = reinterpret_cast<__bf16*>(blk + W_KTLO);
-    __bf16* wdst = reinterpret_cast<__bf16*>(blk + W_W);
-    __bf16* wldst = reinterpret_cast<__bf16*>(blk + W_WLO);
+    // ---- write W and K~^T in fragment order (fp16, 16-byte stores, 8 elements per lane-task) ----
+    _Float16* kthi = reinterpret_cast<_Float16*>(blk + W_KTHI);
+    _Float16* wdst = reinterpret_cast<_Float16*>(blk + W_W);
     for (int task = tid; task < C * D / 8; task += NT) {
-      // W hi and lo: [64 tokens][128 channels]
+      // W: [64 tokens][128 channels]
       const int t = task >> 4, c8 = (task & 15) * 8;
       const int fo = frag_offset(t, c8, D);
-      *reinterpret_cast<bf16x8*>(wdst + fo) = *reinterpret_cast<const bf16x8*>(sKb + t * PKB + c8);
-      *reinterpret_cast<bf16x8*>(wldst + fo) = *reinterpret_cast<const bf16x8*>(sXlo + t * PKB + c8);
+      *reinterpret_cast<f16x8*>(wdst + fo) = *reinterpret_cast<const f16x8*>(sKb + t * PKB + c8);
       // K~^T = (KC e^(Gam_C - Gam_n(J)))^T: [128 channels][64 tokens]; the lanes of a wave take
       // 64 consecutive channels of one 8-token group, so the column reads of KC hit 64 banks
       const int c = task & 127, t8 = (task >> 7) * 8;
@@ -961,7 +964,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = sG[(t8 + e) * PQ + c] * fac;
-      store_split8(kthi + ko, ktlo + ko, v);
+      *reinterpret_cast<f16x8*>(kthi + ko) = to_f16x8(v);
     }
     // every lane stores (four lanes per value, the same value) so that the number of stores is fixed
     reinterpret_cast<float*>(blk + W_GC)[tid & 127] = sGC[tid & 127];
@@ -1069,15 +1072,14 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     }
     __syncthreads();
 
-    // ---- write P in fragment order ----
-    __bf16* phi = reinterpret_cast<__bf16*>(blk + W_PHI);
-    __bf16* plo = reinterpret_cast<__bf16*>(blk + W_PLO);
+    // ---- write P in fragment order (fp16) ----
+    _Float16* phi = reinterpret_cast<_Float16*>(blk + W_PHI);
     for (int task = tid; task < C * D / 8; task += NT) {
       const int t = task >> 4, c8 = (task & 15) * 8;
       const int fo = frag_offset(t, c8, D);
       float v[8];
       ld8(sQ + t * PQ + c8, v);
-      store_split8(phi + fo, plo + fo, v);
+      *reinterpret_cast<f16x8*>(phi + fo) = to_f16x8(v);
     }
     __syncthreads();  // the next task overwrites the staging rows and tables
     cur = nxt;
@@ -1095,18 +1097,15 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 // ---------------------------------------------------------------------------------------------
 // Operands the output waves (4-7) keep in registers: P hi / lo of their row tile and their Y tile.
 struct OpTiles {
-  bf16x8 x0[4], x1[4];  // P hi / lo, row tile I = wave - 4 (4 k-steps)
-  f32x4 y;              // Y tile (I, column tile vb)
+  f16x8 x0[4];  // P (fp16), row tile I = wave - 4 (4 k-steps)
+  f32x4 y;      // Y tile (I, column tile vb)
 };
 
 __device__ __forceinline__ void load_out_tiles(const unsigned char* blk, int I, int lane, int vb, OpTiles& o) {
-  const bf16x8* x0p = reinterpret_cast<const bf16x8*>(blk + W_PHI) + (I * 4) * 64 + lane;
-  const bf16x8* x1p = reinterpret_cast<const bf16x8*>(blk + W_PLO) + (I * 4) * 64 + lane;
+  const f16x8* x0p = reinterpret_cast<const f16x8*>(blk + W_PHI) + (I * 4) * 64 + lane;
 #pragma unroll
   for (int s = 0; s < 4; ++s) o.x0[s] = x0p[s * 64];
   o.y = reinterpret_cast<const f32x4*>(blk + W_Y)[(I * 8 + vb) * 64 + lane];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) o.x1[s] = x1p[s * 64];
 }
 
 // Direct global -> LDS copies (gfx950 global_load_lds): lane l's bytes land at lds + l * size.
@@ -1130,10 +1129,10 @@ template <bool VL>
 __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTab st, const unsigned char* __restrict__ ws,
                                                            float* __restrict__ ows) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __bf16* sUhi = reinterpret_cast<__bf16*>(smem + B_UHI);
-  __bf16* sUlo = reinterpret_cast<__bf16*>(smem + B_ULO);
-  __bf16* sShi = reinterpret_cast<__bf16*>(smem + B_SHI);
-  __bf16* sSlo = reinterpret_cast<__bf16*>(smem + B_SLO);
+  _Float16* sUhi = reinterpret_cast<_Float16*>(smem + B_UHI);
+  _Float16* sUlo = reinterpret_cast<_Float16*>(smem + B_ULO);
+  _Float16* sShi = reinterpret_cast<_Float16*>(smem + B_SHI);
+  _Float16* sSlo = reinterpret_cast<_Float16*>(smem + B_SLO);
 
   const int H = a.H;
   const int h = blockIdx.x % H;
@@ -1190,19 +1189,19 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
   auto wubuf = [&](int c) { return smem + B_WU0 + (c & 1) * WU_BYTES; };
   auto kbuf = [&](int c) { return smem + B_KB0 + (c & 1) * KB_BYTES; };
 
-  // ---- loader waves (lw = 0..3): each copies 9 of the 36 W hi | W lo | Ut fragments and 8 of the
-  //      32 K~^T fragments of a chunk (wave 3 also e^Gam_C); cache lines of later chunks touched ----
+  // ---- loader waves (lw = 0..3): each copies 5 of the 20 W | Ut fragments and 4 of the 16 K~^T
+  //      fragments of a chunk (wave 3 also e^Gam_C); cache lines of later chunks touched ----
   const int lw = wave - 8;
-  constexpr int N_WU = 9, N_K = 8;
+  constexpr int N_WU = 5, N_K = 4;
   Cursor cur_wu = cursor0(), cur_k = cursor0(), cur_t = cursor0();
   auto issue_wu = [&](int cn) {
     const unsigned char* blk = chunk_ptr(cur_wu, cn);
     unsigned char* wb = wubuf(cn);
 #pragma unroll
     for (int q = 0; q < N_WU; ++q) {
-      // 0..15: W hi fragment f; 16..31: W lo fragment f - 16; 32..35: Ut row tile f - 32 of column tile vb
+      // 0..15: W fragment f; 16..19: Ut row tile f - 16 of column tile vb
       const int f = lw * N_WU + q;
-      const unsigned char* src = f < 32 ? blk + W_W + f * 1024 : blk + W_UT + ((f - 32) * 8 + vb) * 1024;
+      const unsigned char* src = f < 16 ? blk + W_W + f * 1024 : blk + W_UT + ((f - 16) * 8 + vb) * 1024;
       dma16(src + lane * 16, wb + WU_W + f * 1024);
     }
   };
@@ -1211,7 +1210,7 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
     unsigned char* kb = kbuf(cn);
 #pragma unroll
     for (int q = 0; q < N_K; ++q) {
-      const int f = lw * N_K + q;  // 0..15: K~^T hi fragment f; 16..31: lo fragment f - 16
+      const int f = lw * N_K + q;  // K~^T fragment f
       dma16(blk + W_KTHI + f * 1024 + lane * 16, kb + KB_KHI + f * 1024);
     }
     if (lw == 3) {
@@ -1322,19 +1321,20 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
   f32x4 Sacc[2];
   auto s_in = [&](int sq) { return a.state_in + (seq_slot(sq) * H + h) * D * D + vb * NVB + l16; };
   auto s_out = [&](int sq) { return a.state_out + (seq_slot(sq) * H + h) * D * D + vb * NVB + l16; };
-  // S^T as the split B operand [column][channel]; the lane's four rows are contiguous
+  // S^T as the split fp16 B operand [column][channel] (hi + lo: ~22 significant bits); the lane's
+  // four rows are contiguous
   auto write_state_operand = [&]() {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int t = wave + 4 * u;
-      bf16x4 hi, lo;
+      f16x4 hi, lo;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        hi[r] = (__bf16)Sacc[u][r];
-        lo[r] = (__bf16)(Sacc[u][r] - (float)hi[r]);
+        hi[r] = (_Float16)Sacc[u][r];
+        lo[r] = (_Float16)(Sacc[u][r] - (float)hi[r]);
       }
-      *reinterpret_cast<bf16x4*>(sShi + l16 * PST + 16 * t + 4 * lg) = hi;
-      *reinterpret_cast<bf16x4*>(sSlo + l16 * PST + 16 * t + 4 * lg) = lo;
+      *reinterpret_cast<f16x4*>(sShi + l16 * PST + 16 * t + 4 * lg) = hi;
+      *reinterpret_cast<f16x4*>(sSlo + l16 * PST + 16 * t + 4 * lg) = lo;
     }
   };
 
@@ -1354,16 +1354,14 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const bf16x8 uh = *reinterpret_cast<const bf16x8*>(sUhi + l16 * PVT + 32 * s + 8 * lg);
-      const bf16x8 ul = *reinterpret_cast<const bf16x8*>(sUlo + l16 * PVT + 32 * s + 8 * lg);
+      const f16x8 uh = *reinterpret_cast<const f16x8*>(sUhi + l16 * PVT + 32 * s + 8 * lg);
+      const f16x8 ul = *reinterpret_cast<const f16x8*>(sUlo + l16 * PVT + 32 * s + 8 * lg);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int t = wave + 4 * u;
-        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kb + KB_KHI + ((t * 2 + s) * 64 + lane) * 16);
-        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kb + KB_KLO + ((t * 2 + s) * 64 + lane) * 16);
-        sa[u] = mfma(k0, uh, sa[u]);
-        sb[u] = mfma(k0, ul, sb[u]);
-        sb[u] = mfma(k1, uh, sb[u]);
+        const f16x8 k0 = *reinterpret_cast<const f16x8*>(kb + KB_KHI + ((t * 2 + s) * 64 + lane) * 16);
+        sa[u] = mfma16(k0, uh, sa[u]);
+        sb[u] = mfma16(k0, ul, sb[u]);
       }
     }
 #pragma unroll
@@ -1404,24 +1402,22 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
       f32x4 pa = zero4(), pb = zero4();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 w = *reinterpret_cast<const bf16x8*>(wb + WU_W + ((I * 4 + s) * 64 + lane) * 16);
-        const bf16x8 wl = *reinterpret_cast<const bf16x8*>(wb + WU_WLO + ((I * 4 + s) * 64 + lane) * 16);
-        const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
-        const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSlo + l16 * PST + 32 * s + 8 * lg);
-        pa = mfma(w, sh, pa);
-        pb = mfma(w, sl, pb);
-        pb = mfma(wl, sh, pb);
+        const f16x8 w = *reinterpret_cast<const f16x8*>(wb + WU_W + ((I * 4 + s) * 64 + lane) * 16);
+        const f16x8 sh = *reinterpret_cast<const f16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
+        const f16x8 sl = *reinterpret_cast<const f16x8*>(sSlo + l16 * PST + 32 * s + 8 * lg);
+        pa = mfma16(w, sh, pa);
+        pb = mfma16(w, sl, pb);
       }
       const f32x4 ut = *reinterpret_cast<const f32x4*>(wb + WU_UT + (I * 64 + lane) * 16);
-      bf16x4 hi, lo;
+      f16x4 hi, lo;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float u = ut[r] - (pa[r] + pb[r]);
-        hi[r] = (__bf16)u;
-        lo[r] = (__bf16)(u - (float)hi[r]);
+        hi[r] = (_Float16)u;
+        lo[r] = (_Float16)(u - (float)hi[r]);
       }
-      *reinterpret_cast<bf16x4*>(sUhi + l16 * PVT + 16 * I + 4 * lg) = hi;
-      *reinterpret_cast<bf16x4*>(sUlo + l16 * PVT + 16 * I + 4 * lg) = lo;
+      *reinterpret_cast<f16x4*>(sUhi + l16 * PVT + 16 * I + 4 * lg) = hi;
+      *reinterpret_cast<f16x4*>(sUlo + l16 * PVT + 16 * I + 4 * lg) = lo;
       lds_barrier();  // (b)
       state_update(kbuf(ci));
       if (seq_last) {
@@ -1454,11 +1450,10 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
       f32x4 oa = zero4(), ob = zero4();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
-        const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSlo + l16 * PST + 32 * s + 8 * lg);
-        oa = mfma(cur.x0[s], sh, oa);
-        ob = mfma(cur.x0[s], sl, ob);
-        ob = mfma(cur.x1[s], sh, ob);
+        const f16x8 sh = *reinterpret_cast<const f16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
+        const f16x8 sl = *reinterpret_cast<const f16x8*>(sSlo + l16 * PST + 32 * s + 8 * lg);
+        oa = mfma16(cur.x0[s], sh, oa);
+        ob = mfma16(cur.x0[s], sl, ob);
       }
       f32x4 o;
 #pragma unroll
