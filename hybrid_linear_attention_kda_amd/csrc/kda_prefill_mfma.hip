@@ -23,8 +23,8 @@
 //      Ut = T (beta V),  Y = A_qk Ut,  P = Q~ - A_qk W,
 //    with Q~ = Q e^Gam and K~ = K e^(Gam_C - Gam).  Everything that does not
 //    depend on the state is written to the workspace once per chunk: P, W and K~^T
-//    (transposed) as fp16, Ut and Y as fp32 and e^Gam_C as fp32, each in the order
-//    the matrix cores consume it.
+//    (transposed) and Y as fp16, Ut and e^Gam_C as fp32, each in the order the
+//    matrix cores consume it.
 //  B (sequential over chunks, one workgroup per (sequence, head, 16-column
 //    block of d_v); with a sequence table, per group of consecutive sequences,
 //    whose chunks it runs as one stream): per chunk
@@ -110,9 +110,9 @@ constexpr int W_PHI = 0;                   // P = Q~ - A_qk W [64][128] fp16 (16
 constexpr int W_KTHI = W_PHI + C * D * 2;  // K~^T [128][64] fp16
 constexpr int W_W = W_KTHI + D * C * 2;    // W [64][128] fp16
 constexpr int W_UT = W_W + C * D * 2;      // Ut = T (beta V) [64][128] fp32, accumulator-fragment order
-constexpr int W_Y = W_UT + C * D * 4;      // Y = A_qk Ut [64][128] fp32, accumulator-fragment order
-constexpr int W_GC = W_Y + C * D * 4;      // e^Gam_C [128] fp32
-constexpr int CH_BYTES = W_GC + D * 4;     // 115200
+constexpr int W_Y = W_UT + C * D * 4;      // Y = A_qk Ut [64][128] fp16, accumulator-fragment order
+constexpr int W_GC = W_Y + C * D * 2;      // e^Gam_C [128] fp32
+constexpr int CH_BYTES = W_GC + D * 4;     // 98816
 static_assert(CH_BYTES % 256 == 0, "tile blocks stay 256-byte aligned");
 
 // Phase B: 8 compute waves and 4 loader waves per workgroup.
@@ -1048,7 +1048,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
         }
         ub[st] = split(x);
       }
-      f32x4* yd = reinterpret_cast<f32x4*>(blk + W_Y);
+      f16x4* yd = reinterpret_cast<f16x4*>(blk + W_Y);
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
         f32x4 ya = zero4(), pa = zero4();
@@ -1061,7 +1061,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
           ya = mfma3(as, ub[st], ya);
           pa = mfma3(as, Split8{wb[st], wbl[st]}, pa);
         }
-        yd[(I * 8 + wave) * 64 + lane] = ya;
+        yd[(I * 8 + wave) * 64 + lane] = f16x4{(_Float16)ya[0], (_Float16)ya[1], (_Float16)ya[2], (_Float16)ya[3]};
         // P = QR e^Gam_n - A_qk W, in place of QR (this lane owns these elements)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -1098,14 +1098,14 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 // Operands the output waves (4-7) keep in registers: P hi / lo of their row tile and their Y tile.
 struct OpTiles {
   f16x8 x0[4];  // P (fp16), row tile I = wave - 4 (4 k-steps)
-  f32x4 y;      // Y tile (I, column tile vb)
+  f16x4 y;      // Y tile (I, column tile vb), fp16
 };
 
 __device__ __forceinline__ void load_out_tiles(const unsigned char* blk, int I, int lane, int vb, OpTiles& o) {
   const f16x8* x0p = reinterpret_cast<const f16x8*>(blk + W_PHI) + (I * 4) * 64 + lane;
 #pragma unroll
   for (int s = 0; s < 4; ++s) o.x0[s] = x0p[s * 64];
-  o.y = reinterpret_cast<const f32x4*>(blk + W_Y)[(I * 8 + vb) * 64 + lane];
+  o.y = reinterpret_cast<const f16x4*>(blk + W_Y)[(I * 8 + vb) * 64 + lane];
 }
 
 // Direct global -> LDS copies (gfx950 global_load_lds): lane l's bytes land at lds + l * size.
@@ -1457,7 +1457,7 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
       }
       f32x4 o;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = (oa[r] + ob[r]) + cur.y[r];
+      for (int r = 0; r < 4; ++r) o[r] = (oa[r] + ob[r]) + (float)cur.y[r];
       lds_barrier();  // (b)
       const int c0 = rc.ci * C, L = min(C, rc.len - c0);
       float* op = ows + ((rc.tok0 + c0) * H + h) * D + vb * NVB + l16;
