@@ -57,8 +57,9 @@
 // is below 2).
 //
 // The output RMSNorm needs all 128 columns of o, which live in eight
-// workgroups, so o (fp32) goes to the workspace and a third, bandwidth-bound
-// kernel applies the norm, weight and gate.  Phase B's loader waves also write the new conv state.
+// workgroups, so o goes to the workspace as fp16 (11 significant bits; |o| stays far inside
+// fp16's range) and a third, bandwidth-bound kernel applies the norm,
+// weight and gate.  Phase B's loader waves also write the new conv state.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -1127,7 +1128,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 template <bool VL>
 __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTab st, const unsigned char* __restrict__ ws,
-                                                           float* __restrict__ ows) {
+                                                           _Float16* __restrict__ ows) {
   extern __shared__ __align__(16) unsigned char smem[];
   _Float16* sUhi = reinterpret_cast<_Float16*>(smem + B_UHI);
   _Float16* sUlo = reinterpret_cast<_Float16*>(smem + B_ULO);
@@ -1442,7 +1443,7 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
     // the end of the sequence go to a scratch slot after o, so that every lane issues the same
     // stores; the last chunk's tiles are loaded again in place of chunks past the end.
     const int I = wave - 4;
-    float* scratch = ows + (VL ? (long long)st.tok0[st.n] : (long long)a.B * a.T) * HD + lane * 4;
+    _Float16* scratch = ows + (VL ? (long long)st.tok0[st.n] : (long long)a.B * a.T) * HD + lane * 4;
     Cursor cur_o = cursor0(), cur_l = cursor0();
     auto chunk_o = [&](int ci, OpTiles& cur) __attribute__((always_inline)) {
       const ChunkRef rc = locate(cur_o, ci);
@@ -1460,11 +1461,11 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
       for (int r = 0; r < 4; ++r) o[r] = (oa[r] + ob[r]) + (float)cur.y[r];
       lds_barrier();  // (b)
       const int c0 = rc.ci * C, L = min(C, rc.len - c0);
-      float* op = ows + ((rc.tok0 + c0) * H + h) * D + vb * NVB + l16;
+      _Float16* op = ows + ((rc.tok0 + c0) * H + h) * D + vb * NVB + l16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * I + 4 * lg + r;
-        *(t < L ? op + (long long)t * HD : scratch + r) = o[r];
+        *(t < L ? op + (long long)t * HD : scratch + r) = (_Float16)o[r];
       }
       load_out_tiles(chunk_ptr(cur_l, min(ci + 2, NG - 1)), I, lane, vb, cur);
     };
@@ -1502,21 +1503,21 @@ __device__ __forceinline__ void unpack8(const uint4 u, float (&v)[8]) {
 }
 
 template <typename OT>
-__global__ __launch_bounds__(256) void kda_out_norm_kernel(const float* __restrict__ ows, const bf16_t* __restrict__ gout,
+__global__ __launch_bounds__(256) void kda_out_norm_kernel(const _Float16* __restrict__ ows, const bf16_t* __restrict__ gout,
                                                         const bf16_t* __restrict__ nw, OT* __restrict__ out,
                                                         long long rows, float eps) {
   const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int c8 = (threadIdx.x & 15) * 8;
   if (row >= rows) return;  // the 16 lanes of a row leave together
   // o and the gate are read once: non-temporal loads keep them from displacing cached lines
-  const f32x4 a0v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ows + row * D + c8));
-  const f32x4 a1v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ows + row * D + c8 + 4));
-  const float4 a0 = make_float4(a0v.x, a0v.y, a0v.z, a0v.w), a1 = make_float4(a1v.x, a1v.y, a1v.z, a1v.w);
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const f16x8 ov = __builtin_bit_cast(f16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ows + row * D + c8)));
   const u32x4 gq = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gout + row * D + c8));
   const uint4 g = make_uint4(gq.x, gq.y, gq.z, gq.w);
   const uint4 w = *reinterpret_cast<const uint4*>(nw + c8);
-  const float o[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (float)ov[e];
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss += o[e] * o[e];
@@ -1544,7 +1545,7 @@ bool prefill_mfma_supported(int Dh, int chunk, int io, int W, float lb, int gate
 }
 
 size_t prefill_mfma_workspace(long long chunks, long long tokens, int H) {
-  return (size_t)chunks * H * CH_BYTES + (size_t)tokens * H * D * sizeof(float) + 64 * 4 * sizeof(float);
+  return (size_t)chunks * H * CH_BYTES + (size_t)tokens * H * D * sizeof(_Float16) + 64 * 4 * sizeof(_Float16);
 }
 
 template <bool VL>
@@ -1553,7 +1554,7 @@ static hipError_t launch_mfma_t(const LayerArgs& a, const SeqTab& st, void* ws, 
   const int NC = (a.T + C - 1) / C;
   const long long chunks = VL ? st.total_chunks : (long long)a.B * NC;
   const long long tokens = VL ? st.tok0[st.n] : (long long)a.B * a.T;
-  float* ows = reinterpret_cast<float*>(tiles + (size_t)chunks * a.H * CH_BYTES);
+  _Float16* ows = reinterpret_cast<_Float16*>(tiles + (size_t)chunks * a.H * CH_BYTES);
   {
     hipError_t e0 = set_lds_limit(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL, 0>), LDS_A);
     if (e0 == hipSuccess) e0 = set_lds_limit(reinterpret_cast<const void*>(kda_chunk_prep_kernel<VL, 1>), LDS_A);
