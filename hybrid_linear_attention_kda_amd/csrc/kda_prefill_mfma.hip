@@ -77,6 +77,7 @@ constexpr int PQ = 132;      // fp32 pitch of [64][128] arrays
 constexpr int PKB = 136;     // bf16 pitch of [64][128] arrays
 constexpr int PA = 68;       // fp32 pitch of [64][64] arrays
 constexpr int PTB = 68;      // bf16 pitch of the [64][64] split planes (8-byte aligned rows)
+constexpr int PXT = 68;      // bf16 pitch of the transposed [128][64] X planes (8-byte aligned rows)
 constexpr int PR = 280;      // bf16 pitch of the raw staging rows: q 128 | k 128 | v 16 | pad
 constexpr int RROWS = C + HALO;
 
@@ -99,6 +100,7 @@ constexpr int OFF_AQK = OFF_SEG + 4 * D * 4;           // A_qk hi | lo [64][PTB]
 constexpr int OFF_GA = OFF_AQK + C * PA * 4;           // softplus branch: Gam at the sub-chunk ends [4][128]
 constexpr int LDS_A = OFF_GA + 4 * D * 4;
 static_assert(STG_BYTES >= 2 * C * PA * 4, "staging aliases");
+static_assert(D * PXT * 2 <= C * PKB * 2 && C * PA * 4 + D * PXT * 2 <= STG_BYTES, "X planes alias KR and the fp32 T");
 static_assert(LDS_A <= 160 * 1024, "LDS budget");
 
 // Workspace tile block per (sequence, head, chunk), written by phase A and read by phase B.
@@ -644,17 +646,37 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       const float* nq = sNrm + 16 * seg;
       const float* nk = sNrm + C + 16 * seg;
       if (!SP) {
+        // the segment's normalisers and betas are the same for every lane of the wave: 16-byte
+        // broadcast reads
+        float nqv[16], nkv[16], bev[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 a4 = reinterpret_cast<const float4*>(nq)[g];
+          const float4 b4 = reinterpret_cast<const float4*>(nk)[g];
+          const float4 c4 = reinterpret_cast<const float4*>(sBeta + 16 * seg)[g];
+          nqv[4 * g] = a4.x; nqv[4 * g + 1] = a4.y; nqv[4 * g + 2] = a4.z; nqv[4 * g + 3] = a4.w;
+          nkv[4 * g] = b4.x; nkv[4 * g + 1] = b4.y; nkv[4 * g + 2] = b4.z; nkv[4 * g + 3] = b4.w;
+          bev[4 * g] = c4.x; bev[4 * g + 1] = c4.y; bev[4 * g + 2] = c4.z; bev[4 * g + 3] = c4.w;
+        }
+        // every read of the lane's column comes before its first write: the compiler cannot tell
+        // the writes from the later reads, and would otherwise wait out each round trip in turn
+        float qr[16], kr[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          qr[k] = qp[k * PQ];
+          kr[k] = kp[k * PQ];
+        }
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
           const float d = gl[k] - gl[0];
           const float e1 = exp2f_(d);   // <= 1
           const float e2 = exp2f_(-d);  // in [1, e^(15|lb|)]
-          const float q = qp[k * PQ] * nq[k];
-          const float kv = kp[k * PQ] * nk[k];
+          const float q = qr[k] * nqv[k];
+          const float kv = kr[k] * nkv[k];
           qp[k * PQ] = q * e1;
           rp[k * PKB] = (__bf16)(kv * e1);
           kp[k * PQ] = kv * e2;
-          xk[k] = sBeta[16 * seg + k] * (kv * e1) * egn;
+          xk[k] = bev[k] * (kv * e1) * egn;
         }
       } else {
         float qn[16], kn[16], al[16];
@@ -703,19 +725,18 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
         }
       }
     }
-    if (tid < D) {
-      const int c = tid;
+    // factor tables: lane -> channel c, sub-chunk I = tid / 128 (the rows of I spread over all waves)
+    {
+      const int c = tid & 127, I = tid >> 7;
       const float GC = sGn[4 * D + c];
+      const float GI = sGn[I * D + c];
+      sEn[I * D + c] = exp2f_(GI);
+      // column anchors: the sub-chunk's first token, or its last one for the softplus branch
+      sFac[I * D + c] = exp2f_(GC - (SP ? sGa[I * D + c] : GI));
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        const float GI = sGn[I * D + c];
-        sEn[I * D + c] = exp2f_(GI);
-        // column anchors: the sub-chunk's first token, or its last one for the softplus branch
-        sFac[I * D + c] = exp2f_(GC - (SP ? sGa[I * D + c] : GI));
-#pragma unroll
-        for (int J = 0; J < I; ++J) sE[pair_index(I, J) * D + c] = exp2f_(GI - (SP ? sGa[J * D + c] : sGn[J * D + c]));
-      }
-      sGC[c] = exp2f_(GC);
+      for (int J = 0; J < 3; ++J)
+        if (J < I) sE[pair_index(I, J) * D + c] = exp2f_(GI - (SP ? sGa[J * D + c] : sGn[J * D + c]));
+      if (I == 0) sGC[c] = exp2f_(GC);
     }
     __syncthreads();
 
@@ -849,17 +870,26 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     __syncthreads();
     // Off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, column block J = wave (0..2)
     // top to bottom on the fp32 matrix cores, while waves 3-7 form A_qk blocks 5..9.
+    // The sums M_I = sum_K A_IK T_KJ of every block below are started at once with their K = J
+    // terms, and each gains its K term as soon as T_KJ is formed (the terms in the order K = J, J+1,
+    // ...), so independent products overlap on the matrix core.
     if (wave < 3) {
       const int J = wave;
       float* sM = sTmp + wave * 16 * 17;
-      for (int I = J + 1; I < 4; ++I) {
-        f32x4 m = zero4();
-        for (int K = J; K < I; ++K)
+      auto add_term = [&](f32x4& m, int I, int K) __attribute__((always_inline)) {
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            m = mfma_f32(sAkk[(16 * I + l16) * PA + 16 * K + 4 * s + lg], sT[(16 * K + 4 * s + lg) * PA + 16 * J + l16], m);
+        for (int s = 0; s < 4; ++s)
+          m = mfma_f32(sAkk[(16 * I + l16) * PA + 16 * K + 4 * s + lg], sT[(16 * K + 4 * s + lg) * PA + 16 * J + l16], m);
+      };
+      f32x4 m[3] = {zero4(), zero4(), zero4()};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sM[(4 * lg + r) * 17 + l16] = m[r];
+      for (int I = 1; I < 4; ++I)
+        if (I > J) add_term(m[I - 1], I, J);
+#pragma unroll
+      for (int I = 1; I < 4; ++I) {
+        if (I <= J) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sM[(4 * lg + r) * 17 + l16] = m[I - 1][r];
         wave_lds_sync();
         f32x4 tij = zero4();
 #pragma unroll
@@ -868,6 +898,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 #pragma unroll
         for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * lg + r) * PA + 16 * J + l16] = -tij[r];
         wave_lds_sync();
+#pragma unroll
+        for (int I2 = I + 1; I2 < 4; ++I2) add_term(m[I2 - 1], I2, I);
       }
     } else {
       aqk_block(wave + 2);
@@ -890,16 +922,25 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 
     // ---- P8: W = T X on split bf16 (T hi.X hi + T hi.X lo + T lo.X hi): W sits beside the state in
     //      U = Ut - W S, a small difference of large terms when little decays, so it keeps ~16 bits.
-    //      X goes to LDS as split planes in place of KR (no longer read) and of the fp32 T (split
-    //      above); wave -> 16 key channels ----
-    __bf16* sXlo = reinterpret_cast<__bf16*>(smem + OFF_STG + C * PA * 4);  // [64][PKB], old fp32 T
+    //      X goes to LDS transposed, [channel][token], as split planes in place of KR (no longer
+    //      read) and of the fp32 T (split above): a lane writes its 16 tokens of one channel, and
+    //      a B-operand fragment (8 tokens of one channel) is two 8-byte reads; wave -> 16 key
+    //      channels ----
+    __bf16* sXhi = sKb;                                                      // [128][PXT]
+    __bf16* sXlo = reinterpret_cast<__bf16*>(smem + OFF_STG + C * PA * 4);  // [128][PXT], old fp32 T
     {
       const int i = tid & 127, seg = tid >> 7;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const __bf16 hi = (__bf16)xk[k];
-        sKb[(16 * seg + k) * PKB + i] = hi;
-        sXlo[(16 * seg + k) * PKB + i] = (__bf16)(xk[k] - (float)hi);
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 h4, l4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = xk[4 * g + e];
+          h4[e] = (__bf16)x;
+          l4[e] = (__bf16)(x - (float)h4[e]);
+        }
+        *reinterpret_cast<bf16x4*>(sXhi + i * PXT + 16 * seg + 4 * g) = h4;
+        *reinterpret_cast<bf16x4*>(sXlo + i * PXT + 16 * seg + 4 * g) = l4;
       }
     }
     __syncthreads();
@@ -909,12 +950,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int tb = 32 * s + 8 * lg;
-        bf16x8 xh, xl;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          xh[e] = sKb[(tb + e) * PKB + c];
-          xl[e] = sXlo[(tb + e) * PKB + c];
-        }
+        const bf16x8 xh = ld4x2(sXhi + c * PXT + tb, 4), xl = ld4x2(sXlo + c * PXT + tb, 4);
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
           if (32 * s > 16 * I + 15) continue;  // T is lower triangular
@@ -999,9 +1035,42 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     __syncthreads();
 
     // ---- P9: per wave, column tile j = wave of the value axis:
-    //      Ut = T (beta V) (split bf16), Y = A_qk Ut (split bf16), P = Q~ - A_qk W (A_qk split) ----
+    //      Ut = T (beta V) (split bf16), Y = A_qk Ut (split bf16), P = Q~ - A_qk W (A_qk split).
+    //      P does not depend on V: waves 4-7 form it first (matrix cores) while waves 0-3, which
+    //      share their SIMDs, run the conv of v (vector ALU), so the two units overlap ----
     {
       const int vc = 16 * wave + l16;
+      const bool pfirst = wave >= 4;
+      // A_qk W for row block I; P = QR e^Gam_n - A_qk W is written in place of QR at the end (this
+      // lane owns these elements), after every read of the A_qk planes, which the compiler could
+      // not otherwise move ahead of the writes
+      f32x4 pacc[4];
+      auto p_rows = [&](int I, const Split8 (&as)[2]) __attribute__((always_inline)) {
+        f32x4 pa = zero4();
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          if (32 * st > 16 * I + 15) continue;  // A_qk is lower triangular
+          pa = mfma3(as[st], Split8{wb[st], wbl[st]}, pa);
+        }
+        pacc[I] = pa;
+      };
+      auto aqk_rows = [&](int I, Split8 (&as)[2]) __attribute__((always_inline)) {
+        const int t = 16 * I + l16;  // A_qk row of this lane
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          if (32 * st > 16 * I + 15) continue;
+          const int o = t * PTB + 32 * st + 4 * lg;
+          as[st] = Split8{ld4x2(sAhi + o, 16), ld4x2(sAlo + o, 16)};
+        }
+      };
+      if (pfirst) {
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          Split8 as[2];
+          aqk_rows(I, as);
+          p_rows(I, as);
+        }
+      }
       // beta V for tokens 32 s + 8 lg + 0..7 of channel vc: the B operand of Ut
       Split8 bv[2];
 #pragma unroll
@@ -1052,24 +1121,28 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       f16x4* yd = reinterpret_cast<f16x4*>(blk + W_Y);
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
-        f32x4 ya = zero4(), pa = zero4();
-        const int t = 16 * I + l16;  // A_qk row of this lane
+        Split8 as[2];
+        aqk_rows(I, as);
+        f32x4 ya = zero4();
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           if (32 * st > 16 * I + 15) continue;  // A_qk is lower triangular
-          const int o = t * PTB + 32 * st + 4 * lg;
-          const Split8 as{ld4x2(sAhi + o, 16), ld4x2(sAlo + o, 16)};
-          ya = mfma3(as, ub[st], ya);
-          pa = mfma3(as, Split8{wb[st], wbl[st]}, pa);
+          ya = mfma3(as[st], ub[st], ya);
         }
         yd[(I * 8 + wave) * 64 + lane] = f16x4{(_Float16)ya[0], (_Float16)ya[1], (_Float16)ya[2], (_Float16)ya[3]};
-        // P = QR e^Gam_n - A_qk W, in place of QR (this lane owns these elements)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tr = 16 * I + 4 * lg + r;
-          sQ[tr * PQ + vc] = sQ[tr * PQ + vc] * sEn[I * D + vc] - pa[r];
-        }
+        if (!pfirst) p_rows(I, as);
       }
+      float qo[16], en[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        en[I] = sEn[I * D + vc];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) qo[4 * I + r] = sQ[(16 * I + 4 * lg + r) * PQ + vc];
+      }
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sQ[(16 * I + 4 * lg + r) * PQ + vc] = qo[4 * I + r] * en[I] - pacc[I][r];
     }
     __syncthreads();
 
