@@ -45,10 +45,11 @@
 // sub-chunk instead, which keeps every off-diagonal factor <= 1, and sums the four
 // diagonal blocks exactly per channel (see kda_chunk_prep_kernel).
 //
-// Precision.  bf16 operands round to 8 bits; phase A's contractions that feed
-// the output or the state use split bf16 (x = hi + lo, three MFMAs: hi.hi +
-// hi.lo + lo.hi): A_qk, Ut, Y, W = T X, A_qk W; A_kk runs in plain bf16 and T is
-// formed in fp32.  Phase B's three products with the state (W S, P S, K~^T U) take
+// Precision.  bf16 operands round to 8 bits; A_qk is formed on split bf16 (x = hi
+// + lo, three MFMAs: hi.hi + hi.lo + lo.hi), A_kk in plain bf16, and T in fp32.
+// The products of phase A that use them (W = T X, Ut = T (beta V), Y = A_qk Ut,
+// A_qk W) take T and A_qk as fp16 (11 significant bits) and the other operand
+// split into fp16 hi + lo (~22 bits), two MFMAs each, as phase B does.  Phase B's three products with the state (W S, P S, K~^T U) take
 // W, P and K~^T as fp16 (11 significant bits, half the bytes of a split bf16 pair
 // on the per-chunk operand path) and S or U split into fp16 hi + lo (~22 bits),
 // two MFMAs each.  fp16's range holds these values: |q| and |k| are at most
@@ -194,6 +195,25 @@ __device__ __forceinline__ Split8 split(const float (&x)[8]) {
   }
   return s;
 }
+// fp16 hi + lo of 8 values (~22 significant bits): the B operands of the products with an fp16 A
+struct Half8 {
+  f16x8 hi, lo;
+};
+__device__ __forceinline__ Half8 split16(const float (&x)[8]) {
+  Half8 s;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const _Float16 h = (_Float16)x[e];
+    s.hi[e] = h;
+    s.lo[e] = (_Float16)(x[e] - (float)h);
+  }
+  return s;
+}
+// A (fp16) times B (fp16 hi + lo): the small term first
+__device__ __forceinline__ f32x4 mfma2h(f16x8 a, const Half8& b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b.lo, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b.hi, c, 0, 0, 0);
+}
 __device__ __forceinline__ bf16x8 round8(const float (&x)[8]) {
   bf16x8 r;
 #pragma unroll
@@ -212,6 +232,11 @@ __device__ __forceinline__ bf16x8 ld4x2(const __bf16* p, int off2) {
   const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
   const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + off2);
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ f16x8 ld4x2(const _Float16* p, int off2) {
+  const f16x4 a = *reinterpret_cast<const f16x4*>(p);
+  const f16x4 b = *reinterpret_cast<const f16x4*>(p + off2);
+  return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 // fp32 matrix core step: D += A[16 x 4] B[4 x 16]; lane l holds A[l % 16][l / 16] and B[l / 16][l % 16]
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
@@ -418,10 +443,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
   __bf16* sRaw = reinterpret_cast<__bf16*>(smem + OFF_STG);
   float* sAkk = reinterpret_cast<float*>(smem + OFF_STG);
   float* sT = reinterpret_cast<float*>(smem + OFF_STG + C * PA * 4);
-  __bf16* sAhi = reinterpret_cast<__bf16*>(smem + OFF_AQK);  // A_qk split planes [64][PTB]
-  __bf16* sAlo = sAhi + C * PTB;
-  __bf16* sThi = reinterpret_cast<__bf16*>(smem + OFF_STG);  // T split planes, in place of A_kk
-  __bf16* sTlo = sThi + C * PTB;
+  _Float16* sA16 = reinterpret_cast<_Float16*>(smem + OFF_AQK);  // A_qk [64][PTB] fp16
+  _Float16* sT16 = reinterpret_cast<_Float16*>(smem + OFF_STG);  // T [64][PTB] fp16, in place of A_kk
   float* sTmp = reinterpret_cast<float*>(smem + OFF_TMP);
   float* sGn = reinterpret_cast<float*>(smem + OFF_GN);
   float* sEn = reinterpret_cast<float*>(smem + OFF_EN);
@@ -781,9 +804,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
         diag_entry(64 * b + lane, qk, i, j);
         const int R = base + i, Cc = base + j;
         if (qk) {
-          const __bf16 hi = (__bf16)tot;
-          sAhi[R * PTB + Cc] = hi;
-          sAlo[R * PTB + Cc] = (__bf16)(tot - (float)hi);
+          sA16[R * PTB + Cc] = (_Float16)tot;
         } else {
           sAkk[R * PA + Cc] = sBeta[R] * tot;
         }
@@ -792,10 +813,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       for (int e = 0; e < 4; ++e) {
         const int j = 4 * lg + e, R = base + l16, Cc = base + j;
         if (j >= l16) sAkk[R * PA + Cc] = 0.f;
-        if (j > l16) {
-          sAhi[R * PTB + Cc] = (__bf16)0.f;
-          sAlo[R * PTB + Cc] = (__bf16)0.f;
-        }
+        if (j > l16) sA16[R * PTB + Cc] = (_Float16)0.f;
       }
     }
     __syncthreads();
@@ -822,10 +840,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * I + 4 * lg + r, j = 16 * J + l16;
-        const float v = j <= i ? acc[r] : 0.f;  // zero above the diagonal
-        const __bf16 hi = (__bf16)v;
-        sAhi[i * PTB + j] = hi;
-        sAlo[i * PTB + j] = (__bf16)(v - (float)hi);
+        sA16[i * PTB + j] = (_Float16)(j <= i ? acc[r] : 0.f);  // zero above the diagonal
       }
     };
 
@@ -859,8 +874,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       for (int idx = tid - 64; idx < 2 * 256; idx += NT - 64) {
         const int I = 2 * (idx >> 8), e = idx & 255;
         const int o = (16 * I + (e >> 4)) * PTB + 16 * (I + 1) + (e & 15);
-        sAhi[o] = (__bf16)0.f;
-        sAlo[o] = (__bf16)0.f;
+        sA16[o] = (_Float16)0.f;
       }
       if (wave < 3)
         akk_block(wave + 6);
@@ -905,42 +919,38 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       aqk_block(wave + 2);
     }
     __syncthreads();
-    // T as split bf16 planes in place of A_kk: eight elements per lane
+    // T as fp16 in place of A_kk: eight elements per lane
     {
       const int t = tid >> 3, j8 = (tid & 7) * 8;
       float v[8];
       ld8(sT + t * PA + j8, v);
-      const Split8 sp = split(v);
-      *reinterpret_cast<bf16x4*>(sThi + t * PTB + j8) = bf16x4{sp.hi[0], sp.hi[1], sp.hi[2], sp.hi[3]};
-      *reinterpret_cast<bf16x4*>(sThi + t * PTB + j8 + 4) = bf16x4{sp.hi[4], sp.hi[5], sp.hi[6], sp.hi[7]};
-      *reinterpret_cast<bf16x4*>(sTlo + t * PTB + j8) = bf16x4{sp.lo[0], sp.lo[1], sp.lo[2], sp.lo[3]};
-      *reinterpret_cast<bf16x4*>(sTlo + t * PTB + j8 + 4) = bf16x4{sp.lo[4], sp.lo[5], sp.lo[6], sp.lo[7]};
+      *reinterpret_cast<f16x4*>(sT16 + t * PTB + j8) = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+      *reinterpret_cast<f16x4*>(sT16 + t * PTB + j8 + 4) = f16x4{(_Float16)v[4], (_Float16)v[5], (_Float16)v[6], (_Float16)v[7]};
     }
     __syncthreads();
 
     prep_issue<VL>(a, st, knext, tid, nxt, 2);
 
-    // ---- P8: W = T X on split bf16 (T hi.X hi + T hi.X lo + T lo.X hi): W sits beside the state in
-    //      U = Ut - W S, a small difference of large terms when little decays, so it keeps ~16 bits.
-    //      X goes to LDS transposed, [channel][token], as split planes in place of KR (no longer
-    //      read) and of the fp32 T (split above): a lane writes its 16 tokens of one channel, and
-    //      a B-operand fragment (8 tokens of one channel) is two 8-byte reads; wave -> 16 key
+    // ---- P8: W = T X with T in fp16 and X split into fp16 hi + lo (T.X lo + T.X hi).  X goes to
+    //      LDS transposed, [channel][token], as two planes in place of KR (no longer read) and of
+    //      the fp32 T (converted above): a lane writes its 16 tokens of one channel, and a
+    //      B-operand fragment (8 tokens of one channel) is two 8-byte reads; wave -> 16 key
     //      channels ----
-    __bf16* sXhi = sKb;                                                      // [128][PXT]
-    __bf16* sXlo = reinterpret_cast<__bf16*>(smem + OFF_STG + C * PA * 4);  // [128][PXT], old fp32 T
+    _Float16* sXhi = reinterpret_cast<_Float16*>(sKb);                          // [128][PXT]
+    _Float16* sXlo = reinterpret_cast<_Float16*>(smem + OFF_STG + C * PA * 4);  // [128][PXT], old fp32 T
     {
       const int i = tid & 127, seg = tid >> 7;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        bf16x4 h4, l4;
+        f16x4 h4, l4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float x = xk[4 * g + e];
-          h4[e] = (__bf16)x;
-          l4[e] = (__bf16)(x - (float)h4[e]);
+          h4[e] = (_Float16)x;
+          l4[e] = (_Float16)(x - (float)h4[e]);
         }
-        *reinterpret_cast<bf16x4*>(sXhi + i * PXT + 16 * seg + 4 * g) = h4;
-        *reinterpret_cast<bf16x4*>(sXlo + i * PXT + 16 * seg + 4 * g) = l4;
+        *reinterpret_cast<f16x4*>(sXhi + i * PXT + 16 * seg + 4 * g) = h4;
+        *reinterpret_cast<f16x4*>(sXlo + i * PXT + 16 * seg + 4 * g) = l4;
       }
     }
     __syncthreads();
@@ -950,15 +960,11 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int tb = 32 * s + 8 * lg;
-        const bf16x8 xh = ld4x2(sXhi + c * PXT + tb, 4), xl = ld4x2(sXlo + c * PXT + tb, 4);
+        const Half8 x{ld4x2(sXhi + c * PXT + tb, 4), ld4x2(sXlo + c * PXT + tb, 4)};
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
           if (32 * s > 16 * I + 15) continue;  // T is lower triangular
-          const int o = (16 * I + l16) * PTB + 32 * s + 8 * lg;
-          const bf16x8 th = ld4x2(sThi + o, 4), tl = ld4x2(sTlo + o, 4);
-          wacc[I] = mfma(tl, xh, wacc[I]);
-          wacc[I] = mfma(th, xl, wacc[I]);
-          wacc[I] = mfma(th, xh, wacc[I]);
+          wacc[I] = mfma2h(ld4x2(sT16 + (16 * I + l16) * PTB + 32 * s + 8 * lg, 4), x, wacc[I]);
         }
       }
     }
@@ -972,17 +978,17 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       }
     // W as this wave's split B operand over tokens, in the token order of its own accumulators: k-step
     // s, lane group g, element e <-> token 32 s + 4 g + e (e < 4), 32 s + 16 + 4 g + e - 4 (e >= 4)
-    bf16x8 wb[2], wbl[2];
+    Half8 wb[2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < 2; ++st) {
+      float x[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float a0 = wacc[2 * st][e], a1 = wacc[2 * st + 1][e];
-        wb[st][e] = (__bf16)a0;
-        wb[st][e + 4] = (__bf16)a1;
-        wbl[st][e] = (__bf16)(a0 - (float)wb[st][e]);
-        wbl[st][e + 4] = (__bf16)(a1 - (float)wb[st][e + 4]);
+        x[e] = wacc[2 * st][e];
+        x[e + 4] = wacc[2 * st + 1][e];
       }
+      wb[st] = split16(x);
+    }
     __syncthreads();
 
     // ---- write W and K~^T in fragment order (fp16, 16-byte stores, 8 elements per lane-task) ----
@@ -1035,7 +1041,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     __syncthreads();
 
     // ---- P9: per wave, column tile j = wave of the value axis:
-    //      Ut = T (beta V) (split bf16), Y = A_qk Ut (split bf16), P = Q~ - A_qk W (A_qk split).
+    //      Ut = T (beta V), Y = A_qk Ut, P = Q~ - A_qk W (T and A_qk fp16, the other side fp16
+    //      hi + lo).
     //      P does not depend on V: waves 4-7 form it first (matrix cores) while waves 0-3, which
     //      share their SIMDs, run the conv of v (vector ALU), so the two units overlap ----
     {
@@ -1045,34 +1052,34 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       // lane owns these elements), after every read of the A_qk planes, which the compiler could
       // not otherwise move ahead of the writes
       f32x4 pacc[4];
-      auto p_rows = [&](int I, const Split8 (&as)[2]) __attribute__((always_inline)) {
+      auto p_rows = [&](int I, const f16x8 (&as)[2]) __attribute__((always_inline)) {
         f32x4 pa = zero4();
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           if (32 * st > 16 * I + 15) continue;  // A_qk is lower triangular
-          pa = mfma3(as[st], Split8{wb[st], wbl[st]}, pa);
+          pa = mfma2h(as[st], wb[st], pa);
         }
         pacc[I] = pa;
       };
-      auto aqk_rows = [&](int I, Split8 (&as)[2]) __attribute__((always_inline)) {
+      auto aqk_rows = [&](int I, f16x8 (&as)[2]) __attribute__((always_inline)) {
         const int t = 16 * I + l16;  // A_qk row of this lane
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           if (32 * st > 16 * I + 15) continue;
           const int o = t * PTB + 32 * st + 4 * lg;
-          as[st] = Split8{ld4x2(sAhi + o, 16), ld4x2(sAlo + o, 16)};
+          as[st] = ld4x2(sA16 + o, 16);
         }
       };
       if (pfirst) {
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-          Split8 as[2];
+          f16x8 as[2];
           aqk_rows(I, as);
           p_rows(I, as);
         }
       }
       // beta V for tokens 32 s + 8 lg + 0..7 of channel vc: the B operand of Ut
-      Split8 bv[2];
+      Half8 bv[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int tb = 32 * st + 8 * lg;
@@ -1091,7 +1098,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
                                   : dot2(tv23, pe[m + 1], dot2(tv01, pe[m], 0.f));
           xv[e] = sBeta[tb + e] * silu_fast(y);
         }
-        bv[st] = split(xv);
+        bv[st] = split16(xv);
       }
       f32x4 ut[4];
       f32x4* utd = reinterpret_cast<f32x4*>(blk + W_UT);
@@ -1101,13 +1108,12 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           if (32 * st > 16 * I + 15) continue;  // T is lower triangular
-          const int o = (16 * I + l16) * PTB + 32 * st + 8 * lg;
-          ut[I] = mfma3(Split8{ld4x2(sThi + o, 4), ld4x2(sTlo + o, 4)}, bv[st], ut[I]);
+          ut[I] = mfma2h(ld4x2(sT16 + (16 * I + l16) * PTB + 32 * st + 8 * lg, 4), bv[st], ut[I]);
         }
         utd[(I * 8 + wave) * 64 + lane] = ut[I];
       }
       // Ut as the B operand over tokens in accumulator token order (see wb)
-      Split8 ub[2];
+      Half8 ub[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         float x[8];
@@ -1116,18 +1122,18 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
           x[e] = ut[2 * st][e];
           x[e + 4] = ut[2 * st + 1][e];
         }
-        ub[st] = split(x);
+        ub[st] = split16(x);
       }
       f16x4* yd = reinterpret_cast<f16x4*>(blk + W_Y);
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
-        Split8 as[2];
+        f16x8 as[2];
         aqk_rows(I, as);
         f32x4 ya = zero4();
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           if (32 * st > 16 * I + 15) continue;  // A_qk is lower triangular
-          ya = mfma3(as[st], ub[st], ya);
+          ya = mfma2h(as[st], ub[st], ya);
         }
         yd[(I * 8 + wave) * 64 + lane] = f16x4{(_Float16)ya[0], (_Float16)ya[1], (_Float16)ya[2], (_Float16)ya[3]};
         if (!pfirst) p_rows(I, as);
@@ -1609,8 +1615,8 @@ __global__ __launch_bounds__(256) void kda_out_norm_kernel(const _Float16* __res
 // The staging halo covers conv widths up to 4.  Every gate whose log-decay is <= 0 runs here: the
 // bounded gate with -5.5 <= lb <= 0 on start-anchored sub-chunks (its factors stay finite while
 // 15 |lb| < 87), with lb < -5.5 and the softplus branch on end-anchored ones with exact diagonal
-// blocks.  W is formed and used as split bf16, so weak decay (lb near 0, or pre-activations that
-// keep the gate near 0) keeps the state within the tolerance.  A positive bound (log-decay above
+// blocks.  W keeps ~11 bits through phase B (fp16) and Ut fp32, so weak decay (lb near 0, or
+// pre-activations that keep the gate near 0) keeps the state within the tolerance.  A positive bound (log-decay above
 // 0, a growing state) takes the fp32 path.
 bool prefill_mfma_supported(int Dh, int chunk, int io, int W, float lb, int gate) {
   if (!(Dh == D && chunk == C && io == kBF16 && W >= 1 && W <= HALO + 1)) return false;
