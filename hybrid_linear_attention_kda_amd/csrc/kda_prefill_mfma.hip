@@ -89,16 +89,16 @@ constexpr int OFF_G = OFF_KB + C * PKB * 2;           // k^ -> KC = k e^(Gam_n -
 constexpr int OFF_STG = OFF_G + C * PQ * 4;           // raw q|k staging | A_kk + T (-> T split planes)
 constexpr int STG_BYTES = RROWS * PR * 2;             // 37520 >= 2 * C * PA * 4 and >= C * PQ * 4
 constexpr int OFF_TMP = OFF_STG + STG_BYTES;          // scratch while forming T [1024]
-constexpr int OFF_GN = OFF_TMP + 1024 * 4;            // Gam at the four anchors + Gam_C [5][128]
+constexpr int OFF_GN = OFF_TMP + 1024 * 4;            // log-decay of each sub-chunk's first token [4][128] (+ spare)
 constexpr int OFF_EN = OFF_GN + 5 * D * 4;            // e^(Gam_n(I)) [4][128]
 constexpr int OFF_E = OFF_EN + 4 * D * 4;             // e^(Gam_n(I) - Gam_n(J)), I > J [6][128]
 constexpr int OFF_FAC = OFF_E + 6 * D * 4;            // e^(Gam_C - Gam_n(J)) [4][128]
 constexpr int OFF_GC = OFF_FAC + 4 * D * 4;           // e^(Gam_C) [128]
 constexpr int OFF_BETA = OFF_GC + D * 4;              // [64]
-constexpr int OFF_NRM = OFF_BETA + C * 4;             // q / k normalisers [2][64]
+constexpr int OFF_NRM = OFF_BETA + C * 4;             // spare [2][64]
 constexpr int OFF_SEG = OFF_NRM + 2 * C * 4;          // cumulative-sum segment totals [4][128]
 constexpr int OFF_AQK = OFF_SEG + 4 * D * 4;           // A_qk hi | lo [64][PTB] bf16 (formed while T is)
-constexpr int OFF_GA = OFF_AQK + C * PA * 4;           // softplus branch: Gam at the sub-chunk ends [4][128]
+constexpr int OFF_GA = OFF_AQK + C * PA * 4;           // per-wave squared-norm sums, then normalisers [2][8][32]
 constexpr int LDS_A = OFF_GA + 4 * D * 4;
 static_assert(STG_BYTES >= 2 * C * PA * 4, "staging aliases");
 static_assert(D * PXT * 2 <= C * PKB * 2 && C * PA * 4 + D * PXT * 2 <= STG_BYTES, "X planes alias KR and the fp32 T");
@@ -287,6 +287,28 @@ __device__ __forceinline__ float reduce_scatter64(float (&v)[64], int lane) {
   return (b0 ? v[1] : v[0]) + dpp_xor1(b0 ? v[0] : v[1]);
 }
 
+// The same over 32 values: lane l returns the sum over the 64 lanes of v[l / 2] (lanes 2m and 2m + 1
+// hold the same sum; the last step adds the partner's copy of the one value left).
+__device__ __forceinline__ float reduce_scatter32(float (&v)[32], int lane) {
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[m]), __float_as_uint(v[m + 16]), false, false);
+    v[m] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[m]), __float_as_uint(v[m + 8]), false, false);
+    v[m] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) v[m] = (b3 ? v[m + 4] : v[m]) + dpp_ror8(b3 ? v[m] : v[m + 4]);
+#pragma unroll
+  for (int m = 0; m < 2; ++m) v[m] = (b2 ? v[m + 2] : v[m]) + swz_xor4(b2 ? v[m] : v[m + 2]);
+  const float x = (b1 ? v[1] : v[0]) + dpp_xor2(b1 ? v[0] : v[1]);
+  return x + dpp_xor1(x);
+}
+
 // Softplus branch, exact diagonal sub-chunk blocks: the values of one 16-token sub-chunk are
 // enumerated column by column, n = 0..255: for column j, A_qk(j, j), then for each row i > j
 // A_kk(i, j) and A_qk(i, j).  Column j starts at n = 32 j - j^2.
@@ -325,7 +347,7 @@ __device__ __forceinline__ float exp2f_(float x) { return __builtin_amdgcn_exp2f
 // Phase A: persistent workgroups (one per CU) loop over the tasks (chunk, head, sequence); the
 // global inputs of the next task are loaded into registers while the current one is computed.
 // ---------------------------------------------------------------------------------------------
-constexpr int NRAW = (RROWS * 32 + NT - 1) / NT;  // raw q | k row loads per lane
+constexpr int NRAW = (RROWS * 16 + NT - 1) / NT;  // raw q and k row-segment loads per lane
 constexpr int NRV = (RROWS * 16 + NT - 1) / NT;   // raw v row loads per lane
 
 struct PrepTask {
@@ -363,7 +385,7 @@ __device__ __forceinline__ PrepTask prep_task(int task, int H, int NC, const Seq
 // The global inputs of one task, as loaded: 16-byte loads only (addresses clamped into the
 // sequence and into the parameter blocks; rows outside the sequence are replaced when staged).
 struct PrepIn {
-  uint4 raw[NRAW];   // raw q | k rows c0-3 .. c0+63: lane task (row, 8-channel segment)
+  uint4 raw[NRAW][2];  // raw rows c0-3 .. c0+63: lane task (row, 8-channel segment), q then k
   uint4 rawv[NRV];   // raw v rows, the same way
   uint4 f[2];        // gate inputs of tokens c0 .. c0+63: lane task (token, 8-channel segment)
   uint4 par;         // 16 bytes of the head's parameter block (q, k, v conv taps, dt_bias)
@@ -386,10 +408,11 @@ __device__ __forceinline__ void prep_issue(const LayerArgs& a, const SeqTab& st,
   if (part == 0) {
 #pragma unroll
     for (int s = 0; s < NRAW; ++s) {
-      const int r = min((tid + s * NT) >> 5, RROWS - 1), sg = tid & 31;
+      const int r = min((tid + s * NT) >> 4, RROWS - 1), sg = tid & 15;
       const int tt = min(max(c0 - HALO + r, 0), T - 1);
-      const long long ch = sg < 16 ? (long long)h * D + sg * 8 : (long long)HD + h * D + (sg - 16) * 8;
-      in.raw[s] = *reinterpret_cast<const uint4*>(qkv + (long long)tt * Cq + ch);
+      const bf16_t* row = qkv + (long long)tt * Cq + h * D + sg * 8;
+      in.raw[s][0] = *reinterpret_cast<const uint4*>(row);
+      in.raw[s][1] = *reinterpret_cast<const uint4*>(row + HD);
     }
   } else if (part == 1) {
 #pragma unroll
@@ -446,15 +469,12 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
   _Float16* sA16 = reinterpret_cast<_Float16*>(smem + OFF_AQK);  // A_qk [64][PTB] fp16
   _Float16* sT16 = reinterpret_cast<_Float16*>(smem + OFF_STG);  // T [64][PTB] fp16, in place of A_kk
   float* sTmp = reinterpret_cast<float*>(smem + OFF_TMP);
-  float* sGn = reinterpret_cast<float*>(smem + OFF_GN);
   float* sEn = reinterpret_cast<float*>(smem + OFF_EN);
   float* sE = reinterpret_cast<float*>(smem + OFF_E);
   float* sFac = reinterpret_cast<float*>(smem + OFF_FAC);
   float* sGC = reinterpret_cast<float*>(smem + OFF_GC);
   float* sBeta = reinterpret_cast<float*>(smem + OFF_BETA);
-  float* sNrm = reinterpret_cast<float*>(smem + OFF_NRM);
   float* sSeg = reinterpret_cast<float*>(smem + OFF_SEG);
-  float* sGa = reinterpret_cast<float*>(smem + OFF_GA);
 
   const int H = a.H, W = a.W;
   const int NC = (a.T + C - 1) / C;  // chunks per sequence of a uniform launch
@@ -486,18 +506,35 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     unsigned char* __restrict__ blk =
         ws + ((long long)sv.chunk0 * H + (long long)h * ((T + C - 1) / C) + ci) * (long long)CH_BYTES;
 
-    // ---- P1: stage this task's raw q | k rows for tokens c0-3 .. c0+63, its gate inputs and
+    // ---- P1: stage this task's raw q | k rows for tokens c0-3 .. c0+63 with q and k of each
+    //      channel side by side (one 32-bit word per channel: q low, k high), its gate inputs and
     //      its head's parameter block (bf16) from the registers loaded during the previous task ----
     __bf16* sF = reinterpret_cast<__bf16*>(smem + OFF_AQK);  // f [64][PKB] until A_qk is formed
     unsigned char* sPar = smem + OFF_TMP;                    // parameter block until T is formed
+    float* sFirst = reinterpret_cast<float*>(smem + OFF_GN);  // log-decay of each sub-chunk's first token [4][128]
+    float* sPart = reinterpret_cast<float*>(smem + OFF_GA);   // per-wave squared-norm sums [8][32], then normalisers [8][32]
     const float alog = cur.alog;
+    // 8 q and 8 k values of one row as 8 (q, k) words
+    auto stage_pairs = [&](__bf16* dst, uint4 q, uint4 k) __attribute__((always_inline)) {
+      const uint32_t qw[4] = {q.x, q.y, q.z, q.w}, kw[4] = {k.x, k.y, k.z, k.w};
+      uint32_t o[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = __builtin_amdgcn_perm(kw[e], qw[e], 0x05040100u);
+        o[2 * e + 1] = __builtin_amdgcn_perm(kw[e], qw[e], 0x07060302u);
+      }
+      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+    };
 #pragma unroll
     for (int s = 0; s < NRAW; ++s) {
       const int idx = tid + s * NT;
-      if (idx < RROWS * 32) {
-        const int r = idx >> 5, sg = idx & 31;
+      if (idx < RROWS * 16) {
+        const int r = idx >> 4, sg = idx & 15;
         const int tt = c0 - HALO + r;
-        *reinterpret_cast<uint4*>(sRaw + r * PR + sg * 8) = (tt >= 0 && tt < T) ? cur.raw[s] : make_uint4(0u, 0u, 0u, 0u);
+        const bool in_seq = tt >= 0 && tt < T;
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        stage_pairs(sRaw + r * PR + sg * 16, in_seq ? cur.raw[s][0] : z, in_seq ? cur.raw[s][1] : z);
       }
     }
 #pragma unroll
@@ -506,35 +543,43 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       *reinterpret_cast<uint4*>(sF + t * PKB + sg * 8) = cur.f[s];
     }
     if (tid < par_segments(W)) reinterpret_cast<uint4*>(sPar)[tid] = cur.par;
-    if (ci == 0 && tid < HALO * 32) {
+    if (ci == 0 && tid < HALO * 16) {
       // rows before the sequence start come from the conv state (the same lane wrote them as zeros)
-      const int r = tid >> 5, sg = tid & 31;
+      const int r = tid >> 4, sg = tid & 15;
       const int tt = r - HALO;
       if ((W - 1) + tt >= 0) {
-        const long long ch = sg < 16 ? (long long)h * D + sg * 8 : (long long)HD + h * D + (sg - 16) * 8;
-        uint16_t e8[8];
+        const long long ch = (long long)h * D + sg * 8;
+        uint16_t eq[8], ek[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) e8[e] = cin[(ch + e) * (W - 1) + (W - 1) + tt];
-        *reinterpret_cast<uint4*>(sRaw + r * PR + sg * 8) =
-            make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16, e8[4] | (uint32_t)e8[5] << 16,
-                       e8[6] | (uint32_t)e8[7] << 16);
+        for (int e = 0; e < 8; ++e) {
+          eq[e] = cin[(ch + e) * (W - 1) + (W - 1) + tt];
+          ek[e] = cin[(HD + ch + e) * (W - 1) + (W - 1) + tt];
+        }
+        stage_pairs(sRaw + r * PR + sg * 16,
+                    make_uint4(eq[0] | (uint32_t)eq[1] << 16, eq[2] | (uint32_t)eq[3] << 16,
+                               eq[4] | (uint32_t)eq[5] << 16, eq[6] | (uint32_t)eq[7] << 16),
+                    make_uint4(ek[0] | (uint32_t)ek[1] << 16, ek[2] | (uint32_t)ek[3] << 16,
+                               ek[4] | (uint32_t)ek[5] << 16, ek[6] | (uint32_t)ek[7] << 16));
       }
     }
     if (tid < C) sBeta[tid] = tid < L ? to_f32(cur.beta) : 0.f;
     __syncthreads();
-    // conv taps of this lane's two q|k channels 2 (tid % 128) and 2 (tid % 128) + 1 and of the v
-    // channel it converts in P9 (16 * wave + lane % 16), zero-padded on the left to 4 taps; read
-    // before T reuses the block; taps as bf16 pairs (tap of the older token first): {t0, t1}, {t2, t3}
+
+    // From here to the A_kk blocks a lane owns key channel c = tid % 128 of q and k and the 16
+    // tokens of segment seg = tid / 128 (sub-chunk seg), which is also the channel of the gate.
+    const int c = tid & 127, seg = tid >> 7;
+    // conv taps of this lane's q and k channels and of the v channel it converts in P9
+    // (16 * wave + lane % 16), zero-padded on the left to 4 taps; read before T reuses the block;
+    // taps as bf16 pairs (tap of the older token first): {t0, t1}, {t2, t3}
     bf16x2 ta01, ta23, tb01, tb23, tv01, tv23;
     {
-      const __bf16* taps = reinterpret_cast<const __bf16*>(sPar);
-      const int ca = 2 * (tid & 127);  // q channels then k channels: the block rows in that order
+      const __bf16* taps = reinterpret_cast<const __bf16*>(sPar);  // rows: q channels, k channels, v channels
       __bf16 ta[4], tb[4], tv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int w = max(j - (4 - W), 0);
-        ta[j] = j >= 4 - W ? taps[ca * W + w] : (__bf16)0.f;
-        tb[j] = j >= 4 - W ? taps[(ca + 1) * W + w] : (__bf16)0.f;
+        ta[j] = j >= 4 - W ? taps[c * W + w] : (__bf16)0.f;
+        tb[j] = j >= 4 - W ? taps[(D + c) * W + w] : (__bf16)0.f;
         tv[j] = j >= 4 - W ? taps[(2 * D + 16 * wave + l16) * W + w] : (__bf16)0.f;
       }
       ta01 = bf16x2{ta[0], ta[1]};
@@ -546,17 +591,17 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     }
     const float* sDtb = reinterpret_cast<const float*>(sPar + 3 * D * W * 2);
 
-    // ---- P2: causal conv + SiLU over q|k: lane -> channels 2 (tid % 128) + {0, 1}, 16 tokens.
-    //      Tokens past the sequence's end are not masked: beta is 0 there, so their rows of W and
-    //      Ut, and with them their share of the state update, are exactly 0, and their outputs are
-    //      not stored ----
+    // ---- P2: causal conv + SiLU of q and k of channel c over the segment's 16 tokens, kept in
+    //      registers.  Tokens past the sequence's end are not masked: beta is 0 there, so their
+    //      rows of W and Ut, and with them their share of the state update, are exactly 0, and
+    //      their outputs are not stored ----
+    float qx[16], kx[16];
     {
-      const int tb = 16 * (tid >> 7), ca = 2 * (tid & 127);
-      const uint32_t* col = reinterpret_cast<const uint32_t*>(sRaw + ca);  // both channels of a row
-      float* dst = ca < D ? sQ + ca : sG + (ca - D);
-      // the lane's 19 raw rows (one 32-bit word: channel ca low, ca + 1 high) are read before any
-      // arithmetic, then regrouped per channel as pairs pe[m] = (row 2m, row 2m+1) and, between
-      // them, po[m] = (row 2m+1, row 2m+2); output row i takes pairs i and i+2
+      const int tb = 16 * seg;
+      const uint32_t* col = reinterpret_cast<const uint32_t*>(sRaw + 2 * c);  // (q, k) of a row
+      // the lane's 19 raw rows are read before any arithmetic, then regrouped per channel as
+      // pairs pe[m] = (row 2m, row 2m+1) and, between them, po[m] = (row 2m+1, row 2m+2); output
+      // row i takes pairs i and i+2
       uint32_t w[20];
 #pragma unroll
       for (int r = 0; r < 19; ++r) w[r] = col[(tb + r) * (PR / 2)];
@@ -579,32 +624,24 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
                                  : dot2(ta23, pa[m + 1], dot2(ta01, pa[m], 0.f));
         const float yb = (i & 1) ? dot2(tb23, qb[m + 1], dot2(tb01, qb[m], 0.f))
                                  : dot2(tb23, pb[m + 1], dot2(tb01, pb[m], 0.f));
-        *reinterpret_cast<float2*>(dst + (tb + i) * PQ) = make_float2(silu_fast(ya), silu_fast(yb));
+        qx[i] = silu_fast(ya);
+        kx[i] = silu_fast(yb);
       }
     }
-    __syncthreads();
 
-    // the next task's inputs (the last task loads its own again: the loads stay unconditional),
-    // issued in three groups spread over this task
-    const PrepTask knext = prep_task<VL>(min(tk + (int)gridDim.x, ntask - 1), H, NC, st);
-    PrepIn nxt;
-    prep_issue<VL>(a, st, knext, tid, nxt, 0);
-
-    // ---- P3: bounded-sigmoid gate and its cumulative sum (lane -> channel, 16-token segment);
-    //      gl[k] = Gam(16 seg + k) - Gam(16 seg - 1) stays in registers for P5.  From here on every
-    //      log-decay is held in base-2 units (Gam log2 e), so each decay factor is one v_exp_f32 ----
+    // ---- P3: bounded-sigmoid gate of channel c and its cumulative sum over the segment;
+    //      gl[k] = Gam(16 seg + k) - Gam(16 seg - 1).  From here on every log-decay is held in
+    //      base-2 units (Gam log2 e), so each decay factor is one v_exp_f32 ----
     float gl[16];
     float graw[16];  // softplus branch: this token's own log-decay, for the exact diagonal blocks
-    float gn0;       // Gam at this lane's segment anchor (base-2 units)
     {
-      const int i = tid & 127, seg = tid >> 7;
       const float Ah = __expf(alog);
-      const float dtb = sDtb[i];
+      const float dtb = sDtb[c];
       const float Ah2 = Ah * kLog2e, lb2 = a.lb * kLog2e;
       float acc = 0.f;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        const float fv = (float)sF[(16 * seg + k) * PKB + i] + dtb;
+        const float fv = (float)sF[(16 * seg + k) * PKB + c] + dtb;
         // bounded sigmoid or softplus; under the end-anchored factoring floored at -100 (a decay
         // below e^-100 is zero at fp32 precision either way), which keeps the 16-token sums of the
         // log-decay well scaled
@@ -617,85 +654,83 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
         gl[k] = acc;
         graw[k] = gv;
       }
-      sSeg[seg * D + i] = acc;
-      // ---- P4 (same phase): q / k L2 normalisers: eight lanes per token, 16 channels each ----
-      {
-        const int t = tid >> 3, p = tid & 7;
-        const float4* qp = reinterpret_cast<const float4*>(sQ + t * PQ + 16 * p);
-        const float4* kp = reinterpret_cast<const float4*>(sG + t * PQ + 16 * p);
-        float qq = 0.f, kk = 0.f;
+      sSeg[seg * D + c] = acc;
+      sFirst[seg * D + c] = gl[0];
+    }
+    // ---- P4 (same phase): squared norms of q and k per token, summed over this wave's 64
+    //      channels (value m of the reduce-scatter: q of token m, k of token m - 16); lanes 2m and
+    //      2m + 1 end with the sum m ----
+    {
+      float v[32];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float4 x = qp[e], y = kp[e];
-          qq += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
-          kk += y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
-        }
-#pragma unroll
-        for (int o = 4; o > 0; o >>= 1) {
-          qq += __shfl_xor(qq, o, 64);
-          kk += __shfl_xor(kk, o, 64);
-        }
-        if (p == 0) {
-          // 1 / max(||x||, eps) = min(1 / ||x||, 1 / eps) (rsq(0) is +inf)
-          const float inv_eps = 1.0f / a.l2_eps;
-          sNrm[t] = a.scale * fminf(__builtin_amdgcn_rsqf(qq), inv_eps);
-          sNrm[C + t] = fminf(__builtin_amdgcn_rsqf(kk), inv_eps);
-        }
+      for (int k = 0; k < 16; ++k) {
+        v[k] = qx[k] * qx[k];
+        v[16 + k] = kx[k] * kx[k];
       }
-      __syncthreads();
-      float off = 0.f;
-      for (int s = 0; s < seg; ++s) off += sSeg[s * D + i];
-      gn0 = gl[0] + off;
-      sGn[seg * D + i] = gn0;
-      if (seg == 3) sGn[4 * D + i] = gl[15] + off;
-      if (SP) sGa[seg * D + i] = gl[15] + off;
+      const float tot = reduce_scatter32(v, lane);
+      if ((lane & 1) == 0) sPart[wave * 32 + (lane >> 1)] = tot;
     }
     __syncthreads();
 
-    prep_issue<VL>(a, st, knext, tid, nxt, 1);
+    // the next task's inputs (the last task loads its own again: the loads stay unconditional),
+    // issued in three groups spread over this task
+    const PrepTask knext = prep_task<VL>(min(tk + (int)gridDim.x, ntask - 1), H, NC, st);
+    PrepIn nxt;
+    prep_issue<VL>(a, st, knext, tid, nxt, 0);
 
-    // ---- P5: anchored operands QR, KR (bf16), KC (lane -> channel, 16-token segment, as in P3:
-    //      Gam_t - Gam_n(I) = gl[k] - gl[0]) and the per-channel factor tables ----
+    // ---- P5: the segment offsets of the cumulative log-decay and the L2 normalisers, then the
+    //      anchored operands QR, KR (bf16), KC (Gam_t - Gam_n(I) = gl[k] - gl[0]) and this
+    //      lane's row of the per-channel factor tables ----
     float dpart[4];  // softplus branch: this lane's share of its wave's diagonal-block sums
     // X = beta K e^Gam (Gam from the chunk start) of this lane's channel and 16 tokens, in fp32: the
     // right-hand side of W = T X, kept in registers until T is formed
     float xk[16];
     {
-      const int i = tid & 127, seg = tid >> 7;
+      // Gam at each sub-chunk's first token (gn), at its last token (ga) and at the chunk end
+      float off = 0.f, gn[4], ga[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        const float segt = sSeg[J * D + c];
+        gn[J] = sFirst[J * D + c] + off;
+        ga[J] = segt + off;
+        off += segt;
+      }
+      const float GC = ga[3];
+      const float gn0 = gn[seg];
       const float egn = exp2f_(gn0);
-      float* qp = sQ + 16 * seg * PQ + i;
-      float* kp = sG + 16 * seg * PQ + i;
-      __bf16* rp = sKb + 16 * seg * PKB + i;
-      const float* nq = sNrm + 16 * seg;
-      const float* nk = sNrm + C + 16 * seg;
-      if (!SP) {
-        // the segment's normalisers and betas are the same for every lane of the wave: 16-byte
-        // broadcast reads
-        float nqv[16], nkv[16], bev[16];
+      // 1 / max(||x||, eps) = min(1 / ||x||, 1 / eps) (rsq(0) is +inf): the two waves of the
+      // segment hold channels 0-63 and 64-127; lanes 2m and 2m + 1 form normaliser m (q of token
+      // m, k of token m - 16) into this wave's own slot, which every lane then reads with 16-byte
+      // broadcast reads
+      float nqv[16], nkv[16], bev[16];
+      {
+        const int m = lane >> 1;
+        const float ss = sPart[(2 * seg) * 32 + m] + sPart[(2 * seg + 1) * 32 + m];
+        const float nrm = fminf(__builtin_amdgcn_rsqf(ss), 1.0f / a.l2_eps) * (m < 16 ? a.scale : 1.0f);
+        float* mine = sPart + 256 + wave * 32;
+        if ((lane & 1) == 0) mine[m] = nrm;
+        wave_lds_sync();
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float4 a4 = reinterpret_cast<const float4*>(nq)[g];
-          const float4 b4 = reinterpret_cast<const float4*>(nk)[g];
-          const float4 c4 = reinterpret_cast<const float4*>(sBeta + 16 * seg)[g];
-          nqv[4 * g] = a4.x; nqv[4 * g + 1] = a4.y; nqv[4 * g + 2] = a4.z; nqv[4 * g + 3] = a4.w;
-          nkv[4 * g] = b4.x; nkv[4 * g + 1] = b4.y; nkv[4 * g + 2] = b4.z; nkv[4 * g + 3] = b4.w;
-          bev[4 * g] = c4.x; bev[4 * g + 1] = c4.y; bev[4 * g + 2] = c4.z; bev[4 * g + 3] = c4.w;
+          const float4 q4 = reinterpret_cast<const float4*>(mine)[g];
+          const float4 k4 = reinterpret_cast<const float4*>(mine)[4 + g];
+          const float4 b4 = reinterpret_cast<const float4*>(sBeta + 16 * seg)[g];
+          nqv[4 * g] = q4.x; nqv[4 * g + 1] = q4.y; nqv[4 * g + 2] = q4.z; nqv[4 * g + 3] = q4.w;
+          nkv[4 * g] = k4.x; nkv[4 * g + 1] = k4.y; nkv[4 * g + 2] = k4.z; nkv[4 * g + 3] = k4.w;
+          bev[4 * g] = b4.x; bev[4 * g + 1] = b4.y; bev[4 * g + 2] = b4.z; bev[4 * g + 3] = b4.w;
         }
-        // every read of the lane's column comes before its first write: the compiler cannot tell
-        // the writes from the later reads, and would otherwise wait out each round trip in turn
-        float qr[16], kr[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          qr[k] = qp[k * PQ];
-          kr[k] = kp[k * PQ];
-        }
+      }
+      float* qp = sQ + 16 * seg * PQ + c;
+      float* kp = sG + 16 * seg * PQ + c;
+      __bf16* rp = sKb + 16 * seg * PKB + c;
+      if (!SP) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
           const float d = gl[k] - gl[0];
           const float e1 = exp2f_(d);   // <= 1
           const float e2 = exp2f_(-d);  // in [1, e^(15|lb|)]
-          const float q = qr[k] * nqv[k];
-          const float kv = kr[k] * nkv[k];
+          const float q = qx[k] * nqv[k];
+          const float kv = kx[k] * nkv[k];
           qp[k * PQ] = q * e1;
           rp[k * PKB] = (__bf16)(kv * e1);
           kp[k * PQ] = kv * e2;
@@ -705,8 +740,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
         float qn[16], kn[16], al[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          qn[k] = qp[k * PQ] * nq[k];
-          kn[k] = kp[k * PQ] * nk[k];
+          qn[k] = qx[k] * nqv[k];
+          kn[k] = kx[k] * nkv[k];
         }
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
@@ -715,7 +750,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
           qp[k * PQ] = qn[k] * e1;
           rp[k * PKB] = (__bf16)(kn[k] * e1);
           kp[k * PQ] = kn[k] * e2;
-          xk[k] = sBeta[16 * seg + k] * (kn[k] * e1) * egn;
+          xk[k] = bev[k] * (kn[k] * e1) * egn;
           al[k] = exp2f_(graw[k]);  // this token's decay
         }
         // the diagonal block entries of this channel (enumerated as in diag_entry), 64 at a time,
@@ -747,21 +782,20 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
           for (int b = 0; b < 4; ++b) sTmp[seg * 256 + 64 * b + lane] = dpart[b];
         }
       }
-    }
-    // factor tables: lane -> channel c, sub-chunk I = tid / 128 (the rows of I spread over all waves)
-    {
-      const int c = tid & 127, I = tid >> 7;
-      const float GC = sGn[4 * D + c];
-      const float GI = sGn[I * D + c];
+      // factor tables, row I = seg of channel c
+      const int I = seg;
+      const float GI = gn0;
       sEn[I * D + c] = exp2f_(GI);
       // column anchors: the sub-chunk's first token, or its last one for the softplus branch
-      sFac[I * D + c] = exp2f_(GC - (SP ? sGa[I * D + c] : GI));
+      sFac[I * D + c] = exp2f_(GC - (SP ? ga[I] : GI));
 #pragma unroll
       for (int J = 0; J < 3; ++J)
-        if (J < I) sE[pair_index(I, J) * D + c] = exp2f_(GI - (SP ? sGa[J * D + c] : sGn[J * D + c]));
+        if (J < I) sE[pair_index(I, J) * D + c] = exp2f_(GI - (SP ? ga[J] : gn[J]));
       if (I == 0) sGC[c] = exp2f_(GC);
     }
     __syncthreads();
+
+    prep_issue<VL>(a, st, knext, tid, nxt, 1);
 
     // ---- P6a: A_kk = beta_i * KR_I E_IJ . KC_J^T (plain bf16), strictly lower: one 16 x 16 block.
     //      The diagonal blocks and four below them here, one per wave; blocks (3,1) and (3,2),
