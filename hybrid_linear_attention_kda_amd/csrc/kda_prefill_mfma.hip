@@ -77,7 +77,7 @@ constexpr int HALO = 3;      // staged rows before the chunk (conv width <= 4)
 constexpr int PQ = 132;      // fp32 pitch of [64][128] arrays
 constexpr int PKB = 136;     // bf16 pitch of [64][128] arrays
 constexpr int PA = 68;       // fp32 pitch of [64][64] arrays
-constexpr int PTB = 68;      // bf16 pitch of the [64][64] split planes (8-byte aligned rows)
+constexpr int PTB = 72;      // fp16 pitch of the [64][64] T and A_qk planes (row r starts 36 r banks on)
 constexpr int PXT = 68;      // bf16 pitch of the transposed [128][64] X planes (8-byte aligned rows)
 constexpr int PR = 280;      // bf16 pitch of the raw staging rows: q 128 | k 128 | v 16 | pad
 constexpr int RROWS = C + HALO;
@@ -97,10 +97,11 @@ constexpr int OFF_GC = OFF_FAC + 4 * D * 4;           // e^(Gam_C) [128]
 constexpr int OFF_BETA = OFF_GC + D * 4;              // [64]
 constexpr int OFF_NRM = OFF_BETA + C * 4;             // spare [2][64]
 constexpr int OFF_SEG = OFF_NRM + 2 * C * 4;          // cumulative-sum segment totals [4][128]
-constexpr int OFF_AQK = OFF_SEG + 4 * D * 4;           // A_qk hi | lo [64][PTB] bf16 (formed while T is)
+constexpr int OFF_AQK = OFF_SEG + 4 * D * 4;           // f [64][PKB] bf16 -> A_qk [64][PTB] fp16 (formed while T is)
 constexpr int OFF_GA = OFF_AQK + C * PA * 4;           // per-wave squared-norm sums, then normalisers [2][8][32]
 constexpr int LDS_A = OFF_GA + 4 * D * 4;
 static_assert(STG_BYTES >= 2 * C * PA * 4, "staging aliases");
+static_assert(C * PTB * 2 <= C * PA * 4, "the fp16 T and A_qk planes fit their regions");
 static_assert(D * PXT * 2 <= C * PKB * 2 && C * PA * 4 + D * PXT * 2 <= STG_BYTES, "X planes alias KR and the fp32 T");
 static_assert(LDS_A <= 160 * 1024, "LDS budget");
 
