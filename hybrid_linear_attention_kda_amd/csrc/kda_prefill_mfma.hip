@@ -157,6 +157,13 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float dot2(bf16x2 a, bf16x2 b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
 }
+// a.x * b.x + a.y * b.y with the zero addend as an inline constant (the accumulating form would
+// first have to move a zero into its destination)
+__device__ __forceinline__ float dot2z(bf16x2 a, bf16x2 b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 // (x.y, y.x): the pair between two consecutive pairs of a column
 __device__ __forceinline__ bf16x2 mid_pair(bf16x2 x, bf16x2 y) {
   return __builtin_bit_cast(bf16x2, __builtin_amdgcn_alignbit(__builtin_bit_cast(uint32_t, y),
@@ -621,10 +628,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int m = i >> 1;
-        const float ya = (i & 1) ? dot2(ta23, qa[m + 1], dot2(ta01, qa[m], 0.f))
-                                 : dot2(ta23, pa[m + 1], dot2(ta01, pa[m], 0.f));
-        const float yb = (i & 1) ? dot2(tb23, qb[m + 1], dot2(tb01, qb[m], 0.f))
-                                 : dot2(tb23, pb[m + 1], dot2(tb01, pb[m], 0.f));
+        const float ya = (i & 1) ? dot2(ta23, qa[m + 1], dot2z(ta01, qa[m])) : dot2(ta23, pa[m + 1], dot2z(ta01, pa[m]));
+        const float yb = (i & 1) ? dot2(tb23, qb[m + 1], dot2z(tb01, qb[m])) : dot2(tb23, pb[m + 1], dot2z(tb01, pb[m]));
         qx[i] = silu_fast(ya);
         kx[i] = silu_fast(yb);
       }
@@ -640,21 +645,28 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       const float dtb = sDtb[c];
       const float Ah2 = Ah * kLog2e, lb2 = a.lb * kLog2e;
       float acc = 0.f;
+      // tokens past the sequence's end (a partial last chunk only) take no decay
+      auto gate = [&](bool full) __attribute__((always_inline)) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float fv = (float)sF[(16 * seg + k) * PKB + c] + dtb;
-        // bounded sigmoid or softplus; under the end-anchored factoring floored at -100 (a decay
-        // below e^-100 is zero at fp32 precision either way), which keeps the 16-token sums of the
-        // log-decay well scaled
-        const float gb = lb2 * __builtin_amdgcn_rcpf(1.0f + __expf(-Ah * fv));
-        const float g = GK == 1 ? fmaxf(-Ah2 * (fmaxf(fv, 0.f) + __logf(1.0f + __expf(-fabsf(fv)))), -100.f * kLog2e)
-                      : GK == 2 ? fmaxf(gb, -100.f * kLog2e)
-                                : gb;
-        const float gv = (L == C || 16 * seg + k < L) ? g : 0.f;
-        acc += gv;
-        gl[k] = acc;
-        graw[k] = gv;
-      }
+        for (int k = 0; k < 16; ++k) {
+          const float fv = (float)sF[(16 * seg + k) * PKB + c] + dtb;
+          // bounded sigmoid or softplus; under the end-anchored factoring floored at -100 (a decay
+          // below e^-100 is zero at fp32 precision either way), which keeps the 16-token sums of
+          // the log-decay well scaled
+          const float gb = lb2 * __builtin_amdgcn_rcpf(1.0f + __expf(-Ah * fv));
+          const float g = GK == 1 ? fmaxf(-Ah2 * (fmaxf(fv, 0.f) + __logf(1.0f + __expf(-fabsf(fv)))), -100.f * kLog2e)
+                        : GK == 2 ? fmaxf(gb, -100.f * kLog2e)
+                                  : gb;
+          const float gv = (full || 16 * seg + k < L) ? g : 0.f;
+          acc += gv;
+          gl[k] = acc;
+          graw[k] = gv;
+        }
+      };
+      if (L == C)
+        gate(true);
+      else
+        gate(false);
       sSeg[seg * D + c] = acc;
       sFirst[seg * D + c] = gl[0];
     }
@@ -1129,8 +1141,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int m = e >> 1;
-          const float y = (e & 1) ? dot2(tv23, po[m + 1], dot2(tv01, po[m], 0.f))
-                                  : dot2(tv23, pe[m + 1], dot2(tv01, pe[m], 0.f));
+          const float y = (e & 1) ? dot2(tv23, po[m + 1], dot2z(tv01, po[m])) : dot2(tv23, pe[m + 1], dot2z(tv01, pe[m]));
           xv[e] = sBeta[tb + e] * silu_fast(y);
         }
         bv[st] = split16(xv);
