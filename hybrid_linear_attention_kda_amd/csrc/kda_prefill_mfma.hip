@@ -644,16 +644,19 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       const float Ah = __expf(alog);
       const float dtb = sDtb[c];
       const float Ah2 = Ah * kLog2e, lb2 = a.lb * kLog2e;
+      // the sigmoid's exponent -A (f + dt_bias) in base 2 as one fma of the raw f
+      const float k1 = -Ah2, k2 = k1 * dtb;
       float acc = 0.f;
       // tokens past the sequence's end (a partial last chunk only) take no decay
       auto gate = [&](bool full) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          const float fv = (float)sF[(16 * seg + k) * PKB + c] + dtb;
+          const float fr = (float)sF[(16 * seg + k) * PKB + c];
+          const float fv = fr + dtb;
           // bounded sigmoid or softplus; under the end-anchored factoring floored at -100 (a decay
           // below e^-100 is zero at fp32 precision either way), which keeps the 16-token sums of
           // the log-decay well scaled
-          const float gb = lb2 * __builtin_amdgcn_rcpf(1.0f + __expf(-Ah * fv));
+          const float gb = lb2 * __builtin_amdgcn_rcpf(1.0f + exp2f_(fmaf(fr, k1, k2)));
           const float g = GK == 1 ? fmaxf(-Ah2 * (fmaxf(fv, 0.f) + __logf(1.0f + __expf(-fabsf(fv)))), -100.f * kLog2e)
                         : GK == 2 ? fmaxf(gb, -100.f * kLog2e)
                                   : gb;
