@@ -85,14 +85,14 @@ constexpr int RROWS = C + HALO;
 // Phase A LDS layout (bytes)
 constexpr int OFF_Q = 0;                              // q^ -> QR = q e^(Gam - Gam_n) -> P
 constexpr int OFF_KB = OFF_Q + C * PQ * 4;            // KR (bf16) -> W (bf16)
-constexpr int OFF_G = OFF_KB + C * PKB * 2;           // k^ -> KC = k e^(Gam_n - Gam) -> raw v rows
-constexpr int OFF_STG = OFF_G + C * PQ * 4;           // raw q|k staging | A_kk + T (-> T split planes)
+constexpr int OFF_G = OFF_KB + C * PKB * 2;           // KC = k e^(Gam_n - Gam) as bf16 hi | lo [2][64][PKB] -> raw v rows
+constexpr int OFF_STG = OFF_G + 2 * C * PKB * 2;      // raw q|k staging | A_kk + T (-> T split planes)
 constexpr int STG_BYTES = RROWS * PR * 2;             // 37520 >= 2 * C * PA * 4 and >= C * PQ * 4
 constexpr int OFF_TMP = OFF_STG + STG_BYTES;          // scratch while forming T [1024]
 constexpr int OFF_GN = OFF_TMP + 1024 * 4;            // log-decay of each sub-chunk's first token [4][128] (+ spare)
 constexpr int OFF_EN = OFF_GN + 5 * D * 4;            // e^(Gam_n(I)) [4][128]
 constexpr int OFF_E = OFF_EN + 4 * D * 4;             // e^(Gam_n(I) - Gam_n(J)), I > J [6][128]
-constexpr int OFF_FAC = OFF_E + 6 * D * 4;            // e^(Gam_C - Gam_n(J)) [4][128]
+constexpr int OFF_FAC = OFF_E + 6 * D * 4;            // spare [4][128]
 constexpr int OFF_GC = OFF_FAC + 4 * D * 4;           // e^(Gam_C) [128]
 constexpr int OFF_BETA = OFF_GC + D * 4;              // [64]
 constexpr int OFF_NRM = OFF_BETA + C * 4;             // spare [2][64]
@@ -470,7 +470,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
   extern __shared__ __align__(16) unsigned char smem[];
   float* sQ = reinterpret_cast<float*>(smem + OFF_Q);
   __bf16* sKb = reinterpret_cast<__bf16*>(smem + OFF_KB);
-  float* sG = reinterpret_cast<float*>(smem + OFF_G);
+  __bf16* sKChi = reinterpret_cast<__bf16*>(smem + OFF_G);  // KC split planes [64][PKB]
+  __bf16* sKClo = sKChi + C * PKB;
   __bf16* sRaw = reinterpret_cast<__bf16*>(smem + OFF_STG);
   float* sAkk = reinterpret_cast<float*>(smem + OFF_STG);
   float* sT = reinterpret_cast<float*>(smem + OFF_STG + C * PA * 4);
@@ -479,7 +480,6 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
   float* sTmp = reinterpret_cast<float*>(smem + OFF_TMP);
   float* sEn = reinterpret_cast<float*>(smem + OFF_EN);
   float* sE = reinterpret_cast<float*>(smem + OFF_E);
-  float* sFac = reinterpret_cast<float*>(smem + OFF_FAC);
   float* sGC = reinterpret_cast<float*>(smem + OFF_GC);
   float* sBeta = reinterpret_cast<float*>(smem + OFF_BETA);
   float* sSeg = reinterpret_cast<float*>(smem + OFF_SEG);
@@ -737,8 +737,20 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
         }
       }
       float* qp = sQ + 16 * seg * PQ + c;
-      float* kp = sG + 16 * seg * PQ + c;
+      __bf16* khp = sKChi + 16 * seg * PKB + c;
+      __bf16* klp = sKClo + 16 * seg * PKB + c;
       __bf16* rp = sKb + 16 * seg * PKB + c;
+      // KC = K e^(Gam_n - Gam) goes to LDS split into bf16 hi + lo (the column operand of A_kk and
+      // A_qk), and K~ = KC e^(Gam_C - Gam_n) straight to the workspace: K~^T [128][64] in fragment
+      // order, this lane's 16 tokens as two 8-token pieces
+      const float fac = exp2f_(GC - (SP ? ga[seg] : gn0));
+      float kt[16];
+      auto put_kc = [&](int k, float kcv) __attribute__((always_inline)) {
+        const __bf16 kh = (__bf16)kcv;
+        khp[k * PKB] = kh;
+        klp[k * PKB] = (__bf16)(kcv - (float)kh);
+        kt[k] = kcv * fac;
+      };
       if (!SP) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
@@ -749,7 +761,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
           const float kv = kx[k] * nkv[k];
           qp[k * PQ] = q * e1;
           rp[k * PKB] = (__bf16)(kv * e1);
-          kp[k * PQ] = kv * e2;
+          put_kc(k, kv * e2);
           xk[k] = bev[k] * (kv * e1) * egn;
         }
       } else {
@@ -765,7 +777,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
           const float e2 = exp2f_(gl[15] - gl[k]);  // <= 1: key columns anchored at the sub-chunk's end
           qp[k * PQ] = qn[k] * e1;
           rp[k * PKB] = (__bf16)(kn[k] * e1);
-          kp[k * PQ] = kn[k] * e2;
+          put_kc(k, kn[k] * e2);
           xk[k] = bev[k] * (kn[k] * e1) * egn;
           al[k] = exp2f_(graw[k]);  // this token's decay
         }
@@ -798,12 +810,22 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
           for (int b = 0; b < 4; ++b) sTmp[seg * 256 + 64 * b + lane] = dpart[b];
         }
       }
-      // factor tables, row I = seg of channel c
+      {
+        _Float16* kthi = reinterpret_cast<_Float16*>(blk + W_KTHI);
+        float a8[8], b8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          a8[e] = kt[e];
+          b8[e] = kt[8 + e];
+        }
+        *reinterpret_cast<f16x8*>(kthi + frag_offset(c, 16 * seg, C)) = to_f16x8(a8);
+        *reinterpret_cast<f16x8*>(kthi + frag_offset(c, 16 * seg + 8, C)) = to_f16x8(b8);
+      }
+      // factor tables, row I = seg of channel c; column anchors: the sub-chunk's first token, or
+      // its last one for the softplus branch
       const int I = seg;
       const float GI = gn0;
       sEn[I * D + c] = exp2f_(GI);
-      // column anchors: the sub-chunk's first token, or its last one for the softplus branch
-      sFac[I * D + c] = exp2f_(GC - (SP ? ga[I] : GI));
 #pragma unroll
       for (int J = 0; J < 3; ++J)
         if (J < I) sE[pair_index(I, J) * D + c] = exp2f_(GI - (SP ? ga[J] : gn[J]));
@@ -830,9 +852,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 #pragma unroll
           for (int e = 0; e < 8; ++e) av[e] = (__bf16)((float)av[e] * ef[e]);
         }
-        float kc[8];
-        ld8(sG + (16 * J + l16) * PQ + c, kc);
-        acc = mfma(av, round8(kc), acc);
+        acc = mfma(av, *reinterpret_cast<const bf16x8*>(sKChi + (16 * J + l16) * PKB + c), acc);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -877,15 +897,15 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int c = 32 * s + 8 * lg;
-        float qv[8], kc[8];
+        float qv[8];
         ld8(sQ + (16 * I + l16) * PQ + c, qv);
         if (I > J) {
           const float* ef = sE + pair_index(I, J) * D + c;
 #pragma unroll
           for (int e = 0; e < 8; ++e) qv[e] *= ef[e];
         }
-        ld8(sG + (16 * J + l16) * PQ + c, kc);
-        acc = mfma3(split(qv), split(kc), acc);
+        const int ko = (16 * J + l16) * PKB + c;
+        acc = mfma3(split(qv), Split8{*reinterpret_cast<const bf16x8*>(sKChi + ko), *reinterpret_cast<const bf16x8*>(sKClo + ko)}, acc);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -1041,23 +1061,13 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     }
     __syncthreads();
 
-    // ---- write W and K~^T in fragment order (fp16, 16-byte stores, 8 elements per lane-task) ----
-    _Float16* kthi = reinterpret_cast<_Float16*>(blk + W_KTHI);
+    // ---- write W in fragment order (fp16, 16-byte stores, 8 elements per lane-task) ----
     _Float16* wdst = reinterpret_cast<_Float16*>(blk + W_W);
     for (int task = tid; task < C * D / 8; task += NT) {
       // W: [64 tokens][128 channels]
       const int t = task >> 4, c8 = (task & 15) * 8;
       const int fo = frag_offset(t, c8, D);
       *reinterpret_cast<f16x8*>(wdst + fo) = *reinterpret_cast<const f16x8*>(sKb + t * PKB + c8);
-      // K~^T = (KC e^(Gam_C - Gam_n(J)))^T: [128 channels][64 tokens]; the lanes of a wave take
-      // 64 consecutive channels of one 8-token group, so the column reads of KC hit 64 banks
-      const int c = task & 127, t8 = (task >> 7) * 8;
-      const int ko = frag_offset(c, t8, C);
-      const float fac = sFac[(t8 >> 4) * D + c];
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = sG[(t8 + e) * PQ + c] * fac;
-      *reinterpret_cast<f16x8*>(kthi + ko) = to_f16x8(v);
     }
     // every lane stores (four lanes per value, the same value) so that the number of stores is fixed
     reinterpret_cast<float*>(blk + W_GC)[tid & 127] = sGC[tid & 127];
