@@ -170,6 +170,11 @@ def short_kernel_name(full):
     if name == "kda_chunk_state64_kernel":  # the uniform-batch state pass (the library's timing name)
         name = "kda_chunk_state_kernel"
     targs = m.group(2) or ""
+    if not targs:
+        # a name the profiler left mangled: template arguments as ILb<0|1>E[Li<n>E]...
+        mm = re.match(re.escape(m.group(1)) + r"I(Lb([01])E)(Li(\d+)E)?", full[m.start(1):])
+        if mm:
+            targs = "<" + ("true" if mm.group(2) == "1" else "false") + (", " + mm.group(4) if mm.group(4) else "") + ">"
     if name in ("kda_chunk_prep_kernel", "kda_chunk_state_kernel") and targs.startswith("<true"):
         name += "[varlen]"
     if name == "kda_chunk_prep_kernel":
@@ -199,13 +204,13 @@ def pmc_summary(fetch_dir, write_dir, command):
                 name = short_kernel_name(r["Kernel_Name"])
                 if name is not None:
                     acc.setdefault(name, []).append(v)
-                elif "neg" in r["Kernel_Name"].lower() or "elementwise" in r["Kernel_Name"]:
+                elif "neg_kernel" in r["Kernel_Name"]:
                     calib.append(v)
         return acc, calib
 
     fetch, fcal = per_kernel(fetch_dir, "FETCH_SIZE")
     write, wcal = per_kernel(write_dir, "WRITE_SIZE")
-    # the calibration copy is the elementwise launch that moved about CALIB_BYTES
+    # the calibration copy is torch's neg over CALIB_BYTES (the only neg launch of the run)
     fc = max(fcal) / CALIB_BYTES
     wc = max(wcal) / CALIB_BYTES
     out = {"command": command, "source_sha256": source_fingerprint(),
@@ -221,9 +226,11 @@ def pmc_summary(fetch_dir, write_dir, command):
 
 
 def mfma_summary(pmc_dir, command, n_cu=256):
-    """Per-kernel matrix-core busy fraction from one rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES,
-    GRBM_GUI_ACTIVE, SQ_INSTS_MFMA and SQ_INSTS_VALU: busy / (GRBM_GUI_ACTIVE x 4 SIMDs x CUs), the
-    mean over the kernel's dispatches; stored in profiles/pmc_mfma.json with the sources' sha256."""
+    """Per-kernel instruction counts from one rocprofv3 --pmc run of the SQ counters (SQ_INSTS_MFMA,
+    SQ_INSTS_VALU, SQ_INSTS_LDS, ...): the mean over the kernel's dispatches, and the issued matrix-core
+    rate, SQ_INSTS_MFMA x 16,384 flop (one 16x16x32 bf16 / fp16 product; the few fp32 16x16x4 steps of
+    the prefill count the same, an upper bound) over the dispatch's duration, as a fraction of the dense
+    bf16 peak; stored in profiles/pmc_mfma.json with the sources' sha256."""
     import csv
     import glob
     vals = {}
@@ -233,20 +240,25 @@ def mfma_summary(pmc_dir, command, n_cu=256):
             if name is None:
                 continue
             key = (name, r.get("Dispatch_Id", r.get("Correlation_Id", "")))
-            vals.setdefault(name, {}).setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+            rec = vals.setdefault(name, {}).setdefault(key, {})
+            rec[r["Counter_Name"]] = float(r["Counter_Value"])
+            rec["duration_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
     out = {"command": command, "source_sha256": source_fingerprint(), "n_cu": n_cu, "kernels": {}}
     for name, disp in sorted(vals.items()):
-        fr, mf, va = [], [], []
+        fr, mf, va, ld = [], [], [], []
         for c in disp.values():
-            if c.get("GRBM_GUI_ACTIVE", 0) > 0 and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
-                fr.append(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * 4 * n_cu))
+            if "SQ_INSTS_MFMA" in c and c["duration_ns"] > 0:
+                fr.append(c["SQ_INSTS_MFMA"] * 16384 / (c["duration_ns"] * 1e-9) / 1e12 / BF16_MFMA_PEAK_TFLOPS)
             if "SQ_INSTS_MFMA" in c:
                 mf.append(c["SQ_INSTS_MFMA"])
             if "SQ_INSTS_VALU" in c:
                 va.append(c["SQ_INSTS_VALU"])
-        out["kernels"][name] = {"mfma_busy_frac": float(np.mean(fr)) if fr else None,
+            if "SQ_INSTS_LDS" in c:
+                ld.append(c["SQ_INSTS_LDS"])
+        out["kernels"][name] = {"mfma_issued_frac": float(np.mean(fr)) if fr else None,
                                 "insts_mfma": float(np.mean(mf)) if mf else None,
-                                "insts_valu": float(np.mean(va)) if va else None, "dispatches": len(disp)}
+                                "insts_valu": float(np.mean(va)) if va else None,
+                                "insts_lds": float(np.mean(ld)) if ld else None, "dispatches": len(disp)}
     json.dump(out, open(SQ_FILE, "w"), indent=1)
     print(json.dumps(out, indent=1))
 
@@ -304,9 +316,9 @@ def prefill_alg_flops(T, H, D, C=PREFILL_CHUNK):
 SQ_FILE = os.path.join(ROOT, "profiles", "pmc_mfma.json")
 
 
-def stored_mfma_busy(kernel):
-    """Fraction of the chip's matrix-core cycles busy during `kernel` from the committed counter run
-    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x 4 SIMDs x CUs), or None when there is none or
+def stored_mfma_issued(kernel):
+    """Issued matrix-core rate of `kernel` as a fraction of the dense bf16 peak from the committed
+    counter run (SQ_INSTS_MFMA x 16,384 flop over the dispatch time), or None when there is none or
     the sources changed since."""
     if not os.path.exists(SQ_FILE):
         return None
@@ -314,7 +326,7 @@ def stored_mfma_busy(kernel):
     if rec.get("source_sha256") != source_fingerprint():
         return None
     k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("mfma_busy_frac")
+    return None if k is None else k.get("mfma_issued_frac")
 
 
 def hbm_ceilings(dev, nbytes=1 << 30, reps=5):
@@ -755,11 +767,11 @@ def main():
             res["roofline"]["prefill_mfma"] = {
                 "alg_tflops": pl["alg_tflops"], "peak": BF16_MFMA_PEAK_TFLOPS,
                 "frac": pl["alg_tflops"] / BF16_MFMA_PEAK_TFLOPS,
-                "busy_frac_by_kernel": {kn: stored_mfma_busy(kn) for kn in
-                                        ("kda_chunk_prep_kernel", "kda_chunk_state_kernel")},
-                "note": "algorithmic dense-tile flops of the prefill call over its mean call time; busy fraction "
-                        "from profiles/pmc_mfma.json (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 4 x CUs)), "
-                        "null when those counters were taken on other sources"}
+                "issued_frac_by_kernel": {kn: stored_mfma_issued(kn) for kn in
+                                          ("kda_chunk_prep_kernel", "kda_chunk_state_kernel")},
+                "note": "algorithmic dense-tile flops of the prefill call over its mean call time; issued fraction "
+                        "from profiles/pmc_mfma.json (SQ_INSTS_MFMA x 16,384 flop over the dispatch time, of the "
+                        "2.5 PFLOP/s dense bf16 peak), null when those counters were taken on other sources"}
     else:  # --only projection: its GEMM against the dense bf16 matrix-core peak
         name = max((n for n in kern if kern[n].get("flops")), key=share)
         k = kern[name]
