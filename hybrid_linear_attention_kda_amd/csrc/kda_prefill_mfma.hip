@@ -102,7 +102,8 @@ constexpr int OFF_GA = OFF_AQK + C * PA * 4;           // per-wave squared-norm 
 constexpr int LDS_A = OFF_GA + 4 * D * 4;
 static_assert(STG_BYTES >= 2 * C * PA * 4, "staging aliases");
 static_assert(C * PTB * 2 <= C * PA * 4, "the fp16 T and A_qk planes fit their regions");
-static_assert(D * PXT * 2 <= C * PKB * 2 && C * PA * 4 + D * PXT * 2 <= STG_BYTES, "X planes alias KR and the fp32 T");
+static_assert(D * PXT * 2 <= C * PKB * 2 && D * PXT * 2 <= 2 * C * PKB * 2, "X planes alias KR and the KC planes");
+static_assert(C * PKB * 2 <= C * PA * 4 && (RROWS) * PKB * 2 <= 2 * C * PKB * 2, "W aliases the fp32 T, the v rows the KC planes");
 static_assert(LDS_A <= 160 * 1024, "LDS budget");
 
 // Workspace tile block per (sequence, head, chunk), written by phase A and read by phase B.
@@ -997,17 +998,13 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       *reinterpret_cast<f16x4*>(sT16 + t * PTB + j8) = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
       *reinterpret_cast<f16x4*>(sT16 + t * PTB + j8 + 4) = f16x4{(_Float16)v[4], (_Float16)v[5], (_Float16)v[6], (_Float16)v[7]};
     }
-    __syncthreads();
-
-    prep_issue<VL>(a, st, knext, tid, nxt, 2);
-
-    // ---- P8: W = T X with T in fp16 and X split into fp16 hi + lo (T.X lo + T.X hi).  X goes to
-    //      LDS transposed, [channel][token], as two planes in place of KR (no longer read) and of
-    //      the fp32 T (converted above): a lane writes its 16 tokens of one channel, and a
-    //      B-operand fragment (8 tokens of one channel) is two 8-byte reads; wave -> 16 key
-    //      channels ----
-    _Float16* sXhi = reinterpret_cast<_Float16*>(sKb);                          // [128][PXT]
-    _Float16* sXlo = reinterpret_cast<_Float16*>(smem + OFF_STG + C * PA * 4);  // [128][PXT], old fp32 T
+    // ---- P8 (from the same phase): W = T X with T in fp16 and X split into fp16 hi + lo (T.X lo +
+    //      T.X hi).  X goes to LDS transposed, [channel][token], as two planes in place of KR and
+    //      of the KC planes (both last read by the A blocks): a lane writes its 16 tokens of one
+    //      channel, and a B-operand fragment (8 tokens of one channel) is two 8-byte reads;
+    //      wave -> 16 key channels ----
+    _Float16* sXhi = reinterpret_cast<_Float16*>(sKb);           // [128][PXT]
+    _Float16* sXlo = reinterpret_cast<_Float16*>(smem + OFF_G);  // [128][PXT]
     {
       const int i = tid & 127, seg = tid >> 7;
 #pragma unroll
@@ -1024,6 +1021,9 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       }
     }
     __syncthreads();
+
+    prep_issue<VL>(a, st, knext, tid, nxt, 2);
+
     f32x4 wacc[4] = {zero4(), zero4(), zero4(), zero4()};
     {
       const int c = 16 * wave + l16;
@@ -1038,14 +1038,12 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
         }
       }
     }
-    __syncthreads();  // every read of X is done: W (fp16) takes X hi's place
+    // W (fp16) in place of the fp32 T (converted above), for its fragment-order store
+    _Float16* sW = reinterpret_cast<_Float16*>(smem + OFF_STG + C * PA * 4);  // [64][PKB]
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int o = (16 * I + 4 * lg + r) * PKB + 16 * wave + l16;
-        reinterpret_cast<_Float16*>(sKb)[o] = (_Float16)wacc[I][r];
-      }
+      for (int r = 0; r < 4; ++r) sW[(16 * I + 4 * lg + r) * PKB + 16 * wave + l16] = (_Float16)wacc[I][r];
     // W as this wave's split B operand over tokens, in the token order of its own accumulators: k-step
     // s, lane group g, element e <-> token 32 s + 4 g + e (e < 4), 32 s + 16 + 4 g + e - 4 (e >= 4)
     Half8 wb[2];
@@ -1059,7 +1057,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       }
       wb[st] = split16(x);
     }
-    __syncthreads();
+    __syncthreads();  // W is in LDS and every read of X is done: the raw v rows take X lo's place
 
     // ---- write W in fragment order (fp16, 16-byte stores, 8 elements per lane-task) ----
     _Float16* wdst = reinterpret_cast<_Float16*>(blk + W_W);
@@ -1067,13 +1065,12 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       // W: [64 tokens][128 channels]
       const int t = task >> 4, c8 = (task & 15) * 8;
       const int fo = frag_offset(t, c8, D);
-      *reinterpret_cast<f16x8*>(wdst + fo) = *reinterpret_cast<const f16x8*>(sKb + t * PKB + c8);
+      *reinterpret_cast<f16x8*>(wdst + fo) = *reinterpret_cast<const f16x8*>(sW + t * PKB + c8);
     }
     // every lane stores (four lanes per value, the same value) so that the number of stores is fixed
     reinterpret_cast<float*>(blk + W_GC)[tid & 127] = sGC[tid & 127];
-    __syncthreads();  // KC is read: the raw v rows take its place
 
-    // ---- stage raw v rows for tokens c0-3 .. c0+63 (bf16, pitch PKB) ----
+    // ---- stage raw v rows for tokens c0-3 .. c0+63 (bf16, pitch PKB; same phase) ----
     __bf16* sRv = reinterpret_cast<__bf16*>(smem + OFF_G);
 #pragma unroll
     for (int s = 0; s < NRV; ++s) {
