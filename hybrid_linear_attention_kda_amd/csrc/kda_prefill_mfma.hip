@@ -1205,17 +1205,17 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       for (int I = 0; I < 4; ++I)
 #pragma unroll
         for (int r = 0; r < 4; ++r) sQ[(16 * I + 4 * lg + r) * PQ + vc] = qo[4 * I + r] * en[I] - pacc[I][r];
-    }
-    __syncthreads();
-
-    // ---- write P in fragment order (fp16) ----
-    _Float16* phi = reinterpret_cast<_Float16*>(blk + W_PHI);
-    for (int task = tid; task < C * D / 8; task += NT) {
-      const int t = task >> 4, c8 = (task & 15) * 8;
-      const int fo = frag_offset(t, c8, D);
-      float v[8];
-      ld8(sQ + t * PQ + c8, v);
-      *reinterpret_cast<f16x8*>(phi + fo) = to_f16x8(v);
+      // ---- write this wave's 16 columns of P in fragment order (fp16): 64 rows x 2 pieces of 8
+      //      channels, read back from the wave's own LDS columns ----
+      wave_lds_sync();
+      _Float16* phi = reinterpret_cast<_Float16*>(blk + W_PHI);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int sl = lane + 64 * q, t = sl >> 1, c8 = 16 * wave + 8 * (sl & 1);
+        float v[8];
+        ld8(sQ + t * PQ + c8, v);
+        *reinterpret_cast<f16x8*>(phi + frag_offset(t, c8, D)) = to_f16x8(v);
+      }
     }
     __syncthreads();  // the next task overwrites the staging rows and tables
     cur = nxt;
