@@ -1038,12 +1038,22 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
         }
       }
     }
-    // W (fp16) in place of the fp32 T (converted above), for its fragment-order store
+    // W (fp16) in place of the fp32 T (converted above); each wave stores its own 16 columns in
+    // fragment order (64 rows x 2 pieces of 8 channels) from there, after a wave-local sync
     _Float16* sW = reinterpret_cast<_Float16*>(smem + OFF_STG + C * PA * 4);  // [64][PKB]
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
       for (int r = 0; r < 4; ++r) sW[(16 * I + 4 * lg + r) * PKB + 16 * wave + l16] = (_Float16)wacc[I][r];
+    wave_lds_sync();
+    {
+      _Float16* wdst = reinterpret_cast<_Float16*>(blk + W_W);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int sl = lane + 64 * q, t = sl >> 1, c8 = 16 * wave + 8 * (sl & 1);
+        *reinterpret_cast<f16x8*>(wdst + frag_offset(t, c8, D)) = *reinterpret_cast<const f16x8*>(sW + t * PKB + c8);
+      }
+    }
     // W as this wave's split B operand over tokens, in the token order of its own accumulators: k-step
     // s, lane group g, element e <-> token 32 s + 4 g + e (e < 4), 32 s + 16 + 4 g + e - 4 (e >= 4)
     Half8 wb[2];
@@ -1057,20 +1067,12 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       }
       wb[st] = split16(x);
     }
-    __syncthreads();  // W is in LDS and every read of X is done: the raw v rows take X lo's place
+    __syncthreads();  // every read of X is done: the raw v rows take X lo's place
 
-    // ---- write W in fragment order (fp16, 16-byte stores, 8 elements per lane-task) ----
-    _Float16* wdst = reinterpret_cast<_Float16*>(blk + W_W);
-    for (int task = tid; task < C * D / 8; task += NT) {
-      // W: [64 tokens][128 channels]
-      const int t = task >> 4, c8 = (task & 15) * 8;
-      const int fo = frag_offset(t, c8, D);
-      *reinterpret_cast<f16x8*>(wdst + fo) = *reinterpret_cast<const f16x8*>(sW + t * PKB + c8);
-    }
     // every lane stores (four lanes per value, the same value) so that the number of stores is fixed
     reinterpret_cast<float*>(blk + W_GC)[tid & 127] = sGC[tid & 127];
 
-    // ---- stage raw v rows for tokens c0-3 .. c0+63 (bf16, pitch PKB; same phase) ----
+    // ---- stage raw v rows for tokens c0-3 .. c0+63 (bf16, pitch PKB) ----
     __bf16* sRv = reinterpret_cast<__bf16*>(smem + OFF_G);
 #pragma unroll
     for (int s = 0; s < NRV; ++s) {
