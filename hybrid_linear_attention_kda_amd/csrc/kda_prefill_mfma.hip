@@ -496,6 +496,11 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     prep_issue<VL>(a, st, k0, (int)threadIdx.x, cur, 0);
     prep_issue<VL>(a, st, k0, (int)threadIdx.x, cur, 1);
     prep_issue<VL>(a, st, k0, (int)threadIdx.x, cur, 2);
+    // the first task's inputs are awaited here, so that inside the loop the waits for a task's
+    // inputs count only the loads and stores issued after them in the previous task (without
+    // it the loop entry would force a wait for every outstanding access, the previous task's
+    // tile stores included)
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
   }
   for (int tk = blockIdx.x; tk < ntask; tk += gridDim.x) {
     // lane indices are re-derived per task from an opaque copy, so that the address arithmetic
