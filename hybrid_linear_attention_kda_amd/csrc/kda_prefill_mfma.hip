@@ -848,7 +848,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       int I, J;
       block_ij(bi, I, J);
       if (SP && I == J) return;  // formed exactly from the per-channel sums
-      f32x4 acc = zero4();
+      // two accumulators (even and odd k-steps): independent products overlap on the matrix core
+      f32x4 acc2[2] = {zero4(), zero4()};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int c = 32 * s + 8 * lg;
@@ -858,8 +859,11 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 #pragma unroll
           for (int e = 0; e < 8; ++e) av[e] = (__bf16)((float)av[e] * ef[e]);
         }
-        acc = mfma(av, *reinterpret_cast<const bf16x8*>(sKChi + (16 * J + l16) * PKB + c), acc);
+        acc2[s & 1] = mfma(av, *reinterpret_cast<const bf16x8*>(sKChi + (16 * J + l16) * PKB + c), acc2[s & 1]);
       }
+      f32x4 acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = acc2[0][r] + acc2[1][r];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * I + 4 * lg + r, j = 16 * J + l16;
@@ -899,7 +903,9 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       int I, J;
       block_ij(bi, I, J);
       if (SP && I == J) return;  // formed exactly from the per-channel sums
-      f32x4 acc = zero4();
+      // the three split products (lo.hi, hi.lo, hi.hi) in three accumulators: three independent
+      // chains on the matrix core instead of one of twelve dependent products
+      f32x4 acc3[3] = {zero4(), zero4(), zero4()};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int c = 32 * s + 8 * lg;
@@ -911,8 +917,15 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
           for (int e = 0; e < 8; ++e) qv[e] *= ef[e];
         }
         const int ko = (16 * J + l16) * PKB + c;
-        acc = mfma3(split(qv), Split8{*reinterpret_cast<const bf16x8*>(sKChi + ko), *reinterpret_cast<const bf16x8*>(sKClo + ko)}, acc);
+        const Split8 qs = split(qv);
+        const Split8 ks{*reinterpret_cast<const bf16x8*>(sKChi + ko), *reinterpret_cast<const bf16x8*>(sKClo + ko)};
+        acc3[0] = mfma(qs.lo, ks.hi, acc3[0]);
+        acc3[1] = mfma(qs.hi, ks.lo, acc3[1]);
+        acc3[2] = mfma(qs.hi, ks.hi, acc3[2]);
       }
+      f32x4 acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = (acc3[0][r] + acc3[1][r]) + acc3[2][r];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * I + 4 * lg + r, j = 16 * J + l16;
@@ -1036,10 +1049,18 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       for (int s = 0; s < 2; ++s) {
         const int tb = 32 * s + 8 * lg;
         const Half8 x{ld4x2(sXhi + c * PXT + tb, 4), ld4x2(sXlo + c * PXT + tb, 4)};
+        // the lo products of every row block, then the hi ones: consecutive products independent
+        f16x8 tI[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
           if (32 * s > 16 * I + 15) continue;  // T is lower triangular
-          wacc[I] = mfma2h(ld4x2(sT16 + (16 * I + l16) * PTB + 32 * s + 8 * lg, 4), x, wacc[I]);
+          tI[I] = ld4x2(sT16 + (16 * I + l16) * PTB + 32 * s + 8 * lg, 4);
+          wacc[I] = mfma16(tI[I], x.lo, wacc[I]);
+        }
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          if (32 * s > 16 * I + 15) continue;
+          wacc[I] = mfma16(tI[I], x.hi, wacc[I]);
         }
       }
     }
@@ -1166,15 +1187,25 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       f32x4 ut[4];
       f32x4* utd = reinterpret_cast<f32x4*>(blk + W_UT);
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        ut[I] = zero4();
+      for (int I = 0; I < 4; ++I) ut[I] = zero4();
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          if (32 * st > 16 * I + 15) continue;  // T is lower triangular
-          ut[I] = mfma2h(ld4x2(sT16 + (16 * I + l16) * PTB + 32 * st + 8 * lg, 4), bv[st], ut[I]);
+      for (int st = 0; st < 2; ++st) {
+        // the lo products of every row block, then the hi ones (T is lower triangular)
+        f16x8 tI[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          if (32 * st > 16 * I + 15) continue;
+          tI[I] = ld4x2(sT16 + (16 * I + l16) * PTB + 32 * st + 8 * lg, 4);
+          ut[I] = mfma16(tI[I], bv[st].lo, ut[I]);
         }
-        utd[(I * 8 + wave) * 64 + lane] = ut[I];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          if (32 * st > 16 * I + 15) continue;
+          ut[I] = mfma16(tI[I], bv[st].hi, ut[I]);
+        }
       }
+#pragma unroll
+      for (int I = 0; I < 4; ++I) utd[(I * 8 + wave) * 64 + lane] = ut[I];
       // Ut as the B operand over tokens in accumulator token order (see wb)
       Half8 ub[2];
 #pragma unroll
