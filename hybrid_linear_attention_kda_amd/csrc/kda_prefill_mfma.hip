@@ -23,7 +23,7 @@
 //      Ut = T (beta V),  Y = A_qk Ut,  P = Q~ - A_qk W,
 //    with Q~ = Q e^Gam and K~ = K e^(Gam_C - Gam).  Everything that does not
 //    depend on the state is written to the workspace once per chunk: P, W and K~^T
-//    (transposed) and Y as fp16, Ut and e^Gam_C as fp32, each in the order the
+//    (transposed), Ut and Y as fp16, e^Gam_C as fp32, each in the order the
 //    matrix cores consume it.
 //  B (sequential over chunks, one workgroup per (sequence, head, 16-column
 //    block of d_v); with a sequence table, per group of consecutive sequences,
@@ -115,10 +115,11 @@ static_assert(LDS_A <= 160 * 1024, "LDS budget");
 constexpr int W_PHI = 0;                   // P = Q~ - A_qk W [64][128] fp16 (16 fragments)
 constexpr int W_KTHI = W_PHI + C * D * 2;  // K~^T [128][64] fp16
 constexpr int W_W = W_KTHI + D * C * 2;    // W [64][128] fp16
-constexpr int W_UT = W_W + C * D * 2;      // Ut = T (beta V) [64][128] fp32, accumulator-fragment order
-constexpr int W_Y = W_UT + C * D * 4;      // Y = A_qk Ut [64][128] fp16, accumulator-fragment order
+constexpr int W_UT = W_W + C * D * 2;      // Ut = T (beta V) [64][128] fp16, accumulator-fragment order,
+                                           // column tile major (a column tile's 4 row tiles are 2 KB)
+constexpr int W_Y = W_UT + C * D * 2;      // Y = A_qk Ut [64][128] fp16, accumulator-fragment order
 constexpr int W_GC = W_Y + C * D * 2;      // e^Gam_C [128] fp32
-constexpr int CH_BYTES = W_GC + D * 4;     // 98816
+constexpr int CH_BYTES = W_GC + D * 4;     // 82432
 static_assert(CH_BYTES % 256 == 0, "tile blocks stay 256-byte aligned");
 
 // Phase B: 8 compute waves and 4 loader waves per workgroup.
@@ -137,7 +138,7 @@ constexpr int B_TRASH = B_SLO + NVB * PST * 2;   // 256 B, written by warming lo
 // buffers: two of W | Ut (each copied a chunk and a half ahead) and two of K~^T | e^Gam_C.
 constexpr int WU_W = 0;
 constexpr int WU_UT = WU_W + C * D * 2;
-constexpr int WU_BYTES = WU_UT + 4 * 1024;       // 20480
+constexpr int WU_BYTES = WU_UT + 4 * 512;        // 18432
 constexpr int KB_KHI = 0;
 constexpr int KB_GC = KB_KHI + D * C * 2;
 constexpr int KB_BYTES = KB_GC + D * 4;          // 16896
@@ -1185,7 +1186,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
         bv[st] = split16(xv);
       }
       f32x4 ut[4];
-      f32x4* utd = reinterpret_cast<f32x4*>(blk + W_UT);
+      f16x4* utd = reinterpret_cast<f16x4*>(blk + W_UT);
 #pragma unroll
       for (int I = 0; I < 4; ++I) ut[I] = zero4();
 #pragma unroll
@@ -1205,7 +1206,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
         }
       }
 #pragma unroll
-      for (int I = 0; I < 4; ++I) utd[(I * 8 + wave) * 64 + lane] = ut[I];
+      for (int I = 0; I < 4; ++I)
+        utd[(wave * 4 + I) * 64 + lane] = f16x4{(_Float16)ut[I][0], (_Float16)ut[I][1], (_Float16)ut[I][2], (_Float16)ut[I][3]};
       // Ut as the B operand over tokens in accumulator token order (see wb)
       Half8 ub[2];
 #pragma unroll
@@ -1363,8 +1365,9 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
   auto wubuf = [&](int c) { return smem + B_WU0 + (c & 1) * WU_BYTES; };
   auto kbuf = [&](int c) { return smem + B_KB0 + (c & 1) * KB_BYTES; };
 
-  // ---- loader waves (lw = 0..3): each copies 5 of the 20 W | Ut fragments and 4 of the 16 K~^T
-  //      fragments of a chunk (wave 3 also e^Gam_C); cache lines of later chunks touched ----
+  // ---- loader waves (lw = 0..3): each copies 4 of the 16 W fragments, row tile lw of this block's
+  //      Ut (512 B, half the lanes) and 4 of the 16 K~^T fragments of a chunk (wave 3 also e^Gam_C);
+  //      cache lines of later chunks touched ----
   const int lw = wave - 8;
   constexpr int N_WU = 5, N_K = 4;
   Cursor cur_wu = cursor0(), cur_k = cursor0(), cur_t = cursor0();
@@ -1372,12 +1375,11 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
     const unsigned char* blk = chunk_ptr(cur_wu, cn);
     unsigned char* wb = wubuf(cn);
 #pragma unroll
-    for (int q = 0; q < N_WU; ++q) {
-      // 0..15: W fragment f; 16..19: Ut row tile f - 16 of column tile vb
-      const int f = lw * N_WU + q;
-      const unsigned char* src = f < 16 ? blk + W_W + f * 1024 : blk + W_UT + ((f - 16) * 8 + vb) * 1024;
-      dma16(src + lane * 16, wb + WU_W + f * 1024);
+    for (int q = 0; q < N_WU - 1; ++q) {
+      const int f = lw * (N_WU - 1) + q;  // W fragment f
+      dma16(blk + W_W + f * 1024 + lane * 16, wb + WU_W + f * 1024);
     }
+    if (lane < 32) dma16(blk + W_UT + (vb * 4 + lw) * 512 + lane * 16, wb + WU_UT + lw * 512);
   };
   auto issue_k = [&](int cn) {
     const unsigned char* blk = chunk_ptr(cur_k, cn);
@@ -1582,11 +1584,11 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
         pa = mfma16(w, sh, pa);
         pb = mfma16(w, sl, pb);
       }
-      const f32x4 ut = *reinterpret_cast<const f32x4*>(wb + WU_UT + (I * 64 + lane) * 16);
+      const f16x4 ut = *reinterpret_cast<const f16x4*>(wb + WU_UT + (I * 64 + lane) * 8);
       f16x4 hi, lo;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float u = ut[r] - (pa[r] + pb[r]);
+        const float u = (float)ut[r] - (pa[r] + pb[r]);
         hi[r] = (_Float16)u;
         lo[r] = (_Float16)(u - (float)hi[r]);
       }
@@ -1709,7 +1711,7 @@ __global__ __launch_bounds__(256) void kda_out_norm_kernel(const _Float16* __res
 // The staging halo covers conv widths up to 4.  Every gate whose log-decay is <= 0 runs here: the
 // bounded gate with -5.5 <= lb <= 0 on start-anchored sub-chunks (its factors stay finite while
 // 15 |lb| < 87), with lb < -5.5 and the softplus branch on end-anchored ones with exact diagonal
-// blocks.  W keeps ~11 bits through phase B (fp16) and Ut fp32, so weak decay (lb near 0, or
+// blocks.  W and Ut keep ~11 bits through phase B (fp16), so weak decay (lb near 0, or
 // pre-activations that keep the gate near 0) keeps the state within the tolerance.  A positive bound (log-decay above
 // 0, a growing state) takes the fp32 path.
 bool prefill_mfma_supported(int Dh, int chunk, int io, int W, float lb, int gate) {
