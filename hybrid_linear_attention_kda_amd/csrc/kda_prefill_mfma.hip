@@ -1623,13 +1623,15 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
     auto chunk_o = [&](int ci, OpTiles& cur) __attribute__((always_inline)) {
       const ChunkRef rc = locate(cur_o, ci);
       lds_barrier();  // (a)
+      // the state's fp16 hi part only: O is not fed back into the state, so its rounding does not
+      // accumulate over chunks, and P itself is fp16
       f32x4 oa = zero4(), ob = zero4();
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const f16x8 sh = *reinterpret_cast<const f16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
-        const f16x8 sl = *reinterpret_cast<const f16x8*>(sSlo + l16 * PST + 32 * s + 8 * lg);
-        oa = mfma16(cur.x0[s], sh, oa);
-        ob = mfma16(cur.x0[s], sl, ob);
+      for (int s = 0; s < 4; s += 2) {
+        const f16x8 s0 = *reinterpret_cast<const f16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
+        const f16x8 s1 = *reinterpret_cast<const f16x8*>(sShi + l16 * PST + 32 * (s + 1) + 8 * lg);
+        oa = mfma16(cur.x0[s], s0, oa);
+        ob = mfma16(cur.x0[s + 1], s1, ob);
       }
       f32x4 o;
 #pragma unroll
