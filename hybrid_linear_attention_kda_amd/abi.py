@@ -19,7 +19,9 @@ from typing import Optional
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkda.so")
+# KDA_LIBRARY names another build of the same library (the host-sanitizer build of
+# build.build_host_sanitized); by default the in-tree libkda.so is loaded.
+LIB_PATH = os.environ.get("KDA_LIBRARY") or os.path.join(HERE, "libkda.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "kda.h")
 
 KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
