@@ -11,24 +11,23 @@
 // max(||x||, eps), bounded-sigmoid per-channel decay on the key axis, gated
 // output RMSNorm with a plain weight).
 //
-// Expanding U in O gives O = (Q~ - A_qk W) S + A_qk Ut, so only products with the
-// chunk-start state S remain in the sequential part.
+// O is taken as written, Q~ S + A_qk U: U is formed in the sequential part anyway, so the
+// chunk-parallel part needs no product with A_qk beyond A_qk itself.
 //
 // Two phases.
 //  A (chunk-parallel: persistent workgroups, one per CU, looping over the
 //    (sequence, head, chunk) tasks chunk-major from the last chunk down, so that
 //    the tiles B reads first were written last and are still in the last-level
 //    cache): conv + SiLU,
-//    L2 norms, gate and its cumulative sum, A_kk, T, A_qk, W, and from them
-//      Ut = T (beta V),  Y = A_qk Ut,  P = Q~ - A_qk W,
+//    L2 norms, gate and its cumulative sum, A_kk, T, A_qk, W and Ut = T (beta V),
 //    with Q~ = Q e^Gam and K~ = K e^(Gam_C - Gam).  Everything that does not
-//    depend on the state is written to the workspace once per chunk: P, W and K~^T
-//    (transposed), Ut and Y as fp16, e^Gam_C as fp32, each in the order the
+//    depend on the state is written to the workspace once per chunk: Q~, W, K~^T
+//    (transposed), Ut and A_qk as fp16, e^Gam_C as fp32, each in the order the
 //    matrix cores consume it.
 //  B (sequential over chunks, one workgroup per (sequence, head, 16-column
 //    block of d_v); with a sequence table, per group of consecutive sequences,
 //    whose chunks it runs as one stream): per chunk
-//      U = Ut - W S,  O = P S + Y,  S <- e^Gam_C S + K~^T U,
+//      U = Ut - W S,  O = Q~ S + A_qk U,  S <- e^Gam_C S + K~^T U,
 //    with the 128 x 16 state block in MFMA accumulators and the operands of
 //    chunk c+1 loaded into registers while chunk c is computed.  blockIdx.x =
 //    vb * H + h, so with H a multiple of 8 the eight workgroups of a head run on
@@ -47,10 +46,10 @@
 //
 // Precision.  bf16 operands round to 8 bits; A_qk is formed on split bf16 (x = hi
 // + lo, three MFMAs: hi.hi + hi.lo + lo.hi), A_kk in plain bf16, and T in fp32.
-// The products of phase A that use them (W = T X, Ut = T (beta V), Y = A_qk Ut,
-// A_qk W) take T and A_qk as fp16 (11 significant bits) and the other operand
-// split into fp16 hi + lo (~22 bits), two MFMAs each, as phase B does.  Phase B's three products with the state (W S, P S, K~^T U) take
-// W, P and K~^T as fp16 (11 significant bits, half the bytes of a split bf16 pair
+// The products of phase A that use them (W = T X, Ut = T (beta V)) take T as fp16
+// (11 significant bits) and the other operand split into fp16 hi + lo (~22 bits),
+// two MFMAs each, as phase B does.  Phase B's products (W S, Q~ S, A_qk U, K~^T U) take
+// W, Q~, A_qk and K~^T as fp16 (11 significant bits, half the bytes of a split bf16 pair
 // on the per-chunk operand path) and S or U split into fp16 hi + lo (~22 bits),
 // two MFMAs each.  fp16's range holds these values: |q| and |k| are at most
 // 1 after the L2 norm, and the delta rule keeps every state entry within the
@@ -112,14 +111,15 @@ static_assert(LDS_A <= 160 * 1024, "LDS budget");
 // k = 32*(f % (K/32)) + 8*(l / 16) + 0..7), so a wave loads one fragment as 1 KB contiguous.
 // The fp32 [64][128] matrices are stored as 16 x 16 accumulator tiles (I, j), tile-major
 // (I * 8 + j), lane l holding rows 16 I + 4 (l / 16) + 0..3 of column 16 j + l % 16.
-constexpr int W_PHI = 0;                   // P = Q~ - A_qk W [64][128] fp16 (16 fragments)
-constexpr int W_KTHI = W_PHI + C * D * 2;  // K~^T [128][64] fp16
+constexpr int W_QT = 0;                    // Q~ = Q e^Gam [64][128] fp16 (16 fragments)
+constexpr int W_KTHI = W_QT + C * D * 2;   // K~^T [128][64] fp16
 constexpr int W_W = W_KTHI + D * C * 2;    // W [64][128] fp16
 constexpr int W_UT = W_W + C * D * 2;      // Ut = T (beta V) [64][128] fp16, accumulator-fragment order,
                                            // column tile major (a column tile's 4 row tiles are 2 KB)
-constexpr int W_Y = W_UT + C * D * 2;      // Y = A_qk Ut [64][128] fp16, accumulator-fragment order
-constexpr int W_GC = W_Y + C * D * 2;      // e^Gam_C [128] fp32
-constexpr int CH_BYTES = W_GC + D * 4;     // 82432
+constexpr int W_AQK = W_UT + C * D * 2;    // A_qk [64][64] fp16 (8 fragments; (0, 1) and (1, 1), above
+                                           // the diagonal, hold zeros)
+constexpr int W_GC = W_AQK + C * C * 2;    // e^Gam_C [128] fp32
+constexpr int CH_BYTES = W_GC + D * 4;     // 74240
 static_assert(CH_BYTES % 256 == 0, "tile blocks stay 256-byte aligned");
 
 // Phase B: 8 compute waves and 4 loader waves per workgroup.
@@ -1081,19 +1081,6 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
         *reinterpret_cast<f16x8*>(wdst + frag_offset(t, c8, D)) = *reinterpret_cast<const f16x8*>(sW + t * PKB + c8);
       }
     }
-    // W as this wave's split B operand over tokens, in the token order of its own accumulators: k-step
-    // s, lane group g, element e <-> token 32 s + 4 g + e (e < 4), 32 s + 16 + 4 g + e - 4 (e >= 4)
-    Half8 wb[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = wacc[2 * st][e];
-        x[e + 4] = wacc[2 * st + 1][e];
-      }
-      wb[st] = split16(x);
-    }
     __syncthreads();  // every read of X is done: the raw v rows take X lo's place
 
     // every lane stores (four lanes per value, the same value) so that the number of stores is fixed
@@ -1126,44 +1113,34 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
     }
     __syncthreads();
 
-    // ---- P9: per wave, column tile j = wave of the value axis:
-    //      Ut = T (beta V), Y = A_qk Ut, P = Q~ - A_qk W (T and A_qk fp16, the other side fp16
-    //      hi + lo).
-    //      P does not depend on V: waves 4-7 form it first (matrix cores) while waves 0-3, which
-    //      share their SIMDs, run the conv of v (vector ALU), so the two units overlap ----
+    // ---- P9: the operands of O = Q~ S + A_qk U for phase B, both fp16 in fragment order:
+    //      Q~ = QR e^Gam_n (each wave its own 16 columns: 64 rows x 2 pieces of 8 channels) and
+    //      the six A_qk fragments on or below the diagonal (one per wave 0-5); then per wave,
+    //      column tile j = wave of the value axis, Ut = T (beta V) (T fp16, beta V fp16 hi + lo) ----
+    {
+      _Float16* qdst = reinterpret_cast<_Float16*>(blk + W_QT);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int sl = lane + 64 * q, t = sl >> 1, c8 = 16 * wave + 8 * (sl & 1);
+        float v[8], e[8];
+        ld8(sQ + t * PQ + c8, v);
+        ld8(sEn + (t >> 4) * D + c8, e);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) v[x] *= e[x];
+        *reinterpret_cast<f16x8*>(qdst + frag_offset(t, c8, D)) = to_f16x8(v);
+      }
+      {
+        // fragment f = 2 I + s of [64][64]: wave 0 -> (0, 0), 1 -> (1, 0), 2.. 5 -> (2, 0) .. (3, 1);
+        // waves 6 and 7 write (0, 1) and (1, 1), which lie above the diagonal, as zeros, so that
+        // phase B runs every row tile's product over both k-steps without a branch
+        const int f = wave < 2 ? 2 * wave : wave < 6 ? wave + 2 : 2 * (wave - 6) + 1;
+        const int t = 16 * (f >> 1) + l16, k = 32 * (f & 1) + 8 * lg;
+        const f16x8 z = {};
+        reinterpret_cast<f16x8*>(blk + W_AQK)[f * 64 + lane] = wave < 6 ? ld4x2(sA16 + t * PTB + k, 4) : z;
+      }
+    }
     {
       const int vc = 16 * wave + l16;
-      const bool pfirst = wave >= 4;
-      // A_qk W for row block I; P = QR e^Gam_n - A_qk W is written in place of QR at the end (this
-      // lane owns these elements), after every read of the A_qk planes, which the compiler could
-      // not otherwise move ahead of the writes
-      f32x4 pacc[4];
-      auto p_rows = [&](int I, const f16x8 (&as)[2]) __attribute__((always_inline)) {
-        f32x4 pa = zero4();
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          if (32 * st > 16 * I + 15) continue;  // A_qk is lower triangular
-          pa = mfma2h(as[st], wb[st], pa);
-        }
-        pacc[I] = pa;
-      };
-      auto aqk_rows = [&](int I, f16x8 (&as)[2]) __attribute__((always_inline)) {
-        const int t = 16 * I + l16;  // A_qk row of this lane
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          if (32 * st > 16 * I + 15) continue;
-          const int o = t * PTB + 32 * st + 4 * lg;
-          as[st] = ld4x2(sA16 + o, 16);
-        }
-      };
-      if (pfirst) {
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          f16x8 as[2];
-          aqk_rows(I, as);
-          p_rows(I, as);
-        }
-      }
       // beta V for tokens 32 s + 8 lg + 0..7 of channel vc: the B operand of Ut
       Half8 bv[2];
 #pragma unroll
@@ -1208,54 +1185,6 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 #pragma unroll
       for (int I = 0; I < 4; ++I)
         utd[(wave * 4 + I) * 64 + lane] = f16x4{(_Float16)ut[I][0], (_Float16)ut[I][1], (_Float16)ut[I][2], (_Float16)ut[I][3]};
-      // Ut as the B operand over tokens in accumulator token order (see wb)
-      Half8 ub[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] = ut[2 * st][e];
-          x[e + 4] = ut[2 * st + 1][e];
-        }
-        ub[st] = split16(x);
-      }
-      f16x4* yd = reinterpret_cast<f16x4*>(blk + W_Y);
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        f16x8 as[2];
-        aqk_rows(I, as);
-        f32x4 ya = zero4();
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          if (32 * st > 16 * I + 15) continue;  // A_qk is lower triangular
-          ya = mfma2h(as[st], ub[st], ya);
-        }
-        yd[(I * 8 + wave) * 64 + lane] = f16x4{(_Float16)ya[0], (_Float16)ya[1], (_Float16)ya[2], (_Float16)ya[3]};
-        if (!pfirst) p_rows(I, as);
-      }
-      float qo[16], en[4];
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        en[I] = sEn[I * D + vc];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) qo[4 * I + r] = sQ[(16 * I + 4 * lg + r) * PQ + vc];
-      }
-#pragma unroll
-      for (int I = 0; I < 4; ++I)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sQ[(16 * I + 4 * lg + r) * PQ + vc] = qo[4 * I + r] * en[I] - pacc[I][r];
-      // ---- write this wave's 16 columns of P in fragment order (fp16): 64 rows x 2 pieces of 8
-      //      channels, read back from the wave's own LDS columns ----
-      wave_lds_sync();
-      _Float16* phi = reinterpret_cast<_Float16*>(blk + W_PHI);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int sl = lane + 64 * q, t = sl >> 1, c8 = 16 * wave + 8 * (sl & 1);
-        float v[8];
-        ld8(sQ + t * PQ + c8, v);
-        *reinterpret_cast<f16x8*>(phi + frag_offset(t, c8, D)) = to_f16x8(v);
-      }
     }
     __syncthreads();  // the next task overwrites the staging rows and tables
     cur = nxt;
@@ -1266,23 +1195,16 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 // Phase B: one workgroup per (16-column block of d_v, head, sequence or group of sequences),
 // sequential over chunks.
 // Waves 0-3 form U = Ut - W S for row tile I = wave and then update state row tiles wave and
-// wave + 4; waves 4-7 form O = P S + Y for row tile I = wave - 4 and, while the state is
-// updated, store it and load their P and Y of two chunks later into registers.  Waves 8-11 only
+// wave + 4; waves 4-7 form O = Q~ S + A_qk U for row tile I = wave - 4, store it and load their
+// Q~ and A_qk of two chunks later into registers.  Waves 8-11 only
 // move data: they copy the tiles that waves 0-3 read (W, Ut, K~^T, e^Gam_C) straight into LDS
 // ahead of use and touch later chunks so that they are in L2.
 // ---------------------------------------------------------------------------------------------
-// Operands the output waves (4-7) keep in registers: P hi / lo of their row tile and their Y tile.
+// Operands the output waves (4-7) keep in registers: their row tile of Q~ and of A_qk.
 struct OpTiles {
-  f16x8 x0[4];  // P (fp16), row tile I = wave - 4 (4 k-steps)
-  f16x4 y;      // Y tile (I, column tile vb), fp16
+  f16x8 x0[4];  // Q~ (fp16), row tile I = wave - 4 (4 k-steps over the key channels)
+  f16x8 aq[2];  // A_qk (fp16), row tile I (2 k-steps over the tokens; zeros above the diagonal)
 };
-
-__device__ __forceinline__ void load_out_tiles(const unsigned char* blk, int I, int lane, int vb, OpTiles& o) {
-  const f16x8* x0p = reinterpret_cast<const f16x8*>(blk + W_PHI) + (I * 4) * 64 + lane;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) o.x0[s] = x0p[s * 64];
-  o.y = reinterpret_cast<const f16x4*>(blk + W_Y)[(I * 8 + vb) * 64 + lane];
-}
 
 // Direct global -> LDS copies (gfx950 global_load_lds): lane l's bytes land at lds + l * size.
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
@@ -1342,16 +1264,21 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
                        (long long)st.tok0[s_first]}
               : Cursor{s_first, 0, NCu, a.T, (long long)s_first * a.T};
   };
+  // Every sequence of the table has at least one chunk (the host leaves empty sequences out), so a
+  // cursor that moves one chunk at a time crosses at most one sequence boundary per step: the
+  // advance is one select over values loaded unconditionally, with no loop or branch, which keeps
+  // the compiler's memory-counter waits in the role loops per load.
   auto locate = [&](Cursor& cu, int g) -> ChunkRef {
     if (!VL) return ChunkRef{s_first, g, NCu, s_first * NCu, (long long)s_first * a.T, a.T};
     const int gc = g0 + g;
-    while (gc >= cu.next && cu.s + 1 < s_end) {
-      ++cu.s;
-      cu.base = cu.next;
-      cu.next = st.chunk0[cu.s + 1];
-      cu.tok0 = st.tok0[cu.s];
-      cu.len = st.tok0[cu.s + 1] - st.tok0[cu.s];
-    }
+    const bool adv = gc >= cu.next && cu.s + 1 < s_end;
+    const int s1 = min(cu.s + 1, s_end - 1);
+    const int nb = st.chunk0[s1], nn = st.chunk0[s1 + 1], t0 = st.tok0[s1], t1 = st.tok0[s1 + 1];
+    cu.s = adv ? s1 : cu.s;
+    cu.base = adv ? nb : cu.base;
+    cu.next = adv ? nn : cu.next;
+    cu.tok0 = adv ? (long long)t0 : cu.tok0;
+    cu.len = adv ? t1 - t0 : cu.len;
     return ChunkRef{cu.s, gc - cu.base, cu.next - cu.base, cu.base, cu.tok0, cu.len};
   };
   // tile block of a chunk: sequence-major, then head, then chunk
@@ -1419,7 +1346,10 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
     issue_wu(0);
     issue_k(0);
     if (NG > 1) issue_wu(1);
-    if (NG > 2) touch_chunk(2);
+    if (NG > 2) {
+      (void)locate(cur_t, 1);  // the touch cursor starts at chunk 2: step it through chunk 1 first
+      touch_chunk(2);
+    }
     KDA_WAIT_VMCNT(0);
     for (int ci = 0; ci < NG; ++ci) {
       if (ci >= 2) {
@@ -1612,19 +1542,33 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
       }
     }
   } else {
-    // O = P S + Y for row tile I = wave - 4 from P and Y in registers; after barrier (b) the rows
-    // are stored and the register set is refilled with the tiles of chunk ci + 2 (two sets
-    // alternate, so no loaded value is copied, and a load has two chunks to arrive).  Rows past
-    // the end of the sequence go to a scratch slot after o, so that every lane issues the same
-    // stores; the last chunk's tiles are loaded again in place of chunks past the end.
+    // O = Q~ S + A_qk U for row tile I = wave - 4, with Q~ and A_qk in registers: Q~ S between
+    // barriers (a) and (b) (the state operand is replaced after (b)), A_qk U after (b), where U
+    // is in LDS until the U waves replace it after the next barrier (a), so the matrix-core work of
+    // the output waves is split between the two halves of the chunk.  Then the rows are stored and
+    // the register set is refilled with the tiles of chunk ci + 2 (two sets alternate, so no
+    // loaded value is copied, and a load has two chunks to arrive).  The loop body has no branch,
+    // which keeps the compiler's memory-counter waits per load (a branch there made it wait for
+    // every outstanding load and store at the top of each chunk).  Rows past the end of the
+    // sequence go to a scratch slot after o, so that every lane issues the same stores; the last
+    // chunk's tiles are loaded again in place of chunks past the end.
     const int I = wave - 4;
     _Float16* scratch = ows + (VL ? (long long)st.tok0[st.n] : (long long)a.B * a.T) * HD + lane * 4;
     Cursor cur_o = cursor0(), cur_l = cursor0();
+    auto load_tiles = [&](int c, OpTiles& o) __attribute__((always_inline)) {
+      const unsigned char* blk = chunk_ptr(cur_l, c);
+      const f16x8* x0p = reinterpret_cast<const f16x8*>(blk + W_QT) + (I * 4) * 64 + lane;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) o.x0[s] = x0p[s * 64];
+      const f16x8* ap = reinterpret_cast<const f16x8*>(blk + W_AQK) + (I * 2) * 64 + lane;
+      o.aq[0] = ap[0];
+      o.aq[1] = ap[64];
+    };
     auto chunk_o = [&](int ci, OpTiles& cur) __attribute__((always_inline)) {
       const ChunkRef rc = locate(cur_o, ci);
       lds_barrier();  // (a)
       // the state's fp16 hi part only: O is not fed back into the state, so its rounding does not
-      // accumulate over chunks, and P itself is fp16
+      // accumulate over chunks, and Q~ itself is fp16
       f32x4 oa = zero4(), ob = zero4();
 #pragma unroll
       for (int s = 0; s < 4; s += 2) {
@@ -1633,22 +1577,29 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
         oa = mfma16(cur.x0[s], s0, oa);
         ob = mfma16(cur.x0[s + 1], s1, ob);
       }
-      f32x4 o;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = (oa[r] + ob[r]) + (float)cur.y[r];
+      asm volatile("" : "+v"(oa), "+v"(ob));  // both products ahead of barrier (b)
       lds_barrier();  // (b)
+      // A_qk U with U split into fp16 hi + lo (A_qk's fragments above the diagonal are zeros)
+      f32x4 oc = zero4(), od = zero4();
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const f16x8 uh = *reinterpret_cast<const f16x8*>(sUhi + l16 * PVT + 32 * s + 8 * lg);
+        const f16x8 ul = *reinterpret_cast<const f16x8*>(sUlo + l16 * PVT + 32 * s + 8 * lg);
+        oc = mfma16(cur.aq[s], uh, oc);
+        od = mfma16(cur.aq[s], ul, od);
+      }
       const int c0 = rc.ci * C, L = min(C, rc.len - c0);
       _Float16* op = ows + ((rc.tok0 + c0) * H + h) * D + vb * NVB + l16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * I + 4 * lg + r;
-        *(t < L ? op + (long long)t * HD : scratch + r) = (_Float16)o[r];
+        *(t < L ? op + (long long)t * HD : scratch + r) = (_Float16)((oa[r] + ob[r]) + (oc[r] + od[r]));
       }
-      load_out_tiles(chunk_ptr(cur_l, min(ci + 2, NG - 1)), I, lane, vb, cur);
+      load_tiles(min(ci + 2, NG - 1), cur);
     };
     OpTiles ta, tb2;
-    load_out_tiles(chunk_ptr(cur_l, 0), I, lane, vb, ta);
-    load_out_tiles(chunk_ptr(cur_l, min(1, NG - 1)), I, lane, vb, tb2);
+    load_tiles(0, ta);
+    load_tiles(min(1, NG - 1), tb2);
     int ci = 0;
     for (; ci + 1 < NG; ci += 2) {
       chunk_o(ci, ta);

@@ -145,7 +145,7 @@ kda_status kda_prefill(const kda_layer_desc* desc, int32_t B, int32_t T, const v
  * and results are those of kda_prefill; no device memory is allocated or
  * freed.  A request whose scratch, kda_prefill_workspace_size(desc, B, T),
  * exceeds 64 MiB returns KDA_ERR_UNSUPPORTED before anything runs (at H = 32,
- * B = 1 that is T up to 1344 tokens; chain calls for longer prompts).  Every
+ * B = 1 that is T up to 1472 tokens; chain calls for longer prompts).  Every
  * call on one GPU uses the same array: calls that overlap in time on one GPU
  * (on different streams, or from different threads) race and must not be
  * issued; calls in one stream's order are safe.

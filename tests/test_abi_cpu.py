@@ -244,21 +244,21 @@ def test_timing_read_without_records_is_empty():
 
 
 def test_noalloc_prefill_refuses_requests_beyond_its_scratch():
-    # the fixed scratch holds 64 MiB per GPU: at H = 32, d = 128 (matrix-core path) 1344 tokens of one
-    # sequence fit, 1345 do not; the refusal comes before any HIP call or pointer check
+    # the fixed scratch holds 64 MiB per GPU: at H = 32, d = 128 (matrix-core path) 1472 tokens of one
+    # sequence fit, 1473 do not; the refusal comes before any HIP call or pointer check
     lib = abi.load()
     d = desc(num_heads=32, head_dim_k=128, head_dim_v=128, chunk_size=64, io_dtype=abi.KDA_BF16)
-    assert lib.kda_prefill_workspace_size(ctypes.byref(d), 1, 1344) <= (64 << 20)
-    assert lib.kda_prefill_workspace_size(ctypes.byref(d), 1, 1345) > (64 << 20)
+    assert lib.kda_prefill_workspace_size(ctypes.byref(d), 1, 1472) <= (64 << 20)
+    assert lib.kda_prefill_workspace_size(ctypes.byref(d), 1, 1473) > (64 << 20)
 
     def call(B, T, ptr=FAKE):
         return lib.kda_prefill_noalloc(ctypes.byref(d), B, T, ptr, ptr, ptr, ptr, ptr, ptr, ptr, None)
 
-    assert call(1, 1345) == abi.KDA_ERR_UNSUPPORTED
+    assert call(1, 1473) == abi.KDA_ERR_UNSUPPORTED
     msg = lib.kda_last_error()
     assert b"kda_prefill_noalloc" in msg and b"more than the library's fixed" in msg
-    assert call(2, 641) == abi.KDA_ERR_UNSUPPORTED
-    assert call(1, 1344, ptr=0) == abi.KDA_ERR_INVALID_ARGUMENT  # within the limit: pointers are checked next
+    assert call(2, 705) == abi.KDA_ERR_UNSUPPORTED
+    assert call(1, 1472, ptr=0) == abi.KDA_ERR_INVALID_ARGUMENT  # within the limit: pointers are checked next
     assert call(0, 5000, ptr=0) == abi.KDA_OK and call(1, 0, ptr=0) == abi.KDA_OK  # empty calls are no-ops
     assert lib.kda_prefill_noalloc(ctypes.byref(desc(gate_lower_bound=math.nan)), 1, 8, FAKE, FAKE, FAKE, FAKE,
                                    FAKE, FAKE, FAKE, None) == abi.KDA_ERR_INVALID_ARGUMENT

@@ -33,7 +33,7 @@ def _run(wl, inp, S0, C0, noalloc):
 
 
 def test_noalloc_prefill_matches_workspace_prefill_twice():
-    cases = [I.WORKLOADS["prefill_t4096"].with_(T=1344, seed=80),          # the largest call the scratch holds
+    cases = [I.WORKLOADS["prefill_t4096"].with_(T=1472, seed=80),          # the largest call the scratch holds
              I.WORKLOADS["prefill_t4096"].with_(T=130, H=4, B=3, seed=81)]  # then a smaller one
     for wl in cases:
         say(f"case kda_prefill_noalloc B={wl.B} T={wl.T} H={wl.H} vs kda_prefill with a workspace")
