@@ -1258,27 +1258,32 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
   struct Cursor {
     int s, base, next, len;
     long long tok0;
+    int nn, nt;  // chunk0 and tok0 of sequence s + 2 (the end of s + 1), loaded one step ahead
   };
   auto cursor0 = [&]() {
+    const int s2 = min(s_first + 2, s_end);
     return VL ? Cursor{s_first, st.chunk0[s_first], st.chunk0[s_first + 1], st.tok0[s_first + 1] - st.tok0[s_first],
-                       (long long)st.tok0[s_first]}
-              : Cursor{s_first, 0, NCu, a.T, (long long)s_first * a.T};
+                       (long long)st.tok0[s_first], st.chunk0[s2], st.tok0[s2]}
+              : Cursor{s_first, 0, NCu, a.T, (long long)s_first * a.T, 0, 0};
   };
   // Every sequence of the table has at least one chunk (the host leaves empty sequences out), so a
   // cursor that moves one chunk at a time crosses at most one sequence boundary per step: the
-  // advance is one select over values loaded unconditionally, with no loop or branch, which keeps
-  // the compiler's memory-counter waits in the role loops per load.
+  // advance is one select over values the previous step loaded (the next sequence starts where this
+  // one ends), with no loop or branch, which keeps the compiler's memory-counter waits in the role
+  // loops per load, and no step waits for its own table reads.
   auto locate = [&](Cursor& cu, int g) -> ChunkRef {
     if (!VL) return ChunkRef{s_first, g, NCu, s_first * NCu, (long long)s_first * a.T, a.T};
     const int gc = g0 + g;
     const bool adv = gc >= cu.next && cu.s + 1 < s_end;
-    const int s1 = min(cu.s + 1, s_end - 1);
-    const int nb = st.chunk0[s1], nn = st.chunk0[s1 + 1], t0 = st.tok0[s1], t1 = st.tok0[s1 + 1];
-    cu.s = adv ? s1 : cu.s;
-    cu.base = adv ? nb : cu.base;
-    cu.next = adv ? nn : cu.next;
-    cu.tok0 = adv ? (long long)t0 : cu.tok0;
-    cu.len = adv ? t1 - t0 : cu.len;
+    const long long t0 = cu.tok0 + cu.len;
+    cu.s = adv ? cu.s + 1 : cu.s;
+    cu.base = adv ? cu.next : cu.base;
+    cu.len = adv ? (int)(cu.nt - t0) : cu.len;
+    cu.tok0 = adv ? t0 : cu.tok0;
+    cu.next = adv ? cu.nn : cu.next;
+    const int s2 = min(cu.s + 2, s_end);
+    cu.nn = st.chunk0[s2];
+    cu.nt = st.tok0[s2];
     return ChunkRef{cu.s, gc - cu.base, cu.next - cu.base, cu.base, cu.tok0, cu.len};
   };
   // tile block of a chunk: sequence-major, then head, then chunk
@@ -1492,11 +1497,11 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
     // U = Ut - W S for row tile I = wave, as the split B operand [column][token]
     const int I = wave;
     Cursor cur_s = cursor0();
-    f32x4 Snext[2];  // the next sequence's state, loaded during the current one's last chunk
+    f32x4 Snext[2];  // the next sequence's state, loaded during the current one's first chunk
     for (int ci = 0; ci < NG; ++ci) {
       const ChunkRef rc = locate(cur_s, ci);
       const bool seq_last = rc.ci == rc.nc - 1, more = ci + 1 < NG;
-      if (seq_last && more) {
+      if (rc.ci == 0 && rc.s + 1 < s_end) {
         const float* si = s_in(rc.s + 1);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -1528,17 +1533,19 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
       state_update(kbuf(ci));
       if (seq_last) {
         // the sequence's final state; the next sequence starts from its own slot's state (its
-        // operand replaces the one state_update just wrote, before barrier (a) publishes it)
-        float* so = s_out(rc.s);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) so[(16 * (wave + 4 * u) + 4 * lg + r) * D] = Sacc[u][r];
+        // operand replaces the one state_update just wrote, before barrier (a) publishes it).  The
+        // swap comes before the stores, so that waiting for the prefetched state never waits for them.
+        const f32x4 fin[2] = {Sacc[0], Sacc[1]};
         if (more) {
           Sacc[0] = Snext[0];
           Sacc[1] = Snext[1];
           write_state_operand();
         }
+        float* so = s_out(rc.s);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) so[(16 * (wave + 4 * u) + 4 * lg + r) * D] = fin[u][r];
       }
     }
   } else {
