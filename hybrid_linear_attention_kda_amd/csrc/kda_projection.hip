@@ -25,6 +25,7 @@ constexpr int PJ_COLS = 128;   // output columns per workgroup
 constexpr int PJ_NT = 256;
 constexpr int PJ_PB = kProjRank + 8;    // LDS pitch of a weight row (bf16), spreads the banks
 constexpr int PJ_XCD = 8;               // L2 domains the workgroups are dealt over, round robin
+constexpr int PJ_CB = 8;                // 128-column blocks one low-rank workgroup walks
 
 __device__ __forceinline__ f32x4 pj_mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -32,6 +33,18 @@ __device__ __forceinline__ f32x4 pj_mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ void pj_store(float* p, float v) { *p = v; }
 __device__ __forceinline__ void pj_store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+// four consecutive outputs of one token through a buffer resource (byte offset; out of range: dropped)
+template <typename OT>
+__device__ __forceinline__ void pj_buffer_store4(__amdgpu_buffer_rsrc_t r, int off, f32x4 v);
+template <>
+__device__ __forceinline__ void pj_buffer_store4<float>(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), r, off, 0, 0);
+}
+template <>
+__device__ __forceinline__ void pj_buffer_store4<bf16_t>(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
+  const __attribute__((ext_vector_type(2))) unsigned u = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  __builtin_amdgcn_raw_buffer_store_b64(u, r, off, 0, 0);
+}
 // four consecutive outputs of one token
 __device__ __forceinline__ void pj_store4(float* p, f32x4 v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
@@ -45,40 +58,47 @@ __device__ __forceinline__ void pj_store4(bf16_t* p, f32x4 v) {
 
 // out[T, HD] = act[T, R] . W^T for W [HD, R] (a Linear weight), act the fp32 rank activations
 // (columns which*R .. which*R + R - 1 of the workspace rows, leading dimension ld), f for which = 0
-// and g for which = 1.  A workgroup multiplies one 64-token tile by one 128-column block of W held
-// in LDS.  The product is taken transposed (out^T tile = W tile . act^T) so that each lane ends
-// with four consecutive output columns of one token and stores them directly.
+// and g for which = 1.  A workgroup keeps one 64-token tile of activations in registers (split into
+// bf16 hi + lo once) and walks up to PJ_CB consecutive 128-column blocks of W: block j + 1 is loaded
+// into registers while block j is multiplied from LDS, then written into the other of two LDS
+// buffers.  The product is taken transposed (out^T tile = W tile . act^T) so that each lane ends
+// with four consecutive output columns of one token; the stores go through a buffer resource that
+// ends at row T, so rows past the end are dropped by the hardware and the loop has no branch.
 //
 // Workgroup b runs on L2 domain b % 8 and takes a row tile = b % 8 modulo 8, so one domain's L2
 // holds the activations of its own row tiles only, beside the 2 MB of weights; within a domain
-// the (column block, which) pairs run fastest.  The workgroups of column block 0 of f also write
+// the (column group, which) pairs run fastest.  The workgroups of column group 0 of f also write
 // beta = sigmoid(b x) for their tile.
+// two workgroups per CU by LDS (two weight buffers), so two waves per SIMD: the register budget
+// that leaves keeps the next block's weights in registers without spilling them
 template <typename OT>
-__global__ __launch_bounds__(PJ_NT) void kda_proj_lowrank_kernel(const float* __restrict__ act, int ld, int T,
+__global__ __launch_bounds__(PJ_NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void kda_proj_lowrank_kernel(const float* __restrict__ act, int ld, int T,
                                                                  int HD, int H, const bf16_t* __restrict__ w_fb,
                                                                  const bf16_t* __restrict__ w_gb, OT* __restrict__ f,
                                                                  OT* __restrict__ g, OT* __restrict__ beta) {
   constexpr int R = kProjRank;
-  __shared__ __align__(16) __bf16 sW[PJ_COLS * PJ_PB];
-  const int ncb2 = 2 * (HD / PJ_COLS);
+  __shared__ __align__(16) __bf16 sW[2][PJ_COLS * PJ_PB];
+  const int ncb = HD / PJ_COLS, ncg = (ncb + PJ_CB - 1) / PJ_CB;
   const int xcd = blockIdx.x % PJ_XCD, k = blockIdx.x / PJ_XCD;
-  const int r0 = ((k / ncb2) * PJ_XCD + xcd) * PJ_ROWS;
+  const int r0 = ((k / (2 * ncg)) * PJ_XCD + xcd) * PJ_ROWS;
   if (r0 >= T) return;  // the spare workgroups of the last domains
-  const int which = k % 2, c0 = ((k % ncb2) / 2) * PJ_COLS;
+  const int which = k % 2, cb0 = ((k % (2 * ncg)) / 2) * PJ_CB;
+  const int nb = min(PJ_CB, ncb - cb0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const bf16_t* W = which == 0 ? w_fb : w_gb;
   OT* out = which == 0 ? f : g;
 
-  // the weight rows of this column block, 16-byte pieces (16 per row): all loads, then the LDS writes
+  // the weight rows of a column block, 16-byte pieces (16 per row)
   constexpr int NW = PJ_COLS * (R / 8) / PJ_NT;
-  uint4 wv[NW];
+  const bf16_t* wsrc = W + (long long)(tid / (R / 8)) * R + (tid % (R / 8)) * 8;  // piece j: + j * (PJ_NT / 16) rows
+  const int wdst = (tid / (R / 8)) * PJ_PB + (tid % (R / 8)) * 8;
+  constexpr int WROWS = PJ_NT / (R / 8);
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 wv[NW];
 #pragma unroll
-  for (int j = 0; j < NW; ++j) {
-    const int i = tid + j * PJ_NT, row = i / (R / 8), seg = i % (R / 8);
-    wv[j] = *reinterpret_cast<const uint4*>(W + (long long)(c0 + row) * R + seg * 8);
-  }
-  // this wave's 16 activation rows (rows past T read row T-1 and are not stored)
+  for (int j = 0; j < NW; ++j) wv[j] = *reinterpret_cast<const u32x4*>(wsrc + ((long long)cb0 * PJ_COLS + j * WROWS) * R);
+  // this wave's 16 activation rows (rows past T read row T-1; their outputs are dropped)
   const int trow = r0 + 16 * wave + l16;
   const float* ap = act + (long long)min(trow, T - 1) * ld + which * R + 8 * lg;
   float4 xv[R / 32][2];
@@ -88,10 +108,7 @@ __global__ __launch_bounds__(PJ_NT) void kda_proj_lowrank_kernel(const float* __
     xv[s][1] = *reinterpret_cast<const float4*>(ap + 32 * s + 4);
   }
 #pragma unroll
-  for (int j = 0; j < NW; ++j) {
-    const int i = tid + j * PJ_NT, row = i / (R / 8), seg = i % (R / 8);
-    *reinterpret_cast<uint4*>(sW + row * PJ_PB + seg * 8) = wv[j];
-  }
+  for (int j = 0; j < NW; ++j) *reinterpret_cast<u32x4*>(&sW[0][wdst + j * WROWS * PJ_PB]) = wv[j];
   // split B operands: fp32 activations as bf16 hi + lo
   bf16x8 xhi[R / 32], xlo[R / 32];
 #pragma unroll
@@ -105,25 +122,39 @@ __global__ __launch_bounds__(PJ_NT) void kda_proj_lowrank_kernel(const float* __
       xlo[s][e] = (__bf16)(x[e] - (float)hi);
     }
   }
+  // output rows r0 .. T-1 of this workgroup's tile; lane: columns 16 ct + 4 lg .. + 3 of token trow
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      out + (long long)r0 * HD, 0, (int)((long long)min(PJ_ROWS, T - r0) * HD * (int)sizeof(OT)), 0x00020000);
+  const int obase = ((16 * wave + l16) * HD + 4 * lg) * (int)sizeof(OT);
   __syncthreads();
-  f32x4 acc[PJ_COLS / 16];
+  for (int j = 0; j < nb; ++j) {
+    // the next block (the last one again at the end)
+    u32x4 wn[NW];
+    const long long nrow = (long long)(cb0 + min(j + 1, nb - 1)) * PJ_COLS;
 #pragma unroll
-  for (int ct = 0; ct < PJ_COLS / 16; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < NW; ++q) wn[q] = *reinterpret_cast<const u32x4*>(wsrc + (nrow + q * WROWS) * R);
+    f32x4 acc[PJ_COLS / 16];
 #pragma unroll
-  for (int s = 0; s < R / 32; ++s)
+    for (int ct = 0; ct < PJ_COLS / 16; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const __bf16* sb = sW[j & 1];
 #pragma unroll
-    for (int ct = 0; ct < PJ_COLS / 16; ++ct) {
-      const bf16x8 w = *reinterpret_cast<const bf16x8*>(sW + (16 * ct + l16) * PJ_PB + 32 * s + 8 * lg);
-      acc[ct] = pj_mfma(w, xlo[s], acc[ct]);
-      acc[ct] = pj_mfma(w, xhi[s], acc[ct]);
-    }
-  // lane: output columns 16 ct + 4 lg .. + 3 of token trow
-  if (trow < T) {
-    OT* orow = out + (long long)trow * HD + c0 + 4 * lg;
+    for (int s = 0; s < R / 32; ++s)
 #pragma unroll
-    for (int ct = 0; ct < PJ_COLS / 16; ++ct) pj_store4(orow + 16 * ct, acc[ct]);
+      for (int ct = 0; ct < PJ_COLS / 16; ++ct) {
+        const bf16x8 w = *reinterpret_cast<const bf16x8*>(sb + (16 * ct + l16) * PJ_PB + 32 * s + 8 * lg);
+        acc[ct] = pj_mfma(w, xlo[s], acc[ct]);
+        acc[ct] = pj_mfma(w, xhi[s], acc[ct]);
+      }
+    const int ob = obase + (cb0 + j) * PJ_COLS * (int)sizeof(OT);
+#pragma unroll
+    for (int ct = 0; ct < PJ_COLS / 16; ++ct) pj_buffer_store4<OT>(orsrc, ob + 16 * ct * (int)sizeof(OT), acc[ct]);
+    // buffer (j + 1) & 1 was last read in block j - 1, before the previous barrier
+    __bf16* sn = sW[(j + 1) & 1];
+#pragma unroll
+    for (int q = 0; q < NW; ++q) *reinterpret_cast<u32x4*>(sn + wdst + q * WROWS * PJ_PB) = wn[q];
+    __syncthreads();
   }
-  if (which == 0 && c0 == 0) {
+  if (which == 0 && cb0 == 0) {
     for (int i0 = 0; i0 < PJ_ROWS * H; i0 += 4 * PJ_NT) {
       float z[4];
 #pragma unroll
@@ -456,9 +487,9 @@ hipError_t launch_projection(const ProjArgs& p, hipStream_t s, char* err, size_t
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // per domain ceil(tiles / 8) row tiles, times the (column block, which) pairs
+  // per domain ceil(tiles / 8) row tiles, times the (column group, which) pairs
   const int tiles = (p.T + PJ_ROWS - 1) / PJ_ROWS;
-  const dim3 grid(((tiles + PJ_XCD - 1) / PJ_XCD) * PJ_XCD * 2 * (HD / PJ_COLS));
+  const dim3 grid(((tiles + PJ_XCD - 1) / PJ_XCD) * PJ_XCD * 2 * ((HD / PJ_COLS + PJ_CB - 1) / PJ_CB));
   timing_begin("kda_proj_lowrank_kernel", s);
   if (p.out_type == kBF16)
     kda_proj_lowrank_kernel<bf16_t><<<grid, PJ_NT, 0, s>>>(
