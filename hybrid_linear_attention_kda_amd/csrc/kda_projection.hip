@@ -426,16 +426,40 @@ __global__ __launch_bounds__(G_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
   }
 }
 
-// act [T, ns] = sum over the K pieces of part [p] [T, np] (np = g_pitch(ns))
+// act [T, ns] = sum over the K pieces of part [p] [T, np] (np = g_pitch(ns)): a wave per row, four
+// consecutive columns per lane (16-byte loads; every piece's load issued before the sums)
 __global__ __launch_bounds__(256) void kda_proj_act_reduce_kernel(const float* __restrict__ part, int pieces,
                                                                  int T, int ns, float* __restrict__ act) {
-  const int np = g_pitch(ns);
-  const long long n = (long long)T * ns, pstride = (long long)T * np;
-  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
-    const long long t = i / ns, c = i - t * ns;
-    float v = 0.f;
-    for (int p = 0; p < pieces; ++p) v += part[p * pstride + t * np + c];
-    act[i] = v;
+  const int np = g_pitch(ns), nq = np / 4;
+  const long long pstride = (long long)T * np;
+  const int lane = threadIdx.x & 63;
+  for (long long t = blockIdx.x * 4LL + (threadIdx.x >> 6); t < T; t += gridDim.x * 4LL) {
+    for (int c4 = lane; c4 < nq; c4 += 64) {
+      const float* src = part + t * np + 4 * c4;
+      float4 x[G_KSPLIT];
+#pragma unroll
+      for (int p = 0; p < G_KSPLIT; ++p)
+        x[p] = *reinterpret_cast<const float4*>(src + min(p, pieces - 1) * pstride);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int p = 0; p < G_KSPLIT; ++p) {
+        if (p < pieces) {
+          v.x += x[p].x;
+          v.y += x[p].y;
+          v.z += x[p].z;
+          v.w += x[p].w;
+        }
+      }
+      float* dst = act + t * ns + 4 * c4;
+      if ((ns & 3) == 0) {
+        *reinterpret_cast<float4*>(dst) = v;  // 4 c4 < np = ns
+      } else {
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (4 * c4 + j < ns) dst[j] = vv[j];
+      }
+    }
   }
 }
 
@@ -479,10 +503,9 @@ hipError_t launch_projection(const ProjArgs& p, hipStream_t s, char* err, size_t
     if (e != hipSuccess) return e;
   }
   {
-    const long long n = (long long)p.T * NS;
     timing_begin("kda_proj_act_reduce_kernel", s);
-    kda_proj_act_reduce_kernel<<<(unsigned)std::min<long long>((n + 255) / 256, 2048), 256, 0, s>>>(part, gi.ksplit,
-                                                                                                   p.T, NS, act);
+    kda_proj_act_reduce_kernel<<<(unsigned)std::min<long long>((p.T + 3) / 4, 4096), 256, 0, s>>>(part, gi.ksplit,
+                                                                                                 p.T, NS, act);
     timing_end(s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
