@@ -256,6 +256,7 @@ __global__ __launch_bounds__(RecLayout<D>::NT) void kda_recurrent_kernel(LayerAr
 //   state[b]      <- snaps[b, m-1]                      (untouched when m == 0)
 //   conv_state[b] <- last W-1 rows of (conv_state[b] || qkv[b, :m])
 // grid.x splits a sequence's state into float4 ranges, grid.y = sequence.
+constexpr int kRollbackPer = 8;  // 16-byte pieces of the state copy per lane
 template <typename IO>
 __global__ __launch_bounds__(256) void kda_rollback_kernel(RollbackArgs a) {
   const int lb = blockIdx.y;
@@ -264,10 +265,21 @@ __global__ __launch_bounds__(256) void kda_rollback_kernel(RollbackArgs a) {
   const int b = a.B0 + lb;
   const long long HDD = (long long)a.H * a.D * a.D;
   const long long n4 = HDD / 4;
-  const float4* src = reinterpret_cast<const float4*>(a.snaps + ((long long)b * a.T_d + (m - 1)) * HDD);
-  float4* dst = reinterpret_cast<float4*>(a.state + (long long)b * HDD);
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  const f32x4v* __restrict__ src = reinterpret_cast<const f32x4v*>(a.snaps + ((long long)b * a.T_d + (m - 1)) * HDD);
+  f32x4v* __restrict__ dst = reinterpret_cast<f32x4v*>(a.state + (long long)b * HDD);
   const long long stride = (long long)gridDim.x * blockDim.x;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) dst[i] = src[i];
+  // the launch gives every lane at most kRollbackPer 16-byte pieces: all loads in flight before the
+  // first store (the snapshot is read once, the state written once: non-temporal both ways)
+  const long long i0 = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  f32x4v v[kRollbackPer];
+#pragma unroll
+  for (int k = 0; k < kRollbackPer; ++k) v[k] = __builtin_nontemporal_load(src + min(i0 + k * stride, n4 - 1));
+#pragma unroll
+  for (int k = 0; k < kRollbackPer; ++k) {
+    const long long i = i0 + k * stride;
+    if (i < n4) __builtin_nontemporal_store(v[k], dst + i);
+  }
 
   const long long Cqkv = 3LL * a.H * a.D;
   const int Wm1 = a.W - 1;
@@ -420,7 +432,7 @@ hipError_t launch_recurrent(const LayerArgs& a, int io, int ot, hipStream_t s) {
 
 hipError_t launch_rollback(const RollbackArgs& a, int io, hipStream_t s) {
   const long long n4 = (long long)a.H * a.D * a.D / 4;
-  int gx = (int)((n4 + 256 * 8 - 1) / (256 * 8));  // 8 float4 per lane
+  int gx = (int)((n4 + 256 * kRollbackPer - 1) / (256 * kRollbackPer));  // kRollbackPer float4 per lane
   if (gx < 1) gx = 1;
   dim3 grid(gx, a.nB), block(256);
   timing_begin("kda_rollback_kernel", s);
