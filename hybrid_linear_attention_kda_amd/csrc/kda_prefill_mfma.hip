@@ -60,6 +60,8 @@
 // workgroups, so o goes to the workspace as fp16 (11 significant bits; |o| stays far inside
 // fp16's range) and a third, bandwidth-bound kernel applies the norm,
 // weight and gate.  Phase B's loader waves also write the new conv state.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -1562,57 +1564,66 @@ __global__ __launch_bounds__(NTB) void kda_chunk_state_kernel(LayerArgs a, SeqTa
     const int I = wave - 4;
     _Float16* scratch = ows + (VL ? (long long)st.tok0[st.n] : (long long)a.B * a.T) * HD + lane * 4;
     Cursor cur_o = cursor0(), cur_l = cursor0();
-    auto load_tiles = [&](int c, OpTiles& o) __attribute__((always_inline)) {
-      const unsigned char* blk = chunk_ptr(cur_l, c);
-      const f16x8* x0p = reinterpret_cast<const f16x8*>(blk + W_QT) + (I * 4) * 64 + lane;
+    // Row tiles 0 and 1 see tokens 0-31 only (A_qk's second k-step is zero for them): the loop is
+    // instantiated for them with one k-step of A_qk U, chosen once, outside the loop
+    auto run = [&](auto low) __attribute__((always_inline)) {
+      constexpr int NKA = decltype(low)::value ? 1 : 2;  // k-steps of A_qk U
+      auto load_tiles = [&](int c, OpTiles& o) __attribute__((always_inline)) {
+        const unsigned char* blk = chunk_ptr(cur_l, c);
+        const f16x8* x0p = reinterpret_cast<const f16x8*>(blk + W_QT) + (I * 4) * 64 + lane;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) o.x0[s] = x0p[s * 64];
-      const f16x8* ap = reinterpret_cast<const f16x8*>(blk + W_AQK) + (I * 2) * 64 + lane;
-      o.aq[0] = ap[0];
-      o.aq[1] = ap[64];
+        for (int s = 0; s < 4; ++s) o.x0[s] = x0p[s * 64];
+        const f16x8* ap = reinterpret_cast<const f16x8*>(blk + W_AQK) + (I * 2) * 64 + lane;
+#pragma unroll
+        for (int s = 0; s < NKA; ++s) o.aq[s] = ap[s * 64];
+      };
+      auto chunk_o = [&](int ci, OpTiles& cur) __attribute__((always_inline)) {
+        const ChunkRef rc = locate(cur_o, ci);
+        lds_barrier();  // (a)
+        // the state's fp16 hi part only: O is not fed back into the state, so its rounding does not
+        // accumulate over chunks, and Q~ itself is fp16
+        f32x4 oa = zero4(), ob = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; s += 2) {
+          const f16x8 s0 = *reinterpret_cast<const f16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
+          const f16x8 s1 = *reinterpret_cast<const f16x8*>(sShi + l16 * PST + 32 * (s + 1) + 8 * lg);
+          oa = mfma16(cur.x0[s], s0, oa);
+          ob = mfma16(cur.x0[s + 1], s1, ob);
+        }
+        asm volatile("" : "+v"(oa), "+v"(ob));  // both products ahead of barrier (b)
+        lds_barrier();  // (b)
+        // A_qk U with U split into fp16 hi + lo
+        f32x4 oc = zero4(), od = zero4();
+#pragma unroll
+        for (int s = 0; s < NKA; ++s) {
+          const f16x8 uh = *reinterpret_cast<const f16x8*>(sUhi + l16 * PVT + 32 * s + 8 * lg);
+          const f16x8 ul = *reinterpret_cast<const f16x8*>(sUlo + l16 * PVT + 32 * s + 8 * lg);
+          oc = mfma16(cur.aq[s], uh, oc);
+          od = mfma16(cur.aq[s], ul, od);
+        }
+        const int c0 = rc.ci * C, L = min(C, rc.len - c0);
+        _Float16* op = ows + ((rc.tok0 + c0) * H + h) * D + vb * NVB + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * I + 4 * lg + r;
+          *(t < L ? op + (long long)t * HD : scratch + r) = (_Float16)((oa[r] + ob[r]) + (oc[r] + od[r]));
+        }
+        load_tiles(min(ci + 2, NG - 1), cur);
+      };
+      OpTiles ta, tb2;
+      load_tiles(0, ta);
+      load_tiles(min(1, NG - 1), tb2);
+      int ci = 0;
+      for (; ci + 1 < NG; ci += 2) {
+        chunk_o(ci, ta);
+        chunk_o(ci + 1, tb2);
+      }
+      if (ci < NG) chunk_o(ci, ta);
     };
-    auto chunk_o = [&](int ci, OpTiles& cur) __attribute__((always_inline)) {
-      const ChunkRef rc = locate(cur_o, ci);
-      lds_barrier();  // (a)
-      // the state's fp16 hi part only: O is not fed back into the state, so its rounding does not
-      // accumulate over chunks, and Q~ itself is fp16
-      f32x4 oa = zero4(), ob = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; s += 2) {
-        const f16x8 s0 = *reinterpret_cast<const f16x8*>(sShi + l16 * PST + 32 * s + 8 * lg);
-        const f16x8 s1 = *reinterpret_cast<const f16x8*>(sShi + l16 * PST + 32 * (s + 1) + 8 * lg);
-        oa = mfma16(cur.x0[s], s0, oa);
-        ob = mfma16(cur.x0[s + 1], s1, ob);
-      }
-      asm volatile("" : "+v"(oa), "+v"(ob));  // both products ahead of barrier (b)
-      lds_barrier();  // (b)
-      // A_qk U with U split into fp16 hi + lo (A_qk's fragments above the diagonal are zeros)
-      f32x4 oc = zero4(), od = zero4();
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const f16x8 uh = *reinterpret_cast<const f16x8*>(sUhi + l16 * PVT + 32 * s + 8 * lg);
-        const f16x8 ul = *reinterpret_cast<const f16x8*>(sUlo + l16 * PVT + 32 * s + 8 * lg);
-        oc = mfma16(cur.aq[s], uh, oc);
-        od = mfma16(cur.aq[s], ul, od);
-      }
-      const int c0 = rc.ci * C, L = min(C, rc.len - c0);
-      _Float16* op = ows + ((rc.tok0 + c0) * H + h) * D + vb * NVB + l16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * I + 4 * lg + r;
-        *(t < L ? op + (long long)t * HD : scratch + r) = (_Float16)((oa[r] + ob[r]) + (oc[r] + od[r]));
-      }
-      load_tiles(min(ci + 2, NG - 1), cur);
-    };
-    OpTiles ta, tb2;
-    load_tiles(0, ta);
-    load_tiles(min(1, NG - 1), tb2);
-    int ci = 0;
-    for (; ci + 1 < NG; ci += 2) {
-      chunk_o(ci, ta);
-      chunk_o(ci + 1, tb2);
-    }
-    if (ci < NG) chunk_o(ci, ta);
+    if (I < 2)
+      run(std::true_type());
+    else
+      run(std::false_type());
   }
 }
 
