@@ -1133,8 +1133,8 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
       }
       {
         // fragment f = 2 I + s of [64][64]: wave 0 -> (0, 0), 1 -> (1, 0), 2.. 5 -> (2, 0) .. (3, 1);
-        // waves 6 and 7 write (0, 1) and (1, 1), which lie above the diagonal, as zeros, so that
-        // phase B runs every row tile's product over both k-steps without a branch
+        // waves 6 and 7 write (0, 1) and (1, 1), which lie above the diagonal, as zeros (phase B reads
+        // only fragment (I, 0) for I < 2; the fixed store count keeps this phase free of a branch)
         const int f = wave < 2 ? 2 * wave : wave < 6 ? wave + 2 : 2 * (wave - 6) + 1;
         const int t = 16 * (f >> 1) + l16, k = 32 * (f & 1) + 8 * lg;
         const f16x8 z = {};
@@ -1205,7 +1205,7 @@ __global__ __launch_bounds__(NT) void kda_chunk_prep_kernel(LayerArgs a, SeqTab 
 // Operands the output waves (4-7) keep in registers: their row tile of Q~ and of A_qk.
 struct OpTiles {
   f16x8 x0[4];  // Q~ (fp16), row tile I = wave - 4 (4 k-steps over the key channels)
-  f16x8 aq[2];  // A_qk (fp16), row tile I (2 k-steps over the tokens; zeros above the diagonal)
+  f16x8 aq[2];  // A_qk (fp16), row tile I (2 k-steps over the tokens; 1 for I < 2)
 };
 
 // Direct global -> LDS copies (gfx950 global_load_lds): lane l's bytes land at lds + l * size.
