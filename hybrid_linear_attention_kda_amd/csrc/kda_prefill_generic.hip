@@ -18,7 +18,7 @@
 
 namespace kda {
 
-constexpr int kGenericThreads = 256;
+constexpr int kGenericThreads = 1024;  // four waves per SIMD: the loops below are chains of LDS reads and FMAs
 constexpr int kGenericChunkElems = 4096;  // internal chunk <= 4096 / D keeps LDS within 160 KB
 
 __host__ __device__ constexpr int generic_chunk(int D, int chunk) {
