@@ -13,8 +13,18 @@
 // nothing overflows whatever the decay.  Every contraction is fp32 FMA: this
 // is the path that holds the fp32 tolerance.  The conv / SiLU / L2 / gate
 // prologue and the gated RMSNorm epilogue are fused in.
+//
+// Where (sequence, head) pairs alone would leave most CUs idle and out is fp32, the value columns
+// are split over nvb workgroups per pair (grid.z): each one forms the key side (conv, norms, gate,
+// A_kk, A_qk, W) in full and Ut, U, O and the state for its own D / nvb columns, writes O un-normed
+// into out, and kda_prefill_generic_norm_kernel then applies the gated RMSNorm in place (it needs
+// whole rows of O) and writes the new conv state: conv_state is updated in place, so it is written
+// only once every column block has read the old one.
 #include "kda_device.h"
 #include "kda_launch.h"
+
+#include <algorithm>
+#include <type_traits>
 
 namespace kda {
 
@@ -29,8 +39,27 @@ __host__ __device__ constexpr size_t generic_lds_floats(int D, int Cc) {
   return (size_t)4 * Cc * (D + 1) + (size_t)D * D + (size_t)2 * Cc * (Cc + 1) + Cc + D + 2 * Cc;
 }
 
+// New conv state of head h of one sequence: the last W-1 raw inputs of (conv state || its tokens).
+template <int D, typename IO>
+__device__ void generic_conv_state(const LayerArgs& a, const SeqView& sv, int h, int tid, int nt) {
+  const int H = a.H, W = a.W, T = sv.len;
+  const long long Cqkv = 3LL * H * D, b = sv.slot, tok0 = sv.tok0;
+  const IO* qkv = static_cast<const IO*>(a.qkv);
+  const IO* cin = static_cast<const IO*>(a.conv_in);
+  IO* cs = static_cast<IO*>(a.conv_out);
+  for (int c = tid; c < 3 * D; c += nt) {
+    const long long gc = (long long)(c / D) * H * D + (long long)h * D + (c % D);
+    IO win[kMaxConvWidth - 1];
+    for (int w = 0; w < W - 1; ++w) {
+      const int tt = T - (W - 1) + w;
+      win[w] = tt >= 0 ? qkv[(tok0 + tt) * Cqkv + gc] : cin[(b * Cqkv + gc) * (W - 1) + (W - 1) + tt];
+    }
+    for (int w = 0; w < W - 1; ++w) cs[(b * Cqkv + gc) * (W - 1) + w] = win[w];
+  }
+}
+
 template <int D, typename IO, typename OT>
-__global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(LayerArgs a, SeqTab st, int Cc) {
+__global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(LayerArgs a, SeqTab st, int Cc, int nvb) {
   constexpr int NT = kGenericThreads;
   constexpr int NW = NT / 64;
   constexpr int LP = D + 1;
@@ -40,7 +69,7 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
   float* sk = sq + Cc * LP;         // [Cc][LP]  k, then K exp(Gam_L - Gam)
   float* sv = sk + Cc * LP;         // [Cc][LP]  v, then beta V, Ut, U
   float* sg = sv + Cc * LP;         // [Cc][LP]  g, Gam, beta K exp(Gam), W, O
-  float* sS = sg + Cc * LP;         // [D][D]    state
+  float* sS = sg + Cc * LP;         // [D][DV]   this workgroup's state columns
   float* sAkk = sS + D * D;         // [Cc][AP]
   float* sAqk = sAkk + Cc * AP;     // [Cc][AP]
   float* sbeta = sAqk + Cc * AP;    // [Cc]
@@ -48,6 +77,7 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
   float* snrm = sgl + D;            // [2*Cc]    per-token q / k normalisers
 
   const int h = blockIdx.x, tid = threadIdx.x;
+  const int DV = D / nvb, v0 = blockIdx.z * DV;  // this workgroup's value columns v0 .. v0 + DV - 1
   const int lane = tid & 63, wave = tid >> 6;
   const SeqView sq0 = st.n > 0 ? seq_view<true>(st, blockIdx.y, a.T, 0) : seq_view<false>(st, blockIdx.y, a.T, 0);
   const long long tok0 = sq0.tok0;  // packed token of the sequence's first token
@@ -64,7 +94,7 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
   const IO* cin = static_cast<const IO*>(a.conv_in);
   OT* out = static_cast<OT*>(a.out);
 
-  for (int e = tid; e < D * D; e += NT) sS[e] = a.state_in[bh * D * D + e];
+  for (int e = tid; e < D * DV; e += NT) sS[e] = a.state_in[bh * D * D + (long long)(e / DV) * D + v0 + e % DV];
   const float Ah = expf(a.A_log[h]);
 
   for (int c0 = 0; c0 < T; c0 += Cc) {
@@ -147,11 +177,12 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
       sv[t * LP + i] *= sbeta[t];
     }
     __syncthreads();
-    // -- UT solve by forward substitution: X[i] -= sum_{j<i} A_kk[i,j] X[j]  (X = W | Ut)
+    // -- UT solve by forward substitution: X[i] -= sum_{j<i} A_kk[i,j] X[j]  (X = W | this
+    //    workgroup's columns of Ut)
     for (int i = 1; i < L; ++i) {
-      for (int col = tid; col < 2 * D; col += NT) {
+      for (int col = tid; col < D + DV; col += NT) {
         float* X = col < D ? sg : sv;
-        const int cc = col < D ? col : col - D;
+        const int cc = col < D ? col : v0 + col - D;
         float acc = X[i * LP + cc];
         for (int j = 0; j < i; ++j) acc -= sAkk[i * AP + j] * X[j * LP + cc];
         X[i * LP + cc] = acc;
@@ -159,29 +190,36 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
       __syncthreads();
     }
     // -- U = Ut - W S
-    for (int idx = tid; idx < L * D; idx += NT) {
-      const int i = idx / D, j = idx % D;
+    for (int idx = tid; idx < L * DV; idx += NT) {
+      const int i = idx / DV, jj = idx % DV, j = v0 + jj;
       float acc = sv[i * LP + j];
-      for (int c = 0; c < D; ++c) acc -= sg[i * LP + c] * sS[c * D + j];
+      for (int c = 0; c < D; ++c) acc -= sg[i * LP + c] * sS[c * DV + jj];
       sv[i * LP + j] = acc;
     }
     __syncthreads();
     // -- O = Q exp(Gam) S + A_qk U   (into sg; W is no longer needed)
-    for (int idx = tid; idx < L * D; idx += NT) {
-      const int i = idx / D, j = idx % D;
+    for (int idx = tid; idx < L * DV; idx += NT) {
+      const int i = idx / DV, jj = idx % DV, j = v0 + jj;
       float acc = 0.f;
-      for (int c = 0; c < D; ++c) acc += sq[i * LP + c] * sS[c * D + j];
+      for (int c = 0; c < D; ++c) acc += sq[i * LP + c] * sS[c * DV + jj];
       for (int m = 0; m <= i; ++m) acc += sAqk[i * AP + m] * sv[m * LP + j];
       sg[i * LP + j] = acc;
     }
     __syncthreads();
     // -- S <- Diag(exp(Gam_L)) S + (K exp(Gam_L - Gam))^T U
-    for (int idx = tid; idx < D * D; idx += NT) {
-      const int c = idx / D, j = idx % D;
-      float acc = expf(sgl[c]) * sS[c * D + j];
-      for (int i = 0; i < L; ++i) acc += sk[i * LP + c] * sv[i * LP + j];
-      sS[c * D + j] = acc;
+    for (int idx = tid; idx < D * DV; idx += NT) {
+      const int c = idx / DV, jj = idx % DV;
+      float acc = expf(sgl[c]) * sS[c * DV + jj];
+      for (int i = 0; i < L; ++i) acc += sk[i * LP + c] * sv[i * LP + v0 + jj];
+      sS[c * DV + jj] = acc;
     }
+    if (nvb > 1) {
+      // split columns (out is fp32): O un-normed; the norm kernel finishes the rows
+      for (int idx = tid; idx < L * DV; idx += NT) {
+        const int t = idx / DV, j = v0 + idx % DV;
+        store_as(&out[(tok0 + c0 + t) * H * D + (long long)h * D + j], sg[t * LP + j]);
+      }
+    } else
     // -- gated RMSNorm epilogue (one wave per token)
     for (int t = wave; t < L; t += NW) {
       float oo = 0.f;
@@ -197,20 +235,56 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
     __syncthreads();
   }
 
-  for (int e = tid; e < D * D; e += NT) a.state_out[bh * D * D + e] = sS[e];
-  // new conv state: the last W-1 raw inputs of (conv state || this call's tokens)
-  if (a.conv_out != nullptr) {
-    IO* cs = static_cast<IO*>(a.conv_out);
-    for (int c = tid; c < 3 * D; c += NT) {
-      const long long gc = (long long)(c / D) * H * D + (long long)h * D + (c % D);
-      IO win[kMaxConvWidth - 1];
-      for (int w = 0; w < W - 1; ++w) {
-        const int tt = T - (W - 1) + w;
-        win[w] = tt >= 0 ? qkv[(tok0 + tt) * Cqkv + gc] : cin[(b * Cqkv + gc) * (W - 1) + (W - 1) + tt];
+  for (int e = tid; e < D * DV; e += NT) a.state_out[bh * D * D + (long long)(e / DV) * D + v0 + e % DV] = sS[e];
+  // with split columns the norm kernel writes the conv state (the other blocks still read it)
+  if (a.conv_out != nullptr && nvb == 1) generic_conv_state<D, IO>(a, sq0, h, tid, NT);
+}
+
+// Gated RMSNorm of the un-normed fp32 O rows the split-column kernel left in out, in place, one wave
+// per token row; grid (H, sequences, token slices).  Slice 0 also writes the new conv state.
+constexpr int kGenericNormThreads = 256;
+
+template <int D, typename IO>
+__global__ __launch_bounds__(kGenericNormThreads) void kda_prefill_generic_norm_kernel(LayerArgs a, SeqTab st) {
+  constexpr int NW = kGenericNormThreads / 64;
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const SeqView sv = st.n > 0 ? seq_view<true>(st, blockIdx.y, a.T, 0) : seq_view<false>(st, blockIdx.y, a.T, 0);
+  const int H = a.H;
+  const IO* gin = static_cast<const IO*>(a.g_out);
+  const IO* nw = static_cast<const IO*>(a.norm_w);
+  float* out = static_cast<float*>(a.out);
+  for (int t = blockIdx.z * NW + wave; t < sv.len; t += gridDim.z * NW) {
+    const long long ob = (sv.tok0 + t) * H * D + (long long)h * D;
+    float o[(D + 63) / 64];
+    float oo = 0.f;
+#pragma unroll
+    for (int r = 0; r < (D + 63) / 64; ++r) {
+      const int i = lane + 64 * r;
+      o[r] = i < D ? out[ob + i] : 0.f;
+      oo += o[r] * o[r];
+    }
+    oo = wave_sum(oo);
+    const float rr = rsqrtf(oo / (float)D + a.rms_eps);
+#pragma unroll
+    for (int r = 0; r < (D + 63) / 64; ++r) {
+      const int i = lane + 64 * r;
+      if (i < D) {
+        const float gv = to_f32(gin[ob + i]);
+        out[ob + i] = o[r] * rr * to_f32(nw[i]) / (1.0f + expf(-gv));
       }
-      for (int w = 0; w < W - 1; ++w) cs[(b * Cqkv + gc) * (W - 1) + w] = win[w];
     }
   }
+  if (a.conv_out != nullptr && blockIdx.z == 0) generic_conv_state<D, IO>(a, sv, h, tid, kGenericNormThreads);
+}
+
+// Column blocks per (sequence, head): enough workgroups for the 256 CUs where the pairs alone are
+// too few, and only for fp32 out (it holds the un-normed O); each block keeps at least
+// kGenericThreads / Cc columns so that its (token, column) loops still occupy every lane.
+int generic_column_blocks(int D, int Cc, long long pairs, bool fp32_out) {
+  int nvb = 1;
+  if (!fp32_out) return nvb;
+  while (pairs * nvb < 256 && D % (2 * nvb) == 0 && (D / (2 * nvb)) * Cc >= kGenericThreads) nvb *= 2;
+  return nvb;
 }
 
 template <int D, typename IO, typename OT>
@@ -220,8 +294,24 @@ static hipError_t launch_generic_t(const LayerArgs& a, const SeqTab& st, int Cc,
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
+  const int nseq = st.n > 0 ? st.n : a.B;
+  const int nvb = generic_column_blocks(D, Cc, (long long)a.H * nseq, std::is_same<OT, float>::value);
   timing_begin("kda_prefill_generic_kernel", s);
-  kern<<<dim3(a.H, st.n > 0 ? st.n : a.B), dim3(kGenericThreads), lds, s>>>(a, st, Cc);
+  kern<<<dim3(a.H, nseq, nvb), dim3(kGenericThreads), lds, s>>>(a, st, Cc, nvb);
+  timing_end(s);
+  e = hipGetLastError();
+  if (e != hipSuccess || nvb == 1) return e;
+  // the norm pass: about 1024 workgroups, each slice at least 16 token rows per wave
+  const long long pairs = (long long)a.H * nseq;
+  int maxlen = a.T;
+  if (st.n > 0) {
+    maxlen = 0;
+    for (int i = 0; i < st.n; ++i) maxlen = std::max(maxlen, st.tok0[i + 1] - st.tok0[i]);
+  }
+  int slices = (int)((1024 + pairs - 1) / pairs);
+  slices = std::max(1, std::min(slices, (maxlen + 16 * 4 - 1) / (16 * 4)));
+  timing_begin("kda_prefill_generic_norm_kernel", s);
+  kda_prefill_generic_norm_kernel<D, IO><<<dim3(a.H, nseq, slices), dim3(kGenericNormThreads), 0, s>>>(a, st);
   timing_end(s);
   return hipGetLastError();
 }

@@ -626,6 +626,38 @@ def test_fp32_prefill_head_size_128(T, gate):
     _check("conv_state", cs, ref["conv_state"], 0.0)
 
 
+def test_fp32_prefill_head_size_128_bf16_out():
+    # bf16 out keeps one workgroup per (sequence, head), the RMSNorm fused into the prefill kernel
+    # (fp32 out with few pairs splits the value columns over workgroups and norms in a second pass)
+    wl = I.WORKLOADS["prefill_t4096"].with_(T=70, H=2, B=2, io="f32", seed=13)
+    say("case fp32 io, bf16 out, d=128 H=2 B=2 T=70")
+    inp = I.generate(wl)
+    rng = np.random.default_rng(170)
+    S0 = (rng.standard_normal(inp["state0"].shape) * 0.3).astype(np.float32)
+    C0 = rng.standard_normal(inp["conv_state0"].shape).astype(np.float32)
+    layer = TT.make_layer(wl, inp, DEV, out="bf16")
+    st, cs = _dev_state(wl, inp, S0, C0)
+    out = _gpu_prefill(wl, inp, layer, 0, 70, st, cs, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle_layer(wl, inp, 0, 70, S0, C0)
+    _check("out", out, ref["out"], TOL_BF16_OUT)
+    _check("state", st, ref["state"], TOL["f32"])
+    _check("conv_state", cs, ref["conv_state"], 0.0)
+
+
+def test_fp32_varlen_prefill_head_size_128():
+    # split value columns with the state and conv-state pools updated in place, ragged lengths
+    wl = I.WORKLOADS["prefill_t4096"].with_(H=2, io="f32", seed=23)
+    lens = [0, 1, 33, 70]
+    slots = [1, 3, 0, 2]
+    say(f"case fp32 varlen d=128 H=2 lengths {lens} slots {slots} (pool of 5)")
+    out, st, cs, ref, pool, cpool = _varlen_case(wl, lens, slots, 5, seed=9)
+    _check("out", out, ref["out"], TOL["f32"])
+    _check("state pool", st, ref["state"], TOL["f32"])
+    _check("conv-state pool", cs, ref["conv_state"], 0.0)
+    _check("unnamed slot and empty sequence's slot untouched", st[[4, 1]], pool[[4, 1]], 0.0)
+
+
 # ---------------------------------------------------------------------------
 # Edge cases: the L2 clamp, weak decay over long sequences, a visible query scale
 # ---------------------------------------------------------------------------
