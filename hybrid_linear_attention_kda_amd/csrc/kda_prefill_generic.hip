@@ -30,6 +30,7 @@ namespace kda {
 
 constexpr int kGenericThreads = 1024;  // four waves per SIMD: the loops below are chains of LDS reads and FMAs
 constexpr int kGenericChunkElems = 4096;  // internal chunk <= 4096 / D keeps LDS within 160 KB
+static_assert(kGenericChunkElems <= 4 * kGenericThreads, "the prologue loads a chunk's gate inputs in one batch of four");
 
 __host__ __device__ constexpr int generic_chunk(int D, int chunk) {
   return chunk < kGenericChunkElems / D ? chunk : kGenericChunkElems / D;
@@ -99,27 +100,68 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
 
   for (int c0 = 0; c0 < T; c0 += Cc) {
     const int L = min(Cc, T - c0);
-    // -- prologue: conv (halo from earlier tokens or the conv state), SiLU, gate, beta
-    for (int idx = tid; idx < L * 3 * D; idx += NT) {
-      const int t = idx / (3 * D), c = idx % (3 * D);
+    // -- prologue.  Every load below has a valid (clamped) address and its value is selected
+    //    afterwards, so a thread issues all of a batch before its first use: the chunk costs a few
+    //    memory round trips, not one per token.
+    // gate and beta inputs first (L * D <= 4 * NT: one batch of four per thread)
+    float fv[4], bv;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = min(tid + u * NT, L * D - 1), t = idx / D, i = idx % D;
+      fv[u] = to_f32(fin[(tok0 + c0 + t) * H * D + (long long)h * D + i]) + a.dt_bias[(long long)h * D + i];
+    }
+    bv = to_f32(bin[(tok0 + c0 + min(tid, L - 1)) * H + h]);
+    // conv (halo from earlier tokens or the conv state) and SiLU: a thread takes one of the 3D
+    // channels and a run of tpg consecutive tokens, with its taps and an 8 + 7 value window in
+    // registers; tap k of the eight multiplies token t - 7 + k (taps below 8 - W are zero)
+    {
+      constexpr int KW = kMaxConvWidth;
+      const int G = NT / (3 * D), tpg = (L + G - 1) / G;
+      const int c = tid % (3 * D), grp = tid / (3 * D);
       const int part = c / D, i = c % D;
       const long long gc = (long long)part * H * D + (long long)h * D + i;
-      float y = 0.f;
-      for (int w = 0; w < W; ++w) {
-        const int tt = c0 + t - (W - 1) + w;
-        const float x = tt >= 0 ? to_f32(qkv[(tok0 + tt) * Cqkv + gc])
-                                : to_f32(cin[(b * Cqkv + gc) * (W - 1) + (W - 1) + tt]);
-        y += to_f32(cw[gc * W + w]) * x;
+      float* dst = part == 0 ? sq : part == 1 ? sk : sv;
+      const int ts = grp * tpg, te = min(ts + tpg, L);
+      if (grp < G && ts < te) {
+        float wk[KW];
+#pragma unroll
+        for (int k = 0; k < KW; ++k) {
+          const int w = k - (KW - W);
+          const float v = to_f32(cw[gc * W + max(w, 0)]);
+          wk[k] = w >= 0 ? v : 0.f;
+        }
+        // raw input of token tt of this sequence (tt < -(W-1) meets only zero taps)
+        auto raw = [&](int tt) {
+          const bool from_state = tt < 0 && tt >= -(W - 1);
+          const IO* p = from_state ? cin + (b * Cqkv + gc) * (W - 1) + (W - 1) + tt
+                                   : qkv + (tok0 + min(max(tt, 0), T - 1)) * Cqkv + gc;
+          const float v = to_f32(*p);
+          return tt >= -(W - 1) ? v : 0.f;
+        };
+        float win[KW - 1 + 8];
+#pragma unroll
+        for (int k = 0; k < KW - 1; ++k) win[k] = raw(c0 + ts - (KW - 1) + k);
+        for (int t0 = ts; t0 < te; t0 += 8) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) win[KW - 1 + k] = raw(c0 + t0 + k);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            float y = 0.f;
+#pragma unroll
+            for (int w = 0; w < KW; ++w) y += wk[w] * win[k + w];
+            if (t0 + k < te) dst[(t0 + k) * LP + i] = y / (1.0f + expf(-y));
+          }
+#pragma unroll
+          for (int k = 0; k < KW - 1; ++k) win[k] = win[8 + k];
+        }
       }
-      (part == 0 ? sq : part == 1 ? sk : sv)[t * LP + i] = y / (1.0f + expf(-y));
     }
-    for (int idx = tid; idx < L * D; idx += NT) {
-      const int t = idx / D, i = idx % D;
-      const float fv = to_f32(fin[(tok0 + c0 + t) * H * D + (long long)h * D + i]) +
-                       a.dt_bias[(long long)h * D + i];
-      sg[t * LP + i] = log_decay(a.gate, a.lb, Ah, fv);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = tid + u * NT;
+      if (idx < L * D) sg[(idx / D) * LP + idx % D] = log_decay(a.gate, a.lb, Ah, fv[u]);
     }
-    for (int t = tid; t < L; t += NT) sbeta[t] = to_f32(bin[(tok0 + c0 + t) * H + h]);
+    if (tid < L) sbeta[tid] = bv;
     __syncthreads();
     // -- q/k L2 normalisation (one wave per token), q scale
     for (int t = wave; t < L; t += NW) {
