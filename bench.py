@@ -406,6 +406,7 @@ def main():
     nsets = max(1, args.sets)
 
     wp, wd, wv = I.WORKLOADS["prefill_t4096"], I.WORKLOADS["decode_b64"], I.WORKLOADS["verify_b16"]
+    wf, wt = wp.with_(T=1024, io="f32"), I.WORKLOADS["tiny_fp32"]
     ops = ["prefill", "varlen", "projection", "decode", "verify"] if args.only is None else [args.only]
 
     def strong_layer(lay):
@@ -441,6 +442,18 @@ def main():
                 out=torch.empty((1, wp.T, wp.H * wp.dv), dtype=torch.bfloat16, device=dev),
                 ws=workspace(lay, 1, wp.T)))
         del tok
+        # the fp32 vector-ALU prefill (fp32 io and out) on a 1024-token cut of the same layer shape,
+        # and the small fp32 layer (B=1, T=64, H=2, d=16, chunk 16) through the same path
+        for key, wl in (("prefill_f32", wf), ("prefill_tiny", wt)):
+            inp = I.generate(wl)
+            lay = TT.make_layer(wl, inp, dev, out="f32")
+            tok = TT.token_tensors(wl, inp, 0, wl.T, dev)
+            sets[key] = [dict(layer=lay, tok={k: v.clone() for k, v in tok.items()},
+                              state=torch.zeros((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev),
+                              conv=torch.zeros((wl.B, wl.c_qkv, wl.W - 1), dtype=torch.float32, device=dev),
+                              out=torch.empty((wl.B, wl.T, wl.H * wl.dv), dtype=torch.float32, device=dev),
+                              ws=workspace(lay, wl.B, wl.T)) for _ in range(nsets)]
+            del tok
     # --- variable-length sets: the prefill tokens as packed sequences of a seeded length mix
     var_lens = I.varlen_lengths(wp.T, VARLEN_SEQS, VARLEN_SEED)
     var_cu = I.cu_seqlens(var_lens)
@@ -520,8 +533,8 @@ def main():
 
     def run(op, s):
         t = s.get("tok")
-        if op in ("prefill", "prefill_softplus", "prefill_strong"):
-            lay = {"prefill": "layer", "prefill_softplus": "layer_sp", "prefill_strong": "layer_st"}[op]
+        if op in ("prefill", "prefill_softplus", "prefill_strong", "prefill_f32", "prefill_tiny"):
+            lay = {"prefill_softplus": "layer_sp", "prefill_strong": "layer_st"}.get(op, "layer")
             abi.kda_prefill(s[lay], t["qkv"], t["f"], t["beta"], t["g_out"],
                             s["state"], s["conv"], s["out"], workspace=s["ws"], stream=stream)
         elif op == "varlen":
@@ -551,13 +564,15 @@ def main():
         if op in ("prefill", "decode"):
             seq.append(op + "_softplus")
         if op == "prefill":
-            seq.append("prefill_strong")
+            seq += ["prefill_strong", "prefill_f32", "prefill_tiny"]
 
     def setof(op):
         if op.endswith("_softplus"):
             return op[: -len("_softplus")]
         if op == "prefill_strong":
             return "prefill"
+        if op in ("prefill_f32", "prefill_tiny"):
+            return op
         return "verify" if op in ("rollback", "verify_tape", "commit") else op
 
     for i in range(args.warmup):
@@ -585,14 +600,15 @@ def main():
     # the same K steps again with an event pair around every kernel (the library's timing hook),
     # for the per-kernel durations; kept out of the timed steps above so its events add no gaps
     abi.timing_enable(True)
+    kernel_ms, op_kernel_ms = {}, {}
     for op in seq:
         for i in range(K):
             run(op, sets[setof(op)][i % nsets])
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        for name, t in abi.timing_read():  # this call type's launches, in order
+            kernel_ms.setdefault(name, []).append(t)
+            op_kernel_ms.setdefault(op, {}).setdefault(name, []).append(t)
     abi.timing_enable(False)
-    kernel_ms = {}
-    for name, t in abi.timing_read():
-        kernel_ms.setdefault(name, []).append(t)
     if args.calib_copy:
         src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
         dst = torch.empty_like(src)
@@ -637,7 +653,8 @@ def main():
                                "sequences + their input projection (hidden 4096) + decode_b64 (B=64,H=32,d=128) "
                                "+ verify_b16 (B=16,T_d=8,H=32,d=128) with rollback and with the replay tape; "
                                "prefill_t4096 and decode_b64 again on the softplus decay branch; prefill_t4096 "
-                               "with gate_lower_bound -8",
+                               "with gate_lower_bound -8; the fp32 prefill at T=1024 and the small fp32 layer (T=64, H=2, "
+                               "d=16)",
                    "io": "bf16 inputs and outputs, fp32 state and accumulation", "buffer_sets": nsets},
         "wall_s": wall,
     }
@@ -686,6 +703,14 @@ def main():
         detail["prefill_strong"] = {"ms_mean": ms, "tokens_per_s": wp.T / (ms * 1e-3), "alg_bytes": pb,
                                     "gbps": pb / (ms * 1e-3) / 1e9, "vs_prefill": ms / mean["prefill"],
                                     "workload": "prefill_t4096 with the bounded gate at gate_lower_bound = -8"}
+        for op, wl, what in (("prefill_f32", wf, "fp32 io and out, B=1, T=1024, H=32, d=128, chunk 64 (the "
+                                                 "vector-ALU prefill, internal chunk 32)"),
+                             ("prefill_tiny", wt, "the small fp32 layer: B=1, T=64, H=2, d=16, chunk 16 "
+                                                  "(launch-latency bound)")):
+            ms = mean[op]
+            nb = prefill_bytes(wl.B, wl.T, wl.H, wl.dk, wl.W, io_b=4, out_b=4)
+            detail[op] = {"ms_mean": ms, "tokens_per_s": wl.B * wl.T / (ms * 1e-3), "alg_bytes": nb,
+                          "gbps": nb / (ms * 1e-3) / 1e9, "workload": what}
     if "decode" in ops:
         db = decode_bytes(wd.B, wd.H, wd.dk, wd.W)
         gb = db / (mean["decode"] * 1e-3) / 1e9
@@ -717,10 +742,14 @@ def main():
         if "value" not in res:
             res["value"], res["unit"] = gv, "GB/s"
     line_of = {"prefill": "prefill", "varlen": "prefill_varlen", "projection": "input_projection",
-               "prefill_softplus": "prefill_softplus", "prefill_strong": "prefill_strong", "decode": "decode",
+               "prefill_softplus": "prefill_softplus", "prefill_strong": "prefill_strong",
+               "prefill_f32": "prefill_f32", "prefill_tiny": "prefill_tiny", "decode": "decode",
                "decode_softplus": "decode_softplus",
                "verify": "verify", "rollback": "rollback", "verify_tape": "verify_tape", "commit": "commit_tape"}
     for op, line in line_of.items():
+        if op in op_kernel_ms and line in detail:
+            # the call's kernels alone (their mean event time per launch), apart from host submission
+            detail[line]["kernels_ms_mean"] = {n: float(np.mean(t)) for n, t in op_kernel_ms[op].items()}
         if op in dist and line in detail:
             detail[line].update(dist[op])
             if "alg_bytes" in detail[line] and detail[line]["alg_bytes"]:

@@ -220,17 +220,19 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
     }
     __syncthreads();
     // -- UT solve by forward substitution: X[i] -= sum_{j<i} A_kk[i,j] X[j]  (X = W | this
-    //    workgroup's columns of Ut)
-    for (int i = 1; i < L; ++i) {
-      for (int col = tid; col < D + DV; col += NT) {
-        float* X = col < D ? sg : sv;
-        const int cc = col < D ? col : v0 + col - D;
+    //    workgroup's columns of Ut).  A column's rows depend only on that column, and one thread
+    //    owns each column (D + DV <= NT), so the rows need no barrier between them.
+    static_assert(2 * D <= NT, "one thread per column of W | Ut");
+    if (tid < D + DV) {
+      float* X = tid < D ? sg : sv;
+      const int cc = tid < D ? tid : v0 + tid - D;
+      for (int i = 1; i < L; ++i) {
         float acc = X[i * LP + cc];
         for (int j = 0; j < i; ++j) acc -= sAkk[i * AP + j] * X[j * LP + cc];
         X[i * LP + cc] = acc;
       }
-      __syncthreads();
     }
+    __syncthreads();
     // -- U = Ut - W S
     for (int idx = tid; idx < L * DV; idx += NT) {
       const int i = idx / DV, jj = idx % DV, j = v0 + jj;
