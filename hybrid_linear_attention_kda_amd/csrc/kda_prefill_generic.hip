@@ -222,14 +222,36 @@ __global__ __launch_bounds__(kGenericThreads) void kda_prefill_generic_kernel(La
     // -- UT solve by forward substitution: X[i] -= sum_{j<i} A_kk[i,j] X[j]  (X = W | this
     //    workgroup's columns of Ut).  A column's rows depend only on that column, and one thread
     //    owns each column (D + DV <= NT), so the rows need no barrier between them.
+    //    Where a chunk has at most 32 rows the column sits in registers and the rows are unrolled,
+    //    so the A_kk reads are independent of the running sums and all in flight together.
     static_assert(2 * D <= NT, "one thread per column of W | Ut");
     if (tid < D + DV) {
       float* X = tid < D ? sg : sv;
       const int cc = tid < D ? tid : v0 + tid - D;
-      for (int i = 1; i < L; ++i) {
-        float acc = X[i * LP + cc];
-        for (int j = 0; j < i; ++j) acc -= sAkk[i * AP + j] * X[j * LP + cc];
-        X[i * LP + cc] = acc;
+      constexpr int R = kGenericChunkElems / D;  // rows of the largest chunk
+      if constexpr (R <= 32) {
+        float x[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[r] = X[min(r, L - 1) * LP + cc];
+#pragma unroll
+        for (int i = 1; i < R; ++i) {
+          if (i < L) {
+            float acc = x[i];
+#pragma unroll
+            for (int j = 0; j < i; ++j) acc -= sAkk[i * AP + j] * x[j];
+            x[i] = acc;
+          }
+        }
+#pragma unroll
+        for (int r = 1; r < R; ++r)
+          if (r < L) X[r * LP + cc] = x[r];
+      } else {
+        for (int i = 1; i < L; ++i) {
+          float acc = X[i * LP + cc];
+#pragma unroll 8
+          for (int j = 0; j < i; ++j) acc -= sAkk[i * AP + j] * X[j * LP + cc];
+          X[i * LP + cc] = acc;
+        }
       }
     }
     __syncthreads();
