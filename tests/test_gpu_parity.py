@@ -645,6 +645,27 @@ def test_fp32_prefill_head_size_128_bf16_out():
     _check("conv_state", cs, ref["conv_state"], 0.0)
 
 
+@pytest.mark.parametrize("d,io", [(32, "f32"), (64, "f32"), (64, "bf16")])
+def test_vector_alu_prefill_head_sizes_32_64(d, io):
+    # head sizes the matrix-core path does not take: internal chunk 64, the value columns split over
+    # two (d = 32) or four (d = 64, 16 columns each) workgroups per head, one full chunk and a ragged
+    # tail; the arithmetic is fp32 throughout for bf16 io too
+    wl = I.WORKLOADS["prefill_t4096"].with_(T=100, H=2, B=2, dk=d, dv=d, io=io, seed=14)
+    say(f"case vector-ALU prefill d={d} io={io} H=2 B=2 T=100")
+    inp = I.generate(wl)
+    rng = np.random.default_rng(200 + d)
+    S0 = (rng.standard_normal(inp["state0"].shape) * 0.3).astype(np.float32)
+    C0 = I.round_to_io(rng.standard_normal(inp["conv_state0"].shape), io)
+    layer = TT.make_layer(wl, inp, DEV, out="f32")
+    st, cs = _dev_state(wl, inp, S0, C0)
+    out = _gpu_prefill(wl, inp, layer, 0, 100, st, cs)
+    torch.cuda.synchronize()
+    ref = oracle_layer(wl, inp, 0, 100, S0, C0)
+    _check("out", out, ref["out"], TOL["f32"])
+    _check("state", st, ref["state"], TOL["f32"])
+    _check("conv_state", cs, ref["conv_state"], 0.0)
+
+
 def test_fp32_varlen_prefill_head_size_128():
     # split value columns with the state and conv-state pools updated in place, ragged lengths
     wl = I.WORKLOADS["prefill_t4096"].with_(H=2, io="f32", seed=23)
