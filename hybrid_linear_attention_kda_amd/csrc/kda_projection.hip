@@ -26,6 +26,7 @@ constexpr int PJ_NT = 256;
 constexpr int PJ_PB = kProjRank + 8;    // LDS pitch of a weight row (bf16), spreads the banks
 constexpr int PJ_XCD = 8;               // L2 domains the workgroups are dealt over, round robin
 constexpr int PJ_CB = 8;                // 128-column blocks one low-rank workgroup walks
+constexpr int PJ_OUT_POLICY = 2;        // cache policy of the low-rank outputs' stores: non-temporal
 
 __device__ __forceinline__ f32x4 pj_mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -38,12 +39,33 @@ template <typename OT>
 __device__ __forceinline__ void pj_buffer_store4(__amdgpu_buffer_rsrc_t r, int off, f32x4 v);
 template <>
 __device__ __forceinline__ void pj_buffer_store4<float>(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), r, off, 0, PJ_OUT_POLICY);
 }
 template <>
 __device__ __forceinline__ void pj_buffer_store4<bf16_t>(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
   const __attribute__((ext_vector_type(2))) unsigned u = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
   __builtin_amdgcn_raw_buffer_store_b64(u, r, off, 0, 0);
+}
+// eight consecutive outputs of one token, a then b, through a buffer resource (as above)
+template <typename OT>
+__device__ __forceinline__ void pj_buffer_store8(__amdgpu_buffer_rsrc_t r, int off, f32x4 a, f32x4 b);
+template <>
+__device__ __forceinline__ void pj_buffer_store8<float>(__amdgpu_buffer_rsrc_t r, int off, f32x4 a, f32x4 b) {
+  pj_buffer_store4<float>(r, off, a);
+  pj_buffer_store4<float>(r, off + 16, b);
+}
+template <>
+__device__ __forceinline__ void pj_buffer_store8<bf16_t>(__amdgpu_buffer_rsrc_t r, int off, f32x4 a, f32x4 b) {
+  const __attribute__((ext_vector_type(4))) unsigned u = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                                          pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+  __builtin_amdgcn_raw_buffer_store_b128(u, r, off, 0, PJ_OUT_POLICY);
+}
+// LDS row of weight row n within its 128-row block: n = 32 p + 8 a + 4 h + i goes to row
+// 16 (2 p + h) + 4 a + i, so that product tile 2 p + h gives lane group a (accumulator rows
+// 4 a .. 4 a + 3) the columns 32 p + 8 a + 4 h + 0..3, and the lane holds eight consecutive
+// columns of its token over tiles 2 p and 2 p + 1
+__device__ __forceinline__ int pj_lds_row(int n) {
+  return 16 * (2 * (n >> 5) + ((n >> 2) & 1)) + 4 * ((n >> 3) & 3) + (n & 3);
 }
 // four consecutive outputs of one token
 __device__ __forceinline__ void pj_store4(float* p, f32x4 v) {
@@ -61,8 +83,10 @@ __device__ __forceinline__ void pj_store4(bf16_t* p, f32x4 v) {
 // and g for which = 1.  A workgroup keeps one 64-token tile of activations in registers (split into
 // bf16 hi + lo once) and walks up to PJ_CB consecutive 128-column blocks of W: block j + 1 is loaded
 // into registers while block j is multiplied from LDS, then written into the other of two LDS
-// buffers.  The product is taken transposed (out^T tile = W tile . act^T) so that each lane ends
-// with four consecutive output columns of one token; the stores go through a buffer resource that
+// buffers.  The product is taken transposed (out^T tile = W tile . act^T), with the weight rows
+// placed in LDS in the order pj_lds_row gives, so that each lane ends with eight consecutive output
+// columns of one token over two tiles and writes them as one 16-byte store (bf16; two for fp32),
+// 64 contiguous bytes per token row and store; the stores go through a buffer resource that
 // ends at row T, so rows past the end are dropped by the hardware and the loop has no branch.
 //
 // Workgroup b runs on L2 domain b % 8 and takes a row tile = b % 8 modulo 8, so one domain's L2
@@ -92,8 +116,11 @@ __global__ __launch_bounds__(PJ_NT) __attribute__((amdgpu_waves_per_eu(1, 2))) v
   // the weight rows of a column block, 16-byte pieces (16 per row)
   constexpr int NW = PJ_COLS * (R / 8) / PJ_NT;
   const bf16_t* wsrc = W + (long long)(tid / (R / 8)) * R + (tid % (R / 8)) * 8;  // piece j: + j * (PJ_NT / 16) rows
-  const int wdst = (tid / (R / 8)) * PJ_PB + (tid % (R / 8)) * 8;
   constexpr int WROWS = PJ_NT / (R / 8);
+  // LDS position of piece j (weight row tid / 16 + j WROWS of the block, permuted by pj_lds_row)
+  auto wdst = [&](int j) __attribute__((always_inline)) {
+    return pj_lds_row(tid / (R / 8) + j * WROWS) * PJ_PB + (tid % (R / 8)) * 8;
+  };
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   u32x4 wv[NW];
 #pragma unroll
@@ -108,7 +135,7 @@ __global__ __launch_bounds__(PJ_NT) __attribute__((amdgpu_waves_per_eu(1, 2))) v
     xv[s][1] = *reinterpret_cast<const float4*>(ap + 32 * s + 4);
   }
 #pragma unroll
-  for (int j = 0; j < NW; ++j) *reinterpret_cast<u32x4*>(&sW[0][wdst + j * WROWS * PJ_PB]) = wv[j];
+  for (int j = 0; j < NW; ++j) *reinterpret_cast<u32x4*>(&sW[0][wdst(j)]) = wv[j];
   // split B operands: fp32 activations as bf16 hi + lo
   bf16x8 xhi[R / 32], xlo[R / 32];
 #pragma unroll
@@ -122,10 +149,10 @@ __global__ __launch_bounds__(PJ_NT) __attribute__((amdgpu_waves_per_eu(1, 2))) v
       xlo[s][e] = (__bf16)(x[e] - (float)hi);
     }
   }
-  // output rows r0 .. T-1 of this workgroup's tile; lane: columns 16 ct + 4 lg .. + 3 of token trow
+  // output rows r0 .. T-1 of this workgroup's tile; lane: columns 32 p + 8 lg .. + 7 of token trow
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
       out + (long long)r0 * HD, 0, (int)((long long)min(PJ_ROWS, T - r0) * HD * (int)sizeof(OT)), 0x00020000);
-  const int obase = ((16 * wave + l16) * HD + 4 * lg) * (int)sizeof(OT);
+  const int obase = ((16 * wave + l16) * HD + 8 * lg) * (int)sizeof(OT);
   __syncthreads();
   for (int j = 0; j < nb; ++j) {
     // the next block (the last one again at the end)
@@ -147,11 +174,12 @@ __global__ __launch_bounds__(PJ_NT) __attribute__((amdgpu_waves_per_eu(1, 2))) v
       }
     const int ob = obase + (cb0 + j) * PJ_COLS * (int)sizeof(OT);
 #pragma unroll
-    for (int ct = 0; ct < PJ_COLS / 16; ++ct) pj_buffer_store4<OT>(orsrc, ob + 16 * ct * (int)sizeof(OT), acc[ct]);
+    for (int p = 0; p < PJ_COLS / 32; ++p)
+      pj_buffer_store8<OT>(orsrc, ob + 32 * p * (int)sizeof(OT), acc[2 * p], acc[2 * p + 1]);
     // buffer (j + 1) & 1 was last read in block j - 1, before the previous barrier
     __bf16* sn = sW[(j + 1) & 1];
 #pragma unroll
-    for (int q = 0; q < NW; ++q) *reinterpret_cast<u32x4*>(sn + wdst + q * WROWS * PJ_PB) = wn[q];
+    for (int q = 0; q < NW; ++q) *reinterpret_cast<u32x4*>(sn + wdst(q)) = wn[q];
     __syncthreads();
   }
   if (which == 0 && cb0 == 0) {
